@@ -1,0 +1,133 @@
+// Device-side helpers shared by the libmok kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOK_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+MOK_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// float32 -> bf16, round to nearest even (NaN stays NaN).
+MOK_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <class T> MOK_DEV float load_as_f32(const T* p);
+template <> MOK_DEV float load_as_f32<float>(const float* p) { return *p; }
+template <> MOK_DEV float load_as_f32<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+template <class T> MOK_DEV T f32_to(float v);
+template <> MOK_DEV float f32_to<float>(float v) { return v; }
+template <> MOK_DEV bf16_t f32_to<bf16_t>(float v) { return f32_to_bf16(v); }
+
+MOK_DEV int lane_id() { return __lane_id(); }
+
+MOK_DEV uint64_t ballot(bool p) { return __ballot(p); }
+
+MOK_DEV uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+MOK_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m, kWave);
+  hi = __shfl_xor(hi, m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+MOK_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ----------------------------------------------------------------------- MXFP8 (OCP MX)
+// Shared exponent of a block from its absolute maximum: floor(log2(amax)) - 8, clamped to
+// [-127, 127]; amax == 0 -> -127. Exact integer arithmetic on the float's fields.
+MOK_DEV int mx_shared_exp(float amax) {
+  uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
+  if (u == 0) return -127;
+  int e;
+  if ((u >> 23) == 0) {                 // float32 subnormal: value = m * 2^-149
+    e = 31 - __clz(u) - 149;           // floor(log2(m)) - 149
+  } else {
+    e = (int)(u >> 23) - 127;
+  }
+  int s = e - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// E4M3 ("FN") code of v * 2^-s: round to nearest, ties to even, saturate to 448, keep sign.
+// Integer-only: the float32's bits are re-rounded at the bit position of E4M3's step.
+MOK_DEV uint32_t e4m3_encode(float v, int s) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a == 0) return sign;
+  // unbiased exponent and 24-bit significand of |v| (subnormal floats handled)
+  int ex;
+  uint32_t sig;
+  if ((a >> 23) == 0) {
+    int lz = __clz(a) - 8;             // shift the leading one to bit 23
+    sig = a << lz;
+    ex = -126 - lz;
+  } else {
+    sig = (a & 0x7FFFFFu) | 0x800000u;
+    ex = (int)(a >> 23) - 127;
+  }
+  int e = ex - s;                      // exponent of |v| * 2^-s
+  if (e > 8) return sign | 0x7Eu;      // >= 512 -> saturate
+  // step of the E4M3 grid in this binade: 2^(e-3) for e >= -6, 2^-9 below
+  int step_e = (e >= -6 ? e : -6) - 3;
+  // |v|*2^-s = sig * 2^(e-23); quantum index q = sig * 2^(e-23-step_e)
+  int sh = 23 + step_e - e;            // right shift amount (>= 3)
+  uint32_t q;
+  if (sh >= 25) {
+    q = 0;                             // below half a step: sig < 2^24 <= 2^(sh-1)
+  } else {
+    uint32_t kept = sig >> sh;
+    uint32_t rem = sig & ((1u << sh) - 1u);
+    uint32_t half = 1u << (sh - 1);
+    q = kept + ((rem > half || (rem == half && (kept & 1u))) ? 1u : 0u);
+  }
+  // value = q * 2^step_e; encode
+  if (q == 0) return sign;
+  if (q < 8) return sign | q;          // only possible with step 2^-9: subnormal, field 0
+  // normal: value = q * 2^step_e with q in [8, 16]; q == 16 carries into the next binade
+  int ef = step_e + 3 + 7;             // exponent field for q in [8, 16)
+  if (q == 16) { q = 8; ef += 1; }
+  if (ef > 15 || (ef == 15 && q > 14)) return sign | 0x7Eu;  // > 448 -> 448
+  return sign | ((uint32_t)ef << 3) | (q - 8);
+}
+
+// One 32-element block of bf16 -> 32 E4M3 code bytes + 1 E8M0 scale byte (16 B aligned).
+MOK_DEV void quantize_block32(const bf16_t* __restrict__ src, uint8_t* __restrict__ codes,
+                              uint8_t* __restrict__ scale) {
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = ((const uint4*)src)[i];
+  const bf16_t* v = (const bf16_t*)raw;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(v[i])));
+  const int s = mx_shared_exp(amax);
+  uint32_t packed[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) word |= e4m3_encode(bf16_to_f32(v[4 * w + b]), s) << (8 * b);
+    packed[w] = word;
+  }
+  ((uint4*)codes)[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  ((uint4*)codes)[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  *scale = (uint8_t)(s + 127);
+}

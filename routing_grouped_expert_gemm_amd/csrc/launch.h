@@ -1,0 +1,67 @@
+// Internal launchers of libmok (host side). Not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mok {
+
+hipError_t launch_router_logits(const void* x, const void* wr, int64_t n_tok, int d, int E,
+                                bool bf16, float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, int64_t n_tok, int E, int k, int32_t* idx,
+                       float* w, hipStream_t s);
+
+int64_t plan_chunk(int64_t n_routes);
+int64_t plan_n_blocks(int64_t n_routes);
+hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
+                       int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
+                       int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
+                       int32_t* blk_base, hipStream_t s);
+
+hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s);
+
+// Operand element type of the expert GEMMs.
+enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+// Everything the expert-GEMM stages of one forward need (device pointers unless noted).
+struct ExpertPass {
+  Elem elem;             // GEMM operand type
+  bool out_f32;          // outputs (H for non-MX, P, S, y) in float32 (else bf16)
+  int d, k, I, E_l;
+  int I_sh;              // n_shared * I_shared (0: no shared expert)
+  int I_seg;             // I_shared: K-segment length of the shared down projection
+  int64_t own_begin;
+  int T_own;
+  int mb;                // minibatch rows
+  int n_slots;           // ring slots (ring rows = n_slots * mb)
+  int Hld;               // ring row length in elements: max(I, I_sh)
+  int max_mb;            // capacity of the minibatch tables
+  int bm, bn;            // GEMM tile (rows, B-tile rows)
+  int grid;              // workgroups of the tile loops
+  // inputs
+  const void* x;         // [T_pool, d] float32 or bf16
+  const int32_t* route_ids;
+  const float* topk_w;   // [T_pool*k]
+  const int32_t* counts;
+  const int32_t* offsets;
+  const void *wg, *wu, *wd;     // routed weights (float32 / bf16) -- or MX codes
+  const void *sg, *su, *sd;     // shared weights
+  const uint8_t *wg_sc, *wu_sc, *wd_sc, *sg_sc, *su_sc, *sd_sc;  // MX scales (FP8 only)
+  // ring
+  void* H;               // [n_slots*mb, Hld] (float32/bf16) -- MX: codes
+  uint8_t* H_sc;         // MX: [n_slots*mb, Hld/32]
+  uint8_t* A_codes;      // MX: gathered x rows [n_slots*mb, d]
+  uint8_t* A_sc;         // MX: [n_slots*mb, d/32]
+  // work list
+  int32_t* wl;           // work-list block (see expert_gemm.hip)
+  // outputs
+  void* y_slots;
+  void* y_shared;
+};
+
+size_t worklist_ints(int max_mb);
+hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s);
+hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, int64_t n_tok,
+                          int k, int d, bool f32, hipStream_t s);
+
+}  // namespace mok

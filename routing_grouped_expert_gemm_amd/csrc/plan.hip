@@ -1,0 +1,189 @@
+// Stage 2: the pull dispatch plan, and the GEMM work list derived from it on the device.
+//
+// The MoK write-up's "Scheduling" section: for a pull dispatch the schedule is a table
+// {src_rank, src_index} whose row index is the row of the local destination buffer; it needs
+// no sort, only a walk over the routing results that records every route to a local expert,
+// together with the count per local expert, the count per (local expert, source rank) and
+// the region offsets. The Telegram summary adds that pulling lets each expert read its
+// tokens as large contiguous chunks with no contended atomic slot counters.
+//
+// Here the walk is split over workgroups and stays deterministic: (1) each workgroup counts
+// the local routes of its contiguous chunk of routes per expert; (2) one workgroup scans
+// those counts into region offsets and per-chunk bases; (3) each workgroup walks its chunk
+// again in order and writes every local route at base + its stable rank (ballot prefix
+// counts), so each region is in ascending route order -- a stable counting sort; (4) the
+// per-(expert, source rank) counts are read off the sorted regions by binary search.
+// Only order-independent integer arithmetic is used; no position is taken by an atomic.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mok {
+
+constexpr int PLAN_THREADS = 256;
+
+__global__ __launch_bounds__(PLAN_THREADS) void k_plan_count(const int32_t* __restrict__ idx,
+                                                             int64_t n_routes, int64_t chunk,
+                                                             int e0, int E_l,
+                                                             int32_t* __restrict__ blk_counts) {
+  extern __shared__ int32_t hist[];  // [E_l]
+  for (int e = threadIdx.x; e < E_l; e += PLAN_THREADS) hist[e] = 0;
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * chunk;
+  const int64_t r1 = min(n_routes, r0 + chunk);
+  for (int64_t r = r0 + threadIdx.x; r < r1; r += PLAN_THREADS) {
+    const int le = idx[r] - e0;
+    if (le >= 0 && le < E_l) atomicAdd(&hist[le], 1);  // integer count: order-independent
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E_l; e += PLAN_THREADS)
+    blk_counts[(int64_t)blockIdx.x * E_l + e] = hist[e];
+}
+
+// One workgroup of 1024 threads. blk_base[b][e] = offsets[e] + sum_{b' < b} blk_counts[b'][e].
+__global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ blk_counts,
+                                                    int n_blk, int E_l,
+                                                    int32_t* __restrict__ blk_base,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t tot[1024];
+  const int e = threadIdx.x;
+  int32_t sum = 0;
+  if (e < E_l)
+    for (int b = 0; b < n_blk; ++b) {
+      const int32_t c = blk_counts[(int64_t)b * E_l + e];
+      blk_base[(int64_t)b * E_l + e] = sum;
+      sum += c;
+    }
+  tot[e] = e < E_l ? sum : 0;
+  part[e] = tot[e];
+  __syncthreads();
+  // inclusive Hillis-Steele scan over experts
+  for (int off = 1; off < 1024; off <<= 1) {
+    int32_t v = e >= off ? part[e - off] : 0;
+    __syncthreads();
+    part[e] += v;
+    __syncthreads();
+  }
+  const int32_t excl = part[e] - tot[e];
+  if (e < E_l) {
+    counts[e] = tot[e];
+    offsets[e] = excl;
+    if (e == E_l - 1) offsets[E_l] = part[e];
+    for (int b = 0; b < n_blk; ++b) blk_base[(int64_t)b * E_l + e] += excl;
+  }
+}
+
+__global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __restrict__ idx,
+                                                               int64_t n_routes, int64_t chunk,
+                                                               int e0, int E_l,
+                                                               const int32_t* __restrict__ blk_base,
+                                                               int32_t* __restrict__ route_ids) {
+  extern __shared__ int32_t sm[];
+  int32_t* base = sm;                 // [E_l] next free row of each region (this chunk)
+  int32_t* wcnt = sm + E_l;           // [4][E_l] per-wave counts of the current sub-chunk
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < E_l; e += PLAN_THREADS) {
+    base[e] = blk_base[(int64_t)blockIdx.x * E_l + e];
+    for (int q = 0; q < 4; ++q) wcnt[q * E_l + e] = 0;
+  }
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * chunk;
+  const int64_t r1 = min(n_routes, r0 + chunk);
+  for (int64_t rs = r0; rs < r1; rs += PLAN_THREADS) {
+    const int64_t r = rs + tid;
+    int le = -1;
+    if (r < r1) {
+      le = idx[r] - e0;
+      if (le < 0 || le >= E_l) le = -1;
+    }
+    // stable rank among the lanes of this wave with the same expert
+    int rank = 0;
+    bool leader = false;
+    int cnt = 0;
+    uint64_t remaining = ballot(le >= 0);
+    while (remaining) {
+      const int lead = __ffsll((unsigned long long)remaining) - 1;
+      const int key = __shfl(le, lead, kWave);
+      const uint64_t m = ballot(le == key);
+      if (le == key) rank = __popcll(m & lanemask_lt());
+      if (lane == lead) { leader = true; cnt = __popcll(m); }
+      remaining &= ~m;
+    }
+    if (leader) wcnt[w * E_l + le] = cnt;
+    __syncthreads();
+    if (le >= 0) {
+      int32_t pos = base[le] + rank;
+      for (int q = 0; q < w; ++q) pos += wcnt[q * E_l + le];
+      route_ids[pos] = (int32_t)r;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&base[le], cnt);      // integer: order-independent
+      wcnt[w * E_l + le] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// rank_counts[e][rho] = routes of expert e from source rank rho: the sorted region's entries
+// in [rho * tpr * k, (rho + 1) * tpr * k).
+MOK_DEV int32_t lower_bound_i32(const int32_t* a, int32_t n, int64_t v) {
+  int32_t lo = 0, hi = n;
+  while (lo < hi) {
+    int32_t mid = (lo + hi) >> 1;
+    if ((int64_t)a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void k_plan_rank_counts(const int32_t* __restrict__ route_ids,
+                                   const int32_t* __restrict__ offsets, int E_l, int64_t R,
+                                   int64_t routes_per_rank, int32_t* __restrict__ rank_counts) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= (int64_t)E_l * R) return;
+  const int e = (int)(q / R);
+  const int64_t rho = q % R;
+  const int32_t* reg = route_ids + offsets[e];
+  const int32_t n = offsets[e + 1] - offsets[e];
+  rank_counts[q] = lower_bound_i32(reg, n, (rho + 1) * routes_per_rank) -
+                   lower_bound_i32(reg, n, rho * routes_per_rank);
+}
+
+int64_t plan_chunk(int64_t n_routes) {
+  // ~4096 routes per workgroup, at most 4096 workgroups
+  int64_t chunk = 4096;
+  while ((n_routes + chunk - 1) / chunk > 4096) chunk *= 2;
+  return chunk;
+}
+
+int64_t plan_n_blocks(int64_t n_routes) {
+  const int64_t c = plan_chunk(n_routes);
+  return n_routes == 0 ? 1 : (n_routes + c - 1) / c;
+}
+
+hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
+                       int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
+                       int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
+                       int32_t* blk_base, hipStream_t s) {
+  const int64_t n_routes = n_tok * k;
+  const int64_t chunk = plan_chunk(n_routes);
+  const int64_t nb = plan_n_blocks(n_routes);
+  const size_t sh_count = sizeof(int32_t) * (size_t)E_l;
+  hipLaunchKernelGGL(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS), sh_count, s, idx,
+                     n_routes, chunk, e0, E_l, blk_counts);
+  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, s, blk_counts, (int)nb, E_l, blk_base,
+                     counts, offsets);
+  hipLaunchKernelGGL(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS), sh_count * 5, s, idx,
+                     n_routes, chunk, e0, E_l, blk_base, route_ids);
+  if (rank_counts) {
+    const int64_t R = n_tok / tokens_per_rank;
+    const int64_t n = (int64_t)E_l * R;
+    if (n > 0)
+      hipLaunchKernelGGL(k_plan_rank_counts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                         route_ids, offsets, E_l, R, tokens_per_rank * k, rank_counts);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mok
