@@ -1,0 +1,179 @@
+"""Throughput of the MoE-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step = one mok_moe_forward over the workload's whole batch: router projection + top-k,
+dispatch plan, pull gather + gate/up GEMM with SwiGLU, down GEMM with the routing-weight
+scale, shared experts and the fixed-order combine. Inputs are seeded synthetic tensors
+already resident in HBM. Prints ONE JSON line.
+
+`roofline` is taken live for the dominant kernel (the gate/up stage: grouped gate/up GEMM
+with the fused pull gather and SwiGLU, routed + shared): HIP events recorded by the library
+on the forward's own stream around that launch, averaged over the timed steps, against the
+algorithmic FLOPs of one launch (4 * d * I per routed row + 4 * d * I_shared * n_shared per
+own token). `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/s + routed-expert TFLOP/s on 1 MI355X (bf16, MXFP8)"
+PEAK = {"bf16": 2.5e15, "mxfp8": 5.0e15, "fp32": 157.3e12}
+HBM_PEAK = 8.0e12
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime (the library records them on its stream)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float(0)
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        return out.value
+
+    def ptr(self):
+        return ctypes.cast(self.ev, ctypes.c_void_p).value
+
+
+def algorithmic_work(wl, n_routes: int) -> dict:
+    I_sh = wl.n_shared * wl.I_shared
+    up = 4.0 * wl.d * wl.I * n_routes + 4.0 * wl.d * I_sh * wl.T_own
+    down = 2.0 * wl.d * wl.I * n_routes + 2.0 * wl.d * I_sh * wl.T_own
+    return dict(routed_flop=6.0 * wl.d * wl.I * n_routes, shared_flop=6.0 * wl.d * I_sh * wl.T_own,
+                up_flop=up, down_flop=down)
+
+
+def cpu_baseline(wl, inputs_cpu, sample_tokens: int) -> dict:
+    """The oracle (as it stands) on the first `sample_tokens` tokens of the workload."""
+    import numpy as np
+    import oracle
+    import synth
+    sub = synth.scaled(wl, T_pool=sample_tokens, tokens_per_rank=sample_tokens,
+                       T_own=min(wl.T_own, sample_tokens))
+    x = inputs_cpu["x"][:sample_tokens]
+    t0 = time.perf_counter()
+    if wl.routing == "router":
+        out = oracle.moe_forward(sub, x, w_router=inputs_cpu["w_router"], wg=inputs_cpu["wg"],
+                                 wu=inputs_cpu["wu"], wd=inputs_cpu["wd"], sg=inputs_cpu["sg"],
+                                 su=inputs_cpu["su"], sd=inputs_cpu["sd"])
+    else:
+        idx, w = oracle.topk(inputs_cpu["logits"][:sample_tokens], wl.k)
+        out = oracle.moe_forward(sub, x, wg=inputs_cpu["wg"], wu=inputs_cpu["wu"],
+                                 wd=inputs_cpu["wd"], sg=inputs_cpu["sg"], su=inputs_cpu["su"],
+                                 sd=inputs_cpu["sd"], topk_in=(idx, w))
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["y_shared"]).all()
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {sample_tokens} of {wl.T_pool} tokens, whole forward "
+                      f"(routing, plan, float64 expert and shared FFNs, combine); {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--ring", action="store_true", help="persistent ring work loop")
+    ap.add_argument("--minibatch", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import routing_grouped_expert_gemm_amd as mok
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _layer import gpu_layer, gpu_topk, make_inputs
+
+    wl = synth.WORKLOADS[args.workload or synth.EP1]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = make_inputs(wl, dev)
+    topk = gpu_topk(inp["logits"], wl.k) if wl.routing == "logits" else None
+    flags = 0 if args.ring else mok.MOK_FLAG_NO_RING
+    layer = gpu_layer(wl, inp, topk=topk, flags=flags, mb=args.minibatch, keep=True)
+    ev = HipEvents(2 * mok.MOK_N_STAGES * (args.steps + 1))
+    stream = torch.cuda.current_stream()
+
+    def step(i=None):
+        layer.args.stage_events = None if i is None else \
+            ctypes.cast(ctypes.byref(ev.ev, 8 * 2 * mok.MOK_N_STAGES * i), ctypes.c_void_p).value
+        layer.forward(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = 1e3 * elapsed / args.steps
+    assert layer.device_error(stream) == 0
+
+    n_routes = int(layer.inter["offsets"][-1])
+    work = algorithmic_work(wl, n_routes)
+    stage_ms = {}
+    names = ["route", "plan", "quant", "up", "down", "combine"]
+    for s, name in enumerate(names):
+        vals = [ev.elapsed_ms(2 * 6 * i + 2 * s, 2 * 6 * i + 2 * s + 1) for i in range(args.steps)]
+        stage_ms[name] = sum(vals) / len(vals)
+    up_s = stage_ms["up"] * 1e-3
+    peak = PEAK[wl.dtype]
+    achieved = work["up_flop"] / up_s
+    tokens = wl.T_own if not wl.full_layer else wl.T_pool
+    value = tokens / (ms * 1e-3)
+    gemm_s = (stage_ms["up"] + stage_ms["down"]) * 1e-3
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "mxfp8": "mxfp8", "fp32": "f32"}[wl.dtype],
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": wl.name, "T_pool": wl.T_pool, "d": wl.d, "E": wl.E, "k": wl.k,
+                   "I": wl.I, "E_local": wl.E_l, "n_shared": wl.n_shared,
+                   "I_shared": wl.I_shared, "minibatch_rows": layer.args.minibatch_rows,
+                   "work_loop": "ring" if args.ring else "stage-ordered"},
+        "routed_rows": n_routes,
+        "routed_tflops": round(work["routed_flop"] / (ms * 1e-3) / 1e12, 2),
+        "gemm_tflops": round((work["routed_flop"] + work["shared_flop"]) / gemm_s / 1e12, 2),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": {"bound": "mfma", "kernel": "gate/up stage (k_expert_stage up)",
+                     "achieved": round(achieved / 1e12, 2), "peak": peak / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        import synth as _s  # noqa: F401
+        cpu_inp = {k: (v.cpu() if v is not None else None) for k, v in inp.items()}
+        out["cpu_baseline"] = cpu_baseline(wl, cpu_inp, min(args.cpu_sample, wl.T_pool))
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -151,7 +151,21 @@ typedef struct mok_moe_args {
   int32_t* offsets_out;    /* [E_l + 1]                                                     */
   int32_t* rank_counts_out;/* [E_l * R]                                                     */
   int32_t* route_ids_out;  /* [T_pool * min(k, E_l)]                                        */
+  /* optional measurement hook (host array, may be NULL): 2 * MOK_N_STAGES hipEvent_t created
+     by the caller; event 2s is recorded on the stream before stage s's first launch and event
+     2s+1 after its last launch (a stage that launches nothing records both back to back).
+     With the ring work loop both GEMM stages run in one launch, recorded as MOK_STAGE_UP. */
+  void* const* stage_events;
 } mok_moe_args;
+
+/* stages of mok_moe_forward, for stage_events */
+#define MOK_STAGE_ROUTE 0    /* router logits + top-k (router runs only)          */
+#define MOK_STAGE_PLAN 1     /* dispatch plan                                      */
+#define MOK_STAGE_QUANT 2    /* MXFP8 weight quantisation (MXFP8 only)             */
+#define MOK_STAGE_UP 3       /* work list + gather + gate/up GEMM with SwiGLU      */
+#define MOK_STAGE_DOWN 4     /* down GEMM with routing-weight scale                */
+#define MOK_STAGE_COMBINE 5  /* fixed-order combine (full layer only)              */
+#define MOK_N_STAGES 6
 
 /* flags */
 #define MOK_FLAG_NO_RING 1u  /* stage-ordered launches over all routes (ring sized to every

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libmok.so")
 MOK_OK, MOK_EINVAL, MOK_EUNSUPPORTED, MOK_EWORKSPACE, MOK_EHIP = range(5)
 MOK_FP32, MOK_BF16, MOK_MXFP8 = 0, 1, 2
 MOK_FLAG_NO_RING = 1
+MOK_STAGE_ROUTE, MOK_STAGE_PLAN, MOK_STAGE_QUANT, MOK_STAGE_UP, MOK_STAGE_DOWN, MOK_STAGE_COMBINE = range(6)
+MOK_N_STAGES = 6
 
 EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
            "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_moe_workspace_bytes",
@@ -54,6 +56,7 @@ class MoeArgs(ctypes.Structure):
         ("y_slots", _P), ("y_shared", _P), ("y", _P),
         ("logits_out", _P), ("topk_idx_out", _P), ("topk_w_out", _P),
         ("counts_out", _P), ("offsets_out", _P), ("rank_counts_out", _P), ("route_ids_out", _P),
+        ("stage_events", _P),
     ]
 
 

@@ -205,8 +205,13 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   char* ws = (char*)a->workspace;
   auto at = [&](size_t off) { return (void*)(ws + off); };
   const int k = a->k;
+  void* const* ev = a->stage_events;
+  auto record = [&](int i) {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], s);
+  };
 
   // stage 1: routing
+  record(2 * MOK_STAGE_ROUTE);
   const int32_t* idx = a->topk_idx_in;
   const float* w = a->topk_w_in;
   if (a->w_router) {
@@ -223,8 +228,10 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     idx = oidx;
     w = ow;
   }
+  record(2 * MOK_STAGE_ROUTE + 1);
 
   // stage 2: plan
+  record(2 * MOK_STAGE_PLAN);
   int32_t* counts = a->counts_out ? a->counts_out : (int32_t*)at(L.counts);
   int32_t* offsets = a->offsets_out ? a->offsets_out : (int32_t*)at(L.offsets);
   int32_t* route_ids = a->route_ids_out ? a->route_ids_out : (int32_t*)at(L.route_ids);
@@ -234,6 +241,7 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
                                (int32_t*)at(L.blk_base), s);
     if (e != hipSuccess) return MOK_EHIP;
   }
+  record(2 * MOK_STAGE_PLAN + 1);
 
   // stages 3-5
   ExpertPass p = {};
@@ -261,6 +269,7 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.wl = (int32_t*)at(L.wl);
   p.y_slots = a->y_slots;
   p.y_shared = a->y_shared;
+  record(2 * MOK_STAGE_QUANT);
   if (a->dtype == MOK_MXFP8) {
     char* q = ws;
     uint8_t* wg_q = (uint8_t*)(q + L.wg_q); uint8_t* wu_q = (uint8_t*)(q + L.wu_q);
@@ -290,14 +299,17 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     p.wg = a->w_gate; p.wu = a->w_up; p.wd = a->w_down;
     p.sg = a->ws_gate; p.su = a->ws_up; p.sd = a->ws_down;
   }
-  if (launch_expert_stages(p, s) != hipSuccess) return MOK_EHIP;
+  record(2 * MOK_STAGE_QUANT + 1);
+  if (launch_expert_stages(p, s, ev) != hipSuccess) return MOK_EHIP;
 
   // combine (full layer only)
+  record(2 * MOK_STAGE_COMBINE);
   if (a->E_l == a->E) {
     if (launch_combine(a->y_shared, a->y_slots, a->y, a->T_pool, k, a->d, p.out_f32, s) !=
         hipSuccess)
       return MOK_EHIP;
   }
+  record(2 * MOK_STAGE_COMBINE + 1);
   return MOK_OK;
 }
 

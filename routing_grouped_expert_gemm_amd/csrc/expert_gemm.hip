@@ -161,6 +161,19 @@ struct Smem {
 
 MOK_DEV int swz(int r, int c) { return c ^ (r & 7); }
 
+// 16-byte chunk (of a 128 B LDS row) that lane half h feeds to the MFMA of K sub-step s.
+//  bf16 32x32x16: one chunk, k = 16s + 8h + [0, 8).
+//  fp32 32x32x2 (x8): two chunks, k = 16s + 8h + [0, 8).
+//  fp8 32x32x64 (scaled): bytes 0-15 of a lane belong to the MFMA's first 32-wide K block and
+//  bytes 16-31 to the second, each lane half taking 16 of a block's 32 k; the E8M0 scale of
+//  lane l covers (row l % 32, block l / 32). So: chunks 4s + h and 4s + 2 + h.
+template <Elem EL>
+MOK_DEV int frag_chunk(int s, int h, int q) {
+  if (EL == Elem::BF16) return 2 * s + h;
+  if (EL == Elem::F32) return 4 * s + 2 * h + q;
+  return 4 * s + 2 * q + h;
+}
+
 template <Elem EL>
 MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const uint32_t* asc,
                        const uint32_t* bsc, f32x16_t (&acc)[FM][FN]);
@@ -379,17 +392,15 @@ MOK_DEV void run_tile(const ExpertPass& p, Smem& sm, int m, int local) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WM + i * 32 + l32;
-        const int c = TR::CPL == 1 ? 2 * s + h : 4 * s + 2 * h;
-        fa[i][0] = sm.A[cur][r][swz(r, c)];
-        if (TR::CPL == 2) fa[i][1] = sm.A[cur][r][swz(r, c + 1)];
+        fa[i][0] = sm.A[cur][r][swz(r, frag_chunk<EL>(s, h, 0))];
+        if (TR::CPL == 2) fa[i][1] = sm.A[cur][r][swz(r, frag_chunk<EL>(s, h, 1))];
         if (EL == Elem::FP8) asc[i] = (sm.Asc[cur][r] >> (8 * (2 * s + h))) & 0xFFu;
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = wn * WN + j * 32 + l32;
-        const int c = TR::CPL == 1 ? 2 * s + h : 4 * s + 2 * h;
-        fb[j][0] = sm.B[cur][r][swz(r, c)];
-        if (TR::CPL == 2) fb[j][1] = sm.B[cur][r][swz(r, c + 1)];
+        fb[j][0] = sm.B[cur][r][swz(r, frag_chunk<EL>(s, h, 0))];
+        if (TR::CPL == 2) fb[j][1] = sm.B[cur][r][swz(r, frag_chunk<EL>(s, h, 1))];
         if (EL == Elem::FP8) bsc[j] = (sm.Bsc[cur][r] >> (8 * (2 * s + h))) & 0xFFu;
       }
       mfma_step<EL>(fa, fb, asc, bsc, acc);
@@ -545,23 +556,31 @@ hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, in
 }
 
 // ------------------------------------------------------------------------- launch
+static void record(void* const* ev, int i, hipStream_t s) {
+  if (ev) (void)hipEventRecord((hipEvent_t)ev[i], s);
+}
+
 template <Elem EL, bool F32OUT>
-static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s) {
+static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
   hipLaunchKernelGGL((k_expert_stage<EL, true, F32OUT>), dim3(p.grid), dim3(NT), 0, s, p);
+  record(ev, 2 * 3 + 1, s);
+  record(ev, 2 * 4, s);
   hipLaunchKernelGGL((k_expert_stage<EL, false, F32OUT>), dim3(p.grid), dim3(NT), 0, s, p);
+  record(ev, 2 * 4 + 1, s);
   return hipGetLastError();
 }
 
-hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s) {
+hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev) {
   const int nU_r = p.I / (BN / 2);
   const int nU_s = p.I_sh / (BN / 2);
   const int nD = p.d / BN;
+  record(ev, 2 * 3, s);
   hipLaunchKernelGGL(k_build_worklist, dim3(1), dim3(1024), 0, s, p.counts, p.offsets, p.E_l,
                      p.T_own, p.mb, BM, nU_r, nU_s, nD, p.max_mb, p.wl);
-  if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s);
-  if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s);
+  if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
+  if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);
-  return launch_stages_t<Elem::FP8, false>(p, s);
+  return launch_stages_t<Elem::FP8, false>(p, s, ev);
 }
 
 }  // namespace mok

@@ -60,7 +60,9 @@ struct ExpertPass {
 };
 
 size_t worklist_ints(int max_mb);
-hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s);
+// ev: optional hipEvent_t[2 * 6] (mok stage events); records UP around the work list, gather
+// and up stage, DOWN around the down stage.
+hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev);
 hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, int64_t n_tok,
                           int k, int d, bool f32, hipStream_t s);
 

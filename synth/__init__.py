@@ -243,11 +243,15 @@ def shared_weights(w: Workload, device="cpu"):
 def zipf_bias(w: Workload) -> torch.Tensor:
     """Per-expert logit bias beta * (-s * ln rank_e), float32 [E]; zero when beta == 0.
 
-    Local experts 0..3 of rank 0 take Zipf ranks 1, 16, 128 and E; the other experts take the
-    remaining ranks in a seeded order."""
+    Experts 0..3 (the local experts of rank 0) take Zipf ranks 1, E/24, E/3 and E (1, 16, 128
+    and 384 for E = 384); the other experts take the remaining ranks in a seeded order."""
     if w.zipf_beta == 0.0:
         return torch.zeros(w.E, dtype=torch.float32)
-    fixed = [1, 16, 128, w.E][:min(4, w.E_l)]
+    fixed = []
+    for r in (1, max(2, w.E // 24), max(3, w.E // 3), w.E):
+        if r <= w.E and r not in fixed:
+            fixed.append(r)
+    fixed = fixed[:min(4, w.E)]
     rest = [r for r in range(1, w.E + 1) if r not in fixed]
     perm = seeded_permutation(SEED, S_PERM, len(rest)).tolist()
     ranks = fixed + [rest[p] for p in perm]

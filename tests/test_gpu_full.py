@@ -1,0 +1,149 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+Routing, plan and per-(expert, rank) counts are compared in full and bit-exactly; the layer's
+floating-point outputs on sampled rows that the oracle computes one by one (float64). Inputs
+are generated on the GPU by the seeded generator; the oracle gets the same tensors (the
+generator gives the same bits on every device, checked in test_gpu_parity)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _layer import TOL, gpu_layer, gpu_topk, make_inputs, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _cpu(inp):
+    return {k: (v.cpu() if v is not None else None) for k, v in inp.items()}
+
+
+def _sample(rng, n, size):
+    return np.sort(rng.choice(n, size=min(n, size), replace=False))
+
+
+def _check_plan(layer, ref_plan):
+    for key in ("counts", "offsets", "rank_counts"):
+        assert np.array_equal(to_np(layer.inter[key]).reshape(ref_plan[key].shape), ref_plan[key]), key
+    n = ref_plan["n"]
+    assert np.array_equal(to_np(layer.inter["route_ids"])[:n], ref_plan["route_ids"])
+
+
+def _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng, n_routes=96, n_own=24):
+    mx = wl.dtype == "mxfp8"
+    tol = TOL[wl.dtype]
+    rids = plan["route_ids"].astype(np.int64)
+    pick = rids[_sample(rng, len(rids), n_routes)]
+    ref = oracle.route_outputs(pick, cpu["x"][torch.from_numpy(pick // wl.k)], idx, w, wl.e0,
+                               cpu["wg"], cpu["wu"], cpu["wd"], mx)
+    got = to_np(layer.y_slots[torch.from_numpy(pick).to(DEV)])
+    err_p = rel_err(got, ref)
+    assert err_p <= tol, err_p
+    own = _sample(rng, wl.T_own, n_own)
+    a = oracle._operand(cpu["x"][torch.from_numpy(wl.own_begin + own)], mx)
+    S = oracle.shared_ffn(a, oracle._operand(cpu["sg"], mx), oracle._operand(cpu["su"], mx),
+                          oracle._operand(cpu["sd"], mx), mx)
+    err_s = rel_err(to_np(layer.y_shared[torch.from_numpy(own).to(DEV)]), S)
+    assert err_s <= tol, err_s
+    return err_p, err_s
+
+
+def test_ep1_full_layer_bf16():
+    """T=8192, d=2048, 64 experts top-6, I=1408, 2 shared experts: the whole layer."""
+    import routing_grouped_expert_gemm_amd as mok
+    wl = synth.WORKLOADS[synth.EP1]
+    inp = make_inputs(wl, DEV)
+    layer = gpu_layer(wl, inp, flags=mok.MOK_FLAG_NO_RING)
+    layer.forward()
+    torch.cuda.synchronize()
+    cpu = _cpu(inp)
+    logits = oracle.router_logits(cpu["x"], cpu["w_router"])
+    assert np.array_equal(to_np(layer.inter["logits"]), logits)
+    idx, w = oracle.topk(logits, wl.k)
+    assert np.array_equal(to_np(layer.inter["topk_idx"]), idx)
+    np.testing.assert_allclose(to_np(layer.inter["topk_w"]), w, rtol=2e-6, atol=1e-7)
+    plan = oracle.dispatch_plan(idx, 0, wl.E, wl.tokens_per_rank)
+    _check_plan(layer, plan)
+    mean = wl.T_pool * wl.k / wl.E
+    assert plan["counts"].min() >= 0.8 * mean and plan["counts"].max() <= 1.2 * mean
+    rng = np.random.default_rng(11)
+    _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng)
+    # combined output on sampled tokens: S + sum_j P, float64
+    toks = _sample(rng, wl.T_pool, 24)
+    xf = oracle._f32(cpu["x"][torch.from_numpy(toks)])
+    ref = oracle.shared_ffn(xf, oracle._f32(cpu["sg"]), oracle._f32(cpu["su"]), oracle._f32(cpu["sd"]))
+    for j in range(wl.k):
+        ref += oracle.route_outputs(toks * wl.k + j, cpu["x"][torch.from_numpy(toks)], idx, w, 0,
+                                    cpu["wg"], cpu["wu"], cpu["wd"])
+    assert rel_err(to_np(layer.y[torch.from_numpy(toks).to(DEV)]), ref) <= TOL["bf16"]
+    # reruns are bit-identical
+    y0 = layer.y.clone()
+    for _ in range(2):
+        layer.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(layer.y.view(torch.int16), y0.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", [synth.EP64, synth.EP64_MX, synth.EP96])
+def test_share_workloads(name):
+    """One rank's share: pool of 64 x 4096 (or 96 x 2048) tokens, d=7168, 4 local experts."""
+    import routing_grouped_expert_gemm_amd as mok
+    wl = synth.WORKLOADS[name]
+    inp = make_inputs(wl, DEV)
+    idx_g, w_g = gpu_topk(inp["logits"], wl.k)
+    cpu = _cpu(inp)
+    idx, w = oracle.topk(cpu["logits"], wl.k)
+    assert np.array_equal(to_np(idx_g), idx)
+    np.testing.assert_allclose(to_np(w_g), w, rtol=2e-6, atol=1e-7)
+    del cpu["logits"]
+    layer = gpu_layer(wl, inp, topk=(idx_g, w_g), flags=mok.MOK_FLAG_NO_RING)
+    layer.forward()
+    torch.cuda.synchronize()
+    assert layer.device_error() == 0
+    plan = oracle.dispatch_plan(idx, wl.e0, wl.E_l, wl.tokens_per_rank)
+    _check_plan(layer, plan)
+    if name == synth.EP96:
+        assert plan["counts"].tolist() == [16382, 7934, 4008, 2696]   # calibrated Zipf load
+    rng = np.random.default_rng(12)
+    _check_sampled_outputs(wl, layer, cpu, idx, to_np(w_g), plan, rng)
+    if wl.dtype == "mxfp8":
+        # the on-device quantiser (the same device code the forward uses) on real operands
+        for t in (inp["wg"][0, :64], inp["wd"][1, :64], inp["x"][:64]):
+            codes = torch.empty(t.shape, dtype=torch.uint8, device=DEV)
+            sc = torch.empty((t.shape[0], t.shape[1] // 32), dtype=torch.uint8, device=DEV)
+            mok.mok_quantize_mxfp8(t.contiguous(), codes, sc)
+            torch.cuda.synchronize()
+            rc, rs = oracle.mxfp8_quantize(t.cpu())
+            assert np.array_equal(to_np(codes), rc) and np.array_equal(to_np(sc), rs)
+    # rerun bit-identical at the sampled rows
+    rids = torch.from_numpy(plan["route_ids"][:: max(1, plan["n"] // 512)].astype(np.int64)).to(DEV)
+    before = layer.y_slots[rids].clone()
+    s_before = layer.y_shared.clone()
+    layer.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(layer.y_slots[rids].view(torch.int16), before.view(torch.int16))
+    assert torch.equal(layer.y_shared.view(torch.int16), s_before.view(torch.int16))
+
+
+def test_zipf_share_minibatch_sweep_bit_identical():
+    """The skewed share at minibatch sizes 128..1024 gives the same bits."""
+    import routing_grouped_expert_gemm_amd as mok
+    wl = synth.WORKLOADS[synth.EP96]
+    inp = make_inputs(wl, DEV)
+    topk = gpu_topk(inp["logits"], wl.k)
+    ref = None
+    for mb in (128, 256, 512, 1024):
+        layer = gpu_layer(wl, inp, topk=topk, mb=mb, flags=mok.MOK_FLAG_NO_RING)
+        layer.forward()
+        torch.cuda.synchronize()
+        n = int(layer.inter["offsets"][-1])
+        rid = layer.inter["route_ids"][:n].long()
+        out = (layer.y_slots[rid].clone(), layer.y_shared.clone())
+        if ref is None:
+            ref = out
+        else:
+            assert torch.equal(out[0].view(torch.int16), ref[0].view(torch.int16))
+            assert torch.equal(out[1].view(torch.int16), ref[1].view(torch.int16))
+        del layer
