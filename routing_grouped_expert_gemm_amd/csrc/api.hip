@@ -53,6 +53,11 @@ int validate_moe(const mok_moe_args* a) {
   if (a->I <= 0 || a->e0 < 0 || a->E_l < 1 || a->e0 + a->E_l > a->E) return MOK_EINVAL;
   if (a->T_pool < 0 || a->tokens_per_rank < 1 || a->T_pool % a->tokens_per_rank) return MOK_EINVAL;
   if (a->T_pool * (int64_t)a->k >= (int64_t)1 << 31) return MOK_EINVAL;
+  // the GEMMs address pool rows with 32-bit byte offsets from the pool base
+  const int64_t x_es = a->dtype == MOK_FP32 ? 4 : 2;
+  if (a->T_pool * (int64_t)a->d * x_es >= (int64_t)1 << 32) return MOK_EUNSUPPORTED;
+  if ((int64_t)std::max(a->I, a->n_shared * a->I_shared) * a->d * x_es >= (int64_t)1 << 32)
+    return MOK_EUNSUPPORTED;
   if (a->own_begin < 0 || a->T_own < 0 || a->own_begin + a->T_own > a->T_pool) return MOK_EINVAL;
   if (a->n_shared < 0) return MOK_EINVAL;
   const int mb = a->minibatch_rows;
@@ -259,7 +264,7 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.n_slots = L.n_slots;
   p.Hld = L.Hld;
   p.max_mb = L.max_mb;
-  p.grid = ((device_cus() * 2 + 7) / 8) * 8;
+  p.grid = ((device_cus() + 7) / 8) * 8;   // one 256 x 256 tile workgroup per CU
   p.x = a->x;
   p.route_ids = route_ids;
   p.topk_w = w;

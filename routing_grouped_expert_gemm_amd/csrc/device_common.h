@@ -33,6 +33,16 @@ template <> MOK_DEV bf16_t f32_to<bf16_t>(float v) { return f32_to_bf16(v); }
 
 MOK_DEV int lane_id() { return __lane_id(); }
 
+// Values every lane of the wave holds identically, moved to scalar registers.
+MOK_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+MOK_DEV T* uniform_ptr(T* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
 MOK_DEV uint64_t ballot(bool p) { return __ballot(p); }
 
 MOK_DEV uint64_t lanemask_lt() {

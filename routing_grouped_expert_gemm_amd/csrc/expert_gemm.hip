@@ -139,27 +139,49 @@ MOK_DEV int find_mb(const int32_t* start, int n_mb, int32_t t) {
 }
 
 // ------------------------------------------------------------------------- GEMM tiles
-constexpr int BM = 128, BN = 128, NT = 256;
-constexpr int WAVES_M = 2, WAVES_N = 2, WM = BM / WAVES_M, WN = BN / WAVES_N;
-constexpr int FM = WM / 32, FN = WN / 32;
-constexpr int ROWS_PER_PASS = NT / 8;               // 32 rows per pass of 8 x 16 B chunks
-constexpr int A_PASSES = BM / ROWS_PER_PASS, B_PASSES = BN / ROWS_PER_PASS;
+// Tile geometry. A workgroup of WAVES_M x WAVES_N waves computes a BM x BN block of the
+// stage's product; each wave a WM x WN block of 32 x 32 MFMA accumulators (FM x FN).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  // operand tiles are filled by LDS-DMA slabs of 8 rows x 128 B (one per wave instruction)
+  static constexpr int A_SLABS = BM / 8 / NW, B_SLABS = BN / 8 / NW;
+  static_assert(FN % 2 == 0, "gate/up pairing needs an even number of N blocks per wave");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole slabs per wave");
+  static_assert(BM == 64 * NW && BN == 64 * NW, "one 4-byte scale per lane per tile row");
+};
+// 256 x 256 tiles, 4 waves of 128 x 128 (16 accumulator blocks = 256 AGPRs per lane), one
+// workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs, so LDS reads stay near
+// 64 B/clk per CU while the MFMA pipes are busy.
+typedef Cfg<256, 256, 2, 2> Big;
 
 template <Elem EL> struct Tr;
 template <> struct Tr<Elem::BF16> { static constexpr int ES = 2, KT = 64, SUB = 4, CPL = 1; };
 template <> struct Tr<Elem::F32> { static constexpr int ES = 4, KT = 32, SUB = 2, CPL = 2; };
 template <> struct Tr<Elem::FP8> { static constexpr int ES = 1, KT = 128, SUB = 2, CPL = 2; };
 
-struct Smem {
-  uint4 A[2][BM][8];
-  uint4 B[2][BN][8];
-  uint32_t Asc[2][BM];
-  uint32_t Bsc[2][BN];
-  int32_t row_dst[BM];
-  float row_w[BM];
+// LDS: two buffers of the A and B tiles (128 B per row per K step), their MX scale words,
+// and the down stage's row table. Chunk c of row r sits at chunk c ^ (r & 7) of the row. The
+// buffers are separate LDS objects so the compiler can tell that reading one does not wait on
+// LDS-DMA still writing the other.
+template <class C>
+struct Bufs {
+  uint4 (*A)[8];
+  uint4 (*B)[8];
+  uint32_t* As;
+  uint32_t* Bs;
+};
+template <class C>
+struct Lds {
+  Bufs<C> buf[2];
+  int32_t* row_dst;
+  float* row_w;
 };
 
-MOK_DEV int swz(int r, int c) { return c ^ (r & 7); }
+typedef __attribute__((address_space(3))) void lds_void;
 
 // 16-byte chunk (of a 128 B LDS row) that lane half h feeds to the MFMA of K sub-step s.
 //  bf16 32x32x16: one chunk, k = 16s + 8h + [0, 8).
@@ -168,61 +190,48 @@ MOK_DEV int swz(int r, int c) { return c ^ (r & 7); }
 //  bytes 16-31 to the second, each lane half taking 16 of a block's 32 k; the E8M0 scale of
 //  lane l covers (row l % 32, block l / 32). So: chunks 4s + h and 4s + 2 + h.
 template <Elem EL>
-MOK_DEV int frag_chunk(int s, int h, int q) {
-  if (EL == Elem::BF16) return 2 * s + h;
-  if (EL == Elem::F32) return 4 * s + 2 * h + q;
-  return 4 * s + 2 * q + h;
+MOK_DEV constexpr int frag_chunk(int s, int h, int q) {
+  return EL == Elem::BF16 ? 2 * s + h : (EL == Elem::F32 ? 4 * s + 2 * h + q : 4 * s + 2 * q + h);
 }
 
-template <Elem EL>
+template <Elem EL, int FM, int FN>
 MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const uint32_t* asc,
-                       const uint32_t* bsc, f32x16_t (&acc)[FM][FN]);
-
-template <>
-MOK_DEV void mfma_step<Elem::BF16>(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2],
-                                   const uint32_t*, const uint32_t*, f32x16_t (&acc)[FM][FN]) {
+                       const uint32_t* bsc, f32x16_t (&acc)[FM][FN]) {
+  if constexpr (EL == Elem::BF16) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8_t, a[i][0]), __builtin_bit_cast(bf16x8_t, b[j][0]), acc[i][j],
-          0, 0, 0);
-}
-
-template <>
-MOK_DEV void mfma_step<Elem::F32>(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2],
-                                  const uint32_t*, const uint32_t*, f32x16_t (&acc)[FM][FN]) {
-  // Lane half h supplies k = 8h + q of a 16-wide K step to the q-th 32x32x2 product; A and B
-  // use the same assignment, so the 8 products cover the step exactly once.
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a[i][0]), __builtin_bit_cast(bf16x8_t, b[j][0]),
+            acc[i][j], 0, 0, 0);
+  } else if constexpr (EL == Elem::F32) {
+    // Lane half h supplies k = 8h + q of a 16-wide K step to the q-th 32x32x2 product; A and
+    // B use the same assignment, so the 8 products cover the step exactly once.
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const float* av = reinterpret_cast<const float*>(&a[i][0]);
-      const float* bv = reinterpret_cast<const float*>(&b[j][0]);
+      for (int j = 0; j < FN; ++j) {
+        const float* av = reinterpret_cast<const float*>(&a[i][0]);
+        const float* bv = reinterpret_cast<const float*>(&b[j][0]);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], bv[q], acc[i][j], 0, 0, 0);
-    }
-}
-
-template <>
-MOK_DEV void mfma_step<Elem::FP8>(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2],
-                                  const uint32_t* asc, const uint32_t* bsc,
-                                  f32x16_t (&acc)[FM][FN]) {
+        for (int q = 0; q < 8; ++q)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], bv[q], acc[i][j], 0, 0, 0);
+      }
+  } else {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      i32x8_t av, bv;
-      av[0] = a[i][0].x; av[1] = a[i][0].y; av[2] = a[i][0].z; av[3] = a[i][0].w;
-      av[4] = a[i][1].x; av[5] = a[i][1].y; av[6] = a[i][1].z; av[7] = a[i][1].w;
-      bv[0] = b[j][0].x; bv[1] = b[j][0].y; bv[2] = b[j][0].z; bv[3] = b[j][0].w;
-      bv[4] = b[j][1].x; bv[5] = b[j][1].y; bv[6] = b[j][1].z; bv[7] = b[j][1].w;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0,
-                                                                   (int)asc[i], 0, (int)bsc[j]);
-    }
+      for (int j = 0; j < FN; ++j) {
+        i32x8_t av, bv;
+        av[0] = a[i][0].x; av[1] = a[i][0].y; av[2] = a[i][0].z; av[3] = a[i][0].w;
+        av[4] = a[i][1].x; av[5] = a[i][1].y; av[6] = a[i][1].z; av[7] = a[i][1].w;
+        bv[0] = b[j][0].x; bv[1] = b[j][0].y; bv[2] = b[j][0].z; bv[3] = b[j][0].w;
+        bv[4] = b[j][1].x; bv[5] = b[j][1].y; bv[6] = b[j][1].z; bv[7] = b[j][1].w;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            av, bv, acc[i][j], 0, 0, 0, (int)asc[i], 0, (int)bsc[j]);
+      }
+  }
 }
 
 // Output element of the epilogues.
@@ -231,15 +240,24 @@ template <> struct Out<true> { typedef float T; };
 template <> struct Out<false> { typedef bf16_t T; };
 
 // One tile of the up (UP = true) or down (UP = false) stage of minibatch m.
-template <Elem EL, bool UP, bool F32OUT>
-MOK_DEV void run_tile(const ExpertPass& p, Smem& sm, int m, int local) {
+//  up:   the minibatch's rows x (gate, up rows of H columns n0 .. n0 + BN/2) -> H
+//  down: the minibatch's H rows x (W_down rows n0 .. n0 + BN) -> output columns
+// Operands reach LDS by LDS-DMA (global_load_lds_dwordx4): wave w fills rows [64w, 64w+64)
+// of each tile, 8 rows per instruction; lane L carries row 8q + L/8 and, because its LDS
+// destination is fixed (slot L % 8 of the row), fetches global chunk (L % 8) ^ (row & 7), so
+// the swizzle costs nothing. Row addresses are a uniform base plus a 32-bit offset.
+// M and N tails: rows/columns past the end are clamped on load, skipped on store.
+template <Elem EL, bool UP, bool F32OUT, class C>
+MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
   typedef Tr<EL> TR;
   typedef typename Out<F32OUT>::T OT;
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+  constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS;
   const int cap = p.max_mb;
   int32_t* wl = p.wl;
-  const int g = wl_group(wl, cap)[m];
-  const int row0 = wl_row0(wl, cap)[m];
-  const int rows = wl_rows(wl, cap)[m];
+  const int g = uniform(wl_group(wl, cap)[m]);
+  const int row0 = uniform(wl_row0(wl, cap)[m]);
+  const int rows = uniform(wl_rows(wl, cap)[m]);
   const bool shared = g >= p.E_l;
   const int slot = m % p.n_slots;
   const int64_t ring_row0 = (int64_t)slot * p.mb;
@@ -247,92 +265,132 @@ MOK_DEV void run_tile(const ExpertPass& p, Smem& sm, int m, int local) {
   const int mt = local % n_mt, nt = local / n_mt;
   const int m0 = mt * BM;
   const int rows_valid = min(BM, rows - m0);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
   const int K = UP ? p.d : (shared ? p.I_sh : p.I);
+  const int N = UP ? (shared ? p.I_sh : p.I) : p.d;   // output columns of the stage
   const int nk = K / TR::KT;
+  const int chunk_b = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;   // global byte of the lane's chunk
 
-  // ---- operand row pointers (each thread loads chunk c of rows (tid>>3) + 32*i)
-  const int ldc = tid & 7;
-  const char* a_ptr[A_PASSES];
-  const char* b_ptr[B_PASSES];
-  const uint8_t* a_sc = nullptr;   // MX scales row pointer (thread < BM: row tid)
-  const uint8_t* b_sc = nullptr;   // MX scales row pointer (thread >= BM: row tid - BM)
-  int64_t b_seg_len = K, b_seg_stride = 0;
+  // ---- A operand: uniform base + per-slab 32-bit row offsets
+  const char* a_base;
+  int64_t a_row_bytes;
+  if (UP && EL != Elem::FP8) {
+    a_base = (const char*)p.x;
+    a_row_bytes = (int64_t)p.d * TR::ES;
+  } else if (UP) {
+    a_base = (const char*)p.A_codes + (ring_row0 + m0) * p.d;
+    a_row_bytes = p.d;
+  } else {
+    a_base = (const char*)p.H + (ring_row0 + m0) * (int64_t)p.Hld * TR::ES;
+    a_row_bytes = (int64_t)p.Hld * TR::ES;
+  }
+  a_base = uniform_ptr(a_base);
+  uint32_t a_off[A_SLABS];
 #pragma unroll
-  for (int i = 0; i < A_PASSES; ++i) {
-    const int r = min((tid >> 3) + ROWS_PER_PASS * i, rows_valid - 1);
-    int64_t base;
-    if (UP && EL != Elem::FP8) {
-      const int64_t tok = shared ? p.own_begin + row0 + m0 + r
-                                 : (int64_t)(p.route_ids[row0 + m0 + r] / p.k);
-      base = tok * p.d * TR::ES;
-      a_ptr[i] = (const char*)p.x + base;
-    } else if (UP) {
-      a_ptr[i] = (const char*)p.A_codes + (ring_row0 + m0 + r) * p.d;
-    } else {
-      a_ptr[i] = (const char*)p.H + (ring_row0 + m0 + r) * (int64_t)p.Hld * TR::ES;
-    }
+  for (int q = 0; q < A_SLABS; ++q) {
+    const int r = min(64 * wid + 8 * q + (lane >> 3), rows_valid - 1);
+    int64_t row;
+    if (UP && EL != Elem::FP8)
+      row = shared ? p.own_begin + row0 + m0 + r : (int64_t)(p.route_ids[row0 + m0 + r] / p.k);
+    else
+      row = r;
+    a_off[q] = (uint32_t)(row * a_row_bytes) + chunk_b;
   }
+  // ---- B operand. Up: wave w loads gate (w even) or up (w odd) rows of H columns
+  // nt*BN/2 + (w/2)*WN/2 + [0, 64); this matches the accumulator pairing of the waves. Down:
+  // W_down rows nt*BN + 64w + [0, 64).
+  const char* b_base;
+  int64_t b_row_bytes, b_seg_len = K, b_seg_stride = 0;
+  int b_n0;
+  if (UP) {
+    const bool uph = (wid & 1) != 0;
+    const void* W = shared ? (uph ? p.su : p.sg) : (uph ? p.wu : p.wg);
+    b_base = (const char*)W + (shared ? 0 : (int64_t)g * p.I * p.d * TR::ES);
+    b_row_bytes = (int64_t)p.d * TR::ES;
+    b_n0 = nt * (BN / 2) + (wid >> 1) * (WN / 2);
+  } else {
+    if (shared) {
+      b_base = (const char*)p.sd;
+      b_row_bytes = (int64_t)p.I_seg * TR::ES;
+      b_seg_len = p.I_seg;
+      b_seg_stride = (int64_t)p.d * p.I_seg * TR::ES;
+    } else {
+      b_base = (const char*)p.wd + (int64_t)g * p.d * p.I * TR::ES;
+      b_row_bytes = (int64_t)p.I * TR::ES;
+    }
+    b_n0 = nt * BN + 64 * wid;
+  }
+  b_base = uniform_ptr(b_base);
+  uint32_t b_off[B_SLABS];
 #pragma unroll
-  for (int i = 0; i < B_PASSES; ++i) {
-    const int j = (tid >> 3) + ROWS_PER_PASS * i;
-    if (UP) {
-      const int jw = j / WN, jj = j % WN;
-      const int n = nt * (BN / 2) + jw * (WN / 2) + (jj % (WN / 2));
-      const bool up = jj >= WN / 2;
-      const void* W = shared ? (up ? p.su : p.sg) : (up ? p.wu : p.wg);
-      const int64_t wrow = shared ? (int64_t)n : (int64_t)g * p.I + n;
-      b_ptr[i] = (const char*)W + wrow * p.d * TR::ES;
-    } else {
-      const int n = nt * BN + j;
-      if (shared) {
-        b_ptr[i] = (const char*)p.sd + (int64_t)n * p.I_seg * TR::ES;
-      } else {
-        b_ptr[i] = (const char*)p.wd + ((int64_t)g * p.d + n) * p.I * TR::ES;
-      }
-    }
+  for (int q = 0; q < B_SLABS; ++q) {
+    const int n = min(b_n0 + 8 * q + (lane >> 3), N - 1);
+    b_off[q] = (uint32_t)(n * b_row_bytes) + chunk_b;
   }
-  if (!UP && shared) {
-    b_seg_len = p.I_seg;
-    b_seg_stride = (int64_t)p.d * p.I_seg * TR::ES;
-  }
+  // ---- MX scales: lane L of wave w carries tile row 64w + L (4 scale bytes per K step)
+  const uint8_t* a_sc_base = nullptr;
+  const uint8_t* b_sc_base = nullptr;
+  uint32_t a_sc_off = 0, b_sc_off = 0;
+  int64_t a_sc_row = 0, b_sc_row = 0;
   if (EL == Elem::FP8) {
-    if (tid < BM) {
-      const int r = min(tid, rows_valid - 1);
-      a_sc = UP ? p.A_sc + (ring_row0 + m0 + r) * (int64_t)(p.d / 32)
-                : p.H_sc + (ring_row0 + m0 + r) * (int64_t)(p.Hld / 32);
+    const int r = min(64 * wid + lane, rows_valid - 1);
+    a_sc_row = UP ? p.d / 32 : p.Hld / 32;
+    a_sc_base = (UP ? p.A_sc : p.H_sc) + (ring_row0 + m0) * a_sc_row;
+    a_sc_off = (uint32_t)(r * a_sc_row);
+    if (UP) {
+      const bool uph = (wid & 1) != 0;
+      const uint8_t* S = shared ? (uph ? p.su_sc : p.sg_sc) : (uph ? p.wu_sc : p.wg_sc);
+      b_sc_row = p.d / 32;
+      b_sc_base = S + (shared ? 0 : (int64_t)g * p.I * b_sc_row);
     } else {
-      const int j = tid - BM;
-      if (UP) {
-        const int jw = j / WN, jj = j % WN;
-        const int n = nt * (BN / 2) + jw * (WN / 2) + (jj % (WN / 2));
-        const bool up = jj >= WN / 2;
-        const uint8_t* S = shared ? (up ? p.su_sc : p.sg_sc) : (up ? p.wu_sc : p.wg_sc);
-        const int64_t wrow = shared ? (int64_t)n : (int64_t)g * p.I + n;
-        b_sc = S + wrow * (p.d / 32);
-      } else {
-        const int n = nt * BN + j;
-        b_sc = shared ? p.sd_sc + (int64_t)n * (p.I_seg / 32)
-                      : p.wd_sc + ((int64_t)g * p.d + n) * (p.I / 32);
-      }
+      b_sc_row = shared ? p.I_seg / 32 : p.I / 32;
+      b_sc_base = shared ? p.sd_sc : p.wd_sc + (int64_t)g * p.d * b_sc_row;
     }
+    const int n = min(b_n0 + lane, N - 1);
+    b_sc_off = (uint32_t)(n * b_sc_row);
+    a_sc_base = uniform_ptr(a_sc_base);
+    b_sc_base = uniform_ptr(b_sc_base);
   }
   // epilogue row table (down stage)
-  if (!UP && tid < BM) {
-    if (tid < rows_valid) {
-      if (shared) {
-        sm.row_dst[tid] = row0 + m0 + tid;
-        sm.row_w[tid] = 1.0f;
-      } else {
-        const int32_t route = p.route_ids[row0 + m0 + tid];
-        sm.row_dst[tid] = route;
-        sm.row_w[tid] = p.topk_w[route];
-      }
+  if (!UP && tid < BM && tid < rows_valid) {
+    if (shared) {
+      sm.row_dst[tid] = row0 + m0 + tid;
+      sm.row_w[tid] = 1.0f;
+    } else {
+      const int32_t route = p.route_ids[row0 + m0 + tid];
+      sm.row_dst[tid] = route;
+      sm.row_w[tid] = p.topk_w[route];
     }
   }
 
-  // ---- main loop
+  // issue the LDS-DMA loads of K step kt into buffer b. The K offset is added to the 32-bit
+  // row offsets (not to the 64-bit base) so each load stays "scalar base + 32-bit offset".
+  auto issue = [&](int kt, const Bufs<C>& b) {
+    const uint32_t k0 = (uint32_t)kt * TR::KT;
+    const uint32_t ka = k0 * TR::ES;
+    const uint32_t seg = k0 / (uint32_t)b_seg_len;
+    const uint32_t kin = k0 - seg * (uint32_t)b_seg_len;
+    const char* b_seg = uniform_ptr(b_base + (int64_t)seg * b_seg_stride);
+    const uint32_t kb = kin * TR::ES;
+#pragma unroll
+    for (int q = 0; q < A_SLABS; ++q)
+      __builtin_amdgcn_global_load_lds(a_base + (uint32_t)(a_off[q] + ka),
+                                       (lds_void*)&b.A[64 * wid + 8 * q][0], 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < B_SLABS; ++q)
+      __builtin_amdgcn_global_load_lds(b_seg + (uint32_t)(b_off[q] + kb),
+                                       (lds_void*)&b.B[64 * wid + 8 * q][0], 16, 0, 0);
+    if (EL == Elem::FP8) {
+      __builtin_amdgcn_global_load_lds(a_sc_base + (uint32_t)(a_sc_off + k0 / 32),
+                                       (lds_void*)&b.As[64 * wid], 4, 0, 0);
+      const uint8_t* bs_seg = uniform_ptr(b_sc_base + (int64_t)seg * (b_seg_stride / 32));
+      __builtin_amdgcn_global_load_lds(bs_seg + (uint32_t)(b_sc_off + kin / 32),
+                                       (lds_void*)&b.Bs[64 * wid], 4, 0, 0);
+    }
+  };
+
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -341,82 +399,71 @@ MOK_DEV void run_tile(const ExpertPass& p, Smem& sm, int m, int local) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  uint4 ra[A_PASSES], rb[B_PASSES];
-  uint32_t rsc = 0;
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * TR::KT;
-    const int64_t aoff = k0 * TR::ES + ldc * 16;
-    const int64_t seg = k0 / b_seg_len;
-    const int64_t boff = seg * b_seg_stride + (k0 - seg * b_seg_len) * TR::ES + ldc * 16;
-#pragma unroll
-    for (int i = 0; i < A_PASSES; ++i) ra[i] = *(const uint4*)(a_ptr[i] + aoff);
-#pragma unroll
-    for (int i = 0; i < B_PASSES; ++i) rb[i] = *(const uint4*)(b_ptr[i] + boff);
-    if (EL == Elem::FP8) {
-      const int64_t kb = k0 / 32;
-      if (tid < BM) rsc = *(const uint32_t*)(a_sc + kb);
-      else {
-        const int64_t kbs = (k0 - seg * b_seg_len) / 32;
-        rsc = *(const uint32_t*)(b_sc + kbs + (seg * b_seg_stride) / 32);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PASSES; ++i) {
-      const int r = (tid >> 3) + ROWS_PER_PASS * i;
-      sm.A[buf][r][swz(r, ldc)] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PASSES; ++i) {
-      const int r = (tid >> 3) + ROWS_PER_PASS * i;
-      sm.B[buf][r][swz(r, ldc)] = rb[i];
-    }
-    if (EL == Elem::FP8) {
-      if (tid < BM) sm.Asc[buf][tid] = rsc;
-      else sm.Bsc[buf][tid - BM] = rsc;
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int h = lane >> 5, l32 = lane & 31;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int s = 0; s < TR::SUB; ++s) {
-      uint4 fa[FM][2], fb[FN][2];
-      uint32_t asc[FM], bsc[FN];
+  const int h = lane >> 5, l32 = lane & 31, x7 = lane & 7;
+  // MFMAs of one K step from buffer b. Fragments are double-buffered across the K sub-steps:
+  // the reads of sub-step s + 1 are issued before the MFMAs of s, and a scheduling barrier
+  // keeps the compiler from hoisting further reads (which would only add live registers).
+  auto compute = [&](const Bufs<C>& b) {
+    const char* a_buf = (const char*)&b.A[wm * WM + l32][0];
+    const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
+    uint4 fa[2][FM][2], fb[2][FN][2];
+    uint32_t asc[2][FM], bsc[2][FN];
+    auto load = [&](int s, int f) {
+      const int c0 = ((frag_chunk<EL>(s, h, 0)) ^ x7) * 16;
+      const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ x7) * 16;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int r = wm * WM + i * 32 + l32;
-        fa[i][0] = sm.A[cur][r][swz(r, frag_chunk<EL>(s, h, 0))];
-        if (TR::CPL == 2) fa[i][1] = sm.A[cur][r][swz(r, frag_chunk<EL>(s, h, 1))];
-        if (EL == Elem::FP8) asc[i] = (sm.Asc[cur][r] >> (8 * (2 * s + h))) & 0xFFu;
+        fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * 128 + c0);
+        if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * 128 + c1);
+        if (EL == Elem::FP8)
+          asc[f][i] = (b.As[wm * WM + i * 32 + l32] >> (8 * (2 * s + h))) & 0xFFu;
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int r = wn * WN + j * 32 + l32;
-        fb[j][0] = sm.B[cur][r][swz(r, frag_chunk<EL>(s, h, 0))];
-        if (TR::CPL == 2) fb[j][1] = sm.B[cur][r][swz(r, frag_chunk<EL>(s, h, 1))];
-        if (EL == Elem::FP8) bsc[j] = (sm.Bsc[cur][r] >> (8 * (2 * s + h))) & 0xFFu;
+        fb[f][j][0] = *(const uint4*)(b_buf + j * 32 * 128 + c0);
+        if (TR::CPL == 2) fb[f][j][1] = *(const uint4*)(b_buf + j * 32 * 128 + c1);
+        if (EL == Elem::FP8)
+          bsc[f][j] = (b.Bs[wn * WN + j * 32 + l32] >> (8 * (2 * s + h))) & 0xFFu;
       }
-      mfma_step<EL>(fa, fb, asc, bsc, acc);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int s = 0; s < TR::SUB; ++s) {
+      if (s + 1 < TR::SUB) load(s + 1, (s + 1) & 1);
+      mfma_step<EL, FM, FN>(fa[s & 1], fb[s & 1], asc[s & 1], bsc[s & 1], acc);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+  };
+
+  // K loop, unrolled by two so each buffer's role is static: wait for step kt's DMA (own
+  // wave), barrier (every wave's DMA landed, every wave done with kt - 1), issue kt + 1 into
+  // the other buffer, compute kt.
+  issue(0, sm.buf[0]);
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    issue(kt + 1, sm.buf[1]);
+    compute(sm.buf[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 2 < nk) issue(kt + 2, sm.buf[0]);
+    compute(sm.buf[1]);
+  }
+  if (kt < nk) {  // odd number of K steps: the last one is in buffer 0
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    compute(sm.buf[0]);
   }
 
   // ---- epilogue. Accumulator v of block (i, j) is (row 8*(v/4) + 4*h + v%4, col l32).
   if (UP) {
-    const int64_t col0 = (int64_t)nt * (BN / 2) + wn * (WN / 2);
+    const int col0 = nt * (BN / 2) + wn * (WN / 2);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN / 2; ++j) {
-        const int64_t col = col0 + j * 32 + l32;
+        const int col = col0 + j * 32 + l32;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -427,30 +474,30 @@ MOK_DEV void run_tile(const ExpertPass& p, Smem& sm, int m, int local) {
 #pragma unroll
             for (int msk = 1; msk < 32; msk <<= 1) amax = fmaxf(amax, __shfl_xor(amax, msk, kWave));
             const int se = mx_shared_exp(amax);
-            if (r < rows_valid) {
+            if (r < rows_valid && col < N) {
               const int64_t hr = ring_row0 + m0 + r;
               ((uint8_t*)p.H)[hr * p.Hld + col] = (uint8_t)e4m3_encode(hv, se);
               if (l32 == 0) p.H_sc[hr * (p.Hld / 32) + col / 32] = (uint8_t)(se + 127);
             }
-          } else if (r < rows_valid) {
+          } else if (r < rows_valid && col < N) {
             const int64_t hr = ring_row0 + m0 + r;
             ((OT*)p.H)[hr * p.Hld + col] = f32_to<OT>(hv);
           }
         }
       }
   } else {
-    const int64_t col0 = (int64_t)nt * BN + wn * WN;
+    const int col0 = nt * BN + wn * WN;
+    OT* out = shared ? (OT*)p.y_shared : (OT*)p.y_slots;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int64_t col = col0 + j * 32 + l32;
+        const int col = col0 + j * 32 + l32;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (r < rows_valid) {
+          if (r < rows_valid && col < N) {
             const int64_t dst = sm.row_dst[r];
-            OT* out = shared ? (OT*)p.y_shared : (OT*)p.y_slots;
             out[dst * p.d + col] = f32_to<OT>(acc[i][j][v] * sm.row_w[r]);
           }
         }
@@ -462,9 +509,13 @@ MOK_DEV void run_tile(const ExpertPass& p, Smem& sm, int m, int local) {
 // Stage kernel: the workgroups walk the stage's tiles; consecutive tile ids land on the same
 // XCD (workgroups are dispatched round-robin over the 8 XCDs), so tiles that share operand
 // rows share that XCD's L2.
-template <Elem EL, bool UP, bool F32OUT>
-__global__ __launch_bounds__(NT, 2) void k_expert_stage(ExpertPass p) {
-  __shared__ Smem sm;
+template <Elem EL, bool UP, bool F32OUT, class C>
+__global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
+  __shared__ uint4 a0[C::BM][8], a1[C::BM][8], b0[C::BN][8], b1[C::BN][8];
+  __shared__ uint32_t as0[C::BM], as1[C::BM], bs0[C::BN], bs1[C::BN];
+  __shared__ int32_t row_dst[C::BM];
+  __shared__ float row_w[C::BM];
+  const Lds<C> sm = {{{a0, b0, as0, bs0}, {a1, b1, as1, bs1}}, row_dst, row_w};
   const int cap = p.max_mb;
   const int n_mb = p.wl[WL_N_MB];
   const int32_t total = p.wl[UP ? WL_N_U : WL_N_D];
@@ -475,8 +526,8 @@ __global__ __launch_bounds__(NT, 2) void k_expert_stage(ExpertPass p) {
   for (int32_t t0 = 0; t0 < total; t0 += G) {
     const int32_t t = t0 + xcd_slot;
     if (t >= total) break;
-    const int m = find_mb(start, n_mb, t);
-    run_tile<EL, UP, F32OUT>(p, sm, m, t - start[m]);
+    const int m = uniform(find_mb(start, n_mb, t));
+    run_tile<EL, UP, F32OUT, C>(p, sm, m, uniform(t - start[m]));
   }
 }
 
@@ -562,21 +613,21 @@ static void record(void* const* ev, int i, hipStream_t s) {
 
 template <Elem EL, bool F32OUT>
 static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
-  hipLaunchKernelGGL((k_expert_stage<EL, true, F32OUT>), dim3(p.grid), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((k_expert_stage<EL, true, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
   record(ev, 2 * 3 + 1, s);
   record(ev, 2 * 4, s);
-  hipLaunchKernelGGL((k_expert_stage<EL, false, F32OUT>), dim3(p.grid), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((k_expert_stage<EL, false, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
   record(ev, 2 * 4 + 1, s);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev) {
-  const int nU_r = p.I / (BN / 2);
-  const int nU_s = p.I_sh / (BN / 2);
-  const int nD = p.d / BN;
+  const int nU_r = (p.I + Big::BN / 2 - 1) / (Big::BN / 2);
+  const int nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
+  const int nD = (p.d + Big::BN - 1) / Big::BN;
   record(ev, 2 * 3, s);
   hipLaunchKernelGGL(k_build_worklist, dim3(1), dim3(1024), 0, s, p.counts, p.offsets, p.E_l,
-                     p.T_own, p.mb, BM, nU_r, nU_s, nD, p.max_mb, p.wl);
+                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, p.max_mb, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);
