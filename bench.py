@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--minibatch", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (calibrates the HBM "
+                         "byte counters of a profiler run) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
@@ -105,6 +108,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+        return
 
     import routing_grouped_expert_gemm_amd as mok
     import synth

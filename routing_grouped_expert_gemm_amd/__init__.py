@@ -14,7 +14,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmok.so")
+# MOK_LIBRARY: path of another build of libmok.so to load instead of the in-tree one
+LIB_PATH = os.environ.get("MOK_LIBRARY") or os.path.join(_PKG, "libmok.so")
 
 MOK_OK, MOK_EINVAL, MOK_EUNSUPPORTED, MOK_EWORKSPACE, MOK_EHIP = range(5)
 MOK_FP32, MOK_BF16, MOK_MXFP8 = 0, 1, 2

@@ -18,6 +18,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed-fp32 VALU forms stay off (see the package notes)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # keep private arrays in registers: the GEMM kernels leave LDS spare (one workgroup
+         # per CU), which the backend would otherwise fill with promoted arrays
+         "-mllvm", "-disable-promote-alloca-to-lds=true",
          "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 

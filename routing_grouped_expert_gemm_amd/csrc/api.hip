@@ -5,7 +5,7 @@
 #include <algorithm>
 #include <mutex>
 
-#include "../../include/mok.h"
+#include "mok.h"
 #include "launch.h"
 
 using namespace mok;
@@ -34,7 +34,7 @@ int device_cus() {
 // can be found from the workspace pointer alone.
 struct Layout {
   bool use_ring = false;
-  int n_slots = 0, max_mb = 0, Hld = 0;
+  int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0;
   size_t wl = 0, logits = 0, idx = 0, w = 0, counts = 0, offsets = 0, rank_counts = 0,
          route_ids = 0, blk_counts = 0, blk_base = 0, H = 0, H_sc = 0, A_codes = 0, A_sc = 0,
          wq = 0, total = 0;
@@ -64,6 +64,7 @@ int validate_moe(const mok_moe_args* a) {
   if (mb != 128 && mb != 256 && mb != 512 && mb != 1024) return MOK_EINVAL;
   if (a->ring_rows < mb || a->ring_rows % mb) return MOK_EINVAL;
   // tile divisibility: K steps of 128 bytes, down tiles of 128 columns, up tiles of 64 columns
+  // K steps of 128 bytes per row (fp32 32, bf16 64, fp8 128 elements)
   const int kstep = a->dtype == MOK_FP32 ? 32 : (a->dtype == MOK_BF16 ? 64 : 128);
   if (a->d % 128 || a->d % kstep || a->I % 64 || a->I % kstep) return MOK_EINVAL;
   if (a->n_shared > 0) {
@@ -98,7 +99,8 @@ Layout layout_moe(const mok_moe_args* a) {
   const size_t es = a->dtype == MOK_FP32 ? 4 : 2;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-  L.wl = take(sizeof(int32_t) * worklist_ints(L.max_mb));
+  gemm_tile_caps(L.max_mb, mb, a->I, I_sh, a->d, &L.cap_u, &L.cap_d);
+  L.wl = take(sizeof(int32_t) * worklist_ints(L.max_mb, L.cap_u, L.cap_d));
   const bool route = a->w_router != nullptr;
   L.logits = (route && !a->logits_out) ? take(sizeof(float) * a->T_pool * a->E) : 0;
   L.idx = (route && !a->topk_idx_out) ? take(sizeof(int32_t) * a->T_pool * a->k) : 0;
@@ -264,6 +266,8 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.n_slots = L.n_slots;
   p.Hld = L.Hld;
   p.max_mb = L.max_mb;
+  p.cap_u = L.cap_u;
+  p.cap_d = L.cap_d;
   p.grid = ((device_cus() + 7) / 8) * 8;   // one 256 x 256 tile workgroup per CU
   p.x = a->x;
   p.route_ids = route_ids;

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #define MOK_DEV __device__ __forceinline__
+#define MOK_HOSTDEV __host__ __device__ __forceinline__
 
 typedef uint16_t bf16_t;  // bf16 bit pattern
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -15,13 +16,8 @@ constexpr int kWave = 64;
 
 MOK_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
-// float32 -> bf16, round to nearest even (NaN stays NaN).
-MOK_DEV bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// float32 -> bf16, round to nearest even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32.
+MOK_DEV bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <class T> MOK_DEV float load_as_f32(const T* p);
 template <> MOK_DEV float load_as_f32<float>(const float* p) { return *p; }
@@ -57,7 +53,8 @@ MOK_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-MOK_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware exp2 and reciprocal (~1 ulp each)
+MOK_DEV float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ----------------------------------------------------------------------- MXFP8 (OCP MX)
 // Shared exponent of a block from its absolute maximum: floor(log2(amax)) - 8, clamped to

@@ -22,21 +22,31 @@
 //    v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 block scales (MXFP8). fp32 accumulation.
 //  * LDS rows are 128 B (8 chunks of 16 B) per K step, chunk c of row r stored at c ^ (r & 7)
 //    so the per-lane fragment reads and the row-wise tile writes are bank-conflict free.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace mok {
 
 // ------------------------------------------------------------------------- work list
-// int32 block layout (offsets in ints)
+// int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, and the
+// prefix sums of its up and down tiles; then, 16-byte aligned, one int4 per up tile and per
+// down tile {minibatch, tile within it, first row, group << 16 | rows} so that a workgroup
+// finds its tile with a single load.
 constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_TICKET = 3, WL_ERR = 4, WL_HDR = 16;
 MOK_DEV int32_t* wl_group(int32_t* wl, int cap) { return wl + WL_HDR; }
 MOK_DEV int32_t* wl_row0(int32_t* wl, int cap) { return wl + WL_HDR + cap; }
 MOK_DEV int32_t* wl_rows(int32_t* wl, int cap) { return wl + WL_HDR + 2 * cap; }
 MOK_DEV int32_t* wl_ustart(int32_t* wl, int cap) { return wl + WL_HDR + 3 * cap; }
 MOK_DEV int32_t* wl_dstart(int32_t* wl, int cap) { return wl + WL_HDR + 4 * cap + 1; }
+MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 5 * (size_t)cap + 2 + 3) & ~(size_t)3; }
+MOK_DEV int4* wl_utab(int32_t* wl, int cap) { return (int4*)(wl + wl_tab_off(cap)); }
+MOK_DEV int4* wl_dtab(int32_t* wl, int cap, int cap_u) { return (int4*)(wl + wl_tab_off(cap)) + cap_u; }
 
-size_t worklist_ints(int max_mb) { return WL_HDR + 5 * (size_t)max_mb + 2; }
+size_t worklist_ints(int max_mb, int cap_u, int cap_d) {
+  return wl_tab_off(max_mb) + 4 * ((size_t)cap_u + (size_t)cap_d);
+}
 
 // Block-wide exclusive scan of one int per thread (1024 threads). Returns the exclusive
 // prefix; *total receives the sum.
@@ -60,6 +70,7 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
                                                          const int32_t* __restrict__ offsets,
                                                          int E_l, int T_own, int mb, int bm,
                                                          int nU_r, int nU_s, int nD, int cap,
+                                                         int cap_u, int cap_d,
                                                          int32_t* __restrict__ wl) {
   __shared__ int32_t sh[1024];
   const int t = threadIdx.x;
@@ -117,73 +128,84 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     carry_u += tu;
     carry_d += td;
   }
+  const bool overflow = n_routed + n_sh > cap || carry_u > cap_u || carry_d > cap_d;
   if (t == 0) {
     us[n_mb] = carry_u;
     ds[n_mb] = carry_d;
     wl[WL_N_MB] = n_mb;
-    wl[WL_N_U] = carry_u;
-    wl[WL_N_D] = carry_d;
+    wl[WL_N_U] = overflow ? 0 : carry_u;
+    wl[WL_N_D] = overflow ? 0 : carry_d;
     wl[WL_TICKET] = 0;
-    wl[WL_ERR] = (n_routed + n_sh > cap) ? 1 : 0;
+    wl[WL_ERR] = overflow ? 1 : 0;
   }
-}
-
-// largest m with start[m] <= t (start ascending, start[0] == 0)
-MOK_DEV int find_mb(const int32_t* start, int n_mb, int32_t t) {
-  int lo = 0, hi = n_mb - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= t) lo = mid; else hi = mid - 1;
+  __syncthreads();
+  if (overflow) return;
+  // tile tables (tiles of a minibatch: n-tile major, m-tile minor)
+  int4* ut = wl_utab(wl, cap);
+  int4* dt = wl_dtab(wl, cap, cap_u);
+  for (int m = t; m < n_mb; m += 1024) {
+    const int32_t g = grp[m], rw = nr[m], first = r0[m];
+    const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
+    const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m];
+    for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = l; ut[us[m] + l] = e; }
+    for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = l; dt[ds[m] + l] = e; }
   }
-  return lo;
 }
 
 // ------------------------------------------------------------------------- GEMM tiles
 // Tile geometry. A workgroup of WAVES_M x WAVES_N waves computes a BM x BN block of the
-// stage's product; each wave a WM x WN block of 32 x 32 MFMA accumulators (FM x FN).
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+// stage's product; each wave a WM x WN block of 32 x 32 MFMA accumulators (FM x FN). Each K
+// step moves ROW_B bytes of every operand row into one of STAGES LDS buffers, either through
+// registers (global_load_dwordx4, then ds_write_b128) or by LDS-DMA (global_load_lds_dwordx4).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_, bool DMA_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  // operand tiles are filled by LDS-DMA slabs of 8 rows x 128 B (one per wave instruction)
-  static constexpr int A_SLABS = BM / 8 / NW, B_SLABS = BN / 8 / NW;
+  static constexpr int ROW_B = ROW_B_, STAGES = STAGES_;
+  static constexpr bool DMA = DMA_;
+  static constexpr int CH = ROW_B / 16;            // 16-byte chunks per LDS row
+  static constexpr int RPI = 64 / CH;              // rows one wave instruction covers
+  static constexpr int SWZ_SHIFT = CH == 8 ? 1 : 2;
+  static constexpr int A_SLABS = BM / RPI / NW, B_SLABS = BN / RPI / NW;
+  static_assert(CH == 8 || CH == 4, "64 or 128 bytes per row per K step");
   static_assert(FN % 2 == 0, "gate/up pairing needs an even number of N blocks per wave");
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole slabs per wave");
-  static_assert(BM == 64 * NW && BN == 64 * NW, "one 4-byte scale per lane per tile row");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "whole slabs per wave");
+  static_assert(BM == 64 * NW && BN == 64 * NW, "one scale word per lane per tile row");
+  static_assert(STAGES == 2 || STAGES == 4, "buffer rings of 2 or 4");
 };
 // 256 x 256 tiles, 4 waves of 128 x 128 (16 accumulator blocks = 256 AGPRs per lane), one
-// workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs, so LDS reads stay near
-// 64 B/clk per CU while the MFMA pipes are busy.
-typedef Cfg<256, 256, 2, 2> Big;
+// workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs. Two 64 KB K stages of
+// 128 bytes per row (whole cache lines), filled by LDS-DMA.
+typedef Cfg<256, 256, 2, 2, 128, 2, true> Big;
 
+// Per element type: bytes per element, and the MFMA's K per instruction.
 template <Elem EL> struct Tr;
-template <> struct Tr<Elem::BF16> { static constexpr int ES = 2, KT = 64, SUB = 4, CPL = 1; };
-template <> struct Tr<Elem::F32> { static constexpr int ES = 4, KT = 32, SUB = 2, CPL = 2; };
-template <> struct Tr<Elem::FP8> { static constexpr int ES = 1, KT = 128, SUB = 2, CPL = 2; };
+template <> struct Tr<Elem::BF16> { static constexpr int ES = 2, MK = 16, CPL = 1; };
+template <> struct Tr<Elem::F32> { static constexpr int ES = 4, MK = 16, CPL = 2; };
+template <> struct Tr<Elem::FP8> { static constexpr int ES = 1, MK = 64, CPL = 2; };
 
-// LDS: two buffers of the A and B tiles (128 B per row per K step), their MX scale words,
-// and the down stage's row table. Chunk c of row r sits at chunk c ^ (r & 7) of the row. The
-// buffers are separate LDS objects so the compiler can tell that reading one does not wait on
-// LDS-DMA still writing the other.
+// LDS: STAGES buffers of the A and B tiles (ROW_B per row per K step), their MX scale words and
+// the down stage's row table. Logical 16-byte chunk c of row r sits at slot
+// c ^ ((r >> SWZ_SHIFT) & (CH - 1)): 16 consecutive rows read at one logical chunk then hit
+// 16 distinct groups of the 64 banks. The buffers are separate LDS objects, so the compiler
+// can see that accesses to one do not touch another.
 template <class C>
 struct Bufs {
-  uint4 (*A)[8];
-  uint4 (*B)[8];
+  uint4 (*A)[C::CH];
+  uint4 (*B)[C::CH];
   uint32_t* As;
   uint32_t* Bs;
 };
 template <class C>
 struct Lds {
-  Bufs<C> buf[2];
+  Bufs<C> buf[C::STAGES];
   int32_t* row_dst;
   float* row_w;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16-byte chunk (of a 128 B LDS row) that lane half h feeds to the MFMA of K sub-step s.
+// 16-byte chunk that lane half h feeds to the MFMA of K sub-step s (16 or 64 elements).
 //  bf16 32x32x16: one chunk, k = 16s + 8h + [0, 8).
 //  fp32 32x32x2 (x8): two chunks, k = 16s + 8h + [0, 8).
 //  fp8 32x32x64 (scaled): bytes 0-15 of a lane belong to the MFMA's first 32-wide K block and
@@ -192,6 +214,43 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <Elem EL>
 MOK_DEV constexpr int frag_chunk(int s, int h, int q) {
   return EL == Elem::BF16 ? 2 * s + h : (EL == Elem::F32 ? 4 * s + 2 * h + q : 4 * s + 2 * q + h);
+}
+
+// s_waitcnt with only the vector-memory counter constrained: vmcnt <= n (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+MOK_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS-DMA: every lane copies 16 (or 4) bytes from sbase + voff (sbase uniform) to LDS address
+// lds + lane * 16 (or * 4), lds uniform. Issued as inline asm so that the compiler does not
+// track these writes: its own bookkeeping would make the first read after a loop back-edge
+// wait for every DMA in flight. The K loop orders them with explicit vmcnt waits instead.
+// M0 carries the LDS address; nothing else in these kernels uses M0.
+MOK_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+MOK_DEV void dma_b128(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+MOK_DEV void dma_b32(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+
+// Workgroup barrier for the LDS-DMA K loop. __syncthreads() would also wait for every
+// outstanding LDS-DMA (its fence covers LDS, and DMA writes count as LDS writes), draining the
+// stages still in flight; the K loop instead waits for exactly the step it needs (wait_vmcnt)
+// and then only synchronises. The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+MOK_DEV void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <Elem EL, int FM, int FN>
@@ -242,22 +301,26 @@ template <> struct Out<false> { typedef bf16_t T; };
 // One tile of the up (UP = true) or down (UP = false) stage of minibatch m.
 //  up:   the minibatch's rows x (gate, up rows of H columns n0 .. n0 + BN/2) -> H
 //  down: the minibatch's H rows x (W_down rows n0 .. n0 + BN) -> output columns
-// Operands reach LDS by LDS-DMA (global_load_lds_dwordx4): wave w fills rows [64w, 64w+64)
-// of each tile, 8 rows per instruction; lane L carries row 8q + L/8 and, because its LDS
-// destination is fixed (slot L % 8 of the row), fetches global chunk (L % 8) ^ (row & 7), so
-// the swizzle costs nothing. Row addresses are a uniform base plus a 32-bit offset.
-// M and N tails: rows/columns past the end are clamped on load, skipped on store.
+// Wave w fills rows [64w, 64w+64) of each operand tile, RPI rows per instruction; lane L
+// carries row RPI*q + L / CH, LDS slot L % CH, so it fetches global chunk
+// (L % CH) ^ swz(row) and the swizzle costs nothing. Row addresses are a uniform base plus a
+// 32-bit offset. M and N tails: rows/columns past the end are clamped on load, skipped on
+// store.
 template <Elem EL, bool UP, bool F32OUT, class C>
-MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
+MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   typedef Tr<EL> TR;
   typedef typename Out<F32OUT>::T OT;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
-  constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS;
-  const int cap = p.max_mb;
-  int32_t* wl = p.wl;
-  const int g = uniform(wl_group(wl, cap)[m]);
-  const int row0 = uniform(wl_row0(wl, cap)[m]);
-  const int rows = uniform(wl_rows(wl, cap)[m]);
+  constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS, ST = C::STAGES, CH = C::CH;
+  constexpr int RPI = C::RPI, SWS = C::SWZ_SHIFT;
+  constexpr int KT = C::ROW_B / TR::ES;            // elements per K step
+  constexpr int SUB = KT / TR::MK;                 // MFMA sub-steps per K step
+  constexpr int SC_B = KT / 32;                    // MX scale bytes per row per K step
+  // LDS-DMA instructions one wave issues per K step
+  constexpr int DMA_PER_STEP = A_SLABS + B_SLABS + (EL == Elem::FP8 ? 2 : 0);
+  const int m = uniform(entry.x), local = uniform(entry.y);
+  const int row0 = uniform(entry.z);
+  const int g = uniform(entry.w >> 16), rows = uniform(entry.w & 0xFFFF);
   const bool shared = g >= p.E_l;
   const int slot = m % p.n_slots;
   const int64_t ring_row0 = (int64_t)slot * p.mb;
@@ -270,8 +333,12 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
   const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
   const int K = UP ? p.d : (shared ? p.I_sh : p.I);
   const int N = UP ? (shared ? p.I_sh : p.I) : p.d;   // output columns of the stage
-  const int nk = K / TR::KT;
-  const int chunk_b = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;   // global byte of the lane's chunk
+  const int nk = K / KT;
+  // global byte of lane L's chunk in slab q: slot L % CH of row RPI*q + L / CH (+ 64 * wave)
+  auto chunk_b = [&](int q) {
+    const int row = RPI * q + lane / CH;
+    return ((lane % CH) ^ ((row >> SWS) & (CH - 1))) * 16;
+  };
 
   // ---- A operand: uniform base + per-slab 32-bit row offsets
   const char* a_base;
@@ -290,13 +357,13 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
   uint32_t a_off[A_SLABS];
 #pragma unroll
   for (int q = 0; q < A_SLABS; ++q) {
-    const int r = min(64 * wid + 8 * q + (lane >> 3), rows_valid - 1);
+    const int r = min(64 * wid + RPI * q + lane / CH, rows_valid - 1);
     int64_t row;
     if (UP && EL != Elem::FP8)
       row = shared ? p.own_begin + row0 + m0 + r : (int64_t)(p.route_ids[row0 + m0 + r] / p.k);
     else
       row = r;
-    a_off[q] = (uint32_t)(row * a_row_bytes) + chunk_b;
+    a_off[q] = (uint32_t)(row * a_row_bytes) + chunk_b(q);
   }
   // ---- B operand. Up: wave w loads gate (w even) or up (w odd) rows of H columns
   // nt*BN/2 + (w/2)*WN/2 + [0, 64); this matches the accumulator pairing of the waves. Down:
@@ -326,19 +393,20 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
   uint32_t b_off[B_SLABS];
 #pragma unroll
   for (int q = 0; q < B_SLABS; ++q) {
-    const int n = min(b_n0 + 8 * q + (lane >> 3), N - 1);
-    b_off[q] = (uint32_t)(n * b_row_bytes) + chunk_b;
+    const int n = min(b_n0 + RPI * q + lane / CH, N - 1);
+    b_off[q] = (uint32_t)(n * b_row_bytes) + chunk_b(q);
   }
-  // ---- MX scales: lane L of wave w carries tile row 64w + L (4 scale bytes per K step)
+  // ---- MX scales: lane L of wave w carries tile row 64w + L. A K step needs SC_B scale bytes
+  // of a row; the 4-byte word holding them (4 | SC_B * steps) is loaded.
   const uint8_t* a_sc_base = nullptr;
   const uint8_t* b_sc_base = nullptr;
   uint32_t a_sc_off = 0, b_sc_off = 0;
-  int64_t a_sc_row = 0, b_sc_row = 0;
   if (EL == Elem::FP8) {
     const int r = min(64 * wid + lane, rows_valid - 1);
-    a_sc_row = UP ? p.d / 32 : p.Hld / 32;
+    const int64_t a_sc_row = UP ? p.d / 32 : p.Hld / 32;
     a_sc_base = (UP ? p.A_sc : p.H_sc) + (ring_row0 + m0) * a_sc_row;
     a_sc_off = (uint32_t)(r * a_sc_row);
+    int64_t b_sc_row;
     if (UP) {
       const bool uph = (wid & 1) != 0;
       const uint8_t* S = shared ? (uph ? p.su_sc : p.sg_sc) : (uph ? p.wu_sc : p.wg_sc);
@@ -365,29 +433,58 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
     }
   }
 
-  // issue the LDS-DMA loads of K step kt into buffer b. The K offset is added to the 32-bit
-  // row offsets (not to the 64-bit base) so each load stays "scalar base + 32-bit offset".
-  auto issue = [&](int kt, const Bufs<C>& b) {
-    const uint32_t k0 = (uint32_t)kt * TR::KT;
-    const uint32_t ka = k0 * TR::ES;
+  // address pieces of K step kt
+  struct StepAddr { uint32_t ka, kb, sca, scb; const char* b_seg; const uint8_t* bs_seg; };
+  auto step_addr = [&](int kt) {
+    StepAddr s;
+    const uint32_t k0 = (uint32_t)kt * KT;
     const uint32_t seg = k0 / (uint32_t)b_seg_len;
     const uint32_t kin = k0 - seg * (uint32_t)b_seg_len;
-    const char* b_seg = uniform_ptr(b_base + (int64_t)seg * b_seg_stride);
-    const uint32_t kb = kin * TR::ES;
+    s.ka = k0 * TR::ES;
+    s.kb = kin * TR::ES;
+    s.b_seg = uniform_ptr(b_base + (int64_t)seg * b_seg_stride);
+    s.sca = (k0 / 32) & ~3u;
+    s.scb = (kin / 32) & ~3u;
+    s.bs_seg = EL == Elem::FP8 ? uniform_ptr(b_sc_base + (int64_t)seg * (b_seg_stride / 32))
+                               : nullptr;
+    return s;
+  };
+  // (a) LDS-DMA issue of K step kt into buffer b
+  auto issue = [&](int kt, const Bufs<C>& b) {
+    const StepAddr s = step_addr(kt);
+    const uint32_t la = uniform(lds_addr(&b.A[64 * wid][0]));
+    const uint32_t lb = uniform(lds_addr(&b.B[64 * wid][0]));
 #pragma unroll
-    for (int q = 0; q < A_SLABS; ++q)
-      __builtin_amdgcn_global_load_lds(a_base + (uint32_t)(a_off[q] + ka),
-                                       (lds_void*)&b.A[64 * wid + 8 * q][0], 16, 0, 0);
+    for (int q = 0; q < A_SLABS; ++q) dma_b128(a_base, a_off[q] + s.ka, la + 1024 * q);
 #pragma unroll
-    for (int q = 0; q < B_SLABS; ++q)
-      __builtin_amdgcn_global_load_lds(b_seg + (uint32_t)(b_off[q] + kb),
-                                       (lds_void*)&b.B[64 * wid + 8 * q][0], 16, 0, 0);
+    for (int q = 0; q < B_SLABS; ++q) dma_b128(s.b_seg, b_off[q] + s.kb, lb + 1024 * q);
     if (EL == Elem::FP8) {
-      __builtin_amdgcn_global_load_lds(a_sc_base + (uint32_t)(a_sc_off + k0 / 32),
-                                       (lds_void*)&b.As[64 * wid], 4, 0, 0);
-      const uint8_t* bs_seg = uniform_ptr(b_sc_base + (int64_t)seg * (b_seg_stride / 32));
-      __builtin_amdgcn_global_load_lds(bs_seg + (uint32_t)(b_sc_off + kin / 32),
-                                       (lds_void*)&b.Bs[64 * wid], 4, 0, 0);
+      dma_b32(a_sc_base, a_sc_off + s.sca, uniform(lds_addr(&b.As[64 * wid])));
+      dma_b32(s.bs_seg, b_sc_off + s.scb, uniform(lds_addr(&b.Bs[64 * wid])));
+    }
+  };
+  // (b) register staging: global -> registers, later registers -> LDS
+  uint4 ra[C::DMA ? 1 : A_SLABS], rb[C::DMA ? 1 : B_SLABS];
+  uint32_t rsa = 0, rsb = 0;
+  auto gload = [&](int kt) {
+    const StepAddr s = step_addr(kt);
+#pragma unroll
+    for (int q = 0; q < A_SLABS; ++q) ra[q] = *(const uint4*)(a_base + (uint32_t)(a_off[q] + s.ka));
+#pragma unroll
+    for (int q = 0; q < B_SLABS; ++q) rb[q] = *(const uint4*)(s.b_seg + (uint32_t)(b_off[q] + s.kb));
+    if (EL == Elem::FP8) {
+      rsa = *(const uint32_t*)(a_sc_base + (uint32_t)(a_sc_off + s.sca));
+      rsb = *(const uint32_t*)(s.bs_seg + (uint32_t)(b_sc_off + s.scb));
+    }
+  };
+  auto lstore = [&](const Bufs<C>& b) {
+#pragma unroll
+    for (int q = 0; q < A_SLABS; ++q) b.A[64 * wid + RPI * q + lane / CH][lane % CH] = ra[q];
+#pragma unroll
+    for (int q = 0; q < B_SLABS; ++q) b.B[64 * wid + RPI * q + lane / CH][lane % CH] = rb[q];
+    if (EL == Elem::FP8) {
+      b.As[64 * wid + lane] = rsa;
+      b.Bs[64 * wid + lane] = rsb;
     }
   };
 
@@ -399,65 +496,146 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int h = lane >> 5, l32 = lane & 31, x7 = lane & 7;
-  // MFMAs of one K step from buffer b. Fragments are double-buffered across the K sub-steps:
-  // the reads of sub-step s + 1 are issued before the MFMAs of s, and a scheduling barrier
-  // keeps the compiler from hoisting further reads (which would only add live registers).
-  auto compute = [&](const Bufs<C>& b) {
+  const int h = lane >> 5, l32 = lane & 31;
+  const int xsw = (l32 >> SWS) & (CH - 1);         // swizzle of the lane's fragment rows
+  // MFMAs of one K step from buffer b (kt: the step, for the MX scale byte position).
+  // Fragments are double-buffered across the K sub-steps: the reads of sub-step s + 1 are
+  // issued before the MFMAs of s (scheduling barriers pin that order; left alone the scheduler
+  // sinks each read to just before its first use and every sub-step waits on LDS latency).
+  auto compute = [&](const Bufs<C>& b, int kt) {
     const char* a_buf = (const char*)&b.A[wm * WM + l32][0];
     const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
+    const int sc_shift = 8 * (((uint32_t)kt * SC_B) & 3);
     uint4 fa[2][FM][2], fb[2][FN][2];
     uint32_t asc[2][FM], bsc[2][FN];
     auto load = [&](int s, int f) {
-      const int c0 = ((frag_chunk<EL>(s, h, 0)) ^ x7) * 16;
-      const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ x7) * 16;
+      const int c0 = ((frag_chunk<EL>(s, h, 0)) ^ xsw) * 16;
+      const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ xsw) * 16;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * 128 + c0);
-        if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * 128 + c1);
+        fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c0);
+        if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c1);
         if (EL == Elem::FP8)
-          asc[f][i] = (b.As[wm * WM + i * 32 + l32] >> (8 * (2 * s + h))) & 0xFFu;
+          asc[f][i] = (b.As[wm * WM + i * 32 + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        fb[f][j][0] = *(const uint4*)(b_buf + j * 32 * 128 + c0);
-        if (TR::CPL == 2) fb[f][j][1] = *(const uint4*)(b_buf + j * 32 * 128 + c1);
+        fb[f][j][0] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c0);
+        if (TR::CPL == 2) fb[f][j][1] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c1);
         if (EL == Elem::FP8)
-          bsc[f][j] = (b.Bs[wn * WN + j * 32 + l32] >> (8 * (2 * s + h))) & 0xFFu;
+          bsc[f][j] = (b.Bs[wn * WN + j * 32 + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
       }
     };
     load(0, 0);
 #pragma unroll
-    for (int s = 0; s < TR::SUB; ++s) {
-      if (s + 1 < TR::SUB) load(s + 1, (s + 1) & 1);
+    for (int s = 0; s < SUB; ++s) {
+      if (s + 1 < SUB) load(s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);   // the reads of s + 1 go out before the MFMAs of s
       mfma_step<EL, FM, FN>(fa[s & 1], fb[s & 1], asc[s & 1], bsc[s & 1], acc);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // K loop, unrolled by two so each buffer's role is static: wait for step kt's DMA (own
-  // wave), barrier (every wave's DMA landed, every wave done with kt - 1), issue kt + 1 into
-  // the other buffer, compute kt.
-  issue(0, sm.buf[0]);
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (C::DMA) {
+    // K loop over a ring of ST buffers. Step kt: wait until this wave's DMA of kt has landed
+    // (later steps' DMAs stay in flight), barrier (every wave's DMA of kt landed; every wave
+    // done computing kt - 1), issue step kt + ST - 1 into the buffer kt - 1 used, compute kt.
+    // The steady state is unrolled by ST so every buffer's role is static.
+#pragma unroll
+    for (int q = 0; q < ST - 1; ++q)
+      if (q < nk) issue(q, sm.buf[q]);
+    auto steady = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
+      wait_vmcnt<(ST - 2) * DMA_PER_STEP>();
+      lds_barrier();
+      issue(kt + ST - 1, nxt);
+      compute(cur, kt);
+    };
+    int kt = 0;
+    for (; kt + 2 * ST - 1 <= nk; kt += ST) {
+#pragma unroll
+      for (int q = 0; q < ST; ++q) steady(kt + q, sm.buf[q], sm.buf[(q + ST - 1) % ST]);
+    }
+    for (; kt < nk; ++kt) {     // the last steps, buffers chosen at run time
+      const int ahead = min(nk - 1 - kt, ST - 2);
+      if (ahead >= 2) wait_vmcnt<2 * DMA_PER_STEP>();
+      else if (ahead == 1) wait_vmcnt<DMA_PER_STEP>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + ST - 1 < nk) issue(kt + ST - 1, sm.buf[(kt + ST - 1) % ST]);
+      compute(sm.buf[kt % ST], kt);
+    }
+  } else {
+    // Two buffers, unrolled by two: the loads of step kt + 1 are in flight (registers) while
+    // step kt computes; then they are written to the other buffer and everyone synchronises.
+    static_assert(ST == 2, "register staging uses two buffers");
+    gload(0);
+    lstore(sm.buf[0]);
     __syncthreads();
-    issue(kt + 1, sm.buf[1]);
-    compute(sm.buf[0]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 2 < nk) issue(kt + 2, sm.buf[0]);
-    compute(sm.buf[1]);
-  }
-  if (kt < nk) {  // odd number of K steps: the last one is in buffer 0
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    compute(sm.buf[0]);
+    auto two = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
+      const bool more = kt + 1 < nk;
+      if (more) gload(kt + 1);
+      compute(cur, kt);
+      if (more) lstore(nxt);
+      __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      two(kt, sm.buf[0], sm.buf[1]);
+      two(kt + 1, sm.buf[1], sm.buf[0]);
+    }
+    if (kt < nk) two(kt, sm.buf[0], sm.buf[1]);
   }
 
   // ---- epilogue. Accumulator v of block (i, j) is (row 8*(v/4) + 4*h + v%4, col l32).
-  if (UP) {
+  if constexpr (!F32OUT && !(UP && EL == Elem::FP8)) {
+    // bf16 outputs: each wave stages its block through its own LDS region (the operand buffers
+    // are free once every wave is past the K loop), 32 rows at a time, then writes whole rows
+    // with 16-byte stores: H rows of the ring (up) or route-slot / shared rows (down).
+    constexpr int CW = UP ? WN / 2 : WN;              // output columns per wave
+    constexpr int JB = CW / 32;                       // 32-column blocks per wave
+    constexpr int STRIDE = CW * 2 + 16;               // padded LDS row (bytes)
+    constexpr int LPR = CW * 2 / 16;                  // lanes per row in the store phase
+    constexpr int SRPI = 64 / LPR;                    // rows per store instruction
+    static_assert(32 * STRIDE <= BM * C::ROW_B, "a wave's 32-row pass fits one operand buffer");
+    __syncthreads();
+    typedef __attribute__((address_space(3))) bf16_t lds_bf16;
+    typedef __attribute__((address_space(3))) uint4 lds_u4;
+    char* region_g = (wid & 1) ? (char*)sm.buf[wid >> 1].B : (char*)sm.buf[wid >> 1].A;
+    lds_bf16* region_h = (lds_bf16*)region_g;
+    const lds_u4* region_q = (const lds_u4*)region_g;
+    const int col0 = UP ? nt * (BN / 2) + wn * (WN / 2) : nt * BN + wn * WN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float rw[16];                                     // row weights of this 32-row block
+      if (!UP) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          rw[v] = sm.row_w[min(wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3), BM - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = 8 * (v >> 2) + 4 * h + (v & 3);      // row within the pass
+          const float val = UP ? silu(acc[i][j][v]) * acc[i][j + FN / 2][v] : acc[i][j][v] * rw[v];
+          region_h[rr * (STRIDE / 2) + j * 32 + l32] = f32_to_bf16(val);
+        }
+#pragma unroll
+      for (int q = 0; q < 32 / SRPI; ++q) {
+        const int rr = q * SRPI + lane / LPR;
+        const int c = (lane % LPR) * 8;                 // first column of the lane's 16 B
+        const int r = wm * WM + i * 32 + rr;            // row within the tile
+        const uint4 val = region_q[(rr * STRIDE + c * 2) / 16];
+        if (r < rows_valid && col0 + c < N) {
+          bf16_t* dst;
+          if (UP) dst = (bf16_t*)p.H + (ring_row0 + m0 + r) * p.Hld;
+          else dst = (shared ? (bf16_t*)p.y_shared : (bf16_t*)p.y_slots) + (int64_t)sm.row_dst[r] * p.d;
+          *(uint4*)(dst + col0 + c) = val;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);                // one 32-row block of values live at a time
+    }
+  } else if (UP) {
     const int col0 = nt * (BN / 2) + wn * (WN / 2);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -511,23 +689,38 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, int m, int local) {
 // rows share that XCD's L2.
 template <Elem EL, bool UP, bool F32OUT, class C>
 __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
-  __shared__ uint4 a0[C::BM][8], a1[C::BM][8], b0[C::BN][8], b1[C::BN][8];
+  // LDS: the STAGES buffers as separate objects (only the first STAGES are referenced)
+  __shared__ uint4 a0[C::BM][C::CH], a1[C::BM][C::CH], b0[C::BN][C::CH], b1[C::BN][C::CH];
+  __shared__ uint4 a2[C::STAGES > 2 ? C::BM : 1][C::CH], a3[C::STAGES > 2 ? C::BM : 1][C::CH];
+  __shared__ uint4 b2[C::STAGES > 2 ? C::BN : 1][C::CH], b3[C::STAGES > 2 ? C::BN : 1][C::CH];
   __shared__ uint32_t as0[C::BM], as1[C::BM], bs0[C::BN], bs1[C::BN];
+  __shared__ uint32_t as2[C::STAGES > 2 ? C::BM : 1], as3[C::STAGES > 2 ? C::BM : 1];
+  __shared__ uint32_t bs2[C::STAGES > 2 ? C::BN : 1], bs3[C::STAGES > 2 ? C::BN : 1];
   __shared__ int32_t row_dst[C::BM];
   __shared__ float row_w[C::BM];
-  const Lds<C> sm = {{{a0, b0, as0, bs0}, {a1, b1, as1, bs1}}, row_dst, row_w};
+  Lds<C> sm;
+  sm.buf[0].A = a0; sm.buf[0].B = b0; sm.buf[0].As = as0; sm.buf[0].Bs = bs0;
+  sm.buf[1].A = a1; sm.buf[1].B = b1; sm.buf[1].As = as1; sm.buf[1].Bs = bs1;
+  if constexpr (C::STAGES > 2) {
+    sm.buf[2].A = a2; sm.buf[2].B = b2; sm.buf[2].As = as2; sm.buf[2].Bs = bs2;
+    sm.buf[3].A = a3; sm.buf[3].B = b3; sm.buf[3].As = as3; sm.buf[3].Bs = bs3;
+  }
+  sm.row_dst = row_dst;
+  sm.row_w = row_w;
   const int cap = p.max_mb;
-  const int n_mb = p.wl[WL_N_MB];
   const int32_t total = p.wl[UP ? WL_N_U : WL_N_D];
-  const int32_t* start = UP ? wl_ustart(p.wl, cap) : wl_dstart(p.wl, cap);
+  const int4* tab = UP ? wl_utab(p.wl, cap) : wl_dtab(p.wl, cap, p.cap_u);
   const int G = gridDim.x;
   const int b = blockIdx.x;
-  const int xcd_slot = (b & 7) * (G >> 3) + (b >> 3);
-  for (int32_t t0 = 0; t0 < total; t0 += G) {
-    const int32_t t = t0 + xcd_slot;
-    if (t >= total) break;
-    const int m = uniform(find_mb(start, n_mb, t));
-    run_tile<EL, UP, F32OUT, C>(p, sm, m, uniform(t - start[m]));
+  int32_t t = (b & 7) * (G >> 3) + (b >> 3);
+  if (t >= total) return;
+  int4 cur = tab[t];
+  while (t < total) {
+    const int32_t tn = t + G;
+    const int4 nxt = tn < total ? tab[tn] : cur;   // next tile's entry, loaded before this tile
+    run_tile<EL, UP, F32OUT, C>(p, sm, cur);
+    cur = nxt;
+    t = tn;
   }
 }
 
@@ -621,13 +814,21 @@ static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* cons
   return hipGetLastError();
 }
 
+void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, int* cap_u, int* cap_d) {
+  const int64_t mt = (mb + Big::BM - 1) / Big::BM;
+  const int64_t nU = std::max((I + Big::BN / 2 - 1) / (Big::BN / 2), (I_sh + Big::BN / 2 - 1) / (Big::BN / 2));
+  const int64_t nD = (d + Big::BN - 1) / Big::BN;
+  *cap_u = (int)std::min<int64_t>(INT32_MAX / 8, (int64_t)max_mb * mt * nU);
+  *cap_d = (int)std::min<int64_t>(INT32_MAX / 8, (int64_t)max_mb * mt * nD);
+}
+
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev) {
   const int nU_r = (p.I + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nD = (p.d + Big::BN - 1) / Big::BN;
   record(ev, 2 * 3, s);
   hipLaunchKernelGGL(k_build_worklist, dim3(1), dim3(1024), 0, s, p.counts, p.offsets, p.E_l,
-                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, p.max_mb, p.wl);
+                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, p.max_mb, p.cap_u, p.cap_d, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);

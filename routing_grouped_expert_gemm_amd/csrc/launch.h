@@ -36,6 +36,7 @@ struct ExpertPass {
   int n_slots;           // ring slots (ring rows = n_slots * mb)
   int Hld;               // ring row length in elements: max(I, I_sh)
   int max_mb;            // capacity of the minibatch tables
+  int cap_u, cap_d;      // capacity of the up / down tile tables
   int bm, bn;            // GEMM tile (rows, B-tile rows)
   int grid;              // workgroups of the tile loops
   // inputs
@@ -59,7 +60,8 @@ struct ExpertPass {
   void* y_shared;
 };
 
-size_t worklist_ints(int max_mb);
+size_t worklist_ints(int max_mb, int cap_u, int cap_d);
+void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, int* cap_u, int* cap_d);
 // ev: optional hipEvent_t[2 * 6] (mok stage events); records UP around the work list, gather
 // and up stage, DOWN around the down stage.
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev);

@@ -39,7 +39,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_count(const int32_t* __re
     blk_counts[(int64_t)blockIdx.x * E_l + e] = hist[e];
 }
 
-// One workgroup of 1024 threads. blk_base[b][e] = offsets[e] + sum_{b' < b} blk_counts[b'][e].
+// One workgroup of 1024 threads.
+//   blk_base[b][e] = sum_{b' < b} blk_counts[b'][e]   (the expert's offset is added later)
+//   counts[e] = sum_b blk_counts[b][e],  offsets = exclusive prefix sum of counts.
+// Each expert's block range is split over a group of P threads (P = 1024 / E_l rounded down
+// to a power of two): per-thread segment sums, a scan across the group, then the segment walk.
 __global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ blk_counts,
                                                     int n_blk, int E_l,
                                                     int32_t* __restrict__ blk_base,
@@ -47,30 +51,51 @@ __global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ offsets) {
   __shared__ int32_t part[1024];
   __shared__ int32_t tot[1024];
-  const int e = threadIdx.x;
-  int32_t sum = 0;
-  if (e < E_l)
-    for (int b = 0; b < n_blk; ++b) {
-      const int32_t c = blk_counts[(int64_t)b * E_l + e];
-      blk_base[(int64_t)b * E_l + e] = sum;
-      sum += c;
-    }
-  tot[e] = e < E_l ? sum : 0;
-  part[e] = tot[e];
-  __syncthreads();
-  // inclusive Hillis-Steele scan over experts
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t v = e >= off ? part[e - off] : 0;
+  const int t = threadIdx.x;
+  int P = 1;
+  while (P * 2 * E_l <= 1024) P *= 2;
+  const int experts_per_round = 1024 / P;
+  const int g = t % P, seg = (n_blk + P - 1) / P;
+  const int b0 = min(n_blk, g * seg), b1 = min(n_blk, b0 + seg);
+  for (int e_base = 0; e_base < E_l; e_base += experts_per_round) {
+    const int e = e_base + t / P;
+    const bool active = e < E_l;
+    int32_t local = 0;
+    if (active)
+      for (int b = b0; b < b1; ++b) local += blk_counts[(int64_t)b * E_l + e];
+    part[t] = local;
     __syncthreads();
-    part[e] += v;
+    for (int off = 1; off < P; off <<= 1) {   // inclusive scan inside each group of P
+      const int32_t v = (g >= off) ? part[t - off] : 0;
+      __syncthreads();
+      part[t] += v;
+      __syncthreads();
+    }
+    if (active) {
+      int32_t run = part[t] - local;
+      for (int b = b0; b < b1; ++b) {
+        blk_base[(int64_t)b * E_l + e] = run;
+        run += blk_counts[(int64_t)b * E_l + e];
+      }
+      if (g == P - 1) counts[e] = part[t];
+    }
     __syncthreads();
   }
-  const int32_t excl = part[e] - tot[e];
-  if (e < E_l) {
-    counts[e] = tot[e];
-    offsets[e] = excl;
-    if (e == E_l - 1) offsets[E_l] = part[e];
-    for (int b = 0; b < n_blk; ++b) blk_base[(int64_t)b * E_l + e] += excl;
+  __threadfence_block();
+  // exclusive scan of the counts over experts (E_l <= 1024)
+  const int32_t c = t < E_l ? counts[t] : 0;
+  tot[t] = c;
+  part[t] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  if (t < E_l) {
+    offsets[t] = part[t] - tot[t];
+    if (t == E_l - 1) offsets[E_l] = part[t];
   }
 }
 
@@ -78,13 +103,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __
                                                                int64_t n_routes, int64_t chunk,
                                                                int e0, int E_l,
                                                                const int32_t* __restrict__ blk_base,
+                                                               const int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ route_ids) {
   extern __shared__ int32_t sm[];
   int32_t* base = sm;                 // [E_l] next free row of each region (this chunk)
   int32_t* wcnt = sm + E_l;           // [4][E_l] per-wave counts of the current sub-chunk
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int e = tid; e < E_l; e += PLAN_THREADS) {
-    base[e] = blk_base[(int64_t)blockIdx.x * E_l + e];
+    base[e] = offsets[e] + blk_base[(int64_t)blockIdx.x * E_l + e];
     for (int q = 0; q < 4; ++q) wcnt[q * E_l + e] = 0;
   }
   __syncthreads();
@@ -151,8 +177,8 @@ __global__ void k_plan_rank_counts(const int32_t* __restrict__ route_ids,
 }
 
 int64_t plan_chunk(int64_t n_routes) {
-  // ~4096 routes per workgroup, at most 4096 workgroups
-  int64_t chunk = 4096;
+  // 512 routes (2 sub-chunks of 256) per workgroup, at most 4096 workgroups
+  int64_t chunk = 512;
   while ((n_routes + chunk - 1) / chunk > 4096) chunk *= 2;
   return chunk;
 }
@@ -175,7 +201,7 @@ hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l
   hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, s, blk_counts, (int)nb, E_l, blk_base,
                      counts, offsets);
   hipLaunchKernelGGL(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS), sh_count * 5, s, idx,
-                     n_routes, chunk, e0, E_l, blk_base, route_ids);
+                     n_routes, chunk, e0, E_l, blk_base, offsets, route_ids);
   if (rank_counts) {
     const int64_t R = n_tok / tokens_per_rank;
     const int64_t n = (int64_t)E_l * R;
