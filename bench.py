@@ -11,12 +11,23 @@ already resident in HBM. Prints ONE JSON line.
 with the fused pull gather and SwiGLU, routed + shared): HIP events recorded by the library
 on the forward's own stream around that launch, averaged over the timed steps, against the
 algorithmic FLOPs of one launch (4 * d * I per routed row + 4 * d * I_shared * n_shared per
-own token). `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+own token). `roofline.traffic` is the HBM bytes of one launch of that kernel as measured by
+the rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
+by what the counter reads for a plain copy of known size); it is null when the summary is
+missing or was taken from different kernel sources. `cpu_baseline` is the CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py --summarize DIR
+
+writes that summary from the rocprofv3 output directory DIR (layout and commands listed in
+the summary itself).
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +39,120 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer fwd tokens/s + routed-expert TFLOP/s on 1 MI355X (bf16, MXFP8)"
 PEAK = {"bf16": 2.5e15, "mxfp8": 5.0e15, "fp32": 157.3e12}
 HBM_PEAK = 8.0e12
+
+
+# sources whose machine code the counter passes describe
+KERNEL_SOURCES = ["routing_grouped_expert_gemm_amd/csrc/expert_gemm.hip",
+                  "routing_grouped_expert_gemm_amd/csrc/device_common.h",
+                  "routing_grouped_expert_gemm_amd/csrc/launch.h",
+                  "routing_grouped_expert_gemm_amd/_build.py"]
+UP_KERNEL = "k_expert_stage<(mok::Elem)"   # + element, then "true" for the gate/up stage
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profile_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"expert_gemm_up_{workload}.txt")
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the gate/up kernel from the committed counter summary, or None
+    if there is none for this workload or it was taken from other kernel sources."""
+    try:
+        with open(profile_path(workload)) as fh:
+            kv = dict(line.split(": ", 1) for line in fh.read().splitlines() if ": " in line)
+    except OSError:
+        return None
+    if kv.get("kernel_sources_sha256", "").strip() != kernel_sources_sha256():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _is_up_kernel(name: str, elem: int) -> bool:
+    return f"{UP_KERNEL}{elem}, true," in name
+
+
+def summarize(d: str) -> str:
+    """Write profiles/expert_gemm_up_<workload>.txt from a rocprofv3 output directory holding
+    trace/ (kernel trace + stats of a bench run, its JSON line in trace.json), FETCH_SIZE/ and
+    WRITE_SIZE/ (counter passes over a short bench run) and copy_FETCH_SIZE/, copy_WRITE_SIZE/
+    (the same counters over a 1 GiB device copy)."""
+    bench_line = json.loads(open(os.path.join(d, "trace.json")).read().strip().splitlines()[-1])
+    wl = bench_line["config"]["workload"]
+    elem = {"bf16": 1, "f32": 0, "mxfp8": 2}[bench_line["dtype"]]
+    stats = list(csv.DictReader(open(os.path.join(d, "trace", "trace_kernel_stats.csv"))))
+
+    def counter(sub, name_pred):
+        rows = list(csv.DictReader(open(os.path.join(d, sub, f"{sub}_counter_collection.csv"))))
+        vals = [float(r["Counter_Value"]) for r in rows if name_pred(r["Kernel_Name"])]
+        return sum(vals) / len(vals), len(vals)
+
+    up = lambda n: _is_up_kernel(n, elem)
+    copy = lambda n: "copyBuffer" in n
+    fetch_kib, n_f = counter("FETCH_SIZE", up)
+    write_kib, n_w = counter("WRITE_SIZE", up)
+    copy_fetch, _ = counter("copy_FETCH_SIZE", copy)
+    copy_write, _ = counter("copy_WRITE_SIZE", copy)
+    copy_kib = 1 << 20                               # 1 GiB read and 1 GiB written per copy
+    f_fetch, f_write = copy_kib / copy_fetch, copy_kib / copy_write
+    traffic = int(round((fetch_kib * f_fetch + write_kib * f_write) * 1024))
+    up_stat = [r for r in stats if up(r["Name"])][0]
+    prof_ms = float(up_stat["AverageNs"]) * 1e-6
+    ev_ms = bench_line["stage_ms"]["up"]
+    lines = [
+        f"# gate/up expert GEMM stage (routed + shared, fused pull gather and SwiGLU), workload {wl}",
+        "#",
+        "# commands (from the repository root; D = gpurun_out/prof_" + wl + "):",
+        f"#   rocprofv3 --kernel-trace --stats -d D/trace -o trace --output-format csv -- "
+        f"python3 bench.py --steps 10 --warmup 3 --no-cpu --workload {wl} > D/trace.json",
+        f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'mok::' -d D/FETCH_SIZE -o FETCH_SIZE "
+        f"--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu --workload {wl}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'mok::' -d D/WRITE_SIZE -o WRITE_SIZE "
+        f"--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu --workload {wl}",
+        "#   rocprofv3 --pmc FETCH_SIZE -d D/copy_FETCH_SIZE -o copy_FETCH_SIZE --output-format csv "
+        "-- python3 bench.py --copy-probe-mib 1024",
+        "#   rocprofv3 --pmc WRITE_SIZE -d D/copy_WRITE_SIZE -o copy_WRITE_SIZE --output-format csv "
+        "-- python3 bench.py --copy-probe-mib 1024",
+        "#   python3 bench.py --summarize D",
+        "",
+        "## kernel trace (--kernel-trace --stats), mok kernels, average per dispatch",
+        f"{'kernel':<100} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}",
+    ]
+    for r in stats:
+        if "mok::" not in r["Name"]:
+            continue
+        lines.append(f"{r['Name'][:100]:<100} {r['Calls']:>6} {float(r['AverageNs']) / 1e3:>10.1f} "
+                     f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f}")
+    lines += [
+        "",
+        f"gate/up kernel average (profiler): {prof_ms:.4f} ms",
+        f"gate/up kernel average (bench.py HIP events, same run): {ev_ms:.4f} ms",
+        f"agreement: {100 * (ev_ms - prof_ms) / prof_ms:+.1f} %",
+        f"bench line of the traced run: ms_per_step {bench_line['ms_per_step']}, value "
+        f"{bench_line['value']} tokens/s, roofline frac {bench_line['roofline']['frac']}",
+        "",
+        "## HBM bytes (--pmc), gate/up kernel, per dispatch",
+        f"FETCH_SIZE KiB: {fetch_kib:.1f} (mean of {n_f} dispatches)",
+        f"WRITE_SIZE KiB: {write_kib:.1f} (mean of {n_w} dispatches)",
+        f"copy calibration: 1 GiB device copy reads FETCH_SIZE {copy_fetch:.1f} KiB, WRITE_SIZE "
+        f"{copy_write:.1f} KiB -> factors {f_fetch:.4f} (fetch), {f_write:.4f} (write)",
+        f"traffic_bytes_per_launch: {traffic}",
+        f"kernel_sources_sha256: {kernel_sources_sha256()}",
+    ]
+    path = profile_path(wl)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 class HipEvents:
@@ -98,10 +223,15 @@ def main():
     ap.add_argument("--minibatch", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--summarize", default=None, metavar="DIR",
+                    help="write the profiles/ summary from a rocprofv3 output directory and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize(args.summarize))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
@@ -179,7 +309,8 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": {"bound": "mfma", "kernel": "gate/up stage (k_expert_stage up)",
                      "achieved": round(achieved / 1e12, 2), "peak": peak / 1e12,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": profiled_traffic(wl.name)},
     }
     if not args.no_cpu:
         import synth as _s  # noqa: F401

@@ -599,7 +599,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     static_assert(32 * STRIDE <= BM * C::ROW_B, "a wave's 32-row pass fits one operand buffer");
     __syncthreads();
     typedef __attribute__((address_space(3))) bf16_t lds_bf16;
-    typedef __attribute__((address_space(3))) uint4 lds_u4;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) u32x4 lds_u4;
     char* region_g = (wid & 1) ? (char*)sm.buf[wid >> 1].B : (char*)sm.buf[wid >> 1].A;
     lds_bf16* region_h = (lds_bf16*)region_g;
     const lds_u4* region_q = (const lds_u4*)region_g;
@@ -625,12 +626,12 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
         const int rr = q * SRPI + lane / LPR;
         const int c = (lane % LPR) * 8;                 // first column of the lane's 16 B
         const int r = wm * WM + i * 32 + rr;            // row within the tile
-        const uint4 val = region_q[(rr * STRIDE + c * 2) / 16];
+        const u32x4 val = region_q[(rr * STRIDE + c * 2) / 16];
         if (r < rows_valid && col0 + c < N) {
           bf16_t* dst;
           if (UP) dst = (bf16_t*)p.H + (ring_row0 + m0 + r) * p.Hld;
           else dst = (shared ? (bf16_t*)p.y_shared : (bf16_t*)p.y_slots) + (int64_t)sm.row_dst[r] * p.d;
-          *(uint4*)(dst + col0 + c) = val;
+          *(u32x4*)(dst + col0 + c) = val;
         }
       }
       __builtin_amdgcn_sched_barrier(0);                // one 32-row block of values live at a time
