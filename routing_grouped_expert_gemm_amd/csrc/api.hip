@@ -34,7 +34,7 @@ int device_cus() {
 // can be found from the workspace pointer alone.
 struct Layout {
   bool use_ring = false;
-  int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0;
+  int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0, cap_g = 0, cap_r = 0, lag = 0;
   size_t wl = 0, logits = 0, idx = 0, w = 0, counts = 0, offsets = 0, rank_counts = 0,
          route_ids = 0, blk_counts = 0, blk_base = 0, H = 0, H_sc = 0, A_codes = 0, A_sc = 0,
          wq = 0, total = 0;
@@ -93,14 +93,19 @@ Layout layout_moe(const mok_moe_args* a) {
   const int I_sh = a->n_shared * a->I_shared;
   const int64_t max_mb = ceil_div(n_cap, mb) + a->E_l + (I_sh > 0 ? ceil_div(a->T_own, mb) : 0);
   L.max_mb = (int)std::max<int64_t>(1, max_mb);
-  L.use_ring = !(a->flags & MOK_FLAG_NO_RING) && false;  // the ring work loop is not built yet
+  L.use_ring = !(a->flags & MOK_FLAG_NO_RING);
   L.n_slots = L.use_ring ? a->ring_rows / mb : L.max_mb;
+  // ring order: the down items of minibatch m come after the up items of m + lag, half the
+  // ring ahead; a slot is reused n_slots minibatches later, so lag < n_slots
+  L.lag = L.n_slots >= 2 ? L.n_slots / 2 : 0;
   L.Hld = std::max(a->I, I_sh);
   const size_t es = a->dtype == MOK_FP32 ? 4 : 2;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-  gemm_tile_caps(L.max_mb, mb, a->I, I_sh, a->d, &L.cap_u, &L.cap_d);
-  L.wl = take(sizeof(int32_t) * worklist_ints(L.max_mb, L.cap_u, L.cap_d));
+  gemm_tile_caps(L.max_mb, mb, a->I, I_sh, a->d, L.use_ring && a->dtype == MOK_MXFP8, &L.cap_u,
+                 &L.cap_d, &L.cap_g);
+  L.cap_r = L.use_ring ? L.cap_u + L.cap_d + L.cap_g : 0;
+  L.wl = take(sizeof(int32_t) * worklist_ints(L.max_mb, L.cap_u, L.cap_d, L.cap_r));
   const bool route = a->w_router != nullptr;
   L.logits = (route && !a->logits_out) ? take(sizeof(float) * a->T_pool * a->E) : 0;
   L.idx = (route && !a->topk_idx_out) ? take(sizeof(int32_t) * a->T_pool * a->k) : 0;
@@ -268,6 +273,9 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.max_mb = L.max_mb;
   p.cap_u = L.cap_u;
   p.cap_d = L.cap_d;
+  p.cap_r = L.cap_r;
+  p.ring = L.use_ring;
+  p.lag = L.lag;
   p.grid = ((device_cus() + 7) / 8) * 8;   // one 256 x 256 tile workgroup per CU
   p.x = a->x;
   p.route_ids = route_ids;

@@ -30,22 +30,32 @@
 namespace mok {
 
 // ------------------------------------------------------------------------- work list
-// int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, and the
-// prefix sums of its up and down tiles; then, 16-byte aligned, one int4 per up tile and per
-// down tile {minibatch, tile within it, first row, group << 16 | rows} so that a workgroup
-// finds its tile with a single load.
-constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_TICKET = 3, WL_ERR = 4, WL_HDR = 16;
+// int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, the
+// prefix sums of its gather, up and down items, and three completion counters; then, 16-byte
+// aligned, one int4 per up tile and per down tile {minibatch, tile within it, first row,
+// group << 16 | rows} so that a workgroup finds its tile with a single load, and (ring work
+// loop only) the ring order of all items, the item kind in bits 28+ of the second field.
+constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_TICKET = 3, WL_ERR = 4, WL_N_R = 5,
+              WL_HDR = 16;
+constexpr uint32_t ERR_OVERFLOW = 1u, ERR_WAIT = 2u;
+constexpr int KIND_U = 0, KIND_D = 1, KIND_G = 2, KIND_SHIFT = 28;
+constexpr int G_ROWS = 64;      // rows of one gather + quantise item of the ring loop
 MOK_DEV int32_t* wl_group(int32_t* wl, int cap) { return wl + WL_HDR; }
 MOK_DEV int32_t* wl_row0(int32_t* wl, int cap) { return wl + WL_HDR + cap; }
 MOK_DEV int32_t* wl_rows(int32_t* wl, int cap) { return wl + WL_HDR + 2 * cap; }
 MOK_DEV int32_t* wl_ustart(int32_t* wl, int cap) { return wl + WL_HDR + 3 * cap; }
 MOK_DEV int32_t* wl_dstart(int32_t* wl, int cap) { return wl + WL_HDR + 4 * cap + 1; }
-MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 5 * (size_t)cap + 2 + 3) & ~(size_t)3; }
+MOK_DEV int32_t* wl_gstart(int32_t* wl, int cap) { return wl + WL_HDR + 5 * cap + 2; }
+MOK_DEV int32_t* wl_done(int32_t* wl, int cap, int kind) { return wl + WL_HDR + (6 + kind) * cap + 3; }
+MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 9 * (size_t)cap + 3 + 3) & ~(size_t)3; }
 MOK_DEV int4* wl_utab(int32_t* wl, int cap) { return (int4*)(wl + wl_tab_off(cap)); }
 MOK_DEV int4* wl_dtab(int32_t* wl, int cap, int cap_u) { return (int4*)(wl + wl_tab_off(cap)) + cap_u; }
+MOK_DEV int4* wl_rtab(int32_t* wl, int cap, int cap_u, int cap_d) {
+  return (int4*)(wl + wl_tab_off(cap)) + cap_u + cap_d;
+}
 
-size_t worklist_ints(int max_mb, int cap_u, int cap_d) {
-  return wl_tab_off(max_mb) + 4 * ((size_t)cap_u + (size_t)cap_d);
+size_t worklist_ints(int max_mb, int cap_u, int cap_d, int cap_r) {
+  return wl_tab_off(max_mb) + 4 * ((size_t)cap_u + (size_t)cap_d + (size_t)cap_r);
 }
 
 // Block-wide exclusive scan of one int per thread (1024 threads). Returns the exclusive
@@ -66,11 +76,21 @@ MOK_DEV int32_t block_excl_scan_1024(int32_t v, int32_t* sh, int32_t* total) {
   return incl - v;
 }
 
+// One workgroup of 1024 threads. Minibatches: routed experts ascending (rows ascending within
+// each plan region), then the shared experts' minibatches over the own tokens. Every count
+// comes from the plan on the device; nothing returns to the host.
+//
+// Ring order (ring = true): block b holds the gather items of minibatch b (MXFP8 only), its up
+// tiles, then the down tiles of minibatch b - lag. A down item needs every up tile of its
+// minibatch; an up item needs its gather items and the down items of minibatch m - n_slots
+// (whose ring slot it reuses); a gather item needs the up items of m - n_slots. With
+// lag < n_slots every dependency of an item lies earlier in this order.
 __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restrict__ counts,
                                                          const int32_t* __restrict__ offsets,
                                                          int E_l, int T_own, int mb, int bm,
-                                                         int nU_r, int nU_s, int nD, int cap,
-                                                         int cap_u, int cap_d,
+                                                         int nU_r, int nU_s, int nD, bool gather,
+                                                         bool ring, int lag, int cap, int cap_u,
+                                                         int cap_d, int cap_r,
                                                          int32_t* __restrict__ wl) {
   __shared__ int32_t sh[1024];
   const int t = threadIdx.x;
@@ -79,6 +99,7 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
   int32_t* nr = wl_rows(wl, cap);
   int32_t* us = wl_ustart(wl, cap);
   int32_t* ds = wl_dstart(wl, cap);
+  int32_t* gs = wl_gstart(wl, cap);
   // routed minibatches: experts ascending, rows ascending within each region
   int32_t n_routed = 0;
   for (int c0 = 0; c0 < E_l; c0 += 1024) {
@@ -107,48 +128,71 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     }
   }
   const int32_t n_mb = min(cap, n_routed + n_sh);
+  for (int m = t; m < cap; m += 1024) {
+    wl_done(wl, cap, KIND_U)[m] = 0;
+    wl_done(wl, cap, KIND_D)[m] = 0;
+    wl_done(wl, cap, KIND_G)[m] = 0;
+  }
   __syncthreads();
-  // tile prefix sums: tiles of a minibatch = ceil(rows / bm) * n-tiles of its stage
-  int32_t carry_u = 0, carry_d = 0;
+  // item prefix sums: tiles of a minibatch = ceil(rows / bm) * n-tiles of its stage
+  int32_t carry_u = 0, carry_d = 0, carry_g = 0;
   for (int c0 = 0; c0 < n_mb; c0 += 1024) {
     const int m = c0 + t;
-    int32_t nu = 0, nd = 0;
+    int32_t nu = 0, nd = 0, ng = 0;
     if (m < n_mb) {
       const int32_t mt = (nr[m] + bm - 1) / bm;
       nu = mt * (grp[m] < E_l ? nU_r : nU_s);
       nd = mt * nD;
+      ng = gather ? (nr[m] + G_ROWS - 1) / G_ROWS : 0;
     }
-    int32_t tu, td;
+    int32_t tu, td, tg;
     const int32_t eu = block_excl_scan_1024(nu, sh, &tu);
     const int32_t ed = block_excl_scan_1024(nd, sh, &td);
+    const int32_t eg = block_excl_scan_1024(ng, sh, &tg);
     if (m < n_mb) {
       us[m] = carry_u + eu;
       ds[m] = carry_d + ed;
+      gs[m] = carry_g + eg;
     }
     carry_u += tu;
     carry_d += td;
+    carry_g += tg;
   }
-  const bool overflow = n_routed + n_sh > cap || carry_u > cap_u || carry_d > cap_d;
+  const bool overflow = n_routed + n_sh > cap || carry_u > cap_u || carry_d > cap_d ||
+                        (ring && (int64_t)carry_u + carry_d + carry_g > cap_r);
   if (t == 0) {
     us[n_mb] = carry_u;
     ds[n_mb] = carry_d;
+    gs[n_mb] = carry_g;
     wl[WL_N_MB] = n_mb;
     wl[WL_N_U] = overflow ? 0 : carry_u;
     wl[WL_N_D] = overflow ? 0 : carry_d;
+    wl[WL_N_R] = (overflow || !ring) ? 0 : carry_u + carry_d + carry_g;
     wl[WL_TICKET] = 0;
-    wl[WL_ERR] = overflow ? 1 : 0;
+    wl[WL_ERR] = overflow ? ERR_OVERFLOW : 0;
   }
   __syncthreads();
   if (overflow) return;
   // tile tables (tiles of a minibatch: n-tile major, m-tile minor)
   int4* ut = wl_utab(wl, cap);
   int4* dt = wl_dtab(wl, cap, cap_u);
+  int4* rt = wl_rtab(wl, cap, cap_u, cap_d);
   for (int m = t; m < n_mb; m += 1024) {
     const int32_t g = grp[m], rw = nr[m], first = r0[m];
     const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
-    const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m];
+    const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m], ng = gs[m + 1] - gs[m];
     for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = l; ut[us[m] + l] = e; }
     for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = l; dt[ds[m] + l] = e; }
+    if (ring) {
+      const int mb_lag = max(0, m - lag);
+      const int after = min(m + lag + 1, n_mb);
+      const int32_t pos_g = gs[m] + us[m] + ds[mb_lag];
+      const int32_t pos_u = gs[m + 1] + us[m] + ds[mb_lag];
+      const int32_t pos_d = gs[after] + us[after] + ds[m];
+      for (int l = 0; l < ng; ++l) { int4 e = e0; e.y = (KIND_G << KIND_SHIFT) | l; rt[pos_g + l] = e; }
+      for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = (KIND_U << KIND_SHIFT) | l; rt[pos_u + l] = e; }
+      for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = (KIND_D << KIND_SHIFT) | l; rt[pos_d + l] = e; }
+    }
   }
 }
 
@@ -685,29 +729,33 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   __syncthreads();  // LDS (row table, operand buffers) is reused by the next tile
 }
 
+// LDS of a tile workgroup: the STAGES operand buffers as separate objects (only the first
+// STAGES are referenced), the MX scale words and the down stage's row table.
+#define MOK_TILE_LDS(C, sm)                                                                      \
+  __shared__ uint4 a0[C::BM][C::CH], a1[C::BM][C::CH], b0[C::BN][C::CH], b1[C::BN][C::CH];       \
+  __shared__ uint4 a2[C::STAGES > 2 ? C::BM : 1][C::CH], a3[C::STAGES > 2 ? C::BM : 1][C::CH];   \
+  __shared__ uint4 b2[C::STAGES > 2 ? C::BN : 1][C::CH], b3[C::STAGES > 2 ? C::BN : 1][C::CH];   \
+  __shared__ uint32_t as0[C::BM], as1[C::BM], bs0[C::BN], bs1[C::BN];                            \
+  __shared__ uint32_t as2[C::STAGES > 2 ? C::BM : 1], as3[C::STAGES > 2 ? C::BM : 1];            \
+  __shared__ uint32_t bs2[C::STAGES > 2 ? C::BN : 1], bs3[C::STAGES > 2 ? C::BN : 1];            \
+  __shared__ int32_t row_dst[C::BM];                                                             \
+  __shared__ float row_w[C::BM];                                                                 \
+  Lds<C> sm;                                                                                     \
+  sm.buf[0].A = a0; sm.buf[0].B = b0; sm.buf[0].As = as0; sm.buf[0].Bs = bs0;                    \
+  sm.buf[1].A = a1; sm.buf[1].B = b1; sm.buf[1].As = as1; sm.buf[1].Bs = bs1;                    \
+  if constexpr (C::STAGES > 2) {                                                                 \
+    sm.buf[2].A = a2; sm.buf[2].B = b2; sm.buf[2].As = as2; sm.buf[2].Bs = bs2;                  \
+    sm.buf[3].A = a3; sm.buf[3].B = b3; sm.buf[3].As = as3; sm.buf[3].Bs = bs3;                  \
+  }                                                                                              \
+  sm.row_dst = row_dst;                                                                          \
+  sm.row_w = row_w
+
 // Stage kernel: the workgroups walk the stage's tiles; consecutive tile ids land on the same
 // XCD (workgroups are dispatched round-robin over the 8 XCDs), so tiles that share operand
 // rows share that XCD's L2.
 template <Elem EL, bool UP, bool F32OUT, class C>
 __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
-  // LDS: the STAGES buffers as separate objects (only the first STAGES are referenced)
-  __shared__ uint4 a0[C::BM][C::CH], a1[C::BM][C::CH], b0[C::BN][C::CH], b1[C::BN][C::CH];
-  __shared__ uint4 a2[C::STAGES > 2 ? C::BM : 1][C::CH], a3[C::STAGES > 2 ? C::BM : 1][C::CH];
-  __shared__ uint4 b2[C::STAGES > 2 ? C::BN : 1][C::CH], b3[C::STAGES > 2 ? C::BN : 1][C::CH];
-  __shared__ uint32_t as0[C::BM], as1[C::BM], bs0[C::BN], bs1[C::BN];
-  __shared__ uint32_t as2[C::STAGES > 2 ? C::BM : 1], as3[C::STAGES > 2 ? C::BM : 1];
-  __shared__ uint32_t bs2[C::STAGES > 2 ? C::BN : 1], bs3[C::STAGES > 2 ? C::BN : 1];
-  __shared__ int32_t row_dst[C::BM];
-  __shared__ float row_w[C::BM];
-  Lds<C> sm;
-  sm.buf[0].A = a0; sm.buf[0].B = b0; sm.buf[0].As = as0; sm.buf[0].Bs = bs0;
-  sm.buf[1].A = a1; sm.buf[1].B = b1; sm.buf[1].As = as1; sm.buf[1].Bs = bs1;
-  if constexpr (C::STAGES > 2) {
-    sm.buf[2].A = a2; sm.buf[2].B = b2; sm.buf[2].As = as2; sm.buf[2].Bs = bs2;
-    sm.buf[3].A = a3; sm.buf[3].B = b3; sm.buf[3].As = as3; sm.buf[3].Bs = bs3;
-  }
-  sm.row_dst = row_dst;
-  sm.row_w = row_w;
+  MOK_TILE_LDS(C, sm);
   const int cap = p.max_mb;
   const int32_t total = p.wl[UP ? WL_N_U : WL_N_D];
   const int4* tab = UP ? wl_utab(p.wl, cap) : wl_dtab(p.wl, cap, p.cap_u);
@@ -726,29 +774,140 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
 }
 
 // ------------------------------------------------------------------------- MXFP8 gather
-// Pull-gather + quantise: the A rows of every minibatch (token rows of the pool picked by
-// route id, or the own rows for the shared experts) become MXFP8 rows of its ring slot.
-// One wave per row; lane i quantises blocks i, i+64, ... of the row.
-__global__ __launch_bounds__(256) void k_gather_quantize(ExpertPass p) {
+// Pull-gather + quantise of rows [r_begin, r_end) of minibatch m: the token rows of the pool
+// picked by route id (or the own rows, for the shared experts) become MXFP8 rows of the
+// minibatch's ring slot. One wave per row; lane i quantises blocks i, i+64, ... of the row.
+MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r_end, int wave,
+                                  int n_waves) {
   const int cap = p.max_mb;
-  const int n_mb = p.wl[WL_N_MB];
-  const int32_t* grp = wl_group(p.wl, cap);
-  const int32_t* r0 = wl_row0(p.wl, cap);
-  const int32_t* nr = wl_rows(p.wl, cap);
+  const int32_t g = wl_group(p.wl, cap)[m], first = wl_row0(p.wl, cap)[m];
   const int nbr = p.d / 32;
   const int lane = threadIdx.x & 63;
-  const int64_t total_rows = (int64_t)n_mb * p.mb;
-  for (int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); q < total_rows;
-       q += (int64_t)gridDim.x * 4) {
-    const int m = (int)(q / p.mb), r = (int)(q % p.mb);
-    if (r >= nr[m]) continue;
-    const int64_t tok = grp[m] >= p.E_l ? p.own_begin + r0[m] + r
-                                        : (int64_t)(p.route_ids[r0[m] + r] / p.k);
+  for (int r = r_begin + wave; r < r_end; r += n_waves) {
+    const int64_t tok = g >= p.E_l ? p.own_begin + first + r
+                                   : (int64_t)(p.route_ids[first + r] / p.k);
     const int64_t ring_row = (int64_t)(m % p.n_slots) * p.mb + r;
     const bf16_t* src = (const bf16_t*)p.x + tok * p.d;
     for (int b = lane; b < nbr; b += 64)
       quantize_block32(src + 32 * b, p.A_codes + ring_row * p.d + 32 * b,
                        p.A_sc + ring_row * nbr + b);
+  }
+}
+
+// Stage-ordered path: every minibatch's rows, before the up stage.
+__global__ __launch_bounds__(256) void k_gather_quantize(ExpertPass p) {
+  const int n_mb = p.wl[WL_N_MB];
+  const int32_t* nr = wl_rows(p.wl, p.max_mb);
+  const int per_block = 4 * 8;                  // rows per workgroup per minibatch pass
+  const int chunks = (p.mb + per_block - 1) / per_block;
+  for (int64_t q = blockIdx.x; q < (int64_t)n_mb * chunks; q += gridDim.x) {
+    const int m = (int)(q / chunks), c = (int)(q % chunks);
+    const int r0 = c * per_block, r1 = min(nr[m], r0 + per_block);
+    if (r0 < r1) gather_quantize_rows(p, m, r0, r1, threadIdx.x >> 6, 4);
+  }
+}
+
+// ------------------------------------------------------------------------- ring work loop
+// Persistent loop over the ring order built by k_build_worklist: each workgroup takes the next
+// item with a ticket (an integer atomic: which workgroup runs an item never changes what the
+// item computes), waits until the item's inputs are complete, runs it and counts it complete.
+// Waits are bounded: one that runs out sets ERR_WAIT in the error word and goes on, so the
+// loop always drains. Completion is published with an agent-scope release (the workgroup's
+// stores written back from its XCD's L2) and observed with an agent-scope acquire, since the
+// producer and the consumer of a ring slot may sit on different XCDs.
+constexpr uint32_t kSpinLimit = 1u << 20;   // ~1 s: far above any legitimate wait
+
+// Spin until *ctr >= need. Gives up (setting ERR_WAIT) after kSpinLimit polls, or at once once
+// another wait has given up, so a broken dependency costs about one limit in total. Run by a
+// whole wave: every value it branches on is made wave-uniform first.
+MOK_DEV void wait_count(const int32_t* ctr, int32_t need, int32_t* err) {
+  for (uint32_t it = 0;; ++it) {
+    const int32_t v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v >= need) return;
+    if ((it & 255u) == 255u) {
+      const int32_t e = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (e & (int32_t)ERR_WAIT) return;
+    }
+    if (it >= kSpinLimit) {
+      // one lane sets the bit (the others or in 0)
+      __hip_atomic_fetch_or(err, (threadIdx.x & 63) == 0 ? (int32_t)ERR_WAIT : 0, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The loop's control flow is wave-uniform everywhere: wave 0 as a whole takes the ticket, waits
+// and publishes completion (lane 0 contributes the atomic increments, the other lanes add 0), and
+// every field of the item is read back with readfirstlane. A lane-divergent branch here would let
+// the compiler merge the publish of one item with the ticket of the next across the loop's
+// back-edge, leaving the rest of wave 0 to pass the item barrier without lane 0.
+template <Elem EL, bool F32OUT, class C>
+__global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
+  MOK_TILE_LDS(C, sm);
+  __shared__ int4 item;
+  const int cap = p.max_mb;
+  int32_t* wl = p.wl;
+  const int32_t total = wl[WL_N_R];
+  const int4* rt = wl_rtab(wl, cap, p.cap_u, p.cap_d);
+  const int32_t* us = wl_ustart(wl, cap);
+  const int32_t* ds = wl_dstart(wl, cap);
+  const int32_t* gs = wl_gstart(wl, cap);
+  int32_t* done_u = wl_done(wl, cap, KIND_U);
+  int32_t* done_d = wl_done(wl, cap, KIND_D);
+  int32_t* done_g = wl_done(wl, cap, KIND_G);
+  const int S = p.n_slots;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t one = (threadIdx.x & 63) == 0 ? 1 : 0;
+  for (;;) {
+    if (wid == 0) {
+      const int32_t t = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+          &wl[WL_TICKET], one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      int4 e = make_int4(-1, 0, 0, 0);
+      if (t < total) {
+        e = rt[t];
+        const int m = __builtin_amdgcn_readfirstlane(e.x);
+        const int kind = __builtin_amdgcn_readfirstlane(e.y) >> KIND_SHIFT;
+        if (kind == KIND_D) {
+          wait_count(&done_u[m], us[m + 1] - us[m], &wl[WL_ERR]);
+        } else if (kind == KIND_U) {
+          wait_count(&done_g[m], gs[m + 1] - gs[m], &wl[WL_ERR]);
+          if (m >= S) wait_count(&done_d[m - S], ds[m - S + 1] - ds[m - S], &wl[WL_ERR]);
+        } else if (m >= S) {
+          wait_count(&done_u[m - S], us[m - S + 1] - us[m - S], &wl[WL_ERR]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      item = e;                                   // every lane of wave 0 stores the same value
+    }
+    __syncthreads();
+    int4 e;
+    e.x = __builtin_amdgcn_readfirstlane(item.x);
+    e.y = __builtin_amdgcn_readfirstlane(item.y);
+    e.z = __builtin_amdgcn_readfirstlane(item.z);
+    e.w = __builtin_amdgcn_readfirstlane(item.w);
+    if (e.x < 0) break;
+    const int kind = e.y >> KIND_SHIFT;
+    e.y &= (1 << KIND_SHIFT) - 1;
+    if (kind == KIND_U) {
+      run_tile<EL, true, F32OUT, C>(p, sm, e);
+    } else if (kind == KIND_D) {
+      run_tile<EL, false, F32OUT, C>(p, sm, e);
+    } else if constexpr (EL == Elem::FP8) {
+      const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
+      gather_quantize_rows(p, e.x, r0, r1, wid, C::NW);
+    }
+    // every wave's stores have reached L2; then one release covers the workgroup's item
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (wid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      int32_t* ctr = kind == KIND_U ? done_u : (kind == KIND_D ? done_d : done_g);
+      __hip_atomic_fetch_add(&ctr[e.x], one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -807,6 +966,15 @@ static void record(void* const* ev, int i, hipStream_t s) {
 
 template <Elem EL, bool F32OUT>
 static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
+  if (p.ring) {
+    hipLaunchKernelGGL((k_ring<EL, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
+    record(ev, 2 * 3 + 1, s);
+    record(ev, 2 * 4, s);
+    record(ev, 2 * 4 + 1, s);
+    return hipGetLastError();
+  }
+  if (EL == Elem::FP8)
+    hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);
   hipLaunchKernelGGL((k_expert_stage<EL, true, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
   record(ev, 2 * 3 + 1, s);
   record(ev, 2 * 4, s);
@@ -815,12 +983,14 @@ static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* cons
   return hipGetLastError();
 }
 
-void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, int* cap_u, int* cap_d) {
+void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, bool gather_items, int* cap_u,
+                    int* cap_d, int* cap_g) {
   const int64_t mt = (mb + Big::BM - 1) / Big::BM;
   const int64_t nU = std::max((I + Big::BN / 2 - 1) / (Big::BN / 2), (I_sh + Big::BN / 2 - 1) / (Big::BN / 2));
   const int64_t nD = (d + Big::BN - 1) / Big::BN;
   *cap_u = (int)std::min<int64_t>(INT32_MAX / 8, (int64_t)max_mb * mt * nU);
   *cap_d = (int)std::min<int64_t>(INT32_MAX / 8, (int64_t)max_mb * mt * nD);
+  *cap_g = gather_items ? (int)std::min<int64_t>(INT32_MAX / 8, (int64_t)max_mb * ((mb + G_ROWS - 1) / G_ROWS)) : 0;
 }
 
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev) {
@@ -828,11 +998,12 @@ hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const*
   const int nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nD = (p.d + Big::BN - 1) / Big::BN;
   record(ev, 2 * 3, s);
+  const bool gather_items = p.ring && p.elem == Elem::FP8;
   hipLaunchKernelGGL(k_build_worklist, dim3(1), dim3(1024), 0, s, p.counts, p.offsets, p.E_l,
-                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, p.max_mb, p.cap_u, p.cap_d, p.wl);
+                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.lag,
+                     p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
-  hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);
   return launch_stages_t<Elem::FP8, false>(p, s, ev);
 }
 

@@ -37,6 +37,9 @@ struct ExpertPass {
   int Hld;               // ring row length in elements: max(I, I_sh)
   int max_mb;            // capacity of the minibatch tables
   int cap_u, cap_d;      // capacity of the up / down tile tables
+  int cap_r;             // capacity of the ring-order table (ring work loop), else 0
+  bool ring;             // persistent ring work loop (else stage-ordered launches)
+  int lag;               // ring order: down items of minibatch m follow the up items of m + lag
   int bm, bn;            // GEMM tile (rows, B-tile rows)
   int grid;              // workgroups of the tile loops
   // inputs
@@ -60,10 +63,13 @@ struct ExpertPass {
   void* y_shared;
 };
 
-size_t worklist_ints(int max_mb, int cap_u, int cap_d);
-void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, int* cap_u, int* cap_d);
+size_t worklist_ints(int max_mb, int cap_u, int cap_d, int cap_r);
+// Tile-table capacities for max_mb minibatches of mb rows; cap_g: gather items of the ring loop
+// (MXFP8 only, else 0).
+void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, bool gather_items, int* cap_u,
+                    int* cap_d, int* cap_g);
 // ev: optional hipEvent_t[2 * 6] (mok stage events); records UP around the work list, gather
-// and up stage, DOWN around the down stage.
+// and up stage, DOWN around the down stage (ring loop: UP around everything, DOWN empty).
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev);
 hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, int64_t n_tok,
                           int k, int d, bool f32, hipStream_t s);
