@@ -6,151 +6,115 @@
 // it is computed on the VALU as one float32 fused multiply-add chain per logit, over the
 // model dim in ascending order: the result is reproducible bit for bit. At the layer's sizes
 // it is ~0.2% of the layer's FLOPs.
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace mok {
 
 // ----------------------------------------------------------------------------- logits
-// Workgroup tile: 32 tokens x 64 experts, 256 threads as 16 x 16; thread (tt, te) owns tokens
-// tt + 16a (a < 2) and experts te + 16b (b < 4): 8 independent chains. The d loop runs in
-// chunks of 64 staged through two LDS buffers (float32); the next chunk's global loads are
-// in flight while the current one is consumed 4 values of i at a time (float4 LDS reads).
-// Every chain takes i strictly in ascending order, one FMA per step.
-constexpr int RT_T = 32, RT_E = 64, RT_K = 64, RT_LD = RT_K + 4;
+// One wave: 64 tokens (one per lane) x 8 experts. Per chunk of 16 values of i, lane r*16 + j
+// (4 rows of 16 lanes) holds W_r[e][i0 + j] as float32 for each of the wave's 8 experts (one
+// 2-byte load and one shift per expert), and its own token's 16 values of x. The FMA of step
+// i0 + j takes W_r[e][i0 + j] straight from lane j of the lane's row (DPP row_newbcast), so one
+// VALU instruction is one step of one chain for 64 tokens. The next chunk's loads are in flight
+// while a chunk computes. Every chain takes i strictly in ascending order from +0.
+constexpr int RT_TOK = 64, RT_EXP = 8, RT_K = 16;
 
-template <class T> struct Stage;
-template <> struct Stage<bf16_t> {   // 8 bf16 per 16-byte load
-  static constexpr int V = 8;
-  typedef uint4 Raw;
-  static MOK_DEV void cvt(const Raw& r, float* dst) {
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      dst[2 * q] = __uint_as_float(w[q] << 16);
-      dst[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-    }
+// acc = fma(w of lane J of this 16-lane row, x, acc): the product is exact either way round.
+template <int J>
+MOK_DEV void fma_bcast(float& acc, float w, float x) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc) : "v"(w), "v"(x), "i"(J));
+}
+
+template <class T> struct RowChunk;      // 16 consecutive values of a row
+template <> struct RowChunk<bf16_t> {
+  uint4 r[2];
+  MOK_DEV void load(const bf16_t* p) { r[0] = *(const uint4*)p; r[1] = *(const uint4*)(p + 8); }
+  MOK_DEV float get(int q) const {     // q compile-time after unrolling
+    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+    return (q & 1) ? __uint_as_float(w[q >> 1] & 0xFFFF0000u) : __uint_as_float(w[q >> 1] << 16);
   }
 };
-template <> struct Stage<float> {    // 4 floats per 16-byte load
-  static constexpr int V = 4;
-  typedef float4 Raw;
-  static MOK_DEV void cvt(const Raw& r, float* dst) {
-    dst[0] = r.x; dst[1] = r.y; dst[2] = r.z; dst[3] = r.w;
+template <> struct RowChunk<float> {
+  float4 r[4];
+  MOK_DEV void load(const float* p) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *(const float4*)(p + 4 * q);
+  }
+  MOK_DEV float get(int q) const {
+    const float4 v = r[q >> 2];
+    return (q & 3) == 0 ? v.x : (q & 3) == 1 ? v.y : (q & 3) == 2 ? v.z : v.w;
   }
 };
 
-// Global -> registers for rows [r0, r0 + ROWS) x cols [k0, k0 + 64) of a [n_rows, d] matrix;
-// vector loads when the row chunk is whole and aligned, element loads otherwise (zero fill).
-template <class T, int ROWS>
-struct ChunkLoader {
-  static constexpr int V = Stage<T>::V, PER_ROW = RT_K / V, N = ROWS * PER_ROW / 256;
-  typename Stage<T>::Raw raw[N];
-  float tail[N][Stage<T>::V];
-  bool vec[N];
-  MOK_DEV void load(const T* __restrict__ src, int64_t n_rows, int d, int64_t r0, int k0) {
+template <class T, int J>
+MOK_DEV void chunk_step(float (&acc)[RT_EXP], const float (&wv)[RT_EXP], const RowChunk<T>& xc) {
+  const float xj = xc.get(J);
 #pragma unroll
-    for (int q = 0; q < N; ++q) {
-      const int idx = threadIdx.x + 256 * q;
-      const int r = idx / PER_ROW, c = (idx % PER_ROW) * V;
-      const int64_t row = r0 + r;
-      vec[q] = row < n_rows && k0 + c + V <= d && (d % V) == 0;
-      if (vec[q]) {
-        raw[q] = *(const typename Stage<T>::Raw*)(src + row * d + k0 + c);
-      } else {
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-          tail[q][v] = (row < n_rows && k0 + c + v < d) ? load_as_f32<T>(src + row * d + k0 + c + v) : 0.0f;
-      }
-    }
-  }
-  MOK_DEV void store(float (*dst)[RT_LD]) const {
-#pragma unroll
-    for (int q = 0; q < N; ++q) {
-      const int idx = threadIdx.x + 256 * q;
-      const int r = idx / PER_ROW, c = (idx % PER_ROW) * V;
-      float v[V];
-      if (vec[q]) Stage<T>::cvt(raw[q], v);
-      else
-#pragma unroll
-        for (int e = 0; e < V; ++e) v[e] = tail[q][e];
-#pragma unroll
-      for (int e = 0; e < V; e += 4) *(float4*)&dst[r][c + e] = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
-    }
-  }
-};
+  for (int e = 0; e < RT_EXP; ++e) fma_bcast<J>(acc[e], wv[e], xj);
+}
+
+template <class T, int... J>
+MOK_DEV void chunk_all(float (&acc)[RT_EXP], const float (&wv)[RT_EXP], const RowChunk<T>& xc,
+                       std::integer_sequence<int, J...>) {
+  (chunk_step<T, J>(acc, wv, xc), ...);
+}
 
 template <class T>
 __global__ __launch_bounds__(256) void k_router_logits(const T* __restrict__ x,
                                                        const T* __restrict__ wr, int64_t n_tok,
                                                        int d, int E, float* __restrict__ logits) {
-  __shared__ __align__(16) float xs[2][RT_T][RT_LD];
-  __shared__ __align__(16) float ws[2][RT_E][RT_LD];
-  const int tid = threadIdx.x;
-  const int te = tid & 15, tt = tid >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * RT_T;
-  const int e0 = blockIdx.y * RT_E;
-  float acc[2][4] = {};
-  ChunkLoader<T, RT_T> lx;
-  ChunkLoader<T, RT_E> lw;
-  lx.load(x, n_tok, d, t0, 0);
-  lw.load(wr, E, d, e0, 0);
-  lx.store(xs[0]);
-  lw.store(ws[0]);
-  __syncthreads();
-  const int n_chunks = (d + RT_K - 1) / RT_K;
-  for (int ck = 0; ck < n_chunks; ++ck) {
-    const int cur = ck & 1;
-    const int k0 = ck * RT_K;
-    if (ck + 1 < n_chunks) {
-      lx.load(x, n_tok, d, t0, k0 + RT_K);
-      lw.load(wr, E, d, e0, k0 + RT_K);
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int n_eg = (E + RT_EXP - 1) / RT_EXP;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t tb = wave / n_eg;
+  const int e0 = uniform((int)(wave % n_eg) * RT_EXP);
+  if (tb * RT_TOK >= n_tok) return;
+  const int64_t t = tb * RT_TOK + lane;
+  const T* xr = x + min(t, n_tok - 1) * (int64_t)d;
+  const T* wrow[RT_EXP];
+#pragma unroll
+  for (int e = 0; e < RT_EXP; ++e) wrow[e] = wr + (int64_t)min(e0 + e, E - 1) * d;
+  float acc[RT_EXP];
+#pragma unroll
+  for (int e = 0; e < RT_EXP; ++e) acc[e] = 0.0f;
+  const int dv = (d % RT_K) == 0 ? d : 0;          // whole 16-value chunks (aligned rows)
+  // chunk loads: x from the lane's row; W_r value j of each expert row, at a uniform base plus a
+  // 32-bit lane offset. Two named buffers alternate so the next chunk's loads are in flight
+  // while the current one computes (the scheduling barriers keep that order).
+  auto load = [&](RowChunk<T>& xc, float (&wv)[RT_EXP], int i0) {
+    xc.load(xr + i0);
+#pragma unroll
+    for (int e = 0; e < RT_EXP; ++e)
+      wv[e] = load_as_f32<T>((const T*)((const char*)wrow[e] + (uint32_t)((i0 + j) * sizeof(T))));
+  };
+  if (dv > 0) {
+    RowChunk<T> xa, xb;
+    float wa[RT_EXP], wb[RT_EXP];
+    load(xa, wa, 0);
+    for (int i0 = 0; i0 < dv; i0 += 2 * RT_K) {
+      load(xb, wb, min(i0 + RT_K, dv - RT_K));
+      __builtin_amdgcn_sched_barrier(0);
+      chunk_all<T>(acc, wa, xa, std::make_integer_sequence<int, RT_K>{});
+      __builtin_amdgcn_sched_barrier(0);
+      load(xa, wa, min(i0 + 2 * RT_K, dv - RT_K));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i0 + RT_K < dv) chunk_all<T>(acc, wb, xb, std::make_integer_sequence<int, RT_K>{});
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const int kn = min(RT_K, d - k0);
-    for (int i = 0; i < kn; i += 4) {
-      float4 xa[2], wb[4];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) xa[a] = *(const float4*)&xs[cur][tt + 16 * a][i];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) wb[b] = *(const float4*)&ws[cur][te + 16 * b][i];
-      if (i + 4 <= kn) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            float c = acc[a][b];
-            c = __builtin_fmaf(xa[a].x, wb[b].x, c);
-            c = __builtin_fmaf(xa[a].y, wb[b].y, c);
-            c = __builtin_fmaf(xa[a].z, wb[b].z, c);
-            c = __builtin_fmaf(xa[a].w, wb[b].w, c);
-            acc[a][b] = c;
-          }
-      } else {  // d % 4 != 0: the last kn - i < 4 steps one at a time (no padding term enters)
-        const float xv[2][4] = {{xa[0].x, xa[0].y, xa[0].z, xa[0].w}, {xa[1].x, xa[1].y, xa[1].z, xa[1].w}};
-        const float wv[4][4] = {{wb[0].x, wb[0].y, wb[0].z, wb[0].w}, {wb[1].x, wb[1].y, wb[1].z, wb[1].w},
-                                {wb[2].x, wb[2].y, wb[2].z, wb[2].w}, {wb[3].x, wb[3].y, wb[3].z, wb[3].w}};
-        for (int q = 0; q < kn - i; ++q)
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(xv[a][q], wv[b][q], acc[a][b]);
-      }
-    }
-    if (ck + 1 < n_chunks) {
-      lx.store(xs[cur ^ 1]);
-      lw.store(ws[cur ^ 1]);
-    }
-    __syncthreads();
   }
+  for (int i = dv; i < d; ++i) {                   // rows that are not whole 16-value chunks
+    const float xi = load_as_f32<T>(xr + i);
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int64_t t = t0 + tt + 16 * a;
-    if (t >= n_tok) continue;
+    for (int e = 0; e < RT_EXP; ++e) acc[e] = __builtin_fmaf(xi, load_as_f32<T>(wrow[e] + i), acc[e]);
+  }
+  if (t < n_tok) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int e = e0 + te + 16 * b;
-      if (e < E) logits[t * E + e] = acc[a][b];
-    }
+    for (int e = 0; e < RT_EXP; ++e)
+      if (e0 + e < E) logits[t * E + e0 + e] = acc[e];
   }
 }
 
@@ -220,7 +184,8 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 hipError_t launch_router_logits(const void* x, const void* wr, int64_t n_tok, int d, int E,
                                 bool bf16, float* logits, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
-  dim3 grid((unsigned)((n_tok + RT_T - 1) / RT_T), (unsigned)((E + RT_E - 1) / RT_E));
+  const int64_t waves = ((n_tok + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
+  const dim3 grid((unsigned)((waves + 3) / 4));
   if (bf16)
     hipLaunchKernelGGL(k_router_logits<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
                        (const bf16_t*)wr, n_tok, d, E, logits);
