@@ -115,26 +115,34 @@ MOK_DEV uint32_t e4m3_encode(float v, int s) {
   return sign | ((uint32_t)ef << 3) | (q - 8);
 }
 
-// One 32-element block of bf16 -> 32 E4M3 code bytes + 1 E8M0 scale byte (16 B aligned).
-MOK_DEV void quantize_block32(const bf16_t* __restrict__ src, uint8_t* __restrict__ codes,
-                              uint8_t* __restrict__ scale) {
-  uint4 raw[4];
+// Eight consecutive elements (one 16-byte load of bf16) of a 32-element block held by one lane;
+// the block's four lanes are an aligned quad (lanes 4g .. 4g + 3). The shared exponent comes
+// from the quad's amax; each element is |v| * 2^-s clamped to 448, then rounded to nearest even
+// on the E4M3 grid by the hardware conversion (for a value that rounds past 448, rounding the
+// clamped value gives 448 as well, so the clamp implements the saturation rule). 2^-s is
+// applied with ldexp, which is exact wherever the result can round to a nonzero code.
+// Returns the 8 codes (little-endian) and the block's shared exponent.
+MOK_DEV uint2 quantize_quad8(const uint4 raw, int* s_out) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = ((const uint4*)src)[i];
-  const bf16_t* v = (const bf16_t*)raw;
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(v[i])));
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
   const int s = mx_shared_exp(amax);
-  uint32_t packed[8];
+  float y[8];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) word |= e4m3_encode(bf16_to_f32(v[4 * w + b]), s) << (8 * b);
-    packed[w] = word;
-  }
-  ((uint4*)codes)[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  ((uint4*)codes)[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-  *scale = (uint8_t)(s + 127);
+  for (int q = 0; q < 8; ++q) y[q] = fminf(fmaxf(__builtin_amdgcn_ldexpf(v[q], -s), -448.0f), 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  *s_out = s;
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
 }

@@ -776,21 +776,31 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
 // ------------------------------------------------------------------------- MXFP8 gather
 // Pull-gather + quantise of rows [r_begin, r_end) of minibatch m: the token rows of the pool
 // picked by route id (or the own rows, for the shared experts) become MXFP8 rows of the
-// minibatch's ring slot. One wave per row; lane i quantises blocks i, i+64, ... of the row.
+// minibatch's ring slot. Each lane takes 8 consecutive elements; the 4 lanes of a 32-element
+// block are an aligned quad, and consecutive lanes cover consecutive 16 bytes of a row.
 MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r_end, int wave,
                                   int n_waves) {
   const int cap = p.max_mb;
   const int32_t g = wl_group(p.wl, cap)[m], first = wl_row0(p.wl, cap)[m];
-  const int nbr = p.d / 32;
-  const int lane = threadIdx.x & 63;
-  for (int r = r_begin + wave; r < r_end; r += n_waves) {
+  const int per_row = p.d / 8;                       // lanes per row (a multiple of 4)
+  const int64_t total = (int64_t)(r_end - r_begin) * per_row;
+  const int nt = 64 * n_waves;
+  const int64_t n_iter = (total + nt - 1) / nt;      // the same for every lane of a wave
+  int64_t q = (int64_t)wave * 64 + (threadIdx.x & 63);
+  for (int64_t it = 0; it < n_iter; ++it, q += nt) {
+    const bool ok = q < total;
+    const int r = r_begin + (ok ? (int)(q / per_row) : 0), c = ok ? (int)(q % per_row) : 0;
     const int64_t tok = g >= p.E_l ? p.own_begin + first + r
                                    : (int64_t)(p.route_ids[first + r] / p.k);
-    const int64_t ring_row = (int64_t)(m % p.n_slots) * p.mb + r;
-    const bf16_t* src = (const bf16_t*)p.x + tok * p.d;
-    for (int b = lane; b < nbr; b += 64)
-      quantize_block32(src + 32 * b, p.A_codes + ring_row * p.d + 32 * b,
-                       p.A_sc + ring_row * nbr + b);
+    const uint4 raw = ok ? *(const uint4*)((const bf16_t*)p.x + tok * p.d + 8 * c)
+                         : make_uint4(0, 0, 0, 0);
+    int sh;
+    const uint2 codes = quantize_quad8(raw, &sh);
+    if (ok) {
+      const int64_t ring_row = (int64_t)(m % p.n_slots) * p.mb + r;
+      *(uint2*)(p.A_codes + ring_row * p.d + 8 * c) = codes;
+      if ((c & 3) == 0) p.A_sc[ring_row * (p.d / 32) + c / 4] = (uint8_t)(sh + 127);
+    }
   }
 }
 

@@ -3,30 +3,42 @@
 // rules come from the OCP specification: shared exponent floor(log2(amax)) - 8, elements
 // rounded to nearest-even on the E4M3 grid and saturated at 448.
 //
-// Both kernels are HBM streams: each thread turns one 32-element block (64 B of bf16) into
-// 32 code bytes and one scale byte; neighbouring threads take neighbouring blocks.
+// HBM streams: four lanes per 32-element block, each lane 16 bytes of bf16 in, 8 code bytes out,
+// the quad's first lane writing the scale byte; a wave covers 1 KB of contiguous input.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mok {
 
 __global__ __launch_bounds__(256) void k_quantize_mxfp8(const bf16_t* __restrict__ src,
-                                                        int64_t n_blocks,
+                                                        int64_t n_chunks,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales) {
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < n_blocks; b += stride)
-    quantize_block32(src + b * 32, codes + b * 32, scales + b);
+  // every lane of a wave runs the same number of iterations (the quad shuffles need the whole
+  // quad): lanes past the end load and store nothing
+  const int64_t n_iter = (n_chunks + stride - 1) / stride;
+  int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (int64_t it = 0; it < n_iter; ++it, q += stride) {
+    const bool ok = q < n_chunks;
+    const uint4 raw = ok ? *(const uint4*)(src + q * 8) : make_uint4(0, 0, 0, 0);
+    int sh;
+    const uint2 c = quantize_quad8(raw, &sh);
+    if (ok) {
+      *(uint2*)(codes + q * 8) = c;
+      if ((q & 3) == 0) scales[q >> 2] = (uint8_t)(sh + 127);
+    }
+  }
 }
 
 hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s) {
-  const int64_t n_blocks = rows * (K / 32);
-  if (n_blocks == 0) return hipSuccess;
-  const int64_t want = (n_blocks + 255) / 256;
-  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  const int64_t n_chunks = rows * (K / 8);
+  if (n_chunks == 0) return hipSuccess;
+  const int64_t want = (n_chunks + 255) / 256;
+  const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
   hipLaunchKernelGGL(k_quantize_mxfp8, dim3(grid), dim3(256), 0, s, (const bf16_t*)src_bf16,
-                     n_blocks, codes, scales);
+                     n_chunks, codes, scales);
   return hipGetLastError();
 }
 
