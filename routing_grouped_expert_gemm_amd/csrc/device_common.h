@@ -146,3 +146,22 @@ MOK_DEV uint2 quantize_quad8(const uint4 raw, int* s_out) {
   *s_out = s;
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
+
+// quantize_quad8 for eight float32 values already in registers (same rules).
+MOK_DEV uint2 quantize_quad8_f32(const float (&v)[8], int* s_out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  const int s = mx_shared_exp(amax);
+  float y[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) y[q] = fminf(fmaxf(__builtin_amdgcn_ldexpf(v[q], -s), -448.0f), 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  *s_out = s;
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}

@@ -680,6 +680,53 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       }
       __builtin_amdgcn_sched_barrier(0);                // one 32-row block of values live at a time
     }
+  } else if constexpr (UP && EL == Elem::FP8) {
+    // MXFP8 H (blocks of 32 along I): each wave stages its SwiGLU outputs as float32 through its
+    // own LDS region, 32 rows at a time; then every lane quantises 8 consecutive values of a row
+    // (the 4 lanes of a 32-column block are an aligned quad) and stores 8 code bytes, the quad's
+    // first lane the scale byte.
+    constexpr int CW = WN / 2;                        // H columns per wave
+    constexpr int JB = CW / 32;
+    constexpr int STRIDE = CW * 4 + 16;               // padded LDS row (bytes)
+    constexpr int LPR = CW / 8;                       // lanes per row in the store phase
+    constexpr int SRPI = 64 / LPR;                    // rows per pass of the wave
+    static_assert(LPR % 4 == 0, "whole 32-column blocks per row");
+    static_assert(32 * STRIDE <= BM * C::ROW_B, "a wave's 32-row pass fits one operand buffer");
+    __syncthreads();
+    typedef __attribute__((address_space(3))) float lds_f32;
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) f32x4v lds_f4;
+    char* region_g = (wid & 1) ? (char*)sm.buf[wid >> 1].B : (char*)sm.buf[wid >> 1].A;
+    lds_f32* region_f = (lds_f32*)region_g;
+    const lds_f4* region_q = (const lds_f4*)region_g;
+    const int col0 = nt * (BN / 2) + wn * (WN / 2);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = 8 * (v >> 2) + 4 * h + (v & 3);
+          region_f[rr * (STRIDE / 4) + j * 32 + l32] = silu(acc[i][j][v]) * acc[i][j + FN / 2][v];
+        }
+#pragma unroll
+      for (int q = 0; q < 32 / SRPI; ++q) {
+        const int rr = q * SRPI + lane / LPR;
+        const int c = (lane % LPR) * 8;                 // first column of the lane's 8 values
+        const int r = wm * WM + i * 32 + rr;
+        const f32x4v a = region_q[(rr * STRIDE + c * 4) / 16];
+        const f32x4v b = region_q[(rr * STRIDE + c * 4) / 16 + 1];
+        const float vals[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        int se;
+        const uint2 codes = quantize_quad8_f32(vals, &se);
+        if (r < rows_valid && col0 + c < N) {
+          const int64_t hr = ring_row0 + m0 + r;
+          *(uint2*)((uint8_t*)p.H + hr * p.Hld + col0 + c) = codes;
+          if ((c & 31) == 0) p.H_sc[hr * (p.Hld / 32) + (col0 + c) / 32] = (uint8_t)(se + 127);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   } else if (UP) {
     const int col0 = nt * (BN / 2) + wn * (WN / 2);
 #pragma unroll
