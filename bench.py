@@ -7,6 +7,9 @@ dispatch plan, pull gather + gate/up GEMM with SwiGLU, down GEMM with the routin
 scale, shared experts and the fixed-order combine. Inputs are seeded synthetic tensors
 already resident in HBM. Prints ONE JSON line.
 
+`hbm` gives the same for the memory-bound stages (plan, combine, MXFP8 weight quantisation and
+row gather): algorithmic bytes over the stage's HIP-event time against 8 TB/s.
+
 `roofline` is taken live for the dominant kernel (the gate/up stage: grouped gate/up GEMM
 with the fused pull gather and SwiGLU, routed + shared): HIP events recorded by the library
 on the forward's own stream around that launch, averaged over the timed steps, against the
@@ -187,6 +190,38 @@ def algorithmic_work(wl, n_routes: int) -> dict:
                 up_flop=up, down_flop=down)
 
 
+def hbm_stages(wl, n_routes: int, stage_ms: dict, ring: bool) -> dict:
+    """Achieved HBM rate of the memory-bound stages: algorithmic bytes (each operand read once,
+    each result written once) over the stage's HIP-event time, against the 8 TB/s peak.
+      plan:    the top-k indices (4 B per route of the pool) read, the local route ids
+               (4 B per local route) written;
+      combine: per token the shared row and the k route rows read, y written (full layer);
+      quant:   every bf16 weight element read (2 B), its E4M3 code and 1/32 of a scale byte
+               written (MXFP8);
+      gather:  per routed row and own token the bf16 x row read, its codes and scales written
+               (MXFP8, stage-ordered; also holds the device work-list build)."""
+    eb = 4 if wl.dtype == "fp32" else 2
+    routes_pool = wl.T_pool * wl.k
+    I_sh = wl.n_shared * wl.I_shared
+    bytes_ = {"plan": 4 * routes_pool + 4 * n_routes}
+    if wl.full_layer:
+        bytes_["combine"] = wl.T_pool * wl.d * eb * (wl.k + 2)
+    if wl.dtype == "mxfp8":
+        n_w = wl.E_l * 3 * wl.d * wl.I + 3 * wl.d * I_sh
+        bytes_["quant"] = n_w * (2 + 1 + 1 / 32)
+        if not ring:
+            bytes_["gather"] = (n_routes + wl.T_own) * wl.d * (2 + 1 + 1 / 32)
+    out = {}
+    for name, b in bytes_.items():
+        t = stage_ms[name] * 1e-3
+        if t <= 0:
+            continue
+        gbs = b / t / 1e9
+        out[name] = {"bytes": int(b), "ms": round(stage_ms[name], 4), "achieved": round(gbs, 1),
+                     "unit": "GB/s", "frac": round(gbs * 1e9 / HBM_PEAK, 4)}
+    return out
+
+
 def cpu_baseline(wl, inputs_cpu, sample_tokens: int) -> dict:
     """The oracle (as it stands) on the first `sample_tokens` tokens of the workload."""
     import numpy as np
@@ -283,9 +318,11 @@ def main():
     n_routes = int(layer.inter["offsets"][-1])
     work = algorithmic_work(wl, n_routes)
     stage_ms = {}
-    names = ["route", "plan", "quant", "up", "down", "combine"]
+    names = ["route", "plan", "quant", "up", "down", "combine", "gather"]
+    assert len(names) == mok.MOK_N_STAGES
+    n2 = 2 * mok.MOK_N_STAGES
     for s, name in enumerate(names):
-        vals = [ev.elapsed_ms(2 * 6 * i + 2 * s, 2 * 6 * i + 2 * s + 1) for i in range(args.steps)]
+        vals = [ev.elapsed_ms(n2 * i + 2 * s, n2 * i + 2 * s + 1) for i in range(args.steps)]
         stage_ms[name] = sum(vals) / len(vals)
     up_s = stage_ms["up"] * 1e-3
     peak = PEAK[wl.dtype]
@@ -311,6 +348,7 @@ def main():
                      "achieved": round(achieved / 1e12, 2), "peak": peak / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": profiled_traffic(wl.name)},
+        "hbm": hbm_stages(wl, n_routes, stage_ms, args.ring),
     }
     if not args.no_cpu:
         import synth as _s  # noqa: F401

@@ -162,10 +162,13 @@ typedef struct mok_moe_args {
 #define MOK_STAGE_ROUTE 0    /* router logits + top-k (router runs only)          */
 #define MOK_STAGE_PLAN 1     /* dispatch plan                                      */
 #define MOK_STAGE_QUANT 2    /* MXFP8 weight quantisation (MXFP8 only)             */
-#define MOK_STAGE_UP 3       /* work list + gather + gate/up GEMM with SwiGLU      */
+#define MOK_STAGE_UP 3       /* gate/up GEMM with SwiGLU (fused bf16/fp32 gather)  */
 #define MOK_STAGE_DOWN 4     /* down GEMM with routing-weight scale                */
 #define MOK_STAGE_COMBINE 5  /* fixed-order combine (full layer only)              */
-#define MOK_N_STAGES 6
+#define MOK_STAGE_GATHER 6   /* device work list; MXFP8 stage order: + pull gather and
+                                quantisation of the A rows (MOK_STAGE_UP is then the
+                                gate/up GEMM launch alone)                         */
+#define MOK_N_STAGES 7
 
 /* flags */
 #define MOK_FLAG_NO_RING 1u  /* stage-ordered launches over all routes (ring sized to every

@@ -20,8 +20,9 @@ LIB_PATH = os.environ.get("MOK_LIBRARY") or os.path.join(_PKG, "libmok.so")
 MOK_OK, MOK_EINVAL, MOK_EUNSUPPORTED, MOK_EWORKSPACE, MOK_EHIP = range(5)
 MOK_FP32, MOK_BF16, MOK_MXFP8 = 0, 1, 2
 MOK_FLAG_NO_RING = 1
-MOK_STAGE_ROUTE, MOK_STAGE_PLAN, MOK_STAGE_QUANT, MOK_STAGE_UP, MOK_STAGE_DOWN, MOK_STAGE_COMBINE = range(6)
-MOK_N_STAGES = 6
+(MOK_STAGE_ROUTE, MOK_STAGE_PLAN, MOK_STAGE_QUANT, MOK_STAGE_UP, MOK_STAGE_DOWN, MOK_STAGE_COMBINE,
+ MOK_STAGE_GATHER) = range(7)
+MOK_N_STAGES = 7
 
 EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
            "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_moe_workspace_bytes",

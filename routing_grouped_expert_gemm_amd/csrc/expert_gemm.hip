@@ -1023,6 +1023,10 @@ static void record(void* const* ev, int i, hipStream_t s) {
 
 template <Elem EL, bool F32OUT>
 static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
+  if (EL == Elem::FP8 && !p.ring)
+    hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);
+  record(ev, 2 * 6 + 1, s);
+  record(ev, 2 * 3, s);
   if (p.ring) {
     hipLaunchKernelGGL((k_ring<EL, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
     record(ev, 2 * 3 + 1, s);
@@ -1030,8 +1034,6 @@ static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* cons
     record(ev, 2 * 4 + 1, s);
     return hipGetLastError();
   }
-  if (EL == Elem::FP8)
-    hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);
   hipLaunchKernelGGL((k_expert_stage<EL, true, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
   record(ev, 2 * 3 + 1, s);
   record(ev, 2 * 4, s);
@@ -1054,7 +1056,7 @@ hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const*
   const int nU_r = (p.I + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nD = (p.d + Big::BN - 1) / Big::BN;
-  record(ev, 2 * 3, s);
+  record(ev, 2 * 6, s);
   const bool gather_items = p.ring && p.elem == Elem::FP8;
   hipLaunchKernelGGL(k_build_worklist, dim3(1), dim3(1024), 0, s, p.counts, p.offsets, p.E_l,
                      p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.lag,
