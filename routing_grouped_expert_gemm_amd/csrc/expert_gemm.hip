@@ -201,9 +201,11 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
 // stage's product; each wave a WM x WN block of 32 x 32 MFMA accumulators (FM x FN). Each K
 // step moves ROW_B bytes of every operand row into one of STAGES LDS buffers, either through
 // registers (global_load_dwordx4, then ds_write_b128) or by LDS-DMA (global_load_lds_dwordx4).
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_, bool DMA_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_, bool DMA_,
+          int ISSUE_PARTS_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int ISSUE_PARTS = ISSUE_PARTS_;   // MFMA sub-steps a K step's DMA spans
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
@@ -222,7 +224,7 @@ struct Cfg {
 // 256 x 256 tiles, 4 waves of 128 x 128 (16 accumulator blocks = 256 AGPRs per lane), one
 // workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs. Two 64 KB K stages of
 // 128 bytes per row (whole cache lines), filled by LDS-DMA.
-typedef Cfg<256, 256, 2, 2, 128, 2, true> Big;
+typedef Cfg<256, 256, 2, 2, 128, 2, true, 2> Big;
 
 // Per element type: bytes per element, and the MFMA's K per instruction.
 template <Elem EL> struct Tr;
@@ -248,6 +250,19 @@ struct Lds {
   int32_t* row_dst;
   float* row_w;
 };
+
+// Buffer i (a run-time index), chosen with selects: indexing the pointer array itself at run
+// time would place it in private (scratch) memory.
+template <class C>
+MOK_DEV Bufs<C> pick(const Lds<C>& sm, int i) {
+  Bufs<C> r = sm.buf[0];
+#pragma unroll
+  for (int q = 1; q < C::STAGES; ++q)
+    if (i == q) {
+      r.A = sm.buf[q].A; r.B = sm.buf[q].B; r.As = sm.buf[q].As; r.Bs = sm.buf[q].Bs;
+    }
+  return r;
+}
 
 // 16-byte chunk that lane half h feeds to the MFMA of K sub-step s (16 or 64 elements).
 //  bf16 32x32x16: one chunk, k = 16s + 8h + [0, 8).
@@ -297,6 +312,10 @@ MOK_DEV void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The weight fragment is the MFMA's first operand and the token-row fragment its second, so
+// each accumulator block holds the transposed product: lane (h, l32) of block (i, j) carries
+// output row 32i + l32 and output columns 32j + 8g + 4h + [0, 4) in values 4g .. 4g + 3 --
+// four consecutive columns of one row per register quad, which the epilogues store whole.
 template <Elem EL, int FM, int FN>
 MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const uint32_t* asc,
                        const uint32_t* bsc, f32x16_t (&acc)[FM][FN]) {
@@ -306,7 +325,7 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, a[i][0]), __builtin_bit_cast(bf16x8_t, b[j][0]),
+            __builtin_bit_cast(bf16x8_t, b[j][0]), __builtin_bit_cast(bf16x8_t, a[i][0]),
             acc[i][j], 0, 0, 0);
   } else if constexpr (EL == Elem::F32) {
     // Lane half h supplies k = 8h + q of a 16-wide K step to the q-th 32x32x2 product; A and
@@ -319,7 +338,7 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
         const float* bv = reinterpret_cast<const float*>(&b[j][0]);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], bv[q], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[q], av[q], acc[i][j], 0, 0, 0);
       }
   } else {
 #pragma unroll
@@ -332,15 +351,10 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
         bv[0] = b[j][0].x; bv[1] = b[j][0].y; bv[2] = b[j][0].z; bv[3] = b[j][0].w;
         bv[4] = b[j][1].x; bv[5] = b[j][1].y; bv[6] = b[j][1].z; bv[7] = b[j][1].w;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            av, bv, acc[i][j], 0, 0, 0, (int)asc[i], 0, (int)bsc[j]);
+            bv, av, acc[i][j], 0, 0, 0, (int)bsc[j], 0, (int)asc[i]);
       }
   }
 }
-
-// Output element of the epilogues.
-template <bool F32OUT> struct Out;
-template <> struct Out<true> { typedef float T; };
-template <> struct Out<false> { typedef bf16_t T; };
 
 // One tile of the up (UP = true) or down (UP = false) stage of minibatch m.
 //  up:   the minibatch's rows x (gate, up rows of H columns n0 .. n0 + BN/2) -> H
@@ -353,7 +367,6 @@ template <> struct Out<false> { typedef bf16_t T; };
 template <Elem EL, bool UP, bool F32OUT, class C>
 MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   typedef Tr<EL> TR;
-  typedef typename Out<F32OUT>::T OT;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS, ST = C::STAGES, CH = C::CH;
   constexpr int RPI = C::RPI, SWS = C::SWZ_SHIFT;
@@ -493,16 +506,20 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
                                : nullptr;
     return s;
   };
-  // (a) LDS-DMA issue of K step kt into buffer b
-  auto issue = [&](int kt, const Bufs<C>& b) {
+  // (a) LDS-DMA issue of K step kt into buffer b, part `part` of NP: the step's DMAs (A slabs,
+  // B slabs, then the MX scale words) are dealt round-robin over the parts.
+  constexpr int NP = SUB < C::ISSUE_PARTS ? SUB : C::ISSUE_PARTS;
+  auto issue = [&](int kt, const Bufs<C>& b, int part) {
     const StepAddr s = step_addr(kt);
     const uint32_t la = uniform(lds_addr(&b.A[64 * wid][0]));
     const uint32_t lb = uniform(lds_addr(&b.B[64 * wid][0]));
 #pragma unroll
-    for (int q = 0; q < A_SLABS; ++q) dma_b128(a_base, a_off[q] + s.ka, la + 1024 * q);
+    for (int q = 0; q < A_SLABS; ++q)
+      if (q % NP == part) dma_b128(a_base, a_off[q] + s.ka, la + 1024 * q);
 #pragma unroll
-    for (int q = 0; q < B_SLABS; ++q) dma_b128(s.b_seg, b_off[q] + s.kb, lb + 1024 * q);
-    if (EL == Elem::FP8) {
+    for (int q = 0; q < B_SLABS; ++q)
+      if ((A_SLABS + q) % NP == part) dma_b128(s.b_seg, b_off[q] + s.kb, lb + 1024 * q);
+    if (EL == Elem::FP8 && part == NP - 1) {
       dma_b32(a_sc_base, a_sc_off + s.sca, uniform(lds_addr(&b.As[64 * wid])));
       dma_b32(s.bs_seg, b_sc_off + s.scb, uniform(lds_addr(&b.Bs[64 * wid])));
     }
@@ -546,7 +563,9 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   // Fragments are double-buffered across the K sub-steps: the reads of sub-step s + 1 are
   // issued before the MFMAs of s (scheduling barriers pin that order; left alone the scheduler
   // sinks each read to just before its first use and every sub-step waits on LDS latency).
-  auto compute = [&](const Bufs<C>& b, int kt) {
+  // between(s) runs after those reads and before the MFMAs of s: the K loop issues part s of
+  // the next step's LDS-DMA there, so no sub-step waits behind the whole step's requests.
+  auto compute = [&](const Bufs<C>& b, int kt, auto&& between) {
     const char* a_buf = (const char*)&b.A[wm * WM + l32][0];
     const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
     const int sc_shift = 8 * (((uint32_t)kt * SC_B) & 3);
@@ -575,6 +594,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     for (int s = 0; s < SUB; ++s) {
       if (s + 1 < SUB) load(s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);   // the reads of s + 1 go out before the MFMAs of s
+      between(s);
+      __builtin_amdgcn_sched_barrier(0);
       mfma_step<EL, FM, FN>(fa[s & 1], fb[s & 1], asc[s & 1], bsc[s & 1], acc);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -587,12 +608,15 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     // The steady state is unrolled by ST so every buffer's role is static.
 #pragma unroll
     for (int q = 0; q < ST - 1; ++q)
-      if (q < nk) issue(q, sm.buf[q]);
+      if (q < nk)
+#pragma unroll
+        for (int part = 0; part < NP; ++part) issue(q, sm.buf[q], part);
     auto steady = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
       wait_vmcnt<(ST - 2) * DMA_PER_STEP>();
       lds_barrier();
-      issue(kt + ST - 1, nxt);
-      compute(cur, kt);
+      compute(cur, kt, [&](int s) {
+        if (s < NP) issue(kt + ST - 1, nxt, s);
+      });
     };
     int kt = 0;
     for (; kt + 2 * ST - 1 <= nk; kt += ST) {
@@ -605,8 +629,11 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       else if (ahead == 1) wait_vmcnt<DMA_PER_STEP>();
       else wait_vmcnt<0>();
       lds_barrier();
-      if (kt + ST - 1 < nk) issue(kt + ST - 1, sm.buf[(kt + ST - 1) % ST]);
-      compute(sm.buf[kt % ST], kt);
+      const bool more = kt + ST - 1 < nk;
+      const Bufs<C> cur = pick(sm, kt % ST), nxt = pick(sm, (kt + ST - 1) % ST);
+      compute(cur, kt, [&](int s) {
+        if (more && s < NP) issue(kt + ST - 1, nxt, s);
+      });
     }
   } else {
     // Two buffers, unrolled by two: the loads of step kt + 1 are in flight (registers) while
@@ -618,7 +645,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     auto two = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
       const bool more = kt + 1 < nk;
       if (more) gload(kt + 1);
-      compute(cur, kt);
+      compute(cur, kt, [](int) {});
       if (more) lstore(nxt);
       __syncthreads();
     };
@@ -630,148 +657,126 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     if (kt < nk) two(kt, sm.buf[0], sm.buf[1]);
   }
 
-  // ---- epilogue. Accumulator v of block (i, j) is (row 8*(v/4) + 4*h + v%4, col l32).
-  if constexpr (!F32OUT && !(UP && EL == Elem::FP8)) {
-    // bf16 outputs: each wave stages its block through its own LDS region (the operand buffers
-    // are free once every wave is past the K loop), 32 rows at a time, then writes whole rows
-    // with 16-byte stores: H rows of the ring (up) or route-slot / shared rows (down).
+  // ---- epilogue. Value 4g + r of block (i, j) is (row 32i + l32, column 32j + 8g + 4h + r) of
+  // the wave's block (see mfma_step).
+  const int r_lane = wm * WM + l32;                   // tile row of block row i = 0
+  if constexpr (!F32OUT) {
+    // bf16 (or MXFP8 H) outputs: each wave stages 32 rows at a time through its own LDS region
+    // (the operand buffers are free once every wave is past the K loop), four columns per
+    // write, then stores whole row segments: H rows of the ring (up) or route-slot / shared
+    // rows (down). MXFP8 H is staged as float32 and quantised 8 values per lane, the 4 lanes
+    // of a 32-column block forming an aligned quad (the first stores the scale byte).
+    constexpr bool MX = UP && EL == Elem::FP8;
+    constexpr int VB = MX ? 4 : 2;                    // staged bytes per value
     constexpr int CW = UP ? WN / 2 : WN;              // output columns per wave
     constexpr int JB = CW / 32;                       // 32-column blocks per wave
-    constexpr int STRIDE = CW * 2 + 16;               // padded LDS row (bytes)
-    constexpr int LPR = CW * 2 / 16;                  // lanes per row in the store phase
-    constexpr int SRPI = 64 / LPR;                    // rows per store instruction
+    constexpr int STRIDE = CW * VB + 16;              // padded LDS row (bytes)
+    constexpr int VPL = MX ? 8 : 16 / VB;             // values per lane in the store phase
+    constexpr int LPR = CW / VPL;                     // lanes per row in the store phase
+    constexpr int SRPI = 64 / LPR;                    // rows per store pass
+    static_assert(!MX || LPR % 4 == 0, "whole 32-column blocks per row");
     static_assert(32 * STRIDE <= BM * C::ROW_B, "a wave's 32-row pass fits one operand buffer");
     __syncthreads();
-    typedef __attribute__((address_space(3))) bf16_t lds_bf16;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) u32x2 lds_u2;
     typedef __attribute__((address_space(3))) u32x4 lds_u4;
-    char* region_g = (wid & 1) ? (char*)sm.buf[wid >> 1].B : (char*)sm.buf[wid >> 1].A;
-    lds_bf16* region_h = (lds_bf16*)region_g;
-    const lds_u4* region_q = (const lds_u4*)region_g;
+    // wave w's region: operand buffer w / 2, A half (w even) or B half (w odd); chosen with
+    // selects so that no private array is indexed at run time
+    char* const rA = (wid >> 1) ? (char*)sm.buf[1].A : (char*)sm.buf[0].A;
+    char* const rB = (wid >> 1) ? (char*)sm.buf[1].B : (char*)sm.buf[0].B;
+    char* region = (wid & 1) ? rB : rA;
     const int col0 = UP ? nt * (BN / 2) + wn * (WN / 2) : nt * BN + wn * WN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      float rw[16];                                     // row weights of this 32-row block
-      if (!UP) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          rw[v] = sm.row_w[min(wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3), BM - 1)];
-      }
+      float rw = 1.0f;                                  // routing weight of the lane's row
+      if (!UP) rw = sm.row_w[min(r_lane + i * 32, BM - 1)];
 #pragma unroll
       for (int j = 0; j < JB; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rr = 8 * (v >> 2) + 4 * h + (v & 3);      // row within the pass
-          const float val = UP ? silu(acc[i][j][v]) * acc[i][j + FN / 2][v] : acc[i][j][v] * rw[v];
-          region_h[rr * (STRIDE / 2) + j * 32 + l32] = f32_to_bf16(val);
+        for (int g = 0; g < 4; ++g) {
+          float val[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = 4 * g + r;
+            val[r] = UP ? silu(acc[i][j][v]) * acc[i][j + FN / 2][v] : acc[i][j][v] * rw;
+          }
+          char* dst = region + l32 * STRIDE + (j * 32 + 8 * g + 4 * h) * VB;
+          if constexpr (MX) {
+            u32x4 q;
+            q.x = __float_as_uint(val[0]); q.y = __float_as_uint(val[1]);
+            q.z = __float_as_uint(val[2]); q.w = __float_as_uint(val[3]);
+            *(lds_u4*)dst = q;
+          } else {
+            u32x2 q;
+            q.x = (uint32_t)f32_to_bf16(val[0]) | ((uint32_t)f32_to_bf16(val[1]) << 16);
+            q.y = (uint32_t)f32_to_bf16(val[2]) | ((uint32_t)f32_to_bf16(val[3]) << 16);
+            *(lds_u2*)dst = q;
+          }
         }
 #pragma unroll
       for (int q = 0; q < 32 / SRPI; ++q) {
-        const int rr = q * SRPI + lane / LPR;
-        const int c = (lane % LPR) * 8;                 // first column of the lane's 16 B
+        const int rr = q * SRPI + lane / LPR;           // row within the pass
+        const int c = (lane % LPR) * VPL;               // first column of the lane's values
         const int r = wm * WM + i * 32 + rr;            // row within the tile
-        const u32x4 val = region_q[(rr * STRIDE + c * 2) / 16];
-        if (r < rows_valid && col0 + c < N) {
-          bf16_t* dst;
-          if (UP) dst = (bf16_t*)p.H + (ring_row0 + m0 + r) * p.Hld;
-          else dst = (shared ? (bf16_t*)p.y_shared : (bf16_t*)p.y_slots) + (int64_t)sm.row_dst[r] * p.d;
-          *(u32x4*)(dst + col0 + c) = val;
+        const char* src = region + rr * STRIDE + c * VB;
+        if constexpr (MX) {
+          const u32x4 lo = *(const lds_u4*)src, hi = *(const lds_u4*)(src + 16);
+          const float vals[8] = {__uint_as_float(lo.x), __uint_as_float(lo.y),
+                                 __uint_as_float(lo.z), __uint_as_float(lo.w),
+                                 __uint_as_float(hi.x), __uint_as_float(hi.y),
+                                 __uint_as_float(hi.z), __uint_as_float(hi.w)};
+          int se;
+          const uint2 codes = quantize_quad8_f32(vals, &se);
+          if (r < rows_valid && col0 + c < N) {
+            const int64_t hr = ring_row0 + m0 + r;
+            *(uint2*)((uint8_t*)p.H + hr * p.Hld + col0 + c) = codes;
+            if ((c & 31) == 0) p.H_sc[hr * (p.Hld / 32) + (col0 + c) / 32] = (uint8_t)(se + 127);
+          }
+        } else {
+          const u32x4 val = *(const lds_u4*)src;
+          if (r < rows_valid && col0 + c < N) {
+            bf16_t* dst;
+            if (UP) dst = (bf16_t*)p.H + (ring_row0 + m0 + r) * p.Hld;
+            else dst = (shared ? (bf16_t*)p.y_shared : (bf16_t*)p.y_slots) + (int64_t)sm.row_dst[r] * p.d;
+            *(u32x4*)(dst + col0 + c) = val;
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);                // one 32-row block of values live at a time
     }
-  } else if constexpr (UP && EL == Elem::FP8) {
-    // MXFP8 H (blocks of 32 along I): each wave stages its SwiGLU outputs as float32 through its
-    // own LDS region, 32 rows at a time; then every lane quantises 8 consecutive values of a row
-    // (the 4 lanes of a 32-column block are an aligned quad) and stores 8 code bytes, the quad's
-    // first lane the scale byte.
-    constexpr int CW = WN / 2;                        // H columns per wave
-    constexpr int JB = CW / 32;
-    constexpr int STRIDE = CW * 4 + 16;               // padded LDS row (bytes)
-    constexpr int LPR = CW / 8;                       // lanes per row in the store phase
-    constexpr int SRPI = 64 / LPR;                    // rows per pass of the wave
-    static_assert(LPR % 4 == 0, "whole 32-column blocks per row");
-    static_assert(32 * STRIDE <= BM * C::ROW_B, "a wave's 32-row pass fits one operand buffer");
-    __syncthreads();
-    typedef __attribute__((address_space(3))) float lds_f32;
+  } else {
+    // float32 outputs: each lane stores its four consecutive columns as one 16-byte vector
+    // (N is a multiple of 32, so a group of four is wholly inside or outside the matrix).
     typedef float f32x4v __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) f32x4v lds_f4;
-    char* region_g = (wid & 1) ? (char*)sm.buf[wid >> 1].B : (char*)sm.buf[wid >> 1].A;
-    lds_f32* region_f = (lds_f32*)region_g;
-    const lds_f4* region_q = (const lds_f4*)region_g;
-    const int col0 = nt * (BN / 2) + wn * (WN / 2);
+    const int col0 = UP ? nt * (BN / 2) + wn * (WN / 2) : nt * BN + wn * WN;
+    constexpr int JB = UP ? FN / 2 : FN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const int r = r_lane + i * 32;
+      if (r >= rows_valid) continue;
+      float* dst_row;
+      float rw = 1.0f;
+      if (UP) {
+        dst_row = (float*)p.H + (ring_row0 + m0 + r) * p.Hld;
+      } else {
+        dst_row = (shared ? (float*)p.y_shared : (float*)p.y_slots) + (int64_t)sm.row_dst[r] * p.d;
+        rw = sm.row_w[r];
+      }
 #pragma unroll
       for (int j = 0; j < JB; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rr = 8 * (v >> 2) + 4 * h + (v & 3);
-          region_f[rr * (STRIDE / 4) + j * 32 + l32] = silu(acc[i][j][v]) * acc[i][j + FN / 2][v];
-        }
+        for (int g = 0; g < 4; ++g) {
+          const int col = col0 + j * 32 + 8 * g + 4 * h;
+          f32x4v o;
 #pragma unroll
-      for (int q = 0; q < 32 / SRPI; ++q) {
-        const int rr = q * SRPI + lane / LPR;
-        const int c = (lane % LPR) * 8;                 // first column of the lane's 8 values
-        const int r = wm * WM + i * 32 + rr;
-        const f32x4v a = region_q[(rr * STRIDE + c * 4) / 16];
-        const f32x4v b = region_q[(rr * STRIDE + c * 4) / 16 + 1];
-        const float vals[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        int se;
-        const uint2 codes = quantize_quad8_f32(vals, &se);
-        if (r < rows_valid && col0 + c < N) {
-          const int64_t hr = ring_row0 + m0 + r;
-          *(uint2*)((uint8_t*)p.H + hr * p.Hld + col0 + c) = codes;
-          if ((c & 31) == 0) p.H_sc[hr * (p.Hld / 32) + (col0 + c) / 32] = (uint8_t)(se + 127);
+          for (int q = 0; q < 4; ++q) {
+            const int v = 4 * g + q;
+            o[q] = UP ? silu(acc[i][j][v]) * acc[i][j + FN / 2][v] : acc[i][j][v] * rw;
+          }
+          if (col < N) *(f32x4v*)(dst_row + col) = o;
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
-  } else if (UP) {
-    const int col0 = nt * (BN / 2) + wn * (WN / 2);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN / 2; ++j) {
-        const int col = col0 + j * 32 + l32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          const float hv = silu(acc[i][j][v]) * acc[i][j + FN / 2][v];
-          if (EL == Elem::FP8) {
-            // MXFP8 along I: the 32 columns of this block row sit in the 32 lanes of half h
-            float amax = fabsf(hv);
-#pragma unroll
-            for (int msk = 1; msk < 32; msk <<= 1) amax = fmaxf(amax, __shfl_xor(amax, msk, kWave));
-            const int se = mx_shared_exp(amax);
-            if (r < rows_valid && col < N) {
-              const int64_t hr = ring_row0 + m0 + r;
-              ((uint8_t*)p.H)[hr * p.Hld + col] = (uint8_t)e4m3_encode(hv, se);
-              if (l32 == 0) p.H_sc[hr * (p.Hld / 32) + col / 32] = (uint8_t)(se + 127);
-            }
-          } else if (r < rows_valid && col < N) {
-            const int64_t hr = ring_row0 + m0 + r;
-            ((OT*)p.H)[hr * p.Hld + col] = f32_to<OT>(hv);
-          }
-        }
-      }
-  } else {
-    const int col0 = nt * BN + wn * WN;
-    OT* out = shared ? (OT*)p.y_shared : (OT*)p.y_slots;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = col0 + j * 32 + l32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (r < rows_valid && col < N) {
-            const int64_t dst = sm.row_dst[r];
-            out[dst * p.d + col] = f32_to<OT>(acc[i][j][v] * sm.row_w[r]);
-          }
-        }
-      }
   }
   __syncthreads();  // LDS (row table, operand buffers) is reused by the next tile
 }
