@@ -173,16 +173,21 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
   }
   __syncthreads();
   if (overflow) return;
-  // tile tables (tiles of a minibatch: n-tile major, m-tile minor)
+  // tile tables (tiles of a minibatch: n-tile major, m-tile minor). When the shared experts'
+  // down tiles are the longer ones (K = n_shared * I_shared > I), the stage-ordered down table
+  // lists them first, so that the longest tiles start first and the stage ends evenly.
   int4* ut = wl_utab(wl, cap);
   int4* dt = wl_dtab(wl, cap, cap_u);
   int4* rt = wl_rtab(wl, cap, cap_u, cap_d);
+  const bool shared_first = nU_s > nU_r;
+  const int32_t d_sh0 = ds[min(n_routed, n_mb)], d_sh = carry_d - d_sh0;
   for (int m = t; m < n_mb; m += 1024) {
     const int32_t g = grp[m], rw = nr[m], first = r0[m];
     const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
     const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m], ng = gs[m + 1] - gs[m];
+    const int32_t dpos = !shared_first ? ds[m] : (m >= n_routed ? ds[m] - d_sh0 : ds[m] + d_sh);
     for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = l; ut[us[m] + l] = e; }
-    for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = l; dt[ds[m] + l] = e; }
+    for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = l; dt[dpos + l] = e; }
     if (ring) {
       const int mb_lag = max(0, m - lag);
       const int after = min(m + lag + 1, n_mb);
@@ -202,10 +207,12 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
 // step moves ROW_B bytes of every operand row into one of STAGES LDS buffers, either through
 // registers (global_load_dwordx4, then ds_write_b128) or by LDS-DMA (global_load_lds_dwordx4).
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_, bool DMA_,
-          int ISSUE_PARTS_ = 1>
+          int ISSUE_SPAN_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int ISSUE_PARTS = ISSUE_PARTS_;   // MFMA sub-steps a K step's DMA spans
+  // The LDS-DMA instructions of the next K step are spread evenly over the first ISSUE_SPAN
+  // MFMAs of the current one (0: all before the first MFMA)
+  static constexpr int ISSUE_SPAN = ISSUE_SPAN_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
@@ -224,7 +231,7 @@ struct Cfg {
 // 256 x 256 tiles, 4 waves of 128 x 128 (16 accumulator blocks = 256 AGPRs per lane), one
 // workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs. Two 64 KB K stages of
 // 128 bytes per row (whole cache lines), filled by LDS-DMA.
-typedef Cfg<256, 256, 2, 2, 128, 2, true, 2> Big;
+typedef Cfg<256, 256, 2, 2, 128, 2, true, 32> Big;
 
 // Per element type: bytes per element, and the MFMA's K per instruction.
 template <Elem EL> struct Tr;
@@ -316,17 +323,19 @@ MOK_DEV void lds_barrier() {
 // each accumulator block holds the transposed product: lane (h, l32) of block (i, j) carries
 // output row 32i + l32 and output columns 32j + 8g + 4h + [0, 4) in values 4g .. 4g + 3 --
 // four consecutive columns of one row per register quad, which the epilogues store whole.
-template <Elem EL, int FM, int FN>
+template <Elem EL, int FM, int FN, class After>
 MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const uint32_t* asc,
-                       const uint32_t* bsc, f32x16_t (&acc)[FM][FN]) {
+                       const uint32_t* bsc, f32x16_t (&acc)[FM][FN], After&& after) {
   if constexpr (EL == Elem::BF16) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, b[j][0]), __builtin_bit_cast(bf16x8_t, a[i][0]),
             acc[i][j], 0, 0, 0);
+        after(i * FN + j);
+      }
   } else if constexpr (EL == Elem::F32) {
     // Lane half h supplies k = 8h + q of a 16-wide K step to the q-th 32x32x2 product; A and
     // B use the same assignment, so the 8 products cover the step exactly once.
@@ -339,6 +348,7 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
 #pragma unroll
         for (int q = 0; q < 8; ++q)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[q], av[q], acc[i][j], 0, 0, 0);
+        after(i * FN + j);
       }
   } else {
 #pragma unroll
@@ -352,6 +362,7 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
         bv[4] = b[j][1].x; bv[5] = b[j][1].y; bv[6] = b[j][1].z; bv[7] = b[j][1].w;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             bv, av, acc[i][j], 0, 0, 0, (int)bsc[j], 0, (int)asc[i]);
+        after(i * FN + j);
       }
   }
 }
@@ -506,23 +517,34 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
                                : nullptr;
     return s;
   };
-  // (a) LDS-DMA issue of K step kt into buffer b, part `part` of NP: the step's DMAs (A slabs,
-  // B slabs, then the MX scale words) are dealt round-robin over the parts.
-  constexpr int NP = SUB < C::ISSUE_PARTS ? SUB : C::ISSUE_PARTS;
-  auto issue = [&](int kt, const Bufs<C>& b, int part) {
-    const StepAddr s = step_addr(kt);
-    const uint32_t la = uniform(lds_addr(&b.A[64 * wid][0]));
-    const uint32_t lb = uniform(lds_addr(&b.B[64 * wid][0]));
-#pragma unroll
-    for (int q = 0; q < A_SLABS; ++q)
-      if (q % NP == part) dma_b128(a_base, a_off[q] + s.ka, la + 1024 * q);
-#pragma unroll
-    for (int q = 0; q < B_SLABS; ++q)
-      if ((A_SLABS + q) % NP == part) dma_b128(s.b_seg, b_off[q] + s.kb, lb + 1024 * q);
-    if (EL == Elem::FP8 && part == NP - 1) {
+  // (a) LDS-DMA issue of K step kt into buffer b: instruction q of the step (A slabs, B slabs,
+  // then the MX scale words). issue_at(kt, b, n) issues those that belong after MFMA n of the
+  // current step (q * SPAN / DMA_PER_STEP == n); n = -1: before the first.
+  constexpr int N_MFMA = SUB * FM * FN;             // MFMAs per K step and wave
+  constexpr int SPAN = C::ISSUE_SPAN < N_MFMA ? C::ISSUE_SPAN : N_MFMA;
+  auto issue_one = [&](const StepAddr& s, const Bufs<C>& b, int q) {
+    __builtin_amdgcn_sched_barrier(0);             // keeps the DMA between its two MFMAs
+    if (q < A_SLABS) {
+      dma_b128(a_base, a_off[q] + s.ka, uniform(lds_addr(&b.A[64 * wid][0])) + 1024 * q);
+    } else if (q < A_SLABS + B_SLABS) {
+      const int r = q - A_SLABS;
+      dma_b128(s.b_seg, b_off[r] + s.kb, uniform(lds_addr(&b.B[64 * wid][0])) + 1024 * r);
+    } else if (q == A_SLABS + B_SLABS) {
       dma_b32(a_sc_base, a_sc_off + s.sca, uniform(lds_addr(&b.As[64 * wid])));
+    } else {
       dma_b32(s.bs_seg, b_sc_off + s.scb, uniform(lds_addr(&b.Bs[64 * wid])));
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue_at = [&](const StepAddr& s, const Bufs<C>& b, int n) {
+#pragma unroll
+    for (int q = 0; q < DMA_PER_STEP; ++q)
+      if ((SPAN == 0 ? -1 : q * SPAN / DMA_PER_STEP) == n) issue_one(s, b, q);
+  };
+  auto issue_all = [&](int kt, const Bufs<C>& b) {
+    const StepAddr s = step_addr(kt);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_STEP; ++q) issue_one(s, b, q);
   };
   // (b) register staging: global -> registers, later registers -> LDS
   uint4 ra[C::DMA ? 1 : A_SLABS], rb[C::DMA ? 1 : B_SLABS];
@@ -563,9 +585,10 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   // Fragments are double-buffered across the K sub-steps: the reads of sub-step s + 1 are
   // issued before the MFMAs of s (scheduling barriers pin that order; left alone the scheduler
   // sinks each read to just before its first use and every sub-step waits on LDS latency).
-  // between(s) runs after those reads and before the MFMAs of s: the K loop issues part s of
-  // the next step's LDS-DMA there, so no sub-step waits behind the whole step's requests.
-  auto compute = [&](const Bufs<C>& b, int kt, auto&& between) {
+  // after(n) runs after MFMA n of the step (n = -1: after the first reads, before any MFMA):
+  // the K loop issues the next step's LDS-DMA there, a few instructions at a time, so that no
+  // MFMA waits behind a burst of memory instructions.
+  auto compute = [&](const Bufs<C>& b, int kt, auto&& after) {
     const char* a_buf = (const char*)&b.A[wm * WM + l32][0];
     const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
     const int sc_shift = 8 * (((uint32_t)kt * SC_B) & 3);
@@ -594,9 +617,10 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     for (int s = 0; s < SUB; ++s) {
       if (s + 1 < SUB) load(s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);   // the reads of s + 1 go out before the MFMAs of s
-      between(s);
+      if (s == 0) after(-1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step<EL, FM, FN>(fa[s & 1], fb[s & 1], asc[s & 1], bsc[s & 1], acc);
+      mfma_step<EL, FM, FN>(fa[s & 1], fb[s & 1], asc[s & 1], bsc[s & 1], acc,
+                            [&](int n) { after(s * FM * FN + n); });
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -608,15 +632,12 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     // The steady state is unrolled by ST so every buffer's role is static.
 #pragma unroll
     for (int q = 0; q < ST - 1; ++q)
-      if (q < nk)
-#pragma unroll
-        for (int part = 0; part < NP; ++part) issue(q, sm.buf[q], part);
+      if (q < nk) issue_all(q, sm.buf[q]);
     auto steady = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
       wait_vmcnt<(ST - 2) * DMA_PER_STEP>();
       lds_barrier();
-      compute(cur, kt, [&](int s) {
-        if (s < NP) issue(kt + ST - 1, nxt, s);
-      });
+      const StepAddr sa = step_addr(kt + ST - 1);
+      compute(cur, kt, [&](int n) { issue_at(sa, nxt, n); });
     };
     int kt = 0;
     for (; kt + 2 * ST - 1 <= nk; kt += ST) {
@@ -631,8 +652,9 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       lds_barrier();
       const bool more = kt + ST - 1 < nk;
       const Bufs<C> cur = pick(sm, kt % ST), nxt = pick(sm, (kt + ST - 1) % ST);
-      compute(cur, kt, [&](int s) {
-        if (more && s < NP) issue(kt + ST - 1, nxt, s);
+      const StepAddr sa = step_addr(more ? kt + ST - 1 : kt);
+      compute(cur, kt, [&](int n) {
+        if (more) issue_at(sa, nxt, n);
       });
     }
   } else {
