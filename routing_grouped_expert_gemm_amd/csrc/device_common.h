@@ -29,6 +29,13 @@ template <> MOK_DEV bf16_t f32_to<bf16_t>(float v) { return f32_to_bf16(v); }
 
 MOK_DEV int lane_id() { return __lane_id(); }
 
+// v unchanged, but opaque to the optimiser: expressions of it are not hoisted or shared across
+// this point.
+MOK_DEV int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Values every lane of the wave holds identically, moved to scalar registers.
 MOK_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 template <class T>

@@ -204,10 +204,10 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
 // ------------------------------------------------------------------------- GEMM tiles
 // Tile geometry. A workgroup of WAVES_M x WAVES_N waves computes a BM x BN block of the
 // stage's product; each wave a WM x WN block of 32 x 32 MFMA accumulators (FM x FN). Each K
-// step moves ROW_B bytes of every operand row into one of STAGES LDS buffers, either through
-// registers (global_load_dwordx4, then ds_write_b128) or by LDS-DMA (global_load_lds_dwordx4).
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_, bool DMA_,
-          int ISSUE_SPAN_ = 0>
+// step moves ROW_B bytes of every operand row into one of STAGES LDS buffers by LDS-DMA
+// (global_load_lds_dwordx4); loader wave w fills A rows [RA w, RA w + RA) and B rows
+// [RB w, RB w + RB), RPI rows per instruction.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_, int ISSUE_SPAN_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   // The LDS-DMA instructions of the next K step are spread evenly over the first ISSUE_SPAN
@@ -217,21 +217,23 @@ struct Cfg {
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int ROW_B = ROW_B_, STAGES = STAGES_;
-  static constexpr bool DMA = DMA_;
   static constexpr int CH = ROW_B / 16;            // 16-byte chunks per LDS row
   static constexpr int RPI = 64 / CH;              // rows one wave instruction covers
   static constexpr int SWZ_SHIFT = CH == 8 ? 1 : 2;
-  static constexpr int A_SLABS = BM / RPI / NW, B_SLABS = BN / RPI / NW;
+  static constexpr int RA = BM / NW, RB = BN / NW;
+  static constexpr int A_SLABS = RA / RPI, B_SLABS = RB / RPI;
   static_assert(CH == 8 || CH == 4, "64 or 128 bytes per row per K step");
   static_assert(FN % 2 == 0, "gate/up pairing needs an even number of N blocks per wave");
-  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "whole slabs per wave");
-  static_assert(BM == 64 * NW && BN == 64 * NW, "one scale word per lane per tile row");
-  static_assert(STAGES == 2 || STAGES == 4, "buffer rings of 2 or 4");
+  static_assert(RA % RPI == 0 && RB % RPI == 0, "whole slabs per wave");
+  static_assert((WN / 2) % RPI == 0, "a slab holds gate rows or up rows, not both");
+  static_assert(STAGES == 2, "two LDS stages: each K step waits for all requests (vmcnt 0)");
 };
+// Rows of the M tiles of a minibatch (the work list's tiling).
+constexpr int TILE_M = 256;
 // 256 x 256 tiles, 4 waves of 128 x 128 (16 accumulator blocks = 256 AGPRs per lane), one
 // workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs. Two 64 KB K stages of
 // 128 bytes per row (whole cache lines), filled by LDS-DMA.
-typedef Cfg<256, 256, 2, 2, 128, 2, true, 32> Big;
+typedef Cfg<256, 256, 2, 2, 128, 2, 32> Big;
 
 // Per element type: bytes per element, and the MFMA's K per instruction.
 template <Elem EL> struct Tr;
@@ -370,17 +372,20 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
 // One tile of the up (UP = true) or down (UP = false) stage of minibatch m.
 //  up:   the minibatch's rows x (gate, up rows of H columns n0 .. n0 + BN/2) -> H
 //  down: the minibatch's H rows x (W_down rows n0 .. n0 + BN) -> output columns
-// Wave w fills rows [64w, 64w+64) of each operand tile, RPI rows per instruction; lane L
-// carries row RPI*q + L / CH, LDS slot L % CH, so it fetches global chunk
-// (L % CH) ^ swz(row) and the swizzle costs nothing. Row addresses are a uniform base plus a
-// 32-bit offset. M and N tails: rows/columns past the end are clamped on load, skipped on
-// store.
+// The tile is M tile mt (rows [TILE_M mt, ...) of the minibatch) and N tile nt of the entry;
+// C::BM >= its valid rows. Loader wave w fills rows [RA w, RA w + RA) of the A tile and
+// [RB w, RB w + RB) of the B tile, RPI rows per instruction; lane L carries row RPI*q + L / CH
+// of slab q, LDS slot L % CH, so it fetches global chunk (L % CH) ^ swz(row) and the swizzle
+// costs nothing. Row addresses are a uniform base plus a 32-bit offset. M and N tails:
+// rows/columns past the end are clamped on load, skipped on store.
 template <Elem EL, bool UP, bool F32OUT, class C>
 MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   typedef Tr<EL> TR;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS, ST = C::STAGES, CH = C::CH;
-  constexpr int RPI = C::RPI, SWS = C::SWZ_SHIFT;
+  constexpr int RPI = C::RPI, SWS = C::SWZ_SHIFT, RA = C::RA, RB = C::RB;
+  static_assert(EL != Elem::FP8 || (RA == 64 && RB == 64),
+                "MX scales: lane L of loader wave w carries tile row 64 w + L");
   constexpr int KT = C::ROW_B / TR::ES;            // elements per K step
   constexpr int SUB = KT / TR::MK;                 // MFMA sub-steps per K step
   constexpr int SC_B = KT / 32;                    // MX scale bytes per row per K step
@@ -392,17 +397,22 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   const bool shared = g >= p.E_l;
   const int slot = m % p.n_slots;
   const int64_t ring_row0 = (int64_t)slot * p.mb;
-  const int n_mt = (rows + BM - 1) / BM;
+  const int n_mt = (rows + TILE_M - 1) / TILE_M;
   const int mt = local % n_mt, nt = local / n_mt;
-  const int m0 = mt * BM;
+  const int m0 = mt * TILE_M;
   const int rows_valid = min(BM, rows - m0);
-  const int tid = threadIdx.x, lane = tid & 63;
+  // The thread index is made opaque here and again before the epilogue: values derived from it
+  // are then computed per tile and per phase instead of being hoisted out of the tile loop,
+  // where they would live across the K loop, be spilled to scratch and be reloaded with a
+  // vmcnt(0) wait that also drains the epilogue's stores.
+  const int tid = opaque(threadIdx.x), lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
+  auto blk_row = [&](int i) { return wm * WM + 32 * i; };   // first tile row of block row i
   const int K = UP ? p.d : (shared ? p.I_sh : p.I);
   const int N = UP ? (shared ? p.I_sh : p.I) : p.d;   // output columns of the stage
   const int nk = K / KT;
-  // global byte of lane L's chunk in slab q: slot L % CH of row RPI*q + L / CH (+ 64 * wave)
+  // global byte of lane L's chunk in slab q: slot L % CH of row RPI*q + L / CH (+ RA or RB * w)
   auto chunk_b = [&](int q) {
     const int row = RPI * q + lane / CH;
     return ((lane % CH) ^ ((row >> SWS) & (CH - 1))) * 16;
@@ -425,7 +435,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   uint32_t a_off[A_SLABS];
 #pragma unroll
   for (int q = 0; q < A_SLABS; ++q) {
-    const int r = min(64 * wid + RPI * q + lane / CH, rows_valid - 1);
+    const int r = min(RA * wid + RPI * q + lane / CH, rows_valid - 1);
     int64_t row;
     if (UP && EL != Elem::FP8)
       row = shared ? p.own_begin + row0 + m0 + r : (int64_t)(p.route_ids[row0 + m0 + r] / p.k);
@@ -433,18 +443,19 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       row = r;
     a_off[q] = (uint32_t)(row * a_row_bytes) + chunk_b(q);
   }
-  // ---- B operand. Up: wave w loads gate (w even) or up (w odd) rows of H columns
-  // nt*BN/2 + (w/2)*WN/2 + [0, 64); this matches the accumulator pairing of the waves. Down:
-  // W_down rows nt*BN + 64w + [0, 64).
-  const char* b_base;
+  // ---- B operand. Up: B tile row R belongs to compute wave R / WN, whose WN rows are WN/2
+  // gate rows then the WN/2 up rows of the same H columns nt*BN/2 + (R / WN)*WN/2 + [0, WN/2):
+  // each accumulator block of gate then pairs with the block FN/2 further holding up. A slab
+  // lies wholly in the gate or the up half (b_up_slab). Down: W_down rows nt*BN + R.
+  const char* b_base;              // down: W_down (segment 0); up: gate rows
+  const char* b_up = nullptr;      // up: up rows
   int64_t b_row_bytes, b_seg_len = K, b_seg_stride = 0;
-  int b_n0;
+  auto b_up_slab = [&](int q) { return ((RB * wid + RPI * q) % WN) >= WN / 2; };
   if (UP) {
-    const bool uph = (wid & 1) != 0;
-    const void* W = shared ? (uph ? p.su : p.sg) : (uph ? p.wu : p.wg);
-    b_base = (const char*)W + (shared ? 0 : (int64_t)g * p.I * p.d * TR::ES);
+    const int64_t e_off = shared ? 0 : (int64_t)g * p.I * p.d * TR::ES;
+    b_base = (const char*)(shared ? p.sg : p.wg) + e_off;
+    b_up = uniform_ptr((const char*)(shared ? p.su : p.wu) + e_off);
     b_row_bytes = (int64_t)p.d * TR::ES;
-    b_n0 = nt * (BN / 2) + (wid >> 1) * (WN / 2);
   } else {
     if (shared) {
       b_base = (const char*)p.sd;
@@ -455,13 +466,17 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       b_base = (const char*)p.wd + (int64_t)g * p.d * p.I * TR::ES;
       b_row_bytes = (int64_t)p.I * TR::ES;
     }
-    b_n0 = nt * BN + 64 * wid;
   }
   b_base = uniform_ptr(b_base);
+  // first B row (weight row) of slab q's lanes, lane offset excluded
+  auto b_row0 = [&](int q) {
+    const int R = RB * wid + RPI * q;
+    return UP ? nt * (BN / 2) + (R / WN) * (WN / 2) + (R % (WN / 2)) : nt * BN + R;
+  };
   uint32_t b_off[B_SLABS];
 #pragma unroll
   for (int q = 0; q < B_SLABS; ++q) {
-    const int n = min(b_n0 + RPI * q + lane / CH, N - 1);
+    const int n = min(b_row0(q) + lane / CH, N - 1);
     b_off[q] = (uint32_t)(n * b_row_bytes) + chunk_b(q);
   }
   // ---- MX scales: lane L of wave w carries tile row 64w + L. A K step needs SC_B scale bytes
@@ -470,13 +485,13 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   const uint8_t* b_sc_base = nullptr;
   uint32_t a_sc_off = 0, b_sc_off = 0;
   if (EL == Elem::FP8) {
-    const int r = min(64 * wid + lane, rows_valid - 1);
+    const int r = min(RA * wid + lane, rows_valid - 1);
     const int64_t a_sc_row = UP ? p.d / 32 : p.Hld / 32;
     a_sc_base = (UP ? p.A_sc : p.H_sc) + (ring_row0 + m0) * a_sc_row;
     a_sc_off = (uint32_t)(r * a_sc_row);
     int64_t b_sc_row;
     if (UP) {
-      const bool uph = (wid & 1) != 0;
+      const bool uph = b_up_slab(0);               // the wave's 64 rows are all gate or all up
       const uint8_t* S = shared ? (uph ? p.su_sc : p.sg_sc) : (uph ? p.wu_sc : p.wg_sc);
       b_sc_row = p.d / 32;
       b_sc_base = S + (shared ? 0 : (int64_t)g * p.I * b_sc_row);
@@ -484,22 +499,26 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       b_sc_row = shared ? p.I_seg / 32 : p.I / 32;
       b_sc_base = shared ? p.sd_sc : p.wd_sc + (int64_t)g * p.d * b_sc_row;
     }
-    const int n = min(b_n0 + lane, N - 1);
+    const int n = min(b_row0(0) + lane, N - 1);
     b_sc_off = (uint32_t)(n * b_sc_row);
     a_sc_base = uniform_ptr(a_sc_base);
     b_sc_base = uniform_ptr(b_sc_base);
   }
-  // epilogue row table (down stage)
-  if (!UP && tid < BM && tid < rows_valid) {
-    if (shared) {
-      sm.row_dst[tid] = row0 + m0 + tid;
-      sm.row_w[tid] = 1.0f;
-    } else {
-      const int32_t route = p.route_ids[row0 + m0 + tid];
-      sm.row_dst[tid] = route;
-      sm.row_w[tid] = p.topk_w[route];
+  // epilogue row table (down stage): destination row and routing weight of tile row tid. The
+  // route id is loaded here and written to LDS after the first K step's barrier (by then every
+  // wave is done with the previous tile's epilogue, and the load, older than that step's DMA,
+  // has landed); its weight is loaded then and written after the K loop. Neither load holds up
+  // the K loop.
+  const bool rt_lane = !UP && tid < BM && tid < rows_valid;
+  int32_t rt_dst = 0;
+  float rt_w = 1.0f;
+  if (rt_lane) rt_dst = shared ? row0 + m0 + tid : p.route_ids[row0 + m0 + tid];
+  auto at_step0 = [&]() {
+    if (rt_lane) {
+      sm.row_dst[tid] = rt_dst;
+      if (!shared) rt_w = p.topk_w[rt_dst];
     }
-  }
+  };
 
   // address pieces of K step kt
   struct StepAddr { uint32_t ka, kb, sca, scb; const char* b_seg; const uint8_t* bs_seg; };
@@ -525,10 +544,11 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   auto issue_one = [&](const StepAddr& s, const Bufs<C>& b, int q) {
     __builtin_amdgcn_sched_barrier(0);             // keeps the DMA between its two MFMAs
     if (q < A_SLABS) {
-      dma_b128(a_base, a_off[q] + s.ka, uniform(lds_addr(&b.A[64 * wid][0])) + 1024 * q);
+      dma_b128(a_base, a_off[q] + s.ka, uniform(lds_addr(&b.A[RA * wid][0])) + 1024 * q);
     } else if (q < A_SLABS + B_SLABS) {
       const int r = q - A_SLABS;
-      dma_b128(s.b_seg, b_off[r] + s.kb, uniform(lds_addr(&b.B[64 * wid][0])) + 1024 * r);
+      const char* bb = (UP && b_up_slab(r)) ? b_up : s.b_seg;
+      dma_b128(bb, b_off[r] + s.kb, uniform(lds_addr(&b.B[RB * wid][0])) + 1024 * r);
     } else if (q == A_SLABS + B_SLABS) {
       dma_b32(a_sc_base, a_sc_off + s.sca, uniform(lds_addr(&b.As[64 * wid])));
     } else {
@@ -546,31 +566,6 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
 #pragma unroll
     for (int q = 0; q < DMA_PER_STEP; ++q) issue_one(s, b, q);
   };
-  // (b) register staging: global -> registers, later registers -> LDS
-  uint4 ra[C::DMA ? 1 : A_SLABS], rb[C::DMA ? 1 : B_SLABS];
-  uint32_t rsa = 0, rsb = 0;
-  auto gload = [&](int kt) {
-    const StepAddr s = step_addr(kt);
-#pragma unroll
-    for (int q = 0; q < A_SLABS; ++q) ra[q] = *(const uint4*)(a_base + (uint32_t)(a_off[q] + s.ka));
-#pragma unroll
-    for (int q = 0; q < B_SLABS; ++q) rb[q] = *(const uint4*)(s.b_seg + (uint32_t)(b_off[q] + s.kb));
-    if (EL == Elem::FP8) {
-      rsa = *(const uint32_t*)(a_sc_base + (uint32_t)(a_sc_off + s.sca));
-      rsb = *(const uint32_t*)(s.bs_seg + (uint32_t)(b_sc_off + s.scb));
-    }
-  };
-  auto lstore = [&](const Bufs<C>& b) {
-#pragma unroll
-    for (int q = 0; q < A_SLABS; ++q) b.A[64 * wid + RPI * q + lane / CH][lane % CH] = ra[q];
-#pragma unroll
-    for (int q = 0; q < B_SLABS; ++q) b.B[64 * wid + RPI * q + lane / CH][lane % CH] = rb[q];
-    if (EL == Elem::FP8) {
-      b.As[64 * wid + lane] = rsa;
-      b.Bs[64 * wid + lane] = rsb;
-    }
-  };
-
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -589,7 +584,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   // the K loop issues the next step's LDS-DMA there, a few instructions at a time, so that no
   // MFMA waits behind a burst of memory instructions.
   auto compute = [&](const Bufs<C>& b, int kt, auto&& after) {
-    const char* a_buf = (const char*)&b.A[wm * WM + l32][0];
+    const char* a_buf = (const char*)&b.A[blk_row(0) + l32][0];
     const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
     const int sc_shift = 8 * (((uint32_t)kt * SC_B) & 3);
     uint4 fa[2][FM][2], fb[2][FN][2];
@@ -602,7 +597,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
         fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c0);
         if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c1);
         if (EL == Elem::FP8)
-          asc[f][i] = (b.As[wm * WM + i * 32 + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
+          asc[f][i] = (b.As[blk_row(i) + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -625,7 +620,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     }
   };
 
-  if constexpr (C::DMA) {
+  {
     // K loop over a ring of ST buffers. Step kt: wait until this wave's DMA of kt has landed
     // (later steps' DMAs stay in flight), barrier (every wave's DMA of kt landed; every wave
     // done computing kt - 1), issue step kt + ST - 1 into the buffer kt - 1 used, compute kt.
@@ -636,6 +631,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     auto steady = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
       wait_vmcnt<(ST - 2) * DMA_PER_STEP>();
       lds_barrier();
+      if (kt == 0) at_step0();
       const StepAddr sa = step_addr(kt + ST - 1);
       compute(cur, kt, [&](int n) { issue_at(sa, nxt, n); });
     };
@@ -645,11 +641,9 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       for (int q = 0; q < ST; ++q) steady(kt + q, sm.buf[q], sm.buf[(q + ST - 1) % ST]);
     }
     for (; kt < nk; ++kt) {     // the last steps, buffers chosen at run time
-      const int ahead = min(nk - 1 - kt, ST - 2);
-      if (ahead >= 2) wait_vmcnt<2 * DMA_PER_STEP>();
-      else if (ahead == 1) wait_vmcnt<DMA_PER_STEP>();
-      else wait_vmcnt<0>();
+      wait_vmcnt<0>();
       lds_barrier();
+      if (kt == 0) at_step0();
       const bool more = kt + ST - 1 < nk;
       const Bufs<C> cur = pick(sm, kt % ST), nxt = pick(sm, (kt + ST - 1) % ST);
       const StepAddr sa = step_addr(more ? kt + ST - 1 : kt);
@@ -657,31 +651,19 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
         if (more) issue_at(sa, nxt, n);
       });
     }
-  } else {
-    // Two buffers, unrolled by two: the loads of step kt + 1 are in flight (registers) while
-    // step kt computes; then they are written to the other buffer and everyone synchronises.
-    static_assert(ST == 2, "register staging uses two buffers");
-    gload(0);
-    lstore(sm.buf[0]);
-    __syncthreads();
-    auto two = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
-      const bool more = kt + 1 < nk;
-      if (more) gload(kt + 1);
-      compute(cur, kt, [](int) {});
-      if (more) lstore(nxt);
-      __syncthreads();
-    };
-    int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-      two(kt, sm.buf[0], sm.buf[1]);
-      two(kt + 1, sm.buf[1], sm.buf[0]);
-    }
-    if (kt < nk) two(kt, sm.buf[0], sm.buf[1]);
   }
 
   // ---- epilogue. Value 4g + r of block (i, j) is (row 32i + l32, column 32j + 8g + 4h + r) of
-  // the wave's block (see mfma_step).
-  const int r_lane = wm * WM + l32;                   // tile row of block row i = 0
+  // the wave's block (see mfma_step). One barrier: every wave is past the K loop (both operand
+  // buffers are free) and the row table is complete. There is none at the end: the staging
+  // uses buffer 1 only, the next tile's first DMA fills buffer 0, and that tile writes buffer 1
+  // and the row table only after its first K step's barrier, which every wave reaches after
+  // its epilogue.
+  if (rt_lane) sm.row_w[tid] = rt_w;
+  __syncthreads();
+  {
+  const int lane = opaque(threadIdx.x) & 63, h = lane >> 5, l32 = lane & 31;
+  auto r_of = [&](int i) { return blk_row(i) + l32; };   // tile row of the lane in block row i
   if constexpr (!F32OUT) {
     // bf16 (or MXFP8 H) outputs: each wave stages 32 rows at a time through its own LDS region
     // (the operand buffers are free once every wave is past the K loop), four columns per
@@ -697,22 +679,19 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     constexpr int LPR = CW / VPL;                     // lanes per row in the store phase
     constexpr int SRPI = 64 / LPR;                    // rows per store pass
     static_assert(!MX || LPR % 4 == 0, "whole 32-column blocks per row");
-    static_assert(32 * STRIDE <= BM * C::ROW_B, "a wave's 32-row pass fits one operand buffer");
-    __syncthreads();
+    static_assert(32 * STRIDE <= 16384, "a wave's 32-row pass fits a quarter of buffer 1");
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) u32x2 lds_u2;
     typedef __attribute__((address_space(3))) u32x4 lds_u4;
-    // wave w's region: operand buffer w / 2, A half (w even) or B half (w odd); chosen with
-    // selects so that no private array is indexed at run time
-    char* const rA = (wid >> 1) ? (char*)sm.buf[1].A : (char*)sm.buf[0].A;
-    char* const rB = (wid >> 1) ? (char*)sm.buf[1].B : (char*)sm.buf[0].B;
-    char* region = (wid & 1) ? rB : rA;
+    // wave w's region: 16 KB at (w / 2) * 16 KB into the A half (w even) or the B half (w odd)
+    // of operand buffer 1 (the 256 x 256 configuration's buffers, which every view borrows)
+    char* region = ((wid & 1) ? (char*)sm.buf[1].B : (char*)sm.buf[1].A) + (wid >> 1) * 16384;
     const int col0 = UP ? nt * (BN / 2) + wn * (WN / 2) : nt * BN + wn * WN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       float rw = 1.0f;                                  // routing weight of the lane's row
-      if (!UP) rw = sm.row_w[min(r_lane + i * 32, BM - 1)];
+      if (!UP) rw = sm.row_w[min(r_of(i), BM - 1)];
 #pragma unroll
       for (int j = 0; j < JB; ++j)
 #pragma unroll
@@ -740,7 +719,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       for (int q = 0; q < 32 / SRPI; ++q) {
         const int rr = q * SRPI + lane / LPR;           // row within the pass
         const int c = (lane % LPR) * VPL;               // first column of the lane's values
-        const int r = wm * WM + i * 32 + rr;            // row within the tile
+        const int r = blk_row(i) + rr;                  // row within the tile
         const char* src = region + rr * STRIDE + c * VB;
         if constexpr (MX) {
           const u32x4 lo = *(const lds_u4*)src, hi = *(const lds_u4*)(src + 16);
@@ -775,7 +754,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     constexpr int JB = UP ? FN / 2 : FN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = r_lane + i * 32;
+      const int r = r_of(i);
       if (r >= rows_valid) continue;
       float* dst_row;
       float rw = 1.0f;
@@ -800,7 +779,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
         }
     }
   }
-  __syncthreads();  // LDS (row table, operand buffers) is reused by the next tile
+  }
 }
 
 // LDS of a tile workgroup: the STAGES operand buffers as separate objects (only the first
