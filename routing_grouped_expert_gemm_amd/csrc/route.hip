@@ -14,13 +14,16 @@
 namespace mok {
 
 // ----------------------------------------------------------------------------- logits
-// One wave: 64 tokens (one per lane) x 8 experts. Per chunk of 16 values of i, lane r*16 + j
-// (4 rows of 16 lanes) holds W_r[e][i0 + j] as float32 for each of the wave's 8 experts (one
-// 2-byte load and one shift per expert), and its own token's 16 values of x. The FMA of step
-// i0 + j takes W_r[e][i0 + j] straight from lane j of the lane's row (DPP row_newbcast), so one
-// VALU instruction is one step of one chain for 64 tokens. The next chunk's loads are in flight
-// while a chunk computes. Every chain takes i strictly in ascending order from +0.
-constexpr int RT_TOK = 64, RT_EXP = 8, RT_K = 16;
+// One wave: 64 tokens (one per lane) x 8 experts. A chunk is 16 values of i. Within each row
+// of 16 lanes, lane L holds W_r[e0 + L/2][i0 + 8 (L%2) + q], q = 0..7, as float32 (one 16-byte
+// load and 8 shifts), so the row holds the chunk's 8 x 16 weights once; the FMA of expert e at
+// i0 + j takes its weight straight from register j%8 of lane 2e + j/8 of the row (DPP
+// row_newbcast), so one VALU instruction is one step of one chain for 64 tokens. Each lane
+// also loads its own token's 16 values of x. Chunks are loaded RT_NPRE ahead into a ring of
+// registers (one wave per SIMD: nothing else hides the load latency). The 4 waves of a
+// workgroup share their 64 tokens, so x rows are fetched once per workgroup. Every chain
+// takes i strictly in ascending order from +0.
+constexpr int RT_TOK = 64, RT_EXP = 8, RT_K = 16, RT_NPRE = 4;
 
 // acc = fma(w of lane J of this 16-lane row, x, acc): the product is exact either way round.
 template <int J>
@@ -29,38 +32,58 @@ MOK_DEV void fma_bcast(float& acc, float w, float x) {
                : "+v"(acc) : "v"(w), "v"(x), "i"(J));
 }
 
-template <class T> struct RowChunk;      // 16 consecutive values of a row
-template <> struct RowChunk<bf16_t> {
-  uint4 r[2];
-  MOK_DEV void load(const bf16_t* p) { r[0] = *(const uint4*)p; r[1] = *(const uint4*)(p + 8); }
-  MOK_DEV float get(int q) const {     // q compile-time after unrolling
-    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
-    return (q & 1) ? __uint_as_float(w[q >> 1] & 0xFFFF0000u) : __uint_as_float(w[q >> 1] << 16);
+// Raw (unconverted) loads of one chunk: 16 values of the lane's token row, and the lane's 8
+// weights.
+template <class T> struct RtRaw;
+template <> struct RtRaw<bf16_t> {
+  uint4 x[2];
+  uint4 w;
+  MOK_DEV void load(const bf16_t* xp, const bf16_t* wp) {
+    x[0] = *(const uint4*)xp;
+    x[1] = *(const uint4*)(xp + 8);
+    w = *(const uint4*)wp;
+  }
+  MOK_DEV static float bf(uint32_t u, int hi) {
+    return hi ? __uint_as_float(u & 0xFFFF0000u) : __uint_as_float(u << 16);
+  }
+  MOK_DEV float xv(int q) const {     // q compile-time after unrolling
+    const uint4 v = x[q >> 3];
+    const int d = (q >> 1) & 3;
+    return bf(d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w, q & 1);
+  }
+  MOK_DEV float wv(int q) const {
+    const int d = q >> 1;
+    return bf(d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w, q & 1);
   }
 };
-template <> struct RowChunk<float> {
-  float4 r[4];
-  MOK_DEV void load(const float* p) {
+template <> struct RtRaw<float> {
+  float4 x[4];
+  float4 w[2];
+  MOK_DEV void load(const float* xp, const float* wp) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = *(const float4*)(p + 4 * q);
+    for (int q = 0; q < 4; ++q) x[q] = *(const float4*)(xp + 4 * q);
+    w[0] = *(const float4*)wp;
+    w[1] = *(const float4*)(wp + 4);
   }
-  MOK_DEV float get(int q) const {
-    const float4 v = r[q >> 2];
+  MOK_DEV static float pick(const float4 v, int q) {
     return (q & 3) == 0 ? v.x : (q & 3) == 1 ? v.y : (q & 3) == 2 ? v.z : v.w;
   }
+  MOK_DEV float xv(int q) const { return pick(x[q >> 2], q); }
+  MOK_DEV float wv(int q) const { return pick(w[q >> 2], q); }
 };
 
-template <class T, int J>
-MOK_DEV void chunk_step(float (&acc)[RT_EXP], const float (&wv)[RT_EXP], const RowChunk<T>& xc) {
-  const float xj = xc.get(J);
-#pragma unroll
-  for (int e = 0; e < RT_EXP; ++e) fma_bcast<J>(acc[e], wv[e], xj);
+template <int J, int... Es>
+MOK_DEV void step_experts(float (&acc)[RT_EXP], const float (&wf)[8], float xj,
+                          std::integer_sequence<int, Es...>) {
+  (fma_bcast<2 * Es + J / 8>(acc[Es], wf[J % 8], xj), ...);
 }
 
 template <class T, int... J>
-MOK_DEV void chunk_all(float (&acc)[RT_EXP], const float (&wv)[RT_EXP], const RowChunk<T>& xc,
-                       std::integer_sequence<int, J...>) {
-  (chunk_step<T, J>(acc, wv, xc), ...);
+MOK_DEV void chunk_all(float (&acc)[RT_EXP], const RtRaw<T>& c, std::integer_sequence<int, J...>) {
+  float wf[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) wf[q] = c.wv(q);
+  (step_experts<J>(acc, wf, c.xv(J), std::make_integer_sequence<int, RT_EXP>{}), ...);
 }
 
 template <class T>
@@ -75,38 +98,41 @@ __global__ __launch_bounds__(256) void k_router_logits(const T* __restrict__ x,
   if (tb * RT_TOK >= n_tok) return;
   const int64_t t = tb * RT_TOK + lane;
   const T* xr = x + min(t, n_tok - 1) * (int64_t)d;
-  const T* wrow[RT_EXP];
-#pragma unroll
-  for (int e = 0; e < RT_EXP; ++e) wrow[e] = wr + (int64_t)min(e0 + e, E - 1) * d;
+  // this lane's weight row and offset within a chunk
+  const T* wl = wr + (int64_t)min(e0 + j / 2, E - 1) * d + 8 * (j & 1);
   float acc[RT_EXP];
 #pragma unroll
   for (int e = 0; e < RT_EXP; ++e) acc[e] = 0.0f;
-  const int dv = (d % RT_K) == 0 ? d : 0;          // whole 16-value chunks (aligned rows)
-  // chunk loads: x from the lane's row; W_r value j of each expert row, at a uniform base plus a
-  // 32-bit lane offset. Two named buffers alternate so the next chunk's loads are in flight
-  // while the current one computes (the scheduling barriers keep that order).
-  auto load = [&](RowChunk<T>& xc, float (&wv)[RT_EXP], int i0) {
-    xc.load(xr + i0);
+  const int nc = (d % RT_K) == 0 ? d / RT_K : 0;   // whole 16-value chunks (aligned rows)
+  if (nc > 0) {
+    RtRaw<T> ring[RT_NPRE];
 #pragma unroll
-    for (int e = 0; e < RT_EXP; ++e)
-      wv[e] = load_as_f32<T>((const T*)((const char*)wrow[e] + (uint32_t)((i0 + j) * sizeof(T))));
-  };
-  if (dv > 0) {
-    RowChunk<T> xa, xb;
-    float wa[RT_EXP], wb[RT_EXP];
-    load(xa, wa, 0);
-    for (int i0 = 0; i0 < dv; i0 += 2 * RT_K) {
-      load(xb, wb, min(i0 + RT_K, dv - RT_K));
-      __builtin_amdgcn_sched_barrier(0);
-      chunk_all<T>(acc, wa, xa, std::make_integer_sequence<int, RT_K>{});
-      __builtin_amdgcn_sched_barrier(0);
-      load(xa, wa, min(i0 + 2 * RT_K, dv - RT_K));
-      __builtin_amdgcn_sched_barrier(0);
-      if (i0 + RT_K < dv) chunk_all<T>(acc, wb, xb, std::make_integer_sequence<int, RT_K>{});
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < RT_NPRE; ++q) {
+      const int c = min(q, nc - 1);
+      ring[q].load(xr + c * RT_K, wl + c * RT_K);
+    }
+    // ring slot c % NPRE holds chunk c; after computing it, chunk c + NPRE is loaded into it
+    // (clamped to the last chunk past the end: a harmless reload). Unrolled by NPRE so every
+    // slot index is static; the scheduling barriers keep each load after the FMAs that read
+    // its slot and ahead of the next chunk's FMAs.
+    for (int c0 = 0; c0 < nc; c0 += RT_NPRE) {
+#pragma unroll
+      for (int q = 0; q < RT_NPRE; ++q) {
+        const int c = c0 + q;
+        if (c < nc) {
+          chunk_all<T>(acc, ring[q], std::make_integer_sequence<int, RT_K>{});
+          __builtin_amdgcn_sched_barrier(0);
+          const int cn = min(c + RT_NPRE, nc - 1);
+          ring[q].load(xr + cn * RT_K, wl + cn * RT_K);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   }
-  for (int i = dv; i < d; ++i) {                   // rows that are not whole 16-value chunks
+  const T* wrow[RT_EXP];
+#pragma unroll
+  for (int e = 0; e < RT_EXP; ++e) wrow[e] = wr + (int64_t)min(e0 + e, E - 1) * d;
+  for (int i = nc * RT_K; i < d; ++i) {            // rows that are not whole 16-value chunks
     const float xi = load_as_f32<T>(xr + i);
 #pragma unroll
     for (int e = 0; e < RT_EXP; ++e) acc[e] = __builtin_fmaf(xi, load_as_f32<T>(wrow[e] + i), acc[e]);

@@ -39,7 +39,8 @@ def test_seeded_generator_same_bits_on_gpu_and_cpu():
 # --------------------------------------------------------------------- routing
 
 @pytest.mark.parametrize("dtype,T,d,E,k", [("fp32", 64, 128, 8, 2), ("bf16", 300, 192, 64, 6),
-                                           ("bf16", 97, 64, 130, 8), ("fp32", 33, 100, 5, 5)])
+                                           ("bf16", 97, 64, 130, 8), ("fp32", 33, 100, 5, 5),
+                                           ("bf16", 1000, 2048, 64, 6), ("fp32", 130, 272, 20, 4)])
 def test_route_bit_exact(dtype, T, d, E, k):
     import routing_grouped_expert_gemm_amd as mok
     tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
