@@ -827,32 +827,52 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
 }
 
 // ------------------------------------------------------------------------- MXFP8 gather
-// Pull-gather + quantise of rows [r_begin, r_end) of minibatch m: the token rows of the pool
-// picked by route id (or the own rows, for the shared experts) become MXFP8 rows of the
-// minibatch's ring slot. Each lane takes 8 consecutive elements; the 4 lanes of a 32-element
-// block are an aligned quad, and consecutive lanes cover consecutive 16 bytes of a row.
+// Pull-gather + quantise of rows [r_begin, r_end) (at most G_ROWS) of minibatch m: the token
+// rows of the pool picked by route id (or the own rows, for the shared experts) become MXFP8
+// rows of the minibatch's ring slot. Called by every thread of the workgroup. The rows' token
+// indices are looked up once into LDS; then each lane takes 8 consecutive elements of a row per
+// item (the 4 lanes of a 32-element block are an aligned quad; consecutive lanes cover
+// consecutive 16 bytes), GQ_UNROLL items with their loads in flight together.
+constexpr int GQ_UNROLL = 4;
 MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r_end, int wave,
                                   int n_waves) {
+  __shared__ int64_t tok_row[G_ROWS];
   const int cap = p.max_mb;
   const int32_t g = wl_group(p.wl, cap)[m], first = wl_row0(p.wl, cap)[m];
-  const int per_row = p.d / 8;                       // lanes per row (a multiple of 4)
-  const int64_t total = (int64_t)(r_end - r_begin) * per_row;
+  const int rows = r_end - r_begin;
+  const int t = wave * 64 + (threadIdx.x & 63);
+  __syncthreads();                                   // the previous call's readers are done
+  if (t < rows) {
+    const int r = r_begin + t;
+    tok_row[t] = (g >= p.E_l ? p.own_begin + first + r : (int64_t)(p.route_ids[first + r] / p.k)) * p.d;
+  }
+  __syncthreads();
+  const int per_row = p.d / 8;                       // quads per row (a multiple of 4)
+  const int total = rows * per_row;
   const int nt = 64 * n_waves;
-  const int64_t n_iter = (total + nt - 1) / nt;      // the same for every lane of a wave
-  int64_t q = (int64_t)wave * 64 + (threadIdx.x & 63);
-  for (int64_t it = 0; it < n_iter; ++it, q += nt) {
-    const bool ok = q < total;
-    const int r = r_begin + (ok ? (int)(q / per_row) : 0), c = ok ? (int)(q % per_row) : 0;
-    const int64_t tok = g >= p.E_l ? p.own_begin + first + r
-                                   : (int64_t)(p.route_ids[first + r] / p.k);
-    const uint4 raw = ok ? *(const uint4*)((const bf16_t*)p.x + tok * p.d + 8 * c)
-                         : make_uint4(0, 0, 0, 0);
-    int sh;
-    const uint2 codes = quantize_quad8(raw, &sh);
-    if (ok) {
-      const int64_t ring_row = (int64_t)(m % p.n_slots) * p.mb + r;
-      *(uint2*)(p.A_codes + ring_row * p.d + 8 * c) = codes;
-      if ((c & 3) == 0) p.A_sc[ring_row * (p.d / 32) + c / 4] = (uint8_t)(sh + 127);
+  const int64_t ring0 = (int64_t)(m % p.n_slots) * p.mb + r_begin;
+  const int n_iter = (total + GQ_UNROLL * nt - 1) / (GQ_UNROLL * nt);   // same for every lane
+  for (int it = 0; it < n_iter; ++it) {
+    uint4 raw[GQ_UNROLL];
+    int rr[GQ_UNROLL], cc[GQ_UNROLL];
+#pragma unroll
+    for (int u = 0; u < GQ_UNROLL; ++u) {
+      const int q = t + (it * GQ_UNROLL + u) * nt;
+      const bool ok = q < total;
+      rr[u] = ok ? q / per_row : 0;
+      cc[u] = ok ? q - rr[u] * per_row : -1;
+      raw[u] = ok ? *(const uint4*)((const bf16_t*)p.x + tok_row[rr[u]] + 8 * cc[u])
+                  : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < GQ_UNROLL; ++u) {
+      int sh;
+      const uint2 codes = quantize_quad8(raw[u], &sh);   // all 4 lanes of a quad share cc's validity
+      if (cc[u] >= 0) {
+        const int64_t hr = ring0 + rr[u];
+        *(uint2*)(p.A_codes + hr * p.d + 8 * cc[u]) = codes;
+        if ((cc[u] & 3) == 0) p.A_sc[hr * (p.d / 32) + cc[u] / 4] = (uint8_t)(sh + 127);
+      }
     }
   }
 }
@@ -861,7 +881,7 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
 __global__ __launch_bounds__(256) void k_gather_quantize(ExpertPass p) {
   const int n_mb = p.wl[WL_N_MB];
   const int32_t* nr = wl_rows(p.wl, p.max_mb);
-  const int per_block = 4 * 8;                  // rows per workgroup per minibatch pass
+  const int per_block = 16;                     // rows per work item (many items: even spread)
   const int chunks = (p.mb + per_block - 1) / per_block;
   for (int64_t q = blockIdx.x; q < (int64_t)n_mb * chunks; q += gridDim.x) {
     const int m = (int)(q / chunks), c = (int)(q % chunks);
@@ -1030,7 +1050,7 @@ static void record(void* const* ev, int i, hipStream_t s) {
 template <Elem EL, bool F32OUT>
 static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
   if (EL == Elem::FP8 && !p.ring)
-    hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 4), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 8), dim3(256), 0, s, p);
   record(ev, 2 * 6 + 1, s);
   record(ev, 2 * 3, s);
   if (p.ring) {
