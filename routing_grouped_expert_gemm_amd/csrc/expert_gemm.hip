@@ -378,8 +378,34 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
 // of slab q, LDS slot L % CH, so it fetches global chunk (L % CH) ^ swz(row) and the swizzle
 // costs nothing. Row addresses are a uniform base plus a 32-bit offset. M and N tails:
 // rows/columns past the end are clamped on load, skipped on store.
-template <Elem EL, bool UP, bool F32OUT, class C>
-MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
+// Pool rows of the A-operand slabs of tile `entry` for the calling lane (gate/up stage, bf16 or
+// float32, routed minibatch): the route ids it loads (divided by k at the use). Issued one tile
+// ahead, so that a tile's first DMA does not wait on this dependent load.
+template <Elem EL, bool UP, class C>
+MOK_DEV void prefetch_a_rows(const ExpertPass& p, const int4 entry, int32_t (&route)[C::A_SLABS]) {
+  if constexpr (UP && EL != Elem::FP8) {
+    const int local = uniform(entry.y) & ((1 << KIND_SHIFT) - 1), row0 = uniform(entry.z);
+    const int g = uniform(entry.w >> 16), rows = uniform(entry.w & 0xFFFF);
+    const int n_mt = (rows + TILE_M - 1) / TILE_M;
+    const int m0 = (local % n_mt) * TILE_M, rows_valid = min(C::BM, rows - m0);
+    const int tid = opaque(threadIdx.x), lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int q = 0; q < C::A_SLABS; ++q) {
+      const int r = min(C::RA * wid + C::RPI * q + lane / C::CH, rows_valid - 1);
+      route[q] = g < p.E_l ? p.route_ids[row0 + m0 + r] : 0;
+    }
+  }
+}
+
+// One tile. pre: the route ids prefetch_a_rows loaded for this tile. after_step(s) runs after
+// the barrier of K steps s = 0 and 1 (for a one-step tile, s = 1 runs after the K loop): the
+// stage kernel issues the next tile's route-id loads at step 0 and parks them in LDS at step 1,
+// when they have landed (they are older than that step's DMA), so they hold no register across
+// the K loop.
+template <Elem EL, bool UP, bool F32OUT, class C, class F>
+MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
+                      const int32_t (&pre)[C::A_SLABS], F&& after_step) {
   typedef Tr<EL> TR;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS, ST = C::STAGES, CH = C::CH;
@@ -438,7 +464,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
     const int r = min(RA * wid + RPI * q + lane / CH, rows_valid - 1);
     int64_t row;
     if (UP && EL != Elem::FP8)
-      row = shared ? p.own_begin + row0 + m0 + r : (int64_t)(p.route_ids[row0 + m0 + r] / p.k);
+      row = shared ? p.own_begin + row0 + m0 + r : (int64_t)(pre[q] / p.k);
     else
       row = r;
     a_off[q] = (uint32_t)(row * a_row_bytes) + chunk_b(q);
@@ -518,6 +544,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       sm.row_dst[tid] = rt_dst;
       if (!shared) rt_w = p.topk_w[rt_dst];
     }
+    after_step(0);
   };
 
   // address pieces of K step kt
@@ -632,6 +659,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       wait_vmcnt<(ST - 2) * DMA_PER_STEP>();
       lds_barrier();
       if (kt == 0) at_step0();
+      if (kt == 1) after_step(1);
       const StepAddr sa = step_addr(kt + ST - 1);
       compute(cur, kt, [&](int n) { issue_at(sa, nxt, n); });
     };
@@ -644,6 +672,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
       wait_vmcnt<0>();
       lds_barrier();
       if (kt == 0) at_step0();
+      if (kt == 1) after_step(1);
       const bool more = kt + ST - 1 < nk;
       const Bufs<C> cur = pick(sm, kt % ST), nxt = pick(sm, (kt + ST - 1) % ST);
       const StepAddr sa = step_addr(more ? kt + ST - 1 : kt);
@@ -659,6 +688,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry) {
   // uses buffer 1 only, the next tile's first DMA fills buffer 0, and that tile writes buffer 1
   // and the row table only after its first K step's barrier, which every wave reaches after
   // its epilogue.
+  if (nk == 1) after_step(1);
   if (rt_lane) sm.row_w[tid] = rt_w;
   __syncthreads();
   {
@@ -816,11 +846,33 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
   const int b = blockIdx.x;
   int32_t t = (b & 7) * (G >> 3) + (b >> 3);
   if (t >= total) return;
+  // per-lane parking of the next tile's route ids (each lane reads back only its own)
+  constexpr bool PRE = UP && EL != Elem::FP8;
+  __shared__ int32_t pre_lds[PRE ? C::A_SLABS : 1][C::NT];
+  const int tid = threadIdx.x;
   int4 cur = tab[t];
+  int32_t pre[C::A_SLABS];
+  prefetch_a_rows<EL, UP, C>(p, cur, pre);
   while (t < total) {
     const int32_t tn = t + G;
-    const int4 nxt = tn < total ? tab[tn] : cur;   // next tile's entry, loaded before this tile
-    run_tile<EL, UP, F32OUT, C>(p, sm, cur);
+    const bool more = tn < total;
+    const int4 nxt = more ? tab[tn] : cur;    // next tile's entry, loaded before this tile
+    int32_t pn[C::A_SLABS];
+    run_tile<EL, UP, F32OUT, C>(p, sm, cur, pre, [&](int s) {
+      if constexpr (PRE) {
+        if (s == 0) {
+          // by the first barrier the entry load (older than the first DMA) has landed
+          if (more) prefetch_a_rows<EL, UP, C>(p, nxt, pn);
+        } else if (more) {
+#pragma unroll
+          for (int q = 0; q < C::A_SLABS; ++q) pre_lds[q][tid] = pn[q];
+        }
+      }
+    });
+    if constexpr (PRE) {
+#pragma unroll
+      for (int q = 0; q < C::A_SLABS; ++q) pre[q] = pre_lds[q][tid];
+    }
     cur = nxt;
     t = tn;
   }
@@ -976,9 +1028,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     const int kind = e.y >> KIND_SHIFT;
     e.y &= (1 << KIND_SHIFT) - 1;
     if (kind == KIND_U) {
-      run_tile<EL, true, F32OUT, C>(p, sm, e);
+      int32_t pre[C::A_SLABS];
+      prefetch_a_rows<EL, true, C>(p, e, pre);
+      run_tile<EL, true, F32OUT, C>(p, sm, e, pre, [](int) {});
     } else if (kind == KIND_D) {
-      run_tile<EL, false, F32OUT, C>(p, sm, e);
+      int32_t pre[C::A_SLABS];
+      run_tile<EL, false, F32OUT, C>(p, sm, e, pre, [](int) {});
     } else if constexpr (EL == Elem::FP8) {
       const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
       gather_quantize_rows(p, e.x, r0, r1, wid, C::NW);
