@@ -11,8 +11,8 @@
 // the local routes of its contiguous chunk of routes per expert; (2) one workgroup scans
 // those counts into region offsets and per-chunk bases; (3) each workgroup walks its chunk
 // again in order and writes every local route at base + its stable rank (ballot prefix
-// counts), so each region is in ascending route order -- a stable counting sort; (4) the
-// per-(expert, source rank) counts are read off the sorted regions by binary search.
+// counts), so each region is in ascending route order -- a stable counting sort -- and adds its
+// routes' per-(expert, source rank) counts (integer additions) to totals the first step cleared.
 // Only order-independent integer arithmetic is used; no position is taken by an atomic.
 #include "device_common.h"
 #include "launch.h"
@@ -21,11 +21,18 @@ namespace mok {
 
 constexpr int PLAN_THREADS = 256;
 
+// Also clears the per-(expert, source rank) counts, which the scatter accumulates.
 __global__ __launch_bounds__(PLAN_THREADS) void k_plan_count(const int32_t* __restrict__ idx,
                                                              int64_t n_routes, int64_t chunk,
                                                              int e0, int E_l,
-                                                             int32_t* __restrict__ blk_counts) {
+                                                             int32_t* __restrict__ blk_counts,
+                                                             int32_t* __restrict__ rank_counts,
+                                                             int64_t n_rank_counts) {
   extern __shared__ int32_t hist[];  // [E_l]
+  if (rank_counts)
+    for (int64_t q = (int64_t)blockIdx.x * PLAN_THREADS + threadIdx.x; q < n_rank_counts;
+         q += (int64_t)gridDim.x * PLAN_THREADS)
+      rank_counts[q] = 0;
   for (int e = threadIdx.x; e < E_l; e += PLAN_THREADS) hist[e] = 0;
   __syncthreads();
   const int64_t r0 = (int64_t)blockIdx.x * chunk;
@@ -99,22 +106,33 @@ __global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ 
   }
 }
 
+// rank_counts (optional): each workgroup counts its routes per (local expert, source rank) in
+// LDS -- the chunk's first PLAN_NR source ranks; routes of later ones, which only very small
+// ranks produce, go straight to global memory -- and adds the counts to the cleared totals
+// (integer additions: the totals do not depend on their order).
+constexpr int PLAN_NR = 4;
 __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __restrict__ idx,
                                                                int64_t n_routes, int64_t chunk,
                                                                int e0, int E_l,
                                                                const int32_t* __restrict__ blk_base,
                                                                const int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ route_ids) {
+                                                               int32_t* __restrict__ route_ids,
+                                                               int32_t* __restrict__ rank_counts,
+                                                               int k, int64_t tokens_per_rank,
+                                                               int64_t R) {
   extern __shared__ int32_t sm[];
   int32_t* base = sm;                 // [E_l] next free row of each region (this chunk)
   int32_t* wcnt = sm + E_l;           // [4][E_l] per-wave counts of the current sub-chunk
+  int32_t* rc = sm + 5 * E_l;         // [PLAN_NR][E_l] per-(source rank, expert) counts
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * chunk;
+  const int64_t rho0 = (r0 / k) / tokens_per_rank;   // first source rank of the chunk
   for (int e = tid; e < E_l; e += PLAN_THREADS) {
     base[e] = offsets[e] + blk_base[(int64_t)blockIdx.x * E_l + e];
     for (int q = 0; q < 4; ++q) wcnt[q * E_l + e] = 0;
+    for (int q = 0; q < PLAN_NR; ++q) rc[q * E_l + e] = 0;
   }
   __syncthreads();
-  const int64_t r0 = (int64_t)blockIdx.x * chunk;
   const int64_t r1 = min(n_routes, r0 + chunk);
   for (int64_t rs = r0; rs < r1; rs += PLAN_THREADS) {
     const int64_t r = rs + tid;
@@ -122,6 +140,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __
     if (r < r1) {
       le = idx[r] - e0;
       if (le < 0 || le >= E_l) le = -1;
+    }
+    if (rank_counts && le >= 0) {
+      const int64_t rho = (r / k) / tokens_per_rank;
+      if (rho - rho0 < PLAN_NR) atomicAdd(&rc[(rho - rho0) * E_l + le], 1);
+      else atomicAdd(&rank_counts[(int64_t)le * R + rho], 1);
     }
     // stable rank among the lanes of this wave with the same expert
     int rank = 0;
@@ -150,30 +173,13 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __
     }
     __syncthreads();
   }
-}
-
-// rank_counts[e][rho] = routes of expert e from source rank rho: the sorted region's entries
-// in [rho * tpr * k, (rho + 1) * tpr * k).
-MOK_DEV int32_t lower_bound_i32(const int32_t* a, int32_t n, int64_t v) {
-  int32_t lo = 0, hi = n;
-  while (lo < hi) {
-    int32_t mid = (lo + hi) >> 1;
-    if ((int64_t)a[mid] < v) lo = mid + 1; else hi = mid;
+  if (rank_counts) {
+    for (int i = tid; i < PLAN_NR * E_l; i += PLAN_THREADS) {
+      const int64_t rho = rho0 + i / E_l;
+      const int32_t c = rc[i];
+      if (c != 0 && rho < R) atomicAdd(&rank_counts[(int64_t)(i % E_l) * R + rho], c);
+    }
   }
-  return lo;
-}
-
-__global__ void k_plan_rank_counts(const int32_t* __restrict__ route_ids,
-                                   const int32_t* __restrict__ offsets, int E_l, int64_t R,
-                                   int64_t routes_per_rank, int32_t* __restrict__ rank_counts) {
-  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= (int64_t)E_l * R) return;
-  const int e = (int)(q / R);
-  const int64_t rho = q % R;
-  const int32_t* reg = route_ids + offsets[e];
-  const int32_t n = offsets[e + 1] - offsets[e];
-  rank_counts[q] = lower_bound_i32(reg, n, (rho + 1) * routes_per_rank) -
-                   lower_bound_i32(reg, n, rho * routes_per_rank);
 }
 
 int64_t plan_chunk(int64_t n_routes) {
@@ -196,19 +202,14 @@ hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l
   const int64_t chunk = plan_chunk(n_routes);
   const int64_t nb = plan_n_blocks(n_routes);
   const size_t sh_count = sizeof(int32_t) * (size_t)E_l;
+  const int64_t R = n_tok / tokens_per_rank;
   hipLaunchKernelGGL(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS), sh_count, s, idx,
-                     n_routes, chunk, e0, E_l, blk_counts);
+                     n_routes, chunk, e0, E_l, blk_counts, rank_counts, (int64_t)E_l * R);
   hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, s, blk_counts, (int)nb, E_l, blk_base,
                      counts, offsets);
-  hipLaunchKernelGGL(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS), sh_count * 5, s, idx,
-                     n_routes, chunk, e0, E_l, blk_base, offsets, route_ids);
-  if (rank_counts) {
-    const int64_t R = n_tok / tokens_per_rank;
-    const int64_t n = (int64_t)E_l * R;
-    if (n > 0)
-      hipLaunchKernelGGL(k_plan_rank_counts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                         route_ids, offsets, E_l, R, tokens_per_rank * k, rank_counts);
-  }
+  hipLaunchKernelGGL(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS),
+                     sh_count * (5 + PLAN_NR), s, idx, n_routes, chunk, e0, E_l, blk_base, offsets,
+                     route_ids, rank_counts, k, tokens_per_rank, R);
   return hipGetLastError();
 }
 

@@ -116,7 +116,8 @@ def test_plan_worked_example():
 
 @pytest.mark.parametrize("T,k,E,e0,E_l,tpr", [(4096, 6, 64, 0, 64, 4096), (8192, 8, 256, 12, 4, 256),
                                                (3000, 2, 8, 3, 1, 1000), (64, 2, 8, 0, 8, 64),
-                                               (20000, 8, 384, 380, 4, 2000), (1, 1, 1, 0, 1, 1)])
+                                               (20000, 8, 384, 380, 4, 2000), (1, 1, 1, 0, 1, 1),
+                                               (4096, 2, 8, 0, 8, 16)])
 def test_plan_bit_exact_random(T, k, E, e0, E_l, tpr):
     rng = np.random.default_rng(T + E)
     idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
