@@ -34,7 +34,7 @@ int device_cus() {
 // can be found from the workspace pointer alone.
 struct Layout {
   bool use_ring = false;
-  int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0, cap_g = 0, cap_r = 0, lag = 0;
+  int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0, cap_g = 0, cap_r = 0;
   size_t wl = 0, logits = 0, idx = 0, w = 0, counts = 0, offsets = 0, rank_counts = 0,
          route_ids = 0, blk_counts = 0, blk_base = 0, H = 0, H_sc = 0, A_codes = 0, A_sc = 0,
          wq = 0, total = 0;
@@ -95,9 +95,6 @@ Layout layout_moe(const mok_moe_args* a) {
   L.max_mb = (int)std::max<int64_t>(1, max_mb);
   L.use_ring = !(a->flags & MOK_FLAG_NO_RING);
   L.n_slots = L.use_ring ? a->ring_rows / mb : L.max_mb;
-  // ring order: the down items of minibatch m come after the up items of m + lag, half the
-  // ring ahead; a slot is reused n_slots minibatches later, so lag < n_slots
-  L.lag = L.n_slots >= 2 ? L.n_slots / 2 : 0;
   L.Hld = std::max(a->I, I_sh);
   const size_t es = a->dtype == MOK_FP32 ? 4 : 2;
   size_t off = 0;
@@ -275,7 +272,6 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.cap_d = L.cap_d;
   p.cap_r = L.cap_r;
   p.ring = L.use_ring;
-  p.lag = L.lag;
   p.grid = ((device_cus() + 7) / 8) * 8;   // one 256 x 256 tile workgroup per CU
   p.x = a->x;
   p.route_ids = route_ids;

@@ -31,12 +31,18 @@ namespace mok {
 
 // ------------------------------------------------------------------------- work list
 // int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, the
-// prefix sums of its gather, up and down items, and three completion counters; then, 16-byte
-// aligned, one int4 per up tile and per down tile {minibatch, tile within it, first row,
-// group << 16 | rows} so that a workgroup finds its tile with a single load, and (ring work
-// loop only) the ring order of all items, the item kind in bits 28+ of the second field.
-constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_TICKET = 3, WL_ERR = 4, WL_N_R = 5,
-              WL_HDR = 16;
+// prefix sums of its gather, up and down items, three completion counters, its ring slot, the
+// minibatch that used that slot before it (-1: none) and the prefix of its weighted work (XCD
+// split); then, 16-byte aligned, one int4 per
+// up tile and per down tile {minibatch, tile within it, first row, group << 16 | rows} so that a
+// workgroup finds its tile with a single load, and (ring work loop only) the ring order of all
+// items, the item kind in bits 28+ of the second field.
+// Header: counts, the error word, and for the ring loop the per-XCD split (WL_AFFINE set): XCD
+// x owns minibatches [XB[x], XB[x+1]) and ring items [XR[x], XR[x+1]), and takes them with its
+// own ticket TICKETS[x]; without the split every workgroup uses TICKETS[0] over all items.
+constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_ERR = 4, WL_N_R = 5, WL_AFFINE = 6,
+              WL_XB = 8, WL_XR = 17, WL_TICKETS = 26, WL_HDR = 48;
+constexpr int N_XCD = 8;        // XCDs of an MI355X, each with its own L2
 constexpr uint32_t ERR_OVERFLOW = 1u, ERR_WAIT = 2u;
 constexpr int KIND_U = 0, KIND_D = 1, KIND_G = 2, KIND_SHIFT = 28;
 constexpr int G_ROWS = 64;      // rows of one gather + quantise item of the ring loop
@@ -47,7 +53,10 @@ MOK_DEV int32_t* wl_ustart(int32_t* wl, int cap) { return wl + WL_HDR + 3 * cap;
 MOK_DEV int32_t* wl_dstart(int32_t* wl, int cap) { return wl + WL_HDR + 4 * cap + 1; }
 MOK_DEV int32_t* wl_gstart(int32_t* wl, int cap) { return wl + WL_HDR + 5 * cap + 2; }
 MOK_DEV int32_t* wl_done(int32_t* wl, int cap, int kind) { return wl + WL_HDR + (6 + kind) * cap + 3; }
-MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 9 * (size_t)cap + 3 + 3) & ~(size_t)3; }
+MOK_DEV int32_t* wl_slot(int32_t* wl, int cap) { return wl + WL_HDR + 9 * cap + 3; }
+MOK_DEV int32_t* wl_prev(int32_t* wl, int cap) { return wl + WL_HDR + 10 * cap + 3; }
+MOK_DEV int32_t* wl_wpre(int32_t* wl, int cap) { return wl + WL_HDR + 11 * cap + 3; }   // cap + 1
+MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 12 * (size_t)cap + 4 + 3) & ~(size_t)3; }
 MOK_DEV int4* wl_utab(int32_t* wl, int cap) { return (int4*)(wl + wl_tab_off(cap)); }
 MOK_DEV int4* wl_dtab(int32_t* wl, int cap, int cap_u) { return (int4*)(wl + wl_tab_off(cap)) + cap_u; }
 MOK_DEV int4* wl_rtab(int32_t* wl, int cap, int cap_u, int cap_d) {
@@ -82,14 +91,21 @@ MOK_DEV int32_t block_excl_scan_1024(int32_t v, int32_t* sh, int32_t* total) {
 //
 // Ring order (ring = true): block b holds the gather items of minibatch b (MXFP8 only), its up
 // tiles, then the down tiles of minibatch b - lag. A down item needs every up tile of its
-// minibatch; an up item needs its gather items and the down items of minibatch m - n_slots
-// (whose ring slot it reuses); a gather item needs the up items of m - n_slots. With
-// lag < n_slots every dependency of an item lies earlier in this order.
+// minibatch; an up item needs its gather items and the down items of the minibatch that used
+// its ring slot before it; a gather item needs that minibatch's up items. With lag < slots
+// every dependency of an item lies earlier in this order.
+//
+// With at least 8 slots the ring is split by XCD: the minibatches are cut into 8 contiguous
+// ranges of about equal work (tiles), XCD x runs range x on its own slots (n_slots / 8 of
+// them, lag half of that) in the order above. A slot's producer and consumer then always share
+// one L2, and the handover needs no L2 write-back or invalidation. Otherwise (fewer slots) one
+// order covers all minibatches on all slots and every handover is made coherent device-wide.
 __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restrict__ counts,
                                                          const int32_t* __restrict__ offsets,
                                                          int E_l, int T_own, int mb, int bm,
                                                          int nU_r, int nU_s, int nD, bool gather,
-                                                         bool ring, int lag, int cap, int cap_u,
+                                                         bool ring, int n_slots, int w_up,
+                                                         int w_dr, int w_ds, int w_g, int cap, int cap_u,
                                                          int cap_d, int cap_r,
                                                          int32_t* __restrict__ wl) {
   __shared__ int32_t sh[1024];
@@ -160,6 +176,7 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
   }
   const bool overflow = n_routed + n_sh > cap || carry_u > cap_u || carry_d > cap_d ||
                         (ring && (int64_t)carry_u + carry_d + carry_g > cap_r);
+  const bool affine = ring && n_slots >= N_XCD;
   if (t == 0) {
     us[n_mb] = carry_u;
     ds[n_mb] = carry_d;
@@ -168,10 +185,50 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     wl[WL_N_U] = overflow ? 0 : carry_u;
     wl[WL_N_D] = overflow ? 0 : carry_d;
     wl[WL_N_R] = (overflow || !ring) ? 0 : carry_u + carry_d + carry_g;
-    wl[WL_TICKET] = 0;
     wl[WL_ERR] = overflow ? ERR_OVERFLOW : 0;
+    wl[WL_AFFINE] = affine ? 1 : 0;
   }
+  if (t < N_XCD) wl[WL_TICKETS + t] = 0;
+  // XCD split (affine ring): minibatch m goes to the XCD holding the midpoint of its work
+  // (non-decreasing in m): its items weighted by their K steps (w_up per up tile, w_dr / w_ds
+  // per routed / shared down tile, w_g per gather item); xb[x] = first minibatch of XCD x
   __syncthreads();
+  int32_t* wpre = wl_wpre(wl, cap);                 // weighted work prefix
+  int64_t W = 0;
+  if (affine) {
+    int32_t carry = 0;
+    for (int c0 = 0; c0 < n_mb; c0 += 1024) {
+      const int m = c0 + t;
+      int32_t w = 0;
+      if (m < n_mb)
+        w = (us[m + 1] - us[m]) * w_up + (ds[m + 1] - ds[m]) * (grp[m] < E_l ? w_dr : w_ds) +
+            (gs[m + 1] - gs[m]) * w_g;
+      int32_t tot;
+      const int32_t e = block_excl_scan_1024(w, sh, &tot);
+      if (m < n_mb) wpre[m] = carry + e;
+      carry += tot;
+    }
+    if (t == 0) wpre[n_mb] = carry;
+    W = carry;
+  }
+  int32_t* xb = sh;                                 // reuses the scan buffer (9 entries)
+  __syncthreads();
+  if (t <= N_XCD) xb[t] = affine ? n_mb : (t == 0 ? 0 : n_mb);
+  __syncthreads();
+  auto xcd_of = [&](int m) {
+    const int64_t pre = wpre[m], w = (int64_t)wpre[m + 1] - wpre[m];
+    return (int)min<int64_t>(N_XCD - 1, (N_XCD * (2 * pre + w)) / max<int64_t>(1, 2 * W));
+  };
+  if (affine && !overflow)
+    for (int m = t; m < n_mb; m += 1024) {
+      const int xm = xcd_of(m), xp = m > 0 ? xcd_of(m - 1) : -1;
+      for (int x = xp + 1; x <= xm; ++x) xb[x] = m;
+    }
+  __syncthreads();
+  if (t <= N_XCD) {
+    wl[WL_XB + t] = xb[t];
+    wl[WL_XR + t] = gs[xb[t]] + us[xb[t]] + ds[xb[t]];
+  }
   if (overflow) return;
   // tile tables (tiles of a minibatch: n-tile major, m-tile minor). When the shared experts'
   // down tiles are the longer ones (K = n_shared * I_shared > I), the stage-ordered down table
@@ -181,6 +238,8 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
   int4* rt = wl_rtab(wl, cap, cap_u, cap_d);
   const bool shared_first = nU_s > nU_r;
   const int32_t d_sh0 = ds[min(n_routed, n_mb)], d_sh = carry_d - d_sh0;
+  int32_t* slot = wl_slot(wl, cap);
+  int32_t* prev = wl_prev(wl, cap);
   for (int m = t; m < n_mb; m += 1024) {
     const int32_t g = grp[m], rw = nr[m], first = r0[m];
     const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
@@ -188,12 +247,25 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     const int32_t dpos = !shared_first ? ds[m] : (m >= n_routed ? ds[m] - d_sh0 : ds[m] + d_sh);
     for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = l; ut[us[m] + l] = e; }
     for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = l; dt[dpos + l] = e; }
+    // this minibatch's range: [lo, hi) of S slots starting at slot s0, order lag L
+    int lo = 0, hi = n_mb, S = n_slots, s0 = 0;
+    if (affine) {
+      const int x = xcd_of(m);
+      lo = xb[x];
+      hi = xb[x + 1];
+      S = n_slots / N_XCD;
+      s0 = x * S;
+    }
+    const int L = S >= 2 ? S / 2 : 0;
+    slot[m] = s0 + (m - lo) % S;
+    prev[m] = m - S >= lo ? m - S : -1;
     if (ring) {
-      const int mb_lag = max(0, m - lag);
-      const int after = min(m + lag + 1, n_mb);
-      const int32_t pos_g = gs[m] + us[m] + ds[mb_lag];
-      const int32_t pos_u = gs[m + 1] + us[m] + ds[mb_lag];
-      const int32_t pos_d = gs[after] + us[after] + ds[m];
+      const int mb_lag = max(lo, m - L);
+      const int after = min(m + L + 1, hi);
+      const int32_t R0 = gs[lo] + us[lo] + ds[lo];      // items of the earlier ranges
+      const int32_t pos_g = R0 + (gs[m] - gs[lo]) + (us[m] - us[lo]) + (ds[mb_lag] - ds[lo]);
+      const int32_t pos_u = R0 + (gs[m + 1] - gs[lo]) + (us[m] - us[lo]) + (ds[mb_lag] - ds[lo]);
+      const int32_t pos_d = R0 + (gs[after] - gs[lo]) + (us[after] - us[lo]) + (ds[m] - ds[lo]);
       for (int l = 0; l < ng; ++l) { int4 e = e0; e.y = (KIND_G << KIND_SHIFT) | l; rt[pos_g + l] = e; }
       for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = (KIND_U << KIND_SHIFT) | l; rt[pos_u + l] = e; }
       for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = (KIND_D << KIND_SHIFT) | l; rt[pos_d + l] = e; }
@@ -300,13 +372,25 @@ MOK_DEV void wait_vmcnt() {
 MOK_DEV uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// L2C (ring data: written by another workgroup during this kernel): the load bypasses the
+// CU's L1 (sc0) and reads the XCD's L2, where the producer's stores landed.
+template <bool L2C = false>
 MOK_DEV void dma_b128(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+  if constexpr (L2C)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 sc0"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
+template <bool L2C = false>
 MOK_DEV void dma_b32(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+  if constexpr (L2C)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 sc0"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
 // Workgroup barrier for the LDS-DMA K loop. __syncthreads() would also wait for every
@@ -399,13 +483,15 @@ MOK_DEV void prefetch_a_rows(const ExpertPass& p, const int4 entry, int32_t (&ro
 }
 
 // One tile. pre: the route ids prefetch_a_rows loaded for this tile. after_step(s) runs after
-// the barrier of K steps s = 0 and 1 (for a one-step tile, s = 1 runs after the K loop): the
-// stage kernel issues the next tile's route-id loads at step 0 and parks them in LDS at step 1,
-// when they have landed (they are older than that step's DMA), so they hold no register across
-// the K loop.
-template <Elem EL, bool UP, bool F32OUT, class C, class F>
+// the barrier of K steps s = 0 .. 3 (for shorter K loops, the missing ones run after the loop):
+// there every load issued before the step's DMA has landed. The stage kernel issues the next
+// tile's route-id loads at step 0 and parks them in LDS at step 1, so they hold no register
+// across the K loop; the ring loop fetches its next item over steps 0 .. 3.
+template <Elem EL, bool UP, bool F32OUT, class C, bool RING = false, class F>
 MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
                       const int32_t (&pre)[C::A_SLABS], F&& after_step) {
+  // A operands written during this launch (ring loop): H (down) and the MXFP8 A rows (up)
+  constexpr bool A_L2C = RING && (!UP || EL == Elem::FP8);
   typedef Tr<EL> TR;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS, ST = C::STAGES, CH = C::CH;
@@ -421,7 +507,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
   const int row0 = uniform(entry.z);
   const int g = uniform(entry.w >> 16), rows = uniform(entry.w & 0xFFFF);
   const bool shared = g >= p.E_l;
-  const int slot = m % p.n_slots;
+  const int slot = wl_slot(p.wl, p.max_mb)[m];
   const int64_t ring_row0 = (int64_t)slot * p.mb;
   const int n_mt = (rows + TILE_M - 1) / TILE_M;
   const int mt = local % n_mt, nt = local / n_mt;
@@ -571,13 +657,13 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
   auto issue_one = [&](const StepAddr& s, const Bufs<C>& b, int q) {
     __builtin_amdgcn_sched_barrier(0);             // keeps the DMA between its two MFMAs
     if (q < A_SLABS) {
-      dma_b128(a_base, a_off[q] + s.ka, uniform(lds_addr(&b.A[RA * wid][0])) + 1024 * q);
+      dma_b128<A_L2C>(a_base, a_off[q] + s.ka, uniform(lds_addr(&b.A[RA * wid][0])) + 1024 * q);
     } else if (q < A_SLABS + B_SLABS) {
       const int r = q - A_SLABS;
       const char* bb = (UP && b_up_slab(r)) ? b_up : s.b_seg;
       dma_b128(bb, b_off[r] + s.kb, uniform(lds_addr(&b.B[RB * wid][0])) + 1024 * r);
     } else if (q == A_SLABS + B_SLABS) {
-      dma_b32(a_sc_base, a_sc_off + s.sca, uniform(lds_addr(&b.As[64 * wid])));
+      dma_b32<A_L2C>(a_sc_base, a_sc_off + s.sca, uniform(lds_addr(&b.As[64 * wid])));
     } else {
       dma_b32(s.bs_seg, b_sc_off + s.scb, uniform(lds_addr(&b.Bs[64 * wid])));
     }
@@ -659,7 +745,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
       wait_vmcnt<(ST - 2) * DMA_PER_STEP>();
       lds_barrier();
       if (kt == 0) at_step0();
-      if (kt == 1) after_step(1);
+      else if (kt < 4) after_step(kt);
       const StepAddr sa = step_addr(kt + ST - 1);
       compute(cur, kt, [&](int n) { issue_at(sa, nxt, n); });
     };
@@ -672,7 +758,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
       wait_vmcnt<0>();
       lds_barrier();
       if (kt == 0) at_step0();
-      if (kt == 1) after_step(1);
+      else if (kt < 4) after_step(kt);
       const bool more = kt + ST - 1 < nk;
       const Bufs<C> cur = pick(sm, kt % ST), nxt = pick(sm, (kt + ST - 1) % ST);
       const StepAddr sa = step_addr(more ? kt + ST - 1 : kt);
@@ -688,7 +774,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
   // uses buffer 1 only, the next tile's first DMA fills buffer 0, and that tile writes buffer 1
   // and the row table only after its first K step's barrier, which every wave reaches after
   // its epilogue.
-  if (nk == 1) after_step(1);
+  for (int s = max(nk, 1); s < 4; ++s) after_step(s);
   if (rt_lane) sm.row_w[tid] = rt_w;
   __syncthreads();
   {
@@ -863,7 +949,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
         if (s == 0) {
           // by the first barrier the entry load (older than the first DMA) has landed
           if (more) prefetch_a_rows<EL, UP, C>(p, nxt, pn);
-        } else if (more) {
+        } else if (s == 1 && more) {
 #pragma unroll
           for (int q = 0; q < C::A_SLABS; ++q) pre_lds[q][tid] = pn[q];
         }
@@ -902,7 +988,7 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
   const int per_row = p.d / 8;                       // quads per row (a multiple of 4)
   const int total = rows * per_row;
   const int nt = 64 * n_waves;
-  const int64_t ring0 = (int64_t)(m % p.n_slots) * p.mb + r_begin;
+  const int64_t ring0 = (int64_t)wl_slot(p.wl, cap)[m] * p.mb + r_begin;
   const int n_iter = (total + GQ_UNROLL * nt - 1) / (GQ_UNROLL * nt);   // same for every lane
   for (int it = 0; it < n_iter; ++it) {
     uint4 raw[GQ_UNROLL];
@@ -980,41 +1066,83 @@ MOK_DEV void wait_count(const int32_t* ctr, int32_t need, int32_t* err) {
 // every field of the item is read back with readfirstlane. A lane-divergent branch here would let
 // the compiler merge the publish of one item with the ticket of the next across the loop's
 // back-edge, leaving the rest of wave 0 to pass the item barrier without lane 0.
+//
+// XCD split (WL_AFFINE): a workgroup serves the queue of the XCD it runs on (read from the
+// hardware), so every ring slot is produced and consumed under one L2. A producer's stores have
+// reached that L2 once its vmcnt drains (the L1 writes through); consumers read ring data past
+// their L1 (sc0). No fence beyond that is needed. Without the split, items move between XCDs:
+// completion is published with an agent-scope release (the L2 written back) and observed with
+// an agent-scope acquire (the L2 invalidated).
 template <Elem EL, bool F32OUT, class C>
 __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
   MOK_TILE_LDS(C, sm);
   __shared__ int4 item;
   const int cap = p.max_mb;
   int32_t* wl = p.wl;
-  const int32_t total = wl[WL_N_R];
   const int4* rt = wl_rtab(wl, cap, p.cap_u, p.cap_d);
   const int32_t* us = wl_ustart(wl, cap);
   const int32_t* ds = wl_dstart(wl, cap);
   const int32_t* gs = wl_gstart(wl, cap);
+  const int32_t* prev = wl_prev(wl, cap);
   int32_t* done_u = wl_done(wl, cap, KIND_U);
   int32_t* done_d = wl_done(wl, cap, KIND_D);
   int32_t* done_g = wl_done(wl, cap, KIND_G);
-  const int S = p.n_slots;
+  const bool affine = uniform(wl[WL_AFFINE]) != 0;
+  uint32_t hw_xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw_xcc));
+  const int x = affine ? (int)(hw_xcc & (N_XCD - 1)) : 0;
+  const int32_t seg0 = uniform(wl[WL_XR + x]);
+  const int32_t seg1 = affine ? uniform(wl[WL_XR + x + 1]) : uniform(wl[WL_N_R]);
+  int32_t* ticket = &wl[WL_TICKETS + x];
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t one = (threadIdx.x & 63) == 0 ? 1 : 0;
+  // The next item is fetched while the current tile runs (wave 0, after K-step barriers 0..3,
+  // where each load issued before has landed): ticket, entry, its slot predecessor, parked in
+  // LDS. A gather item has no K loop: the next item is then fetched in line.
+  __shared__ int4 nitem;
+  __shared__ int32_t nprev;
+  int32_t tk = 0;
+  int4 ne = make_int4(-1, 0, 0, 0);
+  auto fetch_step = [&](int s) {
+    if (wid != 0) return;
+    if (s == 0) {
+      tk = __hip_atomic_fetch_add(ticket, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (s == 1) {
+      const int32_t t = seg0 + __builtin_amdgcn_readfirstlane(tk);
+      ne = make_int4(-1, 0, 0, 0);
+      if (t < seg1) ne = rt[t];
+    } else if (s == 2) {
+      int4 v;
+      v.x = __builtin_amdgcn_readfirstlane(ne.x);
+      v.y = __builtin_amdgcn_readfirstlane(ne.y);
+      v.z = __builtin_amdgcn_readfirstlane(ne.z);
+      v.w = __builtin_amdgcn_readfirstlane(ne.w);
+      nitem = v;
+      tk = v.x >= 0 ? prev[v.x] : -1;
+    } else {
+      nprev = __builtin_amdgcn_readfirstlane(tk);
+    }
+  };
+  for (int s = 0; s < 4; ++s) {
+    fetch_step(s);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   for (;;) {
     if (wid == 0) {
-      const int32_t t = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
-          &wl[WL_TICKET], one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      int4 e = make_int4(-1, 0, 0, 0);
-      if (t < total) {
-        e = rt[t];
+      int4 e = nitem;
+      if (e.x >= 0) {
         const int m = __builtin_amdgcn_readfirstlane(e.x);
         const int kind = __builtin_amdgcn_readfirstlane(e.y) >> KIND_SHIFT;
+        const int pm = __builtin_amdgcn_readfirstlane(nprev);
         if (kind == KIND_D) {
           wait_count(&done_u[m], us[m + 1] - us[m], &wl[WL_ERR]);
         } else if (kind == KIND_U) {
           wait_count(&done_g[m], gs[m + 1] - gs[m], &wl[WL_ERR]);
-          if (m >= S) wait_count(&done_d[m - S], ds[m - S + 1] - ds[m - S], &wl[WL_ERR]);
-        } else if (m >= S) {
-          wait_count(&done_u[m - S], us[m - S + 1] - us[m - S], &wl[WL_ERR]);
+          if (pm >= 0) wait_count(&done_d[pm], ds[pm + 1] - ds[pm], &wl[WL_ERR]);
+        } else if (pm >= 0) {
+          wait_count(&done_u[pm], us[pm + 1] - us[pm], &wl[WL_ERR]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (!affine) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       item = e;                                   // every lane of wave 0 stores the same value
     }
@@ -1030,19 +1158,25 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     if (kind == KIND_U) {
       int32_t pre[C::A_SLABS];
       prefetch_a_rows<EL, true, C>(p, e, pre);
-      run_tile<EL, true, F32OUT, C>(p, sm, e, pre, [](int) {});
+      run_tile<EL, true, F32OUT, C, true>(p, sm, e, pre, fetch_step);
     } else if (kind == KIND_D) {
       int32_t pre[C::A_SLABS];
-      run_tile<EL, false, F32OUT, C>(p, sm, e, pre, [](int) {});
-    } else if constexpr (EL == Elem::FP8) {
-      const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
-      gather_quantize_rows(p, e.x, r0, r1, wid, C::NW);
+      run_tile<EL, false, F32OUT, C, true>(p, sm, e, pre, fetch_step);
+    } else {
+      if constexpr (EL == Elem::FP8) {
+        const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
+        gather_quantize_rows(p, e.x, r0, r1, wid, C::NW);
+      }
+      for (int s = 0; s < 4; ++s) {
+        fetch_step(s);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
     }
-    // every wave's stores have reached L2; then one release covers the workgroup's item
+    // every wave's stores have reached L2; then one publish covers the workgroup's item
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (wid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (!affine) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       int32_t* ctr = kind == KIND_U ? done_u : (kind == KIND_D ? done_d : done_g);
       __hip_atomic_fetch_add(&ctr[e.x], one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1139,9 +1273,13 @@ hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const*
   const int nD = (p.d + Big::BN - 1) / Big::BN;
   record(ev, 2 * 6, s);
   const bool gather_items = p.ring && p.elem == Elem::FP8;
+  // XCD-split weights, in 64-element K steps: a gather item (64 rows, ~3 bytes moved per element)
+  // costs about what 3d/1024 steps of a tile do
+  const int w_up = std::max(1, p.d / 64), w_dr = std::max(1, p.I / 64);
+  const int w_ds = std::max(1, p.I_sh / 64), w_g = std::max(1, 3 * p.d / 1024);
   hipLaunchKernelGGL(k_build_worklist, dim3(1), dim3(1024), 0, s, p.counts, p.offsets, p.E_l,
-                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.lag,
-                     p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.wl);
+                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.n_slots,
+                     w_up, w_dr, w_ds, w_g, p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   return launch_stages_t<Elem::FP8, false>(p, s, ev);

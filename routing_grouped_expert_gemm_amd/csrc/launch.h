@@ -33,13 +33,12 @@ struct ExpertPass {
   int64_t own_begin;
   int T_own;
   int mb;                // minibatch rows
-  int n_slots;           // ring slots (ring rows = n_slots * mb)
+  int n_slots;           // ring slots (ring rows = n_slots * mb); >= 8: split by XCD
   int Hld;               // ring row length in elements: max(I, I_sh)
   int max_mb;            // capacity of the minibatch tables
   int cap_u, cap_d;      // capacity of the up / down tile tables
   int cap_r;             // capacity of the ring-order table (ring work loop), else 0
   bool ring;             // persistent ring work loop (else stage-ordered launches)
-  int lag;               // ring order: down items of minibatch m follow the up items of m + lag
   int bm, bn;            // GEMM tile (rows, B-tile rows)
   int grid;              // workgroups of the tile loops
   // inputs
