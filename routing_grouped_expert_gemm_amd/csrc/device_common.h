@@ -36,6 +36,37 @@ MOK_DEV int opaque(int v) {
   return v;
 }
 
+// Block-wide exclusive scan of one int per thread (1024 threads = 16 waves). Returns the
+// exclusive prefix; *total receives the sum. Each wave scans its 64 values with shuffles, wave
+// 0 scans the 16 wave totals, and every lane adds its wave's base: two barriers.
+MOK_DEV int32_t block_excl_scan_1024(int32_t v, int32_t* sh, int32_t* total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t a = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += a;
+  }
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int32_t wt = lane < 16 ? sh[lane] : 0;
+    int32_t wi = wt;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int32_t a = __shfl_up(wi, off, 64);
+      if (lane >= off) wi += a;
+    }
+    if (lane < 16) sh[16 + lane] = wi - wt;        // exclusive wave bases
+    if (lane == 15) sh[32] = wi;                    // block total
+  }
+  __syncthreads();
+  const int32_t r = sh[16 + w] + incl - v;
+  *total = sh[32];
+  __syncthreads();                                  // sh is reused by the next call
+  return r;
+}
+
 // Values every lane of the wave holds identically, moved to scalar registers.
 MOK_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 template <class T>

@@ -67,23 +67,6 @@ size_t worklist_ints(int max_mb, int cap_u, int cap_d, int cap_r) {
   return wl_tab_off(max_mb) + 4 * ((size_t)cap_u + (size_t)cap_d + (size_t)cap_r);
 }
 
-// Block-wide exclusive scan of one int per thread (1024 threads). Returns the exclusive
-// prefix; *total receives the sum.
-MOK_DEV int32_t block_excl_scan_1024(int32_t v, int32_t* sh, int32_t* total) {
-  const int t = threadIdx.x;
-  sh[t] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t a = t >= off ? sh[t - off] : 0;
-    __syncthreads();
-    sh[t] += a;
-    __syncthreads();
-  }
-  const int32_t incl = sh[t];
-  *total = sh[1023];
-  __syncthreads();
-  return incl - v;
-}
 
 // One workgroup of 1024 threads. Minibatches: routed experts ascending (rows ascending within
 // each plan region), then the shared experts' minibatches over the own tokens. Every count

@@ -49,15 +49,17 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_count(const int32_t* __re
 // One workgroup of 1024 threads.
 //   blk_base[b][e] = sum_{b' < b} blk_counts[b'][e]   (the expert's offset is added later)
 //   counts[e] = sum_b blk_counts[b][e],  offsets = exclusive prefix sum of counts.
-// Each expert's block range is split over a group of P threads (P = 1024 / E_l rounded down
-// to a power of two): per-thread segment sums, a scan across the group, then the segment walk.
+// Each expert's block range is split over a group of P consecutive threads (P = 1024 / E_l
+// rounded down to a power of two): per-thread segment sums, one block scan (a group's prefix
+// is the scan minus its first thread's), then the segment walk. Scans: wave shuffles plus one
+// pass over the wave totals.
 __global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ blk_counts,
                                                     int n_blk, int E_l,
                                                     int32_t* __restrict__ blk_base,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets) {
-  __shared__ int32_t part[1024];
-  __shared__ int32_t tot[1024];
+  __shared__ int32_t sh[64];
+  __shared__ int32_t gbase[1024];
   const int t = threadIdx.x;
   int P = 1;
   while (P * 2 * E_l <= 1024) P *= 2;
@@ -70,39 +72,28 @@ __global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ 
     int32_t local = 0;
     if (active)
       for (int b = b0; b < b1; ++b) local += blk_counts[(int64_t)b * E_l + e];
-    part[t] = local;
+    int32_t tot;
+    const int32_t excl = block_excl_scan_1024(local, sh, &tot);
+    if (g == 0) gbase[t / P] = excl;
     __syncthreads();
-    for (int off = 1; off < P; off <<= 1) {   // inclusive scan inside each group of P
-      const int32_t v = (g >= off) ? part[t - off] : 0;
-      __syncthreads();
-      part[t] += v;
-      __syncthreads();
-    }
     if (active) {
-      int32_t run = part[t] - local;
+      int32_t run = excl - gbase[t / P];
       for (int b = b0; b < b1; ++b) {
         blk_base[(int64_t)b * E_l + e] = run;
         run += blk_counts[(int64_t)b * E_l + e];
       }
-      if (g == P - 1) counts[e] = part[t];
+      if (g == P - 1) counts[e] = run;
     }
     __syncthreads();
   }
   __threadfence_block();
   // exclusive scan of the counts over experts (E_l <= 1024)
   const int32_t c = t < E_l ? counts[t] : 0;
-  tot[t] = c;
-  part[t] = c;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
+  int32_t total;
+  const int32_t ex = block_excl_scan_1024(c, sh, &total);
   if (t < E_l) {
-    offsets[t] = part[t] - tot[t];
-    if (t == E_l - 1) offsets[E_l] = part[t];
+    offsets[t] = ex;
+    if (t == E_l - 1) offsets[E_l] = total;
   }
 }
 
