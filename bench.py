@@ -7,12 +7,14 @@ dispatch plan, pull gather + gate/up GEMM with SwiGLU, down GEMM with the routin
 scale, shared experts and the fixed-order combine. Inputs are seeded synthetic tensors
 already resident in HBM. Prints ONE JSON line.
 
-`hbm` gives the same for the memory-bound stages (plan, combine, MXFP8 weight quantisation and
+`stage_ms` (other than the gate/up stage) comes from a separate untimed pass with an event
+around every stage. `hbm` gives the same for the memory-bound stages (plan, combine, MXFP8 weight quantisation and
 row gather): algorithmic bytes over the stage's HIP-event time against 8 TB/s.
 
 `roofline` is taken live for the dominant kernel (the gate/up stage: grouped gate/up GEMM
 with the fused pull gather and SwiGLU, routed + shared): HIP events recorded by the library
-on the forward's own stream around that launch, averaged over the timed steps, against the
+on the forward's own stream around that launch -- the only events recorded in the timed steps
+-- averaged over the timed steps, against the
 algorithmic FLOPs of one launch (4 * d * I per routed row + 4 * d * I_shared * n_shared per
 own token). `roofline.traffic` is the HBM bytes of one launch of that kernel as measured by
 the rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
@@ -296,34 +298,60 @@ def main():
     topk = gpu_topk(inp["logits"], wl.k) if wl.routing == "logits" else None
     flags = 0 if args.ring else mok.MOK_FLAG_NO_RING
     layer = gpu_layer(wl, inp, topk=topk, flags=flags, mb=args.minibatch, keep=True)
-    ev = HipEvents(2 * mok.MOK_N_STAGES * (args.steps + 1))
     stream = torch.cuda.current_stream()
+    n2 = 2 * mok.MOK_N_STAGES
+    UP = mok.MOK_STAGE_UP
 
-    def step(i=None):
-        layer.args.stage_events = None if i is None else \
-            ctypes.cast(ctypes.byref(ev.ev, 8 * 2 * mok.MOK_N_STAGES * i), ctypes.c_void_p).value
+    def event_table(events, only_up):
+        """Per-step stage_events arrays: all stages, or only the gate/up pair (others NULL)."""
+        n_steps = len(events.ev) // (2 if only_up else n2)
+        tables = []
+        for i in range(n_steps):
+            t = (ctypes.c_void_p * n2)()
+            if only_up:
+                t[2 * UP], t[2 * UP + 1] = events.ev[2 * i], events.ev[2 * i + 1]
+            else:
+                for q in range(n2):
+                    t[q] = events.ev[n2 * i + q]
+            tables.append(t)
+        return tables
+
+    def step(table=None):
+        layer.args.stage_events = None if table is None else ctypes.cast(table, ctypes.c_void_p).value
         layer.forward(stream)
 
     for _ in range(args.warmup):
         step()
+    # timed steps: events only around the gate/up launch (the roofline kernel); every other
+    # event record would add a few microseconds of stream time to the step
+    ev_up = HipEvents(2 * args.steps)
+    up_tables = event_table(ev_up, True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step(up_tables[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = 1e3 * elapsed / args.steps
     assert layer.device_error(stream) == 0
+    up_ms = sum(ev_up.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
+    # per-stage times: a separate, untimed pass with every stage event
+    n_stage = min(args.steps, 10)
+    ev_all = HipEvents(n2 * n_stage)
+    all_tables = event_table(ev_all, False)
+    for i in range(n_stage):
+        step(all_tables[i])
+    torch.cuda.synchronize()
 
     n_routes = int(layer.inter["offsets"][-1])
     work = algorithmic_work(wl, n_routes)
     stage_ms = {}
     names = ["route", "plan", "quant", "up", "down", "combine", "gather"]
     assert len(names) == mok.MOK_N_STAGES
-    n2 = 2 * mok.MOK_N_STAGES
     for s, name in enumerate(names):
-        vals = [ev.elapsed_ms(n2 * i + 2 * s, n2 * i + 2 * s + 1) for i in range(args.steps)]
+        vals = [ev_all.elapsed_ms(n2 * i + 2 * s, n2 * i + 2 * s + 1) for i in range(n_stage)]
         stage_ms[name] = sum(vals) / len(vals)
+    stage_ms["up"] = up_ms                      # the timed steps' own measurement
     up_s = stage_ms["up"] * 1e-3
     peak = PEAK[wl.dtype]
     achieved = work["up_flop"] / up_s

@@ -154,7 +154,8 @@ typedef struct mok_moe_args {
   /* optional measurement hook (host array, may be NULL): 2 * MOK_N_STAGES hipEvent_t created
      by the caller; event 2s is recorded on the stream before stage s's first launch and event
      2s+1 after its last launch (a stage that launches nothing records both back to back).
-     With the ring work loop both GEMM stages run in one launch, recorded as MOK_STAGE_UP. */
+     NULL entries are skipped (each record costs a few microseconds of stream time). With the
+     ring work loop both GEMM stages run in one launch, recorded as MOK_STAGE_UP. */
   void* const* stage_events;
 } mok_moe_args;
 

@@ -216,7 +216,7 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   const int k = a->k;
   void* const* ev = a->stage_events;
   auto record = [&](int i) {
-    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], s);
+    if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
   };
 
   // stage 1: routing

@@ -1216,7 +1216,7 @@ hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, in
 
 // ------------------------------------------------------------------------- launch
 static void record(void* const* ev, int i, hipStream_t s) {
-  if (ev) (void)hipEventRecord((hipEvent_t)ev[i], s);
+  if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
 }
 
 template <Elem EL, bool F32OUT>

@@ -67,7 +67,7 @@ size_t worklist_ints(int max_mb, int cap_u, int cap_d, int cap_r);
 // (MXFP8 only, else 0).
 void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, bool gather_items, int* cap_u,
                     int* cap_d, int* cap_g);
-// ev: optional hipEvent_t[2 * 7] (mok stage events): GATHER around the work list (and the MXFP8
+// ev: optional hipEvent_t[2 * 7] (mok stage events; NULL entries skipped): GATHER around the work list (and the MXFP8
 // gather), UP around the gate/up launch, DOWN around the down launch (ring loop: UP around the
 // one persistent launch, DOWN empty).
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev);
