@@ -152,10 +152,11 @@ typedef struct mok_moe_args {
   int32_t* rank_counts_out;/* [E_l * R]                                                     */
   int32_t* route_ids_out;  /* [T_pool * min(k, E_l)]                                        */
   /* optional measurement hook (host array, may be NULL): 2 * MOK_N_STAGES hipEvent_t created
-     by the caller; event 2s is recorded on the stream before stage s's first launch and event
-     2s+1 after its last launch (a stage that launches nothing records both back to back).
-     NULL entries are skipped (each record costs a few microseconds of stream time). With the
-     ring work loop both GEMM stages run in one launch, recorded as MOK_STAGE_UP. */
+     by the caller with timing enabled. Event 2s takes the time stage s's first kernel starts
+     and event 2s+1 the time its last kernel ends: they are attached to those kernels' own
+     dispatches (hipExtLaunchKernel), so no marker is queued between kernels. A stage that
+     launches nothing records both as markers, back to back. NULL entries are skipped. With
+     the ring work loop both GEMM stages run in one launch, timed as MOK_STAGE_UP. */
   void* const* stage_events;
 } mok_moe_args;
 

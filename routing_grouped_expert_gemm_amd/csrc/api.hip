@@ -214,13 +214,14 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   char* ws = (char*)a->workspace;
   auto at = [&](size_t off) { return (void*)(ws + off); };
   const int k = a->k;
+  // stage events: tied to the stage's first and last kernels (a stage that launches nothing
+  // records them as markers)
   void* const* ev = a->stage_events;
-  auto record = [&](int i) {
-    if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
-  };
+  auto ev_start = [&](int stage) { return ev ? (hipEvent_t)ev[2 * stage] : nullptr; };
+  auto ev_stop = [&](int stage) { return ev ? (hipEvent_t)ev[2 * stage + 1] : nullptr; };
+  auto mark = [&](int stage) { mark_empty(s, ev_start(stage), ev_stop(stage)); };
 
   // stage 1: routing
-  record(2 * MOK_STAGE_ROUTE);
   const int32_t* idx = a->topk_idx_in;
   const float* w = a->topk_w_in;
   if (a->w_router) {
@@ -229,28 +230,31 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     float* ow = a->topk_w_out ? a->topk_w_out : (float*)at(L.w);
     if (a->T_pool > 0) {
       hipError_t e = launch_router_logits(a->x, a->w_router, a->T_pool, a->d, a->E,
-                                          a->dtype != MOK_FP32, logits, s);
+                                          a->dtype != MOK_FP32, logits, s,
+                                          ev_start(MOK_STAGE_ROUTE), nullptr);
       if (e != hipSuccess) return MOK_EHIP;
-      e = launch_topk(logits, a->T_pool, a->E, k, oidx, ow, s);
+      e = launch_topk(logits, a->T_pool, a->E, k, oidx, ow, s, nullptr, ev_stop(MOK_STAGE_ROUTE));
       if (e != hipSuccess) return MOK_EHIP;
+    } else {
+      mark(MOK_STAGE_ROUTE);
     }
     idx = oidx;
     w = ow;
+  } else {
+    mark(MOK_STAGE_ROUTE);
   }
-  record(2 * MOK_STAGE_ROUTE + 1);
 
   // stage 2: plan
-  record(2 * MOK_STAGE_PLAN);
   int32_t* counts = a->counts_out ? a->counts_out : (int32_t*)at(L.counts);
   int32_t* offsets = a->offsets_out ? a->offsets_out : (int32_t*)at(L.offsets);
   int32_t* route_ids = a->route_ids_out ? a->route_ids_out : (int32_t*)at(L.route_ids);
   {
     hipError_t e = launch_plan(idx, a->T_pool, k, a->e0, a->E_l, a->tokens_per_rank, counts,
                                offsets, a->rank_counts_out, route_ids, (int32_t*)at(L.blk_counts),
-                               (int32_t*)at(L.blk_base), s);
+                               (int32_t*)at(L.blk_base), s, ev_start(MOK_STAGE_PLAN),
+                               ev_stop(MOK_STAGE_PLAN));
     if (e != hipSuccess) return MOK_EHIP;
   }
-  record(2 * MOK_STAGE_PLAN + 1);
 
   // stages 3-5
   ExpertPass p = {};
@@ -282,7 +286,6 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.wl = (int32_t*)at(L.wl);
   p.y_slots = a->y_slots;
   p.y_shared = a->y_shared;
-  record(2 * MOK_STAGE_QUANT);
   if (a->dtype == MOK_MXFP8) {
     char* q = ws;
     uint8_t* wg_q = (uint8_t*)(q + L.wg_q); uint8_t* wu_q = (uint8_t*)(q + L.wu_q);
@@ -292,15 +295,18 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     uint8_t* wd_s = (uint8_t*)(q + L.wd_s); uint8_t* sg_s = (uint8_t*)(q + L.sg_s);
     uint8_t* su_s = (uint8_t*)(q + L.su_s); uint8_t* sd_s = (uint8_t*)(q + L.sd_s);
     const int64_t rI = (int64_t)a->E_l * a->I, rD = (int64_t)a->E_l * a->d;
-    hipError_t e = launch_quantize_mxfp8(a->w_gate, rI, a->d, wg_q, wg_s, s);
+    const bool sh = p.I_sh > 0;
+    hipEvent_t q0 = ev_start(MOK_STAGE_QUANT), q1 = ev_stop(MOK_STAGE_QUANT);
+    hipError_t e = launch_quantize_mxfp8(a->w_gate, rI, a->d, wg_q, wg_s, s, q0, nullptr);
     if (e == hipSuccess) e = launch_quantize_mxfp8(a->w_up, rI, a->d, wu_q, wu_s, s);
-    if (e == hipSuccess) e = launch_quantize_mxfp8(a->w_down, rD, a->I, wd_q, wd_s, s);
-    if (e == hipSuccess && p.I_sh > 0) {
+    if (e == hipSuccess)
+      e = launch_quantize_mxfp8(a->w_down, rD, a->I, wd_q, wd_s, s, nullptr, sh ? nullptr : q1);
+    if (e == hipSuccess && sh) {
       e = launch_quantize_mxfp8(a->ws_gate, p.I_sh, a->d, sg_q, sg_s, s);
       if (e == hipSuccess) e = launch_quantize_mxfp8(a->ws_up, p.I_sh, a->d, su_q, su_s, s);
       if (e == hipSuccess)
         e = launch_quantize_mxfp8(a->ws_down, (int64_t)a->n_shared * a->d, a->I_shared, sd_q,
-                                  sd_s, s);
+                                  sd_s, s, nullptr, q1);
     }
     if (e != hipSuccess) return MOK_EHIP;
     p.wg = wg_q; p.wu = wu_q; p.wd = wd_q; p.sg = sg_q; p.su = su_q; p.sd = sd_q;
@@ -311,18 +317,18 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   } else {
     p.wg = a->w_gate; p.wu = a->w_up; p.wd = a->w_down;
     p.sg = a->ws_gate; p.su = a->ws_up; p.sd = a->ws_down;
+    mark(MOK_STAGE_QUANT);
   }
-  record(2 * MOK_STAGE_QUANT + 1);
   if (launch_expert_stages(p, s, ev) != hipSuccess) return MOK_EHIP;
 
   // combine (full layer only)
-  record(2 * MOK_STAGE_COMBINE);
   if (a->E_l == a->E) {
-    if (launch_combine(a->y_shared, a->y_slots, a->y, a->T_pool, k, a->d, p.out_f32, s) !=
-        hipSuccess)
+    if (launch_combine(a->y_shared, a->y_slots, a->y, a->T_pool, k, a->d, p.out_f32, s,
+                       ev_start(MOK_STAGE_COMBINE), ev_stop(MOK_STAGE_COMBINE)) != hipSuccess)
       return MOK_EHIP;
+  } else {
+    mark(MOK_STAGE_COMBINE);
   }
-  record(2 * MOK_STAGE_COMBINE + 1);
   return MOK_OK;
 }
 

@@ -1200,43 +1200,40 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ S, const
 }
 
 hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, int64_t n_tok,
-                          int k, int d, bool f32, hipStream_t s) {
+                          int k, int d, bool f32, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int V = f32 ? 4 : 8;
   const int64_t n = n_tok * (d / V);
-  if (n == 0) return hipSuccess;
+  if (n == 0) return mark_empty(s, e0, e1), hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (f32)
-    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, s, (const float*)y_shared,
-                       (const float*)y_slots, (float*)y, n_tok, k, d);
+    launch_k(k_combine<float>, grid, dim3(256), 0, s, e0, e1, (const float*)y_shared,
+             (const float*)y_slots, (float*)y, n_tok, k, d);
   else
-    hipLaunchKernelGGL(k_combine<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)y_shared,
-                       (const bf16_t*)y_slots, (bf16_t*)y, n_tok, k, d);
+    launch_k(k_combine<bf16_t>, grid, dim3(256), 0, s, e0, e1, (const bf16_t*)y_shared,
+             (const bf16_t*)y_slots, (bf16_t*)y, n_tok, k, d);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------- launch
-static void record(void* const* ev, int i, hipStream_t s) {
-  if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
-}
+// event i of the stage-event array (stage s: 2s start, 2s + 1 stop), NULL if absent
+static hipEvent_t ev_at(void* const* ev, int i) { return ev ? (hipEvent_t)ev[i] : nullptr; }
+constexpr int EV_UP = 2 * 3, EV_DOWN = 2 * 4, EV_GATHER = 2 * 6;
 
 template <Elem EL, bool F32OUT>
 static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
   if (EL == Elem::FP8 && !p.ring)
-    hipLaunchKernelGGL(k_gather_quantize, dim3(p.grid * 8), dim3(256), 0, s, p);
-  record(ev, 2 * 6 + 1, s);
-  record(ev, 2 * 3, s);
+    launch_k(k_gather_quantize, dim3(p.grid * 8), dim3(256), 0, s, nullptr,
+             ev_at(ev, EV_GATHER + 1), p);
   if (p.ring) {
-    hipLaunchKernelGGL((k_ring<EL, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
-    record(ev, 2 * 3 + 1, s);
-    record(ev, 2 * 4, s);
-    record(ev, 2 * 4 + 1, s);
+    launch_k(k_ring<EL, F32OUT, Big>, dim3(p.grid), dim3(Big::NT), 0, s, ev_at(ev, EV_UP),
+             ev_at(ev, EV_UP + 1), p);
+    mark_empty(s, ev_at(ev, EV_DOWN), ev_at(ev, EV_DOWN + 1));
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_expert_stage<EL, true, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
-  record(ev, 2 * 3 + 1, s);
-  record(ev, 2 * 4, s);
-  hipLaunchKernelGGL((k_expert_stage<EL, false, F32OUT, Big>), dim3(p.grid), dim3(Big::NT), 0, s, p);
-  record(ev, 2 * 4 + 1, s);
+  launch_k(k_expert_stage<EL, true, F32OUT, Big>, dim3(p.grid), dim3(Big::NT), 0, s,
+           ev_at(ev, EV_UP), ev_at(ev, EV_UP + 1), p);
+  launch_k(k_expert_stage<EL, false, F32OUT, Big>, dim3(p.grid), dim3(Big::NT), 0, s,
+           ev_at(ev, EV_DOWN), ev_at(ev, EV_DOWN + 1), p);
   return hipGetLastError();
 }
 
@@ -1254,15 +1251,16 @@ hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const*
   const int nU_r = (p.I + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nD = (p.d + Big::BN - 1) / Big::BN;
-  record(ev, 2 * 6, s);
   const bool gather_items = p.ring && p.elem == Elem::FP8;
+  const bool gather_launch = p.elem == Elem::FP8 && !p.ring;   // ends the GATHER stage
   // XCD-split weights, in 64-element K steps: a gather item (64 rows, ~3 bytes moved per element)
   // costs about what 3d/1024 steps of a tile do
   const int w_up = std::max(1, p.d / 64), w_dr = std::max(1, p.I / 64);
   const int w_ds = std::max(1, p.I_sh / 64), w_g = std::max(1, 3 * p.d / 1024);
-  hipLaunchKernelGGL(k_build_worklist, dim3(1), dim3(1024), 0, s, p.counts, p.offsets, p.E_l,
-                     p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.n_slots,
-                     w_up, w_dr, w_ds, w_g, p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.wl);
+  launch_k(k_build_worklist, dim3(1), dim3(1024), 0, s, ev_at(ev, EV_GATHER),
+           gather_launch ? nullptr : ev_at(ev, EV_GATHER + 1), p.counts, p.offsets, p.E_l,
+           p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.n_slots, w_up, w_dr,
+           w_ds, w_g, p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   return launch_stages_t<Elem::FP8, false>(p, s, ev);

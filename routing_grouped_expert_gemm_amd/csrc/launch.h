@@ -1,24 +1,43 @@
 // Internal launchers of libmok (host side). Not part of the C ABI.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mok {
 
+// Kernel launch with optional timing events (either may be NULL): e0 takes the time the kernel
+// starts and e1 the time it ends. hipExtLaunchKernel ties them to the kernel's own dispatch, so
+// no marker packet is queued on the stream, which would leave it idle for a few microseconds.
+// A stage of several kernels passes e0 to its first launch and e1 to its last.
+template <class... KArgs, class... Args>
+inline void launch_k(void (*k)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                     hipEvent_t e0, hipEvent_t e1, Args... args) {
+  hipExtLaunchKernelGGL(k, grid, block, shmem, s, e0, e1, 0u, args...);
+}
+// The events of a launch that is skipped (nothing to do): recorded as markers instead.
+inline void mark_empty(hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (e0) (void)hipEventRecord(e0, s);
+  if (e1) (void)hipEventRecord(e1, s);
+}
+
 hipError_t launch_router_logits(const void* x, const void* wr, int64_t n_tok, int d, int E,
-                                bool bf16, float* logits, hipStream_t s);
+                                bool bf16, float* logits, hipStream_t s,
+                                hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_topk(const float* logits, int64_t n_tok, int E, int k, int32_t* idx,
-                       float* w, hipStream_t s);
+                       float* w, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 int64_t plan_chunk(int64_t n_routes);
 int64_t plan_n_blocks(int64_t n_routes);
 hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
                        int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
                        int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
-                       int32_t* blk_base, hipStream_t s);
+                       int32_t* blk_base, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 
 hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s);
+                                 uint8_t* scales, hipStream_t s, hipEvent_t e0 = nullptr,
+                                 hipEvent_t e1 = nullptr);
 
 // Operand element type of the expert GEMMs.
 enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2 };
@@ -67,11 +86,12 @@ size_t worklist_ints(int max_mb, int cap_u, int cap_d, int cap_r);
 // (MXFP8 only, else 0).
 void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, bool gather_items, int* cap_u,
                     int* cap_d, int* cap_g);
-// ev: optional hipEvent_t[2 * 7] (mok stage events; NULL entries skipped): GATHER around the work list (and the MXFP8
-// gather), UP around the gate/up launch, DOWN around the down launch (ring loop: UP around the
-// one persistent launch, DOWN empty).
+// ev: optional hipEvent_t[2 * 7] (mok stage events; NULL entries skipped): GATHER on the work
+// list (and the MXFP8 gather), UP on the gate/up launch, DOWN on the down launch (ring loop: UP
+// on the one persistent launch, DOWN recorded empty).
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev);
 hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, int64_t n_tok,
-                          int k, int d, bool f32, hipStream_t s);
+                          int k, int d, bool f32, hipStream_t s, hipEvent_t e0 = nullptr,
+                          hipEvent_t e1 = nullptr);
 
 }  // namespace mok

@@ -188,19 +188,19 @@ int64_t plan_n_blocks(int64_t n_routes) {
 hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
                        int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
                        int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
-                       int32_t* blk_base, hipStream_t s) {
+                       int32_t* blk_base, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t n_routes = n_tok * k;
   const int64_t chunk = plan_chunk(n_routes);
   const int64_t nb = plan_n_blocks(n_routes);
   const size_t sh_count = sizeof(int32_t) * (size_t)E_l;
   const int64_t R = n_tok / tokens_per_rank;
-  hipLaunchKernelGGL(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS), sh_count, s, idx,
-                     n_routes, chunk, e0, E_l, blk_counts, rank_counts, (int64_t)E_l * R);
-  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, s, blk_counts, (int)nb, E_l, blk_base,
-                     counts, offsets);
-  hipLaunchKernelGGL(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS),
-                     sh_count * (5 + PLAN_NR), s, idx, n_routes, chunk, e0, E_l, blk_base, offsets,
-                     route_ids, rank_counts, k, tokens_per_rank, R);
+  launch_k(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS), (uint32_t)sh_count, s, ev0,
+           nullptr, idx, n_routes, chunk, e0, E_l, blk_counts, rank_counts, (int64_t)E_l * R);
+  launch_k(k_plan_scan, dim3(1), dim3(1024), 0, s, nullptr, nullptr, blk_counts, (int)nb, E_l,
+           blk_base, counts, offsets);
+  launch_k(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS),
+           (uint32_t)(sh_count * (5 + PLAN_NR)), s, nullptr, ev1, idx, n_routes, chunk, e0, E_l,
+           blk_base, offsets, route_ids, rank_counts, k, tokens_per_rank, R);
   return hipGetLastError();
 }
 

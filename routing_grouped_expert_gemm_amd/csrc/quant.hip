@@ -32,13 +32,13 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8(const bf16_t* __restrict
 }
 
 hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s) {
+                                 uint8_t* scales, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t n_chunks = rows * (K / 8);
-  if (n_chunks == 0) return hipSuccess;
+  if (n_chunks == 0) return mark_empty(s, e0, e1), hipSuccess;
   const int64_t want = (n_chunks + 255) / 256;
   const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(k_quantize_mxfp8, dim3(grid), dim3(256), 0, s, (const bf16_t*)src_bf16,
-                     n_chunks, codes, scales);
+  launch_k(k_quantize_mxfp8, dim3(grid), dim3(256), 0, s, e0, e1, (const bf16_t*)src_bf16,
+           n_chunks, codes, scales);
   return hipGetLastError();
 }
 

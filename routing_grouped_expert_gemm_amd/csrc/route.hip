@@ -160,23 +160,25 @@ MOK_DEV float float_from_order_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// NQ = keys per lane: the smallest power of two with 64 NQ >= E (compile time, so that a
+// 64-expert top-k does one compare per lane per round, not TK_MAXQ).
+template <int NQ>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int64_t n_tok,
                                               int E, int k, int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= n_tok) return;
-  const int nq = (E + 63) >> 6;
-  uint32_t key[TK_MAXQ];
+  uint32_t key[NQ];
 #pragma unroll
-  for (int q = 0; q < TK_MAXQ; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     const int e = lane + 64 * q;
-    key[q] = (q < nq && e < E) ? float_order_key(logits[t * E + e]) : 0u;
+    key[q] = e < E ? float_order_key(logits[t * E + e]) : 0u;
   }
   uint32_t taken = 0;  // bit q: expert lane+64q already picked (or absent)
 #pragma unroll
-  for (int q = 0; q < TK_MAXQ; ++q)
-    if (!(q < nq && lane + 64 * q < E)) taken |= 1u << q;
+  for (int q = 0; q < NQ; ++q)
+    if (!(lane + 64 * q < E)) taken |= 1u << q;
   float val0 = 0.0f;
   double wsum = 0.0;
   float my_val = 0.0f;
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int q = 0; q < TK_MAXQ; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       if (taken & (1u << q)) continue;
       const uint64_t c = ((uint64_t)key[q] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * q));
       best = c > best ? c : best;
@@ -208,24 +210,35 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 }
 
 hipError_t launch_router_logits(const void* x, const void* wr, int64_t n_tok, int d, int E,
-                                bool bf16, float* logits, hipStream_t s) {
-  if (n_tok == 0) return hipSuccess;
+                                bool bf16, float* logits, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1) {
+  if (n_tok == 0) return mark_empty(s, e0, e1), hipSuccess;
   const int64_t waves = ((n_tok + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (bf16)
-    hipLaunchKernelGGL(k_router_logits<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
-                       (const bf16_t*)wr, n_tok, d, E, logits);
+    launch_k(k_router_logits<bf16_t>, grid, dim3(256), 0, s, e0, e1, (const bf16_t*)x,
+             (const bf16_t*)wr, n_tok, d, E, logits);
   else
-    hipLaunchKernelGGL(k_router_logits<float>, grid, dim3(256), 0, s, (const float*)x,
-                       (const float*)wr, n_tok, d, E, logits);
+    launch_k(k_router_logits<float>, grid, dim3(256), 0, s, e0, e1, (const float*)x,
+             (const float*)wr, n_tok, d, E, logits);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int64_t n_tok, int E, int k, int32_t* idx,
-                       float* w, hipStream_t s) {
-  if (n_tok == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk, dim3((unsigned)((n_tok + 3) / 4)), dim3(256), 0, s, logits, n_tok,
-                     E, k, idx, w);
+                       float* w, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (n_tok == 0) return mark_empty(s, e0, e1), hipSuccess;
+  if (E > 64 * TK_MAXQ) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((n_tok + 3) / 4)), block(256);
+  if (E <= 64)
+    launch_k(k_topk<1>, grid, block, 0, s, e0, e1, logits, n_tok, E, k, idx, w);
+  else if (E <= 128)
+    launch_k(k_topk<2>, grid, block, 0, s, e0, e1, logits, n_tok, E, k, idx, w);
+  else if (E <= 256)
+    launch_k(k_topk<4>, grid, block, 0, s, e0, e1, logits, n_tok, E, k, idx, w);
+  else if (E <= 512)
+    launch_k(k_topk<8>, grid, block, 0, s, e0, e1, logits, n_tok, E, k, idx, w);
+  else
+    launch_k(k_topk<TK_MAXQ>, grid, block, 0, s, e0, e1, logits, n_tok, E, k, idx, w);
   return hipGetLastError();
 }
 

@@ -147,3 +147,64 @@ def test_zipf_share_minibatch_sweep_bit_identical():
             assert torch.equal(out[0].view(torch.int16), ref[0].view(torch.int16))
             assert torch.equal(out[1].view(torch.int16), ref[1].view(torch.int16))
         del layer
+
+
+class _Events:
+    """2 * MOK_N_STAGES timing events through the HIP runtime."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+
+    def elapsed_ms(self, a, b):
+        out = self.ct.c_float(0)
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), self.ev[a], self.ev[b])
+        return rc, out.value
+
+
+@pytest.mark.parametrize("dtype,ring", [("fp32", False), ("fp32", True), ("mxfp8", False)])
+def test_stage_events_time_every_stage(dtype, ring):
+    """Every stage's event pair is recorded (on its kernels, or as markers for a stage that
+    launches nothing), the stages that run kernels take positive time, and a timed forward
+    gives the same bits as an untimed one."""
+    import ctypes
+    import dataclasses
+    import routing_grouped_expert_gemm_amd as mok
+    wl = dataclasses.replace(synth.WORKLOADS[synth.TINY], dtype=dtype,
+                             name=f"tiny_{dtype}_t64_d128_e8_top2")
+    inp = make_inputs(wl, DEV)
+    layer = gpu_layer(wl, inp, flags=0 if ring else mok.MOK_FLAG_NO_RING)
+    layer.forward()
+    torch.cuda.synchronize()
+    y0 = layer.y.clone()
+    n2 = 2 * mok.MOK_N_STAGES
+    ev = _Events(n2)
+    layer.args.stage_events = ctypes.cast(ev.ev, ctypes.c_void_p).value
+    layer.forward()
+    torch.cuda.synchronize()
+    layer.args.stage_events = None
+    assert torch.equal(layer.y.view(torch.int32 if dtype == "fp32" else torch.int16),
+                       y0.view(torch.int32 if dtype == "fp32" else torch.int16))
+    ms = {}
+    for s in range(mok.MOK_N_STAGES):
+        rc, t = ev.elapsed_ms(2 * s, 2 * s + 1)
+        assert rc == 0, (s, rc)
+        assert 0.0 <= t < 1000.0, (s, t)
+        ms[s] = t
+    running = [mok.MOK_STAGE_ROUTE, mok.MOK_STAGE_PLAN, mok.MOK_STAGE_UP, mok.MOK_STAGE_COMBINE,
+               mok.MOK_STAGE_GATHER]
+    if not ring:
+        running.append(mok.MOK_STAGE_DOWN)
+    if dtype == "mxfp8":
+        running.append(mok.MOK_STAGE_QUANT)
+    for s in running:
+        assert ms[s] > 0.0, (s, ms)
