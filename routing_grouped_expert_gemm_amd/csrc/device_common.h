@@ -19,6 +19,14 @@ MOK_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16
 // float32 -> bf16, round to nearest even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32.
 MOK_DEV bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
+// Two values in one 32-bit word (a in the low half), with one v_cvt_pk_bf16_f32.
+MOK_DEV uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 template <class T> MOK_DEV float load_as_f32(const T* p);
 template <> MOK_DEV float load_as_f32<float>(const float* p) { return *p; }
 template <> MOK_DEV float load_as_f32<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }

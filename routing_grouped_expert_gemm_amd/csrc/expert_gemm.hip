@@ -465,13 +465,33 @@ MOK_DEV void prefetch_a_rows(const ExpertPass& p, const int4 entry, int32_t (&ro
   }
 }
 
-// One tile. pre: the route ids prefetch_a_rows loaded for this tile. after_step(s) runs after
-// the barrier of K steps s = 0 .. 3 (for shorter K loops, the missing ones run after the loop):
-// there every load issued before the step's DMA has landed. The stage kernel issues the next
-// tile's route-id loads at step 0 and parks them in LDS at step 1, so they hold no register
-// across the K loop; the ring loop fetches its next item over steps 0 .. 3.
+// Field of the kernel's argument block (an ExpertPass, the kernel's only parameter) at byte
+// offset off, read again from the kernarg segment with a scalar load at each call: a value
+// used by the K loop but loaded once per kernel would be held in registers across every
+// epilogue, where the register file is full.
+template <class T>
+MOK_DEV T kernarg_field(size_t off) {
+  typedef __attribute__((address_space(4))) const char kchar;
+  kchar* base = (kchar*)__builtin_amdgcn_kernarg_segment_ptr();
+  return *(__attribute__((address_space(4))) const volatile T*)(base + off);
+}
+
+// The pool rows of the route ids prefetch_a_rows loaded (route id / k).
+template <class C>
+MOK_DEV void route_rows(const ExpertPass& p, int32_t (&r)[C::A_SLABS]) {
+#pragma unroll
+  for (int q = 0; q < C::A_SLABS; ++q) r[q] /= p.k;
+}
+
+// One tile. slot: the ring slot of the entry's minibatch. pre (routed gate/up tiles of the
+// bf16 / float32 path): the pool rows of the tile's A slabs (prefetch_a_rows, route_rows).
+// after_step(s) runs after the barrier of K steps s = 0 .. 3 (for shorter K loops, the missing
+// ones run after the loop): there every vector load issued before the step's DMA has landed.
+// The stage kernel fetches the next tile's entry, slot and A rows over steps 0 .. 2 and parks
+// the rows in LDS, so they hold no register across the K loop; the ring loop fetches its next
+// item over steps 0 .. 3.
 template <Elem EL, bool UP, bool F32OUT, class C, bool RING = false, class F>
-MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
+MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, const int slot,
                       const int32_t (&pre)[C::A_SLABS], F&& after_step) {
   // A operands written during this launch (ring loop): H (down) and the MXFP8 A rows (up)
   constexpr bool A_L2C = RING && (!UP || EL == Elem::FP8);
@@ -490,7 +510,6 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
   const int row0 = uniform(entry.z);
   const int g = uniform(entry.w >> 16), rows = uniform(entry.w & 0xFFFF);
   const bool shared = g >= p.E_l;
-  const int slot = wl_slot(p.wl, p.max_mb)[m];
   const int64_t ring_row0 = (int64_t)slot * p.mb;
   const int n_mt = (rows + TILE_M - 1) / TILE_M;
   const int mt = local % n_mt, nt = local / n_mt;
@@ -517,7 +536,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
   const char* a_base;
   int64_t a_row_bytes;
   if (UP && EL != Elem::FP8) {
-    a_base = (const char*)p.x;
+    a_base = (const char*)kernarg_field<const void*>(offsetof(ExpertPass, x));
     a_row_bytes = (int64_t)p.d * TR::ES;
   } else if (UP) {
     a_base = (const char*)p.A_codes + (ring_row0 + m0) * p.d;
@@ -533,7 +552,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
     const int r = min(RA * wid + RPI * q + lane / CH, rows_valid - 1);
     int64_t row;
     if (UP && EL != Elem::FP8)
-      row = shared ? p.own_begin + row0 + m0 + r : (int64_t)(pre[q] / p.k);
+      row = shared ? p.own_begin + row0 + m0 + r : (int64_t)pre[q];
     else
       row = r;
     a_off[q] = (uint32_t)(row * a_row_bytes) + chunk_b(q);
@@ -662,13 +681,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
 #pragma unroll
     for (int q = 0; q < DMA_PER_STEP; ++q) issue_one(s, b, q);
   };
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  f32x16_t acc[FM][FN];                             // cleared once the first DMA is out
 
   const int h = lane >> 5, l32 = lane & 31;
   const int xsw = (l32 >> SWS) & (CH - 1);         // swizzle of the lane's fragment rows
@@ -724,6 +737,13 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
 #pragma unroll
     for (int q = 0; q < ST - 1; ++q)
       if (q < nk) issue_all(q, sm.buf[q]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     auto steady = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
       wait_vmcnt<(ST - 2) * DMA_PER_STEP>();
       lds_barrier();
@@ -809,8 +829,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry,
             *(lds_u4*)dst = q;
           } else {
             u32x2 q;
-            q.x = (uint32_t)f32_to_bf16(val[0]) | ((uint32_t)f32_to_bf16(val[1]) << 16);
-            q.y = (uint32_t)f32_to_bf16(val[2]) | ((uint32_t)f32_to_bf16(val[3]) << 16);
+            q.x = pack_bf16x2(val[0], val[1]);
+            q.y = pack_bf16x2(val[2], val[3]);
             *(lds_u2*)dst = q;
           }
         }
@@ -915,34 +935,59 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
   const int b = blockIdx.x;
   int32_t t = (b & 7) * (G >> 3) + (b >> 3);
   if (t >= total) return;
-  // per-lane parking of the next tile's route ids (each lane reads back only its own)
+  // The next tile's entry and slot, and (per lane) its A rows, are parked in LDS: no value is
+  // carried in registers from one tile to the next (across the epilogue, where the register
+  // file is full), so none is spilled and reloaded with a wait that drains the epilogue's
+  // stores.
   constexpr bool PRE = UP && EL != Elem::FP8;
   __shared__ int32_t pre_lds[PRE ? C::A_SLABS : 1][C::NT];
+  __shared__ int4 nxt_lds;
+  __shared__ int nslot_lds;
   const int tid = threadIdx.x;
   int4 cur = tab[t];
+  int slot = wl_slot(p.wl, cap)[cur.x];
   int32_t pre[C::A_SLABS];
   prefetch_a_rows<EL, UP, C>(p, cur, pre);
-  while (t < total) {
+  if constexpr (PRE) route_rows<C>(p, pre);
+  for (;;) {
     const int32_t tn = t + G;
     const bool more = tn < total;
-    const int4 nxt = more ? tab[tn] : cur;    // next tile's entry, loaded before this tile
+    // The next tile's entry (step 0), its slot and route ids (step 1) and their pool rows (step
+    // 2) are fetched under this tile's first K steps, each from values that landed by that
+    // step's barrier, so the next prologue waits on no global load. The epilogue's barrier
+    // orders the LDS writes before the reads below; the next tile's first barriers order those
+    // reads before the next writes.
+    int4 nxt = cur;
+    int nslot = slot;
     int32_t pn[C::A_SLABS];
-    run_tile<EL, UP, F32OUT, C>(p, sm, cur, pre, [&](int s) {
-      if constexpr (PRE) {
-        if (s == 0) {
-          // by the first barrier the entry load (older than the first DMA) has landed
-          if (more) prefetch_a_rows<EL, UP, C>(p, nxt, pn);
-        } else if (s == 1 && more) {
+    run_tile<EL, UP, F32OUT, C>(p, sm, cur, slot, pre, [&](int s) {
+      if (!more) return;
+      if (s == 0) {
+        nxt = tab[tn];
+      } else if (s == 1) {
+        nslot = wl_slot(p.wl, cap)[nxt.x];
+        if constexpr (PRE) prefetch_a_rows<EL, UP, C>(p, nxt, pn);
+        if (tid == 0) nxt_lds = nxt;
+      } else if (s == 2) {
+        if constexpr (PRE) {
+          route_rows<C>(p, pn);
 #pragma unroll
           for (int q = 0; q < C::A_SLABS; ++q) pre_lds[q][tid] = pn[q];
         }
+        if (tid == 0) nslot_lds = nslot;
       }
     });
+    if (!more) break;
     if constexpr (PRE) {
 #pragma unroll
       for (int q = 0; q < C::A_SLABS; ++q) pre[q] = pre_lds[q][tid];
     }
-    cur = nxt;
+    const int4 c = nxt_lds;
+    cur.x = __builtin_amdgcn_readfirstlane(c.x);
+    cur.y = __builtin_amdgcn_readfirstlane(c.y);
+    cur.z = __builtin_amdgcn_readfirstlane(c.z);
+    cur.w = __builtin_amdgcn_readfirstlane(c.w);
+    slot = __builtin_amdgcn_readfirstlane(nslot_lds);
     t = tn;
   }
 }
@@ -1141,10 +1186,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     if (kind == KIND_U) {
       int32_t pre[C::A_SLABS];
       prefetch_a_rows<EL, true, C>(p, e, pre);
-      run_tile<EL, true, F32OUT, C, true>(p, sm, e, pre, fetch_step);
+      if constexpr (EL != Elem::FP8) route_rows<C>(p, pre);
+      run_tile<EL, true, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre, fetch_step);
     } else if (kind == KIND_D) {
       int32_t pre[C::A_SLABS];
-      run_tile<EL, false, F32OUT, C, true>(p, sm, e, pre, fetch_step);
+      run_tile<EL, false, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre,
+                                           fetch_step);
     } else {
       if constexpr (EL == Elem::FP8) {
         const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
