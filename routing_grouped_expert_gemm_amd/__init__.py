@@ -37,7 +37,7 @@ class MokError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libmok.so is not built ({LIB_PATH}); run "
-                      "`python -m routing_grouped_expert_gemm_amd._build` or __graft_entry__.build()")
+                      "`python routing_grouped_expert_gemm_amd/_build.py` or __graft_entry__.build()")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
