@@ -43,6 +43,7 @@ namespace mok {
 constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_ERR = 4, WL_N_R = 5, WL_AFFINE = 6,
               WL_XB = 8, WL_XR = 17, WL_TICKETS = 26, WL_HDR = 48;
 constexpr int N_XCD = 8;        // XCDs of an MI355X, each with its own L2
+constexpr int XB_N = 8;         // N tiles per block of the stage tables' tile order
 constexpr uint32_t ERR_OVERFLOW = 1u, ERR_WAIT = 2u;
 constexpr int KIND_U = 0, KIND_D = 1, KIND_G = 2, KIND_SHIFT = 28;
 constexpr int G_ROWS = 64;      // rows of one gather + quantise item of the ring loop
@@ -212,24 +213,56 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     wl[WL_XB + t] = xb[t];
     wl[WL_XR + t] = gs[xb[t]] + us[xb[t]] + ds[xb[t]];
   }
+  // Stage-ordered tables: when the shared experts' down tiles are the longer ones (K =
+  // n_shared * I_shared > I), the down table lists them first, so that the longest tiles start
+  // first and the stage ends evenly.
+  const bool shared_first = nU_s > nU_r;
+  const int32_t d_sh0 = ds[min(n_routed, n_mb)], d_sh = carry_d - d_sh0;
   if (overflow) return;
-  // tile tables (tiles of a minibatch: n-tile major, m-tile minor). When the shared experts'
-  // down tiles are the longer ones (K = n_shared * I_shared > I), the stage-ordered down table
-  // lists them first, so that the longest tiles start first and the stage ends evenly.
+  // Tile order in the stage tables, per group (routed expert, or the shared experts): blocks of
+  // XB_N consecutive N tiles, and in each block the group's M tiles in order, each with the
+  // block's N tiles. The 32 workgroups of an XCD take 32 consecutive entries, so they run about
+  // 4 M tiles x 8 N tiles together and read 12 operand tiles per K step, not the 18 of 2 M
+  // tiles x 16 N tiles (minibatch-major order), from their L2.
   int4* ut = wl_utab(wl, cap);
   int4* dt = wl_dtab(wl, cap, cap_u);
   int4* rt = wl_rtab(wl, cap, cap_u, cap_d);
-  const bool shared_first = nU_s > nU_r;
-  const int32_t d_sh0 = ds[min(n_routed, n_mb)], d_sh = carry_d - d_sh0;
+  const int mpm = (mb + bm - 1) / bm;               // M tiles of a whole minibatch
+  auto dshift = [&](int m) {
+    return !shared_first ? ds[m] : (m >= n_routed ? ds[m] - d_sh0 : ds[m] + d_sh);
+  };
   int32_t* slot = wl_slot(wl, cap);
   int32_t* prev = wl_prev(wl, cap);
   for (int m = t; m < n_mb; m += 1024) {
     const int32_t g = grp[m], rw = nr[m], first = r0[m];
     const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
     const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m], ng = gs[m + 1] - gs[m];
-    const int32_t dpos = !shared_first ? ds[m] : (m >= n_routed ? ds[m] - d_sh0 : ds[m] + d_sh);
-    for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = l; ut[us[m] + l] = e; }
-    for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = l; dt[dpos + l] = e; }
+    // the group's minibatches [f, f_end): all but the last hold mb rows
+    int f, f_end;
+    if (g < E_l) {
+      f = m - (first - offsets[g]) / mb;
+      f_end = f + (counts[g] + mb - 1) / mb;
+    } else {
+      f = n_routed;
+      f_end = n_mb;
+    }
+    const int mt_m = (rw + bm - 1) / bm;             // this minibatch's M tiles
+    const int mo = (m - f) * mpm;                     // the group's M tiles before it
+    const int MT = (f_end - 1 - f) * mpm + (nr[f_end - 1] + bm - 1) / bm;
+    // table position, within the group, of the tile (M tile mt of this minibatch, N tile nt)
+    auto blocked = [&](int mt, int nt, int nN) {
+      const int nb = nt / XB_N, w = min(XB_N, nN - nb * XB_N);
+      return nb * MT * XB_N + (mo + mt) * w + (nt - nb * XB_N);
+    };
+    const int nU = g < E_l ? nU_r : nU_s;
+    for (int l = 0; l < nu; ++l) {
+      int4 e = e0; e.y = l;
+      ut[us[f] + blocked(l % mt_m, l / mt_m, nU)] = e;
+    }
+    for (int l = 0; l < nd; ++l) {
+      int4 e = e0; e.y = l;
+      dt[dshift(f) + blocked(l % mt_m, l / mt_m, nD)] = e;
+    }
     // this minibatch's range: [lo, hi) of S slots starting at slot s0, order lag L
     int lo = 0, hi = n_mb, S = n_slots, s0 = 0;
     if (affine) {
