@@ -43,7 +43,8 @@ namespace mok {
 constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_ERR = 4, WL_N_R = 5, WL_AFFINE = 6,
               WL_XB = 8, WL_XR = 17, WL_TICKETS = 26, WL_HDR = 48;
 constexpr int N_XCD = 8;        // XCDs of an MI355X, each with its own L2
-constexpr int XB_N = 8;         // N tiles per block of the stage tables' tile order
+constexpr int XB_N = 4;         // N tiles per block of the stage tables' tile order: up
+constexpr int XB_ND = 8;        // ... down
 constexpr uint32_t ERR_OVERFLOW = 1u, ERR_WAIT = 2u;
 constexpr int KIND_U = 0, KIND_D = 1, KIND_G = 2, KIND_SHIFT = 28;
 constexpr int G_ROWS = 64;      // rows of one gather + quantise item of the ring loop
@@ -220,10 +221,11 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
   const int32_t d_sh0 = ds[min(n_routed, n_mb)], d_sh = carry_d - d_sh0;
   if (overflow) return;
   // Tile order in the stage tables, per group (routed expert, or the shared experts): blocks of
-  // XB_N consecutive N tiles, and in each block the group's M tiles in order, each with the
-  // block's N tiles. The 32 workgroups of an XCD take 32 consecutive entries, so they run about
-  // 4 M tiles x 8 N tiles together and read 12 operand tiles per K step, not the 18 of 2 M
-  // tiles x 16 N tiles (minibatch-major order), from their L2.
+  // XB consecutive N tiles (XB_N up, XB_ND down), and in each block the group's M tiles in
+  // order, each with the block's N tiles. The 32 workgroups of an XCD take 32 consecutive
+  // entries: with 8 or more M tiles in a group, an up round runs 8 M tiles x 4 N tiles and reads
+  // 12 operand tiles per K step from the XCD's L2, not the 18 of 2 M tiles x 16 N tiles
+  // (minibatch-major order).
   int4* ut = wl_utab(wl, cap);
   int4* dt = wl_dtab(wl, cap, cap_u);
   int4* rt = wl_rtab(wl, cap, cap_u, cap_d);
@@ -233,36 +235,62 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
   };
   int32_t* slot = wl_slot(wl, cap);
   int32_t* prev = wl_prev(wl, cap);
+  // Stage tables (the ring loop reads only its own). Per chunk of 1024 minibatches: one thread
+  // per minibatch puts its placement in LDS, then one thread per tile finds its minibatch by a
+  // binary search over the chunk's tile prefix sums in LDS and writes the entry.
+  if (!ring) {
+    __shared__ int32_t c_pu[1025], c_pd[1025];
+    __shared__ int32_t c_first[1024], c_gw[1024], c_bu[1024], c_bd[1024], c_mt[1024], c_mo[1024];
+    for (int c0 = 0; c0 < n_mb; c0 += 1024) {
+      const int nc = min(1024, n_mb - c0);
+      __syncthreads();                                 // the previous chunk's readers are done
+      if (t < nc) {
+        const int m = c0 + t;
+        const int32_t g = grp[m], rw = nr[m], first = r0[m];
+        // the group's minibatches [f, f_end): all but the last hold mb rows
+        int f, f_end;
+        if (g < E_l) {
+          f = m - (first - offsets[g]) / mb;
+          f_end = f + (counts[g] + mb - 1) / mb;
+        } else {
+          f = n_routed;
+          f_end = n_mb;
+        }
+        c_first[t] = first;
+        c_gw[t] = (g << 16) | rw;
+        c_bu[t] = us[f];
+        c_bd[t] = dshift(f);
+        c_mt[t] = (f_end - 1 - f) * mpm + (nr[f_end - 1] + bm - 1) / bm;   // the group's M tiles
+        c_mo[t] = (m - f) * mpm;                                            // ... before m
+      }
+      if (t <= nc) {
+        c_pu[t] = us[c0 + t];
+        c_pd[t] = ds[c0 + t];
+      }
+      __syncthreads();
+      auto place = [&](const int32_t* ps, int nN_r, int nN_s, int32_t* bases, int4* tab, int XB) {
+        for (int32_t i = ps[0] + t; i < ps[nc]; i += 1024) {
+          int lo = 0, hi = nc;                         // ps[lo] <= i < ps[hi]
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (ps[mid] <= i) lo = mid; else hi = mid;
+          }
+          const int l = i - ps[lo], gw = c_gw[lo];
+          const int mt_m = ((gw & 0xFFFF) + bm - 1) / bm;
+          const int mt = l % mt_m, nt = l / mt_m, nN = (gw >> 16) < E_l ? nN_r : nN_s;
+          const int nb = nt / XB, w = min(XB, nN - nb * XB);
+          tab[bases[lo] + nb * c_mt[lo] * XB + (c_mo[lo] + mt) * w + (nt - nb * XB)] =
+              make_int4(c0 + lo, l, c_first[lo], gw);
+        }
+      };
+      place(c_pu, nU_r, nU_s, c_bu, ut, XB_N);
+      place(c_pd, nD, nD, c_bd, dt, XB_ND);
+    }
+  }
   for (int m = t; m < n_mb; m += 1024) {
     const int32_t g = grp[m], rw = nr[m], first = r0[m];
     const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
     const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m], ng = gs[m + 1] - gs[m];
-    // the group's minibatches [f, f_end): all but the last hold mb rows
-    int f, f_end;
-    if (g < E_l) {
-      f = m - (first - offsets[g]) / mb;
-      f_end = f + (counts[g] + mb - 1) / mb;
-    } else {
-      f = n_routed;
-      f_end = n_mb;
-    }
-    const int mt_m = (rw + bm - 1) / bm;             // this minibatch's M tiles
-    const int mo = (m - f) * mpm;                     // the group's M tiles before it
-    const int MT = (f_end - 1 - f) * mpm + (nr[f_end - 1] + bm - 1) / bm;
-    // table position, within the group, of the tile (M tile mt of this minibatch, N tile nt)
-    auto blocked = [&](int mt, int nt, int nN) {
-      const int nb = nt / XB_N, w = min(XB_N, nN - nb * XB_N);
-      return nb * MT * XB_N + (mo + mt) * w + (nt - nb * XB_N);
-    };
-    const int nU = g < E_l ? nU_r : nU_s;
-    for (int l = 0; l < nu; ++l) {
-      int4 e = e0; e.y = l;
-      ut[us[f] + blocked(l % mt_m, l / mt_m, nU)] = e;
-    }
-    for (int l = 0; l < nd; ++l) {
-      int4 e = e0; e.y = l;
-      dt[dshift(f) + blocked(l % mt_m, l / mt_m, nD)] = e;
-    }
     // this minibatch's range: [lo, hi) of S slots starting at slot s0, order lag L
     int lo = 0, hi = n_mb, S = n_slots, s0 = 0;
     if (affine) {
@@ -1248,11 +1276,13 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
 
 // ------------------------------------------------------------------------- combine
 // y[t] = S[t] + sum_{j ascending} P[t*k + j], float32 accumulator, one rounding. One thread
-// per 16 B of a row: the k + 1 rows of a token are read once, y is written once.
-template <class OT>
+// per 16 B of a row: the k + 1 rows of a token are read once, y is written once. KC > 0: k ==
+// KC known at compile time, so all k + 1 loads are in flight together; KC == 0: any k.
+template <class OT, int KC>
 __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ S, const OT* __restrict__ P,
-                                                 OT* __restrict__ y, int64_t n_tok, int k, int d) {
+                                                 OT* __restrict__ y, int64_t n_tok, int k_rt, int d) {
   constexpr int V = 16 / sizeof(OT);
+  const int k = KC > 0 ? KC : k_rt;
   const int64_t per_row = d / V;
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= n_tok * per_row) return;
@@ -1260,15 +1290,21 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ S, const
   float acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+  uint4 pv[KC > 0 ? KC : 1];
+  if constexpr (KC > 0) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) pv[j] = *(const uint4*)(P + (t * k + j) * d + c);
+  }
   if (S) {  // no shared expert: S = 0
     const uint4 s = *(const uint4*)(S + t * d + c);
     const OT* sv = (const OT*)&s;
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = load_as_f32<OT>(sv + v);
   }
+#pragma unroll
   for (int j = 0; j < k; ++j) {
-    const uint4 pv = *(const uint4*)(P + (t * k + j) * d + c);
-    const OT* pp = (const OT*)&pv;
+    if constexpr (KC == 0) pv[0] = *(const uint4*)(P + (t * k + j) * d + c);
+    const OT* pp = (const OT*)&pv[KC > 0 ? j : 0];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] += load_as_f32<OT>(pp + v);
   }
@@ -1279,18 +1315,29 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ S, const
   *(uint4*)(y + t * d + c) = o;
 }
 
+template <class OT>
+static void launch_combine_t(dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                             const void* S, const void* P, void* y, int64_t n_tok, int k, int d) {
+  const OT *Sp = (const OT*)S, *Pp = (const OT*)P;
+  OT* yp = (OT*)y;
+  switch (k) {
+    case 1: launch_k(k_combine<OT, 1>, grid, dim3(256), 0, s, e0, e1, Sp, Pp, yp, n_tok, k, d); break;
+    case 2: launch_k(k_combine<OT, 2>, grid, dim3(256), 0, s, e0, e1, Sp, Pp, yp, n_tok, k, d); break;
+    case 4: launch_k(k_combine<OT, 4>, grid, dim3(256), 0, s, e0, e1, Sp, Pp, yp, n_tok, k, d); break;
+    case 6: launch_k(k_combine<OT, 6>, grid, dim3(256), 0, s, e0, e1, Sp, Pp, yp, n_tok, k, d); break;
+    case 8: launch_k(k_combine<OT, 8>, grid, dim3(256), 0, s, e0, e1, Sp, Pp, yp, n_tok, k, d); break;
+    default: launch_k(k_combine<OT, 0>, grid, dim3(256), 0, s, e0, e1, Sp, Pp, yp, n_tok, k, d);
+  }
+}
+
 hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, int64_t n_tok,
                           int k, int d, bool f32, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int V = f32 ? 4 : 8;
   const int64_t n = n_tok * (d / V);
   if (n == 0) return mark_empty(s, e0, e1), hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
-  if (f32)
-    launch_k(k_combine<float>, grid, dim3(256), 0, s, e0, e1, (const float*)y_shared,
-             (const float*)y_slots, (float*)y, n_tok, k, d);
-  else
-    launch_k(k_combine<bf16_t>, grid, dim3(256), 0, s, e0, e1, (const bf16_t*)y_shared,
-             (const bf16_t*)y_slots, (bf16_t*)y, n_tok, k, d);
+  if (f32) launch_combine_t<float>(grid, s, e0, e1, y_shared, y_slots, y, n_tok, k, d);
+  else launch_combine_t<bf16_t>(grid, s, e0, e1, y_shared, y_slots, y, n_tok, k, d);
   return hipGetLastError();
 }
 
