@@ -567,6 +567,9 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   constexpr int SC_B = KT / 32;                    // MX scale bytes per row per K step
   // LDS-DMA instructions one wave issues per K step
   constexpr int DMA_PER_STEP = A_SLABS + B_SLABS + (EL == Elem::FP8 ? 2 : 0);
+  // K-loop barrier placement: before the last sub-step of the previous step (bf16, float32),
+  // or at the start of the step (MXFP8)
+  constexpr bool EARLY_X = EL != Elem::FP8;
   const int m = uniform(entry.x), local = uniform(entry.y);
   const int row0 = uniform(entry.z);
   const int g = uniform(entry.w >> 16), rows = uniform(entry.w & 0xFFFF);
@@ -712,11 +715,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
                                : nullptr;
     return s;
   };
-  // (a) LDS-DMA issue of K step kt into buffer b: instruction q of the step (A slabs, B slabs,
-  // then the MX scale words). issue_at(kt, b, n) issues those that belong after MFMA n of the
-  // current step (q * SPAN / DMA_PER_STEP == n); n = -1: before the first.
-  constexpr int N_MFMA = SUB * FM * FN;             // MFMAs per K step and wave
-  constexpr int SPAN = C::ISSUE_SPAN < N_MFMA ? C::ISSUE_SPAN : N_MFMA;
+  // LDS-DMA instruction q of K step kt into buffer b (A slabs, B slabs, then the MX scale words).
   auto issue_one = [&](const StepAddr& s, const Bufs<C>& b, int q) {
     __builtin_amdgcn_sched_barrier(0);             // keeps the DMA between its two MFMAs
     if (q < A_SLABS) {
@@ -732,6 +731,78 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  // A step's DMA is spread over 2 MPS MFMA slots, one instruction per DMA_SLOT_STRIDE MFMAs or
+  // so: slot sigma(q) = q * 2 MPS / DMA_PER_STEP. Slots [0, MPS) are the last sub-step of the
+  // step two before it, slots [MPS, 2 MPS) the first sub-step of the step before it.
+  constexpr int MPS = FM * FN;                      // MFMAs per sub-step and wave
+  static_assert(SUB >= 2 && SUB % 2 == 0, "the last sub-step uses fragment slot 1");
+  auto issue_slot = [&](const StepAddr& s, const Bufs<C>& b, int slot) {
+#pragma unroll
+    for (int q = 0; q < DMA_PER_STEP; ++q)
+      if (q * 2 * MPS / DMA_PER_STEP == slot) issue_one(s, b, q);
+  };
+  f32x16_t acc[FM][FN];                             // cleared once the first DMA is out
+
+  const int h = lane >> 5, l32 = lane & 31;
+  const int xsw = (l32 >> SWS) & (CH - 1);         // swizzle of the lane's fragment rows
+  // Fragments, double-buffered across the K sub-steps (slot s & 1 for sub-step s): the reads of
+  // sub-step s + 1 are issued before the MFMAs of s, and the reads of the next step's sub-step
+  // 0 before the MFMAs of this step's last sub-step. Scheduling barriers pin that order (left
+  // alone the scheduler sinks each read to just before its first use, and every sub-step waits
+  // on LDS latency).
+  uint4 fa[2][FM][2], fb[2][FN][2];
+  uint32_t asc[2][FM], bsc[2][FN];
+  auto load = [&](const Bufs<C>& b, int kt, int s, int f) {
+    const char* a_buf = (const char*)&b.A[blk_row(0) + l32][0];
+    const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
+    const int sc_shift = 8 * (((uint32_t)kt * SC_B) & 3);
+    const int c0 = ((frag_chunk<EL>(s, h, 0)) ^ xsw) * 16;
+    const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ xsw) * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c0);
+      if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c1);
+      if (EL == Elem::FP8)
+        asc[f][i] = (b.As[blk_row(i) + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      fb[f][j][0] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c0);
+      if (TR::CPL == 2) fb[f][j][1] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c1);
+      if (EL == Elem::FP8)
+        bsc[f][j] = (b.Bs[wn * WN + j * 32 + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
+    }
+  };
+  // MFMAs of sub-steps 0 .. SUB - 2 of step kt from buffer b (sub-step 0's fragments already
+  // read); after(n) runs after MFMA n of sub-step 0 (the DMA slots there).
+  auto phase_b = [&](const Bufs<C>& b, int kt, auto&& after) {
+#pragma unroll
+    for (int s = 0; s + 1 < SUB; ++s) {
+      load(b, kt, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);   // the reads of s + 1 go out before the MFMAs of s
+      mfma_step<EL, FM, FN>(fa[s & 1], fb[s & 1], asc[s & 1], bsc[s & 1], acc,
+                            [&](int n) { if (s == 0) after(n); });
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // MFMAs of the last sub-step (fragments in slot 1); after(n) after MFMA n.
+  auto phase_e = [&](auto&& after) {
+    mfma_step<EL, FM, FN>(fa[1], fb[1], asc[1], bsc[1], acc, [&](int n) { after(n); });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Barrier X(kt) of K step kt: every wave's DMA of step kt has landed, and every wave has its
+  // reads of step kt - 1 back (so that buffer may be refilled). It sits before the last
+  // sub-step of step kt - 1, whose fragments are already in registers.
+  auto barrier_x = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0) (gfx9 encoding, expcnt left at 7)
+    lds_barrier();
+  };
+
+  // Late-barrier K loop (MXFP8: its fragments and scales leave no registers for the early
+  // barrier's overlap). issue_at(kt, b, n) issues the DMA instructions of step kt that belong
+  // after MFMA n of the current step (q * SPAN / DMA_PER_STEP == n); n = -1: before the first.
+  constexpr int N_MFMA = SUB * FM * FN;             // MFMAs per K step and wave
+  constexpr int SPAN = C::ISSUE_SPAN < N_MFMA ? C::ISSUE_SPAN : N_MFMA;
   auto issue_at = [&](const StepAddr& s, const Bufs<C>& b, int n) {
 #pragma unroll
     for (int q = 0; q < DMA_PER_STEP; ++q)
@@ -742,10 +813,6 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
 #pragma unroll
     for (int q = 0; q < DMA_PER_STEP; ++q) issue_one(s, b, q);
   };
-  f32x16_t acc[FM][FN];                             // cleared once the first DMA is out
-
-  const int h = lane >> 5, l32 = lane & 31;
-  const int xsw = (l32 >> SWS) & (CH - 1);         // swizzle of the lane's fragment rows
   // MFMAs of one K step from buffer b (kt: the step, for the MX scale byte position).
   // Fragments are double-buffered across the K sub-steps: the reads of sub-step s + 1 are
   // issued before the MFMAs of s (scheduling barriers pin that order; left alone the scheduler
@@ -790,7 +857,58 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     }
   };
 
-  {
+  if constexpr (EARLY_X) {
+    // K loop over two buffers. Step kt: B phase (sub-steps 0 .. SUB - 2 from buffer kt % 2,
+    // finishing the DMA of step kt + 1), then X(kt + 1), the reads of step kt + 1's sub-step 0,
+    // and the E phase (the last sub-step of kt, starting the DMA of step kt + 2 into the buffer
+    // kt just released). The steady state is unrolled by 2 so every buffer's role is static.
+    if (nk > 0) {
+#pragma unroll
+      for (int q = 0; q < DMA_PER_STEP; ++q) issue_one(step_addr(0), sm.buf[0], q);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    barrier_x();                                    // X(0)
+    at_step0();
+    if (nk > 1) {
+      const StepAddr s1 = step_addr(1);
+#pragma unroll
+      for (int slot = 0; slot < MPS; ++slot) issue_slot(s1, sm.buf[1], slot);
+    }
+    if (nk > 0) load(sm.buf[0], 0, 0, 0);
+    auto steady = [&](int kt, const Bufs<C>& cur, const Bufs<C>& nxt) {
+      const StepAddr s1 = step_addr(kt + 1);
+      phase_b(cur, kt, [&](int n) { issue_slot(s1, nxt, MPS + n); });
+      barrier_x();                                  // X(kt + 1)
+      if (kt + 1 < 4) after_step(kt + 1);
+      load(nxt, kt + 1, 0, 0);
+      const StepAddr s2 = step_addr(kt + 2);
+      phase_e([&](int n) { issue_slot(s2, cur, n); });
+    };
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 2) {
+      steady(kt, sm.buf[0], sm.buf[1]);
+      steady(kt + 1, sm.buf[1], sm.buf[0]);
+    }
+    for (; kt < nk; ++kt) {     // the last steps, buffers chosen at run time
+      const bool has1 = kt + 1 < nk, has2 = kt + 2 < nk;
+      const Bufs<C> cur = pick(sm, kt & 1), nxt = pick(sm, (kt + 1) & 1);
+      const StepAddr s1 = step_addr(has1 ? kt + 1 : kt);
+      phase_b(cur, kt, [&](int n) { if (has1) issue_slot(s1, nxt, MPS + n); });
+      if (has1) {
+        barrier_x();
+        if (kt + 1 < 4) after_step(kt + 1);
+        load(nxt, kt + 1, 0, 0);
+      }
+      const StepAddr s2 = step_addr(has2 ? kt + 2 : kt);
+      phase_e([&](int n) { if (has2) issue_slot(s2, cur, n); });
+    }
+  } else {
     // K loop over a ring of ST buffers. Step kt: wait until this wave's DMA of kt has landed
     // (later steps' DMAs stay in flight), barrier (every wave's DMA of kt landed; every wave
     // done computing kt - 1), issue step kt + ST - 1 into the buffer kt - 1 used, compute kt.
