@@ -297,16 +297,20 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     const int64_t rI = (int64_t)a->E_l * a->I, rD = (int64_t)a->E_l * a->d;
     const bool sh = p.I_sh > 0;
     hipEvent_t q0 = ev_start(MOK_STAGE_QUANT), q1 = ev_stop(MOK_STAGE_QUANT);
-    hipError_t e = launch_quantize_mxfp8(a->w_gate, rI, a->d, wg_q, wg_s, s, q0, nullptr);
-    if (e == hipSuccess) e = launch_quantize_mxfp8(a->w_up, rI, a->d, wu_q, wu_s, s);
+    // scales K-step major per matrix (the layout the GEMMs' scale loads read)
+    hipError_t e = launch_quantize_mxfp8(a->w_gate, rI, a->d, wg_q, wg_s, s, q0, nullptr, a->I);
     if (e == hipSuccess)
-      e = launch_quantize_mxfp8(a->w_down, rD, a->I, wd_q, wd_s, s, nullptr, sh ? nullptr : q1);
+      e = launch_quantize_mxfp8(a->w_up, rI, a->d, wu_q, wu_s, s, nullptr, nullptr, a->I);
+    if (e == hipSuccess)
+      e = launch_quantize_mxfp8(a->w_down, rD, a->I, wd_q, wd_s, s, nullptr, sh ? nullptr : q1,
+                                a->d);
     if (e == hipSuccess && sh) {
-      e = launch_quantize_mxfp8(a->ws_gate, p.I_sh, a->d, sg_q, sg_s, s);
-      if (e == hipSuccess) e = launch_quantize_mxfp8(a->ws_up, p.I_sh, a->d, su_q, su_s, s);
+      e = launch_quantize_mxfp8(a->ws_gate, p.I_sh, a->d, sg_q, sg_s, s, nullptr, nullptr, p.I_sh);
+      if (e == hipSuccess)
+        e = launch_quantize_mxfp8(a->ws_up, p.I_sh, a->d, su_q, su_s, s, nullptr, nullptr, p.I_sh);
       if (e == hipSuccess)
         e = launch_quantize_mxfp8(a->ws_down, (int64_t)a->n_shared * a->d, a->I_shared, sd_q,
-                                  sd_s, s, nullptr, q1);
+                                  sd_s, s, nullptr, q1, a->d);
     }
     if (e != hipSuccess) return MOK_EHIP;
     p.wg = wg_q; p.wu = wu_q; p.wd = wd_q; p.sg = sg_q; p.su = su_q; p.sd = sd_q;

@@ -657,28 +657,29 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     const int n = min(b_row0(q) + lane / CH, N - 1);
     b_off[q] = (uint32_t)(n * b_row_bytes) + chunk_b(q);
   }
-  // ---- MX scales: lane L of wave w carries tile row 64w + L. A K step needs SC_B scale bytes
-  // of a row; the 4-byte word holding them (4 | SC_B * steps) is loaded.
+  // ---- MX scales: lane L of wave w carries tile row 64w + L. A K step needs the 4 scale bytes
+  // of a row, one word of the K-step-major layout (mx_kmajor_scale): the step's words of
+  // consecutive rows are contiguous, so a wave's scale load reads 256 consecutive bytes.
   const uint8_t* a_sc_base = nullptr;
   const uint8_t* b_sc_base = nullptr;
   uint32_t a_sc_off = 0, b_sc_off = 0;
+  int64_t a_sc_R = 0, b_sc_R = 0;                    // rows of the scale matrices
   if (EL == Elem::FP8) {
     const int r = min(RA * wid + lane, rows_valid - 1);
-    const int64_t a_sc_row = UP ? p.d / 32 : p.Hld / 32;
-    a_sc_base = (UP ? p.A_sc : p.H_sc) + (ring_row0 + m0) * a_sc_row;
-    a_sc_off = (uint32_t)(r * a_sc_row);
-    int64_t b_sc_row;
+    a_sc_R = (int64_t)p.n_slots * p.mb;              // A rows and H: the ring rows
+    a_sc_base = (UP ? p.A_sc : p.H_sc) + (ring_row0 + m0) * 4;
+    a_sc_off = (uint32_t)(r * 4);
     if (UP) {
       const bool uph = b_up_slab(0);               // the wave's 64 rows are all gate or all up
       const uint8_t* S = shared ? (uph ? p.su_sc : p.sg_sc) : (uph ? p.wu_sc : p.wg_sc);
-      b_sc_row = p.d / 32;
-      b_sc_base = S + (shared ? 0 : (int64_t)g * p.I * b_sc_row);
+      b_sc_R = shared ? p.I_sh : p.I;
+      b_sc_base = S + (shared ? 0 : (int64_t)g * p.I * (p.d / 32));
     } else {
-      b_sc_row = shared ? p.I_seg / 32 : p.I / 32;
-      b_sc_base = shared ? p.sd_sc : p.wd_sc + (int64_t)g * p.d * b_sc_row;
+      b_sc_R = p.d;
+      b_sc_base = shared ? p.sd_sc : p.wd_sc + (int64_t)g * p.d * (p.I / 32);
     }
     const int n = min(b_row0(0) + lane, N - 1);
-    b_sc_off = (uint32_t)(n * b_sc_row);
+    b_sc_off = (uint32_t)(n * 4);
     a_sc_base = uniform_ptr(a_sc_base);
     b_sc_base = uniform_ptr(b_sc_base);
   }
@@ -709,8 +710,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     s.ka = k0 * TR::ES;
     s.kb = kin * TR::ES;
     s.b_seg = uniform_ptr(b_base + (int64_t)seg * b_seg_stride);
-    s.sca = (k0 / 32) & ~3u;
-    s.scb = (kin / 32) & ~3u;
+    s.sca = (uint32_t)((k0 / 128) * a_sc_R * 4);     // MXFP8: K steps of 128 elements
+    s.scb = (uint32_t)((kin / 128) * b_sc_R * 4);
     s.bs_seg = EL == Elem::FP8 ? uniform_ptr(b_sc_base + (int64_t)seg * (b_seg_stride / 32))
                                : nullptr;
     return s;
@@ -1030,7 +1031,9 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
           if (r < rows_valid && col0 + c < N) {
             const int64_t hr = ring_row0 + m0 + r;
             *(uint2*)((uint8_t*)p.H + hr * p.Hld + col0 + c) = codes;
-            if ((c & 31) == 0) p.H_sc[hr * (p.Hld / 32) + (col0 + c) / 32] = (uint8_t)(se + 127);
+            if ((c & 31) == 0)
+              p.H_sc[mx_kmajor_scale(hr, (col0 + c) / 32, (int64_t)p.n_slots * p.mb)] =
+                  (uint8_t)(se + 127);
           }
         } else {
           const u32x4 val = *(const lds_u4*)src;
@@ -1192,10 +1195,13 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
     tok_row[t] = (g >= p.E_l ? p.own_begin + first + r : (int64_t)(p.route_ids[first + r] / p.k)) * p.d;
   }
   __syncthreads();
-  const int per_row = p.d / 8;                       // quads per row (a multiple of 4)
-  const int total = rows * per_row;
+  // A wave quantises one 128-element K step of 4 consecutive rows (16 lanes a row), so its
+  // scale bytes (K-step-major words of consecutive ring rows) are contiguous.
+  const int steps = p.d / 128;
+  const int total = (rows + 3) / 4 * steps * 64;
   const int nt = 64 * n_waves;
   const int64_t ring0 = (int64_t)wl_slot(p.wl, cap)[m] * p.mb + r_begin;
+  const int64_t R = (int64_t)p.n_slots * p.mb;
   const int n_iter = (total + GQ_UNROLL * nt - 1) / (GQ_UNROLL * nt);   // same for every lane
   for (int it = 0; it < n_iter; ++it) {
     uint4 raw[GQ_UNROLL];
@@ -1203,9 +1209,12 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
 #pragma unroll
     for (int u = 0; u < GQ_UNROLL; ++u) {
       const int q = t + (it * GQ_UNROLL + u) * nt;
-      const bool ok = q < total;
-      rr[u] = ok ? q / per_row : 0;
-      cc[u] = ok ? q - rr[u] * per_row : -1;
+      const uint32_t unit = (uint32_t)q >> 6;
+      const int li = q & 63, rg = (int)(unit / (uint32_t)steps), j = (int)unit - rg * steps;
+      const int r = rg * 4 + (li >> 4);
+      const bool ok = q < total && r < rows;
+      rr[u] = ok ? r : 0;
+      cc[u] = ok ? j * 16 + (li & 15) : -1;
       raw[u] = ok ? *(const uint4*)((const bf16_t*)p.x + tok_row[rr[u]] + 8 * cc[u])
                   : make_uint4(0, 0, 0, 0);
     }
@@ -1216,7 +1225,7 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
       if (cc[u] >= 0) {
         const int64_t hr = ring0 + rr[u];
         *(uint2*)(p.A_codes + hr * p.d + 8 * cc[u]) = codes;
-        if ((cc[u] & 3) == 0) p.A_sc[hr * (p.d / 32) + cc[u] / 4] = (uint8_t)(sh + 127);
+        if ((cc[u] & 3) == 0) p.A_sc[mx_kmajor_scale(hr, cc[u] / 4, R)] = (uint8_t)(sh + 127);
       }
     }
   }

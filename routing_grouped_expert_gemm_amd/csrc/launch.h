@@ -35,9 +35,18 @@ hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l
                        int32_t* blk_base, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
 
+// MX scales of the operands the expert GEMMs read are stored K-step major: a matrix of R rows
+// and K columns keeps the 4 scales of K step j (128 elements) of row r as the 4-byte word
+// j * R + r, so one K step's scales of consecutive rows are contiguous. Byte offset of the
+// scale of (row r, 32-element block b):
+__host__ __device__ inline int64_t mx_kmajor_scale(int64_t r, int b, int64_t R) {
+  return ((int64_t)(b >> 2) * R + r) * 4 + (b & 3);
+}
+// scales_kmajor == 0: scales row-major [rows, K/32] (the mok_quantize_mxfp8 layout); R > 0: the
+// rows form rows / R matrices of R rows, each with K-step-major scales (mx_kmajor_scale).
 hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s, hipEvent_t e0 = nullptr,
-                                 hipEvent_t e1 = nullptr);
+                                 hipEvent_t e1 = nullptr, int64_t scales_kmajor = 0);
 
 // Operand element type of the expert GEMMs.
 enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2 };
@@ -68,12 +77,15 @@ struct ExpertPass {
   const int32_t* offsets;
   const void *wg, *wu, *wd;     // routed weights (float32 / bf16) -- or MX codes
   const void *sg, *su, *sd;     // shared weights
-  const uint8_t *wg_sc, *wu_sc, *wd_sc, *sg_sc, *su_sc, *sd_sc;  // MX scales (FP8 only)
+  // MX scales (FP8 only), K-step major per matrix: routed gate/up one matrix of I rows per
+  // expert, down d rows per expert; shared gate/up one matrix of I_sh rows, down d rows per
+  // shared expert
+  const uint8_t *wg_sc, *wu_sc, *wd_sc, *sg_sc, *su_sc, *sd_sc;
   // ring
   void* H;               // [n_slots*mb, Hld] (float32/bf16) -- MX: codes
-  uint8_t* H_sc;         // MX: [n_slots*mb, Hld/32]
+  uint8_t* H_sc;         // MX: K-step-major scales of the n_slots*mb ring rows of H
   uint8_t* A_codes;      // MX: gathered x rows [n_slots*mb, d]
-  uint8_t* A_sc;         // MX: [n_slots*mb, d/32]
+  uint8_t* A_sc;         // MX: K-step-major scales of the n_slots*mb ring rows of A
   // work list
   int32_t* wl;           // work-list block (see expert_gemm.hip)
   // outputs

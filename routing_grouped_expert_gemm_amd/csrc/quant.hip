@@ -10,35 +10,69 @@
 
 namespace mok {
 
+// KMAJOR: a wave quantises one 128-element K step of 4 consecutive rows (16 lanes a row), so
+// its 16 scale bytes -- 4 K-step-major words of consecutive rows -- are contiguous too.
+template <bool KMAJOR>
 __global__ __launch_bounds__(256) void k_quantize_mxfp8(const bf16_t* __restrict__ src,
-                                                        int64_t n_chunks,
+                                                        int64_t rows, int K, int64_t R,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales) {
+  const int64_t n_chunks = KMAJOR ? (rows + 3) / 4 * (K / 128) * 64 : rows * (K / 8);
   const int64_t stride = (int64_t)gridDim.x * 256;
   // every lane of a wave runs the same number of iterations (the quad shuffles need the whole
   // quad): lanes past the end load and store nothing
   const int64_t n_iter = (n_chunks + stride - 1) / stride;
   int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   for (int64_t it = 0; it < n_iter; ++it, q += stride) {
-    const bool ok = q < n_chunks;
-    const uint4 raw = ok ? *(const uint4*)(src + q * 8) : make_uint4(0, 0, 0, 0);
+    int64_t at;                                   // first element of the lane's 8
+    bool ok;
+    int64_t row = 0;
+    int c8 = 0;
+    if constexpr (KMAJOR) {
+      const uint32_t unit = (uint32_t)(q >> 6);   // 4 rows x one K step (< 2^31 units)
+      const uint32_t steps = (uint32_t)K / 128, li = (uint32_t)q & 63;
+      const uint32_t rg = unit / steps;
+      const int j = (int)(unit - rg * steps);
+      row = (int64_t)rg * 4 + (li >> 4);
+      c8 = j * 16 + (li & 15);
+      ok = q < n_chunks && row < rows;
+      at = row * K + 8 * c8;
+    } else {
+      ok = q < n_chunks;
+      at = q * 8;
+    }
+    const uint4 raw = ok ? *(const uint4*)(src + at) : make_uint4(0, 0, 0, 0);
     int sh;
     const uint2 c = quantize_quad8(raw, &sh);
     if (ok) {
-      *(uint2*)(codes + q * 8) = c;
-      if ((q & 3) == 0) scales[q >> 2] = (uint8_t)(sh + 127);
+      *(uint2*)(codes + at) = c;
+      if (((at >> 3) & 3) == 0) {
+        int64_t sa = at >> 5;
+        if constexpr (KMAJOR) {
+          const int64_t g = (uint32_t)row / (uint32_t)R;   // matrix g, its row row - g R
+          sa = g * R * (K / 32) + mx_kmajor_scale(row - g * R, c8 >> 2, R);
+        }
+        scales[sa] = (uint8_t)(sh + 127);
+      }
     }
   }
 }
 
 hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const int64_t n_chunks = rows * (K / 8);
+                                 uint8_t* scales, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                                 int64_t scales_kmajor) {
+  const int64_t n_chunks = scales_kmajor > 0 ? (rows + 3) / 4 * (K / 128) * 64 : rows * (K / 8);
   if (n_chunks == 0) return mark_empty(s, e0, e1), hipSuccess;
+  if (scales_kmajor > 0 && (rows >= INT32_MAX || n_chunks / 64 >= INT32_MAX))
+    return hipErrorInvalidValue;                  // the K-major index math is 32-bit
   const int64_t want = (n_chunks + 255) / 256;
   const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
-  launch_k(k_quantize_mxfp8, dim3(grid), dim3(256), 0, s, e0, e1, (const bf16_t*)src_bf16,
-           n_chunks, codes, scales);
+  if (scales_kmajor > 0)
+    launch_k(k_quantize_mxfp8<true>, dim3(grid), dim3(256), 0, s, e0, e1, (const bf16_t*)src_bf16,
+             rows, K, scales_kmajor, codes, scales);
+  else
+    launch_k(k_quantize_mxfp8<false>, dim3(grid), dim3(256), 0, s, e0, e1, (const bf16_t*)src_bf16,
+             rows, K, (int64_t)0, codes, scales);
   return hipGetLastError();
 }
 
