@@ -323,12 +323,9 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
 // step moves ROW_B bytes of every operand row into one of STAGES LDS buffers by LDS-DMA
 // (global_load_lds_dwordx4); loader wave w fills A rows [RA w, RA w + RA) and B rows
 // [RB w, RB w + RB), RPI rows per instruction.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_, int ISSUE_SPAN_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROW_B_, int STAGES_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  // The LDS-DMA instructions of the next K step are spread evenly over the first ISSUE_SPAN
-  // MFMAs of the current one (0: all before the first MFMA)
-  static constexpr int ISSUE_SPAN = ISSUE_SPAN_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
@@ -349,7 +346,7 @@ constexpr int TILE_M = 256;
 // 256 x 256 tiles, 4 waves of 128 x 128 (16 accumulator blocks = 256 AGPRs per lane), one
 // workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs. Two 64 KB K stages of
 // 128 bytes per row (whole cache lines), filled by LDS-DMA.
-typedef Cfg<256, 256, 2, 2, 128, 2, 32> Big;
+typedef Cfg<256, 256, 2, 2, 128, 2> Big;
 
 // Per element type: bytes per element, and the MFMA's K per instruction.
 template <Elem EL> struct Tr;
@@ -801,9 +798,11 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
 
   // Late-barrier K loop (MXFP8: its fragments and scales leave no registers for the early
   // barrier's overlap). issue_at(kt, b, n) issues the DMA instructions of step kt that belong
-  // after MFMA n of the current step (q * SPAN / DMA_PER_STEP == n); n = -1: before the first.
+  // after MFMA n of the current step (q * SPAN / DMA_PER_STEP == n), spread over the step's
+  // first half (spread over all of it, the last ones land too late: MXFP8 EP64 share gate/up
+  // 1.16 ms against 1.13).
   constexpr int N_MFMA = SUB * FM * FN;             // MFMAs per K step and wave
-  constexpr int SPAN = C::ISSUE_SPAN < N_MFMA ? C::ISSUE_SPAN : N_MFMA;
+  constexpr int SPAN = N_MFMA / 2;                  // the first half of the step
   auto issue_at = [&](const StepAddr& s, const Bufs<C>& b, int n) {
 #pragma unroll
     for (int q = 0; q < DMA_PER_STEP; ++q)
