@@ -698,39 +698,46 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   };
 
   // address pieces of K step kt
-  struct StepAddr { uint32_t ka, kb, sca, scb; const char* b_seg; const uint8_t* bs_seg; };
+  // Uniform base addresses of K step kt's operand rows (A, B, and for the gate/up stage the up
+  // rows of B) and MX scale words. The step's K offset rides on these scalar bases, so the
+  // per-lane offsets of the DMA instructions stay fixed over the K loop and no vector register
+  // or instruction is spent on addresses per step.
+  struct StepAddr { const char *a, *b, *bu; const uint8_t *sa, *sb; };
   auto step_addr = [&](int kt) {
     StepAddr s;
     const uint32_t k0 = (uint32_t)kt * KT;
     const uint32_t seg = k0 / (uint32_t)b_seg_len;
     const uint32_t kin = k0 - seg * (uint32_t)b_seg_len;
-    s.ka = k0 * TR::ES;
-    s.kb = kin * TR::ES;
-    s.b_seg = uniform_ptr(b_base + (int64_t)seg * b_seg_stride);
-    s.sca = (uint32_t)((k0 / 128) * a_sc_R * 4);     // MXFP8: K steps of 128 elements
-    s.scb = (uint32_t)((kin / 128) * b_sc_R * 4);
-    s.bs_seg = EL == Elem::FP8 ? uniform_ptr(b_sc_base + (int64_t)seg * (b_seg_stride / 32))
-                               : nullptr;
+    s.a = uniform_ptr(a_base + k0 * TR::ES);
+    s.b = uniform_ptr(b_base + (int64_t)seg * b_seg_stride + kin * TR::ES);
+    s.bu = UP ? uniform_ptr(b_up + kin * TR::ES) : nullptr;
+    if (EL == Elem::FP8) {                           // K steps of 128 elements: one scale word
+      s.sa = uniform_ptr(a_sc_base + (int64_t)(k0 / 128) * a_sc_R * 4);
+      s.sb = uniform_ptr(b_sc_base + (int64_t)seg * (b_seg_stride / 32) +
+                         (int64_t)(kin / 128) * b_sc_R * 4);
+    } else {
+      s.sa = s.sb = nullptr;
+    }
     return s;
   };
   // LDS-DMA instruction q of K step kt into buffer b (A slabs, B slabs, then the MX scale words).
   auto issue_one = [&](const StepAddr& s, const Bufs<C>& b, int q) {
     __builtin_amdgcn_sched_barrier(0);             // keeps the DMA between its two MFMAs
     if (q < A_SLABS) {
-      dma_b128<A_L2C>(a_base, a_off[q] + s.ka, uniform(lds_addr(&b.A[RA * wid][0])) + 1024 * q);
+      dma_b128<A_L2C>(s.a, a_off[q], uniform(lds_addr(&b.A[RA * wid][0])) + 1024 * q);
     } else if (q < A_SLABS + B_SLABS) {
       const int r = q - A_SLABS;
-      const char* bb = (UP && b_up_slab(r)) ? b_up : s.b_seg;
-      dma_b128(bb, b_off[r] + s.kb, uniform(lds_addr(&b.B[RB * wid][0])) + 1024 * r);
+      const char* bb = (UP && b_up_slab(r)) ? s.bu : s.b;
+      dma_b128(bb, b_off[r], uniform(lds_addr(&b.B[RB * wid][0])) + 1024 * r);
     } else if (q == A_SLABS + B_SLABS) {
-      dma_b32<A_L2C>(a_sc_base, a_sc_off + s.sca, uniform(lds_addr(&b.As[64 * wid])));
+      dma_b32<A_L2C>(s.sa, a_sc_off, uniform(lds_addr(&b.As[64 * wid])));
     } else {
-      dma_b32(s.bs_seg, b_sc_off + s.scb, uniform(lds_addr(&b.Bs[64 * wid])));
+      dma_b32(s.sb, b_sc_off, uniform(lds_addr(&b.Bs[64 * wid])));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // A step's DMA is spread over 2 MPS MFMA slots, one instruction per DMA_SLOT_STRIDE MFMAs or
-  // so: slot sigma(q) = q * 2 MPS / DMA_PER_STEP. Slots [0, MPS) are the last sub-step of the
+  // A step's DMA is spread over 2 MPS MFMA slots, about one instruction per two MFMAs: slot
+  // sigma(q) = q * 2 MPS / DMA_PER_STEP. Slots [0, MPS) are the last sub-step of the
   // step two before it, slots [MPS, 2 MPS) the first sub-step of the step before it.
   constexpr int MPS = FM * FN;                      // MFMAs per sub-step and wave
   static_assert(SUB >= 2 && SUB % 2 == 0, "the last sub-step uses fragment slot 1");
