@@ -32,8 +32,8 @@ namespace mok {
 // ------------------------------------------------------------------------- work list
 // int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, the
 // prefix sums of its gather, up and down items, three completion counters, its ring slot, the
-// minibatch that used that slot before it (-1: none) and the prefix of its weighted work (XCD
-// split); then, 16-byte aligned, one int4 per
+// minibatch that used that slot before it (-1: none), the prefix of its weighted work (XCD
+// split) and the prefix of its rows; then, 16-byte aligned, one int4 per
 // up tile and per down tile {minibatch, tile within it, first row, group << 16 | rows} so that a
 // workgroup finds its tile with a single load, and (ring work loop only) the ring order of all
 // items, the item kind in bits 28+ of the second field.
@@ -58,7 +58,8 @@ MOK_DEV int32_t* wl_done(int32_t* wl, int cap, int kind) { return wl + WL_HDR + 
 MOK_DEV int32_t* wl_slot(int32_t* wl, int cap) { return wl + WL_HDR + 9 * cap + 3; }
 MOK_DEV int32_t* wl_prev(int32_t* wl, int cap) { return wl + WL_HDR + 10 * cap + 3; }
 MOK_DEV int32_t* wl_wpre(int32_t* wl, int cap) { return wl + WL_HDR + 11 * cap + 3; }   // cap + 1
-MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 12 * (size_t)cap + 4 + 3) & ~(size_t)3; }
+MOK_DEV int32_t* wl_rpre(int32_t* wl, int cap) { return wl + WL_HDR + 12 * cap + 4; }   // cap + 1
+MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 13 * (size_t)cap + 5 + 3) & ~(size_t)3; }
 MOK_DEV int4* wl_utab(int32_t* wl, int cap) { return (int4*)(wl + wl_tab_off(cap)); }
 MOK_DEV int4* wl_dtab(int32_t* wl, int cap, int cap_u) { return (int4*)(wl + wl_tab_off(cap)) + cap_u; }
 MOK_DEV int4* wl_rtab(int32_t* wl, int cap, int cap_u, int cap_d) {
@@ -136,7 +137,8 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
   }
   __syncthreads();
   // item prefix sums: tiles of a minibatch = ceil(rows / bm) * n-tiles of its stage
-  int32_t carry_u = 0, carry_d = 0, carry_g = 0;
+  int32_t carry_u = 0, carry_d = 0, carry_g = 0, carry_r = 0;
+  int32_t* rp = wl_rpre(wl, cap);
   for (int c0 = 0; c0 < n_mb; c0 += 1024) {
     const int m = c0 + t;
     int32_t nu = 0, nd = 0, ng = 0;
@@ -146,18 +148,21 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
       nd = mt * nD;
       ng = gather ? (nr[m] + G_ROWS - 1) / G_ROWS : 0;
     }
-    int32_t tu, td, tg;
+    int32_t tu, td, tg, tr;
     const int32_t eu = block_excl_scan_1024(nu, sh, &tu);
     const int32_t ed = block_excl_scan_1024(nd, sh, &td);
     const int32_t eg = block_excl_scan_1024(ng, sh, &tg);
+    const int32_t er = block_excl_scan_1024(m < n_mb ? nr[m] : 0, sh, &tr);
     if (m < n_mb) {
       us[m] = carry_u + eu;
       ds[m] = carry_d + ed;
       gs[m] = carry_g + eg;
+      rp[m] = carry_r + er;
     }
     carry_u += tu;
     carry_d += td;
     carry_g += tg;
+    carry_r += tr;
   }
   const bool overflow = n_routed + n_sh > cap || carry_u > cap_u || carry_d > cap_d ||
                         (ring && (int64_t)carry_u + carry_d + carry_g > cap_r);
@@ -166,6 +171,7 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     us[n_mb] = carry_u;
     ds[n_mb] = carry_d;
     gs[n_mb] = carry_g;
+    rp[n_mb] = overflow ? 0 : carry_r;
     wl[WL_N_MB] = n_mb;
     wl[WL_N_U] = overflow ? 0 : carry_u;
     wl[WL_N_D] = overflow ? 0 : carry_d;
@@ -1237,16 +1243,34 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
   }
 }
 
-// Stage-ordered path: every minibatch's rows, before the up stage.
+// Stage-ordered path: every minibatch's rows, before the up stage. The rows of all minibatches
+// (in work-list order) are cut into one contiguous range per workgroup, of equal size to a row;
+// a workgroup walks its range in pieces of at most 16 rows of one minibatch.
 __global__ __launch_bounds__(256) void k_gather_quantize(ExpertPass p) {
+  constexpr int PIECE = 16;
   const int n_mb = p.wl[WL_N_MB];
   const int32_t* nr = wl_rows(p.wl, p.max_mb);
-  const int per_block = 16;                     // rows per work item (many items: even spread)
-  const int chunks = (p.mb + per_block - 1) / per_block;
-  for (int64_t q = blockIdx.x; q < (int64_t)n_mb * chunks; q += gridDim.x) {
-    const int m = (int)(q / chunks), c = (int)(q % chunks);
-    const int r0 = c * per_block, r1 = min(nr[m], r0 + per_block);
-    if (r0 < r1) gather_quantize_rows(p, m, r0, r1, threadIdx.x >> 6, 4);
+  const int32_t* rp = wl_rpre(p.wl, p.max_mb);
+  const int64_t total = rp[n_mb], G = gridDim.x;
+  const int32_t r_lo = (int32_t)(blockIdx.x * total / G), r_hi = (int32_t)((blockIdx.x + 1) * total / G);
+  if (r_lo >= r_hi) return;
+  int lo = 0, hi = n_mb;                            // rp[lo] <= r_lo < rp[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (rp[mid] <= r_lo) lo = mid; else hi = mid;
+  }
+  int m = lo;
+  int32_t r = r_lo - rp[m];                         // row within minibatch m
+  for (int32_t done = r_lo; done < r_hi;) {
+    if (r >= nr[m]) {                               // next minibatch (workgroup-uniform)
+      ++m;
+      r = 0;
+      continue;
+    }
+    const int32_t r1 = min(min(nr[m], r + PIECE), r + (r_hi - done));
+    gather_quantize_rows(p, m, r, r1, threadIdx.x >> 6, 4);
+    done += r1 - r;
+    r = r1;
   }
 }
 
