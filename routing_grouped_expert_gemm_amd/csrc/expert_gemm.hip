@@ -32,14 +32,15 @@ namespace mok {
 // ------------------------------------------------------------------------- work list
 // int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, the
 // prefix sums of its gather, up and down items, three completion counters, its ring slot, the
-// minibatch that used that slot before it (-1: none), the prefix of its weighted work (XCD
-// split) and the prefix of its rows; then, 16-byte aligned, one int4 per
+// minibatch that used that slot before it (-1: none), an unused word, the prefix of its rows,
+// and (ring) the item prefix sums in XCD-major order; then, 16-byte aligned, one int4 per
 // up tile and per down tile {minibatch, tile within it, first row, group << 16 | rows} so that a
 // workgroup finds its tile with a single load, and (ring work loop only) the ring order of all
 // items, the item kind in bits 28+ of the second field.
 // Header: counts, the error word, and for the ring loop the per-XCD split (WL_AFFINE set): XCD
-// x owns minibatches [XB[x], XB[x+1]) and ring items [XR[x], XR[x+1]), and takes them with its
-// own ticket TICKETS[x]; without the split every workgroup uses TICKETS[0] over all items.
+// x owns minibatches x, x + 8, x + 16, ... (positions [XB[x], XB[x+1]) of the XCD-major order)
+// and ring items [XR[x], XR[x+1]), and takes them with its own ticket TICKETS[x]; without the
+// split every workgroup uses TICKETS[0] over all items.
 constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_ERR = 4, WL_N_R = 5, WL_AFFINE = 6,
               WL_XB = 8, WL_XR = 17, WL_TICKETS = 26, WL_HDR = 48;
 constexpr int N_XCD = 8;        // XCDs of an MI355X, each with its own L2
@@ -57,9 +58,12 @@ MOK_DEV int32_t* wl_gstart(int32_t* wl, int cap) { return wl + WL_HDR + 5 * cap 
 MOK_DEV int32_t* wl_done(int32_t* wl, int cap, int kind) { return wl + WL_HDR + (6 + kind) * cap + 3; }
 MOK_DEV int32_t* wl_slot(int32_t* wl, int cap) { return wl + WL_HDR + 9 * cap + 3; }
 MOK_DEV int32_t* wl_prev(int32_t* wl, int cap) { return wl + WL_HDR + 10 * cap + 3; }
-MOK_DEV int32_t* wl_wpre(int32_t* wl, int cap) { return wl + WL_HDR + 11 * cap + 3; }   // cap + 1
 MOK_DEV int32_t* wl_rpre(int32_t* wl, int cap) { return wl + WL_HDR + 12 * cap + 4; }   // cap + 1
-MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 13 * (size_t)cap + 5 + 3) & ~(size_t)3; }
+// ring order: prefix sums of gather, up and down items over the minibatches in XCD-major order
+MOK_DEV int32_t* wl_pg(int32_t* wl, int cap) { return wl + WL_HDR + 13 * cap + 5; }     // cap + 1
+MOK_DEV int32_t* wl_pu(int32_t* wl, int cap) { return wl + WL_HDR + 14 * cap + 6; }     // cap + 1
+MOK_DEV int32_t* wl_pd(int32_t* wl, int cap) { return wl + WL_HDR + 15 * cap + 7; }     // cap + 1
+MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 16 * (size_t)cap + 8 + 3) & ~(size_t)3; }
 MOK_DEV int4* wl_utab(int32_t* wl, int cap) { return (int4*)(wl + wl_tab_off(cap)); }
 MOK_DEV int4* wl_dtab(int32_t* wl, int cap, int cap_u) { return (int4*)(wl + wl_tab_off(cap)) + cap_u; }
 MOK_DEV int4* wl_rtab(int32_t* wl, int cap, int cap_u, int cap_d) {
@@ -81,17 +85,16 @@ size_t worklist_ints(int max_mb, int cap_u, int cap_d, int cap_r) {
 // its ring slot before it; a gather item needs that minibatch's up items. With lag < slots
 // every dependency of an item lies earlier in this order.
 //
-// With at least 8 slots the ring is split by XCD: the minibatches are cut into 8 contiguous
-// ranges of about equal work (tiles), XCD x runs range x on its own slots (n_slots / 8 of
-// them, lag half of that) in the order above. A slot's producer and consumer then always share
-// one L2, and the handover needs no L2 write-back or invalidation. Otherwise (fewer slots) one
-// order covers all minibatches on all slots and every handover is made coherent device-wide.
+// With at least 8 slots the ring is split by XCD: XCD x runs minibatches x, x + 8, x + 16, ...
+// on its own slots (n_slots / 8 of them, lag half of that) in the order above. A slot's
+// producer and consumer then always share one L2, and the handover needs no L2 write-back or
+// invalidation. Otherwise (fewer slots) one order covers all minibatches on all slots and
+// every handover is made coherent device-wide.
 __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restrict__ counts,
                                                          const int32_t* __restrict__ offsets,
                                                          int E_l, int T_own, int mb, int bm,
                                                          int nU_r, int nU_s, int nD, bool gather,
-                                                         bool ring, int n_slots, int w_up,
-                                                         int w_dr, int w_ds, int w_g, int cap, int cap_u,
+                                                         bool ring, int n_slots, int cap, int cap_u,
                                                          int cap_d, int cap_r,
                                                          int32_t* __restrict__ wl) {
   __shared__ int32_t sh[1024];
@@ -180,45 +183,63 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     wl[WL_AFFINE] = affine ? 1 : 0;
   }
   if (t < N_XCD) wl[WL_TICKETS + t] = 0;
-  // XCD split (affine ring): minibatch m goes to the XCD holding the midpoint of its work
-  // (non-decreasing in m): its items weighted by their K steps (w_up per up tile, w_dr / w_ds
-  // per routed / shared down tile, w_g per gather item); xb[x] = first minibatch of XCD x
+  // Ring order. With at least 8 slots the ring is split by XCD: minibatch m belongs to XCD
+  // m % 8 as its (m / 8)-th minibatch, so the 8 XCDs run neighbouring minibatches -- mostly of
+  // the same expert -- at the same time, and weights that one XCD reads from HBM the others
+  // find in the chip's last-level cache (the MALL, shared by all XCDs). Without the split one
+  // order spans all minibatches. Positions: XCD-major order p = base(x) + j for m = x + 8 j
+  // (p = m without the split), and prefix sums of each item kind over p.
   __syncthreads();
-  int32_t* wpre = wl_wpre(wl, cap);                 // weighted work prefix
-  int64_t W = 0;
-  if (affine) {
-    int32_t carry = 0;
-    for (int c0 = 0; c0 < n_mb; c0 += 1024) {
-      const int m = c0 + t;
-      int32_t w = 0;
-      if (m < n_mb)
-        w = (us[m + 1] - us[m]) * w_up + (ds[m + 1] - ds[m]) * (grp[m] < E_l ? w_dr : w_ds) +
-            (gs[m + 1] - gs[m]) * w_g;
-      int32_t tot;
-      const int32_t e = block_excl_scan_1024(w, sh, &tot);
-      if (m < n_mb) wpre[m] = carry + e;
-      carry += tot;
-    }
-    if (t == 0) wpre[n_mb] = carry;
-    W = carry;
-  }
-  int32_t* xb = sh;                                 // reuses the scan buffer (9 entries)
-  __syncthreads();
-  if (t <= N_XCD) xb[t] = affine ? n_mb : (t == 0 ? 0 : n_mb);
-  __syncthreads();
-  auto xcd_of = [&](int m) {
-    const int64_t pre = wpre[m], w = (int64_t)wpre[m + 1] - wpre[m];
-    return (int)min<int64_t>(N_XCD - 1, (N_XCD * (2 * pre + w)) / max<int64_t>(1, 2 * W));
+  auto n_of = [&](int x) { return affine ? (n_mb - x + N_XCD - 1) / N_XCD : (x == 0 ? n_mb : 0); };
+  auto base_of = [&](int x) {
+    int b = 0;
+    for (int y = 0; y < x; ++y) b += n_of(y);
+    return b;
   };
-  if (affine && !overflow)
-    for (int m = t; m < n_mb; m += 1024) {
-      const int xm = xcd_of(m), xp = m > 0 ? xcd_of(m - 1) : -1;
-      for (int x = xp + 1; x <= xm; ++x) xb[x] = m;
+  auto m_of = [&](int pp) {                         // the minibatch at XCD-major position pp
+    if (!affine) return pp;
+    int x = 0, b = 0;
+    while (x < N_XCD - 1 && pp >= b + n_of(x)) b += n_of(x++);
+    return x + N_XCD * (pp - b);
+  };
+  int32_t* pg = wl_pg(wl, cap);
+  int32_t* pu = wl_pu(wl, cap);
+  int32_t* pd = wl_pd(wl, cap);
+  if (ring && !overflow) {
+    int32_t cg = 0, cu = 0, cd = 0;
+    for (int c0 = 0; c0 < n_mb; c0 += 1024) {
+      const int pp = c0 + t;
+      int32_t vg = 0, vu = 0, vd = 0;
+      if (pp < n_mb) {
+        const int m = m_of(pp);
+        vg = gs[m + 1] - gs[m];
+        vu = us[m + 1] - us[m];
+        vd = ds[m + 1] - ds[m];
+      }
+      int32_t tg, tu, td;
+      const int32_t eg = block_excl_scan_1024(vg, sh, &tg);
+      const int32_t eu = block_excl_scan_1024(vu, sh, &tu);
+      const int32_t ed = block_excl_scan_1024(vd, sh, &td);
+      if (pp < n_mb) {
+        pg[pp] = cg + eg;
+        pu[pp] = cu + eu;
+        pd[pp] = cd + ed;
+      }
+      cg += tg;
+      cu += tu;
+      cd += td;
     }
+    if (t == 0) {
+      pg[n_mb] = cg;
+      pu[n_mb] = cu;
+      pd[n_mb] = cd;
+    }
+  }
   __syncthreads();
   if (t <= N_XCD) {
-    wl[WL_XB + t] = xb[t];
-    wl[WL_XR + t] = gs[xb[t]] + us[xb[t]] + ds[xb[t]];
+    const int b = t < N_XCD ? base_of(t) : n_mb;
+    wl[WL_XB + t] = b;
+    wl[WL_XR + t] = (ring && !overflow) ? pg[b] + pu[b] + pd[b] : 0;
   }
   // Stage-ordered tables: when the shared experts' down tiles are the longer ones (K =
   // n_shared * I_shared > I), the down table lists them first, so that the longest tiles start
@@ -297,25 +318,26 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     const int32_t g = grp[m], rw = nr[m], first = r0[m];
     const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
     const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m], ng = gs[m + 1] - gs[m];
-    // this minibatch's range: [lo, hi) of S slots starting at slot s0, order lag L
-    int lo = 0, hi = n_mb, S = n_slots, s0 = 0;
+    // this minibatch: the j-th of its XCD's n_x, on S slots starting at slot s0, order lag L
+    int S = n_slots, s0 = 0, j = m, pb = 0, nx = n_mb, mstep = 1;
     if (affine) {
-      const int x = xcd_of(m);
-      lo = xb[x];
-      hi = xb[x + 1];
+      const int x = m % N_XCD;
       S = n_slots / N_XCD;
       s0 = x * S;
+      j = m / N_XCD;
+      pb = base_of(x);
+      nx = n_of(x);
+      mstep = N_XCD;
     }
     const int L = S >= 2 ? S / 2 : 0;
-    slot[m] = s0 + (m - lo) % S;
-    prev[m] = m - S >= lo ? m - S : -1;
+    slot[m] = s0 + j % S;
+    prev[m] = j >= S ? m - mstep * S : -1;
     if (ring) {
-      const int mb_lag = max(lo, m - L);
-      const int after = min(m + L + 1, hi);
-      const int32_t R0 = gs[lo] + us[lo] + ds[lo];      // items of the earlier ranges
-      const int32_t pos_g = R0 + (gs[m] - gs[lo]) + (us[m] - us[lo]) + (ds[mb_lag] - ds[lo]);
-      const int32_t pos_u = R0 + (gs[m + 1] - gs[lo]) + (us[m] - us[lo]) + (ds[mb_lag] - ds[lo]);
-      const int32_t pos_d = R0 + (gs[after] - gs[lo]) + (us[after] - us[lo]) + (ds[m] - ds[lo]);
+      // block j of the XCD's order: gather items of j, up tiles of j, down tiles of j - L
+      const int pp = pb + j, pl = pb + max(0, j - L), pa = pb + min(j + L + 1, nx);
+      const int32_t pos_g = pg[pp] + pu[pp] + pd[pl];
+      const int32_t pos_u = pg[pp + 1] + pu[pp] + pd[pl];
+      const int32_t pos_d = pg[pa] + pu[pa] + pd[pp];
       for (int l = 0; l < ng; ++l) { int4 e = e0; e.y = (KIND_G << KIND_SHIFT) | l; rt[pos_g + l] = e; }
       for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = (KIND_U << KIND_SHIFT) | l; rt[pos_u + l] = e; }
       for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = (KIND_D << KIND_SHIFT) | l; rt[pos_d + l] = e; }
@@ -1537,14 +1559,10 @@ hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const*
   const int nD = (p.d + Big::BN - 1) / Big::BN;
   const bool gather_items = p.ring && p.elem == Elem::FP8;
   const bool gather_launch = p.elem == Elem::FP8 && !p.ring;   // ends the GATHER stage
-  // XCD-split weights, in 64-element K steps: a gather item (64 rows, ~3 bytes moved per element)
-  // costs about what 3d/1024 steps of a tile do
-  const int w_up = std::max(1, p.d / 64), w_dr = std::max(1, p.I / 64);
-  const int w_ds = std::max(1, p.I_sh / 64), w_g = std::max(1, 3 * p.d / 1024);
   launch_k(k_build_worklist, dim3(1), dim3(1024), 0, s, ev_at(ev, EV_GATHER),
            gather_launch ? nullptr : ev_at(ev, EV_GATHER + 1), p.counts, p.offsets, p.E_l,
-           p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.n_slots, w_up, w_dr,
-           w_ds, w_g, p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.wl);
+           p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.n_slots, p.max_mb,
+           p.cap_u, p.cap_d, p.cap_r, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   return launch_stages_t<Elem::FP8, false>(p, s, ev);

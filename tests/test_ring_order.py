@@ -2,8 +2,8 @@
 checked on the CPU over random minibatch mixes and ring sizes:
 
   * the positions of all items form a permutation of 0..n_items-1;
-  * with the XCD split (>= 8 slots) each XCD's items are one contiguous segment, its minibatches
-    one contiguous range, its slots its own;
+  * with the XCD split (>= 8 slots) XCD x owns minibatches x, x + 8, ...: its items are one
+    contiguous segment and its slots its own;
   * every dependency of an item (down <- the minibatch's up tiles; up <- its gather items and
     the down tiles of the slot's previous user; gather <- the previous user's up tiles) comes
     earlier in the same segment, so a loop that takes items in order cannot deadlock;
@@ -16,49 +16,36 @@ import random
 N_XCD = 8
 
 
-def layout(nu, nd, ng, n_slots, w_up=1, w_dr=1, w_g=1):
+def layout(nu, nd, ng, n_slots):
     n = len(nu)
     cs = lambda a: [0] + list(itertools.accumulate(a))
-    us, ds, gs = cs(nu), cs(nd), cs(ng)
     affine = n_slots >= N_XCD
-    wpre = cs([nu[m] * w_up + nd[m] * w_dr + ng[m] * w_g for m in range(n)])
-    W = wpre[n]
-
-    def xcd_of(m):
-        pre, w = wpre[m], wpre[m + 1] - wpre[m]
-        return min(N_XCD - 1, (N_XCD * (2 * pre + w)) // max(1, 2 * W))
-
-    xb = [0] + [n] * N_XCD
-    if affine:
-        xb = [n] * (N_XCD + 1)
-        for m in range(n):
-            xm, xp = xcd_of(m), (xcd_of(m - 1) if m > 0 else -1)
-            for x in range(xp + 1, xm + 1):
-                xb[x] = m
-    xr = [gs[b] + us[b] + ds[b] for b in xb]
+    # XCD x owns minibatches x, x + 8, ... (all of them without the split), XCD-major order
+    n_of = lambda x: (n - x + N_XCD - 1) // N_XCD if affine else (n if x == 0 else 0)
+    base = cs([n_of(x) for x in range(N_XCD)])
+    order = [x + N_XCD * j for x in range(N_XCD) for j in range(n_of(x))] if affine else list(range(n))
+    pg, pu, pd = (cs([a[m] for m in order]) for a in (ng, nu, nd))
+    xb = base
+    xr = [pg[b] + pu[b] + pd[b] for b in xb]
     pos, slot, prev, owner = {}, {}, {}, {}
     for m in range(n):
-        lo, hi, S, s0 = 0, n, n_slots, 0
+        S, s0, j, pb, nx, step = n_slots, 0, m, 0, n, 1
         if affine:
-            x = xcd_of(m)
-            lo, hi, S, s0 = xb[x], xb[x + 1], n_slots // N_XCD, x * (n_slots // N_XCD)
-        owner[m] = lo
+            x = m % N_XCD
+            S, s0, j, pb, nx, step = n_slots // N_XCD, x * (n_slots // N_XCD), m // N_XCD, base[x], n_of(x), N_XCD
+        owner[m] = m % N_XCD if affine else 0
         L = S // 2 if S >= 2 else 0
-        slot[m] = s0 + (m - lo) % S
-        prev[m] = m - S if m - S >= lo else -1
-        ml, after = max(lo, m - L), min(m + L + 1, hi)
-        r0 = gs[lo] + us[lo] + ds[lo]
-        pg = r0 + (gs[m] - gs[lo]) + (us[m] - us[lo]) + (ds[ml] - ds[lo])
-        pu = r0 + (gs[m + 1] - gs[lo]) + (us[m] - us[lo]) + (ds[ml] - ds[lo])
-        pd = r0 + (gs[after] - gs[lo]) + (us[after] - us[lo]) + (ds[m] - ds[lo])
+        slot[m] = s0 + j % S
+        prev[m] = m - step * S if j >= S else -1
+        p, pl, pa = pb + j, pb + max(0, j - L), pb + min(j + L + 1, nx)
         for l in range(ng[m]):
-            pos[("G", m, l)] = pg + l
+            pos[("G", m, l)] = pg[p] + pu[p] + pd[pl] + l
         for l in range(nu[m]):
-            pos[("U", m, l)] = pu + l
+            pos[("U", m, l)] = pg[p + 1] + pu[p] + pd[pl] + l
         for l in range(nd[m]):
-            pos[("D", m, l)] = pd + l
+            pos[("D", m, l)] = pg[pa] + pu[pa] + pd[p] + l
     return dict(pos=pos, slot=slot, prev=prev, owner=owner, xb=xb, xr=xr, affine=affine,
-                total=us[n] + ds[n] + gs[n])
+                total=pg[n] + pu[n] + pd[n])
 
 
 def check(nu, nd, ng, n_slots):
@@ -66,10 +53,10 @@ def check(nu, nd, ng, n_slots):
     pos, slot, prev, owner, xb, xr = (lay[k] for k in ("pos", "slot", "prev", "owner", "xb", "xr"))
     n = len(nu)
     assert sorted(pos.values()) == list(range(lay["total"]))
-    seg = lambda m: next(x for x in range(N_XCD) if xb[x] <= m < xb[x + 1])
     for (k, m, l), p in pos.items():
         if lay["affine"]:
-            assert xr[seg(m)] <= p < xr[seg(m) + 1]
+            assert xr[m % N_XCD] <= p < xr[m % N_XCD + 1]
+            assert slot[m] // (n_slots // N_XCD) == m % N_XCD
         pm = prev[m]
         deps = []
         if k == "D":
