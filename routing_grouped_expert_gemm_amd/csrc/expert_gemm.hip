@@ -1215,7 +1215,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
 // indices are looked up once into LDS; then each lane takes 8 consecutive elements of a row per
 // item (the 4 lanes of a 32-element block are an aligned quad; consecutive lanes cover
 // consecutive 16 bytes), GQ_UNROLL items with their loads in flight together.
-constexpr int GQ_UNROLL = 4;
+// loads in flight per lane: 4 in the gather launch (8 workgroups per CU), 16 in the ring loop
+// (one workgroup per CU, whose registers are free outside the GEMM tiles)
+constexpr int GQ_UNROLL_STAGE = 4, GQ_UNROLL_RING = 16;
+template <int GQ_UNROLL>
 MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r_end, int wave,
                                   int n_waves) {
   __shared__ int64_t tok_row[G_ROWS];
@@ -1290,7 +1293,7 @@ __global__ __launch_bounds__(256) void k_gather_quantize(ExpertPass p) {
       continue;
     }
     const int32_t r1 = min(min(nr[m], r + PIECE), r + (r_hi - done));
-    gather_quantize_rows(p, m, r, r1, threadIdx.x >> 6, 4);
+    gather_quantize_rows<GQ_UNROLL_STAGE>(p, m, r, r1, threadIdx.x >> 6, 4);
     done += r1 - r;
     r = r1;
   }
@@ -1435,7 +1438,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     } else {
       if constexpr (EL == Elem::FP8) {
         const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
-        gather_quantize_rows(p, e.x, r0, r1, wid, C::NW);
+        gather_quantize_rows<GQ_UNROLL_RING>(p, e.x, r0, r1, wid, C::NW);
       }
       for (int s = 0; s < 4; ++s) {
         fetch_step(s);
