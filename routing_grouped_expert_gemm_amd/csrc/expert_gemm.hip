@@ -23,6 +23,7 @@
 //  * LDS rows are 128 B (8 chunks of 16 B) per K step, chunk c of row r stored at c ^ (r & 7)
 //    so the per-lane fragment reads and the row-wise tile writes are bank-conflict free.
 #include <algorithm>
+#include <utility>
 
 #include "device_common.h"
 #include "launch.h"
@@ -478,7 +479,8 @@ MOK_DEV void lds_barrier() {
 // each accumulator block holds the transposed product: lane (h, l32) of block (i, j) carries
 // output row 32i + l32 and output columns 32j + 8g + 4h + [0, 4) in values 4g .. 4g + 3 --
 // four consecutive columns of one row per register quad, which the epilogues store whole.
-template <Elem EL, int FM, int FN, class After>
+// MXFP8: asc / bsc hold scale words; byte SCB of each is the MFMA's E8M0 scale (op_sel).
+template <Elem EL, int FM, int FN, int SCB = 0, class After>
 MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const uint32_t* asc,
                        const uint32_t* bsc, f32x16_t (&acc)[FM][FN], After&& after) {
   if constexpr (EL == Elem::BF16) {
@@ -516,7 +518,7 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
         bv[0] = b[j][0].x; bv[1] = b[j][0].y; bv[2] = b[j][0].z; bv[3] = b[j][0].w;
         bv[4] = b[j][1].x; bv[5] = b[j][1].y; bv[6] = b[j][1].z; bv[7] = b[j][1].w;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            bv, av, acc[i][j], 0, 0, 0, (int)bsc[j], 0, (int)asc[i]);
+            bv, av, acc[i][j], 0, 0, SCB, (int)bsc[j], SCB, (int)asc[i]);
         after(i * FN + j);
       }
   }
@@ -858,9 +860,10 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   auto compute = [&](const Bufs<C>& b, int kt, auto&& after) {
     const char* a_buf = (const char*)&b.A[blk_row(0) + l32][0];
     const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
-    const int sc_shift = 8 * (((uint32_t)kt * SC_B) & 3);
     uint4 fa[2][FM][2], fb[2][FN][2];
-    uint32_t asc[2][FM], bsc[2][FN];
+    // MXFP8 (one scale word of 4 blocks per row and K step): the word shifted right by 8 h, so
+    // byte 2 s holds the lane's block 2 s + h of sub-step s; read once per step
+    uint32_t asc[FM], bsc[FN];
     auto load = [&](int s, int f) {
       const int c0 = ((frag_chunk<EL>(s, h, 0)) ^ xsw) * 16;
       const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ xsw) * 16;
@@ -868,28 +871,32 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
       for (int i = 0; i < FM; ++i) {
         fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c0);
         if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c1);
-        if (EL == Elem::FP8)
-          asc[f][i] = (b.As[blk_row(i) + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
+        if (EL == Elem::FP8 && s == 0) asc[i] = b.As[blk_row(i) + l32] >> (8 * h);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         fb[f][j][0] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c0);
         if (TR::CPL == 2) fb[f][j][1] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c1);
-        if (EL == Elem::FP8)
-          bsc[f][j] = (b.Bs[wn * WN + j * 32 + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
+        if (EL == Elem::FP8 && s == 0) bsc[j] = b.Bs[wn * WN + j * 32 + l32] >> (8 * h);
       }
     };
+    static_assert(EL != Elem::FP8 || (SUB == 2 && SC_B == 4), "one scale word per row and K step");
     load(0, 0);
-#pragma unroll
-    for (int s = 0; s < SUB; ++s) {
+    auto sub = [&](auto S_) {
+      constexpr int s = decltype(S_)::value;
       if (s + 1 < SUB) load(s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);   // the reads of s + 1 go out before the MFMAs of s
       if (s == 0) after(-1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step<EL, FM, FN>(fa[s & 1], fb[s & 1], asc[s & 1], bsc[s & 1], acc,
-                            [&](int n) { after(s * FM * FN + n); });
+      mfma_step<EL, FM, FN, 2 * s>(fa[s & 1], fb[s & 1], asc, bsc, acc,
+                                   [&](int n) { after(s * FM * FN + n); });
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    static_assert(SUB <= 4, "sub-steps unrolled below");
+    sub(std::integral_constant<int, 0>{});
+    if constexpr (SUB > 1) sub(std::integral_constant<int, 1>{});
+    if constexpr (SUB > 2) sub(std::integral_constant<int, 2>{});
+    if constexpr (SUB > 3) sub(std::integral_constant<int, 3>{});
   };
 
   if constexpr (EARLY_X) {
