@@ -864,32 +864,50 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     // MXFP8 (one scale word of 4 blocks per row and K step): the word shifted right by 8 h, so
     // byte 2 s holds the lane's block 2 s + h of sub-step s; read once per step
     uint32_t asc[FM], bsc[FN];
+    // Reads in the order the MFMAs (row-block major) first use them: scale words, A block 0,
+    // the B blocks, the other A blocks. The LDS counter tracks at most 15 reads, so a read
+    // that an MFMA waits for must be among the first of those in flight.
     auto load = [&](int s, int f) {
       const int c0 = ((frag_chunk<EL>(s, h, 0)) ^ xsw) * 16;
       const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ xsw) * 16;
+      if (EL == Elem::FP8 && s == 0) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+        for (int i = 0; i < FM; ++i) asc[i] = b.As[blk_row(i) + l32] >> (8 * h);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bsc[j] = b.Bs[wn * WN + j * 32 + l32] >> (8 * h);
+      }
+      auto ra = [&](int i) {
         fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c0);
         if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c1);
-        if (EL == Elem::FP8 && s == 0) asc[i] = b.As[blk_row(i) + l32] >> (8 * h);
-      }
+      };
+      ra(0);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         fb[f][j][0] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c0);
         if (TR::CPL == 2) fb[f][j][1] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c1);
-        if (EL == Elem::FP8 && s == 0) bsc[j] = b.Bs[wn * WN + j * 32 + l32] >> (8 * h);
       }
+#pragma unroll
+      for (int i = 1; i < FM; ++i) ra(i);
     };
     static_assert(EL != Elem::FP8 || (SUB == 2 && SC_B == 4), "one scale word per row and K step");
     load(0, 0);
+    // The reads of sub-step s + 1 go out after the first NEXT_AT MFMAs of s: issued before
+    // them, they would sit ahead of s's own reads in the LDS counter, and the first MFMA would
+    // wait for most of both sub-steps' reads (scheduling barriers pin the order).
+    constexpr int NEXT_AT = 4;
     auto sub = [&](auto S_) {
       constexpr int s = decltype(S_)::value;
-      if (s + 1 < SUB) load(s + 1, (s + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);   // the reads of s + 1 go out before the MFMAs of s
+      __builtin_amdgcn_sched_barrier(0);
       if (s == 0) after(-1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step<EL, FM, FN, 2 * s>(fa[s & 1], fb[s & 1], asc, bsc, acc,
-                                   [&](int n) { after(s * FM * FN + n); });
+      mfma_step<EL, FM, FN, 2 * s>(fa[s & 1], fb[s & 1], asc, bsc, acc, [&](int n) {
+        if (s + 1 < SUB && n == NEXT_AT - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          load(s + 1, (s + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        after(s * FM * FN + n);
+      });
       __builtin_amdgcn_sched_barrier(0);
     };
     static_assert(SUB <= 4, "sub-steps unrolled below");
