@@ -894,7 +894,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     // The reads of sub-step s + 1 go out after the first NEXT_AT MFMAs of s: issued before
     // them, they would sit ahead of s's own reads in the LDS counter, and the first MFMA would
     // wait for most of both sub-steps' reads (scheduling barriers pin the order).
-    constexpr int NEXT_AT = 4;
+    constexpr int NEXT_AT = 8;
     auto sub = [&](auto S_) {
       constexpr int s = decltype(S_)::value;
       __builtin_amdgcn_sched_barrier(0);
