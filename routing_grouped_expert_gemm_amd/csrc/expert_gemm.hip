@@ -1100,7 +1100,11 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
             bf16_t* dst;
             if (UP) dst = (bf16_t*)p.H + (ring_row0 + m0 + r) * p.Hld;
             else dst = (shared ? (bf16_t*)p.y_shared : (bf16_t*)p.y_slots) + (int64_t)sm.row_dst[r] * p.d;
-            *(u32x4*)(dst + col0 + c) = val;
+            // H rows (read again only by the down stage) stream past the L2 so they do not
+            // evict the operand tiles other workgroups of the XCD are reading; route-slot and
+            // shared rows stay cached for the combine
+            if constexpr (UP) __builtin_nontemporal_store(val, (u32x4*)(dst + col0 + c));
+            else *(u32x4*)(dst + col0 + c) = val;
           }
         }
       }
