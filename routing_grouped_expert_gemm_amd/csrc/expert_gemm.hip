@@ -1089,7 +1089,10 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
           const uint2 codes = quantize_quad8_f32(vals, &se);
           if (r < rows_valid && col0 + c < N) {
             const int64_t hr = ring_row0 + m0 + r;
-            *(uint2*)((uint8_t*)p.H + hr * p.Hld + col0 + c) = codes;
+            u32x2 cv;                                    // streamed past the L2, as bf16 H
+            cv.x = codes.x;
+            cv.y = codes.y;
+            __builtin_nontemporal_store(cv, (u32x2*)((uint8_t*)p.H + hr * p.Hld + col0 + c));
             if ((c & 31) == 0)
               p.H_sc[mx_kmajor_scale(hr, (col0 + c) / 32, (int64_t)p.n_slots * p.mb)] =
                   (uint8_t)(se + 127);
