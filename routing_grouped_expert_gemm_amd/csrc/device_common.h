@@ -193,6 +193,36 @@ MOK_DEV uint2 quantize_quad8(const uint4 raw, int* s_out) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+// The same rules for sixteen bf16 values per lane, the 2 lanes of an aligned pair holding one
+// 32-element block (the even lane the first half): the 16 codes, and the block's exponent.
+MOK_DEV uint4 quantize_pair16(const uint4 raw0, const uint4 raw1, int* s_out) {
+  const uint32_t w[8] = {raw0.x, raw0.y, raw0.z, raw0.w, raw1.x, raw1.y, raw1.z, raw1.w};
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  const int s = mx_shared_exp(amax);
+  uint32_t c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      y[r] = fminf(fmaxf(__builtin_amdgcn_ldexpf(v[4 * q + r], -s), -448.0f), 448.0f);
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+    c[q] = (uint32_t)word;
+  }
+  *s_out = s;
+  return make_uint4(c[0], c[1], c[2], c[3]);
+}
+
 // quantize_quad8 for eight float32 values already in registers (same rules).
 MOK_DEV uint2 quantize_quad8_f32(const float (&v)[8], int* s_out) {
   float amax = 0.0f;

@@ -1244,12 +1244,13 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
 // Pull-gather + quantise of rows [r_begin, r_end) (at most G_ROWS) of minibatch m: the token
 // rows of the pool picked by route id (or the own rows, for the shared experts) become MXFP8
 // rows of the minibatch's ring slot. Called by every thread of the workgroup. The rows' token
-// indices are looked up once into LDS; then each lane takes 8 consecutive elements of a row per
-// item (the 4 lanes of a 32-element block are an aligned quad; consecutive lanes cover
-// consecutive 16 bytes), GQ_UNROLL items with their loads in flight together.
-// loads in flight per lane: 4 in the gather launch (8 workgroups per CU), 16 in the ring loop
+// indices are looked up once into LDS; then a wave quantises one 128-element K step of 8 rows
+// per item, 8 lanes a row and 16 consecutive elements a lane (the 2 lanes of a 32-element block
+// are an aligned pair), GQ_UNROLL items with their loads in flight together. Its scale bytes
+// (K-step-major words of consecutive ring rows) are then contiguous.
+// items in flight per lane: 2 in the gather launch (8 workgroups per CU), 8 in the ring loop
 // (one workgroup per CU, whose registers are free outside the GEMM tiles)
-constexpr int GQ_UNROLL_STAGE = 4, GQ_UNROLL_RING = 16;
+constexpr int GQ_UNROLL_STAGE = 2, GQ_UNROLL_RING = 8;
 template <int GQ_UNROLL>
 MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r_end, int wave,
                                   int n_waves) {
@@ -1264,37 +1265,37 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
     tok_row[t] = (g >= p.E_l ? p.own_begin + first + r : (int64_t)(p.route_ids[first + r] / p.k)) * p.d;
   }
   __syncthreads();
-  // A wave quantises one 128-element K step of 4 consecutive rows (16 lanes a row), so its
-  // scale bytes (K-step-major words of consecutive ring rows) are contiguous.
   const int steps = p.d / 128;
-  const int total = (rows + 3) / 4 * steps * 64;
+  const int total = (rows + 7) / 8 * steps * 64;
   const int nt = 64 * n_waves;
   const int64_t ring0 = (int64_t)wl_slot(p.wl, cap)[m] * p.mb + r_begin;
   const int64_t R = (int64_t)p.n_slots * p.mb;
   const int n_iter = (total + GQ_UNROLL * nt - 1) / (GQ_UNROLL * nt);   // same for every lane
   for (int it = 0; it < n_iter; ++it) {
-    uint4 raw[GQ_UNROLL];
+    uint4 raw[GQ_UNROLL][2];
     int rr[GQ_UNROLL], cc[GQ_UNROLL];
 #pragma unroll
     for (int u = 0; u < GQ_UNROLL; ++u) {
       const int q = t + (it * GQ_UNROLL + u) * nt;
-      const uint32_t unit = (uint32_t)q >> 6;
+      const uint32_t unit = (uint32_t)q >> 6;       // 8 rows x one K step
       const int li = q & 63, rg = (int)(unit / (uint32_t)steps), j = (int)unit - rg * steps;
-      const int r = rg * 4 + (li >> 4);
+      const int r = rg * 8 + (li >> 3);
       const bool ok = q < total && r < rows;
       rr[u] = ok ? r : 0;
-      cc[u] = ok ? j * 16 + (li & 15) : -1;
-      raw[u] = ok ? *(const uint4*)((const bf16_t*)p.x + tok_row[rr[u]] + 8 * cc[u])
-                  : make_uint4(0, 0, 0, 0);
+      cc[u] = ok ? j * 8 + (li & 7) : -1;            // 16-element chunk of the row
+      const bf16_t* src = (const bf16_t*)p.x + tok_row[rr[u]] + 16 * max(cc[u], 0);
+      raw[u][0] = ok ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
+      raw[u][1] = ok ? *(const uint4*)(src + 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < GQ_UNROLL; ++u) {
       int sh;
-      const uint2 codes = quantize_quad8(raw[u], &sh);   // all 4 lanes of a quad share cc's validity
+      // both lanes of a pair share cc's validity
+      const uint4 codes = quantize_pair16(raw[u][0], raw[u][1], &sh);
       if (cc[u] >= 0) {
         const int64_t hr = ring0 + rr[u];
-        *(uint2*)(p.A_codes + hr * p.d + 8 * cc[u]) = codes;
-        if ((cc[u] & 3) == 0) p.A_sc[mx_kmajor_scale(hr, cc[u] / 4, R)] = (uint8_t)(sh + 127);
+        *(uint4*)(p.A_codes + hr * p.d + 16 * cc[u]) = codes;
+        if ((cc[u] & 1) == 0) p.A_sc[mx_kmajor_scale(hr, cc[u] / 2, R)] = (uint8_t)(sh + 127);
       }
     }
   }

@@ -10,49 +10,55 @@
 
 namespace mok {
 
-// KMAJOR: a wave quantises one 128-element K step of 4 consecutive rows (16 lanes a row), so
-// its 16 scale bytes -- 4 K-step-major words of consecutive rows -- are contiguous too.
+// Row-major scales (the mok_quantize_mxfp8 layout): four lanes per 32-element block, 8
+// elements a lane. K-step-major scales (the GEMMs' operands): a wave quantises one 128-element
+// K step of 8 consecutive rows, 8 lanes a row and 16 elements a lane (two lanes a block), so
+// its 32 scale bytes -- 8 K-step-major words of consecutive rows -- are contiguous, and each
+// lane reads 32 and writes 16 bytes.
 template <bool KMAJOR>
 __global__ __launch_bounds__(256) void k_quantize_mxfp8(const bf16_t* __restrict__ src,
                                                         int64_t rows, int K, int64_t R,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales) {
-  const int64_t n_chunks = KMAJOR ? (rows + 3) / 4 * (K / 128) * 64 : rows * (K / 8);
+  const int64_t n_chunks = KMAJOR ? (rows + 7) / 8 * (K / 128) * 64 : rows * (K / 8);
   const int64_t stride = (int64_t)gridDim.x * 256;
-  // every lane of a wave runs the same number of iterations (the quad shuffles need the whole
-  // quad): lanes past the end load and store nothing
+  // every lane of a wave runs the same number of iterations (the quad / pair shuffles need the
+  // whole group): lanes past the end load and store nothing
   const int64_t n_iter = (n_chunks + stride - 1) / stride;
   int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   for (int64_t it = 0; it < n_iter; ++it, q += stride) {
-    int64_t at;                                   // first element of the lane's 8
-    bool ok;
-    int64_t row = 0;
-    int c8 = 0;
     if constexpr (KMAJOR) {
-      const uint32_t unit = (uint32_t)(q >> 6);   // 4 rows x one K step (< 2^31 units)
+      const uint32_t unit = (uint32_t)(q >> 6);   // 8 rows x one K step (< 2^31 units)
       const uint32_t steps = (uint32_t)K / 128, li = (uint32_t)q & 63;
       const uint32_t rg = unit / steps;
       const int j = (int)(unit - rg * steps);
-      row = (int64_t)rg * 4 + (li >> 4);
-      c8 = j * 16 + (li & 15);
-      ok = q < n_chunks && row < rows;
-      at = row * K + 8 * c8;
-    } else {
-      ok = q < n_chunks;
-      at = q * 8;
-    }
-    const uint4 raw = ok ? *(const uint4*)(src + at) : make_uint4(0, 0, 0, 0);
-    int sh;
-    const uint2 c = quantize_quad8(raw, &sh);
-    if (ok) {
-      *(uint2*)(codes + at) = c;
-      if (((at >> 3) & 3) == 0) {
-        int64_t sa = at >> 5;
-        if constexpr (KMAJOR) {
+      const int64_t row = (int64_t)rg * 8 + (li >> 3);
+      const int c16 = j * 8 + (int)(li & 7);      // the lane's 16-element chunk of the row
+      const bool ok = q < n_chunks && row < rows;
+      const int64_t at = row * K + 16 * c16;
+      uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
+      if (ok) {
+        r0 = *(const uint4*)(src + at);
+        r1 = *(const uint4*)(src + at + 8);
+      }
+      int sh;
+      const uint4 c = quantize_pair16(r0, r1, &sh);
+      if (ok) {
+        *(uint4*)(codes + at) = c;
+        if ((c16 & 1) == 0) {
           const int64_t g = (uint32_t)row / (uint32_t)R;   // matrix g, its row row - g R
-          sa = g * R * (K / 32) + mx_kmajor_scale(row - g * R, c8 >> 2, R);
+          scales[g * R * (K / 32) + mx_kmajor_scale(row - g * R, c16 >> 1, R)] = (uint8_t)(sh + 127);
         }
-        scales[sa] = (uint8_t)(sh + 127);
+      }
+    } else {
+      const bool ok = q < n_chunks;
+      const int64_t at = q * 8;
+      const uint4 raw = ok ? *(const uint4*)(src + at) : make_uint4(0, 0, 0, 0);
+      int sh;
+      const uint2 c = quantize_quad8(raw, &sh);
+      if (ok) {
+        *(uint2*)(codes + at) = c;
+        if ((q & 3) == 0) scales[at >> 5] = (uint8_t)(sh + 127);
       }
     }
   }
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8(const bf16_t* __restrict
 hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
                                  int64_t scales_kmajor) {
-  const int64_t n_chunks = scales_kmajor > 0 ? (rows + 3) / 4 * (K / 128) * 64 : rows * (K / 8);
+  const int64_t n_chunks = scales_kmajor > 0 ? (rows + 7) / 8 * (K / 128) * 64 : rows * (K / 8);
   if (n_chunks == 0) return mark_empty(s, e0, e1), hipSuccess;
   if (scales_kmajor > 0 && (rows >= INT32_MAX || n_chunks / 64 >= INT32_MAX))
     return hipErrorInvalidValue;                  // the K-major index math is 32-bit
