@@ -70,14 +70,17 @@ __global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ 
     const int e = e_base + t / P;
     const bool active = e < E_l;
     int32_t local = 0;
-    if (active)
+    if (active) {
+#pragma unroll 4
       for (int b = b0; b < b1; ++b) local += blk_counts[(int64_t)b * E_l + e];
+    }
     int32_t tot;
     const int32_t excl = block_excl_scan_1024(local, sh, &tot);
     if (g == 0) gbase[t / P] = excl;
     __syncthreads();
     if (active) {
       int32_t run = excl - gbase[t / P];
+#pragma unroll 4
       for (int b = b0; b < b1; ++b) {
         blk_base[(int64_t)b * E_l + e] = run;
         run += blk_counts[(int64_t)b * E_l + e];
