@@ -33,8 +33,8 @@ namespace mok {
 // ------------------------------------------------------------------------- work list
 // int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, the
 // prefix sums of its gather, up and down items, three completion counters, its ring slot, the
-// minibatch that used that slot before it (-1: none), an unused word, the prefix of its rows,
-// and (ring) the item prefix sums in XCD-major order; then, 16-byte aligned, one int4 per
+// minibatch that used that slot before it (-1: none), the prefix of its rows, and (ring) the
+// item prefix sums in XCD-major order; then, 16-byte aligned, one int4 per
 // up tile and per down tile {minibatch, tile within it, first row, group << 16 | rows} so that a
 // workgroup finds its tile with a single load, and (ring work loop only) the ring order of all
 // items, the item kind in bits 28+ of the second field.
@@ -59,12 +59,12 @@ MOK_DEV int32_t* wl_gstart(int32_t* wl, int cap) { return wl + WL_HDR + 5 * cap 
 MOK_DEV int32_t* wl_done(int32_t* wl, int cap, int kind) { return wl + WL_HDR + (6 + kind) * cap + 3; }
 MOK_DEV int32_t* wl_slot(int32_t* wl, int cap) { return wl + WL_HDR + 9 * cap + 3; }
 MOK_DEV int32_t* wl_prev(int32_t* wl, int cap) { return wl + WL_HDR + 10 * cap + 3; }
-MOK_DEV int32_t* wl_rpre(int32_t* wl, int cap) { return wl + WL_HDR + 12 * cap + 4; }   // cap + 1
+MOK_DEV int32_t* wl_rpre(int32_t* wl, int cap) { return wl + WL_HDR + 11 * cap + 3; }   // cap + 1
 // ring order: prefix sums of gather, up and down items over the minibatches in XCD-major order
-MOK_DEV int32_t* wl_pg(int32_t* wl, int cap) { return wl + WL_HDR + 13 * cap + 5; }     // cap + 1
-MOK_DEV int32_t* wl_pu(int32_t* wl, int cap) { return wl + WL_HDR + 14 * cap + 6; }     // cap + 1
-MOK_DEV int32_t* wl_pd(int32_t* wl, int cap) { return wl + WL_HDR + 15 * cap + 7; }     // cap + 1
-MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 16 * (size_t)cap + 8 + 3) & ~(size_t)3; }
+MOK_DEV int32_t* wl_pg(int32_t* wl, int cap) { return wl + WL_HDR + 12 * cap + 4; }     // cap + 1
+MOK_DEV int32_t* wl_pu(int32_t* wl, int cap) { return wl + WL_HDR + 13 * cap + 5; }     // cap + 1
+MOK_DEV int32_t* wl_pd(int32_t* wl, int cap) { return wl + WL_HDR + 14 * cap + 6; }     // cap + 1
+MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 15 * (size_t)cap + 7 + 3) & ~(size_t)3; }
 MOK_DEV int4* wl_utab(int32_t* wl, int cap) { return (int4*)(wl + wl_tab_off(cap)); }
 MOK_DEV int4* wl_dtab(int32_t* wl, int cap, int cap_u) { return (int4*)(wl + wl_tab_off(cap)) + cap_u; }
 MOK_DEV int4* wl_rtab(int32_t* wl, int cap, int cap_u, int cap_d) {
