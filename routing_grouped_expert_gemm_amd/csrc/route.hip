@@ -180,7 +180,6 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   for (int q = 0; q < NQ; ++q)
     if (!(lane + 64 * q < E)) taken |= 1u << q;
   float val0 = 0.0f;
-  double wsum = 0.0;
   float my_val = 0.0f;
   int my_idx = 0;
   for (int j = 0; j < k; ++j) {
@@ -200,12 +199,15 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     const float v = float_from_order_key((uint32_t)(best >> 32));
     if ((e & 63) == lane) taken |= 1u << (e >> 6);
     if (j == 0) val0 = v;
-    wsum += exp((double)v - (double)val0);
     if (lane == j) { my_val = v; my_idx = e; }
   }
+  // lane j < k computes exp(l_j - l_0) once; the sum runs over j ascending, in double
+  const double ej = lane < k ? exp((double)my_val - (double)val0) : 0.0;
+  double wsum = 0.0;
+  for (int j = 0; j < k; ++j) wsum += __shfl(ej, j, kWave);
   if (lane < k) {
     topk_idx[t * k + lane] = my_idx;
-    topk_w[t * k + lane] = (float)(exp((double)my_val - (double)val0) / wsum);
+    topk_w[t * k + lane] = (float)(ej / wsum);
   }
 }
 
