@@ -97,7 +97,10 @@ int mok_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk
  *               source index). Entries at and beyond offsets[E_l] are left untouched.
  * Deterministic: integer counting, scans and a stable scatter; no order-dependent atomics.
  * Requires T_pool % tokens_per_rank == 0, 0 <= e0, 1 <= E_l, e0 + E_l <= E, 1 <= k <= E,
- * E_l <= 1024. topk_idx entries outside [0, E) are ignored (never local).
+ * E_l <= 1024. topk_idx entries outside [0, E) are ignored (never local). A token's k ids are
+ * expected to be distinct, as top-k output is; if a token names a local expert twice, counts
+ * and offsets still count every route, route_ids keeps only the entries below its capacity
+ * (nothing is written past it), and offsets[E_l] > T_pool * min(k, E_l) flags the case.
  * ws: device scratch of at least mok_dispatch_plan_workspace_bytes(...) bytes. */
 int mok_dispatch_plan_workspace_bytes(int64_t T_pool, int32_t k, int32_t E_l, size_t* bytes);
 int mok_dispatch_plan(const int32_t* topk_idx, int64_t T_pool, int32_t k, int32_t E, int32_t e0,
@@ -108,17 +111,17 @@ int mok_dispatch_plan(const int32_t* topk_idx, int64_t T_pool, int32_t k, int32_
 /* ---------------------------------------------------------------- stages 1-5: the layer */
 typedef struct mok_moe_args {
   int32_t dtype;           /* mok_dtype                                                     */
-  int32_t d;               /* model dim (multiple of 64; FP32: multiple of 32)              */
+  int32_t d;               /* model dim (multiple of 128)                                   */
   int32_t E;               /* routed experts in the layer                                   */
   int32_t k;               /* top-k                                                         */
-  int32_t I;               /* routed expert intermediate (multiple of 64)                   */
+  int32_t I;               /* routed expert intermediate (multiple of 64; MXFP8: of 128)    */
   int32_t e0, E_l;         /* local experts [e0, e0+E_l)                                    */
   int32_t tokens_per_rank; /* pool rows per source rank (T_pool % tokens_per_rank == 0)     */
   int64_t T_pool;          /* rows of the token pool x                                      */
   int64_t own_begin;       /* first pool row of this rank's own tokens                      */
   int32_t T_own;           /* own tokens (rows of the shared experts)                       */
   int32_t n_shared;        /* shared experts (0 allowed)                                    */
-  int32_t I_shared;        /* shared expert intermediate (multiple of 64)                   */
+  int32_t I_shared;        /* shared expert intermediate (as I)                             */
   int32_t minibatch_rows;  /* rows per minibatch of the work loop: 128, 256, 512 or 1024    */
   int32_t ring_rows;       /* capacity of the macrobatch ring, multiple of minibatch_rows   */
   uint32_t flags;          /* MOK_FLAG_* below; 0 = defaults                                */
@@ -150,7 +153,10 @@ typedef struct mok_moe_args {
   int32_t* counts_out;     /* [E_l]                                                         */
   int32_t* offsets_out;    /* [E_l + 1]                                                     */
   int32_t* rank_counts_out;/* [E_l * R]                                                     */
-  int32_t* route_ids_out;  /* [T_pool * min(k, E_l)]                                        */
+  int32_t* route_ids_out;  /* [T_pool * min(k, E_l)]. If the given routing repeats a local
+                              expert within a token so that the local routes exceed this,
+                              the forward computes nothing past the plan and sets the device
+                              error word (MOK_DEVERR_OVERFLOW)                              */
   /* optional measurement hook (host array, may be NULL): 2 * MOK_N_STAGES hipEvent_t created
      by the caller with timing enabled. Event 2s takes the time stage s's first kernel starts
      and event 2s+1 the time its last kernel ends: they are attached to those kernels' own
@@ -180,13 +186,59 @@ typedef struct mok_moe_args {
 int mok_moe_workspace_bytes(const mok_moe_args* args, size_t* bytes);
 int mok_moe_forward(const mok_moe_args* args, void* stream);
 
+/* ---------------------------------------------------------------- workspace regions
+ * Where a forward keeps an intermediate inside its workspace, so that a caller can read it
+ * back after the forward (parity checks, debugging). Pure host call: validates `args` like
+ * mok_moe_workspace_bytes and returns, for region `region`, the byte offset into the
+ * workspace, its size in bytes and `rows` (below). MOK_EINVAL if the region does not exist
+ * for this configuration (e.g. an MXFP8 region of a BF16 forward).
+ *
+ * MXFP8 codes are E4M3 bytes, row-major [rows, K] like the bf16 source. MXFP8 scales are E8M0
+ * bytes kept "K-step major": a source of `rows` rows splits into matrices of R rows (R is
+ * returned in *rows); in matrix g the scale of (row r, 32-element block b) sits at byte
+ *     g * R * (K / 32) + ((b / 4) * R + r) * 4 + (b % 4)
+ * so the 4 scales of 128-element K step b/4 of consecutive rows are contiguous.
+ *   region                  K      source rows          R
+ *   MOK_REGION_WG/WU/WD_*   d/d/I  E_l*I, E_l*I, E_l*d  I, I, d      (routed gate, up, down)
+ *   MOK_REGION_SG/SU/SD_*   d/d/Is n_s*Is (gate, up)    n_s*Is       (shared: the experts
+ *                                  n_s*d (down)         d             concatenated along I)
+ *   MOK_REGION_A_*          d      ring rows            ring rows    (gathered x rows)
+ *   MOK_REGION_H_*          Hld    ring rows            ring rows    (hidden activations)
+ * Ring rows = n_slots * minibatch_rows, Hld = max(I, n_shared * I_shared); with
+ * MOK_FLAG_NO_RING every minibatch keeps its own slot (the m-th minibatch -- routed experts
+ * ascending, each region cut into minibatch_rows pieces, then the own tokens -- uses ring
+ * rows [m * minibatch_rows, ...)). MOK_REGION_H of a BF16 / FP32 forward holds H itself
+ * ([ring rows, Hld] bf16 / float32). MOK_REGION_WORKLIST is the device work list (int32;
+ * layout internal), whose word 4 is the device error word. */
+#define MOK_REGION_WORKLIST 0
+#define MOK_REGION_H 1
+#define MOK_REGION_H_SCALES 2
+#define MOK_REGION_A_CODES 3
+#define MOK_REGION_A_SCALES 4
+#define MOK_REGION_WG_CODES 5
+#define MOK_REGION_WG_SCALES 6
+#define MOK_REGION_WU_CODES 7
+#define MOK_REGION_WU_SCALES 8
+#define MOK_REGION_WD_CODES 9
+#define MOK_REGION_WD_SCALES 10
+#define MOK_REGION_SG_CODES 11
+#define MOK_REGION_SG_SCALES 12
+#define MOK_REGION_SU_CODES 13
+#define MOK_REGION_SU_SCALES 14
+#define MOK_REGION_SD_CODES 15
+#define MOK_REGION_SD_SCALES 16
+#define MOK_N_REGIONS 17
+int mok_moe_workspace_region(const mok_moe_args* args, int32_t region, size_t* offset,
+                             size_t* bytes, int64_t* rows);
+
 /* ---------------------------------------------------------------- MXFP8 quantiser
  * OCP MX v1.0 MXFP8 along rows: src [rows, K] bf16 (device), K % 32 == 0.
  *   codes  [rows, K]      E4M3 ("FN": bias 7, max 448, no infinities) bytes
  *   scales [rows, K / 32] E8M0 bytes (2^(byte-127))
  * Per block of 32: s = floor(log2(amax)) - 8 clamped to [-127, 127] (amax == 0 -> -127);
  * element = round-to-nearest-even(|v| * 2^-s) on the E4M3 grid, saturated to 448, sign kept.
- * The layer's MXFP8 path quantises its operands with this same device code. */
+ * The forward's own MXFP8 quantisers apply the same rules with other device code (K-step-
+ * major scales, the row gather fused in); mok_moe_workspace_region exposes what they wrote. */
 int mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int32_t K, uint8_t* codes,
                        uint8_t* scales, void* stream);
 
@@ -194,7 +246,11 @@ int mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int32_t K, uint8_t* c
  * The persistent work loop bounds every wait; a wait that runs out sets a nonzero error word
  * in the workspace and the loop exits. This SYNCHRONOUS call waits for `stream`, then reads
  * the word (0 = no error) of a workspace last used by mok_moe_forward. Opt-in: the forward
- * itself never synchronises. */
+ * itself never synchronises. Bits: */
+#define MOK_DEVERR_OVERFLOW 1u  /* the plan did not fit the work list / route_ids capacity
+                                   (only possible with given routing that repeats an expert
+                                   within a token): no expert tile ran                       */
+#define MOK_DEVERR_WAIT 2u      /* a bounded wait of the ring work loop ran out              */
 int mok_get_device_error(const void* workspace, uint32_t* err, void* stream);
 
 #ifdef __cplusplus

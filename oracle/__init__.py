@@ -222,7 +222,10 @@ def moe_forward(wl, x, w_router=None, logits=None, wg=None, wu=None, wd=None, sg
     xf = _f32(x)
     P = route_outputs(rids, xf[rids // wl.k], idx, w, wl.e0, wg, wu, wd, mx)
     own = xf[wl.own_begin:wl.own_begin + wl.T_own]
-    S = shared_ffn(_operand(own, mx), _operand(sg, mx), _operand(su, mx), _operand(sd, mx), mx)
+    if wl.n_shared:
+        S = shared_ffn(_operand(own, mx), _operand(sg, mx), _operand(su, mx), _operand(sd, mx), mx)
+    else:                        # no shared expert: the sum over shared experts is empty
+        S = np.zeros((wl.T_own, wl.d), np.float64)
     y = None
     if wl.full_layer:
         assert wl.own_begin == 0 and wl.T_own == wl.T_pool

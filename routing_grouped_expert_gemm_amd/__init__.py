@@ -14,8 +14,7 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# MOK_LIBRARY: path of another build of libmok.so to load instead of the in-tree one
-LIB_PATH = os.environ.get("MOK_LIBRARY") or os.path.join(_PKG, "libmok.so")
+LIB_PATH = os.path.join(_PKG, "libmok.so")   # always the in-tree build
 
 MOK_OK, MOK_EINVAL, MOK_EUNSUPPORTED, MOK_EWORKSPACE, MOK_EHIP = range(5)
 MOK_FP32, MOK_BF16, MOK_MXFP8 = 0, 1, 2
@@ -23,10 +22,16 @@ MOK_FLAG_NO_RING = 1
 (MOK_STAGE_ROUTE, MOK_STAGE_PLAN, MOK_STAGE_QUANT, MOK_STAGE_UP, MOK_STAGE_DOWN, MOK_STAGE_COMBINE,
  MOK_STAGE_GATHER) = range(7)
 MOK_N_STAGES = 7
+(MOK_REGION_WORKLIST, MOK_REGION_H, MOK_REGION_H_SCALES, MOK_REGION_A_CODES, MOK_REGION_A_SCALES,
+ MOK_REGION_WG_CODES, MOK_REGION_WG_SCALES, MOK_REGION_WU_CODES, MOK_REGION_WU_SCALES,
+ MOK_REGION_WD_CODES, MOK_REGION_WD_SCALES, MOK_REGION_SG_CODES, MOK_REGION_SG_SCALES,
+ MOK_REGION_SU_CODES, MOK_REGION_SU_SCALES, MOK_REGION_SD_CODES, MOK_REGION_SD_SCALES) = range(17)
+MOK_DEVERR_OVERFLOW, MOK_DEVERR_WAIT = 1, 2
 
 EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
            "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_moe_workspace_bytes",
-           "mok_moe_forward", "mok_quantize_mxfp8", "mok_get_device_error"]
+           "mok_moe_forward", "mok_moe_workspace_region", "mok_quantize_mxfp8",
+           "mok_get_device_error"]
 
 
 class MokError(RuntimeError):
@@ -73,6 +78,8 @@ _lib.mok_dispatch_plan.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _
                                    _SZ, _P]
 _lib.mok_moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeArgs), ctypes.POINTER(_SZ)]
 _lib.mok_moe_forward.argtypes = [ctypes.POINTER(MoeArgs), _P]
+_lib.mok_moe_workspace_region.argtypes = [ctypes.POINTER(MoeArgs), _I32, ctypes.POINTER(_SZ),
+                                          ctypes.POINTER(_SZ), ctypes.POINTER(_I64)]
 _lib.mok_quantize_mxfp8.argtypes = [_P, _I64, _I32, _P, _P, _P]
 _lib.mok_get_device_error.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), _P]
 for _n in EXPORTS:
@@ -149,6 +156,15 @@ def mok_moe_forward(args: MoeArgs, stream=None) -> None:
     _check("mok_moe_forward", _lib.mok_moe_forward(ctypes.byref(args), _stream(stream)))
 
 
+def mok_moe_workspace_region(args: MoeArgs, region: int):
+    """(byte offset, bytes, rows R) of an intermediate inside the forward's workspace."""
+    off, n, rows = _SZ(0), _SZ(0), _I64(0)
+    _check("mok_moe_workspace_region",
+           _lib.mok_moe_workspace_region(ctypes.byref(args), region, ctypes.byref(off),
+                                         ctypes.byref(n), ctypes.byref(rows)))
+    return off.value, n.value, rows.value
+
+
 def mok_quantize_mxfp8(src_bf16, codes, scales, stream=None) -> None:
     rows, K = src_bf16.shape
     _check("mok_quantize_mxfp8", _lib.mok_quantize_mxfp8(_ptr(src_bf16), rows, K, _ptr(codes),
@@ -192,9 +208,12 @@ class MoeLayer:
         a.w_gate, a.w_up, a.w_down = _ptr(w_gate), _ptr(w_up), _ptr(w_down)
         a.ws_gate, a.ws_up, a.ws_down = _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down)
         self.y_slots = torch.empty((T_pool * k, d), dtype=odt, device=device)
-        self.y_shared = torch.empty((T_own, d), dtype=odt, device=device) if n_shared else None
+        # at least one row, so that a share with no own tokens still passes a valid pointer
+        ysh = torch.empty((max(1, T_own), d), dtype=odt, device=device) if n_shared else None
+        self.y_shared = ysh[:T_own] if n_shared else None
         self.y = torch.empty((T_pool, d), dtype=odt, device=device) if E_l == E else None
-        a.y_slots, a.y_shared, a.y = _ptr(self.y_slots), _ptr(self.y_shared), _ptr(self.y)
+        a.y_slots, a.y_shared, a.y = _ptr(self.y_slots), _ptr(ysh), _ptr(self.y)
+        self._keep.append(ysh)
         self.inter = {}
         if keep_intermediates:
             i32 = dict(dtype=torch.int32, device=device)
@@ -223,3 +242,9 @@ class MoeLayer:
 
     def device_error(self, stream=None) -> int:
         return mok_get_device_error(self.workspace, stream)
+
+    def region(self, region: int):
+        """(uint8 view of the workspace bytes of an intermediate, rows R); see
+        mok_moe_workspace_region. Read it after the forward has finished."""
+        off, n, rows = mok_moe_workspace_region(self.args, region)
+        return self.workspace[off:off + n], rows

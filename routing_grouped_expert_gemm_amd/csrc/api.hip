@@ -34,6 +34,7 @@ int device_cus() {
 // can be found from the workspace pointer alone.
 struct Layout {
   bool use_ring = false;
+  int64_t route_cap = 1;   // rows of route_ids
   int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0, cap_g = 0, cap_r = 0;
   size_t wl = 0, logits = 0, idx = 0, w = 0, counts = 0, offsets = 0, rank_counts = 0,
          route_ids = 0, blk_counts = 0, blk_base = 0, H = 0, H_sc = 0, A_codes = 0, A_sc = 0,
@@ -90,6 +91,7 @@ Layout layout_moe(const mok_moe_args* a) {
   Layout L;
   const int mb = a->minibatch_rows;
   const int64_t n_cap = a->T_pool * (int64_t)std::min(a->k, a->E_l);
+  L.route_cap = std::max<int64_t>(1, n_cap);
   const int I_sh = a->n_shared * a->I_shared;
   const int64_t max_mb = ceil_div(n_cap, mb) + a->E_l + (I_sh > 0 ? ceil_div(a->T_own, mb) : 0);
   L.max_mb = (int)std::max<int64_t>(1, max_mb);
@@ -193,8 +195,10 @@ int mok_dispatch_plan(const int32_t* topk_idx, int64_t T_pool, int32_t k, int32_
   const int64_t nb = plan_n_blocks(T_pool * k);
   int32_t* blk_counts = (int32_t*)ws;
   int32_t* blk_base = (int32_t*)((char*)ws + align_up(sizeof(int32_t) * nb * E_l));
+  const int64_t cap = std::max<int64_t>(1, T_pool * std::min(k, E_l));
   return status_of(launch_plan(topk_idx, T_pool, k, e0, E_l, tokens_per_rank, counts, offsets,
-                               rank_counts, route_ids, blk_counts, blk_base, (hipStream_t)stream));
+                               rank_counts, route_ids, blk_counts, blk_base, cap,
+                               (hipStream_t)stream));
 }
 
 int mok_moe_workspace_bytes(const mok_moe_args* a, size_t* bytes) {
@@ -251,7 +255,7 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   {
     hipError_t e = launch_plan(idx, a->T_pool, k, a->e0, a->E_l, a->tokens_per_rank, counts,
                                offsets, a->rank_counts_out, route_ids, (int32_t*)at(L.blk_counts),
-                               (int32_t*)at(L.blk_base), s, ev_start(MOK_STAGE_PLAN),
+                               (int32_t*)at(L.blk_base), L.route_cap, s, ev_start(MOK_STAGE_PLAN),
                                ev_stop(MOK_STAGE_PLAN));
     if (e != hipSuccess) return MOK_EHIP;
   }
@@ -276,7 +280,12 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.cap_d = L.cap_d;
   p.cap_r = L.cap_r;
   p.ring = L.use_ring;
-  p.grid = ((device_cus() + 7) / 8) * 8;   // one 256 x 256 tile workgroup per CU
+  p.route_cap = L.route_cap;
+  const int cus = device_cus();
+  p.grid = ((cus + 7) / 8) * 8;            // one 256 x 256 tile workgroup per CU
+  // the ring's per-XCD queues pay off on the whole chip (8 XCDs of 32 CUs, dispatched
+  // round-robin); on a partition of it one queue serves every workgroup
+  p.xcd_split = cus == 256;
   p.x = a->x;
   p.route_ids = route_ids;
   p.topk_w = w;
@@ -333,6 +342,51 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   } else {
     mark(MOK_STAGE_COMBINE);
   }
+  return MOK_OK;
+}
+
+int mok_moe_workspace_region(const mok_moe_args* a, int32_t region, size_t* offset,
+                             size_t* bytes, int64_t* rows) {
+  if (!offset || !bytes || !rows) return MOK_EINVAL;
+  int st = validate_moe(a);
+  if (st != MOK_OK) return st;
+  const Layout L = layout_moe(a);
+  const bool mx = a->dtype == MOK_MXFP8;
+  const int64_t ring = (int64_t)L.n_slots * a->minibatch_rows;
+  const int64_t I_sh = (int64_t)a->n_shared * a->I_shared;
+  const int64_t el = (int64_t)a->E_l * a->I * a->d, sl = I_sh * a->d;
+  const size_t es = a->dtype == MOK_FP32 ? 4 : 2;
+  size_t off = 0, n = 0;
+  int64_t R = 0;
+  switch (region) {
+    case MOK_REGION_WORKLIST:
+      off = L.wl; n = sizeof(int32_t) * worklist_ints(L.max_mb, L.cap_u, L.cap_d, L.cap_r);
+      R = 1; break;
+    case MOK_REGION_H:
+      off = L.H; n = (size_t)ring * L.Hld * (mx ? 1 : es); R = ring; break;
+    case MOK_REGION_H_SCALES: off = L.H_sc; n = (size_t)ring * (L.Hld / 32); R = ring; break;
+    case MOK_REGION_A_CODES: off = L.A_codes; n = (size_t)ring * a->d; R = ring; break;
+    case MOK_REGION_A_SCALES: off = L.A_sc; n = (size_t)ring * (a->d / 32); R = ring; break;
+    case MOK_REGION_WG_CODES: off = L.wg_q; n = el; R = a->I; break;
+    case MOK_REGION_WG_SCALES: off = L.wg_s; n = el / 32; R = a->I; break;
+    case MOK_REGION_WU_CODES: off = L.wu_q; n = el; R = a->I; break;
+    case MOK_REGION_WU_SCALES: off = L.wu_s; n = el / 32; R = a->I; break;
+    case MOK_REGION_WD_CODES: off = L.wd_q; n = el; R = a->d; break;
+    case MOK_REGION_WD_SCALES: off = L.wd_s; n = el / 32; R = a->d; break;
+    case MOK_REGION_SG_CODES: off = L.sg_q; n = sl; R = I_sh; break;
+    case MOK_REGION_SG_SCALES: off = L.sg_s; n = sl / 32; R = I_sh; break;
+    case MOK_REGION_SU_CODES: off = L.su_q; n = sl; R = I_sh; break;
+    case MOK_REGION_SU_SCALES: off = L.su_s; n = sl / 32; R = I_sh; break;
+    case MOK_REGION_SD_CODES: off = L.sd_q; n = sl; R = a->d; break;
+    case MOK_REGION_SD_SCALES: off = L.sd_s; n = sl / 32; R = a->d; break;
+    default: return MOK_EINVAL;
+  }
+  // the MX regions exist only in an MXFP8 forward, the shared ones only with shared experts
+  if (!mx && region >= MOK_REGION_H_SCALES) return MOK_EINVAL;
+  if (region >= MOK_REGION_SG_CODES && I_sh == 0) return MOK_EINVAL;
+  *offset = off;
+  *bytes = n;
+  *rows = R;
   return MOK_OK;
 }
 

@@ -43,7 +43,7 @@ namespace mok {
 // and ring items [XR[x], XR[x+1]), and takes them with its own ticket TICKETS[x]; without the
 // split every workgroup uses TICKETS[0] over all items.
 constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_ERR = 4, WL_N_R = 5, WL_AFFINE = 6,
-              WL_XB = 8, WL_XR = 17, WL_TICKETS = 26, WL_HDR = 48;
+              WL_XB = 8, WL_XR = 17, WL_TICKETS = 26, WL_EXITS = 34, WL_HDR = 48;
 constexpr int N_XCD = 8;        // XCDs of an MI355X, each with its own L2
 constexpr int XB_N = 4;         // N tiles per block of the stage tables' tile order: up
 constexpr int XB_ND = 8;        // ... down
@@ -95,8 +95,9 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
                                                          const int32_t* __restrict__ offsets,
                                                          int E_l, int T_own, int mb, int bm,
                                                          int nU_r, int nU_s, int nD, bool gather,
-                                                         bool ring, int n_slots, int cap, int cap_u,
-                                                         int cap_d, int cap_r,
+                                                         bool ring, bool xcd_split, int n_slots,
+                                                         int cap, int cap_u, int cap_d, int cap_r,
+                                                         int64_t route_cap,
                                                          int32_t* __restrict__ wl) {
   __shared__ int32_t sh[1024];
   const int t = threadIdx.x;
@@ -168,9 +169,12 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     carry_g += tg;
     carry_r += tr;
   }
+  // more local routes than route_ids holds (a token naming one expert twice) also overflows:
+  // no tile then reads past the plan
   const bool overflow = n_routed + n_sh > cap || carry_u > cap_u || carry_d > cap_d ||
-                        (ring && (int64_t)carry_u + carry_d + carry_g > cap_r);
-  const bool affine = ring && n_slots >= N_XCD;
+                        (ring && (int64_t)carry_u + carry_d + carry_g > cap_r) ||
+                        (int64_t)offsets[E_l] > route_cap;
+  const bool affine = ring && xcd_split && n_slots >= N_XCD;
   if (t == 0) {
     us[n_mb] = carry_u;
     ds[n_mb] = carry_d;
@@ -184,6 +188,7 @@ __global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restri
     wl[WL_AFFINE] = affine ? 1 : 0;
   }
   if (t < N_XCD) wl[WL_TICKETS + t] = 0;
+  if (t == 0) wl[WL_EXITS] = 0;
   // Ring order. With at least 8 slots the ring is split by XCD: minibatch m belongs to XCD
   // m % 8 as its (m / 8)-th minibatch, so the 8 XCDs run neighbouring minibatches -- mostly of
   // the same expert -- at the same time, and weights that one XCD reads from HBM the others
@@ -1394,10 +1399,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
   const bool affine = uniform(wl[WL_AFFINE]) != 0;
   uint32_t hw_xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw_xcc));
-  const int x = affine ? (int)(hw_xcc & (N_XCD - 1)) : 0;
-  const int32_t seg0 = uniform(wl[WL_XR + x]);
-  const int32_t seg1 = affine ? uniform(wl[WL_XR + x + 1]) : uniform(wl[WL_N_R]);
+  int x = affine ? (int)(hw_xcc & (N_XCD - 1)) : 0;
+  int32_t seg0 = uniform(wl[WL_XR + x]);
+  int32_t seg1 = affine ? uniform(wl[WL_XR + x + 1]) : uniform(wl[WL_N_R]);
   int32_t* ticket = &wl[WL_TICKETS + x];
+  bool draining = false;               // this workgroup runs queues no workgroup served
+  __shared__ int32_t next_queue;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t one = (threadIdx.x & 63) == 0 ? 1 : 0;
   // The next item is fetched while the current tile runs (wave 0, after K-step barriers 0..3,
@@ -1456,7 +1463,44 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     e.y = __builtin_amdgcn_readfirstlane(item.y);
     e.z = __builtin_amdgcn_readfirstlane(item.z);
     e.w = __builtin_amdgcn_readfirstlane(item.w);
-    if (e.x < 0) break;
+    if (e.x < 0) {
+      // queue x is exhausted. Without the split that ends the loop. With it, a queue is served
+      // only by the workgroups the hardware placed on its XCD; should an XCD get none (a
+      // placement other than round-robin), the last workgroup to finish its own queue runs
+      // each queue whose ticket was never taken, from first item to last. Those items depend
+      // only on items of the same queue, so one workgroup on any XCD computes them correctly.
+      if (!affine) break;
+      if (wid == 0) {
+        bool last = draining;
+        if (!draining) {
+          const int32_t before = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+              &wl[WL_EXITS], one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          last = before == (int32_t)gridDim.x - 1;
+        }
+        int q = -1;
+        if (last) {
+          for (int y = N_XCD - 1; y >= 0; --y) {
+            const int32_t taken = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                &wl[WL_TICKETS + y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (taken == 0 && uniform(wl[WL_XR + y]) < uniform(wl[WL_XR + y + 1])) q = y;
+          }
+        }
+        next_queue = q;                   // every lane of wave 0 stores the same value
+      }
+      __syncthreads();
+      const int q = __builtin_amdgcn_readfirstlane(next_queue);
+      if (q < 0) break;
+      draining = true;
+      x = q;
+      seg0 = uniform(wl[WL_XR + q]);
+      seg1 = uniform(wl[WL_XR + q + 1]);
+      ticket = &wl[WL_TICKETS + q];
+      for (int s = 0; s < 4; ++s) {
+        fetch_step(s);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      continue;
+    }
     const int kind = e.y >> KIND_SHIFT;
     e.y &= (1 << KIND_SHIFT) - 1;
     if (kind == KIND_U) {
@@ -1597,8 +1641,8 @@ hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const*
   const bool gather_launch = p.elem == Elem::FP8 && !p.ring;   // ends the GATHER stage
   launch_k(k_build_worklist, dim3(1), dim3(1024), 0, s, ev_at(ev, EV_GATHER),
            gather_launch ? nullptr : ev_at(ev, EV_GATHER + 1), p.counts, p.offsets, p.E_l,
-           p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.n_slots, p.max_mb,
-           p.cap_u, p.cap_d, p.cap_r, p.wl);
+           p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.xcd_split, p.n_slots,
+           p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.route_cap, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   return launch_stages_t<Elem::FP8, false>(p, s, ev);

@@ -32,8 +32,8 @@ int64_t plan_n_blocks(int64_t n_routes);
 hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
                        int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
                        int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
-                       int32_t* blk_base, hipStream_t s, hipEvent_t ev0 = nullptr,
-                       hipEvent_t ev1 = nullptr);
+                       int32_t* blk_base, int64_t route_cap, hipStream_t s,
+                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // MX scales of the operands the expert GEMMs read are stored K-step major: a matrix of R rows
 // and K columns keeps the 4 scales of K step j (128 elements) of row r as the 4-byte word
@@ -67,6 +67,8 @@ struct ExpertPass {
   int cap_u, cap_d;      // capacity of the up / down tile tables
   int cap_r;             // capacity of the ring-order table (ring work loop), else 0
   bool ring;             // persistent ring work loop (else stage-ordered launches)
+  bool xcd_split;        // ring: one item queue per XCD (whole-chip launch of 256 CUs)
+  int64_t route_cap;     // rows of route_ids: a plan with more local routes is rejected
   int bm, bn;            // GEMM tile (rows, B-tile rows)
   int grid;              // workgroups of the tile loops
   // inputs

@@ -1,19 +1,22 @@
-// Stage 2: the pull dispatch plan, and the GEMM work list derived from it on the device.
+// Stage 2: the pull dispatch plan.
 //
-// The MoK write-up's "Scheduling" section: for a pull dispatch the schedule is a table
-// {src_rank, src_index} whose row index is the row of the local destination buffer; it needs
-// no sort, only a walk over the routing results that records every route to a local expert,
-// together with the count per local expert, the count per (local expert, source rank) and
-// the region offsets. The Telegram summary adds that pulling lets each expert read its
-// tokens as large contiguous chunks with no contended atomic slot counters.
+// Source: the MoK write-up, "Scheduling" section (the pull schedule is found by scanning the
+// routing results, with no sort), and the Telegram post, "Method and experiments" (each
+// expert fetches its own tokens; no contended slot counters).
 //
-// Here the walk is split over workgroups and stays deterministic: (1) each workgroup counts
-// the local routes of its contiguous chunk of routes per expert; (2) one workgroup scans
-// those counts into region offsets and per-chunk bases; (3) each workgroup walks its chunk
-// again in order and writes every local route at base + its stable rank (ballot prefix
-// counts), so each region is in ascending route order -- a stable counting sort -- and adds its
-// routes' per-(expert, source rank) counts (integer additions) to totals the first step cleared.
-// Only order-independent integer arithmetic is used; no position is taken by an atomic.
+// What is built for the local experts [e0, e0 + E_l): the number of routes each one receives,
+// the number per (expert, source rank), the exclusive prefix sum of the per-expert numbers
+// (region offsets), and route_ids: every local route id r = t*k + j, grouped by expert, in
+// ascending r inside each group. Three launches keep it deterministic:
+//   k_plan_count   -- per contiguous chunk of routes, a histogram of local experts;
+//   k_plan_scan    -- one workgroup turns the chunk histograms into region offsets and the
+//                     first free row of every (chunk, expert) pair;
+//   k_plan_scatter -- each chunk walks its routes again in order and writes each local route
+//                     at its (chunk, expert) base plus its rank among the chunk's earlier
+//                     routes of that expert (wave ballots), i.e. a stable counting sort; the
+//                     per-(expert, source rank) counts are integer sums added to totals that
+//                     the first launch cleared.
+// Positions never come from an atomic, so the result does not depend on scheduling.
 #include "device_common.h"
 #include "launch.h"
 
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __
                                                                int32_t* __restrict__ route_ids,
                                                                int32_t* __restrict__ rank_counts,
                                                                int k, int64_t tokens_per_rank,
-                                                               int64_t R) {
+                                                               int64_t R, int64_t cap) {
   extern __shared__ int32_t sm[];
   int32_t* base = sm;                 // [E_l] next free row of each region (this chunk)
   int32_t* wcnt = sm + E_l;           // [4][E_l] per-wave counts of the current sub-chunk
@@ -158,7 +161,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __
     if (le >= 0) {
       int32_t pos = base[le] + rank;
       for (int q = 0; q < w; ++q) pos += wcnt[q * E_l + le];
-      route_ids[pos] = (int32_t)r;
+      // a token that names one expert twice can push a region past the capacity: such rows
+      // are dropped (offsets[E_l] > cap tells the caller)
+      if (pos < cap) route_ids[pos] = (int32_t)r;
     }
     __syncthreads();
     if (leader) {
@@ -191,7 +196,8 @@ int64_t plan_n_blocks(int64_t n_routes) {
 hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
                        int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
                        int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
-                       int32_t* blk_base, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                       int32_t* blk_base, int64_t route_cap, hipStream_t s, hipEvent_t ev0,
+                       hipEvent_t ev1) {
   const int64_t n_routes = n_tok * k;
   const int64_t chunk = plan_chunk(n_routes);
   const int64_t nb = plan_n_blocks(n_routes);
@@ -203,7 +209,7 @@ hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l
            blk_base, counts, offsets);
   launch_k(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS),
            (uint32_t)(sh_count * (5 + PLAN_NR)), s, nullptr, ev1, idx, n_routes, chunk, e0, E_l,
-           blk_base, offsets, route_ids, rank_counts, k, tokens_per_rank, R);
+           blk_base, offsets, route_ids, rank_counts, k, tokens_per_rank, R, route_cap);
   return hipGetLastError();
 }
 

@@ -65,3 +65,38 @@ def gpu_topk(logits: torch.Tensor, k: int):
 def to_np(t):
     return None if t is None else t.detach().float().cpu().numpy() if t.is_floating_point() \
         else t.detach().cpu().numpy()
+
+
+def kmajor_scales_to_rows(buf, n_rows: int, K: int, R: int) -> np.ndarray:
+    """Row-major [n_rows, K/32] E8M0 scales from a K-step-major region (layout stated in
+    include/mok.h): matrix g = row // R; (row r, block b) at g*R*(K/32) + ((b//4)*R + r)*4 + b%4."""
+    buf = np.asarray(buf)
+    rows = np.arange(n_rows, dtype=np.int64)[:, None]
+    b = np.arange(K // 32, dtype=np.int64)[None, :]
+    g, r = rows // R, rows % R
+    return buf[g * R * (K // 32) + ((b // 4) * R + r) * 4 + (b % 4)]
+
+
+def stage_order_minibatches(counts, offsets, route_ids, k: int, mb: int, own_begin: int,
+                            T_own: int, shared: bool):
+    """Ring row -> pool row of the gathered A rows of a stage-ordered (MOK_FLAG_NO_RING)
+    forward, as include/mok.h states it: minibatch m (routed experts ascending, each region
+    cut into mb-row pieces, then the own tokens) keeps ring rows [m*mb, m*mb + rows)."""
+    ring_rows, pool_rows = [], []
+    m = 0
+    for e in range(len(counts)):
+        c = int(counts[e])
+        for i in range(0, c, mb):
+            n = min(mb, c - i)
+            ring_rows.append(m * mb + np.arange(n))
+            pool_rows.append(np.asarray(route_ids[offsets[e] + i:offsets[e] + i + n]) // k)
+            m += 1
+    if shared:
+        for i in range(0, T_own, mb):
+            n = min(mb, T_own - i)
+            ring_rows.append(m * mb + np.arange(n))
+            pool_rows.append(own_begin + i + np.arange(n))
+            m += 1
+    if not ring_rows:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return np.concatenate(ring_rows).astype(np.int64), np.concatenate(pool_rows).astype(np.int64)

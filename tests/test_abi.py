@@ -121,3 +121,35 @@ def test_product_path_never_imports_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "mok_oracle" not in txt, f
+
+
+def test_workspace_regions(mok):
+    """Regions of the forward's intermediates: inside the workspace, disjoint, sized as the
+    header states, and present only where the configuration has them."""
+    a = _args(mok, dtype=2, I=256, minibatch_rows=128, ring_rows=1024)
+    total = mok.mok_moe_workspace_bytes(a)
+    spans = []
+    for reg in range(17):
+        off, n, rows = mok.mok_moe_workspace_region(a, reg)
+        assert off % 256 == 0 and n > 0 and off + n <= total, reg
+        spans.append((off, off + n))
+    spans.sort()
+    assert all(b[0] >= a_[1] for a_, b in zip(spans, spans[1:]))
+    d, I, E_l, Is = 256, 256, 16, 128
+    assert mok.mok_moe_workspace_region(a, mok.MOK_REGION_WG_CODES)[1:] == (E_l * I * d, I)
+    assert mok.mok_moe_workspace_region(a, mok.MOK_REGION_WD_SCALES)[1:] == (E_l * d * I // 32, d)
+    assert mok.mok_moe_workspace_region(a, mok.MOK_REGION_SU_CODES)[1:] == (Is * d, Is)
+    assert mok.mok_moe_workspace_region(a, mok.MOK_REGION_SD_SCALES)[1:] == (d * Is // 32, d)
+    assert mok.mok_moe_workspace_region(a, mok.MOK_REGION_A_CODES)[1:] == (1024 * d, 1024)
+    assert mok.mok_moe_workspace_region(a, mok.MOK_REGION_H_SCALES)[1:] == (1024 * I // 32, 1024)
+    # a bf16 forward has H (bf16) and the work list, no MX regions
+    b = _args(mok)
+    assert mok.mok_moe_workspace_region(b, mok.MOK_REGION_H)[1] == 1024 * 192 * 2
+    for reg in (mok.MOK_REGION_A_CODES, mok.MOK_REGION_WG_SCALES, mok.MOK_REGION_H_SCALES, 99, -1):
+        with pytest.raises(mok.MokError):
+            mok.mok_moe_workspace_region(b, reg)
+    # no shared experts: no shared regions
+    c = _args(mok, dtype=2, I=256, n_shared=0, y_shared=0, ws_gate=0, ws_up=0, ws_down=0)
+    with pytest.raises(mok.MokError):
+        mok.mok_moe_workspace_region(c, mok.MOK_REGION_SG_CODES)
+    mok.mok_moe_workspace_region(c, mok.MOK_REGION_WG_CODES)

@@ -14,6 +14,8 @@ from _layer import TOL, gpu_layer, gpu_topk, make_inputs, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+# local expert loads of the 384-expert Zipf share (oracle top-k of the seeded pool logits)
+EP96_COUNTS = [16382, 7934, 4008, 2696]
 
 
 def _cpu(inp):
@@ -31,7 +33,9 @@ def _check_plan(layer, ref_plan):
     assert np.array_equal(to_np(layer.inter["route_ids"])[:n], ref_plan["route_ids"])
 
 
-def _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng, n_routes=96, n_own=24):
+def _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng, n_routes=1024, n_own=None):
+    """Sampled route slots (default 1024) and the own tokens' shared output (default: all of
+    them) against the oracle, float64; idx and w are the oracle's own routing."""
     mx = wl.dtype == "mxfp8"
     tol = TOL[wl.dtype]
     rids = plan["route_ids"].astype(np.int64)
@@ -41,54 +45,73 @@ def _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng, n_routes=96, n_own
     got = to_np(layer.y_slots[torch.from_numpy(pick).to(DEV)])
     err_p = rel_err(got, ref)
     assert err_p <= tol, err_p
-    own = _sample(rng, wl.T_own, n_own)
+    own = np.arange(wl.T_own) if n_own is None else _sample(rng, wl.T_own, n_own)
     a = oracle._operand(cpu["x"][torch.from_numpy(wl.own_begin + own)], mx)
     S = oracle.shared_ffn(a, oracle._operand(cpu["sg"], mx), oracle._operand(cpu["su"], mx),
                           oracle._operand(cpu["sd"], mx), mx)
     err_s = rel_err(to_np(layer.y_shared[torch.from_numpy(own).to(DEV)]), S)
     assert err_s <= tol, err_s
+    print(f"{wl.name}: {len(pick)} routes rel err {err_p:.2e}, {len(own)} own rows {err_s:.2e}",
+          flush=True)
     return err_p, err_s
 
 
-def test_ep1_full_layer_bf16():
-    """T=8192, d=2048, 64 experts top-6, I=1408, 2 shared experts: the whole layer."""
+def _written(layer, plan):
+    """The forward's written outputs as raw bits: local route slots, S, y."""
+    rid = torch.from_numpy(plan["route_ids"].astype(np.int64)).to(DEV)
+    outs = [layer.y_slots[rid]] + [t for t in (layer.y_shared, layer.y) if t is not None]
+    return [o.clone().view(torch.int32 if o.dtype == torch.float32 else torch.int16) for o in outs]
+
+
+def _reruns_bit_identical(layer, plan, n=10):
+    first = _written(layer, plan)
+    for _ in range(n - 1):
+        layer.forward()
+        torch.cuda.synchronize()
+        assert layer.device_error() == 0
+        for a, b in zip(_written(layer, plan), first):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("ring", [False, True])
+def test_ep1_full_layer_bf16(ring):
+    """T=8192, d=2048, 64 experts top-6, I=1408, 2 shared experts: the whole layer, every
+    output element against the oracle's whole forward, in both work-loop modes; 10 runs
+    bit-identical."""
     import routing_grouped_expert_gemm_amd as mok
     wl = synth.WORKLOADS[synth.EP1]
     inp = make_inputs(wl, DEV)
-    layer = gpu_layer(wl, inp, flags=mok.MOK_FLAG_NO_RING)
+    layer = gpu_layer(wl, inp, flags=0 if ring else mok.MOK_FLAG_NO_RING)
     layer.forward()
     torch.cuda.synchronize()
+    assert layer.device_error() == 0
     cpu = _cpu(inp)
+    ref = oracle.moe_forward(wl, cpu["x"], w_router=cpu["w_router"], wg=cpu["wg"], wu=cpu["wu"],
+                             wd=cpu["wd"], sg=cpu["sg"], su=cpu["su"], sd=cpu["sd"])
     logits = oracle.router_logits(cpu["x"], cpu["w_router"])
     assert np.array_equal(to_np(layer.inter["logits"]), logits)
-    idx, w = oracle.topk(logits, wl.k)
-    assert np.array_equal(to_np(layer.inter["topk_idx"]), idx)
-    np.testing.assert_allclose(to_np(layer.inter["topk_w"]), w, rtol=2e-6, atol=1e-7)
-    plan = oracle.dispatch_plan(idx, 0, wl.E, wl.tokens_per_rank)
+    assert np.array_equal(to_np(layer.inter["topk_idx"]), ref["idx"])
+    np.testing.assert_allclose(to_np(layer.inter["topk_w"]), ref["w"], rtol=2e-6, atol=1e-7)
+    plan = ref["plan"]
     _check_plan(layer, plan)
     mean = wl.T_pool * wl.k / wl.E
     assert plan["counts"].min() >= 0.8 * mean and plan["counts"].max() <= 1.2 * mean
-    rng = np.random.default_rng(11)
-    _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng)
-    # combined output on sampled tokens: S + sum_j P, float64
-    toks = _sample(rng, wl.T_pool, 24)
-    xf = oracle._f32(cpu["x"][torch.from_numpy(toks)])
-    ref = oracle.shared_ffn(xf, oracle._f32(cpu["sg"]), oracle._f32(cpu["su"]), oracle._f32(cpu["sd"]))
-    for j in range(wl.k):
-        ref += oracle.route_outputs(toks * wl.k + j, cpu["x"][torch.from_numpy(toks)], idx, w, 0,
-                                    cpu["wg"], cpu["wu"], cpu["wd"])
-    assert rel_err(to_np(layer.y[torch.from_numpy(toks).to(DEV)]), ref) <= TOL["bf16"]
-    # reruns are bit-identical
-    y0 = layer.y.clone()
-    for _ in range(2):
-        layer.forward()
-    torch.cuda.synchronize()
-    assert torch.equal(layer.y.view(torch.int16), y0.view(torch.int16))
+    tol = TOL["bf16"]
+    err_p = rel_err(to_np(layer.y_slots)[plan["route_ids"]], ref["P"])
+    err_s = rel_err(to_np(layer.y_shared), ref["y_shared"])
+    err_y = rel_err(to_np(layer.y), ref["y"])
+    print(f"ep1 ring={ring}: all {plan['n']} slots {err_p:.2e}, S {err_s:.2e}, y {err_y:.2e}",
+          flush=True)
+    assert err_p <= tol and err_s <= tol and err_y <= tol
+    _reruns_bit_identical(layer, plan, 10)
 
 
-@pytest.mark.parametrize("name", [synth.EP64, synth.EP64_MX, synth.EP96])
-def test_share_workloads(name):
-    """One rank's share: pool of 64 x 4096 (or 96 x 2048) tokens, d=7168, 4 local experts."""
+@pytest.mark.parametrize("name,ring", [(synth.EP64, False), (synth.EP64, True),
+                                       (synth.EP64_MX, False), (synth.EP96, False)])
+def test_share_workloads(name, ring):
+    """One rank's share: pool of 64 x 4096 (or 96 x 2048) tokens, d=7168, 4 local experts.
+    Routing and plan bit-exact over the whole pool; 1024 sampled route slots and every own
+    token's shared output against the oracle; reruns bit-identical (10 for MXFP8)."""
     import routing_grouped_expert_gemm_amd as mok
     wl = synth.WORKLOADS[name]
     inp = make_inputs(wl, DEV)
@@ -98,33 +121,17 @@ def test_share_workloads(name):
     assert np.array_equal(to_np(idx_g), idx)
     np.testing.assert_allclose(to_np(w_g), w, rtol=2e-6, atol=1e-7)
     del cpu["logits"]
-    layer = gpu_layer(wl, inp, topk=(idx_g, w_g), flags=mok.MOK_FLAG_NO_RING)
+    layer = gpu_layer(wl, inp, topk=(idx_g, w_g), flags=0 if ring else mok.MOK_FLAG_NO_RING)
     layer.forward()
     torch.cuda.synchronize()
     assert layer.device_error() == 0
     plan = oracle.dispatch_plan(idx, wl.e0, wl.E_l, wl.tokens_per_rank)
     _check_plan(layer, plan)
     if name == synth.EP96:
-        assert plan["counts"].tolist() == [16382, 7934, 4008, 2696]   # calibrated Zipf load
+        assert plan["counts"].tolist() == EP96_COUNTS   # calibrated Zipf load
     rng = np.random.default_rng(12)
-    _check_sampled_outputs(wl, layer, cpu, idx, to_np(w_g), plan, rng)
-    if wl.dtype == "mxfp8":
-        # the on-device quantiser (the same device code the forward uses) on real operands
-        for t in (inp["wg"][0, :64], inp["wd"][1, :64], inp["x"][:64]):
-            codes = torch.empty(t.shape, dtype=torch.uint8, device=DEV)
-            sc = torch.empty((t.shape[0], t.shape[1] // 32), dtype=torch.uint8, device=DEV)
-            mok.mok_quantize_mxfp8(t.contiguous(), codes, sc)
-            torch.cuda.synchronize()
-            rc, rs = oracle.mxfp8_quantize(t.cpu())
-            assert np.array_equal(to_np(codes), rc) and np.array_equal(to_np(sc), rs)
-    # rerun bit-identical at the sampled rows
-    rids = torch.from_numpy(plan["route_ids"][:: max(1, plan["n"] // 512)].astype(np.int64)).to(DEV)
-    before = layer.y_slots[rids].clone()
-    s_before = layer.y_shared.clone()
-    layer.forward()
-    torch.cuda.synchronize()
-    assert torch.equal(layer.y_slots[rids].view(torch.int16), before.view(torch.int16))
-    assert torch.equal(layer.y_shared.view(torch.int16), s_before.view(torch.int16))
+    _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng)
+    _reruns_bit_identical(layer, plan, 10 if wl.dtype == "mxfp8" else 2)
 
 
 def test_zipf_share_minibatch_sweep_bit_identical():

@@ -198,9 +198,9 @@ def _run_and_compare(wl, flags, mb=None):
     else:
         ridx, rw = oracle.topk(cpu["logits"], wl.k)
         assert np.array_equal(to_np(topk[0]), ridx)
+        np.testing.assert_allclose(to_np(topk[1]), rw, rtol=2e-6, atol=1e-7)
         ref = oracle.moe_forward(wl, cpu["x"], wg=cpu["wg"], wu=cpu["wu"], wd=cpu["wd"],
-                                 sg=cpu["sg"], su=cpu["su"], sd=cpu["sd"],
-                                 topk_in=(ridx, to_np(topk[1])))
+                                 sg=cpu["sg"], su=cpu["su"], sd=cpu["sd"], topk_in=(ridx, rw))
     plan = ref["plan"]
     assert np.array_equal(to_np(layer.inter["counts"]), plan["counts"])
     assert np.array_equal(to_np(layer.inter["offsets"]), plan["offsets"])

@@ -51,10 +51,10 @@ def test_ring_small_layers_match_oracle(name):
                                  wu=cpu["wu"], wd=cpu["wd"], sg=cpu["sg"], su=cpu["su"],
                                  sd=cpu["sd"])
     else:
-        ridx, _ = oracle.topk(cpu["logits"], wl.k)
+        ridx, rw = oracle.topk(cpu["logits"], wl.k)
+        assert np.array_equal(to_np(topk[0]), ridx)
         ref = oracle.moe_forward(wl, cpu["x"], wg=cpu["wg"], wu=cpu["wu"], wd=cpu["wd"],
-                                 sg=cpu["sg"], su=cpu["su"], sd=cpu["sd"],
-                                 topk_in=(ridx, to_np(topk[1])))
+                                 sg=cpu["sg"], su=cpu["su"], sd=cpu["sd"], topk_in=(ridx, rw))
     plan = ref["plan"]
     tol = TOL[wl.dtype]
     assert rel_err(to_np(layer.y_slots)[plan["route_ids"]], ref["P"]) <= tol
@@ -123,11 +123,12 @@ def test_ring_full_share_workloads(name):
     # sampled rows against the oracle (the last ring layer)
     layer = _run(wl, inp, topk, 0)
     cpu = {k: (v.cpu() if v is not None else None) for k, v in inp.items()}
-    idx, w = to_np(topk[0]), to_np(topk[1])
-    n = int(layer.inter["offsets"][-1])
-    rids = to_np(layer.inter["route_ids"])[:n].astype(np.int64)
+    idx, w = oracle.topk(cpu["logits"], wl.k)
+    assert np.array_equal(to_np(topk[0]), idx)
+    rids = oracle.dispatch_plan(idx, wl.e0, wl.E_l, wl.tokens_per_rank)["route_ids"].astype(np.int64)
+    n = len(rids)
     rng = np.random.default_rng(7)
-    pick = np.sort(rng.choice(rids, size=min(64, n), replace=False))
+    pick = np.sort(rng.choice(rids, size=min(1024, n), replace=False))
     mx = wl.dtype == "mxfp8"
     refp = oracle.route_outputs(pick, cpu["x"][torch.from_numpy(pick // wl.k)], idx, w, wl.e0,
                                 cpu["wg"], cpu["wu"], cpu["wd"], mx)
