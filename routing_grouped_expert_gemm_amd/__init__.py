@@ -29,7 +29,8 @@ MOK_N_STAGES = 7
 MOK_DEVERR_OVERFLOW, MOK_DEVERR_WAIT = 1, 2
 
 EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
-           "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_moe_workspace_bytes",
+           "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_dispatch_plan_noalloc",
+           "mok_moe_workspace_bytes",
            "mok_moe_forward", "mok_moe_workspace_region", "mok_quantize_mxfp8",
            "mok_get_device_error"]
 
@@ -76,6 +77,8 @@ _lib.mok_topk.argtypes = [_P, _I64, _I32, _I32, _P, _P, _P]
 _lib.mok_dispatch_plan_workspace_bytes.argtypes = [_I64, _I32, _I32, ctypes.POINTER(_SZ)]
 _lib.mok_dispatch_plan.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                    _SZ, _P]
+_lib.mok_dispatch_plan_noalloc.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                           _P, _P]
 _lib.mok_moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeArgs), ctypes.POINTER(_SZ)]
 _lib.mok_moe_forward.argtypes = [ctypes.POINTER(MoeArgs), _P]
 _lib.mok_moe_workspace_region.argtypes = [ctypes.POINTER(MoeArgs), _I32, ctypes.POINTER(_SZ),
@@ -143,6 +146,16 @@ def mok_dispatch_plan(topk_idx, E: int, e0: int, E_l: int, tokens_per_rank: int,
            _lib.mok_dispatch_plan(_ptr(topk_idx), T, k, E, e0, E_l, tokens_per_rank, _ptr(counts),
                                   _ptr(offsets), _ptr(rank_counts), _ptr(route_ids), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mok_dispatch_plan_noalloc(topk_idx, E: int, e0: int, E_l: int, tokens_per_rank: int, counts,
+                              offsets, rank_counts, route_ids, stream=None) -> None:
+    """mok_dispatch_plan with the library's fixed device scratch (no workspace argument)."""
+    T, k = topk_idx.shape
+    _check("mok_dispatch_plan_noalloc",
+           _lib.mok_dispatch_plan_noalloc(_ptr(topk_idx), T, k, E, e0, E_l, tokens_per_rank,
+                                          _ptr(counts), _ptr(offsets), _ptr(rank_counts),
+                                          _ptr(route_ids), _stream(stream)))
 
 
 def mok_moe_workspace_bytes(args: MoeArgs) -> int:
