@@ -1,32 +1,40 @@
 """Throughput of the MoE-layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--ring] [--no-cpu]
 
-One step = one mok_moe_forward over the workload's whole batch: router projection + top-k,
-dispatch plan, pull gather + gate/up GEMM with SwiGLU, down GEMM with the routing-weight
-scale, shared experts and the fixed-order combine. Inputs are seeded synthetic tensors
-already resident in HBM. Prints ONE JSON line.
+One step = one mok_moe_forward over the workload's whole batch: router projection + top-k
+(or top-k of given logits), dispatch plan, pull gather + gate/up GEMM with SwiGLU, down GEMM
+with the routing-weight scale, shared experts and (full layer) the fixed-order combine. Inputs
+are seeded synthetic tensors already resident in HBM. Prints ONE JSON line.
 
-`stage_ms` (other than the gate/up stage) comes from a separate untimed pass that times every
-stage: the library ties each stage's events to the start of its first kernel and the end of
-its last. `hbm` gives the same for the memory-bound stages (plan, combine, MXFP8 weight quantisation and
-row gather): algorithmic bytes over the stage's HIP-event time against 8 TB/s.
+Default run: the headline is the EP=1 bf16 layer (T=8192, d=2048, 64 experts, top-6) with
+stage-ordered expert launches; the same line carries
+  "ring":  that layer with the persistent ring work loop (the library default), and
+  "mxfp8": the MXFP8 EP=64 share (262144-row pool, d=7168, 4 local experts + 1 shared),
+each timed the same way (W warm-up steps, K timed steps between device synchronisations).
+--workload NAME measures that workload alone (used by the profiling runs).
 
-`roofline` is taken live for the dominant kernel (the gate/up stage: grouped gate/up GEMM
-with the fused pull gather and SwiGLU, routed + shared): HIP events that the library attaches
-to that launch on the forward's own stream (its start and end; the only events in the timed
-steps), averaged over the timed steps, against the
-algorithmic FLOPs of one launch (4 * d * I per routed row + 4 * d * I_shared * n_shared per
-own token). `roofline.traffic` is the HBM bytes of one launch of that kernel as measured by
-the rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
-by what the counter reads for a plain copy of known size); it is null when the summary is
-missing or was taken from different kernel sources. `cpu_baseline` is the CPU oracle timed on
-a bounded sample of the same workload.
+`stage_ms` (other than the roofline kernel's) comes from a separate, untimed pass that times
+every stage with HIP events the library ties to the start of each stage's first kernel and the
+end of its last; before each step of that pass a 1 GiB scratch buffer is overwritten, so the
+stage times are cold-cache times (the 256 MB last-level cache holds nothing of the step
+before). `hbm` gives, for the memory-bound stages, algorithmic bytes over those times against
+8 TB/s.
+
+`roofline` is taken live for the dominant kernel: the gate/up stage (grouped gate/up GEMM with
+the fused pull gather and SwiGLU, routed + shared) when stage-ordered, the whole ring loop
+(gate/up and down tiles) with --ring. Its time comes from HIP events the library attaches to
+that launch on the forward's own stream (the only events in the timed steps); `achieved` is the
+launch's algorithmic FLOPs (gate/up: 4*d*I per routed row + 4*d*I_s*n_s per own token; down:
+half that) over it. `roofline.traffic` is the HBM bytes of one launch of that kernel from the
+rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by
+what the counter reads for a plain 1 GiB copy); null when the summary is missing or was taken
+from other kernel sources. `cpu_baseline` is the CPU oracle timed on the same workload.
 
     python bench.py --summarize DIR
 
-writes that summary from the rocprofv3 output directory DIR (layout and commands listed in
-the summary itself).
+writes the profiles/ summaries from a rocprofv3 output directory DIR (layout and commands are
+listed in the summaries themselves).
 """
 from __future__ import annotations
 
@@ -52,7 +60,9 @@ KERNEL_SOURCES = ["routing_grouped_expert_gemm_amd/csrc/expert_gemm.hip",
                   "routing_grouped_expert_gemm_amd/csrc/device_common.h",
                   "routing_grouped_expert_gemm_amd/csrc/launch.h",
                   "routing_grouped_expert_gemm_amd/_build.py"]
-UP_KERNEL = "k_expert_stage<(mok::Elem)"   # + element, then "true" for the gate/up stage
+ELEM = {"f32": 0, "bf16": 1, "mxfp8": 2}
+ELEM_NAME = {0: "fp32", 1: "bf16", 2: "mxfp8"}
+FLUSH_BYTES = 1 << 30        # scratch overwritten before each step of the per-stage pass
 
 
 def kernel_sources_sha256() -> str:
@@ -83,93 +93,244 @@ def profiled_traffic(workload: str):
         return None
 
 
-def _is_up_kernel(name: str, elem: int) -> bool:
-    return f"{UP_KERNEL}{elem}, true," in name
+# ------------------------------------------------------------------ profile summaries
+
+def kernel_key(name: str) -> str:
+    """Short, stable name of a mok kernel from its demangled name (None for other kernels)."""
+    if "mok::" not in name:
+        return None
+    n = name.replace("void ", "").strip()
+    if n.endswith(")"):                  # drop the parameter list: from the "(" matching the end
+        depth = 0
+        for i in range(len(n) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(n[i], 0)
+            if depth == 0:
+                n = n[:i]
+                break
+    n = n.replace("mok::", "").strip()
+    if n.startswith("k_expert_stage<"):
+        parts = n[len("k_expert_stage<"):].split(",")
+        el = ELEM_NAME[int(parts[0].split(")")[-1])]
+        return f"k_expert_stage<{el}, {'gate/up' if parts[1].strip() == 'true' else 'down'}>"
+    if n.startswith("k_ring<"):
+        el = ELEM_NAME[int(n[len("k_ring<"):].split(",")[0].split(")")[-1])]
+        return f"k_ring<{el}>"
+    return n
 
 
-def summarize(d: str) -> str:
-    """Write profiles/expert_gemm_up_<workload>.txt from a rocprofv3 output directory holding
-    trace/ (kernel trace + stats of a bench run, its JSON line in trace.json), FETCH_SIZE/ and
-    WRITE_SIZE/ (counter passes over a short bench run) and copy_FETCH_SIZE/, copy_WRITE_SIZE/
-    (the same counters over a 1 GiB device copy)."""
-    bench_line = json.loads(open(os.path.join(d, "trace.json")).read().strip().splitlines()[-1])
-    wl = bench_line["config"]["workload"]
-    elem = {"bf16": 1, "f32": 0, "mxfp8": 2}[bench_line["dtype"]]
-    stats = list(csv.DictReader(open(os.path.join(d, "trace", "trace_kernel_stats.csv"))))
+def algorithmic_bytes(wl, n_routes: int) -> dict:
+    """Bytes each memory-bound kernel must move per forward (each operand read once, each
+    result written once); the GEMM stages are priced in FLOPs instead."""
+    es = 4 if wl.dtype == "fp32" else 2
+    T, d, E, k = wl.T_pool, wl.d, wl.E, wl.k
+    I_sh = wl.n_shared * wl.I_shared
+    # keyed by kernel name without template arguments where those vary with the shape
+    out = {"k_plan_count": 4 * T * k, "k_plan_scatter": 4 * T * k + 4 * n_routes,
+           "k_topk": 4 * T * E + 8 * T * k}
+    if wl.routing == "router":
+        out["k_router_logits"] = T * d * es + E * d * es + 4 * T * E
+    if wl.full_layer:
+        out["k_combine"] = T * d * es * (k + 2)
+    if wl.dtype == "mxfp8":
+        n_w = wl.E_l * 3 * d * wl.I + 3 * d * I_sh
+        out["k_quantize_mxfp8<true>"] = n_w * (2 + 1 + 1 / 32)
+        out["k_gather_quantize"] = (n_routes + wl.T_own) * d * (2 + 1 + 1 / 32)
+    return out
 
-    def counter(sub, name_pred):
-        rows = list(csv.DictReader(open(os.path.join(d, sub, f"{sub}_counter_collection.csv"))))
-        vals = [float(r["Counter_Value"]) for r in rows if name_pred(r["Kernel_Name"])]
-        return sum(vals) / len(vals), len(vals)
 
-    up = lambda n: _is_up_kernel(n, elem)
-    copy = lambda n: "copyBuffer" in n
-    fetch_kib, n_f = counter("FETCH_SIZE", up)
-    write_kib, n_w = counter("WRITE_SIZE", up)
-    copy_fetch, _ = counter("copy_FETCH_SIZE", copy)
-    copy_write, _ = counter("copy_WRITE_SIZE", copy)
-    copy_kib = 1 << 20                               # 1 GiB read and 1 GiB written per copy
-    f_fetch, f_write = copy_kib / copy_fetch, copy_kib / copy_write
-    traffic = int(round((fetch_kib * f_fetch + write_kib * f_write) * 1024))
-    up_stat = [r for r in stats if up(r["Name"])][0]
-    prof_ms = float(up_stat["AverageNs"]) * 1e-6
-    ev_ms = bench_line["stage_ms"]["up"]
-    # the same dispatches as the events: the gate/up launches of the timed steps, which follow
-    # the warm-up steps in launch order (the untimed per-stage pass comes after them)
-    trace = [r for r in csv.DictReader(open(os.path.join(d, "trace", "trace_kernel_trace.csv")))
-             if up(r["Kernel_Name"])]
-    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    w, k = bench_line["warmup"], bench_line["steps"]
-    timed = trace[w:w + k]
-    timed_ms = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed) / len(timed) * 1e-6
-    lines = [
-        f"# gate/up expert GEMM stage (routed + shared, fused pull gather and SwiGLU), workload {wl}",
-        "#",
-        "# commands (from the repository root; D = gpurun_out/prof_" + wl + "):",
-        f"#   rocprofv3 --kernel-trace --stats -d D/trace -o trace --output-format csv -- "
-        f"python3 bench.py --steps 10 --warmup 3 --no-cpu --workload {wl} > D/trace.json",
-        f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'mok::' -d D/FETCH_SIZE -o FETCH_SIZE "
-        f"--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu --workload {wl}",
-        f"#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'mok::' -d D/WRITE_SIZE -o WRITE_SIZE "
-        f"--output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu --workload {wl}",
-        "#   rocprofv3 --pmc FETCH_SIZE -d D/copy_FETCH_SIZE -o copy_FETCH_SIZE --output-format csv "
-        "-- python3 bench.py --copy-probe-mib 1024",
-        "#   rocprofv3 --pmc WRITE_SIZE -d D/copy_WRITE_SIZE -o copy_WRITE_SIZE --output-format csv "
-        "-- python3 bench.py --copy-probe-mib 1024",
-        "#   python3 bench.py --summarize D",
-        "",
-        "## kernel trace (--kernel-trace --stats), mok kernels, average per dispatch",
-        f"{'kernel':<100} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}",
-    ]
-    for r in stats:
-        if "mok::" not in r["Name"]:
+def _csv(path):
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _per_forward(rows, key_of, value_of):
+    """Per-kernel totals over a run divided by its forwards (one k_plan_scan per forward)."""
+    tot, n = {}, {}
+    for r in rows:
+        k = key_of(r)
+        if k is None:
             continue
-        lines.append(f"{r['Name'][:100]:<100} {r['Calls']:>6} {float(r['AverageNs']) / 1e3:>10.1f} "
-                     f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f}")
-    lines += [
-        "",
-        f"gate/up kernel average (profiler, all {up_stat['Calls']} dispatches): {prof_ms:.4f} ms",
-        f"gate/up kernel average (profiler, the {len(timed)} dispatches of the timed steps): {timed_ms:.4f} ms",
-        f"gate/up kernel average (bench.py HIP events, timed steps of the same run): {ev_ms:.4f} ms",
-        f"agreement (same dispatches): {100 * (ev_ms - timed_ms) / timed_ms:+.1f} %; against the "
-        f"all-dispatch average: {100 * (ev_ms - prof_ms) / prof_ms:+.1f} %",
-        f"bench line of the traced run: ms_per_step {bench_line['ms_per_step']}, value "
-        f"{bench_line['value']} tokens/s, roofline frac {bench_line['roofline']['frac']}",
-        "",
-        "## HBM bytes (--pmc), gate/up kernel, per dispatch",
-        f"FETCH_SIZE KiB: {fetch_kib:.1f} (mean of {n_f} dispatches)",
-        f"WRITE_SIZE KiB: {write_kib:.1f} (mean of {n_w} dispatches)",
-        f"copy calibration: 1 GiB device copy reads FETCH_SIZE {copy_fetch:.1f} KiB, WRITE_SIZE "
-        f"{copy_write:.1f} KiB -> factors {f_fetch:.4f} (fetch), {f_write:.4f} (write)",
-        f"traffic_bytes_per_launch: {traffic}",
-        f"kernel_sources_sha256: {kernel_sources_sha256()}",
+        tot[k] = tot.get(k, 0.0) + value_of(r)
+        n[k] = n.get(k, 0) + 1
+    fwd = n.get("k_plan_scan", 1)
+    return {k: v / fwd for k, v in tot.items()}, {k: v / fwd for k, v in n.items()}
+
+
+def summarize(d: str) -> list:
+    """Write the profiles/ summaries of one workload from a rocprofv3 output directory d:
+      trace.json + trace/    kernel trace + stats of a bench run (its JSON line in trace.json)
+      FETCH_SIZE/ WRITE_SIZE/             counter passes over a short bench run
+      copy_FETCH_SIZE/ copy_WRITE_SIZE/   the same counters over a plain 1 GiB device copy
+      ctr_p1/ ... (optional)  SQ/TCP/TCC counter sets over the expert GEMM stages
+    into profiles/kernels_<wl>.txt (every kernel: time, counter bytes, algorithmic rate),
+    profiles/expert_gemm_up_<wl>.txt (the gate/up launch: time agreement with bench.py's events
+    and the HBM traffic bench.py reports) and, with ctr_p*, expert_gemm_counters_<wl>.txt."""
+    import synth
+    line = json.loads(open(os.path.join(d, "trace.json")).read().strip().splitlines()[-1])
+    wl_name = line["config"]["workload"]
+    wl = synth.WORKLOADS[wl_name]
+    n_routes = line["routed_rows"]
+    elem = ELEM[line["dtype"]]
+    up_key = f"k_expert_stage<{ELEM_NAME[elem]}, gate/up>"
+    name_col = lambda r: kernel_key(r["Kernel_Name"])
+    trace = _csv(os.path.join(d, "trace", "trace_kernel_trace.csv"))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6   # ms
+    t_fwd, calls = _per_forward(trace, name_col, dur)
+
+    def counter(sub, pred=None):
+        rows = _csv(os.path.join(d, sub, f"{sub}_counter_collection.csv"))
+        if pred is not None:
+            vals = [float(r["Counter_Value"]) for r in rows if pred(r["Kernel_Name"])]
+            return sum(vals) / len(vals)
+        return _per_forward(rows, name_col, lambda r: float(r["Counter_Value"]))[0]
+
+    copy_fetch = counter("copy_FETCH_SIZE", lambda n: "copyBuffer" in n)
+    copy_write = counter("copy_WRITE_SIZE", lambda n: "copyBuffer" in n)
+    f_fetch, f_write = (1 << 20) / copy_fetch, (1 << 20) / copy_write   # 1 GiB each way
+    fetch = {k: v * f_fetch * 1024 for k, v in counter("FETCH_SIZE").items()}
+    write = {k: v * f_write * 1024 for k, v in counter("WRITE_SIZE").items()}
+    alg = algorithmic_bytes(wl, n_routes)
+    work = algorithmic_work(wl, n_routes)
+    cmd = (f"--workload {wl_name}")
+    D = f"gpurun_out/prof_{wl_name}"
+    cmds = [
+        f"#   rocprofv3 --kernel-trace --stats -d {D}/trace -o trace --output-format csv -- "
+        f"python3 bench.py --steps 10 --warmup 3 --no-cpu {cmd} > {D}/trace.json",
+        f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'mok::' -d {D}/FETCH_SIZE -o "
+        f"FETCH_SIZE --output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu {cmd}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'mok::' -d {D}/WRITE_SIZE -o "
+        f"WRITE_SIZE --output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu {cmd}",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {D}/copy_FETCH_SIZE -o copy_FETCH_SIZE --output-format "
+        f"csv -- python3 bench.py --copy-probe-mib 1024",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {D}/copy_WRITE_SIZE -o copy_WRITE_SIZE --output-format "
+        f"csv -- python3 bench.py --copy-probe-mib 1024",
+        f"#   python3 bench.py --summarize {D}",
     ]
-    path = profile_path(wl)
+    written = []
+    # ---- every kernel
+    lines = [f"# every libmok kernel of one forward, workload {wl_name} ({line['dtype']}, "
+             f"stage-ordered), per forward", "#", "# commands (from the repository root):"] + cmds + [
+        "#",
+        "# time: kernel durations from the trace, summed per forward (warm-up, timed and the",
+        "#   cold-cache per-stage steps of the traced run together: 'calls' launches each);",
+        "# fetch/write: FETCH_SIZE / WRITE_SIZE summed per forward, scaled by the copy",
+        f"#   calibration (1 GiB copy reads FETCH_SIZE {copy_fetch:.0f} KiB, WRITE_SIZE "
+        f"{copy_write:.0f} KiB: factors {f_fetch:.4f}, {f_write:.4f});",
+        "# alg: the bytes the kernel must move (each operand read once, each result written once)",
+        "#   and alg/time against 8 TB/s; GEMM stages: algorithmic FLOPs/time against the dtype's",
+        "#   dense MFMA peak.",
+        "",
+        f"{'kernel':<36} {'calls':>5} {'time_us':>9} {'fetch_MB':>9} {'write_MB':>9} "
+        f"{'alg_MB':>9} {'alg_GB/s':>9} {'counter_GB/s':>12} {'of_peak':>8}",
+    ]
+    peak = PEAK[ELEM_NAME[elem]]
+    outside = []
+    for k in sorted(t_fwd, key=lambda k: -t_fwd[k]):
+        if calls[k] < 0.5:               # launched once per run (input preparation)
+            outside.append(k)
+            continue
+        t = t_fwd[k]
+        fb, wb = fetch.get(k, 0.0), write.get(k, 0.0)
+        row = f"{k:<36} {calls[k]:>5.1f} {t * 1e3:>9.1f} {fb / 1e6:>9.1f} {wb / 1e6:>9.1f} "
+        a = alg.get(k, alg.get(k.split("<")[0]))
+        if a is not None:
+            row += (f"{a / 1e6:>9.1f} {a / (t * 1e-3) / 1e9:>9.0f} "
+                    f"{(fb + wb) / (t * 1e-3) / 1e9:>12.0f} {a / (t * 1e-3) / HBM_PEAK:>8.3f}")
+        elif k.startswith("k_expert_stage"):
+            f = work["up_flop"] if "gate/up" in k else work["down_flop"]
+            row += (f"{'-':>9} {'-':>9} {(fb + wb) / (t * 1e-3) / 1e9:>12.0f} "
+                    f"{f / (t * 1e-3) / peak:>8.3f}")
+        else:
+            row += f"{'-':>9} {'-':>9} {(fb + wb) / (t * 1e-3) / 1e9:>12.0f} {'-':>8}"
+        lines.append(row)
+    if outside:
+        lines.append(f"(not part of the forward, launched once per run: {', '.join(outside)})")
+    lines += ["", f"bench line of the traced run: ms_per_step {line['ms_per_step']}, value "
+              f"{line['value']} tokens/s, routed rows {n_routes}",
+              f"kernel_sources_sha256: {kernel_sources_sha256()}"]
+    path = os.path.join(ROOT, "profiles", f"kernels_{wl_name}.txt")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    return path
+    written.append(path)
+    # ---- the gate/up launch (roofline kernel): time agreement and traffic per launch
+    ups = sorted((r for r in trace if name_col(r) == up_key), key=lambda r: int(r["Start_Timestamp"]))
+    w, k = line["warmup"], line["steps"]
+    timed = ups[w:w + k]
+    timed_ms = sum(dur(r) for r in timed) / len(timed)
+    all_ms = sum(dur(r) for r in ups) / len(ups)
+    ev_ms = line["stage_ms"]["up"]
+    traffic = int(round(fetch[up_key] + write[up_key]))     # one gate/up launch per forward
+    alg_up = ((wl.E_l * 2 * wl.I + 2 * wl.n_shared * wl.I_shared) * wl.d +
+              (n_routes + wl.T_own) * wl.d) * (1 if wl.dtype == "mxfp8" else 2)
+    lines = [
+        f"# gate/up expert GEMM stage (routed + shared, fused pull gather and SwiGLU), workload {wl_name}",
+        "#", "# commands (from the repository root):"] + cmds + [
+        "",
+        f"gate/up kernel average (profiler, all {len(ups)} dispatches): {all_ms:.4f} ms",
+        f"gate/up kernel average (profiler, the {len(timed)} dispatches of the timed steps): {timed_ms:.4f} ms",
+        f"gate/up kernel average (bench.py HIP events, timed steps of the same run): {ev_ms:.4f} ms",
+        f"agreement (same dispatches): {100 * (ev_ms - timed_ms) / timed_ms:+.1f} %",
+        f"roofline of the traced run: {line['roofline']['achieved']} TFLOP/s, frac "
+        f"{line['roofline']['frac']} of {line['roofline']['peak']} TFLOP/s",
+        "",
+        "## HBM bytes (--pmc), gate/up kernel, per dispatch",
+        f"FETCH_SIZE: {fetch[up_key] / 1e6:.1f} MB, WRITE_SIZE: {write[up_key] / 1e6:.1f} MB (copy-calibrated)",
+        f"algorithmic operand bytes (A rows + weights once): {alg_up / 1e6:.1f} MB; fetch / algorithmic = "
+        f"{fetch[up_key] / alg_up:.2f}",
+        f"traffic_bytes_per_launch: {traffic}",
+        f"kernel_sources_sha256: {kernel_sources_sha256()}",
+    ]
+    path = profile_path(wl_name)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    written.append(path)
+    # ---- optional counter sets over the expert GEMM stages
+    sets = sorted(x for x in os.listdir(d) if x.startswith("ctr_p") and os.path.isdir(os.path.join(d, x)))
+    if sets:
+        acc = {}
+        for sub in sets:
+            for r in _csv(os.path.join(d, sub, f"{sub}_counter_collection.csv")):
+                kk = name_col(r)
+                if kk and kk.startswith("k_expert_stage"):
+                    acc.setdefault((kk, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        lines = [f"# expert GEMM stages, workload {wl_name}: hardware counters, mean per dispatch",
+                 "#", "# commands (from the repository root; one run per counter set):",
+                 f"#   rocprofv3 --pmc <set> --kernel-include-regex k_expert_stage -d {D}/ctr_pN -o "
+                 f"ctr_pN --output-format csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu {cmd}",
+                 f"#   python3 bench.py --summarize {D}", ""]
+        for kk in sorted({a for a, _ in acc}):
+            m = {c: sum(v) / len(v) for (a, c), v in acc.items() if a == kk}
+            lines.append(kk)
+            lines += [f"  {c:<36} {m[c]:>12.4g}" for c in sorted(m)]
+            if "SQ_CYCLES" in m:
+                cyc = m["SQ_CYCLES"] / 32
+                der = []
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                    der.append(("MFMA busy (of 1024 SIMDs x kernel cycles)",
+                                m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc)))
+                if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
+                    der.append(("L2 hit rate", m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])))
+                if "TCP_TCC_READ_REQ_LATENCY_sum" in m and "TCP_TCC_READ_REQ_sum" in m:
+                    der.append(("L2 read latency seen by the L1 (cycles)",
+                                m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"]))
+                if "TCP_PENDING_STALL_CYCLES_sum" in m:
+                    der.append(("L1 stalled on pending L2 data", m["TCP_PENDING_STALL_CYCLES_sum"] / (256 * cyc)))
+                if "SQ_LDS_BANK_CONFLICT" in m and "SQ_ACTIVE_INST_LDS" in m:
+                    der.append(("LDS bank-conflict cycles / LDS-active cycles",
+                                m["SQ_LDS_BANK_CONFLICT"] / m["SQ_ACTIVE_INST_LDS"]))
+                if "SQ_WAIT_INST_ANY" in m and "SQ_WAVE_CYCLES" in m:
+                    der.append(("waves waiting on a dependency", m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"]))
+                lines.append(f"  derived (kernel cycles = SQ_CYCLES / 32 = {cyc:.3g}):")
+                lines += [f"    {a:<48} {v:.3g}" for a, v in der]
+        path = os.path.join(ROOT, "profiles", f"expert_gemm_counters_{wl_name}.txt")
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        written.append(path)
+    return written
 
+
+# ------------------------------------------------------------------ measurement
 
 class HipEvents:
     """hipEvent_t pairs through the HIP runtime (the library records them on its stream).
@@ -184,7 +345,6 @@ class HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = (ctypes.c_void_p * n)()
         for i in range(n):
             h = ctypes.c_void_p()
@@ -196,9 +356,6 @@ class HipEvents:
         assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
         return out.value
 
-    def ptr(self):
-        return ctypes.cast(self.ev, ctypes.c_void_p).value
-
 
 def algorithmic_work(wl, n_routes: int) -> dict:
     I_sh = wl.n_shared * wl.I_shared
@@ -209,15 +366,16 @@ def algorithmic_work(wl, n_routes: int) -> dict:
 
 
 def hbm_stages(wl, n_routes: int, stage_ms: dict, ring: bool) -> dict:
-    """Achieved HBM rate of the memory-bound stages: algorithmic bytes (each operand read once,
-    each result written once) over the stage's HIP-event time, against the 8 TB/s peak.
+    """Achieved HBM rate of the memory-bound stages (cold-cache stage times): algorithmic bytes
+    (each operand read once, each result written once) over the stage's HIP-event time, against
+    8 TB/s.
       plan:    the top-k indices (4 B per route of the pool) read, the local route ids
                (4 B per local route) written;
       combine: per token the shared row and the k route rows read, y written (full layer);
       quant:   every bf16 weight element read (2 B), its E4M3 code and 1/32 of a scale byte
                written (MXFP8);
       gather:  per routed row and own token the bf16 x row read, its codes and scales written
-               (MXFP8, stage-ordered; also holds the device work-list build)."""
+               (MXFP8, stage-ordered; the stage also holds the device work-list build)."""
     eb = 4 if wl.dtype == "fp32" else 2
     routes_pool = wl.T_pool * wl.k
     I_sh = wl.n_shared * wl.I_shared
@@ -240,6 +398,26 @@ def hbm_stages(wl, n_routes: int, stage_ms: dict, ring: bool) -> dict:
     return out
 
 
+def _cpu_info() -> tuple:
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            threads = max(threads, max(blas))
+    except Exception:
+        pass
+    return model, threads
+
+
 def cpu_baseline(wl, inputs_cpu, sample_tokens: int) -> dict:
     """The oracle (as it stands) on the first `sample_tokens` tokens of the workload."""
     import numpy as np
@@ -260,60 +438,26 @@ def cpu_baseline(wl, inputs_cpu, sample_tokens: int) -> dict:
                                  sd=inputs_cpu["sd"], topk_in=(idx, w))
     dt = time.perf_counter() - t0
     assert np.isfinite(out["y_shared"]).all()
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {sample_tokens} of {wl.T_pool} tokens, whole forward "
-                      f"(routing, plan, float64 expert and shared FFNs, combine); {dt:.1f} s"}
+    model, threads = _cpu_info()
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": model,
+            "sample": f"first {sample_tokens} of {wl.T_pool} tokens, whole forward (routing "
+                      f"(C), plan (C), float64 numpy expert and shared FFNs, combine); {dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--ring", action="store_true", help="persistent ring work loop")
-    ap.add_argument("--minibatch", type=int, default=None)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=8192)
-    ap.add_argument("--summarize", default=None, metavar="DIR",
-                    help="write the profiles/ summary from a rocprofv3 output directory and exit")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB (calibrates the HBM "
-                         "byte counters of a profiler run) and exit")
-    args = ap.parse_args()
-    if args.summarize:
-        print(summarize(args.summarize))
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
-              "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
-        sys.exit(2)
-
+def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0") -> dict:
+    """Time `steps` forwards of workload wl after `warmup` (wall clock between device
+    synchronisations; HIP events on the roofline kernel only), then a cold-cache per-stage pass.
+    Returns the JSON fields of one measurement and the inputs (for the CPU baseline)."""
     import torch
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
-        return
-
     import routing_grouped_expert_gemm_amd as mok
-    import synth
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from _layer import gpu_layer, gpu_topk, make_inputs
 
-    wl = synth.WORKLOADS[args.workload or synth.EP1]
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
     inp = make_inputs(wl, dev)
     topk = gpu_topk(inp["logits"], wl.k) if wl.routing == "logits" else None
-    flags = 0 if args.ring else mok.MOK_FLAG_NO_RING
-    layer = gpu_layer(wl, inp, topk=topk, flags=flags, mb=args.minibatch, keep=True)
+    flags = 0 if ring else mok.MOK_FLAG_NO_RING
+    layer = gpu_layer(wl, inp, topk=topk, flags=flags, mb=minibatch, keep=True)
     stream = torch.cuda.current_stream()
     n2 = 2 * mok.MOK_N_STAGES
     UP = mok.MOK_STAGE_UP
@@ -336,67 +480,147 @@ def main():
         layer.args.stage_events = None if table is None else ctypes.cast(table, ctypes.c_void_p).value
         layer.forward(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
-    # timed steps: events only on the gate/up launch (the roofline kernel); the library ties
-    # them to that kernel's dispatch, so they queue no marker on the stream
-    ev_up = HipEvents(2 * args.steps)
+    # timed steps: events only on the roofline launch; the library ties them to that kernel's
+    # dispatch, so they queue no marker on the stream
+    ev_up = HipEvents(2 * steps)
     up_tables = event_table(ev_up, True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(up_tables[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = 1e3 * elapsed / args.steps
+    ms = 1e3 * (time.perf_counter() - t0) / steps
     assert layer.device_error(stream) == 0
-    up_ms = sum(ev_up.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
-    # per-stage times: a separate, untimed pass with every stage event
-    n_stage = min(args.steps, 10)
+    up_ms = sum(ev_up.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)) / steps
+    # per-stage times: a separate, untimed pass with every stage event, each step after a 1 GiB
+    # scratch write (nothing of the previous step stays in the caches)
+    n_stage = min(steps, 10)
     ev_all = HipEvents(n2 * n_stage)
     all_tables = event_table(ev_all, False)
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     for i in range(n_stage):
+        scratch.fill_(i & 0xFF)
         step(all_tables[i])
     torch.cuda.synchronize()
+    del scratch
 
     n_routes = int(layer.inter["offsets"][-1])
     work = algorithmic_work(wl, n_routes)
     stage_ms = {}
     names = ["route", "plan", "quant", "up", "down", "combine", "gather"]
     assert len(names) == mok.MOK_N_STAGES
-    for s, name in enumerate(names):
-        vals = [ev_all.elapsed_ms(n2 * i + 2 * s, n2 * i + 2 * s + 1) for i in range(n_stage)]
+    for s_, name in enumerate(names):
+        vals = [ev_all.elapsed_ms(n2 * i + 2 * s_, n2 * i + 2 * s_ + 1) for i in range(n_stage)]
         stage_ms[name] = sum(vals) / len(vals)
+    stage_ms["up_cold"] = stage_ms["up"]
     stage_ms["up"] = up_ms                      # the timed steps' own measurement
-    up_s = stage_ms["up"] * 1e-3
     peak = PEAK[wl.dtype]
-    achieved = work["up_flop"] / up_s
-    tokens = wl.T_own if not wl.full_layer else wl.T_pool
-    value = tokens / (ms * 1e-3)
-    gemm_s = (stage_ms["up"] + stage_ms["down"]) * 1e-3
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+    if ring:
+        # one persistent launch runs the gate/up and the down tiles (and the MXFP8 row gather)
+        roof_flop = work["up_flop"] + work["down_flop"]
+        kernel = "ring work loop (k_ring: gate/up and down tiles of every minibatch)"
+        gemm_s = up_ms * 1e-3
+    else:
+        roof_flop = work["up_flop"]
+        kernel = "gate/up stage (k_expert_stage up)"
+        gemm_s = (up_ms + stage_ms["down"]) * 1e-3
+    achieved = roof_flop / (up_ms * 1e-3)
+    tokens = wl.T_pool if wl.full_layer else wl.T_own
+    res = {
+        "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4),
         "dtype": {"bf16": "bf16", "mxfp8": "mxfp8", "fp32": "f32"}[wl.dtype],
-        "data": "synthetic (seeded counter-based generator; random-init weights)",
-        "config": {"workload": wl.name, "T_pool": wl.T_pool, "d": wl.d, "E": wl.E, "k": wl.k,
-                   "I": wl.I, "E_local": wl.E_l, "n_shared": wl.n_shared,
+        "config": {"workload": wl.name, "T_pool": wl.T_pool, "T_own": wl.T_own, "d": wl.d,
+                   "E": wl.E, "k": wl.k, "I": wl.I, "E_local": wl.E_l, "n_shared": wl.n_shared,
                    "I_shared": wl.I_shared, "minibatch_rows": layer.args.minibatch_rows,
-                   "work_loop": "ring" if args.ring else "stage-ordered"},
+                   "ring_rows": layer.args.ring_rows if ring else None,
+                   "work_loop": "ring" if ring else "stage-ordered"},
         "routed_rows": n_routes,
         "routed_tflops": round(work["routed_flop"] / (ms * 1e-3) / 1e12, 2),
         "gemm_tflops": round((work["routed_flop"] + work["shared_flop"]) / gemm_s / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": {"bound": "mfma", "kernel": "gate/up stage (k_expert_stage up)",
-                     "achieved": round(achieved / 1e12, 2), "peak": peak / 1e12,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": profiled_traffic(wl.name)},
-        "hbm": hbm_stages(wl, n_routes, stage_ms, args.ring),
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved / 1e12, 2),
+                     "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None if ring else profiled_traffic(wl.name)},
+        "hbm": hbm_stages(wl, n_routes, stage_ms, ring),
     }
+    del layer
+    return res, inp
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help="measure this workload alone (default: the headline and its extras)")
+    ap.add_argument("--ring", action="store_true", help="persistent ring work loop")
+    ap.add_argument("--minibatch", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--summarize", default=None, metavar="DIR",
+                    help="write the profiles/ summaries from a rocprofv3 output directory and exit")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (calibrates the HBM "
+                         "byte counters of a profiler run) and exit")
+    args = ap.parse_args()
+    if args.summarize:
+        for p_ in summarize(args.summarize):
+            print(p_)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the sharding plan is design only", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+        return
+
+    import synth
+    torch.cuda.set_device(0)
+    name = args.workload or synth.EP1
+    wl = synth.WORKLOADS[name]
+    res, inp = measure(wl, args.ring, args.steps, args.warmup, args.minibatch)
+    out = {"metric": METRIC, "value": res["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": res["dtype"],
+           "data": "synthetic (seeded counter-based generator; random-init weights)",
+           "config": res["config"]}
+    for k in ("routed_rows", "routed_tflops", "gemm_tflops", "stage_ms", "roofline", "hbm"):
+        out[k] = res[k]
+    cpu_inp = None
     if not args.no_cpu:
-        import synth as _s  # noqa: F401
         cpu_inp = {k: (v.cpu() if v is not None else None) for k, v in inp.items()}
+    del inp
+    if args.workload is None:
+        torch.cuda.empty_cache()
+        # the same layer with the persistent ring work loop (the library default)
+        r, i2 = measure(wl, True, args.steps, args.warmup, args.minibatch)
+        del i2
+        out["ring"] = {k: r[k] for k in ("value", "ms_per_step", "routed_tflops", "config",
+                                         "stage_ms", "roofline")}
+        torch.cuda.empty_cache()
+        # the MXFP8 share
+        m, i3 = measure(synth.WORKLOADS[synth.EP64_MX], False, args.steps, args.warmup)
+        del i3
+        torch.cuda.empty_cache()
+        out["mxfp8"] = {k: m[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                          "routed_rows", "routed_tflops", "gemm_tflops",
+                                          "stage_ms", "roofline", "hbm")}
+    if cpu_inp is not None:
         out["cpu_baseline"] = cpu_baseline(wl, cpu_inp, min(args.cpu_sample, wl.T_pool))
     print(json.dumps(out))
 

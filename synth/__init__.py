@@ -4,18 +4,20 @@ Both sides of every parity check draw their inputs from here: the CPU oracle and
 path. The module holds none of the layer's arithmetic (no routing, no top-k, no FFN); it
 only turns (seed, stream, flat index) into numbers.
 
-Generator (counter-based, integer-exact on every device):
+Generator (counter-based):
   u32(seed, stream, j, i) = fmix32(fmix32(i XOR key_j) XOR rotl(key_j))  (MurmurHash3's
   32-bit finaliser, used as a hash of the counter i), key_j derived from (seed, stream, j).
-  normal(i) = sum_{j<4} u32(.., j, i) centred and scaled to unit variance (Irwin-Hall with
-  four 32-bit draws: bounded at +-3.46 sigma, kurtosis 2.7; a stand-in for N(0,1)).
-  The sum is an exact integer; the only float steps are one float64 multiply, a float64 ->
-  float32 rounding and, for bf16 tensors, a float32 -> bf16 rounding, all IEEE
-  round-to-nearest-even, so torch on the CPU and torch on the GPU give the same bits.
+  normal(i) = sqrt(-2 ln u_0) cos(2 pi u_1), u_j = (u32(.., j, i) + 1/2) / 2^32 in (0, 1):
+  the Box-Muller transform (its cosine branch), one standard normal per counter, in float64,
+  scaled by sigma and rounded to float32 (then to bf16 for bf16 tensors). The 32-bit draws
+  bound |normal| by sqrt(2 ln 2^33) = 6.8.
+  The hashes are integer-exact on every device; the float64 log and cosine may differ in the
+  last bit between the CPU and the GPU, which moves a float32 result only when it lies within
+  about 2^-29 of a rounding boundary. Parity tests therefore generate each input once and hand
+  the same tensor (copied) to both sides.
 
 Every element is a pure function of its flat index, so any rows of any tensor can be
-regenerated on any device without producing the rest (the oracle side regenerates only
-the rows it samples).
+regenerated without producing the rest.
 """
 from __future__ import annotations
 
@@ -66,8 +68,15 @@ def u32(seed: int, stream: int, j: int, idx: torch.Tensor) -> torch.Tensor:
     return _fmix32(_fmix32(idx ^ k) ^ k2)
 
 
-_IH_CENTRE = 2 * MASK32                   # mean of the sum of four u32
-_IH_SCALE = math.sqrt(3.0) / 4294967296.0  # 1 / std of that sum (to 2^-64 relative)
+_INV_2_32 = 1.0 / 4294967296.0
+
+
+def _normal_of(seed: int, stream: int, idx: torch.Tensor, sigma: float) -> torch.Tensor:
+    """Box-Muller normal of counters idx (int64 tensor): float32, standard deviation sigma."""
+    u0 = (u32(seed, stream, 0, idx).to(torch.float64) + 0.5) * _INV_2_32
+    u1 = (u32(seed, stream, 1, idx).to(torch.float64) + 0.5) * _INV_2_32
+    z = torch.sqrt(-2.0 * torch.log(u0)) * torch.cos((2.0 * math.pi) * u1)
+    return (z * sigma).to(torch.float32)
 
 
 def normal_flat(seed: int, stream: int, start: int, count: int, sigma: float,
@@ -76,11 +85,7 @@ def normal_flat(seed: int, stream: int, start: int, count: int, sigma: float,
     if start < 0 or start + count > (1 << 32):
         raise ValueError("counter range exceeds 2^32")
     idx = torch.arange(start, start + count, dtype=torch.int64, device=device)
-    s = u32(seed, stream, 0, idx)
-    for j in (1, 2, 3):
-        s = s + u32(seed, stream, j, idx)
-    z = (s - _IH_CENTRE).to(torch.float64) * (_IH_SCALE * sigma)
-    return z.to(torch.float32)
+    return _normal_of(seed, stream, idx, sigma)
 
 
 def normal_rows(seed: int, stream: int, n_cols: int, rows, sigma: float, dtype=torch.float32,
@@ -100,12 +105,7 @@ def normal_rows(seed: int, stream: int, n_cols: int, rows, sigma: float, dtype=t
     out = torch.empty((rows.numel(), n_cols), dtype=dtype, device=device)
     cols = torch.arange(n_cols, dtype=torch.int64, device=device)
     for i, r in enumerate(rows.tolist()):
-        idx = r * n_cols + cols
-        s = u32(seed, stream, 0, idx)
-        for j in (1, 2, 3):
-            s = s + u32(seed, stream, j, idx)
-        z = (s - _IH_CENTRE).to(torch.float64) * (_IH_SCALE * sigma)
-        out[i] = z.to(torch.float32).to(dtype)
+        out[i] = _normal_of(seed, stream, r * n_cols + cols, sigma).to(dtype)
     return out
 
 
@@ -162,7 +162,7 @@ class Workload:
 ZIPF_S = 1.1
 # Bias strength for the skewed 384-expert workload, found by bisection on the oracle's own
 # top-k counts (oracle/calibrate_zipf.py) so that local expert 0 receives 4.0x the mean load.
-ZIPF_BETA_EP96 = 0.1143951416015625
+ZIPF_BETA_EP96 = 0.1245574951171875
 
 WORKLOADS = {
     "tiny_fp32_t64_d128_e8_top2": Workload(
@@ -172,16 +172,16 @@ WORKLOADS = {
     "ep1_bf16_t8192_d2048_e64_top6": Workload(
         name="ep1_bf16_t8192_d2048_e64_top6", dtype="bf16", T_pool=8192, d=2048, E=64, k=6,
         I=1408, e0=0, E_l=64, tokens_per_rank=8192, own_begin=0, T_own=8192, n_shared=2,
-        I_shared=1408, routing="router", ring_rows=65536, minibatch_rows=256),
+        I_shared=1408, routing="router", ring_rows=16384, minibatch_rows=256),
     "ep64_share_bf16_pool262144_d7168_e256_top8": Workload(
         name="ep64_share_bf16_pool262144_d7168_e256_top8", dtype="bf16", T_pool=262144,
         d=7168, E=256, k=8, I=2048, e0=0, E_l=4, tokens_per_rank=4096, own_begin=0,
-        T_own=4096, n_shared=1, I_shared=2048, routing="logits", ring_rows=65536,
+        T_own=4096, n_shared=1, I_shared=2048, routing="logits", ring_rows=16384,
         minibatch_rows=512),
     "ep64_share_mxfp8_pool262144_d7168_e256_top8": Workload(
         name="ep64_share_mxfp8_pool262144_d7168_e256_top8", dtype="mxfp8", T_pool=262144,
         d=7168, E=256, k=8, I=2048, e0=0, E_l=4, tokens_per_rank=4096, own_begin=0,
-        T_own=4096, n_shared=1, I_shared=2048, routing="logits", ring_rows=65536,
+        T_own=4096, n_shared=1, I_shared=2048, routing="logits", ring_rows=16384,
         minibatch_rows=512),
     "ep96_zipf_bf16_pool196608_d7168_e384_top8_ring16384": Workload(
         name="ep96_zipf_bf16_pool196608_d7168_e384_top8_ring16384", dtype="bf16",

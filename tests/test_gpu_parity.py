@@ -20,20 +20,22 @@ def _sync():
 
 # --------------------------------------------------------------------- generator parity
 
-def test_seeded_generator_same_bits_on_gpu_and_cpu():
-    wl = synth.WORKLOADS[synth.EP64]
-    rows = torch.tensor([0, 1, 4095, 77777, 262143])
-    g = synth.x_rows(wl, range(262140, 262144), DEV).cpu()
-    c = synth.x_rows(wl, range(262140, 262144))
-    assert torch.equal(g.view(torch.int16), c.view(torch.int16))
-    g = synth.pool_logits_rows(wl, range(0, 64), DEV).cpu()
-    assert torch.equal(g, synth.pool_logits_rows(wl, range(0, 64)))
-    c2 = synth.x_rows(wl, rows)
-    g2 = torch.stack([synth.x_rows(wl, range(r, r + 1), DEV)[0].cpu() for r in rows.tolist()])
-    assert torch.equal(g2.view(torch.int16), c2.view(torch.int16))
+def test_seeded_generator_on_gpu_and_cpu():
+    """The counter hashes are bit-identical on both devices; the Box-Muller normals (float64
+    log and cosine, whose last bit may differ between devices) agree to one float32 ulp and are
+    nearly all identical. Parity tests never rely on this: they copy one tensor to both sides."""
+    idx = torch.arange(0, 1 << 20, dtype=torch.int64)
+    for j in (0, 1):
+        assert torch.equal(synth.u32(0, 1, j, idx.to(DEV)).cpu(), synth.u32(0, 1, j, idx))
+    g = synth.normal_flat(0, 1, 0, 1 << 20, 1.0, DEV).cpu()
+    c = synth.normal_flat(0, 1, 0, 1 << 20, 1.0)
+    diff = (g.view(torch.int32).long() - c.view(torch.int32).long()).abs()
+    assert int(diff.max()) <= 1
+    assert float((diff == 0).double().mean()) > 0.9999
     wz = synth.WORKLOADS[synth.EP96]
-    assert torch.equal(synth.pool_logits_rows(wz, range(100, 110), DEV).cpu(),
-                       synth.pool_logits_rows(wz, range(100, 110)))
+    a = synth.pool_logits_rows(wz, range(100, 110), DEV).cpu()
+    b = synth.pool_logits_rows(wz, range(100, 110))
+    assert float((a - b).abs().max()) <= 1e-6
 
 
 # --------------------------------------------------------------------- routing
