@@ -167,6 +167,8 @@ def summarize(d: str) -> list:
     and the HBM traffic bench.py reports) and, with ctr_p*, expert_gemm_counters_<wl>.txt."""
     import synth
     line = json.loads(open(os.path.join(d, "trace.json")).read().strip().splitlines()[-1])
+    if line.get("mode") == "dispatch":
+        return [summarize_dispatch(d, line)]
     wl_name = line["config"]["workload"]
     wl = synth.WORKLOADS[wl_name]
     n_routes = line["routed_rows"]
@@ -328,6 +330,72 @@ def summarize(d: str) -> list:
             fh.write("\n".join(lines) + "\n")
         written.append(path)
     return written
+
+
+def summarize_dispatch(d: str, line: dict) -> str:
+    """profiles/kernels_dispatch_<wl>.txt: the pull gather and the push baseline (and the plan
+    the pull needs), per step, with copy-calibrated counter bytes."""
+    import synth
+    wl = synth.WORKLOADS[line["workload"]]
+    n, row = line["routed_rows"], line["row_bytes"]
+    name_col = lambda r: kernel_key(r["Kernel_Name"])
+    trace = _csv(os.path.join(d, "trace", "trace_kernel_trace.csv"))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6
+    t_step, calls = _per_forward(trace, name_col, dur)
+
+    def counter(sub, pred=None):
+        rows = _csv(os.path.join(d, sub, f"{sub}_counter_collection.csv"))
+        if pred is not None:
+            vals = [float(r["Counter_Value"]) for r in rows if pred(r["Kernel_Name"])]
+            return sum(vals) / len(vals)
+        return _per_forward(rows, name_col, lambda r: float(r["Counter_Value"]))[0]
+
+    copy_fetch = counter("copy_FETCH_SIZE", lambda n_: "copyBuffer" in n_)
+    copy_write = counter("copy_WRITE_SIZE", lambda n_: "copyBuffer" in n_)
+    f_fetch, f_write = (1 << 20) / copy_fetch, (1 << 20) / copy_write
+    fetch = {k: v * f_fetch * 1024 for k, v in counter("FETCH_SIZE").items()}
+    write = {k: v * f_write * 1024 for k, v in counter("WRITE_SIZE").items()}
+    routes = wl.T_pool * wl.k
+    alg = {"k_pull_gather": 2 * n * row + 4 * n, "k_push_dispatch": 2 * n * row + 4 * routes + 4 * n,
+           "k_plan_count": 4 * routes, "k_plan_scatter": 4 * routes + 4 * n}
+    D = f"gpurun_out/prof_dispatch"
+    lines = [f"# pull gather against the push-dispatch baseline, {wl.name} routing "
+             f"({n} local routes of {routes}, rows of {row} B), per step",
+             "#", "# commands (from the repository root):",
+             f"#   rocprofv3 --kernel-trace --stats -d {D}/trace -o trace --output-format csv -- "
+             f"python3 bench.py --dispatch --steps 10 --warmup 3 > {D}/trace.json",
+             f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'mok::' -d {D}/FETCH_SIZE -o "
+             f"FETCH_SIZE --output-format csv -- python3 bench.py --dispatch --steps 2 --warmup 1",
+             f"#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'mok::' -d {D}/WRITE_SIZE -o "
+             f"WRITE_SIZE --output-format csv -- python3 bench.py --dispatch --steps 2 --warmup 1",
+             f"#   (copy calibration: the copy-probe passes of the layer profiles, copied here)",
+             f"#   python3 bench.py --summarize {D}", "#",
+             f"# calibration: 1 GiB copy reads FETCH_SIZE {copy_fetch:.0f} KiB, WRITE_SIZE "
+             f"{copy_write:.0f} KiB (factors {f_fetch:.4f}, {f_write:.4f})",
+             "# alg: row bytes read + written once and the index bytes each kernel must touch", "",
+             f"{'kernel':<20} {'calls':>5} {'time_us':>9} {'fetch_MB':>9} {'write_MB':>9} "
+             f"{'alg_MB':>9} {'alg_GB/s':>9} {'counter_GB/s':>12} {'of_8TB/s':>9}"]
+    for k in sorted(t_step, key=lambda k: -t_step[k]):
+        if k not in alg and not k.startswith("k_plan"):
+            continue
+        t = t_step[k]
+        fb, wb = fetch.get(k, 0.0), write.get(k, 0.0)
+        row_s = f"{k:<20} {calls[k]:>5.1f} {t * 1e3:>9.1f} {fb / 1e6:>9.1f} {wb / 1e6:>9.1f} "
+        if k in alg:
+            a = alg[k]
+            row_s += (f"{a / 1e6:>9.1f} {a / (t * 1e-3) / 1e9:>9.0f} {(fb + wb) / (t * 1e-3) / 1e9:>12.0f} "
+                      f"{a / (t * 1e-3) / HBM_PEAK:>9.3f}")
+        else:
+            row_s += f"{'-':>9} {'-':>9} {(fb + wb) / (t * 1e-3) / 1e9:>12.0f} {'-':>9}"
+        lines.append(row_s)
+    lines += ["", "bench line of the traced run (cold-cache HIP-event times): "
+              f"pull_gather {line['pull_gather']}, push_dispatch {line['push_dispatch']}, "
+              f"plan {line['plan']}; push slot order identical in two runs: "
+              f"{line['push_slot_order_same_in_two_runs']}"]
+    path = os.path.join(ROOT, "profiles", f"kernels_dispatch_{wl.name}.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 # ------------------------------------------------------------------ measurement
@@ -550,6 +618,74 @@ def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0
     return res, inp
 
 
+def measure_dispatch(steps: int, warmup: int, dev="cuda:0") -> dict:
+    """Pull (plan + gather in plan order) against push (atomic-slot scatter) on the EP=64 share's
+    routing: 262144 pool rows of d = 7168 bf16, top-8 of 256 experts, 4 local experts. Both
+    move the same rows into expert-contiguous buffers; times are HIP events on the stream,
+    averaged over `steps` after `warmup`, each step after a 1 GiB scratch write."""
+    import torch
+    import routing_grouped_expert_gemm_amd as mok
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _layer import gpu_topk
+    wl = synth.WORKLOADS[synth.EP64]
+    T, d, k, E_l = wl.T_pool, wl.d, wl.k, wl.E_l
+    x = synth.x_rows(wl, range(T), dev)
+    idx, _ = gpu_topk(synth.pool_logits_rows(wl, range(T), dev), k)
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts, offsets = torch.empty(E_l, **i32), torch.empty(E_l + 1, **i32)
+    rank_counts = torch.empty((E_l, wl.n_ranks), **i32)
+    route_ids = torch.empty(T * min(k, E_l), **i32)
+    ws = torch.empty(mok.mok_dispatch_plan_workspace_bytes(T, k, E_l), dtype=torch.uint8, device=dev)
+    pull_buf = torch.empty((T * min(k, E_l), d), dtype=x.dtype, device=dev)
+    cap = T                                   # a token picks an expert at most once: no drops
+    fill = torch.empty(E_l, **i32)
+    push_buf = torch.empty((E_l, cap, d), dtype=x.dtype, device=dev)
+    src = torch.empty((E_l, cap), **i32)
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def plan():
+        mok.mok_dispatch_plan(idx, wl.E, wl.e0, E_l, wl.tokens_per_rank, counts, offsets,
+                              rank_counts, route_ids, ws)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    t = {"plan": 0.0, "pull_gather": 0.0, "push_dispatch": 0.0}
+    orders = []
+    for i in range(warmup + steps):
+        e = [ev() for _ in range(6)]
+        scratch.fill_(i & 0xFF)
+        e[0].record(); plan(); e[1].record()
+        scratch.fill_((i + 1) & 0xFF)
+        e[2].record(); mok.mok_pull_gather(x, k, route_ids, offsets, pull_buf); e[3].record()
+        scratch.fill_((i + 2) & 0xFF)
+        e[4].record(); mok.mok_push_dispatch(x, idx, wl.e0, fill, push_buf, src); e[5].record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            t["plan"] += e[0].elapsed_time(e[1]) / steps
+            t["pull_gather"] += e[2].elapsed_time(e[3]) / steps
+            t["push_dispatch"] += e[4].elapsed_time(e[5]) / steps
+        if i >= warmup + steps - 2:
+            orders.append(src[0, :int(fill[0])].clone())
+    n = int(offsets[-1])
+    assert torch.equal(fill.cpu(), counts.cpu())
+    row = d * x.element_size()
+    moved = 2 * n * row                       # every local route's row read once, written once
+    same = bool(torch.equal(orders[0], orders[1]))
+    res = {"workload": wl.name, "routed_rows": n, "row_bytes": row,
+           "rows_bytes_moved": moved, "unit": "GB/s"}
+    for name, ms in t.items():
+        res[name] = {"ms": round(ms, 4)}
+    for name in ("pull_gather", "push_dispatch"):
+        gbs = moved / (t[name] * 1e-3) / 1e9
+        res[name].update(achieved=round(gbs, 1), frac=round(gbs * 1e9 / HBM_PEAK, 4))
+    pull_total = t["plan"] + t["pull_gather"]
+    res["pull_with_plan"] = {"ms": round(pull_total, 4),
+                             "achieved": round(moved / (pull_total * 1e-3) / 1e9, 1)}
+    res["push_over_pull_time"] = round(t["push_dispatch"] / t["pull_gather"], 3)
+    res["push_slot_order_same_in_two_runs"] = same
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -563,6 +699,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=8192)
     ap.add_argument("--summarize", default=None, metavar="DIR",
                     help="write the profiles/ summaries from a rocprofv3 output directory and exit")
+    ap.add_argument("--dispatch", action="store_true",
+                    help="only the pull-versus-push dispatch comparison (one JSON line)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -590,6 +728,10 @@ def main():
 
     import synth
     torch.cuda.set_device(0)
+    if args.dispatch:
+        print(json.dumps({"mode": "dispatch", "steps": args.steps, "warmup": args.warmup,
+                          **measure_dispatch(args.steps, args.warmup)}))
+        return
     name = args.workload or synth.EP1
     wl = synth.WORKLOADS[name]
     res, inp = measure(wl, args.ring, args.steps, args.warmup, args.minibatch)
@@ -620,6 +762,9 @@ def main():
         out["mxfp8"] = {k: m[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                           "routed_rows", "routed_tflops", "gemm_tflops",
                                           "stage_ms", "roofline", "hbm")}
+        # pull gather against the push baseline on the EP=64 share's routing
+        out["dispatch"] = measure_dispatch(min(args.steps, 10), min(args.warmup, 3))
+        torch.cuda.empty_cache()
     if cpu_inp is not None:
         out["cpu_baseline"] = cpu_baseline(wl, cpu_inp, min(args.cpu_sample, wl.T_pool))
     print(json.dumps(out))

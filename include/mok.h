@@ -243,6 +243,31 @@ int mok_moe_forward(const mok_moe_args* args, void* stream);
 int mok_moe_workspace_region(const mok_moe_args* args, int32_t region, size_t* offset,
                              size_t* bytes, int64_t* rows);
 
+/* ---------------------------------------------------------------- pull vs push dispatch
+ * Two ways to bring each local expert its token rows, measured side by side (the Telegram post
+ * on MoK, "Method and experiments": pushing needs a contended slot counter per expert and
+ * scattered writes; pulling lets each expert read its tokens in large contiguous pieces; the
+ * MoK write-up, "Choosing the right communication direction", pulls for dispatch). The layer
+ * itself pulls inside its gate/up GEMM; these entry points copy the rows on their own.
+ *
+ * mok_pull_gather: buf row i = x[route_ids[i] / k] for i < offsets[E_l], the plan of
+ *   mok_dispatch_plan (route_ids, offsets: device). x [T_pool, d] FP32 or BF16 (io_dtype);
+ *   buf [T_pool * min(k, E_l), d] capacity, rows past offsets[E_l] untouched. Deterministic.
+ * mok_push_dispatch: no plan. Every route r = t*k + j whose expert e = topk_idx[r] is local
+ *   (e0 <= e < e0 + E_l) takes the next slot s of its expert with an atomic add on fill[e - e0]
+ *   and writes buf[(e - e0) * capacity + s] = x[t] and src_route[(e - e0) * capacity + s] = r.
+ *   fill [E_l] int32 is cleared by the call (no memset: a kernel) and ends as the number of
+ *   local routes of each expert; slots >= capacity are not written (fill > capacity tells the
+ *   caller routes were dropped). buf [E_l, capacity, d], src_route [E_l, capacity]. The set of
+ *   rows per expert is determined; their order within an expert is not (it follows atomic
+ *   arrival). Requires d * element size % 16 == 0. */
+int mok_pull_gather(const void* x, int64_t T_pool, int32_t d, int32_t k, int32_t io_dtype,
+                    const int32_t* route_ids, const int32_t* offsets, int32_t E_l, void* buf,
+                    void* stream);
+int mok_push_dispatch(const void* x, int64_t T_pool, int32_t d, int32_t k, int32_t io_dtype,
+                      const int32_t* topk_idx, int32_t e0, int32_t E_l, int64_t capacity,
+                      int32_t* fill, void* buf, int32_t* src_route, void* stream);
+
 /* ---------------------------------------------------------------- MXFP8 quantiser
  * OCP MX v1.0 MXFP8 along rows: src [rows, K] bf16 (device), K % 32 == 0.
  *   codes  [rows, K]      E4M3 ("FN": bias 7, max 448, no infinities) bytes

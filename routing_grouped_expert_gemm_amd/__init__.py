@@ -31,7 +31,8 @@ MOK_DEVERR_OVERFLOW, MOK_DEVERR_WAIT = 1, 2
 EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
            "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_dispatch_plan_noalloc",
            "mok_moe_workspace_bytes",
-           "mok_moe_forward", "mok_moe_workspace_region", "mok_quantize_mxfp8",
+           "mok_moe_forward", "mok_moe_workspace_region", "mok_pull_gather",
+           "mok_push_dispatch", "mok_quantize_mxfp8",
            "mok_get_device_error"]
 
 
@@ -84,6 +85,9 @@ _lib.mok_moe_forward.argtypes = [ctypes.POINTER(MoeArgs), _P]
 _lib.mok_moe_workspace_region.argtypes = [ctypes.POINTER(MoeArgs), _I32, ctypes.POINTER(_SZ),
                                           ctypes.POINTER(_SZ), ctypes.POINTER(_I64)]
 _lib.mok_quantize_mxfp8.argtypes = [_P, _I64, _I32, _P, _P, _P]
+_lib.mok_pull_gather.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _I32, _P, _P]
+_lib.mok_push_dispatch.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _I32, _I32, _I64, _P, _P, _P,
+                                   _P]
 _lib.mok_get_device_error.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), _P]
 for _n in EXPORTS:
     if _n not in ("mok_status_string", "mok_version"):
@@ -176,6 +180,29 @@ def mok_moe_workspace_region(args: MoeArgs, region: int):
            _lib.mok_moe_workspace_region(ctypes.byref(args), region, ctypes.byref(off),
                                          ctypes.byref(n), ctypes.byref(rows)))
     return off.value, n.value, rows.value
+
+
+def _io(x):
+    import torch
+    return MOK_FP32 if x.dtype == torch.float32 else MOK_BF16
+
+
+def mok_pull_gather(x, k: int, route_ids, offsets, buf, stream=None) -> None:
+    """buf[i] = x[route_ids[i] // k] for the plan's rows (E_l = offsets.numel() - 1)."""
+    T, d = x.shape
+    _check("mok_pull_gather", _lib.mok_pull_gather(_ptr(x), T, d, k, _io(x), _ptr(route_ids),
+                                                   _ptr(offsets), offsets.numel() - 1,
+                                                   _ptr(buf), _stream(stream)))
+
+
+def mok_push_dispatch(x, topk_idx, e0: int, fill, buf, src_route, stream=None) -> None:
+    """Atomic-slot push of every local route's row into buf [E_l, capacity, d]."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    E_l, cap = buf.shape[0], buf.shape[1]
+    _check("mok_push_dispatch",
+           _lib.mok_push_dispatch(_ptr(x), T, d, k, _io(x), _ptr(topk_idx), e0, E_l, cap,
+                                  _ptr(fill), _ptr(buf), _ptr(src_route), _stream(stream)))
 
 
 def mok_quantize_mxfp8(src_bf16, codes, scales, stream=None) -> None:

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmok.so")
-SOURCES = ["route.hip", "plan.hip", "quant.hip", "expert_gemm.hip", "api.hip", "noalloc.hip"]
+SOURCES = ["route.hip", "plan.hip", "quant.hip", "expert_gemm.hip", "api.hip", "noalloc.hip",
+           "dispatch.hip"]
 HEADERS = ["device_common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -108,4 +108,12 @@ hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, in
                           int k, int d, bool f32, hipStream_t s, hipEvent_t e0 = nullptr,
                           hipEvent_t e1 = nullptr);
 
+// Standalone dispatch (dispatch.hip): pull gather of the plan's rows, push baseline.
+hipError_t launch_pull_gather(const void* x, int d, int es, int k, const int32_t* route_ids,
+                              const int32_t* offsets, int E_l, int64_t cap_rows, void* buf,
+                              hipStream_t s);
+hipError_t launch_push_dispatch(const void* x, int d, int es, const int32_t* topk_idx,
+                                int64_t T_pool, int k, int e0, int E_l, int64_t cap,
+                                int32_t* fill, void* buf, int32_t* src, hipStream_t s);
+
 }  // namespace mok
