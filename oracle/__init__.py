@@ -60,6 +60,14 @@ def lib():
         L.orc_mx_shared_exponent.restype = i32
         L.orc_mxfp8_quantize.argtypes = [P, i64, i32, P, P]
         L.orc_mxfp8_dequantize.argtypes = [P, P, i64, i32, P]
+        L.orc_e2m1_encode.argtypes = [ctypes.c_float, i32]
+        L.orc_e2m1_encode.restype = ctypes.c_uint8
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_decode.restype = ctypes.c_float
+        L.orc_mx4_shared_exponent.argtypes = [ctypes.c_float]
+        L.orc_mx4_shared_exponent.restype = i32
+        L.orc_mxfp4_quantize.argtypes = [P, i64, i32, P, P]
+        L.orc_mxfp4_dequantize.argtypes = [P, P, i64, i32, P]
         _lib = L
     return _lib
 
@@ -145,23 +153,57 @@ def mx_roundtrip(v) -> np.ndarray:
     return mxfp8_dequantize(*mxfp8_quantize(v))
 
 
+def mxfp4_quantize(v):
+    """OCP MXFP4 along the last axis: (codes uint8 [...,K/2], element 2i in the low nibble of
+    byte i; scales uint8 [...,K/32]) (C)."""
+    a = _f32(v)
+    K = a.shape[-1]
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    rows = a.size // K
+    codes = np.empty(a.shape[:-1] + (K // 2,), np.uint8)
+    scales = np.empty(a.shape[:-1] + (K // 32,), np.uint8)
+    lib().orc_mxfp4_quantize(_p(a), rows, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mxfp4_dequantize(codes, scales) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    K = codes.shape[-1] * 2
+    out = np.empty(codes.shape[:-1] + (K,), np.float32)
+    lib().orc_mxfp4_dequantize(_p(codes), _p(scales), codes.size * 2 // K, K, _p(out))
+    return out
+
+
+def mx4_roundtrip(v) -> np.ndarray:
+    """The value an MXFP4 operand carries: dequantize(quantize(v))."""
+    return mxfp4_dequantize(*mxfp4_quantize(v))
+
+
 # ------------------------------------------------------------------------ expert FFN
 
 def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_ffn(a, w_gate, w_up, w_down, mx_hidden: bool = False) -> np.ndarray:
+def _mx_fn(mx):
+    """The round trip of an MX operand format: MXFP8 (mx True or "mxfp8") or MXFP4."""
+    return mx4_roundtrip if mx == "mxfp4" else mx_roundtrip
+
+
+def swiglu_ffn(a, w_gate, w_up, w_down, mx_hidden=False) -> np.ndarray:
     """FFN(a) = W_down (silu(W_gate a) * (W_up a)) for the rows of a, in float64.
 
     w_gate, w_up: [I, d]; w_down: [d, I] (nn.Linear [out, in] layout). mx_hidden: the hidden
-    activation is an MXFP8 operand of the down projection (blocks of 32 along I)."""
+    activation is an MX operand of the down projection (blocks of 32 along I): True or
+    "mxfp8" for MXFP8, "mxfp4" for MXFP4."""
     a = np.asarray(a, np.float64)
     g = a @ np.asarray(w_gate, np.float64).T
     u = a @ np.asarray(w_up, np.float64).T
     h = silu(g) * u
     if mx_hidden:
-        h = mx_roundtrip(h.astype(np.float32)).astype(np.float64)
+        h = _mx_fn(mx_hidden)(h.astype(np.float32)).astype(np.float64)
     return h @ np.asarray(w_down, np.float64).T
 
 
@@ -176,13 +218,14 @@ def shared_ffn(a, s_gate, s_up, s_down, mx_hidden: bool = False) -> np.ndarray:
 
 # ------------------------------------------------------------------------ the layer
 
-def _operand(v, mx: bool) -> np.ndarray:
-    """Operand values as the GEMMs see them: exact float32 upcast, or the MXFP8 round trip."""
+def _operand(v, mx) -> np.ndarray:
+    """Operand values as the GEMMs see them: exact float32 upcast, or the MX round trip (mx True
+    or "mxfp8": MXFP8; "mxfp4": MXFP4)."""
     v = _f32(v)
-    return mx_roundtrip(v) if mx else v
+    return _mx_fn(mx)(v) if mx else v
 
 
-def route_outputs(routes, x_rows, topk_idx, topk_w, e0, wg, wu, wd, mx: bool = False):
+def route_outputs(routes, x_rows, topk_idx, topk_w, e0, wg, wu, wd, mx=False):
     """P[r] = w[t,j] * FFN_{idx[t,j]}(x[t]) for routes r = t*k+j (x_rows[i] = x[t of routes[i]]).
 
     Returns float64 [len(routes), d]."""
@@ -210,7 +253,7 @@ def moe_forward(wl, x, w_router=None, logits=None, wg=None, wu=None, wd=None, sg
 
     Returns idx, w, plan, P (float64 [n_local_routes, d], row i for plan route_ids[i]),
     y_shared (float64 [T_own, d]) and y (float64 [T_pool, d] or None)."""
-    mx = wl.dtype == "mxfp8"
+    mx = wl.dtype if wl.dtype in ("mxfp8", "mxfp4") else False
     if topk_in is not None:
         idx, w = topk_in
     else:

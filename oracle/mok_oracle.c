@@ -201,3 +201,83 @@ void orc_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t r
       out[r * K + i] = (float)ldexp((double)orc_e4m3_decode(codes[r * K + i]), s);
     }
 }
+
+/* ------------------------------------------------------------------ MXFP4 (OCP MX v1.0)
+ * Element type E2M1 (FP4: sign, 2 exponent bits with bias 1, 1 mantissa bit; no infinities or
+ * NaN). Its finite magnitudes are 0, 0.5 (the one subnormal), 1, 1.5, 2, 3, 4, 6; the largest
+ * normal is 6 = 1.5 * 2^2, so the element's emax is 2. One E8M0 scale per block of 32 along K.
+ * Shared exponent s = floor(log2(amax)) - 2, clamped to [-127, 127]; amax == 0 gives -127.
+ * Element: a = |v| * 2^-s, rounded to the nearest E2M1 magnitude (a tie goes to the one with an
+ * even mantissa bit), then saturated to 6; the sign is kept (-0 encodes as 0x8).
+ * The MX format names the scale and the elements; how two 4-bit codes share a byte is a
+ * storage choice: here element 2i is the low nibble of byte i and element 2i+1 the high one. */
+
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* Nearest magnitude by exhaustive search over the 8 codes; ties to the even code (the even
+ * codes are the ones whose mantissa bit is 0). */
+static int e2m1_encode_mag(double a) {
+  if (a >= 6.0) return 7;
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    double dc = fabs(kE2M1[c] - a), db = fabs(kE2M1[best] - a);
+    if (dc < db || (dc == db && (c & 1) == 0 && (best & 1) == 1)) best = c;
+  }
+  return best;
+}
+
+uint8_t orc_e2m1_encode(float v, int32_t s) {
+  double a = fabs((double)v) * ldexp(1.0, -s);
+  return (uint8_t)((signbit(v) ? 0x8 : 0) | e2m1_encode_mag(a));
+}
+
+float orc_e2m1_decode(uint8_t code) {
+  double m = kE2M1[code & 7];
+  return (float)((code & 8) ? -m : m);
+}
+
+int32_t orc_mx4_shared_exponent(float amax) {
+  if (amax == 0.0f) return -127;
+  int ex;
+  frexp((double)amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+  int s = (ex - 1) - 2;
+  if (s < -127) s = -127;
+  if (s > 127) s = 127;
+  return s;
+}
+
+/* codes [rows, K/2] (two elements a byte, as above), scales [rows, K/32] */
+void orc_mxfp4_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                        uint8_t* scales) {
+  const int32_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t b = 0; b < nb; ++b) {
+      const float* v = src + r * K + (int64_t)b * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+      }
+      int32_t s = orc_mx4_shared_exponent(amax);
+      scales[r * nb + b] = (uint8_t)(s + 127);
+      for (int i = 0; i < 32; i += 2) {
+        uint8_t lo = orc_e2m1_encode(v[i], s), hi = orc_e2m1_encode(v[i + 1], s);
+        codes[r * (K / 2) + ((int64_t)b * 32 + i) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
+void orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t K,
+                          float* out) {
+  const int32_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int32_t i = 0; i < K; ++i) {
+      int s = (int)scales[r * nb + i / 32] - 127;
+      uint8_t byte = codes[r * (K / 2) + i / 2];
+      uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);
+      out[r * K + i] = (float)ldexp((double)orc_e2m1_decode(c), s);
+    }
+}

@@ -375,3 +375,93 @@ def test_mx_layer_uses_dequantised_operands():
     h = oracle.mx_roundtrip(h.astype(np.float32)).astype(np.float64)
     ref = float(out["w"].reshape(-1)[r]) * (h @ rt(wd[e]).T)
     np.testing.assert_allclose(out["P"][0], ref[0], rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------- MXFP4 (OCP MX v1.0, E2M1)
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def test_e2m1_known_codes():
+    """Values worked out by hand from the E2M1 grid (0, 0.5, 1, 1.5, 2, 3, 4, 6): midpoints go
+    to the code with the even mantissa bit, everything past 6 saturates, the sign is bit 3."""
+    L = oracle.lib()
+    cases = [(0.0, 0), (0.24, 0), (0.25, 0), (0.26, 1), (0.5, 1), (0.74, 1), (0.75, 2),
+             (1.0, 2), (1.25, 2), (1.26, 3), (1.5, 3), (1.75, 4), (2.5, 4), (2.51, 5), (3.0, 5),
+             (3.5, 6), (4.0, 6), (5.0, 6), (5.01, 7), (6.0, 7), (7.99, 7), (1e9, 7)]
+    for v, c in cases:
+        assert L.orc_e2m1_encode(v, 0) == c, (v, L.orc_e2m1_encode(v, 0), c)
+        assert L.orc_e2m1_encode(-v, 0) == (c | 8), v
+        assert L.orc_e2m1_encode(v * 2.0 ** 5, 5) == c, v        # the scale is exact
+    for c in range(16):
+        assert L.orc_e2m1_decode(c) == (-1 if c & 8 else 1) * E2M1[c & 7]
+
+
+def test_e2m1_encode_exhaustive_vs_nearest_search():
+    """Every finite bf16 value (sampled) times 2^-s for s in [-20, 20] against a numpy nearest
+    search over the 8 magnitudes, ties to the even code, saturation at 6."""
+    L = oracle.lib()
+    vals = _bf16_all_finite()
+    rng = np.random.default_rng(15)
+    sub = np.concatenate([vals[::53], rng.choice(vals, 2000, replace=False)])
+    for s in range(-20, 21):
+        a = np.abs(sub.astype(np.float64)) * 2.0 ** -s
+        dist = np.abs(a[:, None] - E2M1[None, :])
+        cand = dist == dist.min(1, keepdims=True)
+        codes = np.where(cand.sum(1) > 1, np.argmax(cand & (np.arange(8)[None, :] % 2 == 0), 1),
+                         np.argmin(dist, 1))
+        codes = np.where(a >= 6.0, 7, codes)
+        for v, c in zip(sub, codes):
+            got = L.orc_e2m1_encode(float(v), s)
+            assert got & 7 == c and (got >> 3) == (1 if math.copysign(1, v) < 0 else 0), (v, s)
+
+
+def test_mxfp4_scale_packing_and_grid_round_trip():
+    """Shared exponent = floor(log2 amax) - 2 from the float's exponent field; element 2i in the
+    low nibble of byte i; E2M1 grid values times 2^s round-trip exactly."""
+    L = oracle.lib()
+    vals = _bf16_all_finite()
+    vals = vals[(vals != 0) & (np.abs(vals) >= 2 ** -126)]
+    exp_field = ((vals.view(np.uint32) >> 23) & 0xFF).astype(np.int64) - 127
+    for v, e in zip(vals[::97], exp_field[::97]):
+        assert L.orc_mx4_shared_exponent(abs(float(v))) == max(-127, min(127, e - 2))
+    v = np.zeros((1, 32), np.float32)
+    v[0, 0], v[0, 1], v[0, 2], v[0, 31] = 1.0, -6.0, 0.5, 3.0      # amax 6 -> s = 0
+    codes, scales = oracle.mxfp4_quantize(v)
+    assert scales[0, 0] == 127 and codes.shape == (1, 16)
+    assert codes[0, 0] == (0x2 | (0xF << 4)) and codes[0, 1] == 0x1 and codes[0, 15] == (0x5 << 4)
+    rng = np.random.default_rng(16)
+    for s in (-30, -4, 0, 7):
+        blk = rng.choice(E2M1, (64, 32)) * rng.choice([-1, 1], (64, 32))
+        blk[:, 0] = 6.0
+        x = (blk * 2.0 ** s).astype(np.float32)
+        c, sc = oracle.mxfp4_quantize(x)
+        assert (sc == s + 127).all()
+        assert np.array_equal(oracle.mxfp4_dequantize(c, sc), x)
+
+
+def test_mxfp4_quantize_error_bound():
+    """|q - v| <= max(|v| / 3, amax / 16) per block: half a step (a quarter of the binade) for
+    normals, a quarter of 2^s for the subnormal step, and saturation [6, 8) * 2^s."""
+    rng = np.random.default_rng(17)
+    v = rng.standard_normal((50, 256)).astype(np.float32)
+    q = oracle.mx4_roundtrip(v)
+    blk_max = np.abs(v.reshape(50, 8, 32)).max(2, keepdims=True)
+    err = np.abs(q - v).reshape(50, 8, 32)
+    assert (err <= np.maximum(np.abs(v).reshape(50, 8, 32) / 3, blk_max / 16) + 1e-12).all()
+
+
+def test_mxfp4_layer_uses_dequantised_operands():
+    wl, x, wr, wg, wu, wd, sg, su, sd = _tiny_layer(d=64, I=64, I_s=64, dtype="mxfp4")
+    out = oracle.moe_forward(wl, x, w_router=wr, wg=wg, wu=wu, wd=wd, sg=sg, su=su, sd=sd)
+    rt = lambda t: oracle.mx4_roundtrip(t.float().numpy()).astype(np.float64)
+    r = int(out["plan"]["route_ids"][0])
+    t, e = r // wl.k, int(out["idx"].reshape(-1)[r])
+    h = oracle.silu(rt(x[t:t + 1]) @ rt(wg[e]).T) * (rt(x[t:t + 1]) @ rt(wu[e]).T)
+    h = oracle.mx4_roundtrip(h.astype(np.float32)).astype(np.float64)
+    ref = float(out["w"].reshape(-1)[r]) * (h @ rt(wd[e]).T)
+    np.testing.assert_allclose(out["P"][0], ref[0], rtol=1e-12, atol=1e-12)
+    # MXFP4 differs from MXFP8 (a coarser grid): the two layers do not coincide
+    out8 = oracle.moe_forward(synth.scaled(wl, dtype="mxfp8"), x, w_router=wr, wg=wg, wu=wu,
+                              wd=wd, sg=sg, su=su, sd=sd)
+    assert np.abs(out["y"] - out8["y"]).max() > 1e-3
