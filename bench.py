@@ -11,6 +11,8 @@ Default run: the headline is the EP=1 bf16 layer (T=8192, d=2048, 64 experts, to
 stage-ordered expert launches; the same line carries
   "ring":  that layer with the persistent ring work loop (the library default), and
   "mxfp8": the MXFP8 EP=64 share (262144-row pool, d=7168, 4 local experts + 1 shared),
+  "mxfp4": the same share with MXFP4 operands, and
+  "dispatch": pull gather against the push baseline on that share's routing,
 each timed the same way (W warm-up steps, K timed steps between device synchronisations).
 --workload NAME measures that workload alone (used by the profiling runs).
 
@@ -51,7 +53,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer fwd tokens/s + routed-expert TFLOP/s on 1 MI355X (bf16, MXFP8)"
-PEAK = {"bf16": 2.5e15, "mxfp8": 5.0e15, "fp32": 157.3e12}
+PEAK = {"bf16": 2.5e15, "mxfp8": 5.0e15, "mxfp4": 10.1e15, "fp32": 157.3e12}
 HBM_PEAK = 8.0e12
 
 
@@ -60,8 +62,8 @@ KERNEL_SOURCES = ["routing_grouped_expert_gemm_amd/csrc/expert_gemm.hip",
                   "routing_grouped_expert_gemm_amd/csrc/device_common.h",
                   "routing_grouped_expert_gemm_amd/csrc/launch.h",
                   "routing_grouped_expert_gemm_amd/_build.py"]
-ELEM = {"f32": 0, "bf16": 1, "mxfp8": 2}
-ELEM_NAME = {0: "fp32", 1: "bf16", 2: "mxfp8"}
+ELEM = {"f32": 0, "bf16": 1, "mxfp8": 2, "mxfp4": 3}
+ELEM_NAME = {0: "fp32", 1: "bf16", 2: "mxfp8", 3: "mxfp4"}
 FLUSH_BYTES = 1 << 30        # scratch overwritten before each step of the per-stage pass
 
 
@@ -131,10 +133,11 @@ def algorithmic_bytes(wl, n_routes: int) -> dict:
         out["k_router_logits"] = T * d * es + E * d * es + 4 * T * E
     if wl.full_layer:
         out["k_combine"] = T * d * es * (k + 2)
-    if wl.dtype == "mxfp8":
+    if wl.dtype in ("mxfp8", "mxfp4"):
+        cb = 0.5 if wl.dtype == "mxfp4" else 1.0      # code bytes per element
         n_w = wl.E_l * 3 * d * wl.I + 3 * d * I_sh
-        out["k_quantize_mxfp8<true>"] = n_w * (2 + 1 + 1 / 32)
-        out["k_gather_quantize"] = (n_routes + wl.T_own) * d * (2 + 1 + 1 / 32)
+        out["k_quantize_mx"] = n_w * (2 + cb + 1 / 32)
+        out["k_gather_quantize"] = (n_routes + wl.T_own) * d * (2 + cb + 1 / 32)
     return out
 
 
@@ -264,7 +267,7 @@ def summarize(d: str) -> list:
     ev_ms = line["stage_ms"]["up"]
     traffic = int(round(fetch[up_key] + write[up_key]))     # one gate/up launch per forward
     alg_up = ((wl.E_l * 2 * wl.I + 2 * wl.n_shared * wl.I_shared) * wl.d +
-              (n_routes + wl.T_own) * wl.d) * (1 if wl.dtype == "mxfp8" else 2)
+              (n_routes + wl.T_own) * wl.d) * {"mxfp8": 1, "mxfp4": 0.5}.get(wl.dtype, 2)
     lines = [
         f"# gate/up expert GEMM stage (routed + shared, fused pull gather and SwiGLU), workload {wl_name}",
         "#", "# commands (from the repository root):"] + cmds + [
@@ -450,11 +453,12 @@ def hbm_stages(wl, n_routes: int, stage_ms: dict, ring: bool) -> dict:
     bytes_ = {"plan": 4 * routes_pool + 4 * n_routes}
     if wl.full_layer:
         bytes_["combine"] = wl.T_pool * wl.d * eb * (wl.k + 2)
-    if wl.dtype == "mxfp8":
+    if wl.dtype in ("mxfp8", "mxfp4"):
+        cb = 0.5 if wl.dtype == "mxfp4" else 1.0      # code bytes per element
         n_w = wl.E_l * 3 * wl.d * wl.I + 3 * wl.d * I_sh
-        bytes_["quant"] = n_w * (2 + 1 + 1 / 32)
+        bytes_["quant"] = n_w * (2 + cb + 1 / 32)
         if not ring:
-            bytes_["gather"] = (n_routes + wl.T_own) * wl.d * (2 + 1 + 1 / 32)
+            bytes_["gather"] = (n_routes + wl.T_own) * wl.d * (2 + cb + 1 / 32)
     out = {}
     for name, b in bytes_.items():
         t = stage_ms[name] * 1e-3
@@ -599,7 +603,7 @@ def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0
     res = {
         "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 4),
-        "dtype": {"bf16": "bf16", "mxfp8": "mxfp8", "fp32": "f32"}[wl.dtype],
+        "dtype": {"bf16": "bf16", "mxfp8": "mxfp8", "mxfp4": "mxfp4", "fp32": "f32"}[wl.dtype],
         "config": {"workload": wl.name, "T_pool": wl.T_pool, "T_own": wl.T_own, "d": wl.d,
                    "E": wl.E, "k": wl.k, "I": wl.I, "E_local": wl.E_l, "n_shared": wl.n_shared,
                    "I_shared": wl.I_shared, "minibatch_rows": layer.args.minibatch_rows,
@@ -762,6 +766,13 @@ def main():
         out["mxfp8"] = {k: m[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                           "routed_rows", "routed_tflops", "gemm_tflops",
                                           "stage_ms", "roofline", "hbm")}
+        # the same share with MXFP4 operands
+        m4, i4 = measure(synth.WORKLOADS[synth.EP64_MX4], False, args.steps, args.warmup)
+        del i4
+        torch.cuda.empty_cache()
+        out["mxfp4"] = {k: m4[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                           "routed_rows", "routed_tflops", "gemm_tflops",
+                                           "stage_ms", "roofline", "hbm")}
         # pull gather against the push baseline on the EP=64 share's routing
         out["dispatch"] = measure_dispatch(min(args.steps, 10), min(args.warmup, 3))
         torch.cuda.empty_cache()

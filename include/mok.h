@@ -60,9 +60,11 @@ typedef enum {
 typedef enum {
   MOK_FP32 = 0,   /* float32 inputs, weights and outputs                                    */
   MOK_BF16 = 1,   /* bf16 inputs, weights and outputs; float32 accumulation                 */
-  MOK_MXFP8 = 2   /* bf16 inputs/weights/outputs in memory; the expert GEMMs run on OCP
+  MOK_MXFP8 = 2,  /* bf16 inputs/weights/outputs in memory; the expert GEMMs run on OCP
                      MXFP8 operands (E4M3 elements, one E8M0 scale per 32 along K) that
                      the library quantises on the device on every call                      */
+  MOK_MXFP4 = 3   /* as MOK_MXFP8 with OCP MXFP4 operands (E2M1 elements: 0, 0.5, 1, 1.5,
+                     2, 3, 4, 6 and sign; one E8M0 scale per 32 along K)                    */
 } mok_dtype;
 
 /* Human-readable name of a status code (static string; never NULL). */
@@ -126,7 +128,7 @@ typedef struct mok_moe_args {
   int32_t d;               /* model dim (multiple of 128)                                   */
   int32_t E;               /* routed experts in the layer                                   */
   int32_t k;               /* top-k                                                         */
-  int32_t I;               /* routed expert intermediate (multiple of 64; MXFP8: of 128)    */
+  int32_t I;               /* routed expert intermediate (multiple of 64; MX: of 128)       */
   int32_t e0, E_l;         /* local experts [e0, e0+E_l)                                    */
   int32_t tokens_per_rank; /* pool rows per source rank (T_pool % tokens_per_rank == 0)     */
   int64_t T_pool;          /* rows of the token pool x                                      */
@@ -205,7 +207,8 @@ int mok_moe_forward(const mok_moe_args* args, void* stream);
  * workspace, its size in bytes and `rows` (below). MOK_EINVAL if the region does not exist
  * for this configuration (e.g. an MXFP8 region of a BF16 forward).
  *
- * MXFP8 codes are E4M3 bytes, row-major [rows, K] like the bf16 source. MXFP8 scales are E8M0
+ * MXFP8 codes are E4M3 bytes, row-major [rows, K] like the bf16 source; MXFP4 codes are E2M1
+ * nibbles, row-major [rows, K/2] bytes, element 2i in the low nibble of byte i. Scales are E8M0
  * bytes kept "K-step major": a source of `rows` rows splits into matrices of R rows (R is
  * returned in *rows); in matrix g the scale of (row r, 32-element block b) sits at byte
  *     g * R * (K / 32) + ((b / 4) * R + r) * 4 + (b % 4)
@@ -277,6 +280,14 @@ int mok_push_dispatch(const void* x, int64_t T_pool, int32_t d, int32_t k, int32
  * The forward's own MXFP8 quantisers apply the same rules with other device code (K-step-
  * major scales, the row gather fused in); mok_moe_workspace_region exposes what they wrote. */
 int mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int32_t K, uint8_t* codes,
+                       uint8_t* scales, void* stream);
+
+/* OCP MX v1.0 MXFP4 along rows, the same conventions: codes [rows, K/2] bytes of E2M1 codes
+ * (sign bit 3; element 2i in the low nibble of byte i), scales [rows, K/32] E8M0. Per block of
+ * 32: s = floor(log2(amax)) - 2 clamped to [-127, 127] (amax == 0 -> -127); element = the
+ * nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 to |v| * 2^-s (ties to the even code), saturated to 6,
+ * sign kept. The forward's MXFP4 quantisers apply the same rules (K-step-major scales). */
+int mok_quantize_mxfp4(const void* src_bf16, int64_t rows, int32_t K, uint8_t* codes,
                        uint8_t* scales, void* stream);
 
 /* ---------------------------------------------------------------- device error word

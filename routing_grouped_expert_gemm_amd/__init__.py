@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmok.so")   # always the in-tree build
 
 MOK_OK, MOK_EINVAL, MOK_EUNSUPPORTED, MOK_EWORKSPACE, MOK_EHIP = range(5)
-MOK_FP32, MOK_BF16, MOK_MXFP8 = 0, 1, 2
+MOK_FP32, MOK_BF16, MOK_MXFP8, MOK_MXFP4 = 0, 1, 2, 3
 MOK_FLAG_NO_RING = 1
 (MOK_STAGE_ROUTE, MOK_STAGE_PLAN, MOK_STAGE_QUANT, MOK_STAGE_UP, MOK_STAGE_DOWN, MOK_STAGE_COMBINE,
  MOK_STAGE_GATHER) = range(7)
@@ -32,7 +32,7 @@ EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
            "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_dispatch_plan_noalloc",
            "mok_moe_workspace_bytes",
            "mok_moe_forward", "mok_moe_workspace_region", "mok_pull_gather",
-           "mok_push_dispatch", "mok_quantize_mxfp8",
+           "mok_push_dispatch", "mok_quantize_mxfp8", "mok_quantize_mxfp4",
            "mok_get_device_error"]
 
 
@@ -85,6 +85,7 @@ _lib.mok_moe_forward.argtypes = [ctypes.POINTER(MoeArgs), _P]
 _lib.mok_moe_workspace_region.argtypes = [ctypes.POINTER(MoeArgs), _I32, ctypes.POINTER(_SZ),
                                           ctypes.POINTER(_SZ), ctypes.POINTER(_I64)]
 _lib.mok_quantize_mxfp8.argtypes = [_P, _I64, _I32, _P, _P, _P]
+_lib.mok_quantize_mxfp4.argtypes = [_P, _I64, _I32, _P, _P, _P]
 _lib.mok_pull_gather.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _I32, _P, _P]
 _lib.mok_push_dispatch.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _I32, _I32, _I64, _P, _P, _P,
                                    _P]
@@ -211,6 +212,13 @@ def mok_quantize_mxfp8(src_bf16, codes, scales, stream=None) -> None:
                                                          _ptr(scales), _stream(stream)))
 
 
+def mok_quantize_mxfp4(src_bf16, codes, scales, stream=None) -> None:
+    """MXFP4 along rows: codes [rows, K/2] (two E2M1 codes a byte), scales [rows, K/32]."""
+    rows, K = src_bf16.shape
+    _check("mok_quantize_mxfp4", _lib.mok_quantize_mxfp4(_ptr(src_bf16), rows, K, _ptr(codes),
+                                                         _ptr(scales), _stream(stream)))
+
+
 def mok_get_device_error(workspace, stream=None) -> int:
     err = ctypes.c_uint32(0)
     _check("mok_get_device_error", _lib.mok_get_device_error(_ptr(workspace), ctypes.byref(err),
@@ -220,7 +228,7 @@ def mok_get_device_error(workspace, stream=None) -> int:
 
 # ------------------------------------------------------------------------ layer helper
 
-_DT = {"fp32": MOK_FP32, "bf16": MOK_BF16, "mxfp8": MOK_MXFP8}
+_DT = {"fp32": MOK_FP32, "bf16": MOK_BF16, "mxfp8": MOK_MXFP8, "mxfp4": MOK_MXFP4}
 
 
 class MoeLayer:

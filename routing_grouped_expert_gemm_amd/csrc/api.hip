@@ -48,7 +48,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int validate_moe(const mok_moe_args* a) {
   if (!a) return MOK_EINVAL;
-  if (a->dtype < MOK_FP32 || a->dtype > MOK_MXFP8) return MOK_EINVAL;
+  if (a->dtype < MOK_FP32 || a->dtype > MOK_MXFP4) return MOK_EINVAL;
   if (a->d <= 0 || a->E <= 0 || a->E > 1024 || a->k < 1 || a->k > a->E || a->k > 64)
     return MOK_EINVAL;
   if (a->I <= 0 || a->e0 < 0 || a->E_l < 1 || a->e0 + a->E_l > a->E) return MOK_EINVAL;
@@ -64,8 +64,8 @@ int validate_moe(const mok_moe_args* a) {
   const int mb = a->minibatch_rows;
   if (mb != 128 && mb != 256 && mb != 512 && mb != 1024) return MOK_EINVAL;
   if (a->ring_rows < mb || a->ring_rows % mb) return MOK_EINVAL;
-  // tile divisibility: K steps of 128 bytes, down tiles of 128 columns, up tiles of 64 columns
-  // K steps of 128 bytes per row (fp32 32, bf16 64, fp8 128 elements)
+  // tile divisibility: K steps of 128 bytes per row (fp32 32, bf16 64, fp8 128 elements) or
+  // 64 bytes (fp4: 128 elements); down tiles of 128 columns, up tiles of 64 columns
   const int kstep = a->dtype == MOK_FP32 ? 32 : (a->dtype == MOK_BF16 ? 64 : 128);
   if (a->d % 128 || a->d % kstep || a->I % 64 || a->I % kstep) return MOK_EINVAL;
   if (a->n_shared > 0) {
@@ -101,8 +101,10 @@ Layout layout_moe(const mok_moe_args* a) {
   const size_t es = a->dtype == MOK_FP32 ? 4 : 2;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-  gemm_tile_caps(L.max_mb, mb, a->I, I_sh, a->d, L.use_ring && a->dtype == MOK_MXFP8, &L.cap_u,
-                 &L.cap_d, &L.cap_g);
+  const bool mx = a->dtype == MOK_MXFP8 || a->dtype == MOK_MXFP4;
+  // bytes of n MX codes: one a byte (MXFP8), two a byte (MXFP4)
+  auto cb = [&](size_t n) { return a->dtype == MOK_MXFP4 ? n / 2 : n; };
+  gemm_tile_caps(L.max_mb, mb, a->I, I_sh, a->d, L.use_ring && mx, &L.cap_u, &L.cap_d, &L.cap_g);
   L.cap_r = L.use_ring ? L.cap_u + L.cap_d + L.cap_g : 0;
   L.wl = take(sizeof(int32_t) * worklist_ints(L.max_mb, L.cap_u, L.cap_d, L.cap_r));
   const bool route = a->w_router != nullptr;
@@ -117,16 +119,16 @@ Layout layout_moe(const mok_moe_args* a) {
   L.blk_counts = take(sizeof(int32_t) * nb * a->E_l);
   L.blk_base = take(sizeof(int32_t) * nb * a->E_l);
   const int64_t ring_rows = (int64_t)L.n_slots * mb;
-  if (a->dtype == MOK_MXFP8) {
-    L.H = take((size_t)ring_rows * L.Hld);
+  if (mx) {
+    L.H = take(cb((size_t)ring_rows * L.Hld));
     L.H_sc = take((size_t)ring_rows * (L.Hld / 32));
-    L.A_codes = take((size_t)ring_rows * a->d);
+    L.A_codes = take(cb((size_t)ring_rows * a->d));
     L.A_sc = take((size_t)ring_rows * (a->d / 32));
     const size_t el = (size_t)a->E_l * a->I * a->d;
-    L.wg_q = take(el); L.wu_q = take(el); L.wd_q = take(el);
+    L.wg_q = take(cb(el)); L.wu_q = take(cb(el)); L.wd_q = take(cb(el));
     L.wg_s = take(el / 32); L.wu_s = take(el / 32); L.wd_s = take(el / 32);
     const size_t sl = (size_t)I_sh * a->d;
-    L.sg_q = take(sl); L.su_q = take(sl); L.sd_q = take(sl);
+    L.sg_q = take(cb(sl)); L.su_q = take(cb(sl)); L.sd_q = take(cb(sl));
     L.sg_s = take(sl / 32); L.su_s = take(sl / 32); L.sd_s = take(sl / 32);
   } else {
     L.H = take((size_t)ring_rows * L.Hld * es);
@@ -262,7 +264,9 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
 
   // stages 3-5
   ExpertPass p = {};
-  p.elem = a->dtype == MOK_FP32 ? Elem::F32 : (a->dtype == MOK_BF16 ? Elem::BF16 : Elem::FP8);
+  p.elem = a->dtype == MOK_FP32 ? Elem::F32
+         : a->dtype == MOK_BF16 ? Elem::BF16
+         : a->dtype == MOK_MXFP8 ? Elem::FP8 : Elem::FP4;
   p.out_f32 = a->dtype == MOK_FP32;
   p.d = a->d;
   p.k = k;
@@ -295,7 +299,8 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.wl = (int32_t*)at(L.wl);
   p.y_slots = a->y_slots;
   p.y_shared = a->y_shared;
-  if (a->dtype == MOK_MXFP8) {
+  if (a->dtype == MOK_MXFP8 || a->dtype == MOK_MXFP4) {
+    const bool fp4 = a->dtype == MOK_MXFP4;
     char* q = ws;
     uint8_t* wg_q = (uint8_t*)(q + L.wg_q); uint8_t* wu_q = (uint8_t*)(q + L.wu_q);
     uint8_t* wd_q = (uint8_t*)(q + L.wd_q); uint8_t* sg_q = (uint8_t*)(q + L.sg_q);
@@ -307,19 +312,21 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     const bool sh = p.I_sh > 0;
     hipEvent_t q0 = ev_start(MOK_STAGE_QUANT), q1 = ev_stop(MOK_STAGE_QUANT);
     // scales K-step major per matrix (the layout the GEMMs' scale loads read)
-    hipError_t e = launch_quantize_mxfp8(a->w_gate, rI, a->d, wg_q, wg_s, s, q0, nullptr, a->I);
+    hipError_t e = launch_quantize_mx(a->w_gate, rI, a->d, wg_q, wg_s, fp4, s, q0, nullptr, a->I);
     if (e == hipSuccess)
-      e = launch_quantize_mxfp8(a->w_up, rI, a->d, wu_q, wu_s, s, nullptr, nullptr, a->I);
+      e = launch_quantize_mx(a->w_up, rI, a->d, wu_q, wu_s, fp4, s, nullptr, nullptr, a->I);
     if (e == hipSuccess)
-      e = launch_quantize_mxfp8(a->w_down, rD, a->I, wd_q, wd_s, s, nullptr, sh ? nullptr : q1,
-                                a->d);
+      e = launch_quantize_mx(a->w_down, rD, a->I, wd_q, wd_s, fp4, s, nullptr, sh ? nullptr : q1,
+                             a->d);
     if (e == hipSuccess && sh) {
-      e = launch_quantize_mxfp8(a->ws_gate, p.I_sh, a->d, sg_q, sg_s, s, nullptr, nullptr, p.I_sh);
+      e = launch_quantize_mx(a->ws_gate, p.I_sh, a->d, sg_q, sg_s, fp4, s, nullptr, nullptr,
+                             p.I_sh);
       if (e == hipSuccess)
-        e = launch_quantize_mxfp8(a->ws_up, p.I_sh, a->d, su_q, su_s, s, nullptr, nullptr, p.I_sh);
+        e = launch_quantize_mx(a->ws_up, p.I_sh, a->d, su_q, su_s, fp4, s, nullptr, nullptr,
+                               p.I_sh);
       if (e == hipSuccess)
-        e = launch_quantize_mxfp8(a->ws_down, (int64_t)a->n_shared * a->d, a->I_shared, sd_q,
-                                  sd_s, s, nullptr, q1, a->d);
+        e = launch_quantize_mx(a->ws_down, (int64_t)a->n_shared * a->d, a->I_shared, sd_q, sd_s,
+                               fp4, s, nullptr, q1, a->d);
     }
     if (e != hipSuccess) return MOK_EHIP;
     p.wg = wg_q; p.wu = wu_q; p.wd = wd_q; p.sg = sg_q; p.su = su_q; p.sd = sd_q;
@@ -351,8 +358,9 @@ int mok_moe_workspace_region(const mok_moe_args* a, int32_t region, size_t* offs
   int st = validate_moe(a);
   if (st != MOK_OK) return st;
   const Layout L = layout_moe(a);
-  const bool mx = a->dtype == MOK_MXFP8;
+  const bool mx = a->dtype == MOK_MXFP8 || a->dtype == MOK_MXFP4;
   const int64_t ring = (int64_t)L.n_slots * a->minibatch_rows;
+  const size_t half = a->dtype == MOK_MXFP4 ? 2 : 1;   // MX codes a byte
   const int64_t I_sh = (int64_t)a->n_shared * a->I_shared;
   const int64_t el = (int64_t)a->E_l * a->I * a->d, sl = I_sh * a->d;
   const size_t es = a->dtype == MOK_FP32 ? 4 : 2;
@@ -363,21 +371,21 @@ int mok_moe_workspace_region(const mok_moe_args* a, int32_t region, size_t* offs
       off = L.wl; n = sizeof(int32_t) * worklist_ints(L.max_mb, L.cap_u, L.cap_d, L.cap_r);
       R = 1; break;
     case MOK_REGION_H:
-      off = L.H; n = (size_t)ring * L.Hld * (mx ? 1 : es); R = ring; break;
+      off = L.H; n = (size_t)ring * L.Hld * (mx ? 1 : es) / half; R = ring; break;
     case MOK_REGION_H_SCALES: off = L.H_sc; n = (size_t)ring * (L.Hld / 32); R = ring; break;
-    case MOK_REGION_A_CODES: off = L.A_codes; n = (size_t)ring * a->d; R = ring; break;
+    case MOK_REGION_A_CODES: off = L.A_codes; n = (size_t)ring * a->d / half; R = ring; break;
     case MOK_REGION_A_SCALES: off = L.A_sc; n = (size_t)ring * (a->d / 32); R = ring; break;
-    case MOK_REGION_WG_CODES: off = L.wg_q; n = el; R = a->I; break;
+    case MOK_REGION_WG_CODES: off = L.wg_q; n = el / half; R = a->I; break;
     case MOK_REGION_WG_SCALES: off = L.wg_s; n = el / 32; R = a->I; break;
-    case MOK_REGION_WU_CODES: off = L.wu_q; n = el; R = a->I; break;
+    case MOK_REGION_WU_CODES: off = L.wu_q; n = el / half; R = a->I; break;
     case MOK_REGION_WU_SCALES: off = L.wu_s; n = el / 32; R = a->I; break;
-    case MOK_REGION_WD_CODES: off = L.wd_q; n = el; R = a->d; break;
+    case MOK_REGION_WD_CODES: off = L.wd_q; n = el / half; R = a->d; break;
     case MOK_REGION_WD_SCALES: off = L.wd_s; n = el / 32; R = a->d; break;
-    case MOK_REGION_SG_CODES: off = L.sg_q; n = sl; R = I_sh; break;
+    case MOK_REGION_SG_CODES: off = L.sg_q; n = sl / half; R = I_sh; break;
     case MOK_REGION_SG_SCALES: off = L.sg_s; n = sl / 32; R = I_sh; break;
-    case MOK_REGION_SU_CODES: off = L.su_q; n = sl; R = I_sh; break;
+    case MOK_REGION_SU_CODES: off = L.su_q; n = sl / half; R = I_sh; break;
     case MOK_REGION_SU_SCALES: off = L.su_s; n = sl / 32; R = I_sh; break;
-    case MOK_REGION_SD_CODES: off = L.sd_q; n = sl; R = a->d; break;
+    case MOK_REGION_SD_CODES: off = L.sd_q; n = sl / half; R = a->d; break;
     case MOK_REGION_SD_SCALES: off = L.sd_s; n = sl / 32; R = a->d; break;
     default: return MOK_EINVAL;
   }
@@ -395,7 +403,17 @@ int mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int32_t K, uint8_t* c
   if (rows < 0 || K <= 0 || K % 32) return MOK_EINVAL;
   if (rows == 0) return MOK_OK;
   if (!src_bf16 || !codes || !scales) return MOK_EINVAL;
-  return status_of(launch_quantize_mxfp8(src_bf16, rows, K, codes, scales, (hipStream_t)stream));
+  return status_of(launch_quantize_mx(src_bf16, rows, K, codes, scales, false,
+                                      (hipStream_t)stream));
+}
+
+int mok_quantize_mxfp4(const void* src_bf16, int64_t rows, int32_t K, uint8_t* codes,
+                       uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOK_EINVAL;
+  if (rows == 0) return MOK_OK;
+  if (!src_bf16 || !codes || !scales) return MOK_EINVAL;
+  return status_of(launch_quantize_mx(src_bf16, rows, K, codes, scales, true,
+                                      (hipStream_t)stream));
 }
 
 int mok_get_device_error(const void* workspace, uint32_t* err, void* stream) {

@@ -103,8 +103,11 @@ MOK_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
 MOK_DEV float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ----------------------------------------------------------------------- MXFP8 (OCP MX)
-// Shared exponent of a block from its absolute maximum: floor(log2(amax)) - 8, clamped to
-// [-127, 127]; amax == 0 -> -127. Exact integer arithmetic on the float's fields.
+// Shared exponent of a block from its absolute maximum: floor(log2(amax)) - EMAX, clamped to
+// [-127, 127]; amax == 0 -> -127. EMAX is the exponent of the element type's largest normal: 8
+// for E4M3 (448 = 1.75 * 2^8), 2 for E2M1 (6 = 1.5 * 2^2). Exact integer arithmetic on the
+// float's fields.
+template <int EMAX = 8>
 MOK_DEV int mx_shared_exp(float amax) {
   uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
   if (u == 0) return -127;
@@ -114,7 +117,7 @@ MOK_DEV int mx_shared_exp(float amax) {
   } else {
     e = (int)(u >> 23) - 127;
   }
-  int s = e - 8;
+  int s = e - EMAX;
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
@@ -240,4 +243,79 @@ MOK_DEV uint2 quantize_quad8_f32(const float (&v)[8], int* s_out) {
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
   *s_out = s;
   return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// ----------------------------------------------------------------------- MXFP4 (OCP MX)
+// E2M1 code (sign in bit 3) of y = v * 2^-s, which the caller forms exactly: the nearest of
+// the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a tie going to the even code, and everything
+// past 6 saturating. Decided by comparisons against the midpoints, which are exact floats:
+// a midpoint whose even neighbour lies below (0.25, 1.25, 2.5, 5) rounds down, the others
+// (0.75, 1.75, 3.5) round up.
+MOK_DEV uint32_t e2m1_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
+  const float a = fabsf(y);
+  const uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return sign | m;
+}
+
+// Two elements a byte: element 2i in the low nibble of byte i.
+MOK_DEV uint32_t pack_e2m1x8(const float (&y)[8]) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) w |= e2m1_code(y[q]) << (4 * q);
+  return w;
+}
+
+// MXFP4 of eight values held by one lane of an aligned quad (a 32-element block over 4 lanes):
+// the 8 codes (4 bytes) and the block's shared exponent (emax 2). v * 2^-s is exact (ldexp of
+// a value whose result can reach a nonzero code is a normal float).
+MOK_DEV uint32_t mx4_quad8_f32(const float (&v)[8], int* s_out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  const int s = mx_shared_exp<2>(amax);
+  float y[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) y[q] = __builtin_amdgcn_ldexpf(v[q], -s);
+  *s_out = s;
+  return pack_e2m1x8(y);
+}
+
+MOK_DEV uint32_t mx4_quad8(const uint4 raw, int* s_out) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+  return mx4_quad8_f32(v, s_out);
+}
+
+// Sixteen bf16 values a lane, the 2 lanes of an aligned pair holding one 32-element block:
+// the 16 codes (8 bytes) and the block's shared exponent.
+MOK_DEV uint2 mx4_pair16(const uint4 raw0, const uint4 raw1, int* s_out) {
+  const uint32_t w[8] = {raw0.x, raw0.y, raw0.z, raw0.w, raw1.x, raw1.y, raw1.z, raw1.w};
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  const int s = mx_shared_exp<2>(amax);
+  float lo[8], hi[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    lo[q] = __builtin_amdgcn_ldexpf(v[q], -s);
+    hi[q] = __builtin_amdgcn_ldexpf(v[8 + q], -s);
+  }
+  *s_out = s;
+  return make_uint2(pack_e2m1x8(lo), pack_e2m1x8(hi));
 }

@@ -381,12 +381,23 @@ constexpr int TILE_M = 256;
 // workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs. Two 64 KB K stages of
 // 128 bytes per row (whole cache lines), filled by LDS-DMA.
 typedef Cfg<256, 256, 2, 2, 128, 2> Big;
+// MXFP4: K steps of 64 bytes per row, i.e. 128 elements, as the MXFP8 steps of 128 bytes, so
+// the two MX formats share one scale word per row and K step and the same sub-step structure.
+typedef Cfg<256, 256, 2, 2, 64, 2> Big4;
+template <Elem EL> struct CfgOf { typedef Big type; };
+template <> struct CfgOf<Elem::FP4> { typedef Big4 type; };
 
-// Per element type: bytes per element, and the MFMA's K per instruction.
+// Per element type: bytes per two elements (KB2), the MFMA's K per instruction (MK) and the 16-
+// byte chunks a lane feeds one MFMA (CPL).
 template <Elem EL> struct Tr;
-template <> struct Tr<Elem::BF16> { static constexpr int ES = 2, MK = 16, CPL = 1; };
-template <> struct Tr<Elem::F32> { static constexpr int ES = 4, MK = 16, CPL = 2; };
-template <> struct Tr<Elem::FP8> { static constexpr int ES = 1, MK = 64, CPL = 2; };
+template <> struct Tr<Elem::BF16> { static constexpr int KB2 = 4, MK = 16, CPL = 1; };
+template <> struct Tr<Elem::F32> { static constexpr int KB2 = 8, MK = 16, CPL = 2; };
+template <> struct Tr<Elem::FP8> { static constexpr int KB2 = 2, MK = 64, CPL = 2; };
+template <> struct Tr<Elem::FP4> { static constexpr int KB2 = 1, MK = 64, CPL = 1; };
+// Bytes of n elements along K (n even).
+template <Elem EL> MOK_HOSTDEV constexpr int64_t nbytes(int64_t n) { return n * Tr<EL>::KB2 / 2; }
+// Operands in an MX format (E8M0 block scales; quantised on the device).
+template <Elem EL> constexpr bool is_mx() { return EL == Elem::FP8 || EL == Elem::FP4; }
 
 // LDS: STAGES buffers of the A and B tiles (ROW_B per row per K step), their MX scale words and
 // the down stage's row table. Logical 16-byte chunk c of row r sits at slot
@@ -426,9 +437,14 @@ MOK_DEV Bufs<C> pick(const Lds<C>& sm, int i) {
 //  fp8 32x32x64 (scaled): bytes 0-15 of a lane belong to the MFMA's first 32-wide K block and
 //  bytes 16-31 to the second, each lane half taking 16 of a block's 32 k; the E8M0 scale of
 //  lane l covers (row l % 32, block l / 32). So: chunks 4s + h and 4s + 2 + h.
+//  fp4 32x32x64 (scaled): a lane's 16 bytes are the 32 consecutive k of block l / 32 (a probe
+//  of the instruction with exact small inputs and per-block scales matched only this layout),
+//  and its E8M0 scale covers that block: chunk 2s + h of the 64-byte K step.
 template <Elem EL>
 MOK_DEV constexpr int frag_chunk(int s, int h, int q) {
-  return EL == Elem::BF16 ? 2 * s + h : (EL == Elem::F32 ? 4 * s + 2 * h + q : 4 * s + 2 * q + h);
+  return EL == Elem::BF16 ? 2 * s + h
+       : EL == Elem::F32 ? 4 * s + 2 * h + q
+       : EL == Elem::FP4 ? 2 * s + h : 4 * s + 2 * q + h;
 }
 
 // s_waitcnt with only the vector-memory counter constrained: vmcnt <= n (gfx9 encoding:
@@ -512,6 +528,19 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[q], av[q], acc[i][j], 0, 0, 0);
         after(i * FN + j);
       }
+  } else if constexpr (EL == Elem::FP4) {
+    // operand format 4 (E2M1) for both; the instruction reads the first four registers
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        i32x8_t av = {0, 0, 0, 0, 0, 0, 0, 0}, bv = av;
+        av[0] = a[i][0].x; av[1] = a[i][0].y; av[2] = a[i][0].z; av[3] = a[i][0].w;
+        bv[0] = b[j][0].x; bv[1] = b[j][0].y; bv[2] = b[j][0].z; bv[3] = b[j][0].w;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            bv, av, acc[i][j], 4, 4, SCB, (int)bsc[j], SCB, (int)asc[i]);
+        after(i * FN + j);
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -543,7 +572,7 @@ MOK_DEV void mfma_step(const uint4 (&a)[FM][2], const uint4 (&b)[FN][2], const u
 // ahead, so that a tile's first DMA does not wait on this dependent load.
 template <Elem EL, bool UP, class C>
 MOK_DEV void prefetch_a_rows(const ExpertPass& p, const int4 entry, int32_t (&route)[C::A_SLABS]) {
-  if constexpr (UP && EL != Elem::FP8) {
+  if constexpr (UP && !is_mx<EL>()) {
     const int local = uniform(entry.y) & ((1 << KIND_SHIFT) - 1), row0 = uniform(entry.z);
     const int g = uniform(entry.w >> 16), rows = uniform(entry.w & 0xFFFF);
     const int n_mt = (rows + TILE_M - 1) / TILE_M;
@@ -587,21 +616,22 @@ template <Elem EL, bool UP, bool F32OUT, class C, bool RING = false, class F>
 MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, const int slot,
                       const int32_t (&pre)[C::A_SLABS], F&& after_step) {
   // A operands written during this launch (ring loop): H (down) and the MXFP8 A rows (up)
-  constexpr bool A_L2C = RING && (!UP || EL == Elem::FP8);
+  constexpr bool MXE = is_mx<EL>();
+  constexpr bool A_L2C = RING && (!UP || MXE);
   typedef Tr<EL> TR;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int A_SLABS = C::A_SLABS, B_SLABS = C::B_SLABS, ST = C::STAGES, CH = C::CH;
   constexpr int RPI = C::RPI, SWS = C::SWZ_SHIFT, RA = C::RA, RB = C::RB;
-  static_assert(EL != Elem::FP8 || (RA == 64 && RB == 64),
+  static_assert(!MXE || (RA == 64 && RB == 64),
                 "MX scales: lane L of loader wave w carries tile row 64 w + L");
-  constexpr int KT = C::ROW_B / TR::ES;            // elements per K step
+  constexpr int KT = C::ROW_B * 2 / TR::KB2;       // elements per K step
   constexpr int SUB = KT / TR::MK;                 // MFMA sub-steps per K step
   constexpr int SC_B = KT / 32;                    // MX scale bytes per row per K step
   // LDS-DMA instructions one wave issues per K step
-  constexpr int DMA_PER_STEP = A_SLABS + B_SLABS + (EL == Elem::FP8 ? 2 : 0);
+  constexpr int DMA_PER_STEP = A_SLABS + B_SLABS + (MXE ? 2 : 0);
   // K-loop barrier placement: before the last sub-step of the previous step (bf16, float32),
   // or at the start of the step (MXFP8)
-  constexpr bool EARLY_X = EL != Elem::FP8;
+  constexpr bool EARLY_X = !MXE;
   const int m = uniform(entry.x), local = uniform(entry.y);
   const int row0 = uniform(entry.z);
   const int g = uniform(entry.w >> 16), rows = uniform(entry.w & 0xFFFF);
@@ -631,15 +661,15 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   // ---- A operand: uniform base + per-slab 32-bit row offsets
   const char* a_base;
   int64_t a_row_bytes;
-  if (UP && EL != Elem::FP8) {
+  if (UP && !MXE) {
     a_base = (const char*)kernarg_field<const void*>(offsetof(ExpertPass, x));
-    a_row_bytes = (int64_t)p.d * TR::ES;
+    a_row_bytes = nbytes<EL>(p.d);
   } else if (UP) {
-    a_base = (const char*)p.A_codes + (ring_row0 + m0) * p.d;
-    a_row_bytes = p.d;
+    a_base = (const char*)p.A_codes + (ring_row0 + m0) * nbytes<EL>(p.d);
+    a_row_bytes = nbytes<EL>(p.d);
   } else {
-    a_base = (const char*)p.H + (ring_row0 + m0) * (int64_t)p.Hld * TR::ES;
-    a_row_bytes = (int64_t)p.Hld * TR::ES;
+    a_base = (const char*)p.H + (ring_row0 + m0) * nbytes<EL>(p.Hld);
+    a_row_bytes = nbytes<EL>(p.Hld);
   }
   a_base = uniform_ptr(a_base);
   uint32_t a_off[A_SLABS];
@@ -647,7 +677,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   for (int q = 0; q < A_SLABS; ++q) {
     const int r = min(RA * wid + RPI * q + lane / CH, rows_valid - 1);
     int64_t row;
-    if (UP && EL != Elem::FP8)
+    if (UP && !MXE)
       row = shared ? p.own_begin + row0 + m0 + r : (int64_t)pre[q];
     else
       row = r;
@@ -662,19 +692,19 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   int64_t b_row_bytes, b_seg_len = K, b_seg_stride = 0;
   auto b_up_slab = [&](int q) { return ((RB * wid + RPI * q) % WN) >= WN / 2; };
   if (UP) {
-    const int64_t e_off = shared ? 0 : (int64_t)g * p.I * p.d * TR::ES;
+    const int64_t e_off = shared ? 0 : (int64_t)g * p.I * nbytes<EL>(p.d);
     b_base = (const char*)(shared ? p.sg : p.wg) + e_off;
     b_up = uniform_ptr((const char*)(shared ? p.su : p.wu) + e_off);
-    b_row_bytes = (int64_t)p.d * TR::ES;
+    b_row_bytes = nbytes<EL>(p.d);
   } else {
     if (shared) {
       b_base = (const char*)p.sd;
-      b_row_bytes = (int64_t)p.I_seg * TR::ES;
+      b_row_bytes = nbytes<EL>(p.I_seg);
       b_seg_len = p.I_seg;
-      b_seg_stride = (int64_t)p.d * p.I_seg * TR::ES;
+      b_seg_stride = (int64_t)p.d * nbytes<EL>(p.I_seg);
     } else {
-      b_base = (const char*)p.wd + (int64_t)g * p.d * p.I * TR::ES;
-      b_row_bytes = (int64_t)p.I * TR::ES;
+      b_base = (const char*)p.wd + (int64_t)g * p.d * nbytes<EL>(p.I);
+      b_row_bytes = nbytes<EL>(p.I);
     }
   }
   b_base = uniform_ptr(b_base);
@@ -696,7 +726,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   const uint8_t* b_sc_base = nullptr;
   uint32_t a_sc_off = 0, b_sc_off = 0;
   int64_t a_sc_R = 0, b_sc_R = 0;                    // rows of the scale matrices
-  if (EL == Elem::FP8) {
+  if (MXE) {
     const int r = min(RA * wid + lane, rows_valid - 1);
     a_sc_R = (int64_t)p.n_slots * p.mb;              // A rows and H: the ring rows
     a_sc_base = (UP ? p.A_sc : p.H_sc) + (ring_row0 + m0) * 4;
@@ -743,12 +773,13 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     const uint32_t k0 = (uint32_t)kt * KT;
     const uint32_t seg = k0 / (uint32_t)b_seg_len;
     const uint32_t kin = k0 - seg * (uint32_t)b_seg_len;
-    s.a = uniform_ptr(a_base + k0 * TR::ES);
-    s.b = uniform_ptr(b_base + (int64_t)seg * b_seg_stride + kin * TR::ES);
-    s.bu = UP ? uniform_ptr(b_up + kin * TR::ES) : nullptr;
-    if (EL == Elem::FP8) {                           // K steps of 128 elements: one scale word
+    s.a = uniform_ptr(a_base + nbytes<EL>(k0));
+    s.b = uniform_ptr(b_base + (int64_t)seg * b_seg_stride + nbytes<EL>(kin));
+    s.bu = UP ? uniform_ptr(b_up + nbytes<EL>(kin)) : nullptr;
+    if (MXE) {                                       // K steps of 128 elements: one scale word
+      // a shared down segment's scales: d rows x I_seg / 32 bytes per shared expert
       s.sa = uniform_ptr(a_sc_base + (int64_t)(k0 / 128) * a_sc_R * 4);
-      s.sb = uniform_ptr(b_sc_base + (int64_t)seg * (b_seg_stride / 32) +
+      s.sb = uniform_ptr(b_sc_base + (int64_t)seg * p.d * (p.I_seg / 32) +
                          (int64_t)(kin / 128) * b_sc_R * 4);
     } else {
       s.sa = s.sb = nullptr;
@@ -802,14 +833,14 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     for (int i = 0; i < FM; ++i) {
       fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c0);
       if (TR::CPL == 2) fa[f][i][1] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c1);
-      if (EL == Elem::FP8)
+      if (MXE)
         asc[f][i] = (b.As[blk_row(i) + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       fb[f][j][0] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c0);
       if (TR::CPL == 2) fb[f][j][1] = *(const uint4*)(b_buf + j * 32 * C::ROW_B + c1);
-      if (EL == Elem::FP8)
+      if (MXE)
         bsc[f][j] = (b.Bs[wn * WN + j * 32 + l32] >> (sc_shift + 8 * (2 * s + h))) & 0xFFu;
     }
   };
@@ -875,7 +906,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     auto load = [&](int s, int f) {
       const int c0 = ((frag_chunk<EL>(s, h, 0)) ^ xsw) * 16;
       const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ xsw) * 16;
-      if (EL == Elem::FP8 && s == 0) {
+      if (MXE && s == 0) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) asc[i] = b.As[blk_row(i) + l32] >> (8 * h);
 #pragma unroll
@@ -894,7 +925,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
 #pragma unroll
       for (int i = 1; i < FM; ++i) ra(i);
     };
-    static_assert(EL != Elem::FP8 || (SUB == 2 && SC_B == 4), "one scale word per row and K step");
+    static_assert(!MXE || (SUB == 2 && SC_B == 4), "one scale word per row and K step");
     load(0, 0);
     // The reads of sub-step s + 1 go out after the first NEXT_AT MFMAs of s: issued before
     // them, they would sit ahead of s's own reads in the LDS counter, and the first MFMA would
@@ -1031,9 +1062,9 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     // bf16 (or MXFP8 H) outputs: each wave stages 32 rows at a time through its own LDS region
     // (the operand buffers are free once every wave is past the K loop), four columns per
     // write, then stores whole row segments: H rows of the ring (up) or route-slot / shared
-    // rows (down). MXFP8 H is staged as float32 and quantised 8 values per lane, the 4 lanes
-    // of a 32-column block forming an aligned quad (the first stores the scale byte).
-    constexpr bool MX = UP && EL == Elem::FP8;
+    // rows (down). MX H is staged as float32 and quantised 8 values per lane, the 4 lanes of a
+    // 32-column block forming an aligned quad (the first stores the scale byte).
+    constexpr bool MX = UP && is_mx<EL>();
     constexpr int VB = MX ? 4 : 2;                    // staged bytes per value
     constexpr int CW = UP ? WN / 2 : WN;              // output columns per wave
     constexpr int JB = CW / 32;                       // 32-column blocks per wave
@@ -1091,13 +1122,22 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
                                  __uint_as_float(hi.x), __uint_as_float(hi.y),
                                  __uint_as_float(hi.z), __uint_as_float(hi.w)};
           int se;
-          const uint2 codes = quantize_quad8_f32(vals, &se);
-          if (r < rows_valid && col0 + c < N) {
-            const int64_t hr = ring_row0 + m0 + r;
+          const int64_t hr = ring_row0 + m0 + r;
+          const bool st = r < rows_valid && col0 + c < N;
+          if constexpr (EL == Elem::FP4) {
+            const uint32_t codes = mx4_quad8_f32(vals, &se);   // streamed past the L2
+            if (st)
+              __builtin_nontemporal_store(
+                  codes, (uint32_t*)((uint8_t*)p.H + hr * (p.Hld / 2) + (col0 + c) / 2));
+          } else {
+            const uint2 codes = quantize_quad8_f32(vals, &se);
             u32x2 cv;                                    // streamed past the L2, as bf16 H
             cv.x = codes.x;
             cv.y = codes.y;
-            __builtin_nontemporal_store(cv, (u32x2*)((uint8_t*)p.H + hr * p.Hld + col0 + c));
+            if (st)
+              __builtin_nontemporal_store(cv, (u32x2*)((uint8_t*)p.H + hr * p.Hld + col0 + c));
+          }
+          if (st) {
             if ((c & 31) == 0)
               p.H_sc[mx_kmajor_scale(hr, (col0 + c) / 32, (int64_t)p.n_slots * p.mb)] =
                   (uint8_t)(se + 127);
@@ -1155,9 +1195,15 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
 }
 
 // LDS of a tile workgroup: the STAGES operand buffers as separate objects (only the first
-// STAGES are referenced), the MX scale words and the down stage's row table.
+// STAGES are referenced), the MX scale words and the down stage's row table. Stages 0 and 1 are
+// sized for 128-byte rows whatever the configuration's row: the epilogue stages each wave's
+// outputs through 16 KB of buffer 1's A or B half.
 #define MOK_TILE_LDS(C, sm)                                                                      \
-  __shared__ uint4 a0[C::BM][C::CH], a1[C::BM][C::CH], b0[C::BN][C::CH], b1[C::BN][C::CH];       \
+  __shared__ uint4 a0_[C::BM][8], a1_[C::BM][8], b0_[C::BN][8], b1_[C::BN][8];                   \
+  uint4(*a0)[C::CH] = (uint4(*)[C::CH])a0_;                                                      \
+  uint4(*a1)[C::CH] = (uint4(*)[C::CH])a1_;                                                      \
+  uint4(*b0)[C::CH] = (uint4(*)[C::CH])b0_;                                                      \
+  uint4(*b1)[C::CH] = (uint4(*)[C::CH])b1_;                                                      \
   __shared__ uint4 a2[C::STAGES > 2 ? C::BM : 1][C::CH], a3[C::STAGES > 2 ? C::BM : 1][C::CH];   \
   __shared__ uint4 b2[C::STAGES > 2 ? C::BN : 1][C::CH], b3[C::STAGES > 2 ? C::BN : 1][C::CH];   \
   __shared__ uint32_t as0[C::BM], as1[C::BM], bs0[C::BN], bs1[C::BN];                            \
@@ -1192,7 +1238,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
   // carried in registers from one tile to the next (across the epilogue, where the register
   // file is full), so none is spilled and reloaded with a wait that drains the epilogue's
   // stores.
-  constexpr bool PRE = UP && EL != Elem::FP8;
+  constexpr bool PRE = UP && !is_mx<EL>();
   __shared__ int32_t pre_lds[PRE ? C::A_SLABS : 1][C::NT];
   __shared__ int4 nxt_lds;
   __shared__ int nslot_lds;
@@ -1256,7 +1302,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
 // items in flight per lane: 2 in the gather launch (8 workgroups per CU), 8 in the ring loop
 // (one workgroup per CU, whose registers are free outside the GEMM tiles)
 constexpr int GQ_UNROLL_STAGE = 2, GQ_UNROLL_RING = 8;
-template <int GQ_UNROLL>
+template <int GQ_UNROLL, bool FP4>
 MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r_end, int wave,
                                   int n_waves) {
   __shared__ int64_t tok_row[G_ROWS];
@@ -1296,12 +1342,16 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
     for (int u = 0; u < GQ_UNROLL; ++u) {
       int sh;
       // both lanes of a pair share cc's validity
-      const uint4 codes = quantize_pair16(raw[u][0], raw[u][1], &sh);
-      if (cc[u] >= 0) {
-        const int64_t hr = ring0 + rr[u];
-        *(uint4*)(p.A_codes + hr * p.d + 16 * cc[u]) = codes;
-        if ((cc[u] & 1) == 0) p.A_sc[mx_kmajor_scale(hr, cc[u] / 2, R)] = (uint8_t)(sh + 127);
+      const int64_t hr = ring0 + rr[u];
+      if constexpr (FP4) {
+        const uint2 codes = mx4_pair16(raw[u][0], raw[u][1], &sh);
+        if (cc[u] >= 0) *(uint2*)(p.A_codes + hr * (p.d / 2) + 8 * cc[u]) = codes;
+      } else {
+        const uint4 codes = quantize_pair16(raw[u][0], raw[u][1], &sh);
+        if (cc[u] >= 0) *(uint4*)(p.A_codes + hr * p.d + 16 * cc[u]) = codes;
       }
+      if (cc[u] >= 0 && (cc[u] & 1) == 0)
+        p.A_sc[mx_kmajor_scale(hr, cc[u] / 2, R)] = (uint8_t)(sh + 127);
     }
   }
 }
@@ -1309,6 +1359,7 @@ MOK_DEV void gather_quantize_rows(const ExpertPass& p, int m, int r_begin, int r
 // Stage-ordered path: every minibatch's rows, before the up stage. The rows of all minibatches
 // (in work-list order) are cut into one contiguous range per workgroup, of equal size to a row;
 // a workgroup walks its range in pieces of at most 16 rows of one minibatch.
+template <bool FP4>
 __global__ __launch_bounds__(256) void k_gather_quantize(ExpertPass p) {
   constexpr int PIECE = 16;
   const int n_mb = p.wl[WL_N_MB];
@@ -1331,7 +1382,7 @@ __global__ __launch_bounds__(256) void k_gather_quantize(ExpertPass p) {
       continue;
     }
     const int32_t r1 = min(min(nr[m], r + PIECE), r + (r_hi - done));
-    gather_quantize_rows<GQ_UNROLL_STAGE>(p, m, r, r1, threadIdx.x >> 6, 4);
+    gather_quantize_rows<GQ_UNROLL_STAGE, FP4>(p, m, r, r1, threadIdx.x >> 6, 4);
     done += r1 - r;
     r = r1;
   }
@@ -1506,16 +1557,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     if (kind == KIND_U) {
       int32_t pre[C::A_SLABS];
       prefetch_a_rows<EL, true, C>(p, e, pre);
-      if constexpr (EL != Elem::FP8) route_rows<C>(p, pre);
+      if constexpr (!is_mx<EL>()) route_rows<C>(p, pre);
       run_tile<EL, true, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre, fetch_step);
     } else if (kind == KIND_D) {
       int32_t pre[C::A_SLABS];
       run_tile<EL, false, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre,
                                            fetch_step);
     } else {
-      if constexpr (EL == Elem::FP8) {
+      if constexpr (is_mx<EL>()) {
         const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
-        gather_quantize_rows<GQ_UNROLL_RING>(p, e.x, r0, r1, wid, C::NW);
+        gather_quantize_rows<GQ_UNROLL_RING, EL == Elem::FP4>(p, e.x, r0, r1, wid, C::NW);
       }
       for (int s = 0; s < 4; ++s) {
         fetch_step(s);
@@ -1607,18 +1658,19 @@ constexpr int EV_UP = 2 * 3, EV_DOWN = 2 * 4, EV_GATHER = 2 * 6;
 
 template <Elem EL, bool F32OUT>
 static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
-  if (EL == Elem::FP8 && !p.ring)
-    launch_k(k_gather_quantize, dim3(p.grid * 8), dim3(256), 0, s, nullptr,
+  typedef typename CfgOf<EL>::type C;
+  if (is_mx<EL>() && !p.ring)
+    launch_k(k_gather_quantize<EL == Elem::FP4>, dim3(p.grid * 8), dim3(256), 0, s, nullptr,
              ev_at(ev, EV_GATHER + 1), p);
   if (p.ring) {
-    launch_k(k_ring<EL, F32OUT, Big>, dim3(p.grid), dim3(Big::NT), 0, s, ev_at(ev, EV_UP),
+    launch_k(k_ring<EL, F32OUT, C>, dim3(p.grid), dim3(C::NT), 0, s, ev_at(ev, EV_UP),
              ev_at(ev, EV_UP + 1), p);
     mark_empty(s, ev_at(ev, EV_DOWN), ev_at(ev, EV_DOWN + 1));
     return hipGetLastError();
   }
-  launch_k(k_expert_stage<EL, true, F32OUT, Big>, dim3(p.grid), dim3(Big::NT), 0, s,
+  launch_k(k_expert_stage<EL, true, F32OUT, C>, dim3(p.grid), dim3(C::NT), 0, s,
            ev_at(ev, EV_UP), ev_at(ev, EV_UP + 1), p);
-  launch_k(k_expert_stage<EL, false, F32OUT, Big>, dim3(p.grid), dim3(Big::NT), 0, s,
+  launch_k(k_expert_stage<EL, false, F32OUT, C>, dim3(p.grid), dim3(C::NT), 0, s,
            ev_at(ev, EV_DOWN), ev_at(ev, EV_DOWN + 1), p);
   return hipGetLastError();
 }
@@ -1637,14 +1689,16 @@ hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const*
   const int nU_r = (p.I + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
   const int nD = (p.d + Big::BN - 1) / Big::BN;
-  const bool gather_items = p.ring && p.elem == Elem::FP8;
-  const bool gather_launch = p.elem == Elem::FP8 && !p.ring;   // ends the GATHER stage
+  const bool mx = p.elem == Elem::FP8 || p.elem == Elem::FP4;
+  const bool gather_items = p.ring && mx;
+  const bool gather_launch = mx && !p.ring;                   // ends the GATHER stage
   launch_k(k_build_worklist, dim3(1), dim3(1024), 0, s, ev_at(ev, EV_GATHER),
            gather_launch ? nullptr : ev_at(ev, EV_GATHER + 1), p.counts, p.offsets, p.E_l,
            p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.xcd_split, p.n_slots,
            p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.route_cap, p.wl);
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
+  if (p.elem == Elem::FP4) return launch_stages_t<Elem::FP4, false>(p, s, ev);
   return launch_stages_t<Elem::FP8, false>(p, s, ev);
 }
 

@@ -42,14 +42,16 @@ hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l
 __host__ __device__ inline int64_t mx_kmajor_scale(int64_t r, int b, int64_t R) {
   return ((int64_t)(b >> 2) * R + r) * 4 + (b & 3);
 }
-// scales_kmajor == 0: scales row-major [rows, K/32] (the mok_quantize_mxfp8 layout); R > 0: the
-// rows form rows / R matrices of R rows, each with K-step-major scales (mx_kmajor_scale).
-hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s, hipEvent_t e0 = nullptr,
-                                 hipEvent_t e1 = nullptr, int64_t scales_kmajor = 0);
+// MX quantiser: MXFP8 (E4M3 codes [rows, K]) or, fp4, MXFP4 (E2M1 codes [rows, K/2], element
+// 2i in the low nibble of byte i). scales_kmajor == 0: scales row-major [rows, K/32] (the
+// mok_quantize_mx* layout); R > 0: the rows form rows / R matrices of R rows, each with
+// K-step-major scales (mx_kmajor_scale).
+hipError_t launch_quantize_mx(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
+                              uint8_t* scales, bool fp4, hipStream_t s, hipEvent_t e0 = nullptr,
+                              hipEvent_t e1 = nullptr, int64_t scales_kmajor = 0);
 
 // Operand element type of the expert GEMMs.
-enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2 };
+enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2, FP4 = 3 };
 
 // Everything the expert-GEMM stages of one forward need (device pointers unless noted).
 struct ExpertPass {

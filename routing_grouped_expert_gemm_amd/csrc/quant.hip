@@ -1,7 +1,9 @@
-// MXFP8 operands (OCP Microscaling Formats v1.0: E4M3 elements, one E8M0 scale per block of
-// 32 along K). The news summary of MoK says the kernel supports BF16 and MXFP8; the format's
-// rules come from the OCP specification: shared exponent floor(log2(amax)) - 8, elements
-// rounded to nearest-even on the E4M3 grid and saturated at 448.
+// MX operands (OCP Microscaling Formats v1.0: one E8M0 scale per block of 32 along K). The
+// news summary of MoK says the kernel supports BF16 and MXFP8; MXFP4 is the 4-bit member of the
+// same family (the MoK write-up mentions earlier MXFP8 and NVFP4 training kernels). The rules
+// come from the OCP specification: shared exponent floor(log2(amax)) - emax (8 for E4M3, 2 for
+// E2M1), elements rounded to nearest-even on the element grid and saturated at its maximum
+// (448, 6).
 //
 // HBM streams: four lanes per 32-element block, each lane 16 bytes of bf16 in, 8 code bytes out,
 // the quad's first lane writing the scale byte; a wave covers 1 KB of contiguous input.
@@ -10,16 +12,15 @@
 
 namespace mok {
 
-// Row-major scales (the mok_quantize_mxfp8 layout): four lanes per 32-element block, 8
-// elements a lane. K-step-major scales (the GEMMs' operands): a wave quantises one 128-element
-// K step of 8 consecutive rows, 8 lanes a row and 16 elements a lane (two lanes a block), so
-// its 32 scale bytes -- 8 K-step-major words of consecutive rows -- are contiguous, and each
-// lane reads 32 and writes 16 bytes.
-template <bool KMAJOR>
-__global__ __launch_bounds__(256) void k_quantize_mxfp8(const bf16_t* __restrict__ src,
-                                                        int64_t rows, int K, int64_t R,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales) {
+// Row-major scales (the mok_quantize_mx* layout): four lanes per 32-element block, 8 elements a
+// lane. K-step-major scales (the GEMMs' operands): a wave quantises one 128-element K step of 8
+// consecutive rows, 8 lanes a row and 16 elements a lane (two lanes a block), so its 32 scale
+// bytes -- 8 K-step-major words of consecutive rows -- are contiguous, and each lane reads 32
+// bytes and writes 16 (MXFP8) or 8 (MXFP4). FP4: E2M1 codes, two a byte (MXFP4).
+template <bool KMAJOR, bool FP4>
+__global__ __launch_bounds__(256) void k_quantize_mx(const bf16_t* __restrict__ src, int64_t rows,
+                                                     int K, int64_t R, uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales) {
   const int64_t n_chunks = KMAJOR ? (rows + 7) / 8 * (K / 128) * 64 : rows * (K / 8);
   const int64_t stride = (int64_t)gridDim.x * 256;
   // every lane of a wave runs the same number of iterations (the quad / pair shuffles need the
@@ -42,43 +43,57 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8(const bf16_t* __restrict
         r1 = *(const uint4*)(src + at + 8);
       }
       int sh;
-      const uint4 c = quantize_pair16(r0, r1, &sh);
-      if (ok) {
-        *(uint4*)(codes + at) = c;
-        if ((c16 & 1) == 0) {
-          const int64_t g = (uint32_t)row / (uint32_t)R;   // matrix g, its row row - g R
-          scales[g * R * (K / 32) + mx_kmajor_scale(row - g * R, c16 >> 1, R)] = (uint8_t)(sh + 127);
-        }
+      if constexpr (FP4) {
+        const uint2 c = mx4_pair16(r0, r1, &sh);
+        if (ok) *(uint2*)(codes + at / 2) = c;
+      } else {
+        const uint4 c = quantize_pair16(r0, r1, &sh);
+        if (ok) *(uint4*)(codes + at) = c;
+      }
+      if (ok && (c16 & 1) == 0) {
+        const int64_t g = (uint32_t)row / (uint32_t)R;   // matrix g, its row row - g R
+        scales[g * R * (K / 32) + mx_kmajor_scale(row - g * R, c16 >> 1, R)] = (uint8_t)(sh + 127);
       }
     } else {
       const bool ok = q < n_chunks;
       const int64_t at = q * 8;
       const uint4 raw = ok ? *(const uint4*)(src + at) : make_uint4(0, 0, 0, 0);
       int sh;
-      const uint2 c = quantize_quad8(raw, &sh);
-      if (ok) {
-        *(uint2*)(codes + at) = c;
-        if ((q & 3) == 0) scales[at >> 5] = (uint8_t)(sh + 127);
+      if constexpr (FP4) {
+        const uint32_t c = mx4_quad8(raw, &sh);
+        if (ok) *(uint32_t*)(codes + at / 2) = c;
+      } else {
+        const uint2 c = quantize_quad8(raw, &sh);
+        if (ok) *(uint2*)(codes + at) = c;
       }
+      if (ok && (q & 3) == 0) scales[at >> 5] = (uint8_t)(sh + 127);
     }
   }
 }
 
-hipError_t launch_quantize_mxfp8(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
-                                 int64_t scales_kmajor) {
+hipError_t launch_quantize_mx(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
+                              uint8_t* scales, bool fp4, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1, int64_t scales_kmajor) {
   const int64_t n_chunks = scales_kmajor > 0 ? (rows + 7) / 8 * (K / 128) * 64 : rows * (K / 8);
   if (n_chunks == 0) return mark_empty(s, e0, e1), hipSuccess;
   if (scales_kmajor > 0 && (rows >= INT32_MAX || n_chunks / 64 >= INT32_MAX))
     return hipErrorInvalidValue;                  // the K-major index math is 32-bit
   const int64_t want = (n_chunks + 255) / 256;
   const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
-  if (scales_kmajor > 0)
-    launch_k(k_quantize_mxfp8<true>, dim3(grid), dim3(256), 0, s, e0, e1, (const bf16_t*)src_bf16,
-             rows, K, scales_kmajor, codes, scales);
+  const bf16_t* src = (const bf16_t*)src_bf16;
+  const int64_t R = scales_kmajor > 0 ? scales_kmajor : 0;
+  if (scales_kmajor > 0 && fp4)
+    launch_k(k_quantize_mx<true, true>, dim3(grid), dim3(256), 0, s, e0, e1, src, rows, K, R,
+             codes, scales);
+  else if (scales_kmajor > 0)
+    launch_k(k_quantize_mx<true, false>, dim3(grid), dim3(256), 0, s, e0, e1, src, rows, K, R,
+             codes, scales);
+  else if (fp4)
+    launch_k(k_quantize_mx<false, true>, dim3(grid), dim3(256), 0, s, e0, e1, src, rows, K, R,
+             codes, scales);
   else
-    launch_k(k_quantize_mxfp8<false>, dim3(grid), dim3(256), 0, s, e0, e1, (const bf16_t*)src_bf16,
-             rows, K, (int64_t)0, codes, scales);
+    launch_k(k_quantize_mx<false, false>, dim3(grid), dim3(256), 0, s, e0, e1, src, rows, K, R,
+             codes, scales);
   return hipGetLastError();
 }
 

@@ -131,7 +131,7 @@ def seeded_permutation(seed: int, stream: int, n: int) -> torch.Tensor:
 class Workload:
     """Shapes of one MoE-layer forward (or one rank's share of it)."""
     name: str
-    dtype: str                 # "fp32" | "bf16" | "mxfp8"
+    dtype: str                 # "fp32" | "bf16" | "mxfp8" | "mxfp4"
     T_pool: int                # rows in the token pool held in HBM
     d: int                     # model dim
     E: int                     # routed experts in the whole layer
@@ -188,9 +188,15 @@ WORKLOADS = {
         T_pool=196608, d=7168, E=384, k=8, I=2048, e0=0, E_l=4, tokens_per_rank=2048,
         own_begin=0, T_own=2048, n_shared=1, I_shared=2048, routing="logits",
         zipf_beta=ZIPF_BETA_EP96, ring_rows=16384, minibatch_rows=512),
+    # the MXFP8 share's shapes with MXFP4 operands (the MX sibling of the MXFP8 path)
+    "ep64_share_mxfp4_pool262144_d7168_e256_top8": Workload(
+        name="ep64_share_mxfp4_pool262144_d7168_e256_top8", dtype="mxfp4", T_pool=262144,
+        d=7168, E=256, k=8, I=2048, e0=0, E_l=4, tokens_per_rank=4096, own_begin=0,
+        T_own=4096, n_shared=1, I_shared=2048, routing="logits", ring_rows=16384,
+        minibatch_rows=512),
 }
 
-TINY, EP1, EP64, EP64_MX, EP96 = list(WORKLOADS)
+TINY, EP1, EP64, EP64_MX, EP96, EP64_MX4 = list(WORKLOADS)
 
 
 def scaled(w: Workload, **kw) -> Workload:

@@ -16,7 +16,7 @@ def rel_err(got, ref) -> float:
     return float(np.abs(got - ref).max() / (den if den > 0 else 1.0))
 
 
-TOL = {"fp32": 1e-4, "bf16": 1e-2, "mxfp8": 3e-2}
+TOL = {"fp32": 1e-4, "bf16": 1e-2, "mxfp8": 3e-2, "mxfp4": 3e-2}
 
 
 def make_inputs(wl: synth.Workload, device) -> dict:

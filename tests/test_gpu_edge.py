@@ -118,7 +118,7 @@ def test_no_shared_expert(ring):
     _compare(wl, inp, layer)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8", "mxfp4"])
 def test_share_without_own_tokens(dtype):
     import routing_grouped_expert_gemm_amd as mok
     wl = synth.scaled(BASE, dtype=dtype, I=256, E_l=4, e0=0, routing="logits",
@@ -142,7 +142,8 @@ def _written(layer):
 
 
 @pytest.mark.parametrize("name,ring", [("full_bf16", True), ("full_bf16", False),
-                                       ("share_mxfp8", False), ("share_mxfp8", True)])
+                                       ("share_mxfp8", False), ("share_mxfp8", True),
+                                       ("share_mxfp4", False)])
 def test_forward_captured_in_a_hip_graph(name, ring):
     """The forward records into a HIP graph (so it makes no host synchronisation and reads
     nothing back), and every replay -- with eager work and synchronisations between them --

@@ -36,7 +36,7 @@ def _check_plan(layer, ref_plan):
 def _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng, n_routes=1024, n_own=None):
     """Sampled route slots (default 1024) and the own tokens' shared output (default: all of
     them) against the oracle, float64; idx and w are the oracle's own routing."""
-    mx = wl.dtype == "mxfp8"
+    mx = wl.dtype if wl.dtype in ("mxfp8", "mxfp4") else False
     tol = TOL[wl.dtype]
     rids = plan["route_ids"].astype(np.int64)
     pick = rids[_sample(rng, len(rids), n_routes)]
@@ -107,7 +107,8 @@ def test_ep1_full_layer_bf16(ring):
 
 
 @pytest.mark.parametrize("name,ring", [(synth.EP64, False), (synth.EP64, True),
-                                       (synth.EP64_MX, False), (synth.EP96, False)])
+                                       (synth.EP64_MX, False), (synth.EP96, False),
+                                       (synth.EP64_MX4, False)])
 def test_share_workloads(name, ring):
     """One rank's share: pool of 64 x 4096 (or 96 x 2048) tokens, d=7168, 4 local experts.
     Routing and plan bit-exact over the whole pool; 1024 sampled route slots and every own
@@ -131,7 +132,7 @@ def test_share_workloads(name, ring):
         assert plan["counts"].tolist() == EP96_COUNTS   # calibrated Zipf load
     rng = np.random.default_rng(12)
     _check_sampled_outputs(wl, layer, cpu, idx, w, plan, rng)
-    _reruns_bit_identical(layer, plan, 10 if wl.dtype == "mxfp8" else 2)
+    _reruns_bit_identical(layer, plan, 10 if wl.dtype.startswith("mx") else 2)
 
 
 def test_zipf_share_minibatch_sweep_bit_identical():

@@ -157,6 +157,28 @@ def test_quantize_mxfp8_exhaustive_bf16_patterns():
     assert np.array_equal(to_np(codes), rc)
 
 
+def test_quantize_mxfp4_exhaustive_bf16_patterns():
+    """Every finite bf16 pattern through mok_quantize_mxfp4, bit-exact against the oracle's
+    MXFP4 codes (two a byte) and scales."""
+    import routing_grouped_expert_gemm_amd as mok
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    f = f[np.isfinite(f)]
+    rng = np.random.default_rng(19)
+    f = np.concatenate([f, rng.permutation(f)])
+    f = f[: (len(f) // 256) * 256].reshape(-1, 256)
+    f[::7, 5] = 0.0
+    f[3] = 0.0
+    src = torch.from_numpy(f).to(torch.bfloat16)
+    codes = torch.empty((src.shape[0], 128), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((src.shape[0], 8), dtype=torch.uint8, device=DEV)
+    mok.mok_quantize_mxfp4(src.to(DEV), codes, scales)
+    _sync()
+    rc, rs = oracle.mxfp4_quantize(src)
+    assert np.array_equal(to_np(scales), rs)
+    assert np.array_equal(to_np(codes), rc)
+
+
 # --------------------------------------------------------------------- layer, small sizes
 
 SMALL = {
@@ -169,6 +191,10 @@ SMALL = {
                                own_begin=512, T_own=256, I_shared=256, minibatch_rows=128,
                                ring_rows=1024),
     "share_mxfp8": synth.scaled(synth.WORKLOADS[synth.EP64_MX], name="share_mxfp8", T_pool=2048,
+                                d=256, E=64, k=8, I=256, e0=4, E_l=4, tokens_per_rank=256,
+                                own_begin=256, T_own=256, I_shared=128, minibatch_rows=128,
+                                ring_rows=1024),
+    "share_mxfp4": synth.scaled(synth.WORKLOADS[synth.EP64_MX4], name="share_mxfp4", T_pool=2048,
                                 d=256, E=64, k=8, I=256, e0=4, E_l=4, tokens_per_rank=256,
                                 own_begin=256, T_own=256, I_shared=128, minibatch_rows=128,
                                 ring_rows=1024),
@@ -225,7 +251,7 @@ def test_layer_small_matches_oracle(name):
     _run_and_compare(SMALL[name], mok.MOK_FLAG_NO_RING)
 
 
-@pytest.mark.parametrize("name", ["full_bf16", "share_mxfp8"])
+@pytest.mark.parametrize("name", ["full_bf16", "share_mxfp8", "share_mxfp4"])
 def test_layer_reruns_bit_identical_and_minibatch_invariant(name):
     import routing_grouped_expert_gemm_amd as mok
     wl = SMALL[name]

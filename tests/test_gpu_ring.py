@@ -64,7 +64,8 @@ def test_ring_small_layers_match_oracle(name):
         assert rel_err(to_np(layer.y), ref["y"]) <= tol
 
 
-@pytest.mark.parametrize("name", ["full_bf16", "share_mxfp8", "zipf_bf16", "tiny_fp32"])
+@pytest.mark.parametrize("name", ["full_bf16", "share_mxfp8", "share_mxfp4", "zipf_bf16",
+                                  "tiny_fp32"])
 def test_ring_bit_identical_to_stage_order_any_ring_and_minibatch(name):
     """Ring capacities down to a single slot (every minibatch waits for the previous one's
     down tiles) and minibatch sizes 128..1024 all give the stage-ordered bits."""
@@ -96,7 +97,7 @@ def test_ring_reruns_bit_identical():
             assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", [synth.EP96, synth.EP64_MX])
+@pytest.mark.parametrize("name", [synth.EP96, synth.EP64_MX, synth.EP64_MX4])
 def test_ring_full_share_workloads(name):
     """The skewed 384-expert share with its 16384-row ring at minibatch sizes 128..1024, and
     the MXFP8 share (gather + quantise items in the ring): bit-identical to the stage-ordered
@@ -129,7 +130,7 @@ def test_ring_full_share_workloads(name):
     n = len(rids)
     rng = np.random.default_rng(7)
     pick = np.sort(rng.choice(rids, size=min(1024, n), replace=False))
-    mx = wl.dtype == "mxfp8"
+    mx = wl.dtype if wl.dtype in ("mxfp8", "mxfp4") else False
     refp = oracle.route_outputs(pick, cpu["x"][torch.from_numpy(pick // wl.k)], idx, w, wl.e0,
                                 cpu["wg"], cpu["wu"], cpu["wd"], mx)
     assert rel_err(to_np(layer.y_slots[torch.from_numpy(pick).to(DEV)]), refp) <= TOL[wl.dtype]
