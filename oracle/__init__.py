@@ -278,3 +278,96 @@ def moe_forward(wl, x, w_router=None, logits=None, wg=None, wu=None, wd=None, sg
         for j in range(wl.k):
             y += slot[j::wl.k]
     return dict(idx=idx, w=w, plan=plan, P=P, y_shared=S, y=y)
+
+
+# ------------------------------------------------------------------------ backward
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d silu / dz = sigma(z) (1 + z (1 - sigma(z)))."""
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def swiglu_ffn_backward(a, w_gate, w_up, w_down, d_out, scale=1.0):
+    """Backward of out = scale * W_down (silu(W_gate a) * (W_up a)) for the rows of a (float64).
+
+    d_out: gradient of out, [rows, d]; scale: a per-row weight ([rows] or a number). Returns
+    dict(da, dw_gate, dw_up, dw_down, dscale) where dscale[r] = <d_out[r], FFN(a[r])> (the
+    gradient of the per-row weight)."""
+    a = np.asarray(a, np.float64)
+    wg, wu, wd = (np.asarray(t, np.float64) for t in (w_gate, w_up, w_down))
+    dout = np.asarray(d_out, np.float64)
+    sc = np.broadcast_to(np.asarray(scale, np.float64), (a.shape[0],))[:, None]
+    g = a @ wg.T
+    u = a @ wu.T
+    h = silu(g) * u
+    o = h @ wd.T                                  # unscaled expert output
+    dscale = (dout * o).sum(1)
+    do = sc * dout                                # gradient of o
+    dh = do @ wd
+    dg = dh * u * silu_grad(g)
+    du = dh * silu(g)
+    return dict(da=dg @ wg + du @ wu, dw_gate=dg.T @ a, dw_up=du.T @ a, dw_down=do.T @ h,
+                dscale=dscale)
+
+
+def moe_backward(wl, x, topk_idx, topk_w, wg, wu, wd, sg=None, su=None, sd=None, dy=None,
+                 dy_slots=None, dy_shared=None) -> dict:
+    """Backward of the layer (or share) of moe_forward with the routing held fixed, in float64.
+
+    Upstream gradient: dy [T_pool, d] for the whole layer (each route slot and the shared
+    output then receive dy of their token), or dy_slots [T_pool*k, d] and dy_shared [T_own, d]
+    for a share. Returns the gradient of every input the forward multiplies:
+      dx_slots  [n_local_routes, d]  d x[t] through local route r (row i for plan route_ids[i])
+      dx_shared [T_own, d]           d x through the shared experts (summed over them)
+      dx        [T_pool, d] or None  whole layer: dx_shared + sum_j dx through route t*k+j
+      dtopk_w   [n_local_routes]     d w[t,j] of local route r = <dP_r, FFN_e(x_t)>
+      dwg, dwu [E_l, I, d], dwd [E_l, d, I]; dsg, dsu [n_s, I_s, d], dsd [n_s, d, I_s]."""
+    idx = np.asarray(topk_idx)
+    w = np.asarray(topk_w, np.float64)
+    plan = dispatch_plan(idx, wl.e0, wl.E_l, wl.tokens_per_rank)
+    rids = plan["route_ids"].astype(np.int64)
+    xf = _f32(x).astype(np.float64)
+    k = wl.k
+    if dy is not None:
+        dyf = _f32(dy).astype(np.float64)
+        dP = dyf[rids // k]
+        dS = dyf[wl.own_begin:wl.own_begin + wl.T_own]
+    else:
+        dP = _f32(dy_slots).astype(np.float64)[rids]
+        dS = _f32(dy_shared).astype(np.float64) if wl.n_shared else None
+    wg, wu, wd = _f32(wg), _f32(wu), _f32(wd)
+    dwg, dwu, dwd = np.zeros(wg.shape), np.zeros(wu.shape), np.zeros(wd.shape)
+    dx_slots = np.zeros((len(rids), wl.d))
+    dtw = np.zeros(len(rids))
+    experts = idx.reshape(-1)[rids] - wl.e0
+    for le in range(wl.E_l):
+        sel = np.nonzero(experts == le)[0]
+        if len(sel) == 0:
+            continue
+        r = swiglu_ffn_backward(xf[rids[sel] // k], wg[le], wu[le], wd[le], dP[sel],
+                                w.reshape(-1)[rids[sel]])
+        dx_slots[sel] = r["da"]
+        dtw[sel] = r["dscale"]
+        dwg[le], dwu[le], dwd[le] = r["dw_gate"], r["dw_up"], r["dw_down"]
+    out = dict(plan=plan, dx_slots=dx_slots, dtopk_w=dtw, dwg=dwg, dwu=dwu, dwd=dwd)
+    own = xf[wl.own_begin:wl.own_begin + wl.T_own]
+    dx_shared = np.zeros((wl.T_own, wl.d))
+    if wl.n_shared:
+        sg, su, sd = _f32(sg), _f32(su), _f32(sd)
+        dsg, dsu, dsd = np.zeros(sg.shape), np.zeros(su.shape), np.zeros(sd.shape)
+        for s in range(wl.n_shared):
+            r = swiglu_ffn_backward(own, sg[s], su[s], sd[s], dS)
+            dx_shared += r["da"]
+            dsg[s], dsu[s], dsd[s] = r["dw_gate"], r["dw_up"], r["dw_down"]
+        out.update(dsg=dsg, dsu=dsu, dsd=dsd)
+    out["dx_shared"] = dx_shared
+    out["dx"] = None
+    if wl.full_layer:
+        slot = np.zeros((wl.T_pool * k, wl.d))
+        slot[rids] = dx_slots
+        dx = dx_shared.copy()
+        for j in range(k):
+            dx += slot[j::k]
+        out["dx"] = dx
+    return out

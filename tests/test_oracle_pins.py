@@ -465,3 +465,76 @@ def test_mxfp4_layer_uses_dequantised_operands():
     out8 = oracle.moe_forward(synth.scaled(wl, dtype="mxfp8"), x, w_router=wr, wg=wg, wu=wu,
                               wd=wd, sg=sg, su=su, sd=sd)
     assert np.abs(out["y"] - out8["y"]).max() > 1e-3
+
+
+# ----------------------------------------------------------------- backward
+
+def _fd_layer(seed=3, T=6, d=8, E=4, k=2, I=6, n_s=2, I_s=4):
+    """A tiny layer in float64 with fixed routing, its loss sum(dy * y) and the pieces."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wg, wu = rng.standard_normal((E, I, d)) / 3, rng.standard_normal((E, I, d)) / 3
+    wd = rng.standard_normal((E, d, I)) / 3
+    sg, su = rng.standard_normal((n_s, I_s, d)) / 3, rng.standard_normal((n_s, I_s, d)) / 3
+    sd = rng.standard_normal((n_s, d, I_s)) / 3
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)) + 0.2
+    dy = rng.standard_normal((T, d))
+
+    def loss(x, wg, wu, wd, sg, su, sd, w):
+        y = np.zeros((T, d))
+        for t in range(T):
+            for j in range(k):
+                e = idx[t, j]
+                y[t] += w[t, j] * oracle.swiglu_ffn(x[t:t + 1], wg[e], wu[e], wd[e])[0]
+            for s in range(n_s):
+                y[t] += oracle.swiglu_ffn(x[t:t + 1], sg[s], su[s], sd[s])[0]
+        return float((dy * y).sum())
+
+    wl = synth.scaled(synth.WORKLOADS[synth.TINY], T_pool=T, d=d, E=E, k=k, I=I, E_l=E,
+                      tokens_per_rank=T, T_own=T, n_shared=n_s, I_shared=I_s, dtype="fp32")
+    return wl, dict(x=x, wg=wg, wu=wu, wd=wd, sg=sg, su=su, sd=sd, w=w), idx, dy, loss
+
+
+def test_backward_matches_finite_differences_of_the_forward():
+    """Every gradient of the oracle's backward equals the central difference of the oracle's
+    forward loss sum(dy * y) (float64, step 1e-6): x, all routed and shared weights and the
+    routing weights. A dropped term, a wrong sign or a transposed operand fails here."""
+    wl, P, idx, dy, loss = _fd_layer()
+    g = oracle.moe_backward(wl, P["x"], idx, P["w"], P["wg"], P["wu"], P["wd"], P["sg"],
+                            P["su"], P["sd"], dy=dy)
+    # dtopk_w is per local route in plan order; put it back at [t, j]
+    dw = np.zeros(idx.size)
+    dw[g["plan"]["route_ids"]] = g["dtopk_w"]
+    grads = dict(x=g["dx"], wg=g["dwg"], wu=g["dwu"], wd=g["dwd"], sg=g["dsg"], su=g["dsu"],
+                 sd=g["dsd"], w=dw.reshape(idx.shape))
+    rng = np.random.default_rng(4)
+    h = 1e-6
+    for name, grad in grads.items():
+        for _ in range(6):
+            pos = tuple(rng.integers(0, n) for n in P[name].shape)
+            Pp = {kk: v.copy() for kk, v in P.items()}
+            Pm = {kk: v.copy() for kk, v in P.items()}
+            Pp[name][pos] += h
+            Pm[name][pos] -= h
+            fd = (loss(**Pp) - loss(**Pm)) / (2 * h)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
+def test_backward_share_equals_full_layer_routes():
+    """A share's slot gradients and weight gradients are the full layer's at the share's
+    experts when its slots receive the same upstream gradient."""
+    wl, P, idx, dy, _ = _fd_layer(T=8)
+    full = oracle.moe_backward(wl, P["x"], idx, P["w"], P["wg"], P["wu"], P["wd"], P["sg"],
+                               P["su"], P["sd"], dy=dy)
+    share = synth.scaled(wl, e0=1, E_l=2, tokens_per_rank=4, own_begin=4, T_own=4)
+    slots = np.repeat(dy, wl.k, axis=0)
+    part = oracle.moe_backward(share, P["x"], idx, P["w"], P["wg"][1:3], P["wu"][1:3],
+                               P["wd"][1:3], P["sg"], P["su"], P["sd"], dy_slots=slots,
+                               dy_shared=dy[4:8])
+    fr = full["plan"]["route_ids"]
+    loc = (idx.reshape(-1)[fr] >= 1) & (idx.reshape(-1)[fr] < 3)
+    np.testing.assert_allclose(part["dx_slots"], full["dx_slots"][loc], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dtopk_w"], full["dtopk_w"][loc], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dwg"], full["dwg"][1:3], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dx_shared"], full["dx_shared"][4:8], rtol=1e-12, atol=1e-12)
