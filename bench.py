@@ -12,6 +12,7 @@ stage-ordered expert launches; the same line carries
   "ring":  that layer with the persistent ring work loop (the library default), and
   "mxfp8": the MXFP8 EP=64 share (262144-row pool, d=7168, 4 local experts + 1 shared),
   "mxfp4": the same share with MXFP4 operands, and
+  "backward": the EP=1 layer's backward (mok_moe_backward), and
   "dispatch": pull gather against the push baseline on that share's routing,
 each timed the same way (W warm-up steps, K timed steps between device synchronisations).
 --workload NAME measures that workload alone (used by the profiling runs).
@@ -690,6 +691,49 @@ def measure_dispatch(steps: int, warmup: int, dev="cuda:0") -> dict:
     return res
 
 
+def measure_backward(steps: int, warmup: int, dev="cuda:0") -> dict:
+    """Backward of the EP=1 bf16 layer (mok_moe_backward) with the forward's routing, HIP-event
+    time per step (each step after a 1 GiB scratch write). Its GEMMs execute 16*d*I FLOPs per
+    routed row (gate/up recompute 4, dgrad 6, wgrad 6) and 16*d*I_s*n_s per own token."""
+    import torch
+    import routing_grouped_expert_gemm_amd as mok
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _layer import gpu_layer, make_inputs
+    wl = synth.WORKLOADS[synth.EP1]
+    inp = make_inputs(wl, dev)
+    fwd = gpu_layer(wl, inp, flags=mok.MOK_FLAG_NO_RING, keep=True)
+    fwd.forward()
+    dy = synth.normal_rows(0, 21, wl.d, range(wl.T_pool), 1.0, torch.bfloat16, dev)
+    b = mok.MoeBackward(d=wl.d, E=wl.E, k=wl.k, I=wl.I, e0=wl.e0, E_l=wl.E_l,
+                        tokens_per_rank=wl.tokens_per_rank, T_pool=wl.T_pool, own_begin=0,
+                        T_own=wl.T_own, n_shared=wl.n_shared, I_shared=wl.I_shared, x=inp["x"],
+                        topk_idx=fwd.inter["topk_idx"], topk_w=fwd.inter["topk_w"],
+                        w_gate=inp["wg"], w_up=inp["wu"], w_down=inp["wd"], ws_gate=inp["sg"],
+                        ws_up=inp["su"], ws_down=inp["sd"], dy=dy, device=dev)
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    t = 0.0
+    for i in range(warmup + steps):
+        scratch.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.backward()
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            t += e0.elapsed_time(e1) / steps
+    assert b.device_error() == 0
+    n = int(fwd.inter["offsets"][-1])
+    I_sh = wl.n_shared * wl.I_shared
+    flop = 16.0 * wl.d * wl.I * n + 16.0 * wl.d * I_sh * wl.T_own
+    ach = flop / (t * 1e-3)
+    return {"workload": wl.name, "ms": round(t, 4), "tokens_per_s": round(wl.T_pool / (t * 1e-3), 1),
+            "gemm_flop": flop, "achieved_tflops": round(ach / 1e12, 2), "peak_tflops": 2500.0,
+            "frac": round(ach / PEAK["bf16"], 4),
+            "note": "cold-cache HIP-event time of one mok_moe_backward (plan, gathers, 5 grouped "
+                    "GEMM launches, SwiGLU backward, scatter, combine)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -705,6 +749,8 @@ def main():
                     help="write the profiles/ summaries from a rocprofv3 output directory and exit")
     ap.add_argument("--dispatch", action="store_true",
                     help="only the pull-versus-push dispatch comparison (one JSON line)")
+    ap.add_argument("--backward", action="store_true",
+                    help="only the backward of the EP=1 layer (one JSON line)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -732,6 +778,10 @@ def main():
 
     import synth
     torch.cuda.set_device(0)
+    if args.backward:
+        print(json.dumps({"mode": "backward", "steps": args.steps, "warmup": args.warmup,
+                          **measure_backward(args.steps, args.warmup)}))
+        return
     if args.dispatch:
         print(json.dumps({"mode": "dispatch", "steps": args.steps, "warmup": args.warmup,
                           **measure_dispatch(args.steps, args.warmup)}))
@@ -773,6 +823,9 @@ def main():
         out["mxfp4"] = {k: m4[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                            "routed_rows", "routed_tflops", "gemm_tflops",
                                            "stage_ms", "roofline", "hbm")}
+        # the backward of the headline layer
+        out["backward"] = measure_backward(min(args.steps, 10), min(args.warmup, 3))
+        torch.cuda.empty_cache()
         # pull gather against the push baseline on the EP=64 share's routing
         out["dispatch"] = measure_dispatch(min(args.steps, 10), min(args.warmup, 3))
         torch.cuda.empty_cache()

@@ -246,6 +246,58 @@ int mok_moe_forward(const mok_moe_args* args, void* stream);
 int mok_moe_workspace_region(const mok_moe_args* args, int32_t region, size_t* offset,
                              size_t* bytes, int64_t* rows);
 
+/* ---------------------------------------------------------------- backward
+ * Gradients of the layer (or share) of mok_moe_forward with the routing held fixed (the routing
+ * itself -- router projection, top-k -- is not differentiated here: its weights' gradient
+ * arrives through dtopk_w). The MoK write-up presents MoK as a training kernel (introduction);
+ * the Telegram post reports its forward and backward speed-ups ("Method and experiments").
+ * Through the same pull plan as the forward, per local route r = t*k + j of expert e with
+ * a = x[t], g = Wg a, u = Wu a, h = silu(g) u, and slot gradient dP_r:
+ *   dtopk_w[r]   = <dP_r, Wd h>                        (routing-weight gradient)
+ *   dh = w_r Wd^T dP_r;  dg = dh u silu'(g);  du = dh silu(g)
+ *   dx_slots[r]  = Wg^T dg + Wu^T du                   (source-indexed, like y_slots)
+ *   dw_gate[e] += dg a^T,  dw_up[e] += du a^T,  dw_down[e] += w_r dP_r h^T
+ * and the same, unweighted, for the shared experts on the own tokens (dx_shared sums them).
+ * Whole layer (E_l == E): dP_r = dy[t] and the shared gradient is dy[own]; dx = dx_shared +
+ * sum_{j ascending} dx_slots[t*k + j] (the forward's fixed-order combine). Share: dy_slots
+ * [T_pool*k, d] (read at local routes) and dy_shared [T_own, d].
+ * BF16 only (MOK_EUNSUPPORTED otherwise): bf16 inputs and dx, float32 weight gradients
+ * (overwritten, not accumulated), float32 accumulation throughout. Deterministic: no atomics;
+ * every sum has a fixed order. route_rows_cap bounds the routed rows the workspace holds
+ * (0: the worst case T_pool * min(k, E_l)); a plan with more local routes computes nothing
+ * past the plan and sets MOK_DEVERR_OVERFLOW (mok_moe_backward_error). */
+typedef struct mok_moe_bwd_args {
+  int32_t dtype;           /* MOK_BF16                                                      */
+  int32_t d, E, k, I, e0, E_l, tokens_per_rank;   /* as mok_moe_args (d % 128, I % 64)     */
+  int64_t T_pool, own_begin;
+  int32_t T_own, n_shared, I_shared;              /* I_shared % 64                         */
+  int64_t route_rows_cap;  /* 0 = worst case                                                */
+  /* forward inputs (device) */
+  const void* x;           /* [T_pool, d] bf16                                              */
+  const int32_t* topk_idx; /* [T_pool, k] the forward's routing                             */
+  const float* topk_w;     /* [T_pool, k]                                                   */
+  const void *w_gate, *w_up, *w_down;     /* [E_l, I, d], [E_l, I, d], [E_l, d, I] bf16     */
+  const void *ws_gate, *ws_up, *ws_down;  /* shared: [n_s, I_s, d], .., [n_s, d, I_s]       */
+  /* upstream gradient (device, bf16): dy for a whole layer, else dy_slots and dy_shared */
+  const void* dy;          /* [T_pool, d]                                                   */
+  const void* dy_slots;    /* [T_pool * k, d]                                               */
+  const void* dy_shared;   /* [T_own, d]                                                    */
+  void* workspace;         /* device, >= mok_moe_backward_workspace_bytes                   */
+  size_t workspace_bytes;
+  /* outputs (device) */
+  void* dx_slots;          /* [T_pool * k, d] bf16, written at local routes only            */
+  void* dx_shared;         /* [T_own, d] bf16 (n_shared > 0 and T_own > 0)                  */
+  void* dx;                /* [T_pool, d] bf16, whole layer only (else NULL)                */
+  float* dtopk_w;          /* [T_pool, k], written at local routes only; may be NULL        */
+  float *dw_gate, *dw_up, *dw_down;       /* float32, the weights' shapes                   */
+  float *dws_gate, *dws_up, *dws_down;    /* float32 (n_shared > 0)                         */
+} mok_moe_bwd_args;
+int mok_moe_backward_workspace_bytes(const mok_moe_bwd_args* args, size_t* bytes);
+int mok_moe_backward(const mok_moe_bwd_args* args, void* stream);
+/* SYNCHRONOUS (opt-in): waits for `stream`, then reads the backward's device error word. */
+int mok_moe_backward_error(const void* workspace, const mok_moe_bwd_args* args, uint32_t* err,
+                           void* stream);
+
 /* ---------------------------------------------------------------- pull vs push dispatch
  * Two ways to bring each local expert its token rows, measured side by side (the Telegram post
  * on MoK, "Method and experiments": pushing needs a contended slot counter per expert and

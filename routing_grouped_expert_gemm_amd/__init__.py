@@ -31,7 +31,8 @@ MOK_DEVERR_OVERFLOW, MOK_DEVERR_WAIT = 1, 2
 EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
            "mok_dispatch_plan_workspace_bytes", "mok_dispatch_plan", "mok_dispatch_plan_noalloc",
            "mok_moe_workspace_bytes",
-           "mok_moe_forward", "mok_moe_workspace_region", "mok_pull_gather",
+           "mok_moe_forward", "mok_moe_workspace_region", "mok_moe_backward",
+           "mok_moe_backward_workspace_bytes", "mok_moe_backward_error", "mok_pull_gather",
            "mok_push_dispatch", "mok_quantize_mxfp8", "mok_quantize_mxfp4",
            "mok_get_device_error"]
 
@@ -69,6 +70,22 @@ class MoeArgs(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    """Mirror of struct mok_moe_bwd_args."""
+    _fields_ = [
+        ("dtype", _I32), ("d", _I32), ("E", _I32), ("k", _I32), ("I", _I32), ("e0", _I32),
+        ("E_l", _I32), ("tokens_per_rank", _I32), ("T_pool", _I64), ("own_begin", _I64),
+        ("T_own", _I32), ("n_shared", _I32), ("I_shared", _I32), ("route_rows_cap", _I64),
+        ("x", _P), ("topk_idx", _P), ("topk_w", _P), ("w_gate", _P), ("w_up", _P),
+        ("w_down", _P), ("ws_gate", _P), ("ws_up", _P), ("ws_down", _P),
+        ("dy", _P), ("dy_slots", _P), ("dy_shared", _P),
+        ("workspace", _P), ("workspace_bytes", _SZ),
+        ("dx_slots", _P), ("dx_shared", _P), ("dx", _P), ("dtopk_w", _P),
+        ("dw_gate", _P), ("dw_up", _P), ("dw_down", _P),
+        ("dws_gate", _P), ("dws_up", _P), ("dws_down", _P),
+    ]
+
+
 _lib.mok_status_string.argtypes = [ctypes.c_int]
 _lib.mok_status_string.restype = ctypes.c_char_p
 _lib.mok_version.argtypes = []
@@ -84,6 +101,10 @@ _lib.mok_moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeArgs), ctypes.POINTER
 _lib.mok_moe_forward.argtypes = [ctypes.POINTER(MoeArgs), _P]
 _lib.mok_moe_workspace_region.argtypes = [ctypes.POINTER(MoeArgs), _I32, ctypes.POINTER(_SZ),
                                           ctypes.POINTER(_SZ), ctypes.POINTER(_I64)]
+_lib.mok_moe_backward_workspace_bytes.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(_SZ)]
+_lib.mok_moe_backward.argtypes = [ctypes.POINTER(BwdArgs), _P]
+_lib.mok_moe_backward_error.argtypes = [_P, ctypes.POINTER(BwdArgs), ctypes.POINTER(ctypes.c_uint32),
+                                        _P]
 _lib.mok_quantize_mxfp8.argtypes = [_P, _I64, _I32, _P, _P, _P]
 _lib.mok_quantize_mxfp4.argtypes = [_P, _I64, _I32, _P, _P, _P]
 _lib.mok_pull_gather.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _I32, _P, _P]
@@ -296,3 +317,63 @@ class MoeLayer:
         mok_moe_workspace_region. Read it after the forward has finished."""
         off, n, rows = mok_moe_workspace_region(self.args, region)
         return self.workspace[off:off + n], rows
+
+
+class MoeBackward:
+    """Argument struct, workspace and outputs of one backward configuration (mok_moe_backward).
+
+    Whole layer: pass dy [T_pool, d]. Share: dy_slots [T_pool*k, d] and dy_shared [T_own, d].
+    Outputs: dx_slots, dx_shared, dx (whole layer), dtopk_w, dw_* and dws_* (float32)."""
+
+    def __init__(self, *, d: int, E: int, k: int, I: int, e0: int, E_l: int,
+                 tokens_per_rank: int, T_pool: int, own_begin: int, T_own: int, n_shared: int,
+                 I_shared: int, x, topk_idx, topk_w, w_gate, w_up, w_down, ws_gate=None,
+                 ws_up=None, ws_down=None, dy=None, dy_slots=None, dy_shared=None,
+                 route_rows_cap: int = 0, device="cuda"):
+        import torch
+        self._keep = [x, topk_idx, topk_w, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy,
+                      dy_slots, dy_shared]
+        a = BwdArgs()
+        a.dtype, a.d, a.E, a.k, a.I, a.e0, a.E_l = MOK_BF16, d, E, k, I, e0, E_l
+        a.tokens_per_rank, a.T_pool, a.own_begin, a.T_own = tokens_per_rank, T_pool, own_begin, T_own
+        a.n_shared, a.I_shared, a.route_rows_cap = n_shared, I_shared, route_rows_cap
+        a.x, a.topk_idx, a.topk_w = _ptr(x), _ptr(topk_idx), _ptr(topk_w)
+        a.w_gate, a.w_up, a.w_down = _ptr(w_gate), _ptr(w_up), _ptr(w_down)
+        a.ws_gate, a.ws_up, a.ws_down = _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down)
+        a.dy, a.dy_slots, a.dy_shared = _ptr(dy), _ptr(dy_slots), _ptr(dy_shared)
+        bf, f32 = dict(dtype=torch.bfloat16, device=device), dict(dtype=torch.float32, device=device)
+        self.dx_slots = torch.empty((T_pool * k, d), **bf)
+        sh = n_shared > 0 and T_own > 0
+        self.dx_shared = torch.empty((T_own, d), **bf) if sh else None
+        self.dx = torch.empty((T_pool, d), **bf) if E_l == E else None
+        self.dtopk_w = torch.empty((T_pool, k), **f32)
+        self.dw_gate = torch.empty((E_l, I, d), **f32)
+        self.dw_up = torch.empty((E_l, I, d), **f32)
+        self.dw_down = torch.empty((E_l, d, I), **f32)
+        if n_shared:
+            self.dws_gate = torch.empty((n_shared, I_shared, d), **f32)
+            self.dws_up = torch.empty((n_shared, I_shared, d), **f32)
+            self.dws_down = torch.empty((n_shared, d, I_shared), **f32)
+        else:
+            self.dws_gate = self.dws_up = self.dws_down = None
+        a.dx_slots, a.dx_shared, a.dx = _ptr(self.dx_slots), _ptr(self.dx_shared), _ptr(self.dx)
+        a.dtopk_w = _ptr(self.dtopk_w)
+        a.dw_gate, a.dw_up, a.dw_down = _ptr(self.dw_gate), _ptr(self.dw_up), _ptr(self.dw_down)
+        a.dws_gate, a.dws_up, a.dws_down = (_ptr(self.dws_gate), _ptr(self.dws_up),
+                                            _ptr(self.dws_down))
+        n = _SZ(0)
+        _check("mok_moe_backward_workspace_bytes",
+               _lib.mok_moe_backward_workspace_bytes(ctypes.byref(a), ctypes.byref(n)))
+        self.workspace = torch.empty(max(1, n.value), dtype=torch.uint8, device=device)
+        a.workspace, a.workspace_bytes = _ptr(self.workspace), n.value
+        self.args = a
+
+    def backward(self, stream=None) -> None:
+        _check("mok_moe_backward", _lib.mok_moe_backward(ctypes.byref(self.args), _stream(stream)))
+
+    def device_error(self, stream=None) -> int:
+        err = ctypes.c_uint32(0)
+        _check("mok_moe_backward_error",
+               _lib.mok_moe_backward_error(_ptr(self.workspace), ctypes.byref(self.args),
+                                           ctypes.byref(err), _stream(stream)))
+        return err.value

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmok.so")
 SOURCES = ["route.hip", "plan.hip", "quant.hip", "expert_gemm.hip", "api.hip", "noalloc.hip",
-           "dispatch.hip"]
+           "dispatch.hip", "backward.hip"]
 HEADERS = ["device_common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

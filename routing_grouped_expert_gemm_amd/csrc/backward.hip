@@ -1,0 +1,543 @@
+// Backward of the MoE layer (or one rank's share of it) with the routing held fixed.
+//
+// The layer of the MoK write-up ("Overlapping compute and communication in MoE"): each local
+// route r = t*k + j runs P_r = w_r * W_down (silu(W_gate a) * (W_up a)) on a = x[t]; the shared
+// experts run the same FFN, unweighted, on the own tokens. The write-up presents MoK as a
+// training kernel (its introduction) and the Telegram post reports forward and backward gains
+// ("Method and experiments"); this file computes, through the same pull plan as the forward:
+//   recompute   G = A Wg^T, U = A Wu^T                       (per expert, rows of its region)
+//   dgrad down  D = dP Wd           (dP: the slot gradients gathered in plan order)
+//   SwiGLU bwd  H = silu(G) U;  dw_r = <D_r, H_r>  (= <dP_r, W_down h_r>, the routing-weight
+//               gradient);  dH = w D;  dG = dH U silu'(G);  dU = dH silu(G);  dO = w dP
+//   dgrad up    dA = dG Wg + dU Wu  -> dx through each route (source-indexed slots)
+//   wgrad       dWg = dG^T A, dWu = dU^T A, dWd = dO^T H     (ragged K: the expert's rows)
+// and for a whole layer dx = dx_shared + sum_j dx_slot[t*k + j] with the forward's fixed-order
+// combine. Every product is one launch of a grouped GEMM whose groups (one per expert and
+// matrix) are described on the device from the plan's counts: the host never reads a count.
+//
+// Grouped GEMM: C_g (+)= A_g B_g^T over tiles of 128 x 128, K steps of 32, bf16 operands and
+// float32 accumulation on v_mfma_f32_32x32x16_bf16, 4 waves of 64 x 64. An operand is read
+// either K-contiguous (row-major [rows, K]) or "transposed" (row-major [K, rows]: the wgrad
+// operands, whose K is the token dimension, and the weights read along their output
+// dimension); a transposed tile is loaded row-wise (coalesced) and written to LDS transposed,
+// so that the MFMA fragments always come from K-contiguous LDS rows.
+#include <algorithm>
+
+#include "device_common.h"
+#include "launch.h"
+#include "mok.h"
+
+namespace mok {
+
+struct GGroup {
+  const bf16_t* A;
+  const bf16_t* B;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int32_t M, N, K, tile0;   // tile0: the group's first flat tile
+};
+// A group table: header {groups, tiles, error, pad} then the groups.
+constexpr int GT_HDR = 4;
+MOK_HOSTDEV inline size_t gtable_bytes(int n_groups) {
+  return sizeof(int32_t) * GT_HDR * 4 + sizeof(GGroup) * (size_t)n_groups;
+}
+MOK_DEV GGroup* gtable_groups(int32_t* t) { return (GGroup*)(t + GT_HDR * 4); }
+
+constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LDS = GB_K + 8;   // LDS row: 80 bytes
+
+// One K step of one operand tile (GB_M rows x GB_K) into registers: 2 x 16 bytes a thread.
+// K-contiguous: chunk c = row * 4 + kc; transposed: chunk c = krow * 16 + rc (8 rows a chunk).
+template <bool T>
+MOK_DEV void gg_load(const bf16_t* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
+                     uint4 (&v)[2]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = threadIdx.x + 256 * q;
+    v[q] = make_uint4(0, 0, 0, 0);
+    if constexpr (!T) {
+      const int row = c >> 2, kc = c & 3;
+      if (r0 + row < rows && k0 + kc * 8 < K)
+        v[q] = *(const uint4*)(P + (int64_t)(r0 + row) * ld + k0 + kc * 8);
+    } else {
+      const int krow = c >> 4, rc = c & 15;
+      if (k0 + krow < K && r0 + rc * 8 < rows)
+        v[q] = *(const uint4*)(P + (int64_t)(k0 + krow) * ld + r0 + rc * 8);
+    }
+  }
+}
+
+template <bool T>
+MOK_DEV void gg_store(bf16_t (*S)[GB_LDS], const uint4 (&v)[2]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = threadIdx.x + 256 * q;
+    if constexpr (!T) {
+      *(uint4*)&S[c >> 2][(c & 3) * 8] = v[q];
+    } else {
+      const int krow = c >> 4, rc = c & 15;
+      const bf16_t* e = (const bf16_t*)&v[q];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) S[rc * 8 + i][krow] = e[i];
+    }
+  }
+}
+
+// C_g (+)= A_g B_g^T for every group of the table; TA / TB: operand stored transposed.
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table, bool acc_c) {
+  __shared__ bf16_t As[2][GB_M][GB_LDS], Bs[2][GB_N][GB_LDS];
+  __shared__ int g_sh;
+  const int n_groups = table[0], total = table[1];
+  const int b = blockIdx.x;
+  if (b >= total) return;
+  const GGroup* G = gtable_groups(const_cast<int32_t*>(table));
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = n_groups;                  // G[lo].tile0 <= b < G[hi].tile0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (G[mid].tile0 <= b) lo = mid; else hi = mid;
+    }
+    g_sh = lo;
+  }
+  __syncthreads();
+  const GGroup g = G[g_sh];
+  const int tiles_n = (g.N + GB_N - 1) / GB_N;
+  const int local = b - g.tile0;
+  const int m0 = (local / tiles_n) * GB_M, n0 = (local % tiles_n) * GB_N;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1, h = lane >> 5, l32 = lane & 31;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int nk = (g.K + GB_K - 1) / GB_K;
+  uint4 ra[2], rb[2];
+  if (nk > 0) {
+    gg_load<TA>(g.A, g.lda, g.M, g.K, m0, 0, ra);
+    gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, 0, rb);
+    gg_store<TA>(As[0], ra);
+    gg_store<TB>(Bs[0], rb);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {                          // next step's loads in flight over the MFMAs
+      gg_load<TA>(g.A, g.lda, g.M, g.K, m0, (kt + 1) * GB_K, ra);
+      gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * GB_K, rb);
+    }
+#pragma unroll
+    for (int s = 0; s < GB_K / 16; ++s) {
+      bf16x8_t fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *(const bf16x8_t*)&As[cur][wm * 64 + 32 * i + l32][16 * s + 8 * h];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *(const bf16x8_t*)&Bs[cur][wn * 64 + 32 * j + l32][16 * s + 8 * h];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      gg_store<TA>(As[cur ^ 1], ra);
+      gg_store<TB>(Bs[cur ^ 1], rb);
+    }
+    __syncthreads();
+  }
+  // lane (h, l32) of block (i, j): row m0 + wm*64 + 32 i + l32, columns n0 + wn*64 + 32 j + 8 g
+  // + 4 h + [0, 4) in values 4g .. 4g + 3 (the B fragment is the MFMA's first operand)
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm * 64 + 32 * i + l32;
+    if (m >= g.M) continue;
+    float* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + 32 * j + 8 * q + 4 * h;
+        if (n >= g.N) continue;
+        f32x4v o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = acc[i][j][4 * q + r];
+        if (acc_c) o += *(const f32x4v*)(crow + n);
+        *(f32x4v*)(crow + n) = o;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------- descriptions
+// Everything the backward's kernels need (device pointers).
+struct BwdPass {
+  int d, k, I, E_l, I_s, n_s, T_own;
+  int64_t cap;                   // routed rows the buffers hold
+  const int32_t *counts, *offsets, *route_ids;
+  const float* topk_w;
+  const bf16_t *wg, *wu, *wd, *sg, *su, *sd;
+  const bf16_t* A_own;           // x own rows [T_own, d]
+  const bf16_t* dP_own;          // their output gradient [T_own, d]
+  bf16_t *Ar, *dPr, *dGr, *dUr, *Hr, *dOr, *dGo, *dUo, *Ho;
+  float *Gr, *Ur, *Dr, *dAr, *Go, *Uo, *Do, *dAo, *dw_rows;
+  float *dwg, *dwu, *dwd, *dsg, *dsu, *dsd;
+  int32_t *t_rec, *t_dd, *t_dug, *t_duu, *t_wg;   // group tables
+  int32_t* err;                  // error word (routes past the capacity)
+};
+
+MOK_DEV void put(GGroup* G, int& n, int32_t& tiles, const bf16_t* A, int64_t lda,
+                 const bf16_t* B, int64_t ldb, float* C, int64_t ldc, int M, int N, int K) {
+  GGroup g;
+  g.A = A; g.B = B; g.C = C; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K; g.tile0 = tiles;
+  G[n++] = g;
+  tiles += ((M + GB_M - 1) / GB_M) * ((N + GB_N - 1) / GB_N);
+}
+MOK_DEV void close_table(int32_t* t, int n, int32_t tiles) { t[0] = n; t[1] = tiles; }
+
+// One thread writes every table from the plan's counts (a few hundred groups at most).
+__global__ void k_bwd_describe(BwdPass p) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const int E = p.E_l, d = p.d, I = p.I, Ish = p.n_s * p.I_s;
+  const bool over = (int64_t)p.offsets[E] > p.cap;
+  *p.err = over ? (int32_t)MOK_DEVERR_OVERFLOW : 0;
+  auto cnt = [&](int e) { return over ? 0 : p.counts[e]; };
+  auto off = [&](int e) { return (int64_t)p.offsets[e]; };
+  // recompute: G = A Wg^T, U = A Wu^T (K-contiguous operands)
+  {
+    GGroup* G = gtable_groups(p.t_rec);
+    int n = 0;
+    int32_t tl = 0;
+    for (int e = 0; e < E; ++e) {
+      if (cnt(e) == 0) continue;
+      put(G, n, tl, p.Ar + off(e) * d, d, p.wg + (int64_t)e * I * d, d, p.Gr + off(e) * I, I,
+          cnt(e), I, d);
+      put(G, n, tl, p.Ar + off(e) * d, d, p.wu + (int64_t)e * I * d, d, p.Ur + off(e) * I, I,
+          cnt(e), I, d);
+    }
+    if (Ish > 0 && p.T_own > 0) {
+      put(G, n, tl, p.A_own, d, p.sg, d, p.Go, Ish, p.T_own, Ish, d);
+      put(G, n, tl, p.A_own, d, p.su, d, p.Uo, Ish, p.T_own, Ish, d);
+    }
+    close_table(p.t_rec, n, tl);
+  }
+  // dgrad down: D = dP Wd (Wd read along its output dimension: transposed B)
+  {
+    GGroup* G = gtable_groups(p.t_dd);
+    int n = 0;
+    int32_t tl = 0;
+    for (int e = 0; e < E; ++e)
+      if (cnt(e) > 0)
+        put(G, n, tl, p.dPr + off(e) * d, d, p.wd + (int64_t)e * d * I, I, p.Dr + off(e) * I, I,
+            cnt(e), I, d);
+    if (Ish > 0 && p.T_own > 0)
+      for (int s = 0; s < p.n_s; ++s)
+        put(G, n, tl, p.dP_own, d, p.sd + (int64_t)s * d * p.I_s, p.I_s, p.Do + s * p.I_s, Ish,
+            p.T_own, p.I_s, d);
+    close_table(p.t_dd, n, tl);
+  }
+  // dgrad up: dA = dG Wg (+)= dU Wu (weights read along d: transposed B)
+  for (int part = 0; part < 2; ++part) {
+    int32_t* t = part == 0 ? p.t_dug : p.t_duu;
+    GGroup* G = gtable_groups(t);
+    int n = 0;
+    int32_t tl = 0;
+    for (int e = 0; e < E; ++e)
+      if (cnt(e) > 0)
+        put(G, n, tl, (part == 0 ? p.dGr : p.dUr) + off(e) * I, I,
+            (part == 0 ? p.wg : p.wu) + (int64_t)e * I * d, d, p.dAr + off(e) * d, d, cnt(e), d, I);
+    if (Ish > 0 && p.T_own > 0)
+      put(G, n, tl, part == 0 ? p.dGo : p.dUo, Ish, part == 0 ? p.sg : p.su, d, p.dAo, d,
+          p.T_own, d, Ish);
+    close_table(t, n, tl);
+  }
+  // wgrad (both operands transposed: K is the expert's rows). Every expert gets its tiles,
+  // also with no rows (then its gradient is written as zero).
+  {
+    GGroup* G = gtable_groups(p.t_wg);
+    int n = 0;
+    int32_t tl = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = cnt(e);
+      put(G, n, tl, p.dGr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwg + (int64_t)e * I * d, d,
+          I, d, c);
+      put(G, n, tl, p.dUr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwu + (int64_t)e * I * d, d,
+          I, d, c);
+      put(G, n, tl, p.dOr + off(e) * d, d, p.Hr + off(e) * I, I, p.dwd + (int64_t)e * d * I, I,
+          d, I, c);
+    }
+    if (Ish > 0) {
+      put(G, n, tl, p.dGo, Ish, p.A_own, d, p.dsg, d, Ish, d, p.T_own);
+      put(G, n, tl, p.dUo, Ish, p.A_own, d, p.dsu, d, Ish, d, p.T_own);
+      for (int s = 0; s < p.n_s; ++s)
+        put(G, n, tl, p.dP_own, d, p.Ho + s * p.I_s, Ish, p.dsd + (int64_t)s * d * p.I_s, p.I_s,
+            d, p.I_s, p.T_own);
+    }
+    close_table(p.t_wg, n, tl);
+  }
+}
+
+// SwiGLU backward of one row per workgroup: routed rows [0, N) of the plan, then the own
+// rows. The routing-weight gradient is a fixed-order reduction (per-thread strided sums, then a
+// tree), so it is the same on every run.
+__global__ __launch_bounds__(256) void k_bwd_swiglu(BwdPass p) {
+  __shared__ float red[256];
+  const int64_t N = min((int64_t)p.offsets[p.E_l], p.cap);
+  const int64_t row = blockIdx.x;
+  const bool own = row >= p.cap;
+  if (*p.err) return;
+  if (!own && row >= N) return;
+  const int64_t r = own ? row - p.cap : row;
+  if (own && r >= p.T_own) return;
+  const int I = own ? p.n_s * p.I_s : p.I;
+  const float* G = (own ? p.Go : p.Gr) + r * I;
+  const float* U = (own ? p.Uo : p.Ur) + r * I;
+  const float* D = (own ? p.Do : p.Dr) + r * I;
+  bf16_t* dG = (own ? p.dGo : p.dGr) + r * I;
+  bf16_t* dU = (own ? p.dUo : p.dUr) + r * I;
+  bf16_t* H = (own ? p.Ho : p.Hr) + r * I;
+  const float w = own ? 1.0f : p.topk_w[p.route_ids[r]];
+  float dw = 0.0f;
+  for (int n = threadIdx.x; n < I; n += 256) {
+    const float g = G[n], u = U[n], dd = D[n];
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+    const float sl = g * sg;
+    const float hv = sl * u;
+    dw += dd * hv;
+    const float dh = w * dd;
+    dG[n] = f32_to_bf16(dh * u * sg * (1.0f + g * (1.0f - sg)));
+    dU[n] = f32_to_bf16(dh * sl);
+    H[n] = f32_to_bf16(hv);
+  }
+  if (!own) {
+    // dO = w dP for the down-projection weight gradient
+    const bf16_t* dP = p.dPr + r * p.d;
+    bf16_t* dO = p.dOr + r * p.d;
+    for (int m = threadIdx.x; m < p.d; m += 256) dO[m] = f32_to_bf16(w * bf16_to_f32(dP[m]));
+    red[threadIdx.x] = dw;
+    __syncthreads();
+#pragma unroll
+    for (int s = 128; s > 0; s >>= 1) {
+      if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) p.dw_rows[r] = red[0];
+  }
+}
+
+// dx through each local route to its source-indexed slot (bf16), the routing-weight gradient
+// to [t, j], and the shared experts' dx. One workgroup per row.
+__global__ __launch_bounds__(256) void k_bwd_scatter(BwdPass p, bf16_t* __restrict__ dx_slots,
+                                                     bf16_t* __restrict__ dx_shared,
+                                                     float* __restrict__ dtopk_w) {
+  const int64_t N = min((int64_t)p.offsets[p.E_l], p.cap);
+  const int64_t row = blockIdx.x;
+  if (*p.err) return;
+  if (row < p.cap) {
+    if (row >= N) return;
+    const int32_t rid = p.route_ids[row];
+    const float* src = p.dAr + row * p.d;
+    bf16_t* dst = dx_slots + (int64_t)rid * p.d;
+    for (int m = threadIdx.x; m < p.d; m += 256) dst[m] = f32_to_bf16(src[m]);
+    if (threadIdx.x == 0 && dtopk_w) dtopk_w[rid] = p.dw_rows[row];
+  } else {
+    const int64_t r = row - p.cap;
+    if (r >= p.T_own || !dx_shared) return;
+    const float* src = p.dAo + r * p.d;
+    for (int m = threadIdx.x; m < p.d; m += 256) dx_shared[r * p.d + m] = f32_to_bf16(src[m]);
+  }
+}
+
+}  // namespace mok
+
+// ------------------------------------------------------------------------- C ABI
+using namespace mok;
+
+namespace {
+
+constexpr size_t kAl = 256;
+size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
+
+struct BwdLayout {
+  size_t counts, offsets, route_ids, blk_counts, blk_base, err;
+  size_t Ar, dPr, dGr, dUr, Hr, dOr, dGo, dUo, Ho, Gr, Ur, Dr, dAr, Go, Uo, Do, dAo, dw_rows;
+  size_t t_rec, t_dd, t_dug, t_duu, t_wg, total;
+  int64_t cap;
+  int64_t tiles_rec, tiles_dd, tiles_du, tiles_wg;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int validate_bwd(const mok_moe_bwd_args* a) {
+  if (!a) return MOK_EINVAL;
+  if (a->dtype != MOK_BF16) return MOK_EUNSUPPORTED;   // the backward runs on bf16 operands
+  if (a->d <= 0 || a->E <= 0 || a->E > 1024 || a->k < 1 || a->k > a->E) return MOK_EINVAL;
+  if (a->I <= 0 || a->e0 < 0 || a->E_l < 1 || a->e0 + a->E_l > a->E) return MOK_EINVAL;
+  if (a->T_pool < 0 || a->tokens_per_rank < 1 || a->T_pool % a->tokens_per_rank) return MOK_EINVAL;
+  if (a->T_pool * (int64_t)a->k >= (int64_t)1 << 31) return MOK_EINVAL;
+  if (a->own_begin < 0 || a->T_own < 0 || a->own_begin + a->T_own > a->T_pool) return MOK_EINVAL;
+  if (a->n_shared < 0 || a->route_rows_cap < 0) return MOK_EINVAL;
+  if (a->d % 128 || a->I % 64) return MOK_EINVAL;
+  if (a->n_shared > 0 && (a->I_shared <= 0 || a->I_shared % 64)) return MOK_EINVAL;
+  if (!a->x || !a->topk_idx || !a->topk_w || !a->w_gate || !a->w_up || !a->w_down) return MOK_EINVAL;
+  if (!a->dx_slots || !a->dw_gate || !a->dw_up || !a->dw_down) return MOK_EINVAL;
+  if (a->n_shared > 0 && (!a->ws_gate || !a->ws_up || !a->ws_down || !a->dws_gate ||
+                          !a->dws_up || !a->dws_down))
+    return MOK_EINVAL;
+  const bool full = a->E_l == a->E;
+  if (full) {
+    if (!a->dy || a->dy_slots || a->dy_shared || !a->dx || a->own_begin != 0 ||
+        (a->n_shared > 0 && a->T_own != a->T_pool))
+      return MOK_EINVAL;
+  } else {
+    if (a->dy || !a->dy_slots || a->dx || (a->n_shared > 0 && a->T_own > 0 && !a->dy_shared))
+      return MOK_EINVAL;
+  }
+  if (a->n_shared > 0 && a->T_own > 0 && !a->dx_shared) return MOK_EINVAL;
+  return MOK_OK;
+}
+
+BwdLayout layout_bwd(const mok_moe_bwd_args* a) {
+  BwdLayout L{};
+  const int64_t worst = a->T_pool * (int64_t)std::min(a->k, a->E_l);
+  L.cap = a->route_rows_cap > 0 ? std::min<int64_t>(a->route_rows_cap, worst) : worst;
+  const int64_t cap = std::max<int64_t>(1, L.cap), d = a->d, I = a->I;
+  const int64_t Ish = (int64_t)a->n_shared * a->I_shared, To = std::max(1, a->T_own);
+  size_t off = 0;
+  auto take = [&](size_t n) { size_t o = off; off = al(off + n); return o; };
+  L.counts = take(4 * a->E_l);
+  L.offsets = take(4 * (a->E_l + 1));
+  L.route_ids = take(4 * std::max<int64_t>(1, worst));
+  const int64_t nb = plan_n_blocks(a->T_pool * a->k);
+  L.blk_counts = take(4 * nb * a->E_l);
+  L.blk_base = take(4 * nb * a->E_l);
+  L.err = take(16);
+  L.Ar = take(2 * cap * d); L.dPr = take(2 * cap * d); L.dOr = take(2 * cap * d);
+  L.dGr = take(2 * cap * I); L.dUr = take(2 * cap * I); L.Hr = take(2 * cap * I);
+  L.Gr = take(4 * cap * I); L.Ur = take(4 * cap * I); L.Dr = take(4 * cap * I);
+  L.dAr = take(4 * cap * d); L.dw_rows = take(4 * cap);
+  const int64_t Io = std::max<int64_t>(1, Ish);
+  L.dGo = take(2 * To * Io); L.dUo = take(2 * To * Io); L.Ho = take(2 * To * Io);
+  L.Go = take(4 * To * Io); L.Uo = take(4 * To * Io); L.Do = take(4 * To * Io);
+  L.dAo = take(4 * To * d);
+  const int ng = 3 * a->E_l + 2 + a->n_shared + 2;
+  L.t_rec = take(gtable_bytes(ng)); L.t_dd = take(gtable_bytes(ng)); L.t_dug = take(gtable_bytes(ng));
+  L.t_duu = take(gtable_bytes(ng)); L.t_wg = take(gtable_bytes(ng));
+  L.total = off;
+  // upper bounds of each launch's tiles (the device fills in the exact counts)
+  const int64_t mt_r = cdiv(cap, GB_M) + a->E_l, mt_o = cdiv(a->T_own, GB_M);
+  L.tiles_rec = 2 * (mt_r * cdiv(I, GB_N) + mt_o * cdiv(Ish, GB_N));
+  L.tiles_dd = mt_r * cdiv(I, GB_N) + (int64_t)a->n_shared * mt_o * cdiv(a->I_shared, GB_N);
+  L.tiles_du = (mt_r + mt_o) * cdiv(d, GB_N);
+  L.tiles_wg = (int64_t)a->E_l * (2 * cdiv(I, GB_M) * cdiv(d, GB_N) + cdiv(d, GB_M) * cdiv(I, GB_N)) +
+               2 * cdiv(Ish, GB_M) * cdiv(d, GB_N) +
+               (int64_t)a->n_shared * cdiv(d, GB_M) * cdiv(a->I_shared, GB_N);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mok_moe_backward_workspace_bytes(const mok_moe_bwd_args* a, size_t* bytes) {
+  if (!bytes) return MOK_EINVAL;
+  const int st = validate_bwd(a);
+  if (st != MOK_OK) return st;
+  *bytes = layout_bwd(a).total;
+  return MOK_OK;
+}
+
+int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
+  const int st = validate_bwd(a);
+  if (st != MOK_OK) return st;
+  const BwdLayout L = layout_bwd(a);
+  if (!a->workspace || a->workspace_bytes < L.total) return MOK_EWORKSPACE;
+  if (L.tiles_rec >= INT32_MAX || L.tiles_wg >= INT32_MAX) return MOK_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)a->workspace;
+  auto at = [&](size_t o) { return (void*)(ws + o); };
+  BwdPass p{};
+  p.d = a->d; p.k = a->k; p.I = a->I; p.E_l = a->E_l; p.I_s = a->I_shared;
+  p.n_s = a->n_shared; p.T_own = a->n_shared > 0 ? a->T_own : 0; p.cap = L.cap;
+  p.counts = (int32_t*)at(L.counts); p.offsets = (int32_t*)at(L.offsets);
+  p.route_ids = (int32_t*)at(L.route_ids); p.topk_w = a->topk_w;
+  p.wg = (const bf16_t*)a->w_gate; p.wu = (const bf16_t*)a->w_up; p.wd = (const bf16_t*)a->w_down;
+  p.sg = (const bf16_t*)a->ws_gate; p.su = (const bf16_t*)a->ws_up; p.sd = (const bf16_t*)a->ws_down;
+  const bf16_t* x = (const bf16_t*)a->x;
+  p.A_own = x + a->own_begin * a->d;
+  p.dP_own = a->dy ? (const bf16_t*)a->dy + a->own_begin * a->d : (const bf16_t*)a->dy_shared;
+  p.Ar = (bf16_t*)at(L.Ar); p.dPr = (bf16_t*)at(L.dPr); p.dGr = (bf16_t*)at(L.dGr);
+  p.dUr = (bf16_t*)at(L.dUr); p.Hr = (bf16_t*)at(L.Hr); p.dOr = (bf16_t*)at(L.dOr);
+  p.dGo = (bf16_t*)at(L.dGo); p.dUo = (bf16_t*)at(L.dUo); p.Ho = (bf16_t*)at(L.Ho);
+  p.Gr = (float*)at(L.Gr); p.Ur = (float*)at(L.Ur); p.Dr = (float*)at(L.Dr); p.dAr = (float*)at(L.dAr);
+  p.Go = (float*)at(L.Go); p.Uo = (float*)at(L.Uo); p.Do = (float*)at(L.Do); p.dAo = (float*)at(L.dAo);
+  p.dw_rows = (float*)at(L.dw_rows);
+  p.dwg = a->dw_gate; p.dwu = a->dw_up; p.dwd = a->dw_down;
+  p.dsg = a->dws_gate; p.dsu = a->dws_up; p.dsd = a->dws_down;
+  p.t_rec = (int32_t*)at(L.t_rec); p.t_dd = (int32_t*)at(L.t_dd); p.t_dug = (int32_t*)at(L.t_dug);
+  p.t_duu = (int32_t*)at(L.t_duu); p.t_wg = (int32_t*)at(L.t_wg);
+  p.err = (int32_t*)at(L.err);
+  const int64_t worst = a->T_pool * (int64_t)std::min(a->k, a->E_l);
+  // the plan (also yields route_ids for the gathers), then the rows in plan order
+  if (launch_plan(a->topk_idx, a->T_pool, a->k, a->e0, a->E_l, a->tokens_per_rank,
+                  (int32_t*)p.counts, (int32_t*)p.offsets, nullptr, (int32_t*)p.route_ids,
+                  (int32_t*)at(L.blk_counts), (int32_t*)at(L.blk_base), std::max<int64_t>(1, worst),
+                  s) != hipSuccess)
+    return MOK_EHIP;
+  launch_k(k_bwd_describe, dim3(1), dim3(64), 0, s, nullptr, nullptr, p);
+  // routed x rows and their slot gradients, gathered in plan order (rows past the capacity
+  // are not gathered; the description then runs no tile)
+  if (a->T_pool > 0) {
+    if (launch_pull_gather(a->x, a->d, 2, a->k, p.route_ids, p.offsets, a->E_l, L.cap, p.Ar, s) !=
+        hipSuccess)
+      return MOK_EHIP;
+    // slot r's gradient: dy[r / k] for a whole layer, dy_slots[r] for a share
+    if (launch_pull_gather(a->dy ? a->dy : a->dy_slots, a->d, 2, a->dy ? a->k : 1, p.route_ids,
+                           p.offsets, a->E_l, L.cap, p.dPr, s) != hipSuccess)
+      return MOK_EHIP;
+  }
+  auto gg = [&](int32_t* table, int64_t tiles, bool ta, bool tb, bool accum) {
+    if (tiles <= 0) return;
+    const dim3 grid((unsigned)tiles), block(256);
+    if (!ta && !tb) launch_k(k_ggemm<false, false>, grid, block, 0, s, nullptr, nullptr, table, accum);
+    else if (!ta && tb) launch_k(k_ggemm<false, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
+    else launch_k(k_ggemm<true, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
+  };
+  gg(p.t_rec, L.tiles_rec, false, false, false);           // G, U
+  gg(p.t_dd, L.tiles_dd, false, true, false);              // D = dP Wd
+  const int64_t rows = L.cap + p.T_own;
+  if (rows > 0)
+    launch_k(k_bwd_swiglu, dim3((unsigned)rows), dim3(256), 0, s, nullptr, nullptr, p);
+  gg(p.t_dug, L.tiles_du, false, true, false);             // dA = dG Wg
+  gg(p.t_duu, L.tiles_du, false, true, true);              //    + dU Wu
+  gg(p.t_wg, L.tiles_wg, true, true, false);               // dWg, dWu, dWd (+ shared)
+  if (rows > 0)
+    launch_k(k_bwd_scatter, dim3((unsigned)rows), dim3(256), 0, s, nullptr, nullptr, p,
+             (bf16_t*)a->dx_slots, (bf16_t*)a->dx_shared, a->dtopk_w);
+  if (a->E_l == a->E) {
+    if (launch_combine(p.T_own > 0 ? a->dx_shared : nullptr, a->dx_slots, a->dx, a->T_pool, a->k,
+                       a->d, false, s) != hipSuccess)
+      return MOK_EHIP;
+  }
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EHIP;
+}
+
+int mok_moe_backward_error(const void* workspace, const mok_moe_bwd_args* a, uint32_t* err,
+                           void* stream) {
+  if (!workspace || !err) return MOK_EINVAL;
+  const int st = validate_bwd(a);
+  if (st != MOK_OK) return st;
+  const BwdLayout L = layout_bwd(a);
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOK_EHIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, (const char*)workspace + L.err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+    return MOK_EHIP;
+  *err = (uint32_t)v;
+  return MOK_OK;
+}
+
+}  // extern "C"
