@@ -45,39 +45,60 @@ MOK_DEV GGroup* gtable_groups(int32_t* t) { return (GGroup*)(t + GT_HDR * 4); }
 
 constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LDS = GB_K + 8;   // LDS row: 80 bytes
 
-// One K step of one operand tile (GB_M rows x GB_K) into registers: 2 x 16 bytes a thread.
-// K-contiguous: chunk c = row * 4 + kc; transposed: chunk c = krow * 16 + rc (8 rows a chunk).
+// One K step of one operand tile (GB_M rows x GB_K) into registers, and from registers into
+// LDS as K-contiguous rows.
+//  K-contiguous operand: every thread, 2 x 16 bytes (chunk c = row * 4 + kc).
+//  Transposed operand ([K, rows] row-major): the tile is 4 x 16 blocks of 8 k x 8 rows; thread
+//  b < 64 of the operand's wave loads block b as 8 row-wise 16-byte loads (16 lanes cover 256
+//  contiguous bytes of one k row), transposes it in registers and writes 8 LDS rows of 8 k.
+struct Frag { uint4 v[8]; };
 template <bool T>
 MOK_DEV void gg_load(const bf16_t* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
-                     uint4 (&v)[2]) {
+                     Frag& f, int t) {
+  if constexpr (!T) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = threadIdx.x + 256 * q;
-    v[q] = make_uint4(0, 0, 0, 0);
-    if constexpr (!T) {
+    for (int q = 0; q < 2; ++q) {
+      const int c = t + 256 * q;
       const int row = c >> 2, kc = c & 3;
+      f.v[q] = make_uint4(0, 0, 0, 0);
       if (r0 + row < rows && k0 + kc * 8 < K)
-        v[q] = *(const uint4*)(P + (int64_t)(r0 + row) * ld + k0 + kc * 8);
-    } else {
-      const int krow = c >> 4, rc = c & 15;
-      if (k0 + krow < K && r0 + rc * 8 < rows)
-        v[q] = *(const uint4*)(P + (int64_t)(k0 + krow) * ld + r0 + rc * 8);
+        f.v[q] = *(const uint4*)(P + (int64_t)(r0 + row) * ld + k0 + kc * 8);
+    }
+  } else {
+    if (t >= 64) return;
+    const int kg = t >> 4, rg = t & 15;
+    const bool rok = r0 + rg * 8 < rows;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + kg * 8 + i;
+      f.v[i] = make_uint4(0, 0, 0, 0);
+      if (rok && k < K) f.v[i] = *(const uint4*)(P + (int64_t)k * ld + r0 + rg * 8);
     }
   }
 }
 
 template <bool T>
-MOK_DEV void gg_store(bf16_t (*S)[GB_LDS], const uint4 (&v)[2]) {
+MOK_DEV void gg_store(bf16_t (*S)[GB_LDS], const Frag& f, int t) {
+  if constexpr (!T) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = threadIdx.x + 256 * q;
-    if constexpr (!T) {
-      *(uint4*)&S[c >> 2][(c & 3) * 8] = v[q];
-    } else {
-      const int krow = c >> 4, rc = c & 15;
-      const bf16_t* e = (const bf16_t*)&v[q];
+    for (int q = 0; q < 2; ++q) {
+      const int c = t + 256 * q;
+      *(uint4*)&S[c >> 2][(c & 3) * 8] = f.v[q];
+    }
+  } else {
+    if (t >= 64) return;
+    const int kg = t >> 4, rg = t & 15;
+    // f.v[i] holds rows rg*8 + [0, 8) at k = kg*8 + i; LDS row rg*8 + j takes k = kg*8 + [0, 8)
+    const uint32_t* w = (const uint32_t*)f.v;          // w[4 i + j / 2]: (row j, k i) half j & 1
 #pragma unroll
-      for (int i = 0; i < 8; ++i) S[rc * 8 + i][krow] = e[i];
+    for (int j = 0; j < 8; ++j) {
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = w[4 * (2 * q) + j / 2], b = w[4 * (2 * q + 1) + j / 2];
+        o[q] = (j & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      }
+      *(uint4*)&S[rg * 8 + j][kg * 8] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -114,19 +135,21 @@ __global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int nk = (g.K + GB_K - 1) / GB_K;
-  uint4 ra[2], rb[2];
+  // a transposed operand is loaded by one wave: A by wave 0, B by wave 1 (thread index - 64)
+  const int ta = threadIdx.x, tb = TB && !TA ? threadIdx.x : (int)threadIdx.x - (TB ? 64 : 0);
+  Frag ra, rb;
   if (nk > 0) {
-    gg_load<TA>(g.A, g.lda, g.M, g.K, m0, 0, ra);
-    gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, 0, rb);
-    gg_store<TA>(As[0], ra);
-    gg_store<TB>(Bs[0], rb);
+    gg_load<TA>(g.A, g.lda, g.M, g.K, m0, 0, ra, ta);
+    gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, 0, rb, tb < 0 ? 256 : tb);
+    gg_store<TA>(As[0], ra, ta);
+    gg_store<TB>(Bs[0], rb, tb < 0 ? 256 : tb);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {                          // next step's loads in flight over the MFMAs
-      gg_load<TA>(g.A, g.lda, g.M, g.K, m0, (kt + 1) * GB_K, ra);
-      gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * GB_K, rb);
+      gg_load<TA>(g.A, g.lda, g.M, g.K, m0, (kt + 1) * GB_K, ra, ta);
+      gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * GB_K, rb, tb < 0 ? 256 : tb);
     }
 #pragma unroll
     for (int s = 0; s < GB_K / 16; ++s) {
@@ -144,8 +167,8 @@ __global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) {
-      gg_store<TA>(As[cur ^ 1], ra);
-      gg_store<TB>(Bs[cur ^ 1], rb);
+      gg_store<TA>(As[cur ^ 1], ra, ta);
+      gg_store<TB>(Bs[cur ^ 1], rb, tb < 0 ? 256 : tb);
     }
     __syncthreads();
   }
