@@ -43,29 +43,31 @@ MOK_HOSTDEV inline size_t gtable_bytes(int n_groups) {
 }
 MOK_DEV GGroup* gtable_groups(int32_t* t) { return (GGroup*)(t + GT_HDR * 4); }
 
-constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LDS = GB_K + 8;   // LDS row: 80 bytes
+constexpr int GB_M = 128, GB_N = 128, GB_K = 64, GB_LDS = GB_K + 8;   // LDS row: 144 bytes
+constexpr int GB_KC = GB_K / 8;                 // 16-byte chunks of a tile row per K step
+constexpr int GB_TT = GB_KC * (GB_M / 8);       // 8 x 8 blocks of a transposed tile = its loaders
 
 // One K step of one operand tile (GB_M rows x GB_K) into registers, and from registers into
 // LDS as K-contiguous rows.
-//  K-contiguous operand: every thread, 2 x 16 bytes (chunk c = row * 4 + kc).
-//  Transposed operand ([K, rows] row-major): the tile is 4 x 16 blocks of 8 k x 8 rows; thread
-//  b < 64 of the operand's wave loads block b as 8 row-wise 16-byte loads (16 lanes cover 256
-//  contiguous bytes of one k row), transposes it in registers and writes 8 LDS rows of 8 k.
+//  K-contiguous operand: every thread, 4 x 16 bytes (chunk c = row * 8 + kc).
+//  Transposed operand ([K, rows] row-major): the tile is 8 x 16 blocks of 8 k x 8 rows; thread
+//  b < 128 of the operand's two waves loads block b as 8 row-wise 16-byte loads (16 lanes cover
+//  256 contiguous bytes of one k row), transposes it in registers and writes 8 LDS rows of 8 k.
 struct Frag { uint4 v[8]; };
 template <bool T>
 MOK_DEV void gg_load(const bf16_t* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
                      Frag& f, int t) {
   if constexpr (!T) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < GB_M * GB_KC / 256; ++q) {
       const int c = t + 256 * q;
-      const int row = c >> 2, kc = c & 3;
+      const int row = c / GB_KC, kc = c % GB_KC;
       f.v[q] = make_uint4(0, 0, 0, 0);
       if (r0 + row < rows && k0 + kc * 8 < K)
         f.v[q] = *(const uint4*)(P + (int64_t)(r0 + row) * ld + k0 + kc * 8);
     }
   } else {
-    if (t >= 64) return;
+    if (t >= GB_TT) return;
     const int kg = t >> 4, rg = t & 15;
     const bool rok = r0 + rg * 8 < rows;
 #pragma unroll
@@ -81,12 +83,12 @@ template <bool T>
 MOK_DEV void gg_store(bf16_t (*S)[GB_LDS], const Frag& f, int t) {
   if constexpr (!T) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < GB_M * GB_KC / 256; ++q) {
       const int c = t + 256 * q;
-      *(uint4*)&S[c >> 2][(c & 3) * 8] = f.v[q];
+      *(uint4*)&S[c / GB_KC][(c % GB_KC) * 8] = f.v[q];
     }
   } else {
-    if (t >= 64) return;
+    if (t >= GB_TT) return;
     const int kg = t >> 4, rg = t & 15;
     // f.v[i] holds rows rg*8 + [0, 8) at k = kg*8 + i; LDS row rg*8 + j takes k = kg*8 + [0, 8)
     const uint32_t* w = (const uint32_t*)f.v;          // w[4 i + j / 2]: (row j, k i) half j & 1
@@ -109,7 +111,12 @@ __global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table
   __shared__ bf16_t As[2][GB_M][GB_LDS], Bs[2][GB_N][GB_LDS];
   __shared__ int g_sh;
   const int n_groups = table[0], total = table[1];
-  const int b = blockIdx.x;
+  // Tile map: workgroup w runs on XCD w % 8. In each window of 256 consecutive workgroups (which
+  // run at about the same time) XCD x takes 32 consecutive tiles, so tiles that share an operand
+  // tile share an L2, while the 8 XCDs still work on neighbouring tiles (one expert's operands,
+  // which the last-level cache then serves to all of them).
+  const int w = blockIdx.x, win = w & ~255, in = w & 255;
+  const int b = win + (in & 7) * 32 + (in >> 3);
   if (b >= total) return;
   const GGroup* G = gtable_groups(const_cast<int32_t*>(table));
   if (threadIdx.x == 0) {
@@ -135,21 +142,22 @@ __global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int nk = (g.K + GB_K - 1) / GB_K;
-  // a transposed operand is loaded by one wave: A by wave 0, B by wave 1 (thread index - 64)
-  const int ta = threadIdx.x, tb = TB && !TA ? threadIdx.x : (int)threadIdx.x - (TB ? 64 : 0);
+  // a transposed operand is loaded by two waves: A by waves 0-1, B by waves 2-3 (or 0-1 when A
+  // is K-contiguous)
+  const int ta = threadIdx.x, tb = TB && !TA ? threadIdx.x : (int)threadIdx.x - (TB ? GB_TT : 0);
   Frag ra, rb;
   if (nk > 0) {
     gg_load<TA>(g.A, g.lda, g.M, g.K, m0, 0, ra, ta);
-    gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, 0, rb, tb < 0 ? 256 : tb);
+    gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, 0, rb, tb < 0 ? GB_TT : tb);
     gg_store<TA>(As[0], ra, ta);
-    gg_store<TB>(Bs[0], rb, tb < 0 ? 256 : tb);
+    gg_store<TB>(Bs[0], rb, tb < 0 ? GB_TT : tb);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {                          // next step's loads in flight over the MFMAs
       gg_load<TA>(g.A, g.lda, g.M, g.K, m0, (kt + 1) * GB_K, ra, ta);
-      gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * GB_K, rb, tb < 0 ? 256 : tb);
+      gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * GB_K, rb, tb < 0 ? GB_TT : tb);
     }
 #pragma unroll
     for (int s = 0; s < GB_K / 16; ++s) {
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table
     }
     if (kt + 1 < nk) {
       gg_store<TA>(As[cur ^ 1], ra, ta);
-      gg_store<TB>(Bs[cur ^ 1], rb, tb < 0 ? 256 : tb);
+      gg_store<TB>(Bs[cur ^ 1], rb, tb < 0 ? GB_TT : tb);
     }
     __syncthreads();
   }
@@ -525,7 +533,7 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   }
   auto gg = [&](int32_t* table, int64_t tiles, bool ta, bool tb, bool accum) {
     if (tiles <= 0) return;
-    const dim3 grid((unsigned)tiles), block(256);
+    const dim3 grid((unsigned)((tiles + 255) / 256 * 256)), block(256);
     if (!ta && !tb) launch_k(k_ggemm<false, false>, grid, block, 0, s, nullptr, nullptr, table, accum);
     else if (!ta && tb) launch_k(k_ggemm<false, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
     else launch_k(k_ggemm<true, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
