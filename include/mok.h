@@ -128,7 +128,8 @@ typedef struct mok_moe_args {
   int32_t d;               /* model dim (multiple of 128)                                   */
   int32_t E;               /* routed experts in the layer                                   */
   int32_t k;               /* top-k                                                         */
-  int32_t I;               /* routed expert intermediate (multiple of 64; MX: of 128)       */
+  int32_t I;               /* routed expert intermediate (multiple of 64; MXFP8: of 128;
+                              MXFP4: of 256; d likewise a multiple of 256 for MXFP4)         */
   int32_t e0, E_l;         /* local experts [e0, e0+E_l)                                    */
   int32_t tokens_per_rank; /* pool rows per source rank (T_pool % tokens_per_rank == 0)     */
   int64_t T_pool;          /* rows of the token pool x                                      */

@@ -64,9 +64,11 @@ int validate_moe(const mok_moe_args* a) {
   const int mb = a->minibatch_rows;
   if (mb != 128 && mb != 256 && mb != 512 && mb != 1024) return MOK_EINVAL;
   if (a->ring_rows < mb || a->ring_rows % mb) return MOK_EINVAL;
-  // tile divisibility: K steps of 128 bytes per row (fp32 32, bf16 64, fp8 128 elements) or
-  // 64 bytes (fp4: 128 elements); down tiles of 128 columns, up tiles of 64 columns
-  const int kstep = a->dtype == MOK_FP32 ? 32 : (a->dtype == MOK_BF16 ? 64 : 128);
+  // tile divisibility: K steps of 128 bytes per row (fp32 32, bf16 64, fp8 128, fp4 256
+  // elements); down tiles of 128 columns, up tiles of 64 columns
+  const int kstep = a->dtype == MOK_FP32 ? 32
+                  : a->dtype == MOK_BF16 ? 64
+                  : a->dtype == MOK_MXFP8 ? 128 : 256;
   if (a->d % 128 || a->d % kstep || a->I % 64 || a->I % kstep) return MOK_EINVAL;
   if (a->n_shared > 0) {
     if (a->I_shared <= 0 || a->I_shared % 64 || a->I_shared % kstep) return MOK_EINVAL;

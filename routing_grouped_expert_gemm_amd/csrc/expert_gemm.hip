@@ -381,11 +381,11 @@ constexpr int TILE_M = 256;
 // workgroup per CU: each 1 KB LDS operand fragment feeds 4 MFMAs. Two 64 KB K stages of
 // 128 bytes per row (whole cache lines), filled by LDS-DMA.
 typedef Cfg<256, 256, 2, 2, 128, 2> Big;
-// MXFP4: K steps of 64 bytes per row, i.e. 128 elements, as the MXFP8 steps of 128 bytes, so
-// the two MX formats share one scale word per row and K step and the same sub-step structure.
-typedef Cfg<256, 256, 2, 2, 64, 2> Big4;
+// Every element type uses the same tile and K steps of 128 bytes a row: 64 bf16, 128 E4M3 or
+// 256 E2M1 elements, i.e. one MX scale word (4 blocks of 32) a row and step for MXFP8, two for
+// MXFP4.
 template <Elem EL> struct CfgOf { typedef Big type; };
-template <> struct CfgOf<Elem::FP4> { typedef Big4 type; };
+template <Elem EL> constexpr int scale_words() { return EL == Elem::FP4 ? 2 : 1; }
 
 // Per element type: bytes per two elements (KB2), the MFMA's K per instruction (MK) and the 16-
 // byte chunks a lane feeds one MFMA (CPL).
@@ -628,7 +628,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   constexpr int SUB = KT / TR::MK;                 // MFMA sub-steps per K step
   constexpr int SC_B = KT / 32;                    // MX scale bytes per row per K step
   // LDS-DMA instructions one wave issues per K step
-  constexpr int DMA_PER_STEP = A_SLABS + B_SLABS + (MXE ? 2 : 0);
+  constexpr int SCW = scale_words<EL>();           // MX scale words per row and K step
+  constexpr int DMA_PER_STEP = A_SLABS + B_SLABS + (MXE ? 2 * SCW : 0);
   // K-loop barrier placement: before the last sub-step of the previous step (bf16, float32),
   // or at the start of the step (MXFP8)
   constexpr bool EARLY_X = !MXE;
@@ -776,7 +777,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     s.a = uniform_ptr(a_base + nbytes<EL>(k0));
     s.b = uniform_ptr(b_base + (int64_t)seg * b_seg_stride + nbytes<EL>(kin));
     s.bu = UP ? uniform_ptr(b_up + nbytes<EL>(kin)) : nullptr;
-    if (MXE) {                                       // K steps of 128 elements: one scale word
+    if (MXE) {                                       // one scale word per 128 elements of K
       // a shared down segment's scales: d rows x I_seg / 32 bytes per shared expert
       s.sa = uniform_ptr(a_sc_base + (int64_t)(k0 / 128) * a_sc_R * 4);
       s.sb = uniform_ptr(b_sc_base + (int64_t)seg * p.d * (p.I_seg / 32) +
@@ -795,10 +796,16 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
       const int r = q - A_SLABS;
       const char* bb = (UP && b_up_slab(r)) ? s.bu : s.b;
       dma_b128(bb, b_off[r], uniform(lds_addr(&b.B[RB * wid][0])) + 1024 * r);
-    } else if (q == A_SLABS + B_SLABS) {
-      dma_b32<A_L2C>(s.sa, a_sc_off, uniform(lds_addr(&b.As[64 * wid])));
     } else {
-      dma_b32(s.sb, b_sc_off, uniform(lds_addr(&b.Bs[64 * wid])));
+      // scale words: A word 0, B word 0 (, A word 1, B word 1); word w of the step is the
+      // K-step-major word of 128-element step (k0 / 128 + w), R rows further on
+      const int t = q - A_SLABS - B_SLABS, w = t >> 1;
+      if ((t & 1) == 0)
+        dma_b32<A_L2C>(s.sa + (int64_t)w * a_sc_R * 4, a_sc_off,
+                       uniform(lds_addr(&b.As[w * BM + 64 * wid])));
+      else
+        dma_b32(s.sb + (int64_t)w * b_sc_R * 4, b_sc_off,
+                uniform(lds_addr(&b.Bs[w * BN + 64 * wid])));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -897,9 +904,12 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     const char* a_buf = (const char*)&b.A[blk_row(0) + l32][0];
     const char* b_buf = (const char*)&b.B[wn * WN + l32][0];
     uint4 fa[2][FM][2], fb[2][FN][2];
-    // MXFP8 (one scale word of 4 blocks per row and K step): the word shifted right by 8 h, so
-    // byte 2 s holds the lane's block 2 s + h of sub-step s; read once per step
+    // MX scale bytes of the lane's blocks, one register per row block, read once per step.
+    // MXFP8 (one word of 4 blocks a row and step): the word shifted right by 8 h, so byte 2 s
+    // holds block 2 s + h of sub-step s. MXFP4 (two words a step): a byte permute packs the
+    // bytes h and 2 + h of both words, so byte sc_byte(s) holds block 2 s + h.
     uint32_t asc[FM], bsc[FN];
+    const uint32_t perm_sel = 0x06020400u + 0x01010101u * h;
     // Reads in the order the MFMAs (row-block major) first use them: scale words, A block 0,
     // the B blocks, the other A blocks. The LDS counter tracks at most 15 reads, so a read
     // that an MFMA waits for must be among the first of those in flight.
@@ -908,9 +918,17 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
       const int c1 = ((frag_chunk<EL>(s, h, 1)) ^ xsw) * 16;
       if (MXE && s == 0) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) asc[i] = b.As[blk_row(i) + l32] >> (8 * h);
+        for (int i = 0; i < FM; ++i) {
+          const int r = blk_row(i) + l32;
+          asc[i] = SCW == 1 ? b.As[r] >> (8 * h)
+                            : __builtin_amdgcn_perm(b.As[BM + r], b.As[r], perm_sel);
+        }
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bsc[j] = b.Bs[wn * WN + j * 32 + l32] >> (8 * h);
+        for (int j = 0; j < FN; ++j) {
+          const int r = wn * WN + j * 32 + l32;
+          bsc[j] = SCW == 1 ? b.Bs[r] >> (8 * h)
+                            : __builtin_amdgcn_perm(b.Bs[BN + r], b.Bs[r], perm_sel);
+        }
       }
       auto ra = [&](int i) {
         fa[f][i][0] = *(const uint4*)(a_buf + i * 32 * C::ROW_B + c0);
@@ -925,7 +943,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
 #pragma unroll
       for (int i = 1; i < FM; ++i) ra(i);
     };
-    static_assert(!MXE || (SUB == 2 && SC_B == 4), "one scale word per row and K step");
+    static_assert(!MXE || (SUB == 2 * SCW && SC_B == 4 * SCW), "one scale word per 128 elements");
     load(0, 0);
     // The reads of sub-step s + 1 go out after the first NEXT_AT MFMAs of s: issued before
     // them, they would sit ahead of s's own reads in the LDS counter, and the first MFMA would
@@ -936,7 +954,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
       __builtin_amdgcn_sched_barrier(0);
       if (s == 0) after(-1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step<EL, FM, FN, 2 * s>(fa[s & 1], fb[s & 1], asc, bsc, acc, [&](int n) {
+      mfma_step<EL, FM, FN, SCW == 1 ? 2 * s : 2 * (s & 1) + (s >> 1)>(
+          fa[s & 1], fb[s & 1], asc, bsc, acc, [&](int n) {
         if (s + 1 < SUB && n == NEXT_AT - 1) {
           __builtin_amdgcn_sched_barrier(0);
           load(s + 1, (s + 1) & 1);
@@ -1198,7 +1217,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
 // STAGES are referenced), the MX scale words and the down stage's row table. Stages 0 and 1 are
 // sized for 128-byte rows whatever the configuration's row: the epilogue stages each wave's
 // outputs through 16 KB of buffer 1's A or B half.
-#define MOK_TILE_LDS(C, sm)                                                                      \
+#define MOK_TILE_LDS(C, EL, sm)                                                                  \
+  constexpr int SCW_ = scale_words<EL>();                                                        \
   __shared__ uint4 a0_[C::BM][8], a1_[C::BM][8], b0_[C::BN][8], b1_[C::BN][8];                   \
   uint4(*a0)[C::CH] = (uint4(*)[C::CH])a0_;                                                      \
   uint4(*a1)[C::CH] = (uint4(*)[C::CH])a1_;                                                      \
@@ -1206,7 +1226,8 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   uint4(*b1)[C::CH] = (uint4(*)[C::CH])b1_;                                                      \
   __shared__ uint4 a2[C::STAGES > 2 ? C::BM : 1][C::CH], a3[C::STAGES > 2 ? C::BM : 1][C::CH];   \
   __shared__ uint4 b2[C::STAGES > 2 ? C::BN : 1][C::CH], b3[C::STAGES > 2 ? C::BN : 1][C::CH];   \
-  __shared__ uint32_t as0[C::BM], as1[C::BM], bs0[C::BN], bs1[C::BN];                            \
+  __shared__ uint32_t as0[C::BM * SCW_], as1[C::BM * SCW_], bs0[C::BN * SCW_],                  \
+      bs1[C::BN * SCW_];                                                                         \
   __shared__ uint32_t as2[C::STAGES > 2 ? C::BM : 1], as3[C::STAGES > 2 ? C::BM : 1];            \
   __shared__ uint32_t bs2[C::STAGES > 2 ? C::BN : 1], bs3[C::STAGES > 2 ? C::BN : 1];            \
   __shared__ int32_t row_dst[C::BM];                                                             \
@@ -1226,7 +1247,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
 // rows share that XCD's L2.
 template <Elem EL, bool UP, bool F32OUT, class C>
 __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
-  MOK_TILE_LDS(C, sm);
+  MOK_TILE_LDS(C, EL, sm);
   const int cap = p.max_mb;
   const int32_t total = p.wl[UP ? WL_N_U : WL_N_D];
   const int4* tab = UP ? wl_utab(p.wl, cap) : wl_dtab(p.wl, cap, p.cap_u);
@@ -1435,7 +1456,7 @@ MOK_DEV void wait_count(const int32_t* ctr, int32_t need, int32_t* err) {
 // an agent-scope acquire (the L2 invalidated).
 template <Elem EL, bool F32OUT, class C>
 __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
-  MOK_TILE_LDS(C, sm);
+  MOK_TILE_LDS(C, EL, sm);
   __shared__ int4 item;
   const int cap = p.max_mb;
   int32_t* wl = p.wl;

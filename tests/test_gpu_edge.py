@@ -122,7 +122,8 @@ def test_no_shared_expert(ring):
 def test_share_without_own_tokens(dtype):
     import routing_grouped_expert_gemm_amd as mok
     wl = synth.scaled(BASE, dtype=dtype, I=256, E_l=4, e0=0, routing="logits",
-                      tokens_per_rank=256, T_own=0, own_begin=0, name=f"edge_noown_{dtype}")
+                      tokens_per_rank=256, T_own=0, own_begin=0, name=f"edge_noown_{dtype}",
+                      I_shared=256)
     inp = make_inputs(wl, DEV)
     rng = np.random.default_rng(2)
     idx, w = _routing(wl.T_pool, wl.E, wl.k, rng)

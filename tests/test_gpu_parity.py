@@ -195,8 +195,8 @@ SMALL = {
                                 own_begin=256, T_own=256, I_shared=128, minibatch_rows=128,
                                 ring_rows=1024),
     "share_mxfp4": synth.scaled(synth.WORKLOADS[synth.EP64_MX4], name="share_mxfp4", T_pool=2048,
-                                d=256, E=64, k=8, I=256, e0=4, E_l=4, tokens_per_rank=256,
-                                own_begin=256, T_own=256, I_shared=128, minibatch_rows=128,
+                                d=512, E=64, k=8, I=256, e0=4, E_l=4, tokens_per_rank=256,
+                                own_begin=256, T_own=256, I_shared=256, minibatch_rows=128,
                                 ring_rows=1024),
     "zipf_bf16": synth.scaled(synth.WORKLOADS[synth.EP96], name="zipf_bf16", T_pool=4096,
                               d=256, E=96, k=8, I=128, e0=0, E_l=4, tokens_per_rank=256,
