@@ -113,21 +113,24 @@ __global__ __launch_bounds__(256) void k_router_logits(const T* __restrict__ x,
     }
     // ring slot c % NPRE holds chunk c; after computing it, chunk c + NPRE is loaded into it
     // (clamped to the last chunk past the end: a harmless reload). Unrolled by NPRE so every
-    // slot index is static; the scheduling barriers keep each load after the FMAs that read
-    // its slot and ahead of the next chunk's FMAs.
-    for (int c0 = 0; c0 < nc; c0 += RT_NPRE) {
+    // slot index is static, and without branches inside, so the wait for a slot's loads
+    // counts only the younger loads in flight; the scheduling barriers keep each load after
+    // the FMAs that read its slot and ahead of the next chunk's FMAs. The last nc % NPRE
+    // chunks sit in the first slots and are computed after the loop.
+    const int nc_main = nc - nc % RT_NPRE;
+    for (int c0 = 0; c0 < nc_main; c0 += RT_NPRE) {
 #pragma unroll
       for (int q = 0; q < RT_NPRE; ++q) {
-        const int c = c0 + q;
-        if (c < nc) {
-          chunk_all<T>(acc, ring[q], std::make_integer_sequence<int, RT_K>{});
-          __builtin_amdgcn_sched_barrier(0);
-          const int cn = min(c + RT_NPRE, nc - 1);
-          ring[q].load(xr + cn * RT_K, wl + cn * RT_K);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        chunk_all<T>(acc, ring[q], std::make_integer_sequence<int, RT_K>{});
+        __builtin_amdgcn_sched_barrier(0);
+        const int cn = min(c0 + q + RT_NPRE, nc - 1);
+        ring[q].load(xr + cn * RT_K, wl + cn * RT_K);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+#pragma unroll
+    for (int q = 0; q + 1 < RT_NPRE; ++q)
+      if (nc_main + q < nc) chunk_all<T>(acc, ring[q], std::make_integer_sequence<int, RT_K>{});
   }
   const T* wrow[RT_EXP];
 #pragma unroll
