@@ -112,11 +112,12 @@ int mok_dispatch_plan(const int32_t* topk_idx, int64_t T_pool, int32_t k, int32_
 
 /* The same plan for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): same arguments and results
- * as mok_dispatch_plan without `ws`. Its scratch is a fixed 4 MiB device array inside the
- * library (one per GPU, kept until the process ends); a request needing more -- more than 2^19
- * entries of plan chunks x E_l, where a chunk is 512 or more routes and there are at most 4096
- * chunks -- returns MOK_EWORKSPACE before any launch. Calls no allocator. Every call on one GPU
- * shares that GPU's array, so calls that overlap on one GPU (unordered streams) race. */
+ * as mok_dispatch_plan without `ws`. Its scratch is a fixed 256 KiB device array inside the
+ * library (one per GPU, kept until the process ends) that holds the plan's per-chunk expert
+ * histograms: chunks x E_l int32, at most 2^16 for any valid arguments (the plan cuts the
+ * routes into at most 256 chunks, with chunks^2 x E_l <= 2^23); a request needing more would
+ * return MOK_EWORKSPACE before any launch. Calls no allocator. Every call on one GPU shares
+ * that GPU's array, so calls that overlap on one GPU (unordered streams) race. */
 int mok_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T_pool, int32_t k, int32_t E,
                               int32_t e0, int32_t E_l, int32_t tokens_per_rank, int32_t* counts,
                               int32_t* offsets, int32_t* rank_counts, int32_t* route_ids,

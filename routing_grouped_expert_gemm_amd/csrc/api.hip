@@ -37,7 +37,7 @@ struct Layout {
   int64_t route_cap = 1;   // rows of route_ids
   int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0, cap_g = 0, cap_r = 0;
   size_t wl = 0, logits = 0, idx = 0, w = 0, counts = 0, offsets = 0, rank_counts = 0,
-         route_ids = 0, blk_counts = 0, blk_base = 0, H = 0, H_sc = 0, A_codes = 0, A_sc = 0,
+         route_ids = 0, blk_counts = 0, H = 0, H_sc = 0, A_codes = 0, A_sc = 0,
          wq = 0, total = 0;
   // MX weight codes / scales sub-offsets (relative to wq)
   size_t wg_q = 0, wu_q = 0, wd_q = 0, sg_q = 0, su_q = 0, sd_q = 0;
@@ -117,9 +117,8 @@ Layout layout_moe(const mok_moe_args* a) {
   L.offsets = take(sizeof(int32_t) * (a->E_l + 1));
   L.rank_counts = 0;
   L.route_ids = a->route_ids_out ? 0 : take(sizeof(int32_t) * std::max<int64_t>(1, n_cap));
-  const int64_t nb = plan_n_blocks(a->T_pool * a->k);
+  const int64_t nb = plan_n_blocks(a->T_pool * a->k, a->E_l);
   L.blk_counts = take(sizeof(int32_t) * nb * a->E_l);
-  L.blk_base = take(sizeof(int32_t) * nb * a->E_l);
   const int64_t ring_rows = (int64_t)L.n_slots * mb;
   if (mx) {
     L.H = take(cb((size_t)ring_rows * L.Hld));
@@ -178,8 +177,8 @@ int mok_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk
 
 int mok_dispatch_plan_workspace_bytes(int64_t T_pool, int32_t k, int32_t E_l, size_t* bytes) {
   if (!bytes || T_pool < 0 || k < 1 || E_l < 1 || E_l > 1024) return MOK_EINVAL;
-  const int64_t nb = plan_n_blocks(T_pool * k);
-  *bytes = 2 * align_up(sizeof(int32_t) * nb * E_l);
+  const int64_t nb = plan_n_blocks(T_pool * k, E_l);
+  *bytes = align_up(sizeof(int32_t) * nb * E_l);
   return MOK_OK;
 }
 
@@ -196,13 +195,10 @@ int mok_dispatch_plan(const int32_t* topk_idx, int64_t T_pool, int32_t k, int32_
   size_t need = 0;
   mok_dispatch_plan_workspace_bytes(T_pool, k, E_l, &need);
   if (!ws || ws_bytes < need) return MOK_EWORKSPACE;
-  const int64_t nb = plan_n_blocks(T_pool * k);
   int32_t* blk_counts = (int32_t*)ws;
-  int32_t* blk_base = (int32_t*)((char*)ws + align_up(sizeof(int32_t) * nb * E_l));
   const int64_t cap = std::max<int64_t>(1, T_pool * std::min(k, E_l));
   return status_of(launch_plan(topk_idx, T_pool, k, e0, E_l, tokens_per_rank, counts, offsets,
-                               rank_counts, route_ids, blk_counts, blk_base, cap,
-                               (hipStream_t)stream));
+                               rank_counts, route_ids, blk_counts, cap, (hipStream_t)stream));
 }
 
 int mok_moe_workspace_bytes(const mok_moe_args* a, size_t* bytes) {
@@ -252,17 +248,10 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     mark(MOK_STAGE_ROUTE);
   }
 
-  // stage 2: plan
+  // stage 2: plan (and the expert stages' work list)
   int32_t* counts = a->counts_out ? a->counts_out : (int32_t*)at(L.counts);
   int32_t* offsets = a->offsets_out ? a->offsets_out : (int32_t*)at(L.offsets);
   int32_t* route_ids = a->route_ids_out ? a->route_ids_out : (int32_t*)at(L.route_ids);
-  {
-    hipError_t e = launch_plan(idx, a->T_pool, k, a->e0, a->E_l, a->tokens_per_rank, counts,
-                               offsets, a->rank_counts_out, route_ids, (int32_t*)at(L.blk_counts),
-                               (int32_t*)at(L.blk_base), L.route_cap, s, ev_start(MOK_STAGE_PLAN),
-                               ev_stop(MOK_STAGE_PLAN));
-    if (e != hipSuccess) return MOK_EHIP;
-  }
 
   // stages 3-5
   ExpertPass p = {};
@@ -274,6 +263,7 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.k = k;
   p.I = a->I;
   p.E_l = a->E_l;
+  p.e0 = a->e0;
   p.I_sh = a->n_shared * a->I_shared;
   p.I_seg = a->n_shared > 0 ? a->I_shared : 1;
   p.own_begin = a->own_begin;
@@ -301,6 +291,10 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.wl = (int32_t*)at(L.wl);
   p.y_slots = a->y_slots;
   p.y_shared = a->y_shared;
+  if (launch_plan_worklist(idx, a->T_pool, a->tokens_per_rank, a->rank_counts_out,
+                           (int32_t*)at(L.blk_counts), p, s, ev_start(MOK_STAGE_PLAN),
+                           ev_stop(MOK_STAGE_PLAN)) != hipSuccess)
+    return MOK_EHIP;
   if (a->dtype == MOK_MXFP8 || a->dtype == MOK_MXFP4) {
     const bool fp4 = a->dtype == MOK_MXFP4;
     char* q = ws;

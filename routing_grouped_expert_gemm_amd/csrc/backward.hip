@@ -394,7 +394,7 @@ constexpr size_t kAl = 256;
 size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
 struct BwdLayout {
-  size_t counts, offsets, route_ids, blk_counts, blk_base, err;
+  size_t counts, offsets, route_ids, blk_counts, err;
   size_t Ar, dPr, dGr, dUr, Hr, dOr, dGo, dUo, Ho, Gr, Ur, Dr, dAr, Go, Uo, Do, dAo, dw_rows;
   size_t t_rec, t_dd, t_dug, t_duu, t_wg, total;
   int64_t cap;
@@ -443,9 +443,8 @@ BwdLayout layout_bwd(const mok_moe_bwd_args* a) {
   L.counts = take(4 * a->E_l);
   L.offsets = take(4 * (a->E_l + 1));
   L.route_ids = take(4 * std::max<int64_t>(1, worst));
-  const int64_t nb = plan_n_blocks(a->T_pool * a->k);
+  const int64_t nb = plan_n_blocks(a->T_pool * a->k, a->E_l);
   L.blk_counts = take(4 * nb * a->E_l);
-  L.blk_base = take(4 * nb * a->E_l);
   L.err = take(16);
   L.Ar = take(2 * cap * d); L.dPr = take(2 * cap * d); L.dOr = take(2 * cap * d);
   L.dGr = take(2 * cap * I); L.dUr = take(2 * cap * I); L.Hr = take(2 * cap * I);
@@ -516,8 +515,7 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   // the plan (also yields route_ids for the gathers), then the rows in plan order
   if (launch_plan(a->topk_idx, a->T_pool, a->k, a->e0, a->E_l, a->tokens_per_rank,
                   (int32_t*)p.counts, (int32_t*)p.offsets, nullptr, (int32_t*)p.route_ids,
-                  (int32_t*)at(L.blk_counts), (int32_t*)at(L.blk_base), std::max<int64_t>(1, worst),
-                  s) != hipSuccess)
+                  (int32_t*)at(L.blk_counts), std::max<int64_t>(1, worst), s) != hipSuccess)
     return MOK_EHIP;
   launch_k(k_bwd_describe, dim3(1), dim3(64), 0, s, nullptr, nullptr, p);
   // routed x rows and their slot gradients, gathered in plan order (rows past the capacity

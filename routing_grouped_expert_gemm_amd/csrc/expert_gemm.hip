@@ -27,329 +27,14 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "worklist.h"
 
 namespace mok {
-
-// ------------------------------------------------------------------------- work list
-// int32 block layout (offsets in ints): header; per minibatch: group, first row, rows, the
-// prefix sums of its gather, up and down items, three completion counters, its ring slot, the
-// minibatch that used that slot before it (-1: none), the prefix of its rows, and (ring) the
-// item prefix sums in XCD-major order; then, 16-byte aligned, one int4 per
-// up tile and per down tile {minibatch, tile within it, first row, group << 16 | rows} so that a
-// workgroup finds its tile with a single load, and (ring work loop only) the ring order of all
-// items, the item kind in bits 28+ of the second field.
-// Header: counts, the error word, and for the ring loop the per-XCD split (WL_AFFINE set): XCD
-// x owns minibatches x, x + 8, x + 16, ... (positions [XB[x], XB[x+1]) of the XCD-major order)
-// and ring items [XR[x], XR[x+1]), and takes them with its own ticket TICKETS[x]; without the
-// split every workgroup uses TICKETS[0] over all items.
-constexpr int WL_N_MB = 0, WL_N_U = 1, WL_N_D = 2, WL_ERR = 4, WL_N_R = 5, WL_AFFINE = 6,
-              WL_XB = 8, WL_XR = 17, WL_TICKETS = 26, WL_EXITS = 34, WL_HDR = 48;
-constexpr int N_XCD = 8;        // XCDs of an MI355X, each with its own L2
-constexpr int XB_N = 4;         // N tiles per block of the stage tables' tile order: up
-constexpr int XB_ND = 8;        // ... down
-constexpr uint32_t ERR_OVERFLOW = 1u, ERR_WAIT = 2u;
-constexpr int KIND_U = 0, KIND_D = 1, KIND_G = 2, KIND_SHIFT = 28;
-constexpr int G_ROWS = 64;      // rows of one gather + quantise item of the ring loop
-MOK_DEV int32_t* wl_group(int32_t* wl, int cap) { return wl + WL_HDR; }
-MOK_DEV int32_t* wl_row0(int32_t* wl, int cap) { return wl + WL_HDR + cap; }
-MOK_DEV int32_t* wl_rows(int32_t* wl, int cap) { return wl + WL_HDR + 2 * cap; }
-MOK_DEV int32_t* wl_ustart(int32_t* wl, int cap) { return wl + WL_HDR + 3 * cap; }
-MOK_DEV int32_t* wl_dstart(int32_t* wl, int cap) { return wl + WL_HDR + 4 * cap + 1; }
-MOK_DEV int32_t* wl_gstart(int32_t* wl, int cap) { return wl + WL_HDR + 5 * cap + 2; }
-MOK_DEV int32_t* wl_done(int32_t* wl, int cap, int kind) { return wl + WL_HDR + (6 + kind) * cap + 3; }
-MOK_DEV int32_t* wl_slot(int32_t* wl, int cap) { return wl + WL_HDR + 9 * cap + 3; }
-MOK_DEV int32_t* wl_prev(int32_t* wl, int cap) { return wl + WL_HDR + 10 * cap + 3; }
-MOK_DEV int32_t* wl_rpre(int32_t* wl, int cap) { return wl + WL_HDR + 11 * cap + 3; }   // cap + 1
-// ring order: prefix sums of gather, up and down items over the minibatches in XCD-major order
-MOK_DEV int32_t* wl_pg(int32_t* wl, int cap) { return wl + WL_HDR + 12 * cap + 4; }     // cap + 1
-MOK_DEV int32_t* wl_pu(int32_t* wl, int cap) { return wl + WL_HDR + 13 * cap + 5; }     // cap + 1
-MOK_DEV int32_t* wl_pd(int32_t* wl, int cap) { return wl + WL_HDR + 14 * cap + 6; }     // cap + 1
-MOK_HOSTDEV size_t wl_tab_off(int cap) { return ((size_t)WL_HDR + 15 * (size_t)cap + 7 + 3) & ~(size_t)3; }
-MOK_DEV int4* wl_utab(int32_t* wl, int cap) { return (int4*)(wl + wl_tab_off(cap)); }
-MOK_DEV int4* wl_dtab(int32_t* wl, int cap, int cap_u) { return (int4*)(wl + wl_tab_off(cap)) + cap_u; }
-MOK_DEV int4* wl_rtab(int32_t* wl, int cap, int cap_u, int cap_d) {
-  return (int4*)(wl + wl_tab_off(cap)) + cap_u + cap_d;
-}
 
 size_t worklist_ints(int max_mb, int cap_u, int cap_d, int cap_r) {
   return wl_tab_off(max_mb) + 4 * ((size_t)cap_u + (size_t)cap_d + (size_t)cap_r);
 }
 
-
-// One workgroup of 1024 threads. Minibatches: routed experts ascending (rows ascending within
-// each plan region), then the shared experts' minibatches over the own tokens. Every count
-// comes from the plan on the device; nothing returns to the host.
-//
-// Ring order (ring = true): block b holds the gather items of minibatch b (MXFP8 only), its up
-// tiles, then the down tiles of minibatch b - lag. A down item needs every up tile of its
-// minibatch; an up item needs its gather items and the down items of the minibatch that used
-// its ring slot before it; a gather item needs that minibatch's up items. With lag < slots
-// every dependency of an item lies earlier in this order.
-//
-// With at least 8 slots the ring is split by XCD: XCD x runs minibatches x, x + 8, x + 16, ...
-// on its own slots (n_slots / 8 of them, lag half of that) in the order above. A slot's
-// producer and consumer then always share one L2, and the handover needs no L2 write-back or
-// invalidation. Otherwise (fewer slots) one order covers all minibatches on all slots and
-// every handover is made coherent device-wide.
-__global__ __launch_bounds__(1024) void k_build_worklist(const int32_t* __restrict__ counts,
-                                                         const int32_t* __restrict__ offsets,
-                                                         int E_l, int T_own, int mb, int bm,
-                                                         int nU_r, int nU_s, int nD, bool gather,
-                                                         bool ring, bool xcd_split, int n_slots,
-                                                         int cap, int cap_u, int cap_d, int cap_r,
-                                                         int64_t route_cap,
-                                                         int32_t* __restrict__ wl) {
-  __shared__ int32_t sh[1024];
-  const int t = threadIdx.x;
-  int32_t* grp = wl_group(wl, cap);
-  int32_t* r0 = wl_row0(wl, cap);
-  int32_t* nr = wl_rows(wl, cap);
-  int32_t* us = wl_ustart(wl, cap);
-  int32_t* ds = wl_dstart(wl, cap);
-  int32_t* gs = wl_gstart(wl, cap);
-  // routed minibatches: experts ascending, rows ascending within each region
-  int32_t n_routed = 0;
-  for (int c0 = 0; c0 < E_l; c0 += 1024) {
-    const int e = c0 + t;
-    const int32_t cnt = e < E_l ? counts[e] : 0;
-    const int32_t nm = (cnt + mb - 1) / mb;
-    int32_t tot;
-    const int32_t base = n_routed + block_excl_scan_1024(nm, sh, &tot);
-    for (int i = 0; i < nm; ++i) {
-      const int m = base + i;
-      if (m < cap) {
-        grp[m] = e;
-        r0[m] = offsets[e] + i * mb;
-        nr[m] = min(mb, cnt - i * mb);
-      }
-    }
-    n_routed += tot;
-  }
-  const int32_t n_sh = (nU_s > 0 && T_own > 0) ? (T_own + mb - 1) / mb : 0;
-  for (int i = t; i < n_sh; i += 1024) {
-    const int m = n_routed + i;
-    if (m < cap) {
-      grp[m] = E_l;
-      r0[m] = i * mb;
-      nr[m] = min(mb, T_own - i * mb);
-    }
-  }
-  const int32_t n_mb = min(cap, n_routed + n_sh);
-  for (int m = t; m < cap; m += 1024) {
-    wl_done(wl, cap, KIND_U)[m] = 0;
-    wl_done(wl, cap, KIND_D)[m] = 0;
-    wl_done(wl, cap, KIND_G)[m] = 0;
-  }
-  __syncthreads();
-  // item prefix sums: tiles of a minibatch = ceil(rows / bm) * n-tiles of its stage
-  int32_t carry_u = 0, carry_d = 0, carry_g = 0, carry_r = 0;
-  int32_t* rp = wl_rpre(wl, cap);
-  for (int c0 = 0; c0 < n_mb; c0 += 1024) {
-    const int m = c0 + t;
-    int32_t nu = 0, nd = 0, ng = 0;
-    if (m < n_mb) {
-      const int32_t mt = (nr[m] + bm - 1) / bm;
-      nu = mt * (grp[m] < E_l ? nU_r : nU_s);
-      nd = mt * nD;
-      ng = gather ? (nr[m] + G_ROWS - 1) / G_ROWS : 0;
-    }
-    int32_t tu, td, tg, tr;
-    const int32_t eu = block_excl_scan_1024(nu, sh, &tu);
-    const int32_t ed = block_excl_scan_1024(nd, sh, &td);
-    const int32_t eg = block_excl_scan_1024(ng, sh, &tg);
-    const int32_t er = block_excl_scan_1024(m < n_mb ? nr[m] : 0, sh, &tr);
-    if (m < n_mb) {
-      us[m] = carry_u + eu;
-      ds[m] = carry_d + ed;
-      gs[m] = carry_g + eg;
-      rp[m] = carry_r + er;
-    }
-    carry_u += tu;
-    carry_d += td;
-    carry_g += tg;
-    carry_r += tr;
-  }
-  // more local routes than route_ids holds (a token naming one expert twice) also overflows:
-  // no tile then reads past the plan
-  const bool overflow = n_routed + n_sh > cap || carry_u > cap_u || carry_d > cap_d ||
-                        (ring && (int64_t)carry_u + carry_d + carry_g > cap_r) ||
-                        (int64_t)offsets[E_l] > route_cap;
-  const bool affine = ring && xcd_split && n_slots >= N_XCD;
-  if (t == 0) {
-    us[n_mb] = carry_u;
-    ds[n_mb] = carry_d;
-    gs[n_mb] = carry_g;
-    rp[n_mb] = overflow ? 0 : carry_r;
-    wl[WL_N_MB] = n_mb;
-    wl[WL_N_U] = overflow ? 0 : carry_u;
-    wl[WL_N_D] = overflow ? 0 : carry_d;
-    wl[WL_N_R] = (overflow || !ring) ? 0 : carry_u + carry_d + carry_g;
-    wl[WL_ERR] = overflow ? ERR_OVERFLOW : 0;
-    wl[WL_AFFINE] = affine ? 1 : 0;
-  }
-  if (t < N_XCD) wl[WL_TICKETS + t] = 0;
-  if (t == 0) wl[WL_EXITS] = 0;
-  // Ring order. With at least 8 slots the ring is split by XCD: minibatch m belongs to XCD
-  // m % 8 as its (m / 8)-th minibatch, so the 8 XCDs run neighbouring minibatches -- mostly of
-  // the same expert -- at the same time, and weights that one XCD reads from HBM the others
-  // find in the chip's last-level cache (the MALL, shared by all XCDs). Without the split one
-  // order spans all minibatches. Positions: XCD-major order p = base(x) + j for m = x + 8 j
-  // (p = m without the split), and prefix sums of each item kind over p.
-  __syncthreads();
-  auto n_of = [&](int x) { return affine ? (n_mb - x + N_XCD - 1) / N_XCD : (x == 0 ? n_mb : 0); };
-  auto base_of = [&](int x) {
-    int b = 0;
-    for (int y = 0; y < x; ++y) b += n_of(y);
-    return b;
-  };
-  auto m_of = [&](int pp) {                         // the minibatch at XCD-major position pp
-    if (!affine) return pp;
-    int x = 0, b = 0;
-    while (x < N_XCD - 1 && pp >= b + n_of(x)) b += n_of(x++);
-    return x + N_XCD * (pp - b);
-  };
-  int32_t* pg = wl_pg(wl, cap);
-  int32_t* pu = wl_pu(wl, cap);
-  int32_t* pd = wl_pd(wl, cap);
-  if (ring && !overflow) {
-    int32_t cg = 0, cu = 0, cd = 0;
-    for (int c0 = 0; c0 < n_mb; c0 += 1024) {
-      const int pp = c0 + t;
-      int32_t vg = 0, vu = 0, vd = 0;
-      if (pp < n_mb) {
-        const int m = m_of(pp);
-        vg = gs[m + 1] - gs[m];
-        vu = us[m + 1] - us[m];
-        vd = ds[m + 1] - ds[m];
-      }
-      int32_t tg, tu, td;
-      const int32_t eg = block_excl_scan_1024(vg, sh, &tg);
-      const int32_t eu = block_excl_scan_1024(vu, sh, &tu);
-      const int32_t ed = block_excl_scan_1024(vd, sh, &td);
-      if (pp < n_mb) {
-        pg[pp] = cg + eg;
-        pu[pp] = cu + eu;
-        pd[pp] = cd + ed;
-      }
-      cg += tg;
-      cu += tu;
-      cd += td;
-    }
-    if (t == 0) {
-      pg[n_mb] = cg;
-      pu[n_mb] = cu;
-      pd[n_mb] = cd;
-    }
-  }
-  __syncthreads();
-  if (t <= N_XCD) {
-    const int b = t < N_XCD ? base_of(t) : n_mb;
-    wl[WL_XB + t] = b;
-    wl[WL_XR + t] = (ring && !overflow) ? pg[b] + pu[b] + pd[b] : 0;
-  }
-  // Stage-ordered tables: when the shared experts' down tiles are the longer ones (K =
-  // n_shared * I_shared > I), the down table lists them first, so that the longest tiles start
-  // first and the stage ends evenly.
-  const bool shared_first = nU_s > nU_r;
-  const int32_t d_sh0 = ds[min(n_routed, n_mb)], d_sh = carry_d - d_sh0;
-  if (overflow) return;
-  // Tile order in the stage tables, per group (routed expert, or the shared experts): blocks of
-  // XB consecutive N tiles (XB_N up, XB_ND down), and in each block the group's M tiles in
-  // order, each with the block's N tiles. The 32 workgroups of an XCD take 32 consecutive
-  // entries: with 8 or more M tiles in a group, an up round runs 8 M tiles x 4 N tiles and reads
-  // 12 operand tiles per K step from the XCD's L2, not the 18 of 2 M tiles x 16 N tiles
-  // (minibatch-major order).
-  int4* ut = wl_utab(wl, cap);
-  int4* dt = wl_dtab(wl, cap, cap_u);
-  int4* rt = wl_rtab(wl, cap, cap_u, cap_d);
-  const int mpm = (mb + bm - 1) / bm;               // M tiles of a whole minibatch
-  auto dshift = [&](int m) {
-    return !shared_first ? ds[m] : (m >= n_routed ? ds[m] - d_sh0 : ds[m] + d_sh);
-  };
-  int32_t* slot = wl_slot(wl, cap);
-  int32_t* prev = wl_prev(wl, cap);
-  // Stage tables (the ring loop reads only its own). Per chunk of 1024 minibatches: one thread
-  // per minibatch puts its placement in LDS, then one thread per tile finds its minibatch by a
-  // binary search over the chunk's tile prefix sums in LDS and writes the entry.
-  if (!ring) {
-    __shared__ int32_t c_pu[1025], c_pd[1025];
-    __shared__ int32_t c_first[1024], c_gw[1024], c_bu[1024], c_bd[1024], c_mt[1024], c_mo[1024];
-    for (int c0 = 0; c0 < n_mb; c0 += 1024) {
-      const int nc = min(1024, n_mb - c0);
-      __syncthreads();                                 // the previous chunk's readers are done
-      if (t < nc) {
-        const int m = c0 + t;
-        const int32_t g = grp[m], rw = nr[m], first = r0[m];
-        // the group's minibatches [f, f_end): all but the last hold mb rows
-        int f, f_end;
-        if (g < E_l) {
-          f = m - (first - offsets[g]) / mb;
-          f_end = f + (counts[g] + mb - 1) / mb;
-        } else {
-          f = n_routed;
-          f_end = n_mb;
-        }
-        c_first[t] = first;
-        c_gw[t] = (g << 16) | rw;
-        c_bu[t] = us[f];
-        c_bd[t] = dshift(f);
-        c_mt[t] = (f_end - 1 - f) * mpm + (nr[f_end - 1] + bm - 1) / bm;   // the group's M tiles
-        c_mo[t] = (m - f) * mpm;                                            // ... before m
-      }
-      if (t <= nc) {
-        c_pu[t] = us[c0 + t];
-        c_pd[t] = ds[c0 + t];
-      }
-      __syncthreads();
-      auto place = [&](const int32_t* ps, int nN_r, int nN_s, int32_t* bases, int4* tab, int XB) {
-        for (int32_t i = ps[0] + t; i < ps[nc]; i += 1024) {
-          int lo = 0, hi = nc;                         // ps[lo] <= i < ps[hi]
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (ps[mid] <= i) lo = mid; else hi = mid;
-          }
-          const int l = i - ps[lo], gw = c_gw[lo];
-          const int mt_m = ((gw & 0xFFFF) + bm - 1) / bm;
-          const int mt = l % mt_m, nt = l / mt_m, nN = (gw >> 16) < E_l ? nN_r : nN_s;
-          const int nb = nt / XB, w = min(XB, nN - nb * XB);
-          tab[bases[lo] + nb * c_mt[lo] * XB + (c_mo[lo] + mt) * w + (nt - nb * XB)] =
-              make_int4(c0 + lo, l, c_first[lo], gw);
-        }
-      };
-      place(c_pu, nU_r, nU_s, c_bu, ut, XB_N);
-      place(c_pd, nD, nD, c_bd, dt, XB_ND);
-    }
-  }
-  for (int m = t; m < n_mb; m += 1024) {
-    const int32_t g = grp[m], rw = nr[m], first = r0[m];
-    const int4 e0 = make_int4(m, 0, first, (g << 16) | rw);
-    const int32_t nu = us[m + 1] - us[m], nd = ds[m + 1] - ds[m], ng = gs[m + 1] - gs[m];
-    // this minibatch: the j-th of its XCD's n_x, on S slots starting at slot s0, order lag L
-    int S = n_slots, s0 = 0, j = m, pb = 0, nx = n_mb, mstep = 1;
-    if (affine) {
-      const int x = m % N_XCD;
-      S = n_slots / N_XCD;
-      s0 = x * S;
-      j = m / N_XCD;
-      pb = base_of(x);
-      nx = n_of(x);
-      mstep = N_XCD;
-    }
-    const int L = S >= 2 ? S / 2 : 0;
-    slot[m] = s0 + j % S;
-    prev[m] = j >= S ? m - mstep * S : -1;
-    if (ring) {
-      // block j of the XCD's order: gather items of j, up tiles of j, down tiles of j - L
-      const int pp = pb + j, pl = pb + max(0, j - L), pa = pb + min(j + L + 1, nx);
-      const int32_t pos_g = pg[pp] + pu[pp] + pd[pl];
-      const int32_t pos_u = pg[pp + 1] + pu[pp] + pd[pl];
-      const int32_t pos_d = pg[pa] + pu[pa] + pd[pp];
-      for (int l = 0; l < ng; ++l) { int4 e = e0; e.y = (KIND_G << KIND_SHIFT) | l; rt[pos_g + l] = e; }
-      for (int l = 0; l < nu; ++l) { int4 e = e0; e.y = (KIND_U << KIND_SHIFT) | l; rt[pos_u + l] = e; }
-      for (int l = 0; l < nd; ++l) { int4 e = e0; e.y = (KIND_D << KIND_SHIFT) | l; rt[pos_d + l] = e; }
-    }
-  }
-}
 
 // ------------------------------------------------------------------------- GEMM tiles
 // Tile geometry. A workgroup of WAVES_M x WAVES_N waves computes a BM x BN block of the
@@ -1681,8 +1366,8 @@ template <Elem EL, bool F32OUT>
 static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* const* ev) {
   typedef typename CfgOf<EL>::type C;
   if (is_mx<EL>() && !p.ring)
-    launch_k(k_gather_quantize<EL == Elem::FP4>, dim3(p.grid * 8), dim3(256), 0, s, nullptr,
-             ev_at(ev, EV_GATHER + 1), p);
+    launch_k(k_gather_quantize<EL == Elem::FP4>, dim3(p.grid * 8), dim3(256), 0, s,
+             ev_at(ev, EV_GATHER), ev_at(ev, EV_GATHER + 1), p);
   if (p.ring) {
     launch_k(k_ring<EL, F32OUT, C>, dim3(p.grid), dim3(C::NT), 0, s, ev_at(ev, EV_UP),
              ev_at(ev, EV_UP + 1), p);
@@ -1706,17 +1391,37 @@ void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, bool gather_item
   *cap_g = gather_items ? (int)std::min<int64_t>(INT32_MAX / 8, (int64_t)max_mb * ((mb + G_ROWS - 1) / G_ROWS)) : 0;
 }
 
-hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev) {
-  const int nU_r = (p.I + Big::BN / 2 - 1) / (Big::BN / 2);
-  const int nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
-  const int nD = (p.d + Big::BN - 1) / Big::BN;
+hipError_t launch_plan_worklist(const int32_t* idx, int64_t n_tok, int64_t tokens_per_rank,
+                                int32_t* rank_counts, int32_t* blk_counts, const ExpertPass& p,
+                                hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const bool mx = p.elem == Elem::FP8 || p.elem == Elem::FP4;
-  const bool gather_items = p.ring && mx;
-  const bool gather_launch = mx && !p.ring;                   // ends the GATHER stage
-  launch_k(k_build_worklist, dim3(1), dim3(1024), 0, s, ev_at(ev, EV_GATHER),
-           gather_launch ? nullptr : ev_at(ev, EV_GATHER + 1), p.counts, p.offsets, p.E_l,
-           p.T_own, p.mb, Big::BM, nU_r, nU_s, nD, gather_items, p.ring, p.xcd_split, p.n_slots,
-           p.max_mb, p.cap_u, p.cap_d, p.cap_r, p.route_cap, p.wl);
+  WlBuild wb = {};
+  wb.wl = p.wl;
+  wb.E_l = p.E_l;
+  wb.T_own = p.T_own;
+  wb.mb = p.mb;
+  wb.bm = Big::BM;
+  wb.nU_r = (p.I + Big::BN / 2 - 1) / (Big::BN / 2);
+  wb.nU_s = (p.I_sh + Big::BN / 2 - 1) / (Big::BN / 2);
+  wb.nD = (p.d + Big::BN - 1) / Big::BN;
+  wb.gather = p.ring && mx;
+  wb.ring = p.ring;
+  wb.xcd_split = p.xcd_split;
+  wb.n_slots = p.n_slots;
+  wb.cap = p.max_mb;
+  wb.cap_u = p.cap_u;
+  wb.cap_d = p.cap_d;
+  wb.cap_r = p.cap_r;
+  wb.route_cap = p.route_cap;
+  return launch_plan(idx, n_tok, p.k, p.e0, p.E_l, tokens_per_rank, (int32_t*)p.counts,
+                     (int32_t*)p.offsets, rank_counts, (int32_t*)p.route_ids, blk_counts,
+                     p.route_cap, s, ev0, ev1, &wb);
+}
+
+hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev) {
+  const bool mx = p.elem == Elem::FP8 || p.elem == Elem::FP4;
+  if (!(mx && !p.ring))                  // the GATHER stage launches nothing
+    mark_empty(s, ev_at(ev, EV_GATHER), ev_at(ev, EV_GATHER + 1));
   if (p.elem == Elem::BF16) return launch_stages_t<Elem::BF16, false>(p, s, ev);
   if (p.elem == Elem::F32) return launch_stages_t<Elem::F32, true>(p, s, ev);
   if (p.elem == Elem::FP4) return launch_stages_t<Elem::FP4, false>(p, s, ev);

@@ -27,13 +27,17 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t n_tok, in
 hipError_t launch_topk(const float* logits, int64_t n_tok, int E, int k, int32_t* idx,
                        float* w, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
-int64_t plan_chunk(int64_t n_routes);
-int64_t plan_n_blocks(int64_t n_routes);
+// The plan: chunk histograms (blk_counts: plan_n_blocks * E_l ints of workspace), then the
+// stable scatter; with wb (the expert stages' work list to build) one more workgroup of the
+// scatter launch builds it from the same sums.
+struct WlBuild;
+int64_t plan_chunk(int64_t n_routes, int E_l);
+int64_t plan_n_blocks(int64_t n_routes, int E_l);
 hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
                        int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
                        int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
-                       int32_t* blk_base, int64_t route_cap, hipStream_t s,
-                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                       int64_t route_cap, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr, const WlBuild* wb = nullptr);
 
 // MX scales of the operands the expert GEMMs read are stored K-step major: a matrix of R rows
 // and K columns keeps the 4 scales of K step j (128 elements) of row r as the 4-byte word
@@ -58,6 +62,7 @@ struct ExpertPass {
   Elem elem;             // GEMM operand type
   bool out_f32;          // outputs (H for non-MX, P, S, y) in float32 (else bf16)
   int d, k, I, E_l;
+  int e0;                // first local expert
   int I_sh;              // n_shared * I_shared (0: no shared expert)
   int I_seg;             // I_shared: K-segment length of the shared down projection
   int64_t own_begin;
@@ -91,7 +96,7 @@ struct ExpertPass {
   uint8_t* A_codes;      // MX: gathered x rows [n_slots*mb, d]
   uint8_t* A_sc;         // MX: K-step-major scales of the n_slots*mb ring rows of A
   // work list
-  int32_t* wl;           // work-list block (see expert_gemm.hip)
+  int32_t* wl;           // work list (layout in worklist.h)
   // outputs
   void* y_slots;
   void* y_shared;
@@ -105,6 +110,11 @@ void gemm_tile_caps(int max_mb, int mb, int I, int I_sh, int d, bool gather_item
 // ev: optional hipEvent_t[2 * 7] (mok stage events; NULL entries skipped): GATHER on the work
 // list (and the MXFP8 gather), UP on the gate/up launch, DOWN on the down launch (ring loop: UP
 // on the one persistent launch, DOWN recorded empty).
+// The plan of a forward, with the work list of its expert stages (p) built in the same launch.
+hipError_t launch_plan_worklist(const int32_t* idx, int64_t n_tok, int64_t tokens_per_rank,
+                                int32_t* rank_counts, int32_t* blk_counts, const ExpertPass& p,
+                                hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// The expert stages (MX gather, gate/up, down) over the work list launch_plan_worklist built.
 hipError_t launch_expert_stages(const ExpertPass& p, hipStream_t s, void* const* ev);
 hipError_t launch_combine(const void* y_shared, const void* y_slots, void* y, int64_t n_tok,
                           int k, int d, bool f32, hipStream_t s, hipEvent_t e0 = nullptr,

@@ -1,13 +1,12 @@
 // mok_dispatch_plan_noalloc: the dispatch plan with its scratch in a fixed device array, for
 // callers that cannot allocate (code under graph capture, tight serving loops).
 //
-// The plan's scratch is two int32 tables of plan_n_blocks(T_pool * k) x E_l entries (per
-// chunk of routes: its histogram of local experts and its first free row per expert). Here they
-// live in `scratch`, a file-scope device array of kScratchInts int32 (4 MiB) that every GPU the
-// library runs on holds until the process ends. Both tables are fully written by the plan's
-// first two launches before anything reads them, so no call needs them cleared. Every call on
-// one GPU shares that GPU's array: calls that overlap on one GPU (different streams, no order
-// between them) race.
+// The plan's scratch is one int32 table of plan_n_blocks(T_pool * k, E_l) x E_l entries (per
+// chunk of routes, its histogram of local experts; at most 2^16 entries). Here it lives in
+// `scratch`, a file-scope device array of kScratchInts int32 (256 KiB) that every GPU the
+// library runs on holds until the process ends. The plan's first launch writes the whole table
+// before its second reads it, so no call needs it cleared. Every call on one GPU shares that
+// GPU's array: calls that overlap on one GPU (different streams, no order between them) race.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -18,7 +17,7 @@
 
 namespace {
 
-constexpr int64_t kScratchInts = (int64_t)1 << 20;
+constexpr int64_t kScratchInts = (int64_t)1 << 16;
 constexpr int kMaxDevices = 64;
 
 __device__ __align__(256) int32_t scratch[kScratchInts];
@@ -53,14 +52,14 @@ extern "C" int mok_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T_pool
   if (T_pool * (int64_t)k >= (int64_t)1 << 31) return MOK_EINVAL;
   if ((T_pool > 0 && !topk_idx) || !counts || !offsets || !rank_counts || !route_ids)
     return MOK_EINVAL;
-  const int64_t nb = mok::plan_n_blocks(T_pool * k);
-  const int64_t table = nb * E_l;                    // ints per table
-  if (2 * table > kScratchInts) return MOK_EWORKSPACE;   // larger than the fixed scratch
+  const int64_t nb = mok::plan_n_blocks(T_pool * k, E_l);
+  const int64_t table = nb * E_l;                    // ints of the chunk histograms
+  if (table > kScratchInts) return MOK_EWORKSPACE;   // larger than the fixed scratch
   int32_t* base = scratch_of_current_device();
   if (!base) return MOK_EHIP;
   const int64_t cap = std::max<int64_t>(1, T_pool * std::min(k, E_l));
   const hipError_t e = mok::launch_plan(topk_idx, T_pool, k, e0, E_l, tokens_per_rank, counts,
-                                        offsets, rank_counts, route_ids, base, base + table, cap,
+                                        offsets, rank_counts, route_ids, base, cap,
                                         (hipStream_t)stream);
   return e == hipSuccess ? MOK_OK : MOK_EHIP;
 }

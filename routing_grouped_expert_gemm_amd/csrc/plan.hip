@@ -7,22 +7,27 @@
 // What is built for the local experts [e0, e0 + E_l): the number of routes each one receives,
 // the number per (expert, source rank), the exclusive prefix sum of the per-expert numbers
 // (region offsets), and route_ids: every local route id r = t*k + j, grouped by expert, in
-// ascending r inside each group. Three launches keep it deterministic:
+// ascending r inside each group. Two launches keep it deterministic:
 //   k_plan_count   -- per contiguous chunk of routes, a histogram of local experts;
-//   k_plan_scan    -- one workgroup turns the chunk histograms into region offsets and the
-//                     first free row of every (chunk, expert) pair;
-//   k_plan_scatter -- each chunk walks its routes again in order and writes each local route
-//                     at its (chunk, expert) base plus its rank among the chunk's earlier
-//                     routes of that expert (wave ballots), i.e. a stable counting sort; the
-//                     per-(expert, source rank) counts are integer sums added to totals that
-//                     the first launch cleared.
+//   k_plan_scatter -- every workgroup sums the chunk histograms itself (all of them: the
+//                     per-expert counts and region offsets; those of the chunks before its
+//                     own: its first free row in each region), then walks its routes in
+//                     order and writes each local route at that row plus its rank among the
+//                     chunk's earlier routes of that expert (wave ballots), i.e. a stable
+//                     counting sort; the per-(expert, source rank) counts are integer sums
+//                     added to totals that the first launch cleared. One more workgroup, when
+//                     asked, builds the expert stages' work list from the same sums.
 // Positions never come from an atomic, so the result does not depend on scheduling.
+#include <algorithm>
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
+#include "worklist.h"
 
 namespace mok {
 
-constexpr int PLAN_THREADS = 256;
+constexpr int PLAN_THREADS = 1024;
 
 // Also clears the per-(expert, source rank) counts, which the scatter accumulates.
 __global__ __launch_bounds__(PLAN_THREADS) void k_plan_count(const int32_t* __restrict__ idx,
@@ -49,84 +54,75 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_count(const int32_t* __re
     blk_counts[(int64_t)blockIdx.x * E_l + e] = hist[e];
 }
 
-// One workgroup of 1024 threads.
-//   blk_base[b][e] = sum_{b' < b} blk_counts[b'][e]   (the expert's offset is added later)
-//   counts[e] = sum_b blk_counts[b][e],  offsets = exclusive prefix sum of counts.
-// Each expert's block range is split over a group of P consecutive threads (P = 1024 / E_l
-// rounded down to a power of two): per-thread segment sums, one block scan (a group's prefix
-// is the scan minus its first thread's), then the segment walk. Scans: wave shuffles plus one
-// pass over the wave totals.
-__global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ blk_counts,
-                                                    int n_blk, int E_l,
-                                                    int32_t* __restrict__ blk_base,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets) {
-  __shared__ int32_t sh[64];
-  __shared__ int32_t gbase[1024];
-  const int t = threadIdx.x;
-  int P = 1;
-  while (P * 2 * E_l <= 1024) P *= 2;
-  const int experts_per_round = 1024 / P;
-  const int g = t % P, seg = (n_blk + P - 1) / P;
-  const int b0 = min(n_blk, g * seg), b1 = min(n_blk, b0 + seg);
-  for (int e_base = 0; e_base < E_l; e_base += experts_per_round) {
-    const int e = e_base + t / P;
-    const bool active = e < E_l;
-    int32_t local = 0;
-    if (active) {
-#pragma unroll 4
-      for (int b = b0; b < b1; ++b) local += blk_counts[(int64_t)b * E_l + e];
-    }
-    int32_t tot;
-    const int32_t excl = block_excl_scan_1024(local, sh, &tot);
-    if (g == 0) gbase[t / P] = excl;
-    __syncthreads();
-    if (active) {
-      int32_t run = excl - gbase[t / P];
-#pragma unroll 4
-      for (int b = b0; b < b1; ++b) {
-        blk_base[(int64_t)b * E_l + e] = run;
-        run += blk_counts[(int64_t)b * E_l + e];
-      }
-      if (g == P - 1) counts[e] = run;
-    }
-    __syncthreads();
-  }
-  __threadfence_block();
-  // exclusive scan of the counts over experts (E_l <= 1024)
-  const int32_t c = t < E_l ? counts[t] : 0;
-  int32_t total;
-  const int32_t ex = block_excl_scan_1024(c, sh, &total);
-  if (t < E_l) {
-    offsets[t] = ex;
-    if (t == E_l - 1) offsets[E_l] = total;
-  }
-}
+// LDS of the scatter: the per-expert sums (tot, pre, off), then either the scatter's tables
+// (base, per-wave counts, per-(source rank, expert) counts) or the work-list builder's.
+constexpr int PLAN_NR = 4;            // source ranks a chunk counts in LDS
+MOK_HOSTDEV inline int plan_sums_ints(int E_l) { return (3 * E_l + 1 + 3) & ~3; }
+MOK_HOSTDEV inline int plan_scatter_ints(int E_l) { return (PLAN_THREADS / 64 + 1 + PLAN_NR) * E_l; }
 
-// rank_counts (optional): each workgroup counts its routes per (local expert, source rank) in
-// LDS -- the chunk's first PLAN_NR source ranks; routes of later ones, which only very small
-// ranks produce, go straight to global memory -- and adds the counts to the cleared totals
-// (integer additions: the totals do not depend on their order).
-constexpr int PLAN_NR = 4;
-__global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __restrict__ idx,
-                                                               int64_t n_routes, int64_t chunk,
-                                                               int e0, int E_l,
-                                                               const int32_t* __restrict__ blk_base,
-                                                               const int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ route_ids,
-                                                               int32_t* __restrict__ rank_counts,
-                                                               int k, int64_t tokens_per_rank,
-                                                               int64_t R, int64_t cap) {
+// Workgroups 0 .. nb - 1 scatter chunk b; workgroup nb (launched only with a work list to
+// build) builds it. rank_counts (optional): each workgroup counts its routes per (local expert,
+// source rank) in LDS -- the chunk's first PLAN_NR source ranks; routes of later ones, which
+// only very small ranks produce, go straight to global memory -- and adds the counts to the
+// cleared totals (integer additions: the totals do not depend on their order).
+__global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(
+    const int32_t* __restrict__ idx, int64_t n_routes, int64_t chunk, int nb, int e0, int E_l,
+    const int32_t* __restrict__ blk_counts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ route_ids,
+    int32_t* __restrict__ rank_counts, int k, int64_t tokens_per_rank, int64_t R, int64_t cap,
+    WlBuild wb) {
   extern __shared__ int32_t sm[];
-  int32_t* base = sm;                 // [E_l] next free row of each region (this chunk)
-  int32_t* wcnt = sm + E_l;           // [4][E_l] per-wave counts of the current sub-chunk
-  int32_t* rc = sm + 5 * E_l;         // [PLAN_NR][E_l] per-(source rank, expert) counts
+  int32_t* tot = sm;                  // [E_l] routes of each expert
+  int32_t* pre = sm + E_l;            // [E_l] ... in the chunks before this one
+  int32_t* off = sm + 2 * E_l;        // [E_l + 1] region offsets
+  int32_t* un = sm + plan_sums_ints(E_l);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * chunk;
+  const int b = blockIdx.x;
+  for (int e = tid; e < E_l; e += PLAN_THREADS) tot[e] = pre[e] = 0;
+  __syncthreads();
+  // G threads per expert sum every G-th chunk histogram; integer sums, so the totals do not
+  // depend on the order of the LDS additions
+  {
+    const int G = PLAN_THREADS / E_l;
+    if (tid < G * E_l) {
+      const int e = tid % E_l, g = tid / E_l;
+      int32_t st = 0, sp = 0;
+      for (int c = g; c < nb; c += G) {
+        const int32_t v = blk_counts[(int64_t)c * E_l + e];
+        st += v;
+        if (c < b) sp += v;
+      }
+      atomicAdd(&tot[e], st);
+      atomicAdd(&pre[e], sp);
+    }
+  }
+  __syncthreads();
+  {
+    int32_t total;
+    const int32_t ex = block_excl_scan_1024(tid < E_l ? tot[tid] : 0, un, &total);
+    if (tid < E_l) off[tid] = ex;
+    if (tid == 0) off[E_l] = total;
+    if (b == 0) {
+      if (tid < E_l) {
+        counts[tid] = tot[tid];
+        offsets[tid] = ex;
+      }
+      if (tid == 0) offsets[E_l] = total;
+    }
+  }
+  __syncthreads();
+  if (b == nb) {                      // the work-list workgroup
+    build_worklist(wb, tot, off, un);
+    return;
+  }
+  int32_t* base = un;                 // [E_l] next free row of each region (this chunk)
+  int32_t* wcnt = un + E_l;           // [16][E_l] per-wave counts of the current sub-chunk
+  int32_t* rc = un + (1 + PLAN_THREADS / 64) * E_l;   // [PLAN_NR][E_l] per-(rank, expert)
+  const int64_t r0 = (int64_t)b * chunk;
   const int64_t rho0 = (r0 / k) / tokens_per_rank;   // first source rank of the chunk
   for (int e = tid; e < E_l; e += PLAN_THREADS) {
-    base[e] = offsets[e] + blk_base[(int64_t)blockIdx.x * E_l + e];
-    for (int q = 0; q < 4; ++q) wcnt[q * E_l + e] = 0;
+    base[e] = off[e] + pre[e];
+    for (int q = 0; q < PLAN_THREADS / 64; ++q) wcnt[q * E_l + e] = 0;
     for (int q = 0; q < PLAN_NR; ++q) rc[q * E_l + e] = 0;
   }
   __syncthreads();
@@ -181,35 +177,47 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(const int32_t* __
   }
 }
 
-int64_t plan_chunk(int64_t n_routes) {
-  // 512 routes (2 sub-chunks of 256) per workgroup, at most 4096 workgroups
-  int64_t chunk = 512;
-  while ((n_routes + chunk - 1) / chunk > 4096) chunk *= 2;
-  return chunk;
+// Chunks of whole multiples of PLAN_THREADS routes, at most nb_max of them: every scatter
+// workgroup reads all nb * E_l chunk counts, so nb^2 E_l stays below 2^23.
+int64_t plan_chunk(int64_t n_routes, int E_l) {
+  int64_t nb_max = 256;
+  while (nb_max > 1 && nb_max * nb_max * E_l > ((int64_t)1 << 23)) nb_max /= 2;
+  const int64_t per = PLAN_THREADS * nb_max;
+  return PLAN_THREADS * std::max<int64_t>(1, (n_routes + per - 1) / per);
 }
 
-int64_t plan_n_blocks(int64_t n_routes) {
-  const int64_t c = plan_chunk(n_routes);
+int64_t plan_n_blocks(int64_t n_routes, int E_l) {
+  const int64_t c = plan_chunk(n_routes, E_l);
   return n_routes == 0 ? 1 : (n_routes + c - 1) / c;
 }
 
 hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l,
                        int64_t tokens_per_rank, int32_t* counts, int32_t* offsets,
                        int32_t* rank_counts, int32_t* route_ids, int32_t* blk_counts,
-                       int32_t* blk_base, int64_t route_cap, hipStream_t s, hipEvent_t ev0,
-                       hipEvent_t ev1) {
+                       int64_t route_cap, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                       const WlBuild* wb) {
   const int64_t n_routes = n_tok * k;
-  const int64_t chunk = plan_chunk(n_routes);
-  const int64_t nb = plan_n_blocks(n_routes);
-  const size_t sh_count = sizeof(int32_t) * (size_t)E_l;
+  const int64_t chunk = plan_chunk(n_routes, E_l);
+  const int64_t nb = plan_n_blocks(n_routes, E_l);
   const int64_t R = n_tok / tokens_per_rank;
-  launch_k(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS), (uint32_t)sh_count, s, ev0,
-           nullptr, idx, n_routes, chunk, e0, E_l, blk_counts, rank_counts, (int64_t)E_l * R);
-  launch_k(k_plan_scan, dim3(1), dim3(1024), 0, s, nullptr, nullptr, blk_counts, (int)nb, E_l,
-           blk_base, counts, offsets);
-  launch_k(k_plan_scatter, dim3((unsigned)nb), dim3(PLAN_THREADS),
-           (uint32_t)(sh_count * (5 + PLAN_NR)), s, nullptr, ev1, idx, n_routes, chunk, e0, E_l,
-           blk_base, offsets, route_ids, rank_counts, k, tokens_per_rank, R, route_cap);
+  WlBuild none = {};
+  const WlBuild& w = wb ? *wb : none;
+  const bool build = w.wl != nullptr;
+  const int un = std::max(plan_scatter_ints(E_l), build ? WL_LDS_INTS : 0);
+  const size_t sh_scatter = sizeof(int32_t) * (size_t)(plan_sums_ints(E_l) + std::max(un, 160));
+  // the scatter's LDS passes 64 KiB for large E_l or with the work-list workgroup
+  static std::once_flag lds_once;
+  std::call_once(lds_once, [] {
+    (void)hipFuncSetAttribute((const void*)k_plan_scatter,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+  });
+  launch_k(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS), (uint32_t)(sizeof(int32_t) * E_l),
+           s, ev0, nullptr, idx, n_routes, chunk, e0, E_l, blk_counts, rank_counts,
+           (int64_t)E_l * R);
+  launch_k(k_plan_scatter, dim3((unsigned)(nb + (build ? 1 : 0))), dim3(PLAN_THREADS),
+           (uint32_t)sh_scatter, s, nullptr, ev1, idx, n_routes, chunk, (int)nb, e0, E_l,
+           blk_counts, counts, offsets, route_ids, rank_counts, k, tokens_per_rank, R, route_cap,
+           w);
   return hipGetLastError();
 }
 

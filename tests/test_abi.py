@@ -113,6 +113,16 @@ def test_entry_points_reject_before_launch(mok):
     assert mok.mok_dispatch_plan_workspace_bytes(12, 2, 4) > 0
 
 
+def test_plan_scratch_fits_the_fixed_no_alloc_array(mok):
+    """The plan's scratch (its chunk histograms) is bounded for every valid argument set, so
+    mok_dispatch_plan_noalloc's fixed 256 KiB array always holds it."""
+    limit = 1 << 18
+    for E_l in (1, 4, 8, 64, 100, 256, 257, 512, 1000, 1024):
+        for T, k in ((1, 1), (64, 2), (8192, 6), (262144, 8), (1 << 20, 8), ((1 << 31) // 64 - 1, 64)):
+            assert mok.mok_dispatch_plan_workspace_bytes(T, k, E_l) <= limit, (T, k, E_l)
+    assert mok.mok_dispatch_plan_workspace_bytes((1 << 31) // 64 - 1, 64, 1024) > limit // 8
+
+
 def test_product_path_never_imports_the_oracle():
     pkg = os.path.join(ROOT, "routing_grouped_expert_gemm_amd")
     for dirpath, _, files in os.walk(pkg):

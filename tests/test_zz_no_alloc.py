@@ -47,13 +47,3 @@ def test_noalloc_plan_matches_workspace_plan(first, second):
         for key in ref:
             assert np.array_equal(got[key], ref[key]), (i, key)
         assert int(got["offsets"][-1]) > 0
-
-
-def test_noalloc_plan_rejects_requests_beyond_its_scratch():
-    import routing_grouped_expert_gemm_amd as mok
-    L = ctypes.CDLL(mok.LIB_PATH)
-    P = ctypes.c_void_p
-    L.mok_dispatch_plan_noalloc.argtypes = [P, ctypes.c_int64] + [ctypes.c_int32] * 5 + [P] * 5
-    # 2^21 routes -> 4096 chunks; 4096 x 1024 experts x 2 tables exceeds the 2^20-int array
-    rc = L.mok_dispatch_plan_noalloc(16, 1 << 18, 8, 1024, 0, 1024, 1 << 18, 16, 16, 16, 16, None)
-    assert rc == mok.MOK_EWORKSPACE
