@@ -15,16 +15,17 @@
 // combine. Every product is one launch of a grouped GEMM whose groups (one per expert and
 // matrix) are described on the device from the plan's counts: the host never reads a count.
 //
-// Grouped GEMM: C_g (+)= A_g B_g^T over tiles of 128 x 128, K steps of 32, bf16 operands and
-// float32 accumulation on v_mfma_f32_32x32x16_bf16, 4 waves of 64 x 64. An operand is read
-// either K-contiguous (row-major [rows, K]) or "transposed" (row-major [K, rows]: the wgrad
-// operands, whose K is the token dimension, and the weights read along their output
-// dimension); a transposed tile is loaded row-wise (coalesced) and written to LDS transposed,
-// so that the MFMA fragments always come from K-contiguous LDS rows.
+// Grouped GEMM: C_g (+)= A_g B_g^T over tiles of 256 x 256, K steps of 64, bf16 operands and
+// float32 accumulation on v_mfma_f32_32x32x16_bf16, 4 waves of 128 x 128, operands moved to
+// LDS by LDS-DMA. An operand is read either K-contiguous (row-major [rows, K]) or "transposed"
+// (row-major [K, rows]: the wgrad operands, whose K is the token dimension, and the weights
+// read along their output dimension); a transposed tile is kept in LDS as it lies in memory and
+// gfx950's transposing LDS read turns it into the MFMA's K-contiguous fragments.
 #include <algorithm>
 
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 #include "mok.h"
 
 namespace mok {
@@ -43,79 +44,84 @@ MOK_HOSTDEV inline size_t gtable_bytes(int n_groups) {
 }
 MOK_DEV GGroup* gtable_groups(int32_t* t) { return (GGroup*)(t + GT_HDR * 4); }
 
-constexpr int GB_M = 128, GB_N = 128, GB_K = 64, GB_LDS = GB_K + 8;   // LDS row: 144 bytes
-constexpr int GB_KC = GB_K / 8;                 // 16-byte chunks of a tile row per K step
-constexpr int GB_TT = GB_KC * (GB_M / 8);       // 8 x 8 blocks of a transposed tile = its loaders
+constexpr int GB_M = 256, GB_N = 256, GB_K = 64;   // tile rows, tile columns, K step
+constexpr int GB_NT = 256;                           // threads: 4 waves of 128 x 128
+constexpr int GB_TILE = GB_M * GB_K * 2;             // bytes of one operand tile per K step
+constexpr int GB_DMA = GB_TILE / 1024 / 4;           // LDS-DMA instructions per wave and operand
 
-// One K step of one operand tile (GB_M rows x GB_K) into registers, and from registers into
-// LDS as K-contiguous rows.
-//  K-contiguous operand: every thread, 4 x 16 bytes (chunk c = row * 8 + kc).
-//  Transposed operand ([K, rows] row-major): the tile is 8 x 16 blocks of 8 k x 8 rows; thread
-//  b < 128 of the operand's two waves loads block b as 8 row-wise 16-byte loads (16 lanes cover
-//  256 contiguous bytes of one k row), transposes it in registers and writes 8 LDS rows of 8 k.
-struct Frag { uint4 v[8]; };
+// One operand tile of a K step in LDS (32 KB), filled by LDS-DMA (every lane 16 bytes, an
+// instruction 1 KB). Two layouts:
+//  K-contiguous operand (row-major [rows, K]): 256 rows x 128 bytes; 16-byte chunk c of row r
+//    at slot c ^ ((r >> 1) & 7) (as in the forward's tiles), read by ds_read_b128: lane (h, l32)
+//    takes chunk 2 s + h of its row, the 8 K values of sub-step s.
+//  Transposed operand (row-major [K, rows], e.g. a weight read along its output dimension, or
+//    activations whose K is the token dimension): 64 k rows x 512 bytes; chunk c of k row kr at
+//    slot c ^ (4 (kr & 3)). gfx950's transposing LDS read (ds_read_b64_tr_b16) turns it into
+//    the same fragments: in each group of 16 lanes, lane p addresses 4 consecutive rows-of-the-
+//    operand (4 (p % 4) further on) at k row kbase + p / 4, and lane i receives operand row
+//    mbase + i at k rows kbase .. kbase + 3; two such reads give a lane its 8 K values. The
+//    swizzle puts the 16 (k row, chunk) pairs a 32-lane half reads on 16 distinct slots, so
+//    the 64 banks serve it in one pass.
 template <bool T>
-MOK_DEV void gg_load(const bf16_t* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
-                     Frag& f, int t) {
-  if constexpr (!T) {
-#pragma unroll
-    for (int q = 0; q < GB_M * GB_KC / 256; ++q) {
-      const int c = t + 256 * q;
-      const int row = c / GB_KC, kc = c % GB_KC;
-      f.v[q] = make_uint4(0, 0, 0, 0);
-      if (r0 + row < rows && k0 + kc * 8 < K)
-        f.v[q] = *(const uint4*)(P + (int64_t)(r0 + row) * ld + k0 + kc * 8);
-    }
-  } else {
-    if (t >= GB_TT) return;
-    const int kg = t >> 4, rg = t & 15;
-    const bool rok = r0 + rg * 8 < rows;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = k0 + kg * 8 + i;
-      f.v[i] = make_uint4(0, 0, 0, 0);
-      if (rok && k < K) f.v[i] = *(const uint4*)(P + (int64_t)k * ld + r0 + rg * 8);
+struct GOperand {
+  // this lane's byte offset, from the tile's uniform base, of DMA instruction q of wave w
+  // (K-contiguous: relative to row m0 at K offset k0; transposed: to k row k0, column 0)
+  MOK_DEV static uint32_t dma_off(int w, int q, int lane, int64_t ld, int m0, int rows,
+                                  int kk_max) {
+    if constexpr (!T) {
+      const int r = 64 * w + 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int rr = min(m0 + r, rows - 1) - m0;       // rows past the operand: clamped
+      return (uint32_t)(((int64_t)rr * ld + 8 * c) * 2);
+    } else {
+      const int kr = 16 * w + 2 * q + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (kr & 3));
+      const int m = min(m0 + 8 * c, rows - 8);         // columns past the operand: clamped
+      const int kk = min(kr, kk_max);                  // k rows past K: clamped (masked later)
+      return (uint32_t)(((int64_t)kk * ld + m) * 2);
     }
   }
-}
-
-template <bool T>
-MOK_DEV void gg_store(bf16_t (*S)[GB_LDS], const Frag& f, int t) {
-  if constexpr (!T) {
+  // the 8 bf16 of K sub-step s for operand row blk + l32 (blk: the 32-row block, tile-relative)
+  MOK_DEV static bf16x8_t frag(const char* tile, int blk, int s, int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    if constexpr (!T) {
+      const int r = blk + l32;
+      const int c = (2 * s + h) ^ ((r >> 1) & 7);
+      return *(const bf16x8_t*)(tile + r * 128 + c * 16);
+    } else {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4;
+      const int g = lane >> 4, p = lane & 15;
+      const int m = blk + 16 * (g & 1) + 4 * (p & 3);
+      v4i16 v[2];
 #pragma unroll
-    for (int q = 0; q < GB_M * GB_KC / 256; ++q) {
-      const int c = t + 256 * q;
-      *(uint4*)&S[c / GB_KC][(c % GB_KC) * 8] = f.v[q];
-    }
-  } else {
-    if (t >= GB_TT) return;
-    const int kg = t >> 4, rg = t & 15;
-    // f.v[i] holds rows rg*8 + [0, 8) at k = kg*8 + i; LDS row rg*8 + j takes k = kg*8 + [0, 8)
-    const uint32_t* w = (const uint32_t*)f.v;          // w[4 i + j / 2]: (row j, k i) half j & 1
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t a = w[4 * (2 * q) + j / 2], b = w[4 * (2 * q + 1) + j / 2];
-        o[q] = (j & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kr = 16 * s + 8 * (g >> 1) + 4 * kb + (p >> 2);
+        const int off = kr * 512 + (((m >> 3) ^ (4 * (kr & 3))) << 4) + (m & 7) * 2;
+        v[kb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4*)(uintptr_t)(lds_addr(tile) + off));
       }
-      *(uint4*)&S[rg * 8 + j][kg * 8] = make_uint4(o[0], o[1], o[2], o[3]);
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
-}
+};
 
 // C_g (+)= A_g B_g^T for every group of the table; TA / TB: operand stored transposed.
+// 256 x 256 tiles, 4 waves of 128 x 128 (4 x 4 accumulator blocks of 32 x 32: every LDS
+// fragment feeds four MFMAs). K steps of 64 in two LDS buffers filled by LDS-DMA: the DMA of
+// step kt + 1 is issued once every wave is past step kt - 1 and lands under the MFMAs of kt.
+// A ragged K (the wgrad products: K is an expert's rows) clamps the DMA rows and zeroes the
+// fragments' K values past the end in the last step.
 template <bool TA, bool TB>
-__global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table, bool acc_c) {
-  __shared__ bf16_t As[2][GB_M][GB_LDS], Bs[2][GB_N][GB_LDS];
+__global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ table, bool acc_c) {
+  __shared__ uint4 lds_a[2][GB_TILE / 16], lds_b[2][GB_TILE / 16];
   __shared__ int g_sh;
   const int n_groups = table[0], total = table[1];
   // Tile map: workgroup w runs on XCD w % 8. In each window of 256 consecutive workgroups (which
   // run at about the same time) XCD x takes 32 consecutive tiles, so tiles that share an operand
   // tile share an L2, while the 8 XCDs still work on neighbouring tiles (one expert's operands,
   // which the last-level cache then serves to all of them).
-  const int w = blockIdx.x, win = w & ~255, in = w & 255;
+  const int wgi = blockIdx.x, win = wgi & ~255, in = wgi & 255;
   const int b = win + (in & 7) * 32 + (in >> 3);
   if (b >= total) return;
   const GGroup* G = gtable_groups(const_cast<int32_t*>(table));
@@ -128,71 +134,91 @@ __global__ __launch_bounds__(256) void k_ggemm(const int32_t* __restrict__ table
     g_sh = lo;
   }
   __syncthreads();
-  const GGroup g = G[g_sh];
+  const GGroup g = G[uniform(g_sh)];
   const int tiles_n = (g.N + GB_N - 1) / GB_N;
   const int local = b - g.tile0;
   const int m0 = (local / tiles_n) * GB_M, n0 = (local % tiles_n) * GB_N;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1, h = lane >> 5, l32 = lane & 31;
-  f32x16_t acc[2][2];
+  const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1, h = lane >> 5;
+  constexpr int FM = 4, FN = 4;
+  f32x16_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int nk = (g.K + GB_K - 1) / GB_K;
-  // a transposed operand is loaded by two waves: A by waves 0-1, B by waves 2-3 (or 0-1 when A
-  // is K-contiguous)
-  const int ta = threadIdx.x, tb = TB && !TA ? threadIdx.x : (int)threadIdx.x - (TB ? GB_TT : 0);
-  Frag ra, rb;
-  if (nk > 0) {
-    gg_load<TA>(g.A, g.lda, g.M, g.K, m0, 0, ra, ta);
-    gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, 0, rb, tb < 0 ? GB_TT : tb);
-    gg_store<TA>(As[0], ra, ta);
-    gg_store<TB>(Bs[0], rb, tb < 0 ? GB_TT : tb);
-  }
-  __syncthreads();
+  // uniform base of an operand's tile at K step kt
+  auto base = [&](const bf16_t* P, int64_t ld, int r0, bool T, int kt) {
+    const int64_t k0 = (int64_t)kt * GB_K;
+    return uniform_ptr(T ? P + k0 * ld : P + (int64_t)r0 * ld + k0);
+  };
+  auto issue = [&](int kt, int buf) {
+    const int kk_max = g.K - 1 - kt * GB_K;          // last valid k row of the step
+    const bf16_t* pa = base(g.A, g.lda, m0, TA, kt);
+    const bf16_t* pb = base(g.B, g.ldb, n0, TB, kt);
+    const uint32_t la = uniform(lds_addr(&lds_a[buf][0])) + wid * GB_DMA * 1024;
+    const uint32_t lb = uniform(lds_addr(&lds_b[buf][0])) + wid * GB_DMA * 1024;
+#pragma unroll
+    for (int q = 0; q < GB_DMA; ++q) {
+      dma_b128(pa, GOperand<TA>::dma_off(wid, q, lane, g.lda, m0, g.M, kk_max), la + 1024 * q);
+      dma_b128(pb, GOperand<TB>::dma_off(wid, q, lane, g.ldb, n0, g.N, kk_max), lb + 1024 * q);
+    }
+  };
+  if (nk > 0) issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) {                          // next step's loads in flight over the MFMAs
-      gg_load<TA>(g.A, g.lda, g.M, g.K, m0, (kt + 1) * GB_K, ra, ta);
-      gg_load<TB>(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * GB_K, rb, tb < 0 ? GB_TT : tb);
-    }
+    wait_vmcnt<0>();                            // this wave's DMA of step kt has landed
+    lds_barrier();                              // ... every wave's, and step kt - 1 is done
+    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+    const char* ta = (const char*)&lds_a[cur][0];
+    const char* tb = (const char*)&lds_b[cur][0];
+    const int k_left = g.K - kt * GB_K;          // < GB_K only in a ragged last step
+    bf16x8_t fa[2][FM], fb[2][FN];
+    auto frags = [&](int s, int f) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[f][i] = GOperand<TA>::frag(ta, wm * 128 + 32 * i, s, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[f][j] = GOperand<TB>::frag(tb, wn * 128 + 32 * j, s, lane);
+      if (k_left < GB_K) {                       // zero K values past the end (both operands)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (16 * s + 8 * h + q >= k_left) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[f][i][q] = (__bf16)0.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[f][j][q] = (__bf16)0.0f;
+          }
+        }
+      }
+    };
+    frags(0, 0);
 #pragma unroll
     for (int s = 0; s < GB_K / 16; ++s) {
-      bf16x8_t fa[2], fb[2];
+      if (s + 1 < GB_K / 16) frags(s + 1, (s + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *(const bf16x8_t*)&As[cur][wm * 64 + 32 * i + l32][16 * s + 8 * h];
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *(const bf16x8_t*)&Bs[cur][wn * 64 + 32 * j + l32][16 * s + 8 * h];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[s & 1][i],
+                                                               acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      gg_store<TA>(As[cur ^ 1], ra, ta);
-      gg_store<TB>(Bs[cur ^ 1], rb, tb < 0 ? GB_TT : tb);
-    }
-    __syncthreads();
   }
-  // lane (h, l32) of block (i, j): row m0 + wm*64 + 32 i + l32, columns n0 + wn*64 + 32 j + 8 g
-  // + 4 h + [0, 4) in values 4g .. 4g + 3 (the B fragment is the MFMA's first operand)
+  // lane (h, l32) of block (i, j): row m0 + wm*128 + 32 i + l32, columns n0 + wn*128 + 32 j +
+  // 8 q + 4 h + [0, 4) in values 4q .. 4q + 3 (the B fragment is the MFMA's first operand)
   typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const int l32 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wm * 64 + 32 * i + l32;
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * 128 + 32 * i + l32;
     if (m >= g.M) continue;
     float* crow = g.C + (int64_t)m * g.ldc;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 64 + 32 * j + 8 * q + 4 * h;
+        const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * h;
         if (n >= g.N) continue;
         f32x4v o;
 #pragma unroll
@@ -230,14 +256,23 @@ MOK_DEV void put(GGroup* G, int& n, int32_t& tiles, const bf16_t* A, int64_t lda
 }
 MOK_DEV void close_table(int32_t* t, int n, int32_t tiles) { t[0] = n; t[1] = tiles; }
 
-// One thread writes every table from the plan's counts (a few hundred groups at most).
-__global__ void k_bwd_describe(BwdPass p) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// One thread writes every table from the plan's counts (a few hundred groups at most), after
+// the workgroup has copied the counts and offsets to LDS: the serial walk then waits on no
+// global load.
+constexpr int BD_THREADS = 1024;
+__global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
+  __shared__ int32_t s_cnt[1024], s_off[1025];
   const int E = p.E_l, d = p.d, I = p.I, Ish = p.n_s * p.I_s;
-  const bool over = (int64_t)p.offsets[E] > p.cap;
+  for (int e = threadIdx.x; e <= E; e += BD_THREADS) {
+    if (e < E) s_cnt[e] = p.counts[e];
+    s_off[e] = p.offsets[e];
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const bool over = (int64_t)s_off[E] > p.cap;
   *p.err = over ? (int32_t)MOK_DEVERR_OVERFLOW : 0;
-  auto cnt = [&](int e) { return over ? 0 : p.counts[e]; };
-  auto off = [&](int e) { return (int64_t)p.offsets[e]; };
+  auto cnt = [&](int e) { return over ? 0 : s_cnt[e]; };
+  auto off = [&](int e) { return (int64_t)s_off[e]; };
   // recompute: G = A Wg^T, U = A Wu^T (K-contiguous operands)
   {
     GGroup* G = gtable_groups(p.t_rec);
@@ -313,7 +348,8 @@ __global__ void k_bwd_describe(BwdPass p) {
 }
 
 // SwiGLU backward of one row per workgroup: routed rows [0, N) of the plan, then the own
-// rows. The routing-weight gradient is a fixed-order reduction (per-thread strided sums, then a
+// rows. Four values a thread per pass (16-byte loads of G, U, D; 8-byte stores of dG, dU, H).
+// The routing-weight gradient is a fixed-order reduction (per-thread strided sums, then a
 // tree), so it is the same on every run.
 __global__ __launch_bounds__(256) void k_bwd_swiglu(BwdPass p) {
   __shared__ float red[256];
@@ -333,22 +369,42 @@ __global__ __launch_bounds__(256) void k_bwd_swiglu(BwdPass p) {
   bf16_t* H = (own ? p.Ho : p.Hr) + r * I;
   const float w = own ? 1.0f : p.topk_w[p.route_ids[r]];
   float dw = 0.0f;
-  for (int n = threadIdx.x; n < I; n += 256) {
-    const float g = G[n], u = U[n], dd = D[n];
-    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-    const float sl = g * sg;
-    const float hv = sl * u;
-    dw += dd * hv;
-    const float dh = w * dd;
-    dG[n] = f32_to_bf16(dh * u * sg * (1.0f + g * (1.0f - sg)));
-    dU[n] = f32_to_bf16(dh * sl);
-    H[n] = f32_to_bf16(hv);
+  for (int n = 4 * threadIdx.x; n < I; n += 4 * 256) {   // I is a multiple of 64
+    const float4 g4 = *(const float4*)(G + n), u4 = *(const float4*)(U + n);
+    const float4 d4 = *(const float4*)(D + n);
+    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+    float og[4], ou[4], oh[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float g = gv[q], u = uv[q], dd = dv[q];
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+      const float sl = g * sg;
+      const float hv = sl * u;
+      dw += dd * hv;
+      const float dh = w * dd;
+      og[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
+      ou[q] = dh * sl;
+      oh[q] = hv;
+    }
+    *(uint2*)(dG + n) = make_uint2(pack_bf16x2(og[0], og[1]), pack_bf16x2(og[2], og[3]));
+    *(uint2*)(dU + n) = make_uint2(pack_bf16x2(ou[0], ou[1]), pack_bf16x2(ou[2], ou[3]));
+    *(uint2*)(H + n) = make_uint2(pack_bf16x2(oh[0], oh[1]), pack_bf16x2(oh[2], oh[3]));
   }
   if (!own) {
-    // dO = w dP for the down-projection weight gradient
+    // dO = w dP for the down-projection weight gradient, 8 values a thread per pass
     const bf16_t* dP = p.dPr + r * p.d;
     bf16_t* dO = p.dOr + r * p.d;
-    for (int m = threadIdx.x; m < p.d; m += 256) dO[m] = f32_to_bf16(w * bf16_to_f32(dP[m]));
+    for (int m = 8 * threadIdx.x; m < p.d; m += 8 * 256) {
+      const uint4 v = *(const uint4*)(dP + m);
+      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_bf16x2(w * __uint_as_float(in[q] << 16),
+                           w * __uint_as_float(in[q] & 0xFFFF0000u));
+      *(uint4*)(dO + m) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
     red[threadIdx.x] = dw;
     __syncthreads();
 #pragma unroll
@@ -361,7 +417,14 @@ __global__ __launch_bounds__(256) void k_bwd_swiglu(BwdPass p) {
 }
 
 // dx through each local route to its source-indexed slot (bf16), the routing-weight gradient
-// to [t, j], and the shared experts' dx. One workgroup per row.
+// to [t, j], and the shared experts' dx. One workgroup per row, 8 values a thread per pass.
+MOK_DEV void f32_row_to_bf16(const float* __restrict__ src, bf16_t* __restrict__ dst, int d) {
+  for (int m = 8 * threadIdx.x; m < d; m += 8 * 256) {     // d is a multiple of 128
+    const float4 a = *(const float4*)(src + m), b = *(const float4*)(src + m + 4);
+    *(uint4*)(dst + m) = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                    pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+  }
+}
 __global__ __launch_bounds__(256) void k_bwd_scatter(BwdPass p, bf16_t* __restrict__ dx_slots,
                                                      bf16_t* __restrict__ dx_shared,
                                                      float* __restrict__ dtopk_w) {
@@ -371,15 +434,12 @@ __global__ __launch_bounds__(256) void k_bwd_scatter(BwdPass p, bf16_t* __restri
   if (row < p.cap) {
     if (row >= N) return;
     const int32_t rid = p.route_ids[row];
-    const float* src = p.dAr + row * p.d;
-    bf16_t* dst = dx_slots + (int64_t)rid * p.d;
-    for (int m = threadIdx.x; m < p.d; m += 256) dst[m] = f32_to_bf16(src[m]);
+    f32_row_to_bf16(p.dAr + row * p.d, dx_slots + (int64_t)rid * p.d, p.d);
     if (threadIdx.x == 0 && dtopk_w) dtopk_w[rid] = p.dw_rows[row];
   } else {
     const int64_t r = row - p.cap;
     if (r >= p.T_own || !dx_shared) return;
-    const float* src = p.dAo + r * p.d;
-    for (int m = threadIdx.x; m < p.d; m += 256) dx_shared[r * p.d + m] = f32_to_bf16(src[m]);
+    f32_row_to_bf16(p.dAo + r * p.d, dx_shared + r * p.d, p.d);
   }
 }
 
@@ -517,7 +577,7 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
                   (int32_t*)p.counts, (int32_t*)p.offsets, nullptr, (int32_t*)p.route_ids,
                   (int32_t*)at(L.blk_counts), std::max<int64_t>(1, worst), s) != hipSuccess)
     return MOK_EHIP;
-  launch_k(k_bwd_describe, dim3(1), dim3(64), 0, s, nullptr, nullptr, p);
+  launch_k(k_bwd_describe, dim3(1), dim3(BD_THREADS), 0, s, nullptr, nullptr, p);
   // routed x rows and their slot gradients, gathered in plan order (rows past the capacity
   // are not gathered; the description then runs no tile)
   if (a->T_pool > 0) {
@@ -531,7 +591,7 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   }
   auto gg = [&](int32_t* table, int64_t tiles, bool ta, bool tb, bool accum) {
     if (tiles <= 0) return;
-    const dim3 grid((unsigned)((tiles + 255) / 256 * 256)), block(256);
+    const dim3 grid((unsigned)((tiles + 255) / 256 * 256)), block(GB_NT);
     if (!ta && !tb) launch_k(k_ggemm<false, false>, grid, block, 0, s, nullptr, nullptr, table, accum);
     else if (!ta && tb) launch_k(k_ggemm<false, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
     else launch_k(k_ggemm<true, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
