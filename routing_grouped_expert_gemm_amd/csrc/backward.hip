@@ -154,56 +154,84 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
     const int64_t k0 = (int64_t)kt * GB_K;
     return uniform_ptr(T ? P + k0 * ld : P + (int64_t)r0 * ld + k0);
   };
-  auto issue = [&](int kt, int buf) {
+  // DMA instruction q (A: q < GB_DMA, B: the rest) of K step kt into buffer buf
+  auto issue_q = [&](int kt, int buf, int q) {
+    __builtin_amdgcn_sched_barrier(0);
     const int kk_max = g.K - 1 - kt * GB_K;          // last valid k row of the step
-    const bf16_t* pa = base(g.A, g.lda, m0, TA, kt);
-    const bf16_t* pb = base(g.B, g.ldb, n0, TB, kt);
-    const uint32_t la = uniform(lds_addr(&lds_a[buf][0])) + wid * GB_DMA * 1024;
-    const uint32_t lb = uniform(lds_addr(&lds_b[buf][0])) + wid * GB_DMA * 1024;
-#pragma unroll
-    for (int q = 0; q < GB_DMA; ++q) {
-      dma_b128(pa, GOperand<TA>::dma_off(wid, q, lane, g.lda, m0, g.M, kk_max), la + 1024 * q);
-      dma_b128(pb, GOperand<TB>::dma_off(wid, q, lane, g.ldb, n0, g.N, kk_max), lb + 1024 * q);
+    if (q < GB_DMA) {
+      const uint32_t la = uniform(lds_addr(&lds_a[buf][0])) + (wid * GB_DMA + q) * 1024;
+      dma_b128(base(g.A, g.lda, m0, TA, kt),
+               GOperand<TA>::dma_off(wid, q, lane, g.lda, m0, g.M, kk_max), la);
+    } else {
+      const int r = q - GB_DMA;
+      const uint32_t lb = uniform(lds_addr(&lds_b[buf][0])) + (wid * GB_DMA + r) * 1024;
+      dma_b128(base(g.B, g.ldb, n0, TB, kt),
+               GOperand<TB>::dma_off(wid, r, lane, g.ldb, n0, g.N, kk_max), lb);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  if (nk > 0) issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    wait_vmcnt<0>();                            // this wave's DMA of step kt has landed
-    lds_barrier();                              // ... every wave's, and step kt - 1 is done
-    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
-    const char* ta = (const char*)&lds_a[cur][0];
-    const char* tb = (const char*)&lds_b[cur][0];
-    const int k_left = g.K - kt * GB_K;          // < GB_K only in a ragged last step
-    bf16x8_t fa[2][FM], fb[2][FN];
-    auto frags = [&](int s, int f) {
+  // every wave's DMA issued so far has landed and every wave's LDS reads are back
+  auto barrier_x = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0) (gfx9 encoding, expcnt left at 7)
+    lds_barrier();
+  };
+  bf16x8_t fa[2][FM], fb[2][FN];
+  // fragments of K sub-step s of step kt into slot f; K values past a ragged end zeroed
+  auto frags = [&](int kt, int s, int f) {
+    const char* ta = (const char*)&lds_a[kt & 1][0];
+    const char* tb = (const char*)&lds_b[kt & 1][0];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[f][i] = GOperand<TA>::frag(ta, wm * 128 + 32 * i, s, lane);
+    for (int i = 0; i < FM; ++i) fa[f][i] = GOperand<TA>::frag(ta, wm * 128 + 32 * i, s, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[f][j] = GOperand<TB>::frag(tb, wn * 128 + 32 * j, s, lane);
-      if (k_left < GB_K) {                       // zero K values past the end (both operands)
+    for (int j = 0; j < FN; ++j) fb[f][j] = GOperand<TB>::frag(tb, wn * 128 + 32 * j, s, lane);
+    const int k_left = g.K - kt * GB_K;
+    if (k_left < GB_K) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (16 * s + 8 * h + q >= k_left) {
+      for (int q = 0; q < 8; ++q) {
+        if (16 * s + 8 * h + q >= k_left) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[f][i][q] = (__bf16)0.0f;
+          for (int i = 0; i < FM; ++i) fa[f][i][q] = (__bf16)0.0f;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) fb[f][j][q] = (__bf16)0.0f;
-          }
+          for (int j = 0; j < FN; ++j) fb[f][j][q] = (__bf16)0.0f;
         }
       }
-    };
-    frags(0, 0);
-#pragma unroll
-    for (int s = 0; s < GB_K / 16; ++s) {
-      if (s + 1 < GB_K / 16) frags(s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[s & 1][i],
-                                                               acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the 16 MFMAs of the fragments in slot f; after(n) follows MFMA n
+  auto mfmas = [&](int f, auto&& after) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
+        after(i * FN + j);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  static_assert(2 * GB_DMA == FM * FN && GB_K / 16 == 4, "one DMA per MFMA of the last sub-step");
+  // K loop. Step kt: sub-steps 0-2 (each reading the next sub-step's fragments first), then
+  // barrier X(kt + 1) (step kt + 1 has landed; every wave has its reads of step kt back), the
+  // reads of step kt + 1's first sub-step, and sub-step 3 of kt, whose MFMAs are interleaved with
+  // the DMA of step kt + 2 into the buffer kt just released.
+  if (nk > 0)
+    for (int q = 0; q < 2 * GB_DMA; ++q) issue_q(0, 0, q);
+  barrier_x();                                  // X(0)
+  if (nk > 1)
+    for (int q = 0; q < 2 * GB_DMA; ++q) issue_q(1, 1, q);
+  if (nk > 0) frags(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      frags(kt, s + 1, (s + 1) & 1);
+      mfmas(s & 1, [](int) {});
+    }
+    if (kt + 1 < nk) {
+      barrier_x();                              // X(kt + 1)
+      frags(kt + 1, 0, 0);
+    }
+    const bool more2 = kt + 2 < nk;
+    mfmas(1, [&](int n) { if (more2) issue_q(kt + 2, kt & 1, n); });
   }
   // lane (h, l32) of block (i, j): row m0 + wm*128 + 32 i + l32, columns n0 + wn*128 + 32 j +
   // 8 q + 4 h + [0, 4) in values 4q .. 4q + 3 (the B fragment is the MFMA's first operand)

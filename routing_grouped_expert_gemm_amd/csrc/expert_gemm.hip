@@ -1147,24 +1147,65 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     fetch_step(s);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+  // Completion of a GEMM item is published late: at the next item's first K-step barrier, where
+  // every wave has waited for its earlier stores anyway (vmcnt counts in order), so the store
+  // drain overlaps the next item's first loads. pend (wave 0) is the counter of the item run
+  // last and not yet published. A workgroup never waits while it holds an unpublished item:
+  // unless the next item's inputs are already complete (or there is no next item), it drains
+  // its stores and publishes first, so no chain of waits can lead back to it.
+  int32_t* pend = nullptr;
+  auto publish = [&]() {                          // wave 0; every wave's stores are complete
+    if (pend) {
+      if (!affine) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(pend, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pend = nullptr;
+    }
+  };
+  __shared__ int32_t drain_lds;
   for (;;) {
+    // the counters the next item waits on (wave 0)
+    int32_t *c1 = nullptr, *c2 = nullptr;
+    int32_t n1 = 0, n2 = 0;
+    auto wait_deps = [&]() {
+      if (c1) wait_count(c1, n1, &wl[WL_ERR]);
+      if (c2) wait_count(c2, n2, &wl[WL_ERR]);
+      if (!affine) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    };
+    auto complete = [&](const int32_t* c, int32_t n) {
+      return !c || __builtin_amdgcn_readfirstlane(
+                       __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= n;
+    };
     if (wid == 0) {
       int4 e = nitem;
+      bool drain = pend != nullptr;
       if (e.x >= 0) {
         const int m = __builtin_amdgcn_readfirstlane(e.x);
         const int kind = __builtin_amdgcn_readfirstlane(e.y) >> KIND_SHIFT;
         const int pm = __builtin_amdgcn_readfirstlane(nprev);
         if (kind == KIND_D) {
-          wait_count(&done_u[m], us[m + 1] - us[m], &wl[WL_ERR]);
+          c1 = &done_u[m];
+          n1 = us[m + 1] - us[m];
         } else if (kind == KIND_U) {
-          wait_count(&done_g[m], gs[m + 1] - gs[m], &wl[WL_ERR]);
-          if (pm >= 0) wait_count(&done_d[pm], ds[pm + 1] - ds[pm], &wl[WL_ERR]);
+          c1 = &done_g[m];
+          n1 = gs[m + 1] - gs[m];
+          if (pm >= 0) {
+            c2 = &done_d[pm];
+            n2 = ds[pm + 1] - ds[pm];
+          }
         } else if (pm >= 0) {
-          wait_count(&done_u[pm], us[pm + 1] - us[pm], &wl[WL_ERR]);
+          c1 = &done_u[pm];
+          n1 = us[pm + 1] - us[pm];
         }
-        if (!affine) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (!pend) {
+          wait_deps();
+        } else {
+          // a gather item publishes in line: drain for it too
+          drain = kind == KIND_G || !complete(c1, n1) || !complete(c2, n2);
+          if (!drain && !affine) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
       }
       item = e;                                   // every lane of wave 0 stores the same value
+      drain_lds = drain ? 1 : 0;
     }
     __syncthreads();
     int4 e;
@@ -1172,6 +1213,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     e.y = __builtin_amdgcn_readfirstlane(item.y);
     e.z = __builtin_amdgcn_readfirstlane(item.z);
     e.w = __builtin_amdgcn_readfirstlane(item.w);
+    if (__builtin_amdgcn_readfirstlane(drain_lds)) {
+      // every wave's stores of the pending item have reached L2; publish, then wait
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (wid == 0) {
+        publish();
+        if (e.x >= 0) wait_deps();
+      }
+      __syncthreads();
+    }
     if (e.x < 0) {
       // queue x is exhausted. Without the split that ends the loop. With it, a queue is served
       // only by the workgroups the hardware placed on its XCD; should an XCD get none (a
@@ -1212,15 +1263,22 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     }
     const int kind = e.y >> KIND_SHIFT;
     e.y &= (1 << KIND_SHIFT) - 1;
+    int32_t* ctr = kind == KIND_U ? done_u : (kind == KIND_D ? done_d : done_g);
+    // after the first K-step barrier of a tile every wave's earlier stores are complete
+    auto hook = [&](int s) {
+      if (s == 0 && wid == 0) publish();
+      fetch_step(s);
+    };
     if (kind == KIND_U) {
       int32_t pre[C::A_SLABS];
       prefetch_a_rows<EL, true, C>(p, e, pre);
       if constexpr (!is_mx<EL>()) route_rows<C>(p, pre);
-      run_tile<EL, true, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre, fetch_step);
+      run_tile<EL, true, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre, hook);
+      if (wid == 0) pend = &ctr[e.x];
     } else if (kind == KIND_D) {
       int32_t pre[C::A_SLABS];
-      run_tile<EL, false, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre,
-                                           fetch_step);
+      run_tile<EL, false, F32OUT, C, true>(p, sm, e, wl_slot(p.wl, p.max_mb)[e.x], pre, hook);
+      if (wid == 0) pend = &ctr[e.x];
     } else {
       if constexpr (is_mx<EL>()) {
         const int r0 = e.y * G_ROWS, r1 = min(e.w & 0xFFFF, r0 + G_ROWS);
@@ -1230,14 +1288,13 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
         fetch_step(s);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-    }
-    // every wave's stores have reached L2; then one publish covers the workgroup's item
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (wid == 0) {
-      if (!affine) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      int32_t* ctr = kind == KIND_U ? done_u : (kind == KIND_D ? done_d : done_g);
-      __hip_atomic_fetch_add(&ctr[e.x], one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // every wave's stores have reached L2; then one publish covers the workgroup's item
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (wid == 0) {
+        pend = &ctr[e.x];
+        publish();
+      }
     }
   }
 }
