@@ -61,6 +61,8 @@ HBM_PEAK = 8.0e12
 # sources whose machine code the counter passes describe
 KERNEL_SOURCES = ["routing_grouped_expert_gemm_amd/csrc/expert_gemm.hip",
                   "routing_grouped_expert_gemm_amd/csrc/device_common.h",
+                  "routing_grouped_expert_gemm_amd/csrc/lds_dma.h",
+                  "routing_grouped_expert_gemm_amd/csrc/worklist.h",
                   "routing_grouped_expert_gemm_amd/csrc/launch.h",
                   "routing_grouped_expert_gemm_amd/_build.py"]
 ELEM = {"f32": 0, "bf16": 1, "mxfp8": 2, "mxfp4": 3}
@@ -148,7 +150,8 @@ def _csv(path):
 
 
 def _per_forward(rows, key_of, value_of):
-    """Per-kernel totals over a run divided by its forwards (one k_plan_scan per forward)."""
+    """Per-kernel totals over a run divided by its forwards (or backwards): one k_plan_count
+    each."""
     tot, n = {}, {}
     for r in rows:
         k = key_of(r)
@@ -156,7 +159,7 @@ def _per_forward(rows, key_of, value_of):
             continue
         tot[k] = tot.get(k, 0.0) + value_of(r)
         n[k] = n.get(k, 0) + 1
-    fwd = n.get("k_plan_scan", 1)
+    fwd = n.get("k_plan_count", 1)
     return {k: v / fwd for k, v in tot.items()}, {k: v / fwd for k, v in n.items()}
 
 
@@ -173,6 +176,8 @@ def summarize(d: str) -> list:
     line = json.loads(open(os.path.join(d, "trace.json")).read().strip().splitlines()[-1])
     if line.get("mode") == "dispatch":
         return [summarize_dispatch(d, line)]
+    if line.get("mode") == "backward":
+        return [summarize_backward(d, line)]
     wl_name = line["config"]["workload"]
     wl = synth.WORKLOADS[wl_name]
     n_routes = line["routed_rows"]
@@ -334,6 +339,66 @@ def summarize(d: str) -> list:
             fh.write("\n".join(lines) + "\n")
         written.append(path)
     return written
+
+
+def summarize_backward(d: str, line: dict) -> str:
+    """profiles/kernels_backward_<wl>.txt: every kernel of one mok_moe_backward (per backward:
+    the run's totals over its k_bwd_describe launches), the grouped GEMMs against the bf16 peak."""
+    import synth
+    wl = synth.WORKLOADS[line["workload"]]
+    n = line["routed_rows"]
+    I_sh = wl.n_shared * wl.I_shared
+    per_row = lambda c: c * wl.d * wl.I * n + c * wl.d * I_sh * wl.T_own
+    gemm = {"k_ggemm<false, false>": ("recompute G, U", per_row(4.0)),
+            "k_ggemm<false, true>": ("dgrad: D = dP Wd; dA = dG Wg + dU Wu", per_row(6.0)),
+            "k_ggemm<true, true>": ("wgrad: dWg, dWu, dWd (ragged K)", per_row(6.0))}
+    trace = _csv(os.path.join(d, "trace", "trace_kernel_trace.csv"))
+    key = lambda r: kernel_key(r["Kernel_Name"])
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6   # ms
+    tot, cnt = {}, {}
+    for r in trace:
+        k = key(r)
+        if k is not None:
+            tot[k] = tot.get(k, 0.0) + dur(r)
+            cnt[k] = cnt.get(k, 0) + 1
+    n_bwd = cnt.get("k_bwd_describe", 1)             # one per backward
+    t_b = {k: v / n_bwd for k, v in tot.items()}
+    calls = {k: v / n_bwd for k, v in cnt.items()}
+    D = "gpurun_out/prof_backward"
+    lines = [f"# every libmok kernel of one mok_moe_backward, workload {wl.name} (bf16), per backward",
+             "#", "# commands (from the repository root):",
+             f"#   rocprofv3 --kernel-trace --stats -d {D}/trace -o trace --output-format csv -- "
+             f"python3 bench.py --backward --steps 10 --warmup 3 > {D}/trace.json",
+             f"#   python3 bench.py --summarize {D}",
+             "#",
+             "# time: kernel durations from the trace, summed per backward over the run (the bench's",
+             "#   forward, run once to get the routing, is listed apart); grouped GEMMs: algorithmic",
+             "#   FLOPs (16 d I per routed row, 16 d I_s n_s per own token in all) / time against",
+             "#   the 2.5 PFLOP/s dense bf16 peak.",
+             "",
+             f"{'kernel':<40} {'calls':>5} {'time_us':>9} {'TFLOP/s':>9} {'of_peak':>8}  product"]
+    total = 0.0
+    outside = []
+    for k in sorted(t_b, key=lambda k: -t_b[k]):
+        if calls[k] < 0.5:
+            outside.append(k)
+            continue
+        t = t_b[k]
+        total += t
+        row = f"{k:<40} {calls[k]:>5.1f} {t * 1e3:>9.1f}"
+        if k in gemm:
+            what, f = gemm[k]
+            row += f" {f / (t * 1e-3) / 1e12:>9.1f} {f / (t * 1e-3) / PEAK['bf16']:>8.3f}  {what}"
+        lines.append(row)
+    if outside:
+        lines.append(f"(launched once per run, not per backward: {', '.join(outside)})")
+    lines += ["", f"kernel time per backward: {total:.3f} ms; bench line of the traced run: "
+              f"{line['ms']} ms per backward, {line['achieved_tflops']} TFLOP/s, frac "
+              f"{line['frac']}, routed rows {n}"]
+    path = os.path.join(ROOT, "profiles", f"kernels_backward_{wl.name}.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 def summarize_dispatch(d: str, line: dict) -> str:
@@ -728,6 +793,7 @@ def measure_backward(steps: int, warmup: int, dev="cuda:0") -> dict:
     flop = 16.0 * wl.d * wl.I * n + 16.0 * wl.d * I_sh * wl.T_own
     ach = flop / (t * 1e-3)
     return {"workload": wl.name, "ms": round(t, 4), "tokens_per_s": round(wl.T_pool / (t * 1e-3), 1),
+            "routed_rows": n,
             "gemm_flop": flop, "achieved_tflops": round(ach / 1e12, 2), "peak_tflops": 2500.0,
             "frac": round(ach / PEAK["bf16"], 4),
             "note": "cold-cache HIP-event time of one mok_moe_backward (plan, gathers, 5 grouped "
