@@ -272,7 +272,7 @@ typedef struct mok_moe_bwd_args {
   int32_t dtype;           /* MOK_BF16                                                      */
   int32_t d, E, k, I, e0, E_l, tokens_per_rank;   /* as mok_moe_args (d % 128, I % 64)     */
   int64_t T_pool, own_begin;
-  int32_t T_own, n_shared, I_shared;              /* I_shared % 64                         */
+  int32_t T_own, n_shared, I_shared;              /* n_shared <= 64, I_shared % 64         */
   int64_t route_rows_cap;  /* 0 = worst case                                                */
   /* forward inputs (device) */
   const void* x;           /* [T_pool, d] bf16                                              */

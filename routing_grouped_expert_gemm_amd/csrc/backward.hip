@@ -30,12 +30,22 @@
 
 namespace mok {
 
+// One product of a grouped-GEMM launch. K may come in two segments: A and B for k < kseg,
+// A2 and B2 beyond (kseg = K: one segment). The SwiGLU recompute reads B's rows as gate rows
+// (B) and up rows (B2) instead, and its epilogue takes D, the routing weights (w[rid[row]], or
+// 1 without rid) and writes dG, dU, w H and the per-row routing-weight-gradient partials.
 struct GGroup {
-  const bf16_t* A;
-  const bf16_t* B;
+  const bf16_t *A, *A2, *B, *B2;
   float* C;
   int64_t lda, ldb, ldc;
   int32_t M, N, K, tile0;   // tile0: the group's first flat tile
+  int32_t kseg;
+  int32_t ldp;              // SwiGLU: partials per row
+  const float* D;           // SwiGLU: [M, ldc] float32
+  bf16_t *dG, *dU, *Hw;     // SwiGLU: [M, ldc] bf16
+  float* dwp;               // SwiGLU: [M, ldp] float32, or null
+  const int32_t* rid;       // SwiGLU: route id of each row, or null (weight 1)
+  const float* w;           // SwiGLU: routing weights by route id
 };
 // A group table: header {groups, tiles, error, pad} then the groups.
 constexpr int GT_HDR = 4;
@@ -45,6 +55,7 @@ MOK_HOSTDEV inline size_t gtable_bytes(int n_groups) {
 MOK_DEV GGroup* gtable_groups(int32_t* t) { return (GGroup*)(t + GT_HDR * 4); }
 
 constexpr int GB_M = 256, GB_N = 256, GB_K = 64;   // tile rows, tile columns, K step
+constexpr int GB_MAX_GROUPS = 3 * 1024 + 4 + 64;     // groups of a table (E_l <= 1024, n_s <= 64)
 constexpr int GB_NT = 256;                           // threads: 4 waves of 128 x 128
 constexpr int GB_TILE = GB_M * GB_K * 2;             // bytes of one operand tile per K step
 constexpr int GB_DMA = GB_TILE / 1024 / 4;           // LDS-DMA instructions per wave and operand
@@ -112,148 +123,255 @@ struct GOperand {
 // step kt + 1 is issued once every wave is past step kt - 1 and lands under the MFMAs of kt.
 // A ragged K (the wgrad products: K is an expert's rows) clamps the DMA rows and zeroes the
 // fragments' K values past the end in the last step.
-template <bool TA, bool TB>
-__global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ table, bool acc_c) {
+template <bool TA, bool TB, bool SWIGLU>
+__global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ table) {
+  static_assert(!SWIGLU || (!TA && !TB), "the SwiGLU recompute reads K-contiguous operands");
   __shared__ uint4 lds_a[2][GB_TILE / 16], lds_b[2][GB_TILE / 16];
-  __shared__ int g_sh;
+  __shared__ int g_sh[2];
+  __shared__ int32_t t0[GB_MAX_GROUPS];
   const int n_groups = table[0], total = table[1];
-  // Tile map: workgroup w runs on XCD w % 8. In each window of 256 consecutive workgroups (which
-  // run at about the same time) XCD x takes 32 consecutive tiles, so tiles that share an operand
-  // tile share an L2, while the 8 XCDs still work on neighbouring tiles (one expert's operands,
-  // which the last-level cache then serves to all of them).
-  const int wgi = blockIdx.x, win = wgi & ~255, in = wgi & 255;
-  const int b = win + (in & 7) * 32 + (in >> 3);
+  // Persistent: workgroup w (on XCD w % 8; the grid is a multiple of 256) runs tiles
+  // tile_of(0), tile_of(1), ... In each window of 256 consecutive tile slots XCD x takes 32
+  // consecutive tiles, so tiles that share an operand tile share an L2, while the 8 XCDs still
+  // work on neighbouring tiles (one expert's operands, which the last-level cache then serves
+  // to all of them).
+  auto tile_of = [&](int it) {
+    const int w = blockIdx.x + it * gridDim.x, win = w & ~255, in = w & 255;
+    return win + (in & 7) * 32 + (in >> 3);
+  };
+  int b = tile_of(0);
   if (b >= total) return;
   const GGroup* G = gtable_groups(const_cast<int32_t*>(table));
-  if (threadIdx.x == 0) {
-    int lo = 0, hi = n_groups;                  // G[lo].tile0 <= b < G[hi].tile0
+  // the group of a tile: the groups' first tiles come to LDS once, with one load per thread
+  // (all in flight together); one thread then searches them there for each tile
+  for (int q = threadIdx.x; q < n_groups; q += GB_NT) t0[q] = G[q].tile0;
+  __syncthreads();
+  auto find = [&](int bt) {
+    int lo = 0, hi = n_groups;                  // t0[lo] <= bt < t0[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (G[mid].tile0 <= b) lo = mid; else hi = mid;
+      if (t0[mid] <= bt) lo = mid; else hi = mid;
     }
-    g_sh = lo;
-  }
+    return lo;
+  };
+  if (threadIdx.x == 0) g_sh[0] = find(b);
   __syncthreads();
-  const GGroup g = G[uniform(g_sh)];
-  const int tiles_n = (g.N + GB_N - 1) / GB_N;
-  const int local = b - g.tile0;
-  const int m0 = (local / tiles_n) * GB_M, n0 = (local % tiles_n) * GB_N;
+  GGroup g = G[uniform(g_sh[0])];
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1, h = lane >> 5;
   constexpr int FM = 4, FN = 4;
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  const int nk = (g.K + GB_K - 1) / GB_K;
-  // uniform base of an operand's tile at K step kt
-  auto base = [&](const bf16_t* P, int64_t ld, int r0, bool T, int kt) {
-    const int64_t k0 = (int64_t)kt * GB_K;
-    return uniform_ptr(T ? P + k0 * ld : P + (int64_t)r0 * ld + k0);
+  // a tile's origin and K steps
+  auto origin = [&](const GGroup& gg, int bt, int& m0, int& n0) {
+    const int tiles_n = (gg.N + GB_N - 1) / GB_N, local = bt - gg.tile0;
+    m0 = (local / tiles_n) * GB_M;
+    n0 = (local % tiles_n) * GB_N;
   };
-  // DMA instruction q (A: q < GB_DMA, B: the rest) of K step kt into buffer buf
-  auto issue_q = [&](int kt, int buf, int q) {
+  // uniform base of an operand's tile at K offset kin of its segment
+  auto base = [&](const bf16_t* P, int64_t ld, int r0, bool T, int kin) {
+    return uniform_ptr(T ? P + (int64_t)kin * ld : P + (int64_t)r0 * ld + kin);
+  };
+  // DMA instruction q (A: q < GB_DMA, B: the rest) of K step kt of tile (gg, tm0, tn0) into
+  // buffer buf. SwiGLU recompute: tile column R is a gate row (slab R / 64 even) or an up row
+  // (odd) of output column tn0 / 2 + (R / 128) * 64 + R % 64, so each wave's 128 columns pair
+  // 64 gate columns with the same 64 up columns; wave w loads slab w.
+  auto issue_q = [&](const GGroup& gg, int tm0, int tn0, int kt, int buf, int q) {
     __builtin_amdgcn_sched_barrier(0);
-    const int kk_max = g.K - 1 - kt * GB_K;          // last valid k row of the step
+    const int k0 = kt * GB_K;
+    const bool seg2 = k0 >= gg.kseg;
+    const int kin = seg2 ? k0 - gg.kseg : k0;
+    const int kk_max = (seg2 ? gg.K : gg.kseg) - 1 - k0;   // last valid k row of the step
     if (q < GB_DMA) {
       const uint32_t la = uniform(lds_addr(&lds_a[buf][0])) + (wid * GB_DMA + q) * 1024;
-      dma_b128(base(g.A, g.lda, m0, TA, kt),
-               GOperand<TA>::dma_off(wid, q, lane, g.lda, m0, g.M, kk_max), la);
+      dma_b128(base(seg2 ? gg.A2 : gg.A, gg.lda, tm0, TA, kin),
+               GOperand<TA>::dma_off(wid, q, lane, gg.lda, tm0, gg.M, kk_max), la);
     } else {
       const int r = q - GB_DMA;
+      const int b_r0 = SWIGLU ? tn0 / 2 + (wid >> 1) * 64 - 64 * wid : tn0;
+      const int b_rows = SWIGLU ? gg.N / 2 : gg.N;
       const uint32_t lb = uniform(lds_addr(&lds_b[buf][0])) + (wid * GB_DMA + r) * 1024;
-      dma_b128(base(g.B, g.ldb, n0, TB, kt),
-               GOperand<TB>::dma_off(wid, r, lane, g.ldb, n0, g.N, kk_max), lb);
+      const bf16_t* pb = SWIGLU ? ((wid & 1) ? gg.B2 : gg.B) : (seg2 ? gg.B2 : gg.B);
+      dma_b128(base(pb, gg.ldb, b_r0, TB, kin),
+               GOperand<TB>::dma_off(wid, r, lane, gg.ldb, b_r0, b_rows, kk_max), lb);
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // the first two K steps of a tile, into buffers 0 and 1
+  auto issue_head = [&](const GGroup& gg, int tm0, int tn0) {
+    const int tnk = (gg.K + GB_K - 1) / GB_K;
+    for (int kt = 0; kt < 2 && kt < tnk; ++kt)
+      for (int q = 0; q < 2 * GB_DMA; ++q) issue_q(gg, tm0, tn0, kt, kt, q);
   };
   // every wave's DMA issued so far has landed and every wave's LDS reads are back
   auto barrier_x = [&]() {
     __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0) (gfx9 encoding, expcnt left at 7)
     lds_barrier();
   };
-  bf16x8_t fa[2][FM], fb[2][FN];
-  // fragments of K sub-step s of step kt into slot f; K values past a ragged end zeroed
-  auto frags = [&](int kt, int s, int f) {
-    const char* ta = (const char*)&lds_a[kt & 1][0];
-    const char* tb = (const char*)&lds_b[kt & 1][0];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[f][i] = GOperand<TA>::frag(ta, wm * 128 + 32 * i, s, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[f][j] = GOperand<TB>::frag(tb, wn * 128 + 32 * j, s, lane);
-    const int k_left = g.K - kt * GB_K;
-    if (k_left < GB_K) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (16 * s + 8 * h + q >= k_left) {
-#pragma unroll
-          for (int i = 0; i < FM; ++i) fa[f][i][q] = (__bf16)0.0f;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) fb[f][j][q] = (__bf16)0.0f;
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // the 16 MFMAs of the fragments in slot f; after(n) follows MFMA n
-  auto mfmas = [&](int f, auto&& after) {
+  int m0, n0;
+  origin(g, b, m0, n0);
+  issue_head(g, m0, n0);
+  for (int it = 0;; ++it) {
+    const int bn = tile_of(it + 1);
+    const bool more = bn < total;
+    if (more && tid == 0) g_sh[(it + 1) & 1] = find(bn);   // read after X(0) below
+    const int nk = (g.K + GB_K - 1) / GB_K;
+    f32x16_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
-        after(i * FN + j);
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // SwiGLU: the routing weight of the lane's row in each block row (loaded under the K loop)
+    float wrow[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      wrow[i] = 1.0f;
+      if constexpr (SWIGLU) {
+        const int m = m0 + wm * 128 + 32 * i + (lane & 31);
+        if (g.rid && m < g.M) wrow[i] = g.w[g.rid[m]];
       }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  static_assert(2 * GB_DMA == FM * FN && GB_K / 16 == 4, "one DMA per MFMA of the last sub-step");
-  // K loop. Step kt: sub-steps 0-2 (each reading the next sub-step's fragments first), then
-  // barrier X(kt + 1) (step kt + 1 has landed; every wave has its reads of step kt back), the
-  // reads of step kt + 1's first sub-step, and sub-step 3 of kt, whose MFMAs are interleaved with
-  // the DMA of step kt + 2 into the buffer kt just released.
-  if (nk > 0)
-    for (int q = 0; q < 2 * GB_DMA; ++q) issue_q(0, 0, q);
-  barrier_x();                                  // X(0)
-  if (nk > 1)
-    for (int q = 0; q < 2 * GB_DMA; ++q) issue_q(1, 1, q);
-  if (nk > 0) frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      frags(kt, s + 1, (s + 1) & 1);
-      mfmas(s & 1, [](int) {});
     }
-    if (kt + 1 < nk) {
-      barrier_x();                              // X(kt + 1)
-      frags(kt + 1, 0, 0);
-    }
-    const bool more2 = kt + 2 < nk;
-    mfmas(1, [&](int n) { if (more2) issue_q(kt + 2, kt & 1, n); });
-  }
-  // lane (h, l32) of block (i, j): row m0 + wm*128 + 32 i + l32, columns n0 + wn*128 + 32 j +
-  // 8 q + 4 h + [0, 4) in values 4q .. 4q + 3 (the B fragment is the MFMA's first operand)
-  typedef float f32x4v __attribute__((ext_vector_type(4)));
-  const int l32 = lane & 31;
+    bf16x8_t fa[2][FM], fb[2][FN];
+    // fragments of K sub-step s of step kt into slot f; K values past a ragged end zeroed
+    auto frags = [&](int kt, int s, int f) {
+      const char* ta = (const char*)&lds_a[kt & 1][0];
+      const char* tb = (const char*)&lds_b[kt & 1][0];
+      // in the order the MFMAs (row-block major) first use them: A block 0, the B blocks, the
+      // other A blocks
+      fa[f][0] = GOperand<TA>::frag(ta, wm * 128, s, lane);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * 128 + 32 * i + l32;
-    if (m >= g.M) continue;
-    float* crow = g.C + (int64_t)m * g.ldc;
+      for (int j = 0; j < FN; ++j) fb[f][j] = GOperand<TB>::frag(tb, wn * 128 + 32 * j, s, lane);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int i = 1; i < FM; ++i) fa[f][i] = GOperand<TA>::frag(ta, wm * 128 + 32 * i, s, lane);
+      const int k_left = g.K - kt * GB_K;
+      if (k_left < GB_K) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * h;
-        if (n >= g.N) continue;
-        f32x4v o;
+        for (int q = 0; q < 8; ++q) {
+          if (16 * s + 8 * h + q >= k_left) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = acc[i][j][4 * q + r];
-        if (acc_c) o += *(const f32x4v*)(crow + n);
-        *(f32x4v*)(crow + n) = o;
+            for (int i = 0; i < FM; ++i) fa[f][i][q] = (__bf16)0.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[f][j][q] = (__bf16)0.0f;
+          }
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // the 16 MFMAs of the fragments in slot f; after(n) follows MFMA n
+    auto mfmas = [&](int f, auto&& after) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
+          after(i * FN + j);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(2 * GB_DMA == FM * FN && GB_K / 16 == 4, "one DMA per MFMA of the last sub-step");
+    // K loop. The tile's first two steps were issued before (the first tile's here, later ones'
+    // under the previous tile's epilogue). Step kt: sub-steps 0-2 (each reading the next
+    // sub-step's fragments part-way through), then barrier X(kt + 1) (step kt + 1 has landed;
+    // every wave has its reads of step kt back), and sub-step 3 of kt, whose MFMAs are
+    // interleaved with the DMA of step kt + 2 into the buffer kt just released and, part-way,
+    // with the reads of step kt + 1's first sub-step.
+    // The reads of sub-step s + 1 go out after the first NEXT_AT MFMAs of s: issued before
+    // them, they would sit ahead of s's own reads in the LDS counter (which tracks 15), and the
+    // first MFMA would wait for most of both sub-steps' reads.
+    constexpr int NEXT_AT = 8;
+    barrier_x();                                // X(0)
+    GGroup gn = g;
+    if (more) gn = G[uniform(g_sh[(it + 1) & 1])];
+    if (nk > 0) frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+        mfmas(s & 1, [&](int n) {
+          if (n == NEXT_AT - 1) frags(kt, s + 1, (s + 1) & 1);
+        });
+      const bool next = kt + 1 < nk, more2 = kt + 2 < nk;
+      if (next) barrier_x();                    // X(kt + 1)
+      mfmas(1, [&](int n) {
+        if (more2) issue_q(g, m0, n0, kt + 2, kt & 1, n);
+        if (next && n == NEXT_AT - 1) frags(kt + 1, 0, 0);
+      });
+    }
+    // the next tile's first two steps go out before this tile's stores, so that their loads
+    // and the store drain overlap
+    int m0n = 0, n0n = 0;
+    if (more) {
+      origin(gn, bn, m0n, n0n);
+      barrier_x();                              // every wave is done with both buffers
+      issue_head(gn, m0n, n0n);
+    }
+    // lane (h, l32) of block (i, j): row m0 + wm*128 + 32 i + l32, columns n0 + wn*128 + 32 j +
+    // 8 q + 4 h + [0, 4) in values 4q .. 4q + 3 (the B fragment is the MFMA's first operand)
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const int l32 = lane & 31;
+    if constexpr (!SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * 128 + 32 * i + l32;
+        if (m >= g.M) continue;
+        float* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * h;
+            if (n >= g.N) continue;
+            f32x4v o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = acc[i][j][4 * q + r];
+            *(f32x4v*)(crow + n) = o;
+          }
+      }
+    } else {
+      // SwiGLU backward of the wave's 64 output columns (blocks j = 0, 1: G; j + 2: U, the same
+      // columns): H = silu(G) U, dH = w D, dG = dH U silu'(G), dU = dH silu(G), and the row's
+      // partial <D, H> over these columns (fixed order: the lane's 32 values, then its h pair).
+      const int I = g.N / 2, ic0 = n0 / 2 + 64 * wn;   // I is a multiple of 64
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * 128 + 32 * i + l32;
+        const bool ok = m < g.M && ic0 < I;
+        const float wv = wrow[i];
+        float dws = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = ic0 + 32 * j + 8 * q + 4 * h;
+            const int64_t at = (int64_t)m * g.ldc + col;
+            f32x4v d4 = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (ok) d4 = *(const f32x4v*)(g.D + at);
+            float og[4], ou[4], oh[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float gv = acc[i][j][4 * q + r], uv = acc[i][j + 2][4 * q + r], dd = d4[r];
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+              const float sl = gv * sg, hv = sl * uv, dh = wv * dd;
+              dws += dd * hv;
+              og[r] = dh * uv * sg * (1.0f + gv * (1.0f - sg));
+              ou[r] = dh * sl;
+              oh[r] = wv * hv;
+            }
+            if (ok) {
+              *(uint2*)(g.dG + at) = make_uint2(pack_bf16x2(og[0], og[1]), pack_bf16x2(og[2], og[3]));
+              *(uint2*)(g.dU + at) = make_uint2(pack_bf16x2(ou[0], ou[1]), pack_bf16x2(ou[2], ou[3]));
+              *(uint2*)(g.Hw + at) = make_uint2(pack_bf16x2(oh[0], oh[1]), pack_bf16x2(oh[2], oh[3]));
+            }
+          }
+        dws += __shfl_xor(dws, 32, 64);
+        if (g.dwp && h == 0 && m < g.M)                // a wave past I contributes 0
+          g.dwp[(int64_t)m * g.ldp + (n0 / GB_N) * 2 + wn] = ic0 < I ? dws : 0.0f;
+      }
+    }
+    if (!more) break;
+    g = gn;
+    b = bn;
+    m0 = m0n;
+    n0 = n0n;
   }
 }
 
@@ -262,25 +380,31 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
 struct BwdPass {
   int d, k, I, E_l, I_s, n_s, T_own;
   int64_t cap;                   // routed rows the buffers hold
+  int ldp;                       // routing-weight-gradient partials per routed row
   const int32_t *counts, *offsets, *route_ids;
   const float* topk_w;
   const bf16_t *wg, *wu, *wd, *sg, *su, *sd;
   const bf16_t* A_own;           // x own rows [T_own, d]
   const bf16_t* dP_own;          // their output gradient [T_own, d]
-  bf16_t *Ar, *dPr, *dGr, *dUr, *Hr, *dOr, *dGo, *dUo, *Ho;
-  float *Gr, *Ur, *Dr, *dAr, *Go, *Uo, *Do, *dAo, *dw_rows;
+  bf16_t *Ar, *dPr, *dGr, *dUr, *Hr, *dGo, *dUo, *Ho;   // Hr: w H
+  float *Dr, *dAr, *Do, *dAo, *dwp;
   float *dwg, *dwu, *dwd, *dsg, *dsu, *dsd;
-  int32_t *t_rec, *t_dd, *t_dug, *t_duu, *t_wg;   // group tables
+  int32_t *t_rec, *t_dd, *t_du, *t_wg;   // group tables
   int32_t* err;                  // error word (routes past the capacity)
 };
 
-MOK_DEV void put(GGroup* G, int& n, int32_t& tiles, const bf16_t* A, int64_t lda,
-                 const bf16_t* B, int64_t ldb, float* C, int64_t ldc, int M, int N, int K) {
-  GGroup g;
-  g.A = A; g.B = B; g.C = C; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
-  g.M = M; g.N = N; g.K = K; g.tile0 = tiles;
+MOK_DEV GGroup plain(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, float* C,
+                     int64_t ldc, int M, int N, int K) {
+  GGroup g = {};
+  g.A = A; g.A2 = A; g.B = B; g.B2 = B; g.C = C;
+  g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K; g.kseg = K;
+  return g;
+}
+MOK_DEV void put(GGroup* G, int& n, int32_t& tiles, GGroup g) {
+  g.tile0 = tiles;
   G[n++] = g;
-  tiles += ((M + GB_M - 1) / GB_M) * ((N + GB_N - 1) / GB_N);
+  tiles += ((g.M + GB_M - 1) / GB_M) * ((g.N + GB_N - 1) / GB_N);
 }
 MOK_DEV void close_table(int32_t* t, int n, int32_t tiles) { t[0] = n; t[1] = tiles; }
 
@@ -301,22 +425,28 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
   *p.err = over ? (int32_t)MOK_DEVERR_OVERFLOW : 0;
   auto cnt = [&](int e) { return over ? 0 : s_cnt[e]; };
   auto off = [&](int e) { return (int64_t)s_off[e]; };
-  // recompute: G = A Wg^T, U = A Wu^T (K-contiguous operands)
+  // recompute + SwiGLU backward: G, U = A [Wg; Wu]^T, paired column by column, with D (from the
+  // dgrad-down launch before) in the epilogue
   {
     GGroup* G = gtable_groups(p.t_rec);
     int n = 0;
     int32_t tl = 0;
-    for (int e = 0; e < E; ++e) {
-      if (cnt(e) == 0) continue;
-      put(G, n, tl, p.Ar + off(e) * d, d, p.wg + (int64_t)e * I * d, d, p.Gr + off(e) * I, I,
-          cnt(e), I, d);
-      put(G, n, tl, p.Ar + off(e) * d, d, p.wu + (int64_t)e * I * d, d, p.Ur + off(e) * I, I,
-          cnt(e), I, d);
-    }
-    if (Ish > 0 && p.T_own > 0) {
-      put(G, n, tl, p.A_own, d, p.sg, d, p.Go, Ish, p.T_own, Ish, d);
-      put(G, n, tl, p.A_own, d, p.su, d, p.Uo, Ish, p.T_own, Ish, d);
-    }
+    auto swiglu = [&](const bf16_t* A, const bf16_t* Wg, const bf16_t* Wu, int M, int In,
+                      const float* D, bf16_t* dG, bf16_t* dU, bf16_t* Hw, float* dwp,
+                      const int32_t* rid) {
+      GGroup g = plain(A, d, Wg, d, nullptr, In, M, 2 * In, d);
+      g.B2 = Wu;
+      g.D = D; g.dG = dG; g.dU = dU; g.Hw = Hw; g.dwp = dwp; g.ldp = p.ldp;
+      g.rid = rid; g.w = p.topk_w;
+      put(G, n, tl, g);
+    };
+    for (int e = 0; e < E; ++e)
+      if (cnt(e) > 0)
+        swiglu(p.Ar + off(e) * d, p.wg + (int64_t)e * I * d, p.wu + (int64_t)e * I * d, cnt(e), I,
+               p.Dr + off(e) * I, p.dGr + off(e) * I, p.dUr + off(e) * I, p.Hr + off(e) * I,
+               p.dwp + off(e) * p.ldp, p.route_ids + off(e));
+    if (Ish > 0 && p.T_own > 0)
+      swiglu(p.A_own, p.sg, p.su, p.T_own, Ish, p.Do, p.dGo, p.dUo, p.Ho, nullptr, nullptr);
     close_table(p.t_rec, n, tl);
   }
   // dgrad down: D = dP Wd (Wd read along its output dimension: transposed B)
@@ -326,126 +456,62 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
     int32_t tl = 0;
     for (int e = 0; e < E; ++e)
       if (cnt(e) > 0)
-        put(G, n, tl, p.dPr + off(e) * d, d, p.wd + (int64_t)e * d * I, I, p.Dr + off(e) * I, I,
-            cnt(e), I, d);
+        put(G, n, tl, plain(p.dPr + off(e) * d, d, p.wd + (int64_t)e * d * I, I, p.Dr + off(e) * I,
+                            I, cnt(e), I, d));
     if (Ish > 0 && p.T_own > 0)
       for (int s = 0; s < p.n_s; ++s)
-        put(G, n, tl, p.dP_own, d, p.sd + (int64_t)s * d * p.I_s, p.I_s, p.Do + s * p.I_s, Ish,
-            p.T_own, p.I_s, d);
+        put(G, n, tl, plain(p.dP_own, d, p.sd + (int64_t)s * d * p.I_s, p.I_s, p.Do + s * p.I_s,
+                            Ish, p.T_own, p.I_s, d));
     close_table(p.t_dd, n, tl);
   }
-  // dgrad up: dA = dG Wg (+)= dU Wu (weights read along d: transposed B)
-  for (int part = 0; part < 2; ++part) {
-    int32_t* t = part == 0 ? p.t_dug : p.t_duu;
-    GGroup* G = gtable_groups(t);
+  // dgrad up: dA = [dG dU] [Wg; Wu] as one product over K = 2 I in two segments (the weights
+  // read along d: transposed B)
+  {
+    GGroup* G = gtable_groups(p.t_du);
     int n = 0;
     int32_t tl = 0;
+    auto du = [&](const bf16_t* dG, const bf16_t* dU, const bf16_t* Wg, const bf16_t* Wu, float* dA,
+                  int M, int In) {
+      GGroup g = plain(dG, In, Wg, d, dA, d, M, d, 2 * In);
+      g.A2 = dU; g.B2 = Wu; g.kseg = In;
+      put(G, n, tl, g);
+    };
     for (int e = 0; e < E; ++e)
       if (cnt(e) > 0)
-        put(G, n, tl, (part == 0 ? p.dGr : p.dUr) + off(e) * I, I,
-            (part == 0 ? p.wg : p.wu) + (int64_t)e * I * d, d, p.dAr + off(e) * d, d, cnt(e), d, I);
-    if (Ish > 0 && p.T_own > 0)
-      put(G, n, tl, part == 0 ? p.dGo : p.dUo, Ish, part == 0 ? p.sg : p.su, d, p.dAo, d,
-          p.T_own, d, Ish);
-    close_table(t, n, tl);
+        du(p.dGr + off(e) * I, p.dUr + off(e) * I, p.wg + (int64_t)e * I * d,
+           p.wu + (int64_t)e * I * d, p.dAr + off(e) * d, cnt(e), I);
+    if (Ish > 0 && p.T_own > 0) du(p.dGo, p.dUo, p.sg, p.su, p.dAo, p.T_own, Ish);
+    close_table(p.t_du, n, tl);
   }
   // wgrad (both operands transposed: K is the expert's rows). Every expert gets its tiles,
-  // also with no rows (then its gradient is written as zero).
+  // also with no rows (then its gradient is written as zero). dWd = dP^T (w H).
   {
     GGroup* G = gtable_groups(p.t_wg);
     int n = 0;
     int32_t tl = 0;
     for (int e = 0; e < E; ++e) {
       const int c = cnt(e);
-      put(G, n, tl, p.dGr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwg + (int64_t)e * I * d, d,
-          I, d, c);
-      put(G, n, tl, p.dUr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwu + (int64_t)e * I * d, d,
-          I, d, c);
-      put(G, n, tl, p.dOr + off(e) * d, d, p.Hr + off(e) * I, I, p.dwd + (int64_t)e * d * I, I,
-          d, I, c);
+      put(G, n, tl, plain(p.dGr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwg + (int64_t)e * I * d,
+                          d, I, d, c));
+      put(G, n, tl, plain(p.dUr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwu + (int64_t)e * I * d,
+                          d, I, d, c));
+      put(G, n, tl, plain(p.dPr + off(e) * d, d, p.Hr + off(e) * I, I, p.dwd + (int64_t)e * d * I,
+                          I, d, I, c));
     }
     if (Ish > 0) {
-      put(G, n, tl, p.dGo, Ish, p.A_own, d, p.dsg, d, Ish, d, p.T_own);
-      put(G, n, tl, p.dUo, Ish, p.A_own, d, p.dsu, d, Ish, d, p.T_own);
+      put(G, n, tl, plain(p.dGo, Ish, p.A_own, d, p.dsg, d, Ish, d, p.T_own));
+      put(G, n, tl, plain(p.dUo, Ish, p.A_own, d, p.dsu, d, Ish, d, p.T_own));
       for (int s = 0; s < p.n_s; ++s)
-        put(G, n, tl, p.dP_own, d, p.Ho + s * p.I_s, Ish, p.dsd + (int64_t)s * d * p.I_s, p.I_s,
-            d, p.I_s, p.T_own);
+        put(G, n, tl, plain(p.dP_own, d, p.Ho + s * p.I_s, Ish, p.dsd + (int64_t)s * d * p.I_s,
+                            p.I_s, d, p.I_s, p.T_own));
     }
     close_table(p.t_wg, n, tl);
   }
 }
 
-// SwiGLU backward of one row per workgroup: routed rows [0, N) of the plan, then the own
-// rows. Four values a thread per pass (16-byte loads of G, U, D; 8-byte stores of dG, dU, H).
-// The routing-weight gradient is a fixed-order reduction (per-thread strided sums, then a
-// tree), so it is the same on every run.
-__global__ __launch_bounds__(256) void k_bwd_swiglu(BwdPass p) {
-  __shared__ float red[256];
-  const int64_t N = min((int64_t)p.offsets[p.E_l], p.cap);
-  const int64_t row = blockIdx.x;
-  const bool own = row >= p.cap;
-  if (*p.err) return;
-  if (!own && row >= N) return;
-  const int64_t r = own ? row - p.cap : row;
-  if (own && r >= p.T_own) return;
-  const int I = own ? p.n_s * p.I_s : p.I;
-  const float* G = (own ? p.Go : p.Gr) + r * I;
-  const float* U = (own ? p.Uo : p.Ur) + r * I;
-  const float* D = (own ? p.Do : p.Dr) + r * I;
-  bf16_t* dG = (own ? p.dGo : p.dGr) + r * I;
-  bf16_t* dU = (own ? p.dUo : p.dUr) + r * I;
-  bf16_t* H = (own ? p.Ho : p.Hr) + r * I;
-  const float w = own ? 1.0f : p.topk_w[p.route_ids[r]];
-  float dw = 0.0f;
-  for (int n = 4 * threadIdx.x; n < I; n += 4 * 256) {   // I is a multiple of 64
-    const float4 g4 = *(const float4*)(G + n), u4 = *(const float4*)(U + n);
-    const float4 d4 = *(const float4*)(D + n);
-    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
-    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-    float og[4], ou[4], oh[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float g = gv[q], u = uv[q], dd = dv[q];
-      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-      const float sl = g * sg;
-      const float hv = sl * u;
-      dw += dd * hv;
-      const float dh = w * dd;
-      og[q] = dh * u * sg * (1.0f + g * (1.0f - sg));
-      ou[q] = dh * sl;
-      oh[q] = hv;
-    }
-    *(uint2*)(dG + n) = make_uint2(pack_bf16x2(og[0], og[1]), pack_bf16x2(og[2], og[3]));
-    *(uint2*)(dU + n) = make_uint2(pack_bf16x2(ou[0], ou[1]), pack_bf16x2(ou[2], ou[3]));
-    *(uint2*)(H + n) = make_uint2(pack_bf16x2(oh[0], oh[1]), pack_bf16x2(oh[2], oh[3]));
-  }
-  if (!own) {
-    // dO = w dP for the down-projection weight gradient, 8 values a thread per pass
-    const bf16_t* dP = p.dPr + r * p.d;
-    bf16_t* dO = p.dOr + r * p.d;
-    for (int m = 8 * threadIdx.x; m < p.d; m += 8 * 256) {
-      const uint4 v = *(const uint4*)(dP + m);
-      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = pack_bf16x2(w * __uint_as_float(in[q] << 16),
-                           w * __uint_as_float(in[q] & 0xFFFF0000u));
-      *(uint4*)(dO + m) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    red[threadIdx.x] = dw;
-    __syncthreads();
-#pragma unroll
-    for (int s = 128; s > 0; s >>= 1) {
-      if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) p.dw_rows[r] = red[0];
-  }
-}
-
 // dx through each local route to its source-indexed slot (bf16), the routing-weight gradient
-// to [t, j], and the shared experts' dx. One workgroup per row, 8 values a thread per pass.
+// to [t, j] (the row's partials summed in ascending order), and the shared experts' dx. One
+// workgroup per row, 8 values a thread per pass.
 MOK_DEV void f32_row_to_bf16(const float* __restrict__ src, bf16_t* __restrict__ dst, int d) {
   for (int m = 8 * threadIdx.x; m < d; m += 8 * 256) {     // d is a multiple of 128
     const float4 a = *(const float4*)(src + m), b = *(const float4*)(src + m + 4);
@@ -463,7 +529,11 @@ __global__ __launch_bounds__(256) void k_bwd_scatter(BwdPass p, bf16_t* __restri
     if (row >= N) return;
     const int32_t rid = p.route_ids[row];
     f32_row_to_bf16(p.dAr + row * p.d, dx_slots + (int64_t)rid * p.d, p.d);
-    if (threadIdx.x == 0 && dtopk_w) dtopk_w[rid] = p.dw_rows[row];
+    if (threadIdx.x == 0 && dtopk_w) {
+      float s = 0.0f;
+      for (int q = 0; q < p.ldp; ++q) s += p.dwp[row * p.ldp + q];
+      dtopk_w[rid] = s;
+    }
   } else {
     const int64_t r = row - p.cap;
     if (r >= p.T_own || !dx_shared) return;
@@ -483,9 +553,10 @@ size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
 struct BwdLayout {
   size_t counts, offsets, route_ids, blk_counts, err;
-  size_t Ar, dPr, dGr, dUr, Hr, dOr, dGo, dUo, Ho, Gr, Ur, Dr, dAr, Go, Uo, Do, dAo, dw_rows;
-  size_t t_rec, t_dd, t_dug, t_duu, t_wg, total;
+  size_t Ar, dPr, dGr, dUr, Hr, dGo, dUo, Ho, Dr, dAr, Do, dAo, dwp;
+  size_t t_rec, t_dd, t_du, t_wg, total;
   int64_t cap;
+  int ldp;                       // routing-weight-gradient partials per routed row
   int64_t tiles_rec, tiles_dd, tiles_du, tiles_wg;
 };
 
@@ -499,7 +570,7 @@ int validate_bwd(const mok_moe_bwd_args* a) {
   if (a->T_pool < 0 || a->tokens_per_rank < 1 || a->T_pool % a->tokens_per_rank) return MOK_EINVAL;
   if (a->T_pool * (int64_t)a->k >= (int64_t)1 << 31) return MOK_EINVAL;
   if (a->own_begin < 0 || a->T_own < 0 || a->own_begin + a->T_own > a->T_pool) return MOK_EINVAL;
-  if (a->n_shared < 0 || a->route_rows_cap < 0) return MOK_EINVAL;
+  if (a->n_shared < 0 || a->n_shared > 64 || a->route_rows_cap < 0) return MOK_EINVAL;
   if (a->d % 128 || a->I % 64) return MOK_EINVAL;
   if (a->n_shared > 0 && (a->I_shared <= 0 || a->I_shared % 64)) return MOK_EINVAL;
   if (!a->x || !a->topk_idx || !a->topk_w || !a->w_gate || !a->w_up || !a->w_down) return MOK_EINVAL;
@@ -534,21 +605,22 @@ BwdLayout layout_bwd(const mok_moe_bwd_args* a) {
   const int64_t nb = plan_n_blocks(a->T_pool * a->k, a->E_l);
   L.blk_counts = take(4 * nb * a->E_l);
   L.err = take(16);
-  L.Ar = take(2 * cap * d); L.dPr = take(2 * cap * d); L.dOr = take(2 * cap * d);
+  L.Ar = take(2 * cap * d); L.dPr = take(2 * cap * d);
   L.dGr = take(2 * cap * I); L.dUr = take(2 * cap * I); L.Hr = take(2 * cap * I);
-  L.Gr = take(4 * cap * I); L.Ur = take(4 * cap * I); L.Dr = take(4 * cap * I);
-  L.dAr = take(4 * cap * d); L.dw_rows = take(4 * cap);
+  L.Dr = take(4 * cap * I); L.dAr = take(4 * cap * d);
+  L.ldp = (int)(2 * cdiv(2 * I, GB_N));            // one partial per wave's 64 output columns
+  L.dwp = take(4 * cap * L.ldp);
   const int64_t Io = std::max<int64_t>(1, Ish);
   L.dGo = take(2 * To * Io); L.dUo = take(2 * To * Io); L.Ho = take(2 * To * Io);
-  L.Go = take(4 * To * Io); L.Uo = take(4 * To * Io); L.Do = take(4 * To * Io);
+  L.Do = take(4 * To * Io);
   L.dAo = take(4 * To * d);
   const int ng = 3 * a->E_l + 2 + a->n_shared + 2;
-  L.t_rec = take(gtable_bytes(ng)); L.t_dd = take(gtable_bytes(ng)); L.t_dug = take(gtable_bytes(ng));
-  L.t_duu = take(gtable_bytes(ng)); L.t_wg = take(gtable_bytes(ng));
+  L.t_rec = take(gtable_bytes(ng)); L.t_dd = take(gtable_bytes(ng)); L.t_du = take(gtable_bytes(ng));
+  L.t_wg = take(gtable_bytes(ng));
   L.total = off;
   // upper bounds of each launch's tiles (the device fills in the exact counts)
   const int64_t mt_r = cdiv(cap, GB_M) + a->E_l, mt_o = cdiv(a->T_own, GB_M);
-  L.tiles_rec = 2 * (mt_r * cdiv(I, GB_N) + mt_o * cdiv(Ish, GB_N));
+  L.tiles_rec = mt_r * cdiv(2 * I, GB_N) + mt_o * cdiv(2 * Ish, GB_N);
   L.tiles_dd = mt_r * cdiv(I, GB_N) + (int64_t)a->n_shared * mt_o * cdiv(a->I_shared, GB_N);
   L.tiles_du = (mt_r + mt_o) * cdiv(d, GB_N);
   L.tiles_wg = (int64_t)a->E_l * (2 * cdiv(I, GB_M) * cdiv(d, GB_N) + cdiv(d, GB_M) * cdiv(I, GB_N)) +
@@ -589,15 +661,14 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   p.A_own = x + a->own_begin * a->d;
   p.dP_own = a->dy ? (const bf16_t*)a->dy + a->own_begin * a->d : (const bf16_t*)a->dy_shared;
   p.Ar = (bf16_t*)at(L.Ar); p.dPr = (bf16_t*)at(L.dPr); p.dGr = (bf16_t*)at(L.dGr);
-  p.dUr = (bf16_t*)at(L.dUr); p.Hr = (bf16_t*)at(L.Hr); p.dOr = (bf16_t*)at(L.dOr);
+  p.dUr = (bf16_t*)at(L.dUr); p.Hr = (bf16_t*)at(L.Hr);
   p.dGo = (bf16_t*)at(L.dGo); p.dUo = (bf16_t*)at(L.dUo); p.Ho = (bf16_t*)at(L.Ho);
-  p.Gr = (float*)at(L.Gr); p.Ur = (float*)at(L.Ur); p.Dr = (float*)at(L.Dr); p.dAr = (float*)at(L.dAr);
-  p.Go = (float*)at(L.Go); p.Uo = (float*)at(L.Uo); p.Do = (float*)at(L.Do); p.dAo = (float*)at(L.dAo);
-  p.dw_rows = (float*)at(L.dw_rows);
+  p.Dr = (float*)at(L.Dr); p.dAr = (float*)at(L.dAr); p.Do = (float*)at(L.Do); p.dAo = (float*)at(L.dAo);
+  p.dwp = (float*)at(L.dwp); p.ldp = L.ldp;
   p.dwg = a->dw_gate; p.dwu = a->dw_up; p.dwd = a->dw_down;
   p.dsg = a->dws_gate; p.dsu = a->dws_up; p.dsd = a->dws_down;
-  p.t_rec = (int32_t*)at(L.t_rec); p.t_dd = (int32_t*)at(L.t_dd); p.t_dug = (int32_t*)at(L.t_dug);
-  p.t_duu = (int32_t*)at(L.t_duu); p.t_wg = (int32_t*)at(L.t_wg);
+  p.t_rec = (int32_t*)at(L.t_rec); p.t_dd = (int32_t*)at(L.t_dd); p.t_du = (int32_t*)at(L.t_du);
+  p.t_wg = (int32_t*)at(L.t_wg);
   p.err = (int32_t*)at(L.err);
   const int64_t worst = a->T_pool * (int64_t)std::min(a->k, a->E_l);
   // the plan (also yields route_ids for the gathers), then the rows in plan order
@@ -617,21 +688,16 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
                            p.offsets, a->E_l, L.cap, p.dPr, s) != hipSuccess)
       return MOK_EHIP;
   }
-  auto gg = [&](int32_t* table, int64_t tiles, bool ta, bool tb, bool accum) {
+  auto gg = [&](auto kernel, int32_t* table, int64_t tiles) {
     if (tiles <= 0) return;
-    const dim3 grid((unsigned)((tiles + 255) / 256 * 256)), block(GB_NT);
-    if (!ta && !tb) launch_k(k_ggemm<false, false>, grid, block, 0, s, nullptr, nullptr, table, accum);
-    else if (!ta && tb) launch_k(k_ggemm<false, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
-    else launch_k(k_ggemm<true, true>, grid, block, 0, s, nullptr, nullptr, table, accum);
+    const dim3 grid(256), block(GB_NT);          // persistent: one workgroup per CU
+    launch_k(kernel, grid, block, 0, s, nullptr, nullptr, table);
   };
-  gg(p.t_rec, L.tiles_rec, false, false, false);           // G, U
-  gg(p.t_dd, L.tiles_dd, false, true, false);              // D = dP Wd
+  gg(k_ggemm<false, true, false>, p.t_dd, L.tiles_dd);     // D = dP Wd
+  gg(k_ggemm<false, false, true>, p.t_rec, L.tiles_rec);   // G, U; SwiGLU backward
+  gg(k_ggemm<false, true, false>, p.t_du, L.tiles_du);     // dA = dG Wg + dU Wu
+  gg(k_ggemm<true, true, false>, p.t_wg, L.tiles_wg);      // dWg, dWu, dWd (+ shared)
   const int64_t rows = L.cap + p.T_own;
-  if (rows > 0)
-    launch_k(k_bwd_swiglu, dim3((unsigned)rows), dim3(256), 0, s, nullptr, nullptr, p);
-  gg(p.t_dug, L.tiles_du, false, true, false);             // dA = dG Wg
-  gg(p.t_duu, L.tiles_du, false, true, true);              //    + dU Wu
-  gg(p.t_wg, L.tiles_wg, true, true, false);               // dWg, dWu, dWd (+ shared)
   if (rows > 0)
     launch_k(k_bwd_scatter, dim3((unsigned)rows), dim3(256), 0, s, nullptr, nullptr, p,
              (bf16_t*)a->dx_slots, (bf16_t*)a->dx_shared, a->dtopk_w);
