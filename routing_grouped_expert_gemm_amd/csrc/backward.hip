@@ -46,6 +46,8 @@ struct GGroup {
   float* dwp;               // SwiGLU: [M, ldp] float32, or null
   const int32_t* rid;       // SwiGLU: route id of each row, or null (weight 1)
   const float* w;           // SwiGLU: routing weights by route id
+  bf16_t* Cb;               // bf16 output instead of C: row rmap[m] (or m) of Cb, ld ldc
+  const int32_t* rmap;      // output row of each row, or null
 };
 // A group table: header {groups, tiles, error, pad} then the groups.
 constexpr int GT_HDR = 4;
@@ -221,14 +223,19 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    // SwiGLU: the routing weight of the lane's row in each block row (loaded under the K loop)
+      // SwiGLU: the routing weight of the lane's row in each block row; bf16 output: its output
+    // row (both loaded under the K loop)
     float wrow[FM];
+    int32_t orow[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * 128 + 32 * i + (lane & 31);
       wrow[i] = 1.0f;
+      orow[i] = m;
       if constexpr (SWIGLU) {
-        const int m = m0 + wm * 128 + 32 * i + (lane & 31);
         if (g.rid && m < g.M) wrow[i] = g.w[g.rid[m]];
+      } else {
+        if (g.rmap && m < g.M) orow[i] = g.rmap[m];
       }
     }
     bf16x8_t fa[2][FM], fb[2][FN];
@@ -314,6 +321,7 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
         const int m = m0 + wm * 128 + 32 * i + l32;
         if (m >= g.M) continue;
         float* crow = g.C + (int64_t)m * g.ldc;
+        bf16_t* brow = g.Cb + (int64_t)orow[i] * g.ldc;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -323,7 +331,10 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
             f32x4v o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = acc[i][j][4 * q + r];
-            *(f32x4v*)(crow + n) = o;
+            if (g.Cb)
+              *(uint2*)(brow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            else
+              *(f32x4v*)(crow + n) = o;
           }
       }
     } else {
@@ -387,7 +398,8 @@ struct BwdPass {
   const bf16_t* A_own;           // x own rows [T_own, d]
   const bf16_t* dP_own;          // their output gradient [T_own, d]
   bf16_t *Ar, *dPr, *dGr, *dUr, *Hr, *dGo, *dUo, *Ho;   // Hr: w H
-  float *Dr, *dAr, *Do, *dAo, *dwp;
+  float *Dr, *Do, *dwp;
+  bf16_t *dx_slots, *dx_shared;  // outputs: dx through each route, the shared experts' dx
   float *dwg, *dwu, *dwd, *dsg, *dsu, *dsd;
   int32_t *t_rec, *t_dd, *t_du, *t_wg;   // group tables
   int32_t* err;                  // error word (routes past the capacity)
@@ -470,17 +482,20 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
     GGroup* G = gtable_groups(p.t_du);
     int n = 0;
     int32_t tl = 0;
-    auto du = [&](const bf16_t* dG, const bf16_t* dU, const bf16_t* Wg, const bf16_t* Wu, float* dA,
-                  int M, int In) {
-      GGroup g = plain(dG, In, Wg, d, dA, d, M, d, 2 * In);
+    // dx rows in bf16: a routed row to its source-indexed slot, an own row to dx_shared
+    auto du = [&](const bf16_t* dG, const bf16_t* dU, const bf16_t* Wg, const bf16_t* Wu,
+                  bf16_t* dx, const int32_t* rmap, int M, int In) {
+      GGroup g = plain(dG, In, Wg, d, nullptr, d, M, d, 2 * In);
       g.A2 = dU; g.B2 = Wu; g.kseg = In;
+      g.Cb = dx; g.rmap = rmap;
       put(G, n, tl, g);
     };
     for (int e = 0; e < E; ++e)
       if (cnt(e) > 0)
         du(p.dGr + off(e) * I, p.dUr + off(e) * I, p.wg + (int64_t)e * I * d,
-           p.wu + (int64_t)e * I * d, p.dAr + off(e) * d, cnt(e), I);
-    if (Ish > 0 && p.T_own > 0) du(p.dGo, p.dUo, p.sg, p.su, p.dAo, p.T_own, Ish);
+           p.wu + (int64_t)e * I * d, p.dx_slots, p.route_ids + off(e), cnt(e), I);
+    if (Ish > 0 && p.T_own > 0 && p.dx_shared)
+      du(p.dGo, p.dUo, p.sg, p.su, p.dx_shared, nullptr, p.T_own, Ish);
     close_table(p.t_du, n, tl);
   }
   // wgrad (both operands transposed: K is the expert's rows). Every expert gets its tiles,
@@ -509,36 +524,15 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
   }
 }
 
-// dx through each local route to its source-indexed slot (bf16), the routing-weight gradient
-// to [t, j] (the row's partials summed in ascending order), and the shared experts' dx. One
-// workgroup per row, 8 values a thread per pass.
-MOK_DEV void f32_row_to_bf16(const float* __restrict__ src, bf16_t* __restrict__ dst, int d) {
-  for (int m = 8 * threadIdx.x; m < d; m += 8 * 256) {     // d is a multiple of 128
-    const float4 a = *(const float4*)(src + m), b = *(const float4*)(src + m + 4);
-    *(uint4*)(dst + m) = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
-                                    pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
-  }
-}
-__global__ __launch_bounds__(256) void k_bwd_scatter(BwdPass p, bf16_t* __restrict__ dx_slots,
-                                                     bf16_t* __restrict__ dx_shared,
-                                                     float* __restrict__ dtopk_w) {
+// The routing-weight gradient of each routed row: its partials summed in ascending order, to
+// [t, j] (the dgrad-up product writes dx itself). One thread per row.
+__global__ __launch_bounds__(256) void k_bwd_dtopk(BwdPass p, float* __restrict__ dtopk_w) {
   const int64_t N = min((int64_t)p.offsets[p.E_l], p.cap);
-  const int64_t row = blockIdx.x;
-  if (*p.err) return;
-  if (row < p.cap) {
-    if (row >= N) return;
-    const int32_t rid = p.route_ids[row];
-    f32_row_to_bf16(p.dAr + row * p.d, dx_slots + (int64_t)rid * p.d, p.d);
-    if (threadIdx.x == 0 && dtopk_w) {
-      float s = 0.0f;
-      for (int q = 0; q < p.ldp; ++q) s += p.dwp[row * p.ldp + q];
-      dtopk_w[rid] = s;
-    }
-  } else {
-    const int64_t r = row - p.cap;
-    if (r >= p.T_own || !dx_shared) return;
-    f32_row_to_bf16(p.dAo + r * p.d, dx_shared + r * p.d, p.d);
-  }
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (*p.err || row >= N) return;
+  float s = 0.0f;
+  for (int q = 0; q < p.ldp; ++q) s += p.dwp[row * p.ldp + q];
+  dtopk_w[p.route_ids[row]] = s;
 }
 
 }  // namespace mok
@@ -553,7 +547,7 @@ size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
 struct BwdLayout {
   size_t counts, offsets, route_ids, blk_counts, err;
-  size_t Ar, dPr, dGr, dUr, Hr, dGo, dUo, Ho, Dr, dAr, Do, dAo, dwp;
+  size_t Ar, dPr, dGr, dUr, Hr, dGo, dUo, Ho, Dr, Do, dwp;
   size_t t_rec, t_dd, t_du, t_wg, total;
   int64_t cap;
   int ldp;                       // routing-weight-gradient partials per routed row
@@ -607,13 +601,12 @@ BwdLayout layout_bwd(const mok_moe_bwd_args* a) {
   L.err = take(16);
   L.Ar = take(2 * cap * d); L.dPr = take(2 * cap * d);
   L.dGr = take(2 * cap * I); L.dUr = take(2 * cap * I); L.Hr = take(2 * cap * I);
-  L.Dr = take(4 * cap * I); L.dAr = take(4 * cap * d);
+  L.Dr = take(4 * cap * I);
   L.ldp = (int)(2 * cdiv(2 * I, GB_N));            // one partial per wave's 64 output columns
   L.dwp = take(4 * cap * L.ldp);
   const int64_t Io = std::max<int64_t>(1, Ish);
   L.dGo = take(2 * To * Io); L.dUo = take(2 * To * Io); L.Ho = take(2 * To * Io);
   L.Do = take(4 * To * Io);
-  L.dAo = take(4 * To * d);
   const int ng = 3 * a->E_l + 2 + a->n_shared + 2;
   L.t_rec = take(gtable_bytes(ng)); L.t_dd = take(gtable_bytes(ng)); L.t_du = take(gtable_bytes(ng));
   L.t_wg = take(gtable_bytes(ng));
@@ -663,7 +656,8 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   p.Ar = (bf16_t*)at(L.Ar); p.dPr = (bf16_t*)at(L.dPr); p.dGr = (bf16_t*)at(L.dGr);
   p.dUr = (bf16_t*)at(L.dUr); p.Hr = (bf16_t*)at(L.Hr);
   p.dGo = (bf16_t*)at(L.dGo); p.dUo = (bf16_t*)at(L.dUo); p.Ho = (bf16_t*)at(L.Ho);
-  p.Dr = (float*)at(L.Dr); p.dAr = (float*)at(L.dAr); p.Do = (float*)at(L.Do); p.dAo = (float*)at(L.dAo);
+  p.Dr = (float*)at(L.Dr); p.Do = (float*)at(L.Do);
+  p.dx_slots = (bf16_t*)a->dx_slots; p.dx_shared = (bf16_t*)a->dx_shared;
   p.dwp = (float*)at(L.dwp); p.ldp = L.ldp;
   p.dwg = a->dw_gate; p.dwu = a->dw_up; p.dwd = a->dw_down;
   p.dsg = a->dws_gate; p.dsu = a->dws_up; p.dsd = a->dws_down;
@@ -695,12 +689,11 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   };
   gg(k_ggemm<false, true, false>, p.t_dd, L.tiles_dd);     // D = dP Wd
   gg(k_ggemm<false, false, true>, p.t_rec, L.tiles_rec);   // G, U; SwiGLU backward
-  gg(k_ggemm<false, true, false>, p.t_du, L.tiles_du);     // dA = dG Wg + dU Wu
+  gg(k_ggemm<false, true, false>, p.t_du, L.tiles_du);     // dx = dG Wg + dU Wu
   gg(k_ggemm<true, true, false>, p.t_wg, L.tiles_wg);      // dWg, dWu, dWd (+ shared)
-  const int64_t rows = L.cap + p.T_own;
-  if (rows > 0)
-    launch_k(k_bwd_scatter, dim3((unsigned)rows), dim3(256), 0, s, nullptr, nullptr, p,
-             (bf16_t*)a->dx_slots, (bf16_t*)a->dx_shared, a->dtopk_w);
+  if (L.cap > 0 && a->dtopk_w)
+    launch_k(k_bwd_dtopk, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0, s, nullptr, nullptr,
+             p, a->dtopk_w);
   if (a->E_l == a->E) {
     if (launch_combine(p.T_own > 0 ? a->dx_shared : nullptr, a->dx_slots, a->dx, a->T_pool, a->k,
                        a->d, false, s) != hipSuccess)
