@@ -349,9 +349,11 @@ def summarize_backward(d: str, line: dict) -> str:
     n = line["routed_rows"]
     I_sh = wl.n_shared * wl.I_shared
     per_row = lambda c: c * wl.d * wl.I * n + c * wl.d * I_sh * wl.T_own
-    gemm = {"k_ggemm<false, false>": ("recompute G, U", per_row(4.0)),
-            "k_ggemm<false, true>": ("dgrad: D = dP Wd; dA = dG Wg + dU Wu", per_row(6.0)),
-            "k_ggemm<true, true>": ("wgrad: dWg, dWu, dWd (ragged K)", per_row(6.0))}
+    gemm = {"k_ggemm<false, false, true>": ("recompute G, U; SwiGLU backward in the epilogue",
+                                            per_row(4.0)),
+            "k_ggemm<false, true, false>": ("dgrad: D = dP Wd; dx = [dG dU] [Wg; Wu] (bf16 rows)",
+                                            per_row(6.0)),
+            "k_ggemm<true, true, false>": ("wgrad: dWg, dWu, dWd (ragged K)", per_row(6.0))}
     trace = _csv(os.path.join(d, "trace", "trace_kernel_trace.csv"))
     key = lambda r: kernel_key(r["Kernel_Name"])
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6   # ms
@@ -796,8 +798,9 @@ def measure_backward(steps: int, warmup: int, dev="cuda:0") -> dict:
             "routed_rows": n,
             "gemm_flop": flop, "achieved_tflops": round(ach / 1e12, 2), "peak_tflops": 2500.0,
             "frac": round(ach / PEAK["bf16"], 4),
-            "note": "cold-cache HIP-event time of one mok_moe_backward (plan, gathers, 5 grouped "
-                    "GEMM launches, SwiGLU backward, scatter, combine)"}
+            "note": "cold-cache HIP-event time of one mok_moe_backward (plan, describe, 4 grouped "
+                    "GEMM launches with the SwiGLU backward fused into the recompute, topk-weight "
+                    "gradients, combine)"}
 
 
 def main():

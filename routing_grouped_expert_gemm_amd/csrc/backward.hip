@@ -420,108 +420,103 @@ MOK_DEV void put(GGroup* G, int& n, int32_t& tiles, GGroup g) {
 }
 MOK_DEV void close_table(int32_t* t, int n, int32_t tiles) { t[0] = n; t[1] = tiles; }
 
-// One thread writes every table from the plan's counts (a few hundred groups at most), after
-// the workgroup has copied the counts and offsets to LDS: the serial walk then waits on no
-// global load.
+// Thread e writes expert e's groups of every table; the shared experts' groups follow the
+// routed ones and are written by thread 0. A routed group's place and first tile come from two
+// block scans over the experts: of "has rows" (the recompute and dgrad tables list only experts
+// with rows) and of their M tile counts (a group's tiles are its M tiles times a column count
+// that is the same for every expert of a table). The wgrad table lists three groups per expert,
+// rows or not, each of the same tile count.
 constexpr int BD_THREADS = 1024;
 __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
-  __shared__ int32_t s_cnt[1024], s_off[1025];
-  const int E = p.E_l, d = p.d, I = p.I, Ish = p.n_s * p.I_s;
-  for (int e = threadIdx.x; e <= E; e += BD_THREADS) {
-    if (e < E) s_cnt[e] = p.counts[e];
-    s_off[e] = p.offsets[e];
-  }
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-  const bool over = (int64_t)s_off[E] > p.cap;
-  *p.err = over ? (int32_t)MOK_DEVERR_OVERFLOW : 0;
-  auto cnt = [&](int e) { return over ? 0 : s_cnt[e]; };
-  auto off = [&](int e) { return (int64_t)s_off[e]; };
+  __shared__ int32_t sh[64];
+  const int E = p.E_l, d = p.d, I = p.I, Ish = p.n_s * p.I_s, e = threadIdx.x;
+  const bool over = (int64_t)p.offsets[E] > p.cap;
+  const int c = (e < E && !over) ? p.counts[e] : 0;
+  const int64_t o = e < E ? (int64_t)p.offsets[e] : 0;
+  const int mt = (c + GB_M - 1) / GB_M;
+  int32_t n_has, mt_all;
+  const int32_t pos = block_excl_scan_1024(c > 0 ? 1 : 0, sh, &n_has);
+  const int32_t mt0 = block_excl_scan_1024(mt, sh, &mt_all);
+  auto cols = [](int N) { return (N + GB_N - 1) / GB_N; };
+  auto tiles = [&](const GGroup& g) { return ((g.M + GB_M - 1) / GB_M) * cols(g.N); };
+  GGroup* Grec = gtable_groups(p.t_rec);
+  GGroup* Gdd = gtable_groups(p.t_dd);
+  GGroup* Gdu = gtable_groups(p.t_du);
+  GGroup* Gwg = gtable_groups(p.t_wg);
   // recompute + SwiGLU backward: G, U = A [Wg; Wu]^T, paired column by column, with D (from the
   // dgrad-down launch before) in the epilogue
-  {
-    GGroup* G = gtable_groups(p.t_rec);
-    int n = 0;
-    int32_t tl = 0;
-    auto swiglu = [&](const bf16_t* A, const bf16_t* Wg, const bf16_t* Wu, int M, int In,
-                      const float* D, bf16_t* dG, bf16_t* dU, bf16_t* Hw, float* dwp,
-                      const int32_t* rid) {
-      GGroup g = plain(A, d, Wg, d, nullptr, In, M, 2 * In, d);
-      g.B2 = Wu;
-      g.D = D; g.dG = dG; g.dU = dU; g.Hw = Hw; g.dwp = dwp; g.ldp = p.ldp;
-      g.rid = rid; g.w = p.topk_w;
-      put(G, n, tl, g);
-    };
-    for (int e = 0; e < E; ++e)
-      if (cnt(e) > 0)
-        swiglu(p.Ar + off(e) * d, p.wg + (int64_t)e * I * d, p.wu + (int64_t)e * I * d, cnt(e), I,
-               p.Dr + off(e) * I, p.dGr + off(e) * I, p.dUr + off(e) * I, p.Hr + off(e) * I,
-               p.dwp + off(e) * p.ldp, p.route_ids + off(e));
-    if (Ish > 0 && p.T_own > 0)
-      swiglu(p.A_own, p.sg, p.su, p.T_own, Ish, p.Do, p.dGo, p.dUo, p.Ho, nullptr, nullptr);
-    close_table(p.t_rec, n, tl);
-  }
-  // dgrad down: D = dP Wd (Wd read along its output dimension: transposed B)
-  {
-    GGroup* G = gtable_groups(p.t_dd);
-    int n = 0;
-    int32_t tl = 0;
-    for (int e = 0; e < E; ++e)
-      if (cnt(e) > 0)
-        put(G, n, tl, plain(p.dPr + off(e) * d, d, p.wd + (int64_t)e * d * I, I, p.Dr + off(e) * I,
-                            I, cnt(e), I, d));
-    if (Ish > 0 && p.T_own > 0)
-      for (int s = 0; s < p.n_s; ++s)
-        put(G, n, tl, plain(p.dP_own, d, p.sd + (int64_t)s * d * p.I_s, p.I_s, p.Do + s * p.I_s,
-                            Ish, p.T_own, p.I_s, d));
-    close_table(p.t_dd, n, tl);
-  }
+  auto rec = [&](const bf16_t* A, const bf16_t* Wg, const bf16_t* Wu, int M, int In,
+                 const float* D, bf16_t* dG, bf16_t* dU, bf16_t* Hw, float* dwp,
+                 const int32_t* rid) {
+    GGroup g = plain(A, d, Wg, d, nullptr, In, M, 2 * In, d);
+    g.B2 = Wu;
+    g.D = D; g.dG = dG; g.dU = dU; g.Hw = Hw; g.dwp = dwp; g.ldp = p.ldp;
+    g.rid = rid; g.w = p.topk_w;
+    return g;
+  };
   // dgrad up: dA = [dG dU] [Wg; Wu] as one product over K = 2 I in two segments (the weights
-  // read along d: transposed B)
-  {
-    GGroup* G = gtable_groups(p.t_du);
-    int n = 0;
-    int32_t tl = 0;
-    // dx rows in bf16: a routed row to its source-indexed slot, an own row to dx_shared
-    auto du = [&](const bf16_t* dG, const bf16_t* dU, const bf16_t* Wg, const bf16_t* Wu,
-                  bf16_t* dx, const int32_t* rmap, int M, int In) {
-      GGroup g = plain(dG, In, Wg, d, nullptr, d, M, d, 2 * In);
-      g.A2 = dU; g.B2 = Wu; g.kseg = In;
-      g.Cb = dx; g.rmap = rmap;
-      put(G, n, tl, g);
-    };
-    for (int e = 0; e < E; ++e)
-      if (cnt(e) > 0)
-        du(p.dGr + off(e) * I, p.dUr + off(e) * I, p.wg + (int64_t)e * I * d,
-           p.wu + (int64_t)e * I * d, p.dx_slots, p.route_ids + off(e), cnt(e), I);
-    if (Ish > 0 && p.T_own > 0 && p.dx_shared)
-      du(p.dGo, p.dUo, p.sg, p.su, p.dx_shared, nullptr, p.T_own, Ish);
-    close_table(p.t_du, n, tl);
-  }
-  // wgrad (both operands transposed: K is the expert's rows). Every expert gets its tiles,
-  // also with no rows (then its gradient is written as zero). dWd = dP^T (w H).
-  {
-    GGroup* G = gtable_groups(p.t_wg);
-    int n = 0;
-    int32_t tl = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = cnt(e);
-      put(G, n, tl, plain(p.dGr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwg + (int64_t)e * I * d,
-                          d, I, d, c));
-      put(G, n, tl, plain(p.dUr + off(e) * I, I, p.Ar + off(e) * d, d, p.dwu + (int64_t)e * I * d,
-                          d, I, d, c));
-      put(G, n, tl, plain(p.dPr + off(e) * d, d, p.Hr + off(e) * I, I, p.dwd + (int64_t)e * d * I,
-                          I, d, I, c));
+  // read along d: transposed B); dx rows in bf16: a routed row to its source-indexed slot, an
+  // own row to dx_shared
+  auto du = [&](const bf16_t* dG, const bf16_t* dU, const bf16_t* Wg, const bf16_t* Wu,
+                bf16_t* dx, const int32_t* rmap, int M, int In) {
+    GGroup g = plain(dG, In, Wg, d, nullptr, d, M, d, 2 * In);
+    g.A2 = dU; g.B2 = Wu; g.kseg = In;
+    g.Cb = dx; g.rmap = rmap;
+    return g;
+  };
+  if (e < E) {
+    if (c > 0) {
+      GGroup g = rec(p.Ar + o * d, p.wg + (int64_t)e * I * d, p.wu + (int64_t)e * I * d, c, I,
+                     p.Dr + o * I, p.dGr + o * I, p.dUr + o * I, p.Hr + o * I, p.dwp + o * p.ldp,
+                     p.route_ids + o);
+      g.tile0 = mt0 * cols(2 * I);
+      Grec[pos] = g;
+      // dgrad down: D = dP Wd (Wd read along its output dimension: transposed B)
+      g = plain(p.dPr + o * d, d, p.wd + (int64_t)e * d * I, I, p.Dr + o * I, I, c, I, d);
+      g.tile0 = mt0 * cols(I);
+      Gdd[pos] = g;
+      g = du(p.dGr + o * I, p.dUr + o * I, p.wg + (int64_t)e * I * d, p.wu + (int64_t)e * I * d,
+             p.dx_slots, p.route_ids + o, c, I);
+      g.tile0 = mt0 * cols(d);
+      Gdu[pos] = g;
     }
-    if (Ish > 0) {
-      put(G, n, tl, plain(p.dGo, Ish, p.A_own, d, p.dsg, d, Ish, d, p.T_own));
-      put(G, n, tl, plain(p.dUo, Ish, p.A_own, d, p.dsu, d, Ish, d, p.T_own));
-      for (int s = 0; s < p.n_s; ++s)
-        put(G, n, tl, plain(p.dP_own, d, p.Ho + s * p.I_s, Ish, p.dsd + (int64_t)s * d * p.I_s,
-                            p.I_s, d, p.I_s, p.T_own));
+    // wgrad (both operands transposed: K is the expert's rows); with no rows the gradient is
+    // written as zero. dWd = dP^T (w H).
+    const GGroup w3[3] = {
+        plain(p.dGr + o * I, I, p.Ar + o * d, d, p.dwg + (int64_t)e * I * d, d, I, d, c),
+        plain(p.dUr + o * I, I, p.Ar + o * d, d, p.dwu + (int64_t)e * I * d, d, I, d, c),
+        plain(p.dPr + o * d, d, p.Hr + o * I, I, p.dwd + (int64_t)e * d * I, I, d, I, c)};
+    for (int j = 0; j < 3; ++j) {
+      GGroup g = w3[j];
+      g.tile0 = (3 * e + j) * tiles(w3[0]);
+      Gwg[3 * e + j] = g;
     }
-    close_table(p.t_wg, n, tl);
   }
+  if (e != 0) return;
+  *p.err = over ? (int32_t)MOK_DEVERR_OVERFLOW : 0;
+  int n_rec = n_has, n_dd = n_has, n_du = n_has, n_wg = 3 * E;
+  int32_t tl_rec = mt_all * cols(2 * I), tl_dd = mt_all * cols(I), tl_du = mt_all * cols(d);
+  int32_t tl_wg = 3 * E * ((I + GB_M - 1) / GB_M) * cols(d);
+  if (Ish > 0 && p.T_own > 0) {
+    put(Grec, n_rec, tl_rec,
+        rec(p.A_own, p.sg, p.su, p.T_own, Ish, p.Do, p.dGo, p.dUo, p.Ho, nullptr, nullptr));
+    for (int s = 0; s < p.n_s; ++s)
+      put(Gdd, n_dd, tl_dd, plain(p.dP_own, d, p.sd + (int64_t)s * d * p.I_s, p.I_s,
+                                  p.Do + s * p.I_s, Ish, p.T_own, p.I_s, d));
+    if (p.dx_shared)
+      put(Gdu, n_du, tl_du, du(p.dGo, p.dUo, p.sg, p.su, p.dx_shared, nullptr, p.T_own, Ish));
+  }
+  if (Ish > 0) {
+    put(Gwg, n_wg, tl_wg, plain(p.dGo, Ish, p.A_own, d, p.dsg, d, Ish, d, p.T_own));
+    put(Gwg, n_wg, tl_wg, plain(p.dUo, Ish, p.A_own, d, p.dsu, d, Ish, d, p.T_own));
+    for (int s = 0; s < p.n_s; ++s)
+      put(Gwg, n_wg, tl_wg, plain(p.dP_own, d, p.Ho + s * p.I_s, Ish,
+                                  p.dsd + (int64_t)s * d * p.I_s, p.I_s, d, p.I_s, p.T_own));
+  }
+  close_table(p.t_rec, n_rec, tl_rec);
+  close_table(p.t_dd, n_dd, tl_dd);
+  close_table(p.t_du, n_du, tl_du);
+  close_table(p.t_wg, n_wg, tl_wg);
 }
 
 // The routing-weight gradient of each routed row: its partials summed in ascending order, to
