@@ -246,24 +246,19 @@ MOK_DEV uint2 quantize_quad8_f32(const float (&v)[8], int* s_out) {
 }
 
 // ----------------------------------------------------------------------- MXFP4 (OCP MX)
-// E2M1 code (sign in bit 3) of y = v * 2^-s, which the caller forms exactly: the nearest of
+// E2M1 codes (sign in bit 3) of y = v * 2^-s, which the caller forms exactly: the nearest of
 // the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a tie going to the even code, and everything
-// past 6 saturating. Decided by comparisons against the midpoints, which are exact floats:
-// a midpoint whose even neighbour lies below (0.25, 1.25, 2.5, 5) rounds down, the others
-// (0.75, 1.75, 3.5) round up.
-MOK_DEV uint32_t e2m1_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
-  const float a = fabsf(y);
-  const uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
-  return sign | m;
-}
-
-// Two elements a byte: element 2i in the low nibble of byte i.
+// past 6 saturating to 6. gfx950's conversion (v_cvt_scalef32_pk_fp4_f32, scale 1) implements
+// exactly this rule: checked against comparisons with the midpoints (0.25, 0.75, 1.25, 1.75,
+// 2.5, 3.5, 5; the even neighbour decides a tie) on every bf16 pattern times 2^k (k = -12 ..
+// 12) and on every float32 within 2^20 ulps of a midpoint, 0 or 6, both signs, with no
+// difference. Two elements a byte, element 2i in the low nibble of byte i.
 MOK_DEV uint32_t pack_e2m1x8(const float (&y)[8]) {
   uint32_t w = 0;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) w |= e2m1_code(y[q]) << (4 * q);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
   return w;
 }
 
