@@ -57,7 +57,8 @@ MOK_HOSTDEV inline size_t gtable_bytes(int n_groups) {
 MOK_DEV GGroup* gtable_groups(int32_t* t) { return (GGroup*)(t + GT_HDR * 4); }
 
 constexpr int GB_M = 256, GB_N = 256, GB_K = 64;   // tile rows, tile columns, K step
-constexpr int GB_MAX_GROUPS = 3 * 1024 + 4 + 64;     // groups of a table (E_l <= 1024, n_s <= 64)
+constexpr int GB_MAX_GROUPS = 3 * 1024 + 4 + 64 + 256;   // groups of a table (E_l <= 1024,
+                                                         // n_s <= 64, 256 K pieces)
 constexpr int GB_NT = 256;                           // threads: 4 waves of 128 x 128
 constexpr int GB_TILE = GB_M * GB_K * 2;             // bytes of one operand tile per K step
 constexpr int GB_DMA = GB_TILE / 1024 / 4;           // LDS-DMA instructions per wave and operand
@@ -403,6 +404,18 @@ struct BwdPass {
   float *dwg, *dwu, *dwd, *dsg, *dsu, *dsd;
   int32_t *t_rec, *t_dd, *t_du, *t_wg;   // group tables
   int32_t* err;                  // error word (routes past the capacity)
+  // the wgrad table's last window, when it holds only part of one: its shared-expert tiles
+  // split along K (ws_kept shared tiles stay whole; each later one becomes ws_P pieces of
+  // ws_plen rows, summed by k_bwd_split_sum); ws_kept < 0: no split
+  int ws_kept, ws_P, ws_plen;
+  float* ws_part;                // [split tiles][ws_P][256][256] partial gradients
+  struct SplitTile* ws_split;    // [split tiles] where each sum goes
+};
+
+// A weight-gradient tile computed in K pieces: its block of the gradient matrix.
+struct SplitTile {
+  float* C;
+  int ldc, M, N;
 };
 
 MOK_DEV GGroup plain(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, float* C,
@@ -425,7 +438,8 @@ MOK_DEV void close_table(int32_t* t, int n, int32_t tiles) { t[0] = n; t[1] = ti
 // block scans over the experts: of "has rows" (the recompute and dgrad tables list only experts
 // with rows) and of their M tile counts (a group's tiles are its M tiles times a column count
 // that is the same for every expert of a table). The wgrad table lists three groups per expert,
-// rows or not, each of the same tile count.
+// rows or not, each of the same tile count, then the shared experts' groups (K = all own
+// tokens), the tiles of its last partial window split along K when the host asks for it.
 constexpr int BD_THREADS = 1024;
 __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
   __shared__ int32_t sh[64];
@@ -438,7 +452,8 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
   const int32_t pos = block_excl_scan_1024(c > 0 ? 1 : 0, sh, &n_has);
   const int32_t mt0 = block_excl_scan_1024(mt, sh, &mt_all);
   auto cols = [](int N) { return (N + GB_N - 1) / GB_N; };
-  auto tiles = [&](const GGroup& g) { return ((g.M + GB_M - 1) / GB_M) * cols(g.N); };
+  auto rows = [](int M) { return (M + GB_M - 1) / GB_M; };
+  auto tiles = [&](const GGroup& g) { return rows(g.M) * cols(g.N); };
   GGroup* Grec = gtable_groups(p.t_rec);
   GGroup* Gdd = gtable_groups(p.t_dd);
   GGroup* Gdu = gtable_groups(p.t_du);
@@ -492,7 +507,15 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
       Gwg[3 * e + j] = g;
     }
   }
-  if (e != 0) return;
+  // the split tiles' operands, for the pieces every thread writes at the end
+  struct PieceSrc {
+    const bf16_t *A, *B;
+    int64_t lda, ldb;
+    int K, M, N;
+  };
+  __shared__ PieceSrc src[128];                  // ws_P >= 2 pieces of <= 256 slots
+  __shared__ int32_t piece0[3];                  // first piece group, its first tile, tiles split
+  if (e == 0) {
   *p.err = over ? (int32_t)MOK_DEVERR_OVERFLOW : 0;
   int n_rec = n_has, n_dd = n_has, n_du = n_has, n_wg = 3 * E;
   int32_t tl_rec = mt_all * cols(2 * I), tl_dd = mt_all * cols(I), tl_du = mt_all * cols(d);
@@ -506,17 +529,75 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
     if (p.dx_shared)
       put(Gdu, n_du, tl_du, du(p.dGo, p.dUo, p.sg, p.su, p.dx_shared, nullptr, p.T_own, Ish));
   }
+  int n_split = 0;
   if (Ish > 0) {
-    put(Gwg, n_wg, tl_wg, plain(p.dGo, Ish, p.A_own, d, p.dsg, d, Ish, d, p.T_own));
-    put(Gwg, n_wg, tl_wg, plain(p.dUo, Ish, p.A_own, d, p.dsu, d, Ish, d, p.T_own));
+    // the shared experts' wgrad groups in order; past the first ws_kept of their tiles, each
+    // tile becomes ws_P one-tile groups over consecutive K ranges (written below by every
+    // thread), whose partial sums k_bwd_split_sum adds
+    int32_t left = p.ws_kept < 0 ? INT32_MAX : p.ws_kept;
+    auto put_sh = [&](GGroup g) {
+      const int tn = cols(g.N), tiles = rows(g.M) * tn;
+      const int keep = min(tiles, left);
+      if (keep > 0) {
+        g.tile0 = tl_wg;
+        Gwg[n_wg++] = g;
+        tl_wg += keep;                           // its tiles end where the next group begins
+      }
+      left -= keep;
+      for (int l = keep; l < tiles; ++l, ++n_split) {
+        const int m0 = (l / tn) * GB_M, n0 = (l % tn) * GB_N;
+        const SplitTile st = {g.C + (int64_t)m0 * g.ldc + n0, (int)g.ldc, min(GB_M, g.M - m0),
+                              min(GB_N, g.N - n0)};
+        p.ws_split[n_split] = st;
+        src[n_split] = {g.A + m0, g.B + n0, g.lda, g.ldb, g.K, st.M, st.N};
+      }
+    };
+    put_sh(plain(p.dGo, Ish, p.A_own, d, p.dsg, d, Ish, d, p.T_own));
+    put_sh(plain(p.dUo, Ish, p.A_own, d, p.dsu, d, Ish, d, p.T_own));
     for (int s = 0; s < p.n_s; ++s)
-      put(Gwg, n_wg, tl_wg, plain(p.dP_own, d, p.Ho + s * p.I_s, Ish,
-                                  p.dsd + (int64_t)s * d * p.I_s, p.I_s, d, p.I_s, p.T_own));
+      put_sh(plain(p.dP_own, d, p.Ho + s * p.I_s, Ish, p.dsd + (int64_t)s * d * p.I_s, p.I_s, d,
+                   p.I_s, p.T_own));
   }
   close_table(p.t_rec, n_rec, tl_rec);
   close_table(p.t_dd, n_dd, tl_dd);
   close_table(p.t_du, n_du, tl_du);
-  close_table(p.t_wg, n_wg, tl_wg);
+  const int n_pieces = n_split * p.ws_P;       // one tile each, after every other group
+  close_table(p.t_wg, n_wg + n_pieces, tl_wg + n_pieces);
+  piece0[0] = n_wg;
+  piece0[1] = tl_wg;
+  piece0[2] = n_split;
+  }
+  __syncthreads();
+  const int P = p.ws_P;
+  for (int t = e; t < piece0[2] * P; t += BD_THREADS) {
+    const PieceSrc& g = src[t / P];
+    const int k0 = (t % P) * p.ws_plen;
+    GGroup pg = plain(g.A + (int64_t)k0 * g.lda, g.lda, g.B + (int64_t)k0 * g.ldb, g.ldb,
+                      p.ws_part + (int64_t)t * GB_M * GB_N, GB_N, g.M, g.N,
+                      min(p.ws_plen, g.K - k0));
+    pg.tile0 = piece0[1] + t;
+    Gwg[piece0[0] + t] = pg;
+  }
+}
+
+// The split tiles' gradients: the ws_P partial sums of each element added in ascending piece
+// order (deterministic). Workgroup (t, m): row m of split tile t, a thread per column; the
+// partials are loaded 16 at a time, all in flight together, then added in order.
+__global__ __launch_bounds__(256) void k_bwd_split_sum(BwdPass p) {
+  const SplitTile st = p.ws_split[blockIdx.x];
+  const int m = blockIdx.y, n = threadIdx.x;
+  if (m >= st.M || n >= st.N) return;
+  const float* part = p.ws_part + (int64_t)blockIdx.x * p.ws_P * GB_M * GB_N + m * GB_N + n;
+  float acc = 0.0f;
+  for (int q0 = 0; q0 < p.ws_P; q0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = q0 + q < p.ws_P ? part[(int64_t)(q0 + q) * GB_M * GB_N] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (q0 + q < p.ws_P) acc += v[q];
+  }
+  st.C[(int64_t)m * st.ldc + n] = acc;
 }
 
 // The routing-weight gradient of each routed row: its partials summed in ascending order, to
@@ -541,15 +622,43 @@ constexpr size_t kAl = 256;
 size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
 struct BwdLayout {
-  size_t counts, offsets, route_ids, blk_counts, err;
+  size_t counts, offsets, route_ids, blk_counts, err, ws_part, ws_split;
   size_t Ar, dPr, dGr, dUr, Hr, dGo, dUo, Ho, Dr, Do, dwp;
   size_t t_rec, t_dd, t_du, t_wg, total;
   int64_t cap;
   int ldp;                       // routing-weight-gradient partials per routed row
   int64_t tiles_rec, tiles_dd, tiles_du, tiles_wg;
+  int ws_kept, ws_r, ws_P, ws_plen;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The wgrad launch's tile count is fixed by the shapes: 3 E_l routed groups of
+// ceil(I/256) x ceil(d/256) tiles (every expert, rows or not), then the shared experts'. The
+// persistent grid runs 256 tiles a window, so when the last window holds only r < 256 tiles and
+// they are shared-expert tiles of K = T_own, r workgroups would run them alone (with EP1's
+// 8,192 own tokens ~0.2 ms). Those r tiles are split instead into P K pieces each (P r <= 256,
+// pieces of >= 256 rows), which fill one window, and summed afterwards.
+void wgrad_split(const mok_moe_bwd_args* a, BwdLayout& L) {
+  L.ws_kept = -1;
+  L.ws_r = L.ws_P = L.ws_plen = 0;
+  if (a->n_shared <= 0 || a->T_own < 512) return;
+  const int64_t d = a->d, I = a->I, Ish = (int64_t)a->n_shared * a->I_shared;
+  const int64_t sh = 2 * cdiv(Ish, GB_M) * cdiv(d, GB_N) +
+                     (int64_t)a->n_shared * cdiv(d, GB_M) * cdiv(a->I_shared, GB_N);
+  const int64_t total = 3 * (int64_t)a->E_l * cdiv(I, GB_M) * cdiv(d, GB_N) + sh;
+  const int64_t r = total % 256;
+  if (r == 0 || r > sh) return;
+  int64_t P = std::min<int64_t>(256 / r, a->T_own / 256);
+  if (P < 2) return;
+  const int64_t plen = cdiv(cdiv(a->T_own, P), GB_K) * GB_K;
+  P = cdiv(a->T_own, plen);
+  if (P < 2) return;
+  L.ws_kept = (int)(sh - r);
+  L.ws_r = (int)r;
+  L.ws_P = (int)P;
+  L.ws_plen = (int)plen;
+}
 
 int validate_bwd(const mok_moe_bwd_args* a) {
   if (!a) return MOK_EINVAL;
@@ -602,9 +711,12 @@ BwdLayout layout_bwd(const mok_moe_bwd_args* a) {
   const int64_t Io = std::max<int64_t>(1, Ish);
   L.dGo = take(2 * To * Io); L.dUo = take(2 * To * Io); L.Ho = take(2 * To * Io);
   L.Do = take(4 * To * Io);
+  wgrad_split(a, L);
+  L.ws_part = take(4 * (size_t)L.ws_r * L.ws_P * GB_M * GB_N);
+  L.ws_split = take(sizeof(SplitTile) * (size_t)L.ws_r);
   const int ng = 3 * a->E_l + 2 + a->n_shared + 2;
   L.t_rec = take(gtable_bytes(ng)); L.t_dd = take(gtable_bytes(ng)); L.t_du = take(gtable_bytes(ng));
-  L.t_wg = take(gtable_bytes(ng));
+  L.t_wg = take(gtable_bytes(ng + L.ws_r * L.ws_P));
   L.total = off;
   // upper bounds of each launch's tiles (the device fills in the exact counts)
   const int64_t mt_r = cdiv(cap, GB_M) + a->E_l, mt_o = cdiv(a->T_own, GB_M);
@@ -613,7 +725,8 @@ BwdLayout layout_bwd(const mok_moe_bwd_args* a) {
   L.tiles_du = (mt_r + mt_o) * cdiv(d, GB_N);
   L.tiles_wg = (int64_t)a->E_l * (2 * cdiv(I, GB_M) * cdiv(d, GB_N) + cdiv(d, GB_M) * cdiv(I, GB_N)) +
                2 * cdiv(Ish, GB_M) * cdiv(d, GB_N) +
-               (int64_t)a->n_shared * cdiv(d, GB_M) * cdiv(a->I_shared, GB_N);
+               (int64_t)a->n_shared * cdiv(d, GB_M) * cdiv(a->I_shared, GB_N) +
+               (int64_t)L.ws_r * (L.ws_P - 1);
   return L;
 }
 
@@ -659,6 +772,8 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   p.t_rec = (int32_t*)at(L.t_rec); p.t_dd = (int32_t*)at(L.t_dd); p.t_du = (int32_t*)at(L.t_du);
   p.t_wg = (int32_t*)at(L.t_wg);
   p.err = (int32_t*)at(L.err);
+  p.ws_kept = L.ws_kept; p.ws_P = L.ws_P; p.ws_plen = L.ws_plen;
+  p.ws_part = (float*)at(L.ws_part); p.ws_split = (SplitTile*)at(L.ws_split);
   const int64_t worst = a->T_pool * (int64_t)std::min(a->k, a->E_l);
   // the plan (also yields route_ids for the gathers), then the rows in plan order
   if (launch_plan(a->topk_idx, a->T_pool, a->k, a->e0, a->E_l, a->tokens_per_rank,
@@ -686,6 +801,9 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   gg(k_ggemm<false, false, true>, p.t_rec, L.tiles_rec);   // G, U; SwiGLU backward
   gg(k_ggemm<false, true, false>, p.t_du, L.tiles_du);     // dx = dG Wg + dU Wu
   gg(k_ggemm<true, true, false>, p.t_wg, L.tiles_wg);      // dWg, dWu, dWd (+ shared)
+  if (L.ws_r > 0)
+    launch_k(k_bwd_split_sum, dim3((unsigned)L.ws_r, GB_M), dim3(256), 0, s, nullptr,
+             nullptr, p);
   if (L.cap > 0 && a->dtopk_w)
     launch_k(k_bwd_dtopk, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0, s, nullptr, nullptr,
              p, a->dtopk_w);

@@ -139,3 +139,27 @@ def test_backward_full_ep1_layer():
     cpu, idx, w = _routing(wl, inp)
     b, kw = _run(wl, inp, idx, w)
     _compare(wl, b, kw, cpu, idx, w)
+
+
+def test_backward_wgrad_tail_split_matches_oracle():
+    """A layer whose weight-gradient launch ends in a partial window of shared-expert tiles:
+    80 experts x 3 one-tile gradients + 24 shared tiles = 264 tiles, so the last 8 (K = 1,024
+    own tokens) are computed as 4 K pieces each and summed. Every gradient against the oracle,
+    and reruns bit-identical."""
+    wl = synth.scaled(synth.WORKLOADS[synth.EP1], name="bwd_split", T_pool=1024, d=256, E=80,
+                      k=2, I=128, E_l=80, tokens_per_rank=1024, T_own=1024, n_shared=2,
+                      I_shared=1024)
+    cdiv = lambda a, b: -(-a // b)
+    sh = (2 * cdiv(wl.n_shared * wl.I_shared, 256) * cdiv(wl.d, 256)
+          + wl.n_shared * cdiv(wl.d, 256) * cdiv(wl.I_shared, 256))
+    total = 3 * wl.E_l * cdiv(wl.I, 256) * cdiv(wl.d, 256) + sh
+    assert (sh, total % 256) == (24, 8)          # the split applies: 8 <= 24 shared tiles
+    inp = make_inputs(wl, DEV)
+    cpu, idx, w = _routing(wl, inp)
+    b, kw = _run(wl, inp, idx, w)
+    _compare(wl, b, kw, cpu, idx, w)
+    first = [t.clone() for t in (b.dws_gate, b.dws_up, b.dws_down)]
+    b.backward()
+    torch.cuda.synchronize()
+    for a, c in zip((b.dws_gate, b.dws_up, b.dws_down), first):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32))
