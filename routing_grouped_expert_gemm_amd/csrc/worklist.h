@@ -108,11 +108,12 @@ constexpr int WL_LDS_INTS = 160 + 19 * (WL_MBL + 1);
 // (rows ascending within each plan region), then the shared experts' minibatches over the own
 // tokens. Every count comes from the plan on the device; nothing returns to the host.
 //
-// Ring order (ring): block b holds the gather items of minibatch b (MX only), its up tiles,
-// then the down tiles of minibatch b - lag. A down item needs every up tile of its minibatch;
+// Ring order (ring): block b holds the gather items of minibatch b + 1 (MX only; b itself with
+// a single slot), the up tiles of b, then the down tiles of minibatch b - lag; the first
+// minibatch's gather items open the order. A down item needs every up tile of its minibatch;
 // an up item needs its gather items and the down items of the minibatch that used its ring
-// slot before it; a gather item needs that minibatch's up items. With lag < slots every
-// dependency of an item lies earlier in this order.
+// slot before it; a gather item needs that previous minibatch's up items. With lag < slots and
+// the gather lead < slots every dependency of an item lies earlier in this order.
 //
 // With at least 8 slots the ring is split by XCD: XCD x runs minibatches x, x + 8, x + 16, ...
 // on its own slots (n_slots / 8 of them, lag half of that) in the order above. A slot's
@@ -383,11 +384,14 @@ MOK_DEV void build_worklist(const WlBuild& P, const int32_t* cnt, const int32_t*
     slot[m] = s0 + j % S;
     prev[m] = j >= S ? m - mstep * S : -1;
     if (P.ring) {
-      // block j of the XCD's order: gather items of j, up tiles of j, down tiles of j - L
-      const int pp = pb + j, pl = pb + max(0, j - L), pa = pb + min(j + L + 1, nx);
-      const int32_t pos_g = pg[pp] + pu[pp] + pd[pl];
-      const int32_t pos_u = pg[pp + 1] + pu[pp] + pd[pl];
-      const int32_t pos_d = pg[pa] + pu[pa] + pd[pp];
+      // block b of the XCD's order: gather items of b + G, up tiles of b, down tiles of b - L
+      // (G = 1 with two or more slots: a minibatch's rows are quantised a block before its up
+      // tiles need them; the first minibatch's gather items open the order)
+      const int G = S >= 2 ? 1 : 0;
+      auto at = [&](int i) { return pb + min(max(i, 0), nx); };
+      const int32_t pos_g = pg[at(j)] + pu[at(j - G)] + pd[at(j - G - L)];
+      const int32_t pos_u = pg[at(j + G + 1)] + pu[at(j)] + pd[at(j - L)];
+      const int32_t pos_d = pg[at(j + L + G + 1)] + pu[at(j + L + 1)] + pd[at(j)];
       for (int l = 0; l < ng; ++l) { int4 e = ent; e.y = (KIND_G << KIND_SHIFT) | l; rt[pos_g + l] = e; }
       for (int l = 0; l < nu; ++l) { int4 e = ent; e.y = (KIND_U << KIND_SHIFT) | l; rt[pos_u + l] = e; }
       for (int l = 0; l < nd; ++l) { int4 e = ent; e.y = (KIND_D << KIND_SHIFT) | l; rt[pos_d + l] = e; }

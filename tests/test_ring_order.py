@@ -35,15 +35,17 @@ def layout(nu, nd, ng, n_slots):
             S, s0, j, pb, nx, step = n_slots // N_XCD, x * (n_slots // N_XCD), m // N_XCD, base[x], n_of(x), N_XCD
         owner[m] = m % N_XCD if affine else 0
         L = S // 2 if S >= 2 else 0
+        G = 1 if S >= 2 else 0            # gather items run one block ahead of their up tiles
         slot[m] = s0 + j % S
         prev[m] = m - step * S if j >= S else -1
-        p, pl, pa = pb + j, pb + max(0, j - L), pb + min(j + L + 1, nx)
+        # block b of the XCD's order: gather items of b + G, up tiles of b, down tiles of b - L
+        at = lambda i: pb + min(max(i, 0), nx)
         for l in range(ng[m]):
-            pos[("G", m, l)] = pg[p] + pu[p] + pd[pl] + l
+            pos[("G", m, l)] = pg[at(j)] + pu[at(j - G)] + pd[at(j - G - L)] + l
         for l in range(nu[m]):
-            pos[("U", m, l)] = pg[p + 1] + pu[p] + pd[pl] + l
+            pos[("U", m, l)] = pg[at(j + G + 1)] + pu[at(j)] + pd[at(j - L)] + l
         for l in range(nd[m]):
-            pos[("D", m, l)] = pg[pa] + pu[pa] + pd[p] + l
+            pos[("D", m, l)] = pg[at(j + L + G + 1)] + pu[at(j + L + 1)] + pd[at(j)] + l
     return dict(pos=pos, slot=slot, prev=prev, owner=owner, xb=xb, xr=xr, affine=affine,
                 total=pg[n] + pu[n] + pd[n])
 
