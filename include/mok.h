@@ -344,6 +344,14 @@ int mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int32_t K, uint8_t* c
 int mok_quantize_mxfp4(const void* src_bf16, int64_t rows, int32_t K, uint8_t* codes,
                        uint8_t* scales, void* stream);
 
+/* The same two quantisers for float32 rows (src [rows, K] float32, device; K % 32 == 0),
+ * through the device code the gate/up epilogue uses to encode H from its float32 values: the
+ * MX forward's H codes follow exactly these rules. Same outputs, layouts and errors. */
+int mok_quantize_mxfp8_f32(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                           uint8_t* scales, void* stream);
+int mok_quantize_mxfp4_f32(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                           uint8_t* scales, void* stream);
+
 /* ---------------------------------------------------------------- device error word
  * The persistent work loop bounds every wait; a wait that runs out sets a nonzero error word
  * in the workspace and the loop exits. This SYNCHRONOUS call waits for `stream`, then reads

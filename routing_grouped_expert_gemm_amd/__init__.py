@@ -6,7 +6,8 @@ loudly (ImportError) if it has not been built: there is no fallback of any kind.
 
 Entry points carry the C names: mok_route, mok_topk, mok_dispatch_plan,
 mok_dispatch_plan_workspace_bytes, mok_moe_workspace_bytes, mok_moe_forward,
-mok_quantize_mxfp8, mok_get_device_error, mok_status_string, mok_version.
+mok_quantize_mxfp8, mok_quantize_mxfp8_f32, mok_quantize_mxfp4_f32, mok_get_device_error,
+mok_status_string, mok_version.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ EXPORTS = ["mok_status_string", "mok_version", "mok_route", "mok_topk",
            "mok_moe_forward", "mok_moe_workspace_region", "mok_moe_backward",
            "mok_moe_backward_workspace_bytes", "mok_moe_backward_error", "mok_pull_gather",
            "mok_push_dispatch", "mok_quantize_mxfp8", "mok_quantize_mxfp4",
-           "mok_get_device_error"]
+           "mok_quantize_mxfp8_f32", "mok_quantize_mxfp4_f32", "mok_get_device_error"]
 
 
 class MokError(RuntimeError):
@@ -107,6 +108,8 @@ _lib.mok_moe_backward_error.argtypes = [_P, ctypes.POINTER(BwdArgs), ctypes.POIN
                                         _P]
 _lib.mok_quantize_mxfp8.argtypes = [_P, _I64, _I32, _P, _P, _P]
 _lib.mok_quantize_mxfp4.argtypes = [_P, _I64, _I32, _P, _P, _P]
+_lib.mok_quantize_mxfp8_f32.argtypes = [_P, _I64, _I32, _P, _P, _P]
+_lib.mok_quantize_mxfp4_f32.argtypes = [_P, _I64, _I32, _P, _P, _P]
 _lib.mok_pull_gather.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _I32, _P, _P]
 _lib.mok_push_dispatch.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _I32, _I32, _I64, _P, _P, _P,
                                    _P]
@@ -238,6 +241,20 @@ def mok_quantize_mxfp4(src_bf16, codes, scales, stream=None) -> None:
     rows, K = src_bf16.shape
     _check("mok_quantize_mxfp4", _lib.mok_quantize_mxfp4(_ptr(src_bf16), rows, K, _ptr(codes),
                                                          _ptr(scales), _stream(stream)))
+
+
+def mok_quantize_mxfp8_f32(src_f32, codes, scales, stream=None) -> None:
+    """MXFP8 of float32 rows: codes [rows, K], scales [rows, K/32]."""
+    rows, K = src_f32.shape
+    _check("mok_quantize_mxfp8_f32", _lib.mok_quantize_mxfp8_f32(
+        _ptr(src_f32), rows, K, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def mok_quantize_mxfp4_f32(src_f32, codes, scales, stream=None) -> None:
+    """MXFP4 of float32 rows: codes [rows, K/2], scales [rows, K/32]."""
+    rows, K = src_f32.shape
+    _check("mok_quantize_mxfp4_f32", _lib.mok_quantize_mxfp4_f32(
+        _ptr(src_f32), rows, K, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def mok_get_device_error(workspace, stream=None) -> int:

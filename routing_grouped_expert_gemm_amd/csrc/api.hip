@@ -412,6 +412,22 @@ int mok_quantize_mxfp4(const void* src_bf16, int64_t rows, int32_t K, uint8_t* c
                                       (hipStream_t)stream));
 }
 
+int mok_quantize_mxfp8_f32(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOK_EINVAL;
+  if (rows == 0) return MOK_OK;
+  if (!src || !codes || !scales) return MOK_EINVAL;
+  return status_of(launch_quantize_mx_f32(src, rows, K, codes, scales, false, (hipStream_t)stream));
+}
+
+int mok_quantize_mxfp4_f32(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOK_EINVAL;
+  if (rows == 0) return MOK_OK;
+  if (!src || !codes || !scales) return MOK_EINVAL;
+  return status_of(launch_quantize_mx_f32(src, rows, K, codes, scales, true, (hipStream_t)stream));
+}
+
 int mok_get_device_error(const void* workspace, uint32_t* err, void* stream) {
   if (!workspace || !err) return MOK_EINVAL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOK_EHIP;

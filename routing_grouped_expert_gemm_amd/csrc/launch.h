@@ -53,6 +53,9 @@ __host__ __device__ inline int64_t mx_kmajor_scale(int64_t r, int b, int64_t R) 
 hipError_t launch_quantize_mx(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
                               uint8_t* scales, bool fp4, hipStream_t s, hipEvent_t e0 = nullptr,
                               hipEvent_t e1 = nullptr, int64_t scales_kmajor = 0);
+// The same rules for float32 rows (row-major scales), with the H epilogue's encoders.
+hipError_t launch_quantize_mx_f32(const float* src, int64_t rows, int K, uint8_t* codes,
+                                  uint8_t* scales, bool fp4, hipStream_t s);
 
 // Operand element type of the expert GEMMs.
 enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2, FP4 = 3 };

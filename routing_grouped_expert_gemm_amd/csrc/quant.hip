@@ -71,6 +71,52 @@ __global__ __launch_bounds__(256) void k_quantize_mx(const bf16_t* __restrict__ 
   }
 }
 
+// Float32 rows, row-major scales: the encoders the gate/up epilogue applies to H in float32
+// (quantize_quad8_f32, mx4_quad8_f32), four lanes a 32-element block, 8 elements a lane.
+template <bool FP4>
+__global__ __launch_bounds__(256) void k_quantize_mx_f32(const float* __restrict__ src, int64_t rows,
+                                                         int K, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+  const int64_t n_chunks = rows * (K / 8);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t n_iter = (n_chunks + stride - 1) / stride;   // the same for every lane
+  int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (int64_t it = 0; it < n_iter; ++it, q += stride) {
+    const bool ok = q < n_chunks;
+    const int64_t at = q * 8;
+    float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (ok) {
+      const float4 a = *(const float4*)(src + at), b = *(const float4*)(src + at + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    int sh;
+    if constexpr (FP4) {
+      const uint32_t c = mx4_quad8_f32(v, &sh);
+      if (ok) *(uint32_t*)(codes + at / 2) = c;
+    } else {
+      const uint2 c = quantize_quad8_f32(v, &sh);
+      if (ok) *(uint2*)(codes + at) = c;
+    }
+    if (ok && (q & 3) == 0) scales[at >> 5] = (uint8_t)(sh + 127);
+  }
+}
+
+hipError_t launch_quantize_mx_f32(const float* src, int64_t rows, int K, uint8_t* codes,
+                                  uint8_t* scales, bool fp4, hipStream_t s) {
+  const int64_t n_chunks = rows * (K / 8);
+  if (n_chunks == 0) return hipSuccess;
+  const int64_t want = (n_chunks + 255) / 256;
+  const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
+  if (fp4)
+    launch_k(k_quantize_mx_f32<true>, dim3(grid), dim3(256), 0, s, nullptr, nullptr, src, rows, K,
+             codes, scales);
+  else
+    launch_k(k_quantize_mx_f32<false>, dim3(grid), dim3(256), 0, s, nullptr, nullptr, src, rows, K,
+             codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_mx(const void* src_bf16, int64_t rows, int K, uint8_t* codes,
                               uint8_t* scales, bool fp4, hipStream_t s, hipEvent_t e0,
                               hipEvent_t e1, int64_t scales_kmajor) {

@@ -179,6 +179,57 @@ def test_quantize_mxfp4_exhaustive_bf16_patterns():
     assert np.array_equal(to_np(codes), rc)
 
 
+def _f32_rounding_sweep(fp4, rows=1024, K=256, seed=23):
+    """float32 blocks whose elements sit on, and a few ulps either side of, the midpoints of the
+    E2M1 (fp4) or E4M3 grid after scaling, plus saturating values, zeros, signs and denormals.
+    Each 32-element block gets its own shared exponent (its largest magnitude is fixed first)."""
+    rng = np.random.default_rng(seed)
+    if fp4:
+        grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+        top, emax = 7.0, 2                           # |v| 2^-s < 8 = 2^(emax + 1)
+    else:
+        grid = np.unique(np.concatenate([np.arange(8) * 2.0 ** -9] +
+                                        [np.arange(8, 16) * 2.0 ** (e - 3) for e in range(-6, 9)]))
+        grid = grid[grid <= 448]
+        top, emax = 500.0, 8
+    mids = (grid[1:] + grid[:-1]) / 2
+    out = np.empty((rows, K), np.float32)
+    for r in range(rows):
+        for b in range(K // 32):
+            s = int(rng.integers(-60, 60))
+            y = rng.choice(np.concatenate([mids, grid, [top, 6.5 if fp4 else 460.0]]), 32)
+            y = y.astype(np.float32)
+            ulps = rng.integers(-3, 4, 32).astype(np.int32)
+            y = (y.view(np.int32) + np.where(y > 0, ulps, 0)).view(np.float32)
+            y[0] = np.float32(top)                   # fixes the block's shared exponent
+            v = np.ldexp(y.astype(np.float64), s).astype(np.float32)
+            v *= np.where(rng.random(32) < 0.5, -1, 1).astype(np.float32)
+            out[r, 32 * b:32 * b + 32] = v
+    out[::9, 7] = 0.0
+    out[::11, 9] = -0.0
+    out[5, :32] = np.float32(1e-42)                  # denormal block
+    out[6, :32] = rng.standard_normal(32).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_quantize_mx_f32_rounding_boundaries(fp4):
+    """mok_quantize_mxfp{8,4}_f32 (the H epilogue's encoders) on float32 values at and next to
+    every rounding midpoint of the element grid, bit-exact against the oracle's codes and
+    scales."""
+    import routing_grouped_expert_gemm_amd as mok
+    f = _f32_rounding_sweep(fp4)
+    src = torch.from_numpy(f).to(DEV)
+    rows, K = f.shape
+    codes = torch.empty((rows, K // 2 if fp4 else K), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=DEV)
+    (mok.mok_quantize_mxfp4_f32 if fp4 else mok.mok_quantize_mxfp8_f32)(src, codes, scales)
+    _sync()
+    rc, rs = (oracle.mxfp4_quantize if fp4 else oracle.mxfp8_quantize)(f)
+    assert np.array_equal(to_np(scales), rs)
+    assert np.array_equal(to_np(codes), rc)
+
+
 # --------------------------------------------------------------------- layer, small sizes
 
 SMALL = {
