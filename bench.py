@@ -11,7 +11,8 @@ Default run: the headline is the EP=1 bf16 layer (T=8192, d=2048, 64 experts, to
 stage-ordered expert launches; the same line carries
   "ring":  that layer with the persistent ring work loop (the library default), and
   "mxfp8": the MXFP8 EP=64 share (262144-row pool, d=7168, 4 local experts + 1 shared),
-  "mxfp4": the same share with MXFP4 operands, and
+  "mxfp4": the same share with MXFP4 operands (each with a "ring" object: the ring work loop,
+           whose items include the row gather and quantisation), and
   "backward": the EP=1 layer's backward (mok_moe_backward), and
   "dispatch": pull gather against the push baseline on that share's routing,
 each timed the same way (W warm-up steps, K timed steps between device synchronisations).
@@ -885,6 +886,12 @@ def main():
         out["mxfp8"] = {k: m[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                           "routed_rows", "routed_tflops", "gemm_tflops",
                                           "stage_ms", "roofline", "hbm")}
+        # ... and with the ring work loop (gather items inside the loop)
+        mr, i3 = measure(synth.WORKLOADS[synth.EP64_MX], True, args.steps, args.warmup)
+        del i3
+        torch.cuda.empty_cache()
+        out["mxfp8"]["ring"] = {k: mr[k] for k in ("value", "ms_per_step", "routed_tflops",
+                                                   "config", "roofline")}
         # the same share with MXFP4 operands
         m4, i4 = measure(synth.WORKLOADS[synth.EP64_MX4], False, args.steps, args.warmup)
         del i4
@@ -892,6 +899,11 @@ def main():
         out["mxfp4"] = {k: m4[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                            "routed_rows", "routed_tflops", "gemm_tflops",
                                            "stage_ms", "roofline", "hbm")}
+        m4r, i4 = measure(synth.WORKLOADS[synth.EP64_MX4], True, args.steps, args.warmup)
+        del i4
+        torch.cuda.empty_cache()
+        out["mxfp4"]["ring"] = {k: m4r[k] for k in ("value", "ms_per_step", "routed_tflops",
+                                                    "config", "roofline")}
         # the backward of the headline layer
         out["backward"] = measure_backward(min(args.steps, 10), min(args.warmup, 3))
         torch.cuda.empty_cache()
