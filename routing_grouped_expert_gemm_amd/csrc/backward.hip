@@ -22,6 +22,7 @@
 // read along their output dimension); a transposed tile is kept in LDS as it lies in memory and
 // gfx950's transposing LDS read turns it into the MFMA's K-contiguous fragments.
 #include <algorithm>
+#include <utility>
 
 #include "device_common.h"
 #include "launch.h"
@@ -159,7 +160,20 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
   };
   if (threadIdx.x == 0) g_sh[0] = find(b);
   __syncthreads();
-  GGroup g = G[uniform(g_sh[0])];
+  // a tile's descriptor is read with scalar loads (constant address space, uniform index): a
+  // vector load would count in vmcnt, and waiting for it would wait for every DMA and store
+  // issued before it
+  auto load_group = [&](int q) {
+    static_assert(sizeof(GGroup) % 8 == 0, "whole 8-byte words");
+    typedef const __attribute__((address_space(4))) uint64_t* WordsC;
+    const WordsC w = (WordsC)(G + q);
+    GGroup r;
+    uint64_t* d = (uint64_t*)&r;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(GGroup) / 8); ++i) d[i] = w[i];
+    return r;
+  };
+  GGroup g = load_group(uniform(g_sh[0]));
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1, h = lane >> 5;
   constexpr int FM = 4, FN = 4;
@@ -209,6 +223,20 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
     __builtin_amdgcn_s_waitcnt(0x70);   // vmcnt(0) lgkmcnt(0) (gfx9 encoding, expcnt left at 7)
     lds_barrier();
   };
+  // the same, but the last N vector-memory operations this wave issued may still be in flight
+  // (vmcnt counts in issue order): a barrier for a DMA that N younger operations follow
+  auto barrier_n = [&](auto N_) {
+    constexpr int N = decltype(N_)::value;
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));   // lgkmcnt(0)
+    lds_barrier();
+  };
+  // Plain products: of a tile's 64 stores (16 bytes of float32 or 8 of bf16 a lane each), the
+  // first ST_A go out before the next tile's first two K steps and the other ST_B after them, so
+  // that the next tile's first barrier waits for its step-0 DMA and ST_A stores only (ST_B + 16
+  // younger operations: at most vmcnt's 63).
+  constexpr int ST_A = 17, ST_B = FM * FN * 4 - ST_A;
+  static_assert(ST_B + 2 * GB_DMA == 63, "vmcnt range");
+  bool tail_st = false;                 // the previous tile left ST_B stores behind its head
   int m0, n0;
   origin(g, b, m0, n0);
   issue_head(g, m0, n0);
@@ -224,21 +252,8 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-      // SwiGLU: the routing weight of the lane's row in each block row; bf16 output: its output
-    // row (both loaded under the K loop)
     float wrow[FM];
     int32_t orow[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * 128 + 32 * i + (lane & 31);
-      wrow[i] = 1.0f;
-      orow[i] = m;
-      if constexpr (SWIGLU) {
-        if (g.rid && m < g.M) wrow[i] = g.w[g.rid[m]];
-      } else {
-        if (g.rmap && m < g.M) orow[i] = g.rmap[m];
-      }
-    }
     bf16x8_t fa[2][FM], fb[2][FN];
     // fragments of K sub-step s of step kt into slot f; K values past a ragged end zeroed
     auto frags = [&](int kt, int s, int f) {
@@ -287,9 +302,34 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
     // them, they would sit ahead of s's own reads in the LDS counter (which tracks 15), and the
     // first MFMA would wait for most of both sub-steps' reads.
     constexpr int NEXT_AT = 8;
-    barrier_x();                                // X(0)
+    // X(0): step 0 has landed; younger in flight: step 1's DMA and the previous tile's ST_B
+    // stores (a count below the true one only waits longer)
+    const bool two = nk > 1;
+    if (tail_st) {
+      if (two) barrier_n(std::integral_constant<int, 2 * GB_DMA + ST_B>{});
+      else barrier_n(std::integral_constant<int, ST_B>{});
+    } else {
+      if (two) barrier_n(std::integral_constant<int, 2 * GB_DMA>{});
+      else barrier_x();
+    }
+    // SwiGLU: the routing weight of the lane's row in each block row; bf16 output: its output
+    // row (both loaded under the K loop, after X(0), so that no wait above counts them)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * 128 + 32 * i + (lane & 31);
+      wrow[i] = 1.0f;
+      orow[i] = m;
+      if constexpr (SWIGLU) {
+        if (g.rid && m < g.M) {                  // global loads: a flat one would also count in
+          const int32_t r = *(const __attribute__((address_space(1))) int32_t*)(g.rid + m);
+          wrow[i] = *(const __attribute__((address_space(1))) float*)(g.w + r);   // the LDS counter
+        }
+      } else {
+        if (g.rmap && m < g.M) orow[i] = *(const __attribute__((address_space(1))) int32_t*)(g.rmap + m);
+      }
+    }
     GGroup gn = g;
-    if (more) gn = G[uniform(g_sh[(it + 1) & 1])];
+    if (more) gn = load_group(uniform(g_sh[(it + 1) & 1]));
     if (nk > 0) frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
@@ -298,7 +338,10 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
           if (n == NEXT_AT - 1) frags(kt, s + 1, (s + 1) & 1);
         });
       const bool next = kt + 1 < nk, more2 = kt + 2 < nk;
-      if (next) barrier_x();                    // X(kt + 1)
+      if (next) {                               // X(kt + 1)
+        if (kt == 0 && tail_st) barrier_n(std::integral_constant<int, ST_B>{});
+        else barrier_x();
+      }
       mfmas(1, [&](int n) {
         if (more2) issue_q(g, m0, n0, kt + 2, kt & 1, n);
         if (next && n == NEXT_AT - 1) frags(kt + 1, 0, 0);
@@ -310,35 +353,43 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
     if (more) {
       origin(gn, bn, m0n, n0n);
       barrier_x();                              // every wave is done with both buffers
-      issue_head(gn, m0n, n0n);
     }
     // lane (h, l32) of block (i, j): row m0 + wm*128 + 32 i + l32, columns n0 + wn*128 + 32 j +
     // 8 q + 4 h + [0, 4) in values 4q .. 4q + 3 (the B fragment is the MFMA's first operand)
     typedef float f32x4v __attribute__((ext_vector_type(4)));
     const int l32 = lane & 31;
     if constexpr (!SWIGLU) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      // store t = 16 i + 4 j + q; every one is issued (one past the matrix goes to the table
+      // header's spare words), so the counts above are exact
+      char* trash = (char*)(const_cast<int32_t*>(table) + 8);
+      auto store = [&](int t) {
+        const int i = t / 16, j = (t / 4) % 4, q = t % 4;
         const int m = m0 + wm * 128 + 32 * i + l32;
-        if (m >= g.M) continue;
-        float* crow = g.C + (int64_t)m * g.ldc;
-        bf16_t* brow = g.Cb + (int64_t)orow[i] * g.ldc;
+        const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * h;
+        const bool ok = m < g.M && n < g.N;
+        f32x4v o;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int r = 0; r < 4; ++r) o[r] = acc[i][j][4 * q + r];
+        // global (not flat) stores: a flat store would also count in the LDS counter, which
+        // every fragment read waits on
+        if (g.Cb) {
+          bf16_t* dst = g.Cb + (int64_t)orow[i] * g.ldc + n;
+          typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+          const u32x2v v2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *(__attribute__((address_space(1))) u32x2v*)(ok ? (char*)dst : trash) = v2;
+        } else {
+          float* dst = g.C + (int64_t)m * g.ldc + n;
+          *(__attribute__((address_space(1))) f32x4v*)(ok ? (char*)dst : trash) = o;
+        }
+      };
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * h;
-            if (n >= g.N) continue;
-            f32x4v o;
+      for (int t = 0; t < ST_A; ++t) store(t);
+      if (more) issue_head(gn, m0n, n0n);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = acc[i][j][4 * q + r];
-            if (g.Cb)
-              *(uint2*)(brow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-            else
-              *(f32x4v*)(crow + n) = o;
-          }
-      }
+      for (int t = ST_A; t < ST_A + ST_B; ++t) store(t);
+      tail_st = more;
     } else {
+      if (more) issue_head(gn, m0n, n0n);
       // SwiGLU backward of the wave's 64 output columns (blocks j = 0, 1: G; j + 2: U, the same
       // columns): H = silu(G) U, dH = w D, dG = dH U silu'(G), dU = dH silu(G), and the row's
       // partial <D, H> over these columns (fixed order: the lane's 32 values, then its h pair).
