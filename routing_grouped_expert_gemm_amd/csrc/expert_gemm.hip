@@ -245,10 +245,11 @@ MOK_DEV void route_rows(const ExpertPass& p, int32_t (&r)[C::A_SLABS]) {
 // One tile. slot: the ring slot of the entry's minibatch. pre (routed gate/up tiles of the
 // bf16 / float32 path): the pool rows of the tile's A slabs (prefetch_a_rows, route_rows).
 // after_step(s) runs after the barrier of K steps s = 0 .. 3 (for shorter K loops, the missing
-// ones run after the loop): there every vector load issued before the step's DMA has landed.
-// The stage kernel fetches the next tile's entry, slot and A rows over steps 0 .. 2 and parks
-// the rows in LDS, so they hold no register across the K loop; the ring loop fetches its next
-// item over steps 0 .. 3.
+// ones run after the loop): there every vector load issued before the step's DMA has landed;
+// after_step(-1) runs before the tile's first DMA. The stage kernel fetches the next tile's
+// entry there (a scalar load, which the first barrier waits for with the DMA), and its slot and
+// A rows over steps 1 .. 2, and parks the rows in LDS, so they hold no register across the K
+// loop; the ring loop fetches its next item over steps 0 .. 3.
 template <Elem EL, bool UP, bool F32OUT, class C, bool RING = false, class F>
 MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, const int slot,
                       const int32_t (&pre)[C::A_SLABS], F&& after_step) {
@@ -287,7 +288,11 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
   auto blk_row = [&](int i) { return wm * WM + 32 * i; };   // first tile row of block row i
-  const int K = UP ? p.d : (shared ? p.I_sh : p.I);
+  // K from the kernarg segment per tile: hoisted out of the tile loop, its "nk > 0" and
+  // "nk > 1" flags were spilled to scratch, and their reload's wait held the first DMA back
+  // until the previous epilogue's stores had drained
+  const int K = UP ? kernarg_field<int>(offsetof(ExpertPass, d))
+                 : (shared ? kernarg_field<int>(offsetof(ExpertPass, I_sh)) : kernarg_field<int>(offsetof(ExpertPass, I)));
   const int N = UP ? (shared ? p.I_sh : p.I) : p.d;   // output columns of the stage
   const int nk = K / KT;
   // global byte of lane L's chunk in slab q: slot L % CH of row RPI*q + L / CH (+ RA or RB * w)
@@ -614,6 +619,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     // finishing the DMA of step kt + 1), then X(kt + 1), the reads of step kt + 1's sub-step 0,
     // and the E phase (the last sub-step of kt, starting the DMA of step kt + 2 into the buffer
     // kt just released). The steady state is unrolled by 2 so every buffer's role is static.
+    after_step(-1);
     if (nk > 0) {
 #pragma unroll
       for (int q = 0; q < DMA_PER_STEP; ++q) issue_one(step_addr(0), sm.buf[0], q);
@@ -665,6 +671,7 @@ MOK_DEV void run_tile(const ExpertPass& p, const Lds<C>& sm, const int4 entry, c
     // (later steps' DMAs stay in flight), barrier (every wave's DMA of kt landed; every wave
     // done computing kt - 1), issue step kt + ST - 1 into the buffer kt - 1 used, compute kt.
     // The steady state is unrolled by ST so every buffer's role is static.
+    after_step(-1);
 #pragma unroll
     for (int q = 0; q < ST - 1; ++q)
       if (q < nk) issue_all(q, sm.buf[q]);
@@ -909,9 +916,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
   for (;;) {
     const int32_t tn = t + G;
     const bool more = tn < total;
-    // The next tile's entry (step 0), its slot and route ids (step 1) and their pool rows (step
-    // 2) are fetched under this tile's first K steps, each from values that landed by that
-    // step's barrier, so the next prologue waits on no global load. The epilogue's barrier
+    // The next tile's entry (before the first DMA), its slot and route ids (step 1) and their
+    // pool rows (step 2) are fetched under this tile's first K steps, each from values that
+    // landed by that step's barrier, so the next prologue waits on no global load. The epilogue's barrier
     // orders the LDS writes before the reads below; the next tile's first barriers order those
     // reads before the next writes.
     int4 nxt = cur;
@@ -919,8 +926,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_expert_stage(ExpertPass p) {
     int32_t pn[C::A_SLABS];
     run_tile<EL, UP, F32OUT, C>(p, sm, cur, slot, pre, [&](int s) {
       if (!more) return;
-      if (s == 0) {
-        nxt = tab[tn];
+      if (s < 0) {                              // the entry: scalar loads (uniform index)
+        const __attribute__((address_space(4))) int32_t* tc = (const __attribute__((address_space(4))) int32_t*)(tab + tn);
+        nxt = make_int4(tc[0], tc[1], tc[2], tc[3]);
       } else if (s == 1) {
         nslot = wl_slot(p.wl, cap)[nxt.x];
         if constexpr (PRE) prefetch_a_rows<EL, UP, C>(p, nxt, pn);
@@ -1266,6 +1274,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
     int32_t* ctr = kind == KIND_U ? done_u : (kind == KIND_D ? done_d : done_g);
     // after the first K-step barrier of a tile every wave's earlier stores are complete
     auto hook = [&](int s) {
+      if (s < 0) return;
       if (s == 0 && wid == 0) publish();
       fetch_step(s);
     };
