@@ -42,7 +42,7 @@ struct GGroup {
   int32_t M, N, K, tile0;   // tile0: the group's first flat tile
   int32_t kseg;
   int32_t ldp;              // SwiGLU: partials per row
-  const float* D;           // SwiGLU: [M, ldc] float32
+  const bf16_t* D;          // SwiGLU: [M, ldc] bf16 (the dgrad-down product)
   bf16_t *dG, *dU, *Hw;     // SwiGLU: [M, ldc] bf16
   float* dwp;               // SwiGLU: [M, ldp] float32, or null
   const int32_t* rid;       // SwiGLU: route id of each row, or null (weight 1)
@@ -407,7 +407,12 @@ __global__ __launch_bounds__(GB_NT) void k_ggemm(const int32_t* __restrict__ tab
             const int col = ic0 + 32 * j + 8 * q + 4 * h;
             const int64_t at = (int64_t)m * g.ldc + col;
             f32x4v d4 = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (ok) d4 = *(const f32x4v*)(g.D + at);
+            if (ok) {
+              typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+              const u32x2v w = *(const __attribute__((address_space(1))) u32x2v*)(g.D + at);
+              d4[0] = __uint_as_float(w[0] << 16); d4[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+              d4[2] = __uint_as_float(w[1] << 16); d4[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+            }
             float og[4], ou[4], oh[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -450,7 +455,8 @@ struct BwdPass {
   const bf16_t* A_own;           // x own rows [T_own, d]
   const bf16_t* dP_own;          // their output gradient [T_own, d]
   bf16_t *Ar, *dPr, *dGr, *dUr, *Hr, *dGo, *dUo, *Ho;   // Hr: w H
-  float *Dr, *Do, *dwp;
+  bf16_t *Dr, *Do;               // D = dP Wd in bf16 (read by the recompute epilogue)
+  float* dwp;
   bf16_t *dx_slots, *dx_shared;  // outputs: dx through each route, the shared experts' dx
   float *dwg, *dwu, *dwd, *dsg, *dsu, *dsd;
   int32_t *t_rec, *t_dd, *t_du, *t_wg;   // group tables
@@ -512,7 +518,7 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
   // recompute + SwiGLU backward: G, U = A [Wg; Wu]^T, paired column by column, with D (from the
   // dgrad-down launch before) in the epilogue
   auto rec = [&](const bf16_t* A, const bf16_t* Wg, const bf16_t* Wu, int M, int In,
-                 const float* D, bf16_t* dG, bf16_t* dU, bf16_t* Hw, float* dwp,
+                 const bf16_t* D, bf16_t* dG, bf16_t* dU, bf16_t* Hw, float* dwp,
                  const int32_t* rid) {
     GGroup g = plain(A, d, Wg, d, nullptr, In, M, 2 * In, d);
     g.B2 = Wu;
@@ -538,7 +544,8 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
       g.tile0 = mt0 * cols(2 * I);
       Grec[pos] = g;
       // dgrad down: D = dP Wd (Wd read along its output dimension: transposed B)
-      g = plain(p.dPr + o * d, d, p.wd + (int64_t)e * d * I, I, p.Dr + o * I, I, c, I, d);
+      g = plain(p.dPr + o * d, d, p.wd + (int64_t)e * d * I, I, nullptr, I, c, I, d);
+      g.Cb = p.Dr + o * I;
       g.tile0 = mt0 * cols(I);
       Gdd[pos] = g;
       g = du(p.dGr + o * I, p.dUr + o * I, p.wg + (int64_t)e * I * d, p.wu + (int64_t)e * I * d,
@@ -575,8 +582,12 @@ __global__ __launch_bounds__(BD_THREADS) void k_bwd_describe(BwdPass p) {
     put(Grec, n_rec, tl_rec,
         rec(p.A_own, p.sg, p.su, p.T_own, Ish, p.Do, p.dGo, p.dUo, p.Ho, nullptr, nullptr));
     for (int s = 0; s < p.n_s; ++s)
-      put(Gdd, n_dd, tl_dd, plain(p.dP_own, d, p.sd + (int64_t)s * d * p.I_s, p.I_s,
-                                  p.Do + s * p.I_s, Ish, p.T_own, p.I_s, d));
+    {
+      GGroup gd = plain(p.dP_own, d, p.sd + (int64_t)s * d * p.I_s, p.I_s, nullptr, Ish, p.T_own,
+                        p.I_s, d);
+      gd.Cb = p.Do + s * p.I_s;
+      put(Gdd, n_dd, tl_dd, gd);
+    }
     if (p.dx_shared)
       put(Gdu, n_du, tl_du, du(p.dGo, p.dUo, p.sg, p.su, p.dx_shared, nullptr, p.T_own, Ish));
   }
@@ -756,12 +767,12 @@ BwdLayout layout_bwd(const mok_moe_bwd_args* a) {
   L.err = take(16);
   L.Ar = take(2 * cap * d); L.dPr = take(2 * cap * d);
   L.dGr = take(2 * cap * I); L.dUr = take(2 * cap * I); L.Hr = take(2 * cap * I);
-  L.Dr = take(4 * cap * I);
+  L.Dr = take(2 * cap * I);
   L.ldp = (int)(2 * cdiv(2 * I, GB_N));            // one partial per wave's 64 output columns
   L.dwp = take(4 * cap * L.ldp);
   const int64_t Io = std::max<int64_t>(1, Ish);
   L.dGo = take(2 * To * Io); L.dUo = take(2 * To * Io); L.Ho = take(2 * To * Io);
-  L.Do = take(4 * To * Io);
+  L.Do = take(2 * To * Io);
   wgrad_split(a, L);
   L.ws_part = take(4 * (size_t)L.ws_r * L.ws_P * GB_M * GB_N);
   L.ws_split = take(sizeof(SplitTile) * (size_t)L.ws_r);
@@ -815,7 +826,7 @@ int mok_moe_backward(const mok_moe_bwd_args* a, void* stream) {
   p.Ar = (bf16_t*)at(L.Ar); p.dPr = (bf16_t*)at(L.dPr); p.dGr = (bf16_t*)at(L.dGr);
   p.dUr = (bf16_t*)at(L.dUr); p.Hr = (bf16_t*)at(L.Hr);
   p.dGo = (bf16_t*)at(L.dGo); p.dUo = (bf16_t*)at(L.dUo); p.Ho = (bf16_t*)at(L.Ho);
-  p.Dr = (float*)at(L.Dr); p.Do = (float*)at(L.Do);
+  p.Dr = (bf16_t*)at(L.Dr); p.Do = (bf16_t*)at(L.Do);
   p.dx_slots = (bf16_t*)a->dx_slots; p.dx_shared = (bf16_t*)a->dx_shared;
   p.dwp = (float*)at(L.dwp); p.ldp = L.ldp;
   p.dwg = a->dw_gate; p.dwu = a->dw_up; p.dwd = a->dw_down;
