@@ -162,9 +162,8 @@ int mok_route(const void* x, const void* w_router, int64_t T, int32_t d, int32_t
   if (T == 0) return MOK_OK;
   if (!x || !w_router || !logits || !topk_idx || !topk_w) return MOK_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_router_logits(x, w_router, T, d, E, io_dtype == MOK_BF16, logits, s);
-  if (e != hipSuccess) return MOK_EHIP;
-  return status_of(launch_topk(logits, T, E, k, topk_idx, topk_w, s));
+  return status_of(launch_route(x, w_router, T, d, E, k, io_dtype == MOK_BF16, logits, topk_idx,
+                                topk_w, s));
 }
 
 int mok_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
@@ -233,11 +232,9 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
     int32_t* oidx = a->topk_idx_out ? a->topk_idx_out : (int32_t*)at(L.idx);
     float* ow = a->topk_w_out ? a->topk_w_out : (float*)at(L.w);
     if (a->T_pool > 0) {
-      hipError_t e = launch_router_logits(a->x, a->w_router, a->T_pool, a->d, a->E,
-                                          a->dtype != MOK_FP32, logits, s,
-                                          ev_start(MOK_STAGE_ROUTE), nullptr);
-      if (e != hipSuccess) return MOK_EHIP;
-      e = launch_topk(logits, a->T_pool, a->E, k, oidx, ow, s, nullptr, ev_stop(MOK_STAGE_ROUTE));
+      hipError_t e = launch_route(a->x, a->w_router, a->T_pool, a->d, a->E, k,
+                                  a->dtype != MOK_FP32, logits, oidx, ow, s,
+                                  ev_start(MOK_STAGE_ROUTE), ev_stop(MOK_STAGE_ROUTE));
       if (e != hipSuccess) return MOK_EHIP;
     } else {
       mark(MOK_STAGE_ROUTE);

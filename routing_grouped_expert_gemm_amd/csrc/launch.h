@@ -27,6 +27,13 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t n_tok, in
 hipError_t launch_topk(const float* logits, int64_t n_tok, int E, int k, int32_t* idx,
                        float* w, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
+// Router logits + top-k: for E of 16, 32 or 64 and d a multiple of 16 one fused launch
+// (route_fused_blocks > 0: its workgroup count), otherwise the two launches above.
+int64_t route_fused_blocks(int64_t n_tok, int d, int E, int k);
+hipError_t launch_route(const void* x, const void* wr, int64_t n_tok, int d, int E, int k,
+                        bool bf16, float* logits, int32_t* idx, float* w, hipStream_t s,
+                        hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+
 // The plan: chunk histograms (blk_counts: plan_n_blocks * E_l ints of workspace), then the
 // stable scatter; with wb (the expert stages' work list to build) one more workgroup of the
 // scatter launch builds it from the same sums.

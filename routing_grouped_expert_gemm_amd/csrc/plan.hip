@@ -70,7 +70,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(
     const int32_t* __restrict__ blk_counts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ route_ids,
     int32_t* __restrict__ rank_counts, int k, int64_t tokens_per_rank, int64_t R, int64_t cap,
-    WlBuild wb) {
+    WlBuild wb, int rank_sums) {
   extern __shared__ int32_t sm[];
   int32_t* tot = sm;                  // [E_l] routes of each expert
   int32_t* pre = sm + E_l;            // [E_l] ... in the chunks before this one
@@ -80,17 +80,25 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(
   const int b = blockIdx.x;
   for (int e = tid; e < E_l; e += PLAN_THREADS) tot[e] = pre[e] = 0;
   __syncthreads();
-  // G threads per expert sum every G-th chunk histogram; integer sums, so the totals do not
-  // depend on the order of the LDS additions
+  // G threads per expert sum every G-th chunk histogram, 8 loads in flight; integer sums, so
+  // the totals do not depend on the order of the LDS additions
   {
     const int G = PLAN_THREADS / E_l;
     if (tid < G * E_l) {
       const int e = tid % E_l, g = tid / E_l;
       int32_t st = 0, sp = 0;
-      for (int c = g; c < nb; c += G) {
-        const int32_t v = blk_counts[(int64_t)c * E_l + e];
-        st += v;
-        if (c < b) sp += v;
+      for (int c0 = g; c0 < nb; c0 += 8 * G) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * G;
+          v[u] = c < nb ? blk_counts[(int64_t)c * E_l + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          st += v[u];
+          if (c0 + u * G < b) sp += v[u];
+        }
       }
       atomicAdd(&tot[e], st);
       atomicAdd(&pre[e], sp);
@@ -114,6 +122,36 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan_scatter(
   if (b == nb) {                      // the work-list workgroup
     build_worklist(wb, tot, off, un);
     return;
+  }
+  if (rank_counts && rank_sums) {
+    // chunks never straddle a source rank: rank rho's counts are the sums of its nb / R
+    // chunks' histograms, which workgroup rho writes (no atomics on the totals)
+    if (b < R) {
+      const int64_t cpr = nb / R, c0 = (int64_t)b * cpr;
+      int32_t* rsum = un;
+      for (int e = tid; e < E_l; e += PLAN_THREADS) rsum[e] = 0;
+      __syncthreads();
+      const int G = PLAN_THREADS / E_l;
+      if (tid < G * E_l) {
+        const int e = tid % E_l, g = tid / E_l;
+        int32_t st = 0;
+        for (int64_t c1 = g; c1 < cpr; c1 += 8 * G) {
+          int32_t v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int64_t c = c1 + u * G;
+            v[u] = c < cpr ? blk_counts[(c0 + c) * E_l + e] : 0;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) st += v[u];
+        }
+        atomicAdd(&rsum[e], st);      // integer: order-independent
+      }
+      __syncthreads();
+      for (int e = tid; e < E_l; e += PLAN_THREADS) rank_counts[(int64_t)e * R + b] = rsum[e];
+      __syncthreads();
+    }
+    rank_counts = nullptr;            // nothing left to count per route
   }
   int32_t* base = un;                 // [E_l] next free row of each region (this chunk)
   int32_t* wcnt = un + E_l;           // [16][E_l] per-wave counts of the current sub-chunk
@@ -211,13 +249,15 @@ hipError_t launch_plan(const int32_t* idx, int64_t n_tok, int k, int e0, int E_l
     (void)hipFuncSetAttribute((const void*)k_plan_scatter,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
   });
-  launch_k(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS), (uint32_t)(sizeof(int32_t) * E_l),
-           s, ev0, nullptr, idx, n_routes, chunk, e0, E_l, blk_counts, rank_counts,
-           (int64_t)E_l * R);
+  launch_k(k_plan_count, dim3((unsigned)nb), dim3(PLAN_THREADS),
+           (uint32_t)(sizeof(int32_t) * E_l), s, ev0, nullptr, idx, n_routes, chunk, e0, E_l,
+           blk_counts, rank_counts, (int64_t)E_l * R);
+  // whole chunks per source rank: the rank counts are sums of chunk histograms
+  const bool rank_sums = chunk % k == 0 && tokens_per_rank % (chunk / k) == 0;
   launch_k(k_plan_scatter, dim3((unsigned)(nb + (build ? 1 : 0))), dim3(PLAN_THREADS),
            (uint32_t)sh_scatter, s, nullptr, ev1, idx, n_routes, chunk, (int)nb, e0, E_l,
            blk_counts, counts, offsets, route_ids, rank_counts, k, tokens_per_rank, R, route_cap,
-           w);
+           w, rank_sums ? 1 : 0);
   return hipGetLastError();
 }
 

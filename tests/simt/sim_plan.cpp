@@ -33,6 +33,8 @@ int main(int argc, char** argv) {
   const int64_t chunk = plan_chunk_h(n_routes, E_l);
   const int64_t nb = n_routes == 0 ? 1 : (n_routes + chunk - 1) / chunk;
   const int64_t R = T / tpr;
+  // whole chunks per source rank: the scatter writes the rank counts as chunk sums
+  const bool rank_sums = chunk % k == 0 && tpr % (chunk / k) == 0;
   // exactly sized heap buffers, so that the address sanitizer sees any overrun
   int32_t* blk_counts = (int32_t*)malloc(4 * nb * E_l);
   int32_t* counts = (int32_t*)malloc(4 * E_l);
@@ -53,7 +55,7 @@ int main(int argc, char** argv) {
   const size_t sh = sizeof(int32_t) * (size_t)(plan_sums_ints(E_l) + std::max(un, 160));
   launch((unsigned)(nb + 1), PLAN_THREADS, sh, [&] {
     k_plan_scatter(idxp, n_routes, chunk, (int)nb, e0, E_l, blk_counts, counts, offsets,
-                   route_ids, rank_counts, k, tpr, R, route_cap, wb);
+                   route_ids, rank_counts, k, tpr, R, route_cap, wb, rank_sums ? 1 : 0);
   });
   FILE* o = fopen((dir + "/out.bin").c_str(), "wb");
   int64_t oh[4] = {nb, (int64_t)wl_ints, route_cap, E_l * R};

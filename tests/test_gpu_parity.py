@@ -40,9 +40,14 @@ def test_seeded_generator_on_gpu_and_cpu():
 
 # --------------------------------------------------------------------- routing
 
+# E of 16, 32 or 64 with d a multiple of 16 take the fused router + top-k kernel (32 tokens a
+# workgroup: T = 1, 45, 300, 1000 leave ragged last workgroups), the rest the two-launch path
 @pytest.mark.parametrize("dtype,T,d,E,k", [("fp32", 64, 128, 8, 2), ("bf16", 300, 192, 64, 6),
                                            ("bf16", 97, 64, 130, 8), ("fp32", 33, 100, 5, 5),
-                                           ("bf16", 1000, 2048, 64, 6), ("fp32", 130, 272, 20, 4)])
+                                           ("bf16", 1000, 2048, 64, 6), ("fp32", 130, 272, 20, 4),
+                                           ("fp32", 45, 144, 16, 16), ("bf16", 70, 96, 32, 3),
+                                           ("fp32", 257, 64, 64, 64), ("bf16", 1, 16, 16, 1),
+                                           ("bf16", 96, 48, 32, 32)])
 def test_route_bit_exact(dtype, T, d, E, k):
     import routing_grouped_expert_gemm_amd as mok
     tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
@@ -116,10 +121,13 @@ def test_plan_worked_example():
     _check_plan(idx, 8, 5, 3, 4)
 
 
+# (8192, 8, 256, ...), (16384, 4, ...) and (8192, 8, 64, ...) cut into whole chunks per source
+# rank (the rank counts are then sums of chunk histograms), the rest straddle ranks
 @pytest.mark.parametrize("T,k,E,e0,E_l,tpr", [(4096, 6, 64, 0, 64, 4096), (8192, 8, 256, 12, 4, 256),
                                                (3000, 2, 8, 3, 1, 1000), (64, 2, 8, 0, 8, 64),
                                                (20000, 8, 384, 380, 4, 2000), (1, 1, 1, 0, 1, 1),
-                                               (4096, 2, 8, 0, 8, 16)])
+                                               (4096, 2, 8, 0, 8, 16), (16384, 4, 32, 0, 32, 512),
+                                               (8192, 8, 64, 0, 64, 8192)])
 def test_plan_bit_exact_random(T, k, E, e0, E_l, tpr):
     rng = np.random.default_rng(T + E)
     idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
@@ -249,6 +257,12 @@ SMALL = {
                                 d=512, E=64, k=8, I=256, e0=4, E_l=4, tokens_per_rank=256,
                                 own_begin=256, T_own=256, I_shared=256, minibatch_rows=128,
                                 ring_rows=1024),
+    # the fused router on a partial layer (local experts 8..15 of 32, four source ranks of 250
+    # tokens, which straddle the plan's chunks)
+    "part_router_bf16": synth.scaled(synth.WORKLOADS[synth.EP1], name="part_router_bf16",
+                                     T_pool=1000, d=256, E=32, k=4, I=192, e0=8, E_l=8,
+                                     tokens_per_rank=250, own_begin=250, T_own=250, n_shared=1,
+                                     I_shared=128, minibatch_rows=128, ring_rows=1024),
     "zipf_bf16": synth.scaled(synth.WORKLOADS[synth.EP96], name="zipf_bf16", T_pool=4096,
                               d=256, E=96, k=8, I=128, e0=0, E_l=4, tokens_per_rank=256,
                               own_begin=0, T_own=256, I_shared=128, minibatch_rows=128,
