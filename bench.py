@@ -20,9 +20,10 @@ each timed the same way (W warm-up steps, K timed steps between device synchroni
 
 `stage_ms` (other than the roofline kernel's) comes from a separate, untimed pass that times
 every stage with HIP events the library ties to the start of each stage's first kernel and the
-end of its last; before each step of that pass a 1 GiB scratch buffer is overwritten, so the
+end of its last; before each step of that pass a 1 GiB scratch buffer is read, so the
 stage times are cold-cache times (the 256 MB last-level cache holds nothing of the step
-before). `hbm` gives, for the memory-bound stages, algorithmic bytes over those times against
+before). A read, not a write: overwriting the buffer would leave ~1 GiB of dirty lines whose
+write-back competes with the first stages of the step. `hbm` gives, for the memory-bound stages, algorithmic bytes over those times against
 8 TB/s.
 
 `roofline` is taken live for the dominant kernel: the gate/up stage (grouped gate/up GEMM with
@@ -68,7 +69,23 @@ KERNEL_SOURCES = ["routing_grouped_expert_gemm_amd/csrc/expert_gemm.hip",
                   "routing_grouped_expert_gemm_amd/_build.py"]
 ELEM = {"f32": 0, "bf16": 1, "mxfp8": 2, "mxfp4": 3}
 ELEM_NAME = {0: "fp32", 1: "bf16", 2: "mxfp8", 3: "mxfp4"}
-FLUSH_BYTES = 1 << 30        # scratch overwritten before each step of the per-stage pass
+FLUSH_BYTES = 1 << 30        # scratch read before each step of the per-stage pass
+
+
+def cache_scratch(dev):
+    """A 1 GiB device buffer (4x the last-level cache), written once."""
+    import torch
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    scratch.fill_(1)
+    torch.cuda.synchronize()
+    return scratch
+
+
+def evict_caches(scratch) -> None:
+    """Reads the scratch buffer on the current stream: afterwards no cache holds anything of the
+    earlier work, and no dirty line is left whose write-back would compete with what follows."""
+    import torch
+    scratch.view(torch.int64).sum()
 
 
 def kernel_sources_sha256() -> str:
@@ -636,13 +653,13 @@ def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0
     assert layer.device_error(stream) == 0
     up_ms = sum(ev_up.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)) / steps
     # per-stage times: a separate, untimed pass with every stage event, each step after a 1 GiB
-    # scratch write (nothing of the previous step stays in the caches)
+    # scratch read (nothing of the previous step stays in the caches)
     n_stage = min(steps, 10)
     ev_all = HipEvents(n2 * n_stage)
     all_tables = event_table(ev_all, False)
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    scratch = cache_scratch(dev)
     for i in range(n_stage):
-        scratch.fill_(i & 0xFF)
+        evict_caches(scratch)
         step(all_tables[i])
     torch.cuda.synchronize()
     del scratch
@@ -695,7 +712,7 @@ def measure_dispatch(steps: int, warmup: int, dev="cuda:0") -> dict:
     """Pull (plan + gather in plan order) against push (atomic-slot scatter) on the EP=64 share's
     routing: 262144 pool rows of d = 7168 bf16, top-8 of 256 experts, 4 local experts. Both
     move the same rows into expert-contiguous buffers; times are HIP events on the stream,
-    averaged over `steps` after `warmup`, each step after a 1 GiB scratch write."""
+    averaged over `steps` after `warmup`, each step after a 1 GiB scratch read."""
     import torch
     import routing_grouped_expert_gemm_amd as mok
     import synth
@@ -715,7 +732,7 @@ def measure_dispatch(steps: int, warmup: int, dev="cuda:0") -> dict:
     fill = torch.empty(E_l, **i32)
     push_buf = torch.empty((E_l, cap, d), dtype=x.dtype, device=dev)
     src = torch.empty((E_l, cap), **i32)
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    scratch = cache_scratch(dev)
 
     def plan():
         mok.mok_dispatch_plan(idx, wl.E, wl.e0, E_l, wl.tokens_per_rank, counts, offsets,
@@ -726,11 +743,11 @@ def measure_dispatch(steps: int, warmup: int, dev="cuda:0") -> dict:
     orders = []
     for i in range(warmup + steps):
         e = [ev() for _ in range(6)]
-        scratch.fill_(i & 0xFF)
+        evict_caches(scratch)
         e[0].record(); plan(); e[1].record()
-        scratch.fill_((i + 1) & 0xFF)
+        evict_caches(scratch)
         e[2].record(); mok.mok_pull_gather(x, k, route_ids, offsets, pull_buf); e[3].record()
-        scratch.fill_((i + 2) & 0xFF)
+        evict_caches(scratch)
         e[4].record(); mok.mok_push_dispatch(x, idx, wl.e0, fill, push_buf, src); e[5].record()
         torch.cuda.synchronize()
         if i >= warmup:
@@ -761,7 +778,7 @@ def measure_dispatch(steps: int, warmup: int, dev="cuda:0") -> dict:
 
 def measure_backward(steps: int, warmup: int, dev="cuda:0") -> dict:
     """Backward of the EP=1 bf16 layer (mok_moe_backward) with the forward's routing, HIP-event
-    time per step (each step after a 1 GiB scratch write). Its GEMMs execute 16*d*I FLOPs per
+    time per step (each step after a 1 GiB scratch read). Its GEMMs execute 16*d*I FLOPs per
     routed row (gate/up recompute 4, dgrad 6, wgrad 6) and 16*d*I_s*n_s per own token."""
     import torch
     import routing_grouped_expert_gemm_amd as mok
@@ -779,10 +796,10 @@ def measure_backward(steps: int, warmup: int, dev="cuda:0") -> dict:
                         topk_idx=fwd.inter["topk_idx"], topk_w=fwd.inter["topk_w"],
                         w_gate=inp["wg"], w_up=inp["wu"], w_down=inp["wd"], ws_gate=inp["sg"],
                         ws_up=inp["su"], ws_down=inp["sd"], dy=dy, device=dev)
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    scratch = cache_scratch(dev)
     t = 0.0
     for i in range(warmup + steps):
-        scratch.fill_(i & 0xFF)
+        evict_caches(scratch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         b.backward()

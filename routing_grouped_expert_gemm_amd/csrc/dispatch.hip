@@ -27,15 +27,20 @@ namespace mok {
 constexpr int DISPATCH_THREADS = 256;
 constexpr int COPY_UNROLL = 4;
 
-// Copy n16 16-byte chunks from src to dst with the whole wave, COPY_UNROLL loads in flight.
-MOK_DEV void wave_copy_row(const uint4* __restrict__ src, uint4* __restrict__ dst, int n16) {
+// Copy n16 16-byte chunks from src to dst with the whole wave, COPY_UNROLL loads in flight. The
+// chunks are held as plain vector registers (a uint4 array filled under a condition was placed
+// in scratch, and every load then waited for the one before).
+MOK_DEV void wave_copy_row(const uint4* __restrict__ src_, uint4* __restrict__ dst_, int n16) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* src = (const u32x4*)src_;
+  u32x4* dst = (u32x4*)dst_;
   const int lane = lane_id();
   for (int c0 = 0; c0 < n16; c0 += 64 * COPY_UNROLL) {
-    uint4 v[COPY_UNROLL];
+    u32x4 v[COPY_UNROLL];
 #pragma unroll
     for (int u = 0; u < COPY_UNROLL; ++u) {
       const int c = c0 + u * 64 + lane;
-      if (c < n16) v[u] = src[c];
+      v[u] = c < n16 ? src[c] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < COPY_UNROLL; ++u) {
