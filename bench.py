@@ -603,10 +603,12 @@ def cpu_baseline(wl, inputs_cpu, sample_tokens: int) -> dict:
                       f"(C), plan (C), float64 numpy expert and shared FFNs, combine); {dt:.1f} s"}
 
 
-def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0") -> dict:
+def measure(wl, mode: str, steps: int, warmup: int, minibatch=None, dev="cuda:0") -> dict:
     """Time `steps` forwards of workload wl after `warmup` (wall clock between device
     synchronisations; HIP events on the roofline kernel only), then a cold-cache per-stage pass.
-    Returns the JSON fields of one measurement and the inputs (for the CPU baseline)."""
+    mode: "stage" (two stage launches), "ring" (the ring work loop) or "loop" (the stage order
+    in one persistent launch). Returns the JSON fields of one measurement and the inputs (for
+    the CPU baseline)."""
     import torch
     import routing_grouped_expert_gemm_amd as mok
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -614,7 +616,8 @@ def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0
 
     inp = make_inputs(wl, dev)
     topk = gpu_topk(inp["logits"], wl.k) if wl.routing == "logits" else None
-    flags = 0 if ring else mok.MOK_FLAG_NO_RING
+    ring = mode == "ring"
+    flags = {"stage": mok.MOK_FLAG_NO_RING, "ring": 0, "loop": mok.MOK_FLAG_STAGE_LOOP}[mode]
     layer = gpu_layer(wl, inp, topk=topk, flags=flags, mb=minibatch, keep=True)
     stream = torch.cuda.current_stream()
     n2 = 2 * mok.MOK_N_STAGES
@@ -675,10 +678,12 @@ def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0
     stage_ms["up_cold"] = stage_ms["up"]
     stage_ms["up"] = up_ms                      # the timed steps' own measurement
     peak = PEAK[wl.dtype]
-    if ring:
-        # one persistent launch runs the gate/up and the down tiles (and the MXFP8 row gather)
+    if mode != "stage":
+        # one persistent launch runs the gate/up and the down tiles (and, in the ring, the MX
+        # row gather)
         roof_flop = work["up_flop"] + work["down_flop"]
-        kernel = "ring work loop (k_ring: gate/up and down tiles of every minibatch)"
+        kernel = ("ring work loop (k_ring: gate/up and down tiles of every minibatch)" if ring
+                  else "stage order in one persistent launch (k_ring over the stage tables)")
         gemm_s = up_ms * 1e-3
     else:
         roof_flop = work["up_flop"]
@@ -694,14 +699,15 @@ def measure(wl, ring: bool, steps: int, warmup: int, minibatch=None, dev="cuda:0
                    "E": wl.E, "k": wl.k, "I": wl.I, "E_local": wl.E_l, "n_shared": wl.n_shared,
                    "I_shared": wl.I_shared, "minibatch_rows": layer.args.minibatch_rows,
                    "ring_rows": layer.args.ring_rows if ring else None,
-                   "work_loop": "ring" if ring else "stage-ordered"},
+                   "work_loop": {"stage": "stage-ordered", "ring": "ring",
+                                 "loop": "stage-ordered, one persistent launch"}[mode]},
         "routed_rows": n_routes,
         "routed_tflops": round(work["routed_flop"] / (ms * 1e-3) / 1e12, 2),
         "gemm_tflops": round((work["routed_flop"] + work["shared_flop"]) / gemm_s / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved / 1e12, 2),
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if ring else profiled_traffic(wl.name)},
+                     "traffic": profiled_traffic(wl.name) if mode == "stage" else None},
         "hbm": hbm_stages(wl, n_routes, stage_ms, ring),
     }
     del layer
@@ -829,6 +835,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="measure this workload alone (default: the headline and its extras)")
     ap.add_argument("--ring", action="store_true", help="persistent ring work loop")
+    ap.add_argument("--stage-loop", action="store_true",
+                    help="the stage order in one persistent launch")
     ap.add_argument("--minibatch", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8192)
@@ -875,7 +883,8 @@ def main():
         return
     name = args.workload or synth.EP1
     wl = synth.WORKLOADS[name]
-    res, inp = measure(wl, args.ring, args.steps, args.warmup, args.minibatch)
+    mode = "ring" if args.ring else "loop" if args.stage_loop else "stage"
+    res, inp = measure(wl, mode, args.steps, args.warmup, args.minibatch)
     out = {"metric": METRIC, "value": res["value"], "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -891,32 +900,38 @@ def main():
     if args.workload is None:
         torch.cuda.empty_cache()
         # the same layer with the persistent ring work loop (the library default)
-        r, i2 = measure(wl, True, args.steps, args.warmup, args.minibatch)
+        r, i2 = measure(wl, "ring", args.steps, args.warmup, args.minibatch)
         del i2
         out["ring"] = {k: r[k] for k in ("value", "ms_per_step", "routed_tflops", "config",
                                          "stage_ms", "roofline")}
         torch.cuda.empty_cache()
+        # ... and with the stage order in one persistent launch
+        r, i2 = measure(wl, "loop", args.steps, args.warmup, args.minibatch)
+        del i2
+        out["stage_loop"] = {k: r[k] for k in ("value", "ms_per_step", "routed_tflops", "config",
+                                               "stage_ms", "roofline")}
+        torch.cuda.empty_cache()
         # the MXFP8 share
-        m, i3 = measure(synth.WORKLOADS[synth.EP64_MX], False, args.steps, args.warmup)
+        m, i3 = measure(synth.WORKLOADS[synth.EP64_MX], "stage", args.steps, args.warmup)
         del i3
         torch.cuda.empty_cache()
         out["mxfp8"] = {k: m[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                           "routed_rows", "routed_tflops", "gemm_tflops",
                                           "stage_ms", "roofline", "hbm")}
         # ... and with the ring work loop (gather items inside the loop)
-        mr, i3 = measure(synth.WORKLOADS[synth.EP64_MX], True, args.steps, args.warmup)
+        mr, i3 = measure(synth.WORKLOADS[synth.EP64_MX], "ring", args.steps, args.warmup)
         del i3
         torch.cuda.empty_cache()
         out["mxfp8"]["ring"] = {k: mr[k] for k in ("value", "ms_per_step", "routed_tflops",
                                                    "config", "roofline")}
         # the same share with MXFP4 operands
-        m4, i4 = measure(synth.WORKLOADS[synth.EP64_MX4], False, args.steps, args.warmup)
+        m4, i4 = measure(synth.WORKLOADS[synth.EP64_MX4], "stage", args.steps, args.warmup)
         del i4
         torch.cuda.empty_cache()
         out["mxfp4"] = {k: m4[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                            "routed_rows", "routed_tflops", "gemm_tflops",
                                            "stage_ms", "roofline", "hbm")}
-        m4r, i4 = measure(synth.WORKLOADS[synth.EP64_MX4], True, args.steps, args.warmup)
+        m4r, i4 = measure(synth.WORKLOADS[synth.EP64_MX4], "ring", args.steps, args.warmup)
         del i4
         torch.cuda.empty_cache()
         out["mxfp4"]["ring"] = {k: m4r[k] for k in ("value", "ms_per_step", "routed_tflops",

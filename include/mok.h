@@ -198,6 +198,12 @@ typedef struct mok_moe_args {
 #define MOK_FLAG_NO_RING 1u  /* stage-ordered launches over all routes (ring sized to every
                                 possible route) instead of the persistent ring work loop;
                                 same results                                                */
+#define MOK_FLAG_STAGE_LOOP 2u /* the stage order (every minibatch in its own slot, as with
+                                MOK_FLAG_NO_RING) run by one persistent launch: per-XCD
+                                queues of gate/up tiles then down tiles, a down tile waiting
+                                only for its own minibatch's gate/up tiles, so the two stages
+                                overlap at their boundary; same results. Takes precedence
+                                over MOK_FLAG_NO_RING.                                      */
 
 int mok_moe_workspace_bytes(const mok_moe_args* args, size_t* bytes);
 int mok_moe_forward(const mok_moe_args* args, void* stream);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmok.so")   # always the in-tree build
 
 MOK_OK, MOK_EINVAL, MOK_EUNSUPPORTED, MOK_EWORKSPACE, MOK_EHIP = range(5)
 MOK_FP32, MOK_BF16, MOK_MXFP8, MOK_MXFP4 = 0, 1, 2, 3
-MOK_FLAG_NO_RING = 1
+MOK_FLAG_NO_RING, MOK_FLAG_STAGE_LOOP = 1, 2
 (MOK_STAGE_ROUTE, MOK_STAGE_PLAN, MOK_STAGE_QUANT, MOK_STAGE_UP, MOK_STAGE_DOWN, MOK_STAGE_COMBINE,
  MOK_STAGE_GATHER) = range(7)
 MOK_N_STAGES = 7

@@ -33,7 +33,7 @@ int device_cus() {
 // Workspace layout of one forward. The work list sits at offset 0 so the device error word
 // can be found from the workspace pointer alone.
 struct Layout {
-  bool use_ring = false;
+  bool use_ring = false, loop = false;
   int64_t route_cap = 1;   // rows of route_ids
   int n_slots = 0, max_mb = 0, Hld = 0, cap_u = 0, cap_d = 0, cap_g = 0, cap_r = 0;
   size_t wl = 0, logits = 0, idx = 0, w = 0, counts = 0, offsets = 0, rank_counts = 0,
@@ -97,7 +97,8 @@ Layout layout_moe(const mok_moe_args* a) {
   const int I_sh = a->n_shared * a->I_shared;
   const int64_t max_mb = ceil_div(n_cap, mb) + a->E_l + (I_sh > 0 ? ceil_div(a->T_own, mb) : 0);
   L.max_mb = (int)std::max<int64_t>(1, max_mb);
-  L.use_ring = !(a->flags & MOK_FLAG_NO_RING);
+  L.loop = (a->flags & MOK_FLAG_STAGE_LOOP) != 0;
+  L.use_ring = !(a->flags & MOK_FLAG_NO_RING) && !L.loop;
   L.n_slots = L.use_ring ? a->ring_rows / mb : L.max_mb;
   L.Hld = std::max(a->I, I_sh);
   const size_t es = a->dtype == MOK_FP32 ? 4 : 2;
@@ -107,7 +108,7 @@ Layout layout_moe(const mok_moe_args* a) {
   // bytes of n MX codes: one a byte (MXFP8), two a byte (MXFP4)
   auto cb = [&](size_t n) { return a->dtype == MOK_MXFP4 ? n / 2 : n; };
   gemm_tile_caps(L.max_mb, mb, a->I, I_sh, a->d, L.use_ring && mx, &L.cap_u, &L.cap_d, &L.cap_g);
-  L.cap_r = L.use_ring ? L.cap_u + L.cap_d + L.cap_g : 0;
+  L.cap_r = L.use_ring ? L.cap_u + L.cap_d + L.cap_g : L.loop ? L.cap_u + L.cap_d : 0;
   L.wl = take(sizeof(int32_t) * worklist_ints(L.max_mb, L.cap_u, L.cap_d, L.cap_r));
   const bool route = a->w_router != nullptr;
   L.logits = (route && !a->logits_out) ? take(sizeof(float) * a->T_pool * a->E) : 0;
@@ -273,6 +274,7 @@ int mok_moe_forward(const mok_moe_args* a, void* stream) {
   p.cap_d = L.cap_d;
   p.cap_r = L.cap_r;
   p.ring = L.use_ring;
+  p.loop = L.loop;
   p.route_cap = L.route_cap;
   const int cus = device_cus();
   p.grid = ((cus + 7) / 8) * 8;            // one 256 x 256 tile workgroup per CU

@@ -235,11 +235,14 @@ MOK_DEV T kernarg_field(size_t off) {
   return *(__attribute__((address_space(4))) const volatile T*)(base + off);
 }
 
-// The pool rows of the route ids prefetch_a_rows loaded (route id / k).
+// The pool rows of the route ids prefetch_a_rows loaded (route id / k). k is read from the
+// kernarg segment here, so the division's reciprocal is not hoisted out of a tile loop and
+// held (or spilled) across the tiles.
 template <class C>
 MOK_DEV void route_rows(const ExpertPass& p, int32_t (&r)[C::A_SLABS]) {
+  const int k = kernarg_field<int>(offsetof(ExpertPass, k));
 #pragma unroll
-  for (int q = 0; q < C::A_SLABS; ++q) r[q] /= p.k;
+  for (int q = 0; q < C::A_SLABS; ++q) r[q] /= k;
 }
 
 // One tile. slot: the ring slot of the entry's minibatch. pre (routed gate/up tiles of the
@@ -1079,7 +1082,7 @@ MOK_DEV void wait_count(const int32_t* ctr, int32_t need, int32_t* err) {
     }
     if (it >= kSpinLimit) {
       // one lane sets the bit (the others or in 0)
-      __hip_atomic_fetch_or(err, (threadIdx.x & 63) == 0 ? (int32_t)ERR_WAIT : 0, __ATOMIC_RELAXED,
+      __hip_atomic_fetch_or(err, opaque(lane_id()) == 0 ? (int32_t)ERR_WAIT : 0, __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
@@ -1102,7 +1105,15 @@ MOK_DEV void wait_count(const int32_t* ctr, int32_t need, int32_t* err) {
 template <Elem EL, bool F32OUT, class C>
 __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
   MOK_TILE_LDS(C, EL, sm);
-  __shared__ int4 item;
+  // The loop's own LDS words, reached through a base made afresh at each use: the tile buffers
+  // fill the first 128 KB, so these sit past the 64 KB an LDS instruction's offset field
+  // reaches and need an address register; held across the loop, those registers were spilled.
+  struct RingLds {
+    int4 item, nitem;
+    int32_t nprev, drain, next_queue, pad;
+  };
+  __shared__ RingLds rl_;
+  auto R = [&]() { return (RingLds*)((char*)&rl_ + opaque(0)); };
   const int cap = p.max_mb;
   int32_t* wl = p.wl;
   const int4* rt = wl_rtab(wl, cap, p.cap_u, p.cap_d);
@@ -1121,20 +1132,19 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
   int32_t seg1 = affine ? uniform(wl[WL_XR + x + 1]) : uniform(wl[WL_N_R]);
   int32_t* ticket = &wl[WL_TICKETS + x];
   bool draining = false;               // this workgroup runs queues no workgroup served
-  __shared__ int32_t next_queue;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int32_t one = (threadIdx.x & 63) == 0 ? 1 : 0;
+  // 1 in lane 0, else 0: the increment of a wave-wide atomic. Made afresh at each use (from the
+  // lane id), so no register holds it across the loop.
+  auto one = [&]() { return opaque(lane_id()) == 0 ? 1 : 0; };
   // The next item is fetched while the current tile runs (wave 0, after K-step barriers 0..3,
   // where each load issued before has landed): ticket, entry, its slot predecessor, parked in
   // LDS. A gather item has no K loop: the next item is then fetched in line.
-  __shared__ int4 nitem;
-  __shared__ int32_t nprev;
   int32_t tk = 0;
   int4 ne = make_int4(-1, 0, 0, 0);
   auto fetch_step = [&](int s) {
     if (wid != 0) return;
     if (s == 0) {
-      tk = __hip_atomic_fetch_add(ticket, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      tk = __hip_atomic_fetch_add(ticket, one(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if (s == 1) {
       const int32_t t = seg0 + __builtin_amdgcn_readfirstlane(tk);
       ne = make_int4(-1, 0, 0, 0);
@@ -1145,10 +1155,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
       v.y = __builtin_amdgcn_readfirstlane(ne.y);
       v.z = __builtin_amdgcn_readfirstlane(ne.z);
       v.w = __builtin_amdgcn_readfirstlane(ne.w);
-      nitem = v;
+      R()->nitem = v;
       tk = v.x >= 0 ? prev[v.x] : -1;
     } else {
-      nprev = __builtin_amdgcn_readfirstlane(tk);
+      R()->nprev = __builtin_amdgcn_readfirstlane(tk);
     }
   };
   for (int s = 0; s < 4; ++s) {
@@ -1165,11 +1175,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
   auto publish = [&]() {                          // wave 0; every wave's stores are complete
     if (pend) {
       if (!affine) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(pend, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(pend, one(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       pend = nullptr;
     }
   };
-  __shared__ int32_t drain_lds;
   for (;;) {
     // the counters the next item waits on (wave 0)
     int32_t *c1 = nullptr, *c2 = nullptr;
@@ -1184,12 +1193,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
                        __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= n;
     };
     if (wid == 0) {
-      int4 e = nitem;
+      int4 e = R()->nitem;
       bool drain = pend != nullptr;
       if (e.x >= 0) {
         const int m = __builtin_amdgcn_readfirstlane(e.x);
         const int kind = __builtin_amdgcn_readfirstlane(e.y) >> KIND_SHIFT;
-        const int pm = __builtin_amdgcn_readfirstlane(nprev);
+        const int pm = __builtin_amdgcn_readfirstlane(R()->nprev);
         if (kind == KIND_D) {
           c1 = &done_u[m];
           n1 = us[m + 1] - us[m];
@@ -1212,16 +1221,20 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
           if (!drain && !affine) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
       }
-      item = e;                                   // every lane of wave 0 stores the same value
-      drain_lds = drain ? 1 : 0;
+      RingLds* r = R();
+      r->item = e;                                // every lane of wave 0 stores the same value
+      r->drain = drain ? 1 : 0;
     }
     __syncthreads();
     int4 e;
-    e.x = __builtin_amdgcn_readfirstlane(item.x);
-    e.y = __builtin_amdgcn_readfirstlane(item.y);
-    e.z = __builtin_amdgcn_readfirstlane(item.z);
-    e.w = __builtin_amdgcn_readfirstlane(item.w);
-    if (__builtin_amdgcn_readfirstlane(drain_lds)) {
+    {
+      const RingLds* r = R();
+      e.x = __builtin_amdgcn_readfirstlane(r->item.x);
+      e.y = __builtin_amdgcn_readfirstlane(r->item.y);
+      e.z = __builtin_amdgcn_readfirstlane(r->item.z);
+      e.w = __builtin_amdgcn_readfirstlane(r->item.w);
+    }
+    if (__builtin_amdgcn_readfirstlane(R()->drain)) {
       // every wave's stores of the pending item have reached L2; publish, then wait
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -1242,7 +1255,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
         bool last = draining;
         if (!draining) {
           const int32_t before = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
-              &wl[WL_EXITS], one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+              &wl[WL_EXITS], one(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
           last = before == (int32_t)gridDim.x - 1;
         }
         int q = -1;
@@ -1253,10 +1266,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
             if (taken == 0 && uniform(wl[WL_XR + y]) < uniform(wl[WL_XR + y + 1])) q = y;
           }
         }
-        next_queue = q;                   // every lane of wave 0 stores the same value
+        R()->next_queue = q;              // every lane of wave 0 stores the same value
       }
       __syncthreads();
-      const int q = __builtin_amdgcn_readfirstlane(next_queue);
+      const int q = __builtin_amdgcn_readfirstlane(R()->next_queue);
       if (q < 0) break;
       draining = true;
       x = q;
@@ -1386,7 +1399,7 @@ static hipError_t launch_stages_t(const ExpertPass& p, hipStream_t s, void* cons
   if (is_mx<EL>() && !p.ring)
     launch_k(k_gather_quantize<EL == Elem::FP4>, dim3(p.grid * 8), dim3(256), 0, s,
              ev_at(ev, EV_GATHER), ev_at(ev, EV_GATHER + 1), p);
-  if (p.ring) {
+  if (p.ring || p.loop) {
     launch_k(k_ring<EL, F32OUT, C>, dim3(p.grid), dim3(C::NT), 0, s, ev_at(ev, EV_UP),
              ev_at(ev, EV_UP + 1), p);
     mark_empty(s, ev_at(ev, EV_DOWN), ev_at(ev, EV_DOWN + 1));
@@ -1424,6 +1437,10 @@ hipError_t launch_plan_worklist(const int32_t* idx, int64_t n_tok, int64_t token
   wb.nD = (p.d + Big::BN - 1) / Big::BN;
   wb.gather = p.ring && mx;
   wb.ring = p.ring;
+  wb.loop = p.loop;
+  wb.ks_u = p.d / 64;
+  wb.ks_dr = p.I / 64;
+  wb.ks_ds = p.I_sh / 64;
   wb.xcd_split = p.xcd_split;
   wb.n_slots = p.n_slots;
   wb.cap = p.max_mb;

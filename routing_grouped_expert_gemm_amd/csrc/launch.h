@@ -84,6 +84,7 @@ struct ExpertPass {
   int cap_u, cap_d;      // capacity of the up / down tile tables
   int cap_r;             // capacity of the ring-order table (ring work loop), else 0
   bool ring;             // persistent ring work loop (else stage-ordered launches)
+  bool loop;             // the stage order run by the persistent loop (k_ring) instead
   bool xcd_split;        // ring: one item queue per XCD (whole-chip launch of 256 CUs)
   int64_t route_cap;     // rows of route_ids: a plan with more local routes is rejected
   int bm, bn;            // GEMM tile (rows, B-tile rows)

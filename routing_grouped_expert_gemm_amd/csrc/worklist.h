@@ -56,6 +56,8 @@ struct WlBuild {
   int E_l, T_own, mb, bm;   // local experts, own tokens, minibatch rows, GEMM tile rows
   int nU_r, nU_s, nD;       // N tiles of an up tile row (routed, shared) and of a down tile row
   int gather, ring, xcd_split, n_slots;   // gather items (MX ring), ring order, XCD split
+  int loop;                 // stage order run by the persistent loop (stage tables + rt)
+  int ks_u, ks_dr, ks_ds;   // K steps of an up tile, a routed and a shared down tile (weights)
   int cap, cap_u, cap_d, cap_r;           // capacities of the layout
   int64_t route_cap;        // rows of route_ids
 };
@@ -200,6 +202,7 @@ MOK_DEV void build_worklist(const WlBuild& P, const int32_t* cnt, const int32_t*
   // no tile then reads past the plan
   const bool overflow = n_routed + n_sh > cap || carry.x > P.cap_u || carry.y > P.cap_d ||
                         (P.ring && (int64_t)carry.x + carry.y + carry.z > P.cap_r) ||
+                        (P.loop && (int64_t)carry.x + carry.y > P.cap_r) ||
                         (int64_t)off[E_l] > P.route_cap;
   const bool affine = P.ring && P.xcd_split && P.n_slots >= N_XCD;
   if (t == 0) {
@@ -210,9 +213,9 @@ MOK_DEV void build_worklist(const WlBuild& P, const int32_t* cnt, const int32_t*
     wl[WL_N_MB] = n_mb;
     wl[WL_N_U] = overflow ? 0 : carry.x;
     wl[WL_N_D] = overflow ? 0 : carry.y;
-    wl[WL_N_R] = (overflow || !P.ring) ? 0 : carry.x + carry.y + carry.z;
+    wl[WL_N_R] = overflow ? 0 : P.ring ? carry.x + carry.y + carry.z : P.loop ? carry.x + carry.y : 0;
     wl[WL_ERR] = overflow ? ERR_OVERFLOW : 0;
-    wl[WL_AFFINE] = affine ? 1 : 0;
+    wl[WL_AFFINE] = (affine || (P.loop && P.xcd_split && in_lds)) ? 1 : 0;
     wl[WL_CAPS] = cap;
     wl[WL_CAPS + 1] = P.cap_u;
     wl[WL_CAPS + 2] = P.cap_d;
@@ -267,7 +270,7 @@ MOK_DEV void build_worklist(const WlBuild& P, const int32_t* cnt, const int32_t*
   if (t <= N_XCD) {
     const int b = t < N_XCD ? base_of(t) : n_mb;
     wl[WL_XB + t] = b;
-    wl[WL_XR + t] = (P.ring && !overflow) ? pg[b] + pu[b] + pd[b] : 0;
+    if (!P.loop || overflow) wl[WL_XR + t] = (P.ring && !overflow) ? pg[b] + pu[b] + pd[b] : 0;
   }
   if (in_lds) {                                     // the tables the stages read
     for (int m = t; m <= n_mb; m += 1024) {
@@ -361,6 +364,97 @@ MOK_DEV void build_worklist(const WlBuild& P, const int32_t* cnt, const int32_t*
       };
       place(c_pu, P.nU_r, P.nU_s, c_bu, ut, XB_N);
       place(c_pd, P.nD, P.nD, c_bd, dt, XB_ND);
+    }
+  }
+  if (P.loop) {
+    // The stage order run by the persistent loop. The minibatches are cut, in order, into 8
+    // contiguous ranges of about equal work (K steps of their tiles), one per XCD (with the
+    // split; else one range); XCD x's queue holds the up tiles of its range, then their down
+    // tiles, so a down tile depends only on up tiles earlier in its own queue, produced under
+    // the same L2. Within a queue each expert's tiles keep the stage tables' blocked order,
+    // restricted to the expert's M tiles in the range: blocks of XB N tiles, each with those
+    // M tiles in order (an expert that straddles a cut is split by M tiles).
+    const bool split = P.xcd_split && in_lds;
+    __syncthreads();                                 // the stage tables are complete
+    if (!split) {
+      // one queue: the up table, then the down table
+      for (int32_t i = t; i < carry.x; i += 1024) {
+        int4 e = ut[i];
+        e.y |= KIND_U << KIND_SHIFT;
+        rt[i] = e;
+      }
+      for (int32_t i = t; i < carry.y; i += 1024) {
+        int4 e = dt[i];
+        e.y |= KIND_D << KIND_SHIFT;
+        rt[carry.x + i] = e;
+      }
+      if (t <= N_XCD) wl[WL_XR + t] = t == 0 ? 0 : carry.x + carry.y;
+    } else {
+      int32_t* ub = la(10);                          // per minibatch: queue base of its up tiles
+      int32_t* db = la(11);                          // ... of its down tiles
+      int32_t* mg = la(12);                          // first minibatch of its expert in its range
+      int32_t* mtx = la(13);                         // M tiles of its expert in its range
+      int32_t* xm = la(14);                          // its XCD
+      int32_t* xs = la(15);                          // per XCD: up count, down count, first m
+      // work of minibatch m in K steps, and its exclusive prefix over m (n_mb <= 1024 here)
+      int32_t wm = 0;
+      if (t < n_mb) {
+        const int32_t nu = us[t + 1] - us[t], nd = ds[t + 1] - ds[t];
+        wm = nu * P.ks_u + nd * (grp[t] < E_l ? P.ks_dr : P.ks_ds);
+      }
+      int32_t w_tot;
+      const int32_t wp = block_excl_scan_1024(wm, sh, &w_tot);
+      if (t < N_XCD) { xs[t] = 0; xs[N_XCD + t] = 0; xs[2 * N_XCD + t] = n_mb; }
+      if (t < n_mb) mtx[t] = 0;
+      __syncthreads();
+      // the XCD of m's work midpoint (non-decreasing in m: contiguous ranges)
+      int x = 0;
+      if (t < n_mb) {
+        const int64_t mid2 = 2 * (int64_t)wp + wm;
+        x = w_tot > 0 ? (int)min((int64_t)(N_XCD - 1), mid2 * N_XCD / (2 * (int64_t)w_tot)) : 0;
+        xm[t] = x;
+        atomicAdd(&xs[x], us[t + 1] - us[t]);          // integer sums: order-independent
+        atomicAdd(&xs[N_XCD + x], ds[t + 1] - ds[t]);
+        atomicMin(&xs[2 * N_XCD + x], t);
+      }
+      __syncthreads();
+      if (t < n_mb) {
+        const int g = grp[t];
+        const int f = g < E_l ? mbp[g] : n_routed;     // the expert's first minibatch
+        const int m_g = max(f, xs[2 * N_XCD + x]);
+        mg[t] = m_g;
+        atomicAdd(&mtx[m_g], (nr[t] + bm - 1) / bm);
+        int32_t seg = 0;
+        for (int y = 0; y < x; ++y) seg += xs[y] + xs[N_XCD + y];
+        const int mf = xs[2 * N_XCD + x];
+        ub[t] = seg + (us[m_g] - us[mf]);
+        db[t] = seg + xs[x] + (ds[m_g] - ds[mf]);
+      }
+      if (t <= N_XCD) {
+        int32_t b = 0;
+        for (int y = 0; y < t; ++y) b += xs[y] + xs[N_XCD + y];
+        wl[WL_XR + t] = b;
+      }
+      __syncthreads();
+      // entry (m, l): M tile mt and N tile nt of minibatch m; its place in the expert's part of
+      // the queue: block nb of XB N tiles holds the part's MT M tiles x w N tiles
+      auto place_q = [&](const int4* tab, int32_t n, int kind, int XB) {
+        for (int32_t i = t; i < n; i += 1024) {
+          int4 e = tab[i];
+          const int m = e.x, l = e.y;
+          const int g = grp[m];
+          const int mt_m = (nr[m] + bm - 1) / bm;
+          const int mt = l % mt_m, nt = l / mt_m;
+          const int nN = kind == KIND_U ? (g < E_l ? P.nU_r : P.nU_s) : P.nD;
+          const int nb = nt / XB, w = min(XB, nN - nb * XB);
+          const int MT = mtx[mg[m]];
+          const int32_t rank = nb * MT * XB + ((m - mg[m]) * mpm + mt) * w + (nt - nb * XB);
+          e.y |= kind << KIND_SHIFT;
+          rt[(kind == KIND_U ? ub[m] : db[m]) + rank] = e;
+        }
+      };
+      place_q(ut, carry.x, KIND_U, XB_N);
+      place_q(dt, carry.y, KIND_D, XB_ND);
     }
   }
   int32_t* slot = wl_slot(wl, cap);

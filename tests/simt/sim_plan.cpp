@@ -25,6 +25,7 @@ int main(int argc, char** argv) {
   wb.nU_s = hdr[9]; wb.nD = hdr[10]; wb.gather = hdr[11]; wb.ring = hdr[12]; wb.xcd_split = hdr[13];
   wb.n_slots = hdr[14]; wb.cap = hdr[15]; wb.cap_u = hdr[16]; wb.cap_d = hdr[17]; wb.cap_r = hdr[18];
   const int64_t route_cap = hdr[19];
+  wb.loop = hdr[20]; wb.ks_u = hdr[21]; wb.ks_dr = hdr[22]; wb.ks_ds = hdr[23];
   wb.route_cap = route_cap;
   const int64_t n_routes = T * k;
   std::vector<int32_t> idx(std::max<int64_t>(1, n_routes));

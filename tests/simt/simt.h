@@ -65,6 +65,12 @@ inline int __ffsll(unsigned long long v) { return __builtin_ffsll((long long)v);
 inline int __popcll(unsigned long long v) { return __builtin_popcountll(v); }
 inline int __builtin_amdgcn_readfirstlane(int v) { return wave_get(v, 0); }
 template <class T> inline T atomicAdd(T* p, T v) { return std::atomic_ref<T>(*p).fetch_add(v); }
+template <class T> inline T atomicMin(T* p, T v) {
+  std::atomic_ref<T> a(*p);
+  T cur = a.load();
+  while (v < cur && !a.compare_exchange_weak(cur, v)) {}
+  return cur;
+}
 inline int min(int a, int b) { return a < b ? a : b; }
 inline int max(int a, int b) { return a > b ? a : b; }
 inline int64_t min(int64_t a, int64_t b) { return a < b ? a : b; }

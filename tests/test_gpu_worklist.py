@@ -78,8 +78,62 @@ def _check(wl, layer, counts, offsets, ring):
     return check_worklist(wl, _read(layer), counts, offsets, ring)
 
 
+def check_loop_table(got, ent, nu, nd, grp, E_l, wl):
+    """The persistent stage-order table: every gate/up and down tile exactly once; per queue
+    (XCD segment; one queue without the split) all up tiles before all down tiles, and every
+    down tile's minibatch with all its up tiles in the same queue (so each wait points earlier
+    in its own queue and at data produced under the same L2); a whole expert keeps the stage
+    table's order; the queues' work (K steps) within one unit of an even share."""
+    n, n_r, xr = len(nu), got["n_r"], [int(v) for v in got["xr"]]
+    rt = [tuple(int(v) for v in row) for row in got["rtab"][:n_r]]
+    want = set()
+    for m in range(n):
+        for k, cnt in (("U", nu[m]), ("D", nd[m])):
+            for l in range(cnt):
+                e = ent(m, l)
+                e[1] = (KINDS[k] << KIND_SHIFT) | l
+                want.add(tuple(e))
+    assert len(rt) == len(want) and set(rt) == want
+    segs = [(xr[x], xr[x + 1]) for x in range(8)] if got["affine"] else [(0, n_r)]
+    assert xr[0] == 0 and all(a <= b for a, b in segs) and segs[-1][1] == n_r
+    kind = lambda e: e[1] >> KIND_SHIFT
+    seg_of = {}
+    for q, (a, b) in enumerate(segs):
+        kinds = [kind(e) for e in rt[a:b]]
+        assert kinds == sorted(kinds), "up tiles first"
+        for e in rt[a:b]:
+            seg_of.setdefault(e[0], set()).add(q)
+    assert all(len(v) == 1 for v in seg_of.values()), "a minibatch in one queue"
+    # an expert wholly in one queue keeps the stage tables' order there
+    key = lambda e: (e[0], e[1] & ((1 << KIND_SHIFT) - 1))
+    for tab, k in ((got["utab"], "U"), (got["dtab"], "D")):
+        stage = [key(tuple(int(v) for v in row)) for row in tab[:got["n_u" if k == "U" else "n_d"]]]
+        for g in set(grp):
+            ms = [m for m in range(n) if grp[m] == g]
+            qs = set().union(*(seg_of[m] for m in ms))
+            if len(qs) != 1:
+                continue
+            a, b = segs[next(iter(qs))]
+            inq = [key(e) for e in rt[a:b] if kind(e) == KINDS[k] and grp[e[0]] == g]
+            assert inq == [e for e in stage if grp[e[0]] == g], (k, g)
+    ks_u, ks_dr, ks_ds = wl.d // 64, wl.I // 64, wl.n_shared * wl.I_shared // 64
+    if got["affine"]:
+        work = [nu[m] * ks_u + nd[m] * (ks_dr if grp[m] < E_l else ks_ds) for m in range(n)]
+        q_work = [0] * len(segs)
+        for m in range(n):
+            q_work[next(iter(seg_of[m]))] += work[m]
+        total = sum(work)
+        unit = max(sum(work[m] for m in range(n) if grp[m] == g) for g in set(grp) if g < E_l)
+        unit = min(unit, total // 32 + max(work))
+        assert max(q_work) <= total / 8 + unit, (q_work, total, unit)
+
+
 def check_worklist(wl, got, counts, offsets, ring):
-    """Compares a parsed work list with the models; returns the number of minibatches."""
+    """Compares a parsed work list with the models; returns the number of minibatches. ring:
+    False (stage tables), True (ring order) or "loop" (stage tables and the persistent
+    stage-order table)."""
+    loop = ring == "loop"
+    ring = ring is True
     assert got["err"] == 0
     E_l, mb = wl.E_l, wl.minibatch_rows
     I_sh = wl.n_shared * wl.I_shared
@@ -105,7 +159,8 @@ def check_worklist(wl, got, counts, offsets, ring):
     assert np.array_equal(got["ds"], np.cumsum([0] + nd))
     assert np.array_equal(got["gs"], np.cumsum([0] + ng))
     if not ring:
-        assert got["n_u"] == us[-1] and got["n_d"] == sum(nd) and got["n_r"] == 0
+        assert got["n_u"] == us[-1] and got["n_d"] == sum(nd)
+        assert got["n_r"] == (got["n_u"] + got["n_d"] if loop else 0)
         for p, (m, l) in upos.items():
             assert list(got["utab"][p]) == ent(m, l), ("up", p)
         _, _, _, dpos = stage_table(list(counts), n_own, mb, BM, nD, nD, XB_ND)
@@ -116,6 +171,8 @@ def check_worklist(wl, got, counts, offsets, ring):
             if nN_s > nN_r:                            # shared experts' down tiles first
                 p = p - d_sh0 if m >= n_routed else p + d_sh
             assert list(got["dtab"][p]) == ent(m, l), ("down", p)
+        if loop:
+            check_loop_table(got, ent, nu, nd, [g for g, _ in mbs], E_l, wl)
     else:
         n_slots = wl.ring_rows // mb
         lay = ring_layout(nu, nd, ng, n_slots)
@@ -133,7 +190,7 @@ def check_worklist(wl, got, counts, offsets, ring):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("ring", [False, True])
+@pytest.mark.parametrize("ring", [False, True, "loop"])
 def test_worklist_matches_the_scheduling_models(name, ring):
     import routing_grouped_expert_gemm_amd as mok
     wl = CASES[name]
@@ -143,7 +200,8 @@ def test_worklist_matches_the_scheduling_models(name, ring):
     idx, w = _oracle_topk(wl, cpu)
     plan = oracle.dispatch_plan(idx, wl.e0, wl.E_l, wl.tokens_per_rank)
     topk = (torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV))
-    layer = gpu_layer(wl, inp, topk=topk, flags=0 if ring else mok.MOK_FLAG_NO_RING)
+    flags = {False: mok.MOK_FLAG_NO_RING, True: 0, "loop": mok.MOK_FLAG_STAGE_LOOP}[ring]
+    layer = gpu_layer(wl, inp, topk=topk, flags=flags)
     layer.forward()
     torch.cuda.synchronize()
     assert np.array_equal(to_np(layer.inter["counts"]), plan["counts"])

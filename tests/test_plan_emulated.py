@@ -64,7 +64,10 @@ def _cdiv(a, b):
 
 
 def _params(wl, ring):
-    """The plan and work-list arguments the forward passes (the layout of api.hip)."""
+    """The plan and work-list arguments the forward passes (the layout of api.hip); ring is
+    False (stage order), True (ring order) or "loop" (stage order run by the persistent loop)."""
+    loop = ring == "loop"
+    ring = ring is True
     mb = wl.minibatch_rows
     mx = wl.dtype in ("mxfp8", "mxfp4")
     n_cap = wl.T_pool * min(wl.k, wl.E_l)
@@ -74,11 +77,11 @@ def _params(wl, ring):
     mt, nU, nD = _cdiv(mb, 256), max(_cdiv(wl.I, 128), _cdiv(I_sh, 128)), _cdiv(wl.d, 256)
     cap_u, cap_d = max_mb * mt * nU, max_mb * mt * nD
     cap_g = max_mb * _cdiv(mb, 64) if (ring and mx) else 0
-    cap_r = cap_u + cap_d + cap_g if ring else 0
+    cap_r = cap_u + cap_d + cap_g if ring else (cap_u + cap_d if loop else 0)
     T_own = wl.T_own if wl.n_shared > 0 else 0
     return [wl.T_pool, wl.k, wl.e0, wl.E_l, wl.tokens_per_rank, T_own, mb, 256, _cdiv(wl.I, 128),
             _cdiv(I_sh, 128), nD, int(ring and mx), int(ring), 1, n_slots, max_mb, cap_u, cap_d,
-            cap_r, max(1, n_cap), 0, 0, 0, 0]
+            cap_r, max(1, n_cap), int(loop), wl.d // 64, wl.I // 64, I_sh // 64]
 
 
 def _run(sim, tmp_path, wl, idx, ring):
@@ -140,7 +143,7 @@ CASES = {
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("ring", [False, True])
+@pytest.mark.parametrize("ring", [False, True, "loop"])
 def test_plan_and_worklist_kernels_on_cpu(sim, tmp_path, name, ring):
     wl, make_idx = CASES[name]
     n = _run(sim, tmp_path, wl, make_idx(), ring)
