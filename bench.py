@@ -152,6 +152,7 @@ def algorithmic_bytes(wl, n_routes: int) -> dict:
            "k_topk": 4 * T * E + 8 * T * k}
     if wl.routing == "router":
         out["k_router_logits"] = T * d * es + E * d * es + 4 * T * E
+        out["k_route"] = T * d * es + E * d * es + 4 * T * E + 8 * T * k   # logits + top-k
     if wl.full_layer:
         out["k_combine"] = T * d * es * (k + 2)
     if wl.dtype in ("mxfp8", "mxfp4"):
