@@ -144,7 +144,8 @@ def _written(layer):
 
 @pytest.mark.parametrize("name,ring", [("full_bf16", True), ("full_bf16", False),
                                        ("share_mxfp8", False), ("share_mxfp8", True),
-                                       ("share_mxfp4", False)])
+                                       ("share_mxfp4", False), ("full_bf16", "loop"),
+                                       ("share_mxfp8", "loop")])
 def test_forward_captured_in_a_hip_graph(name, ring):
     """The forward records into a HIP graph (so it makes no host synchronisation and reads
     nothing back), and every replay -- with eager work and synchronisations between them --
@@ -154,7 +155,8 @@ def test_forward_captured_in_a_hip_graph(name, ring):
     wl = SMALL[name]
     inp = make_inputs(wl, DEV)
     topk = gpu_topk(inp["logits"], wl.k) if wl.routing == "logits" else None
-    layer = gpu_layer(wl, inp, topk=topk, flags=0 if ring else mok.MOK_FLAG_NO_RING)
+    flags = {True: 0, False: mok.MOK_FLAG_NO_RING, "loop": mok.MOK_FLAG_STAGE_LOOP}[ring]
+    layer = gpu_layer(wl, inp, topk=topk, flags=flags)
     layer.forward()
     torch.cuda.synchronize()
     ref = _written(layer)
