@@ -1325,6 +1325,13 @@ __global__ __launch_bounds__(C::NT, 1) void k_ring(ExpertPass p) {
 // y[t] = S[t] + sum_{j ascending} P[t*k + j], float32 accumulator, one rounding. One thread
 // per 16 B of a row: the k + 1 rows of a token are read once, y is written once. KC > 0: k ==
 // KC known at compile time, so all k + 1 loads are in flight together; KC == 0: any k.
+// The route slot rows and S are read once here: non-temporal loads keep them from displacing
+// cached lines (measured: 42 against 45 us on the EP1 layer).
+typedef unsigned int cmb_u32x4 __attribute__((ext_vector_type(4)));
+MOK_DEV uint4 cmb_ld(const void* p) {
+  const cmb_u32x4 v = __builtin_nontemporal_load((const cmb_u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 template <class OT, int KC>
 __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ S, const OT* __restrict__ P,
                                                  OT* __restrict__ y, int64_t n_tok, int k_rt, int d) {
@@ -1340,10 +1347,10 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ S, const
   uint4 pv[KC > 0 ? KC : 1];
   if constexpr (KC > 0) {
 #pragma unroll
-    for (int j = 0; j < KC; ++j) pv[j] = *(const uint4*)(P + (t * k + j) * d + c);
+    for (int j = 0; j < KC; ++j) pv[j] = cmb_ld(P + (t * k + j) * d + c);
   }
   if (S) {  // no shared expert: S = 0
-    const uint4 s = *(const uint4*)(S + t * d + c);
+    const uint4 s = cmb_ld(S + t * d + c);
     const OT* sv = (const OT*)&s;
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = load_as_f32<OT>(sv + v);
